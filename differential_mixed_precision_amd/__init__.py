@@ -1,0 +1,54 @@
+"""FMDQ differential linear layer (DSTAR, arXiv 2607.15846) on AMD MI355X.
+
+The layer runs in three HIP kernels behind a C ABI (include/dstar_fmdq.h):
+``quantize`` (differential + sub-channel quantization), ``bucket`` (reorder
+channels by FPoT tag) and ``linear`` (grouped int8 GEMM with shift alignment,
+dequantization and the reverse differential).  This package is the thin
+Python binding; ``FmdqLayer`` allocates the buffers of one layer with torch and
+calls the three stages on the current stream.
+"""
+from __future__ import annotations
+
+from . import _binding
+from ._binding import (FmdqError, Params, bucket, linear, load, make_params,  # noqa: F401
+                       quantize)
+
+__all__ = ["FmdqError", "Params", "FmdqLayer", "bucket", "linear", "load", "make_params",
+           "quantize", "n_tiles"]
+
+
+def n_tiles(rows: int, token_tile: int) -> int:
+    return (rows + token_tile - 1) // token_tile
+
+
+class FmdqLayer:
+    """Device buffers of one FMDQ differential linear layer and its three calls.
+
+    ``step(x_t, x_prev, y)`` updates the cached output ``y`` in place:
+    y ← y + w_scale · W · Δ̂, with Δ̂ the FMDQ-quantized X_t − X_{t−1}.
+    """
+
+    def __init__(self, w, w_scale, rows: int, token_tile: int, base: float, thr0_log2: int,
+                 tokens_per_seq: int | None = None):
+        import torch
+        assert w.dtype == torch.int8 and w.is_cuda and w.dim() == 2
+        self.K, self.N = int(w.shape[0]), int(w.shape[1])
+        self.w, self.w_scale = w.contiguous(), w_scale.contiguous()
+        self.p = make_params(rows, self.K, token_tile, base, thr0_log2, tokens_per_seq)
+        self.T = token_tile
+        nt = n_tiles(rows, token_tile)
+        dev = w.device
+        self.codes = torch.empty((nt, self.K, token_tile), dtype=torch.int8, device=dev)
+        self.tags = torch.empty((nt, self.K), dtype=torch.uint8, device=dev)
+        self.perm = torch.empty((nt, self.K), dtype=torch.int16, device=dev)  # uint16 ids
+        self.group_off = torch.empty((nt, 17), dtype=torch.int32, device=dev)
+        self.bit_hist = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def step(self, x_t, x_prev, y, y_out=None, stream=None, hist: bool = True):
+        quantize(self.p, x_t, x_prev, self.codes, self.tags,
+                 self.bit_hist if hist else None, stream)
+        bucket(self.p, self.tags, self.perm, self.group_off, stream)
+        out = y if y_out is None else y_out
+        linear(self.p, self.N, self.codes, self.perm, self.group_off, self.w, self.w_scale,
+               y, out, stream=stream)
+        return out

@@ -1,0 +1,119 @@
+"""ctypes binding of libdstar_fmdq.so (the C ABI declared in include/dstar_fmdq.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+the library.  Tensors are torch tensors on the GPU (their data_ptr() is passed
+through); torch is used for device memory and streams, nothing else.  If the
+library has not been built, every call raises — there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdstar_fmdq.so")
+
+OK, EINVAL, ENULL, EALIGN, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5
+NUM_TAGS = 16
+TAG_OFFSET = 15
+POT_MAX = 21
+PREC_SHIFT = 4
+MAX_K = 65535
+ABI_VERSION = 1
+
+SYMBOLS = ("dstar_fmdq_quantize", "dstar_fmdq_bucket", "dstar_fmdq_linear",
+           "dstar_fmdq_last_error", "dstar_fmdq_abi_version")
+
+
+class FmdqError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"dstar_fmdq error {code}: {msg}")
+        self.code = code
+
+
+class Params(ctypes.Structure):
+    """dstar_fmdq_params."""
+    _fields_ = [("rows", ctypes.c_int32), ("tokens_per_seq", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("token_tile", ctypes.c_int32),
+                ("base", ctypes.c_float), ("thr0_log2", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Loads the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m differential_mixed_precision_amd.build` "
+            "(or __graft_entry__.build()).  There is no fallback implementation.")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(Params)
+    vp = ctypes.c_void_p
+    i32 = ctypes.c_int32
+    lib.dstar_fmdq_quantize.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.dstar_fmdq_quantize.restype = ctypes.c_int
+    lib.dstar_fmdq_bucket.argtypes = [P, vp, vp, vp, vp]
+    lib.dstar_fmdq_bucket.restype = ctypes.c_int
+    lib.dstar_fmdq_linear.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
+    lib.dstar_fmdq_linear.restype = ctypes.c_int
+    lib.dstar_fmdq_last_error.argtypes = []
+    lib.dstar_fmdq_last_error.restype = ctypes.c_char_p
+    lib.dstar_fmdq_abi_version.argtypes = []
+    lib.dstar_fmdq_abi_version.restype = ctypes.c_int
+    if lib.dstar_fmdq_abi_version() != ABI_VERSION:
+        raise RuntimeError("libdstar_fmdq.so ABI version mismatch; rebuild it")
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int) -> None:
+    if rc != OK:
+        raise FmdqError(rc, load().dstar_fmdq_last_error().decode())
+
+
+def make_params(rows: int, K: int, token_tile: int, base: float, thr0_log2: int,
+                tokens_per_seq: int | None = None) -> Params:
+    return Params(int(rows), int(rows if tokens_per_seq is None else tokens_per_seq), int(K),
+                  int(token_tile), float(base), int(thr0_log2))
+
+
+def quantize(p: Params, x_t, x_prev, codes, tags, bit_hist=None, stream=None) -> None:
+    """dstar_fmdq_quantize."""
+    _check(load().dstar_fmdq_quantize(ctypes.byref(p), _ptr(x_t), _ptr(x_prev), _ptr(codes),
+                                      _ptr(tags), _ptr(bit_hist), _stream(stream)))
+
+
+def bucket(p: Params, tags, perm, group_off, stream=None) -> None:
+    """dstar_fmdq_bucket."""
+    _check(load().dstar_fmdq_bucket(ctypes.byref(p), _ptr(tags), _ptr(perm), _ptr(group_off),
+                                    _stream(stream)))
+
+
+def linear(p: Params, N: int, codes, perm, group_off, w, w_scale, y_prev, y_out,
+           acc_dbg=None, dbg_tile_lo: int = 0, dbg_tile_hi: int = 0, stream=None) -> None:
+    """dstar_fmdq_linear."""
+    _check(load().dstar_fmdq_linear(ctypes.byref(p), int(N), _ptr(codes), _ptr(perm),
+                                    _ptr(group_off), _ptr(w), _ptr(w_scale), _ptr(y_prev),
+                                    _ptr(y_out), _ptr(acc_dbg), int(dbg_tile_lo),
+                                    int(dbg_tile_hi), _stream(stream)))

@@ -1,0 +1,158 @@
+// C ABI of the FMDQ differential linear (declared in include/dstar_fmdq.h):
+// host-side argument checks, then the stream-ordered kernel launches.
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "fmdq_internal.h"
+
+namespace dstar {
+
+int launch_linear_general(const LinearArgs& a, hipStream_t s);
+
+namespace {
+thread_local std::string g_error;
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// Checks the parameters shared by all stages; fills n_t.
+int check_params(const dstar_fmdq_params* p, int64_t* nt) {
+  if (p == nullptr) return set_error(DSTAR_ENULL, "params is NULL");
+  if (p->rows < 0) return set_error(DSTAR_EINVAL, "rows = %d < 0", p->rows);
+  if (p->K < 1 || p->K > DSTAR_FMDQ_MAX_K)
+    return set_error(DSTAR_EINVAL, "K = %d outside [1, %d]", p->K, DSTAR_FMDQ_MAX_K);
+  if (p->token_tile != 16 && p->token_tile != 32 && p->token_tile != 64)
+    return set_error(DSTAR_EINVAL, "token_tile = %d not in {16, 32, 64}", p->token_tile);
+  if (p->tokens_per_seq < 1)
+    return set_error(DSTAR_EINVAL, "tokens_per_seq = %d < 1", p->tokens_per_seq);
+  if (p->rows > p->tokens_per_seq &&
+      (p->rows % p->tokens_per_seq != 0 || p->tokens_per_seq % p->token_tile != 0))
+    return set_error(DSTAR_EINVAL,
+                     "rows = %d spans several sequences of %d tokens: rows must be a multiple of "
+                     "tokens_per_seq and tokens_per_seq a multiple of token_tile = %d",
+                     p->rows, p->tokens_per_seq, p->token_tile);
+  const float b = p->base;
+  if (!std::isfinite(b) || !(b >= std::ldexp(1.0f, -100)) || !(b <= std::ldexp(1.0f, 100)))
+    return set_error(DSTAR_EINVAL, "base = %g outside [2^-100, 2^100]", (double)b);
+  if (p->thr0_log2 < 1 || p->thr0_log2 > 15)
+    return set_error(DSTAR_EINVAL, "thr0_log2 = %d outside [1, 15]", p->thr0_log2);
+  *nt = n_tiles(p->rows, p->token_tile);
+  return DSTAR_OK;
+}
+}  // namespace
+
+int set_error(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+void clear_error() { g_error.clear(); }
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(DSTAR_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return DSTAR_OK;
+}
+
+}  // namespace dstar
+
+using namespace dstar;
+
+extern "C" {
+
+int dstar_fmdq_abi_version(void) { return DSTAR_FMDQ_ABI_VERSION; }
+
+const char* dstar_fmdq_last_error(void) { return g_error.c_str(); }
+
+int dstar_fmdq_quantize(const dstar_fmdq_params* p, const float* x_t, const float* x_prev,
+                        int8_t* codes, uint8_t* tags, uint32_t* bit_hist, void* stream) {
+  clear_error();
+  int64_t nt = 0;
+  if (int rc = check_params(p, &nt)) return rc;
+  if (p->rows == 0) return DSTAR_OK;
+  if (!x_t || !x_prev || !codes || !tags)
+    return set_error(DSTAR_ENULL, "quantize: x_t, x_prev, codes and tags must not be NULL");
+  if (!aligned(x_t, 16) || !aligned(x_prev, 16) || !aligned(codes, 16))
+    return set_error(DSTAR_EALIGN, "quantize: x_t, x_prev and codes must be 16-byte aligned");
+  if (bit_hist && !aligned(bit_hist, 4))
+    return set_error(DSTAR_EALIGN, "quantize: bit_hist must be 4-byte aligned");
+  QuantizeArgs a;
+  a.x_t = x_t;
+  a.x_prev = x_prev;
+  a.codes = codes;
+  a.tags = tags;
+  a.bit_hist = bit_hist;
+  a.rows = p->rows;
+  a.K = p->K;
+  a.T = p->token_tile;
+  a.base = p->base;
+  a.inv_base = (float)(1.0 / (double)p->base);
+  a.k0 = p->thr0_log2;
+  return launch_quantize(a, (hipStream_t)stream);
+}
+
+int dstar_fmdq_bucket(const dstar_fmdq_params* p, const uint8_t* tags, uint16_t* perm,
+                      int32_t* group_off, void* stream) {
+  clear_error();
+  int64_t nt = 0;
+  if (int rc = check_params(p, &nt)) return rc;
+  if (nt == 0) return DSTAR_OK;
+  if (!tags || !perm || !group_off)
+    return set_error(DSTAR_ENULL, "bucket: tags, perm and group_off must not be NULL");
+  if (!aligned(perm, 2) || !aligned(group_off, 4))
+    return set_error(DSTAR_EALIGN, "bucket: perm must be 2-byte and group_off 4-byte aligned");
+  BucketArgs a;
+  a.tags = tags;
+  a.perm = perm;
+  a.group_off = group_off;
+  a.n_tiles = nt;
+  a.K = p->K;
+  return launch_bucket(a, (hipStream_t)stream);
+}
+
+int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N, const int8_t* codes,
+                      const uint16_t* perm, const int32_t* group_off, const int8_t* w,
+                      const float* w_scale, const float* y_prev, float* y_out, int32_t* acc_dbg,
+                      int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream) {
+  clear_error();
+  int64_t nt = 0;
+  if (int rc = check_params(p, &nt)) return rc;
+  if (N < 1 || N > (1 << 20) || N % 4 != 0)
+    return set_error(DSTAR_EINVAL, "linear: N = %d must be a multiple of 4 in [4, 2^20]", N);
+  if (acc_dbg && (dbg_tile_lo < 0 || dbg_tile_lo >= dbg_tile_hi || dbg_tile_hi > nt))
+    return set_error(DSTAR_EINVAL, "linear: debug tile range [%d, %d) not within [0, %lld)",
+                     dbg_tile_lo, dbg_tile_hi, (long long)nt);
+  if (nt == 0) return DSTAR_OK;
+  if (!codes || !perm || !group_off || !w || !w_scale || !y_prev || !y_out)
+    return set_error(DSTAR_ENULL, "linear: codes, perm, group_off, w, w_scale, y_prev and y_out must not be NULL");
+  if (!aligned(codes, 16) || !aligned(w, 16) || !aligned(y_prev, 16) || !aligned(y_out, 16) ||
+      !aligned(w_scale, 4) || !aligned(perm, 2) || !aligned(group_off, 4) ||
+      (acc_dbg && !aligned(acc_dbg, 4)))
+    return set_error(DSTAR_EALIGN,
+                     "linear: codes, w, y_prev, y_out must be 16-byte aligned (w_scale, "
+                     "group_off, acc_dbg 4-byte, perm 2-byte)");
+  LinearArgs a;
+  a.codes = codes;
+  a.perm = perm;
+  a.group_off = group_off;
+  a.w = w;
+  a.w_scale = w_scale;
+  a.y_prev = y_prev;
+  a.y_out = y_out;
+  a.acc_dbg = acc_dbg;
+  a.dbg_lo = dbg_tile_lo;
+  a.dbg_hi = dbg_tile_hi;
+  a.rows = p->rows;
+  a.K = p->K;
+  a.N = N;
+  a.T = p->token_tile;
+  a.base = (double)p->base;
+  return launch_linear(a, (hipStream_t)stream);
+}
+
+}  // extern "C"

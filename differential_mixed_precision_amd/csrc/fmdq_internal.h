@@ -1,0 +1,64 @@
+// Internal declarations shared by the HIP sources of the FMDQ library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+#include <cstdio>
+#include <cstdarg>
+#include "dstar_fmdq.h"
+
+namespace dstar {
+
+// Records a thread-local error message and returns `code`.
+int set_error(int code, const char* fmt, ...);
+void clear_error();
+
+// Checks hipGetLastError() after a launch; returns DSTAR_OK or DSTAR_EHIP.
+int check_launch(const char* what);
+
+inline int64_t n_tiles(int64_t rows, int64_t T) { return (rows + T - 1) / T; }
+
+// Validated launch descriptions (sizes already checked by the API layer).
+struct QuantizeArgs {
+  const float* x_t;
+  const float* x_prev;
+  int8_t* codes;
+  uint8_t* tags;
+  uint32_t* bit_hist;
+  int64_t rows;
+  int32_t K;
+  int32_t T;
+  float base;
+  float inv_base;
+  int32_t k0;
+};
+int launch_quantize(const QuantizeArgs& a, hipStream_t s);
+
+struct BucketArgs {
+  const uint8_t* tags;
+  uint16_t* perm;
+  int32_t* group_off;
+  int64_t n_tiles;
+  int32_t K;
+};
+int launch_bucket(const BucketArgs& a, hipStream_t s);
+
+struct LinearArgs {
+  const int8_t* codes;
+  const uint16_t* perm;
+  const int32_t* group_off;
+  const int8_t* w;
+  const float* w_scale;
+  const float* y_prev;
+  float* y_out;
+  int32_t* acc_dbg;
+  int32_t dbg_lo;
+  int32_t dbg_hi;
+  int64_t rows;
+  int32_t K;
+  int32_t N;
+  int32_t T;
+  double base;
+};
+int launch_linear(const LinearArgs& a, hipStream_t s);
+
+}  // namespace dstar

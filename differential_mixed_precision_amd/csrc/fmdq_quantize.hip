@@ -1,0 +1,165 @@
+// Stage 1 of the FMDQ differential linear: fused differential + sub-channel
+// quantization (DSTAR, arXiv 2607.15846: §2.2 Eq. 1; §3.1 step 1 with Eq. 2-5;
+// §4.2 QPU stages 1-3).
+//
+// HBM-bound streaming kernel.  A thread owns CPT adjacent input channels of
+// one token tile: it reads the T rows of X_t and X_{t-1} for those channels
+// with CPT-wide vector loads (a wave reads 64*CPT*4 contiguous bytes per row),
+// keeps Δ in registers, reduces max|Δ| per channel, picks PoT / precision /
+// tag with exact float32 compares against base*2^j, and writes the T codes of
+// each channel as one contiguous run (codes are channel-major within a tile),
+// so every store is 16-byte and coalesced across the wave.
+#include "fmdq_internal.h"
+
+namespace dstar {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int CPT>
+struct FVec;
+template <>
+struct FVec<4> { using type = float4; };
+template <>
+struct FVec<2> { using type = float2; };
+template <>
+struct FVec<1> { using type = float; };
+
+template <int CPT>
+__device__ __forceinline__ void load_vec(const float* p, float (&v)[CPT]) {
+  typename FVec<CPT>::type t = *reinterpret_cast<const typename FVec<CPT>::type*>(p);
+  __builtin_memcpy(v, &t, sizeof(t));
+}
+
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+  return (uint32_t(a) & 0xFFu) | ((uint32_t(b) & 0xFFu) << 8) | ((uint32_t(c) & 0xFFu) << 16) |
+         ((uint32_t(d) & 0xFFu) << 24);
+}
+
+template <int T, int CPT>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantizeArgs a, int64_t n_work,
+                                                            int32_t slabs) {
+  uint32_t hist[4] = {0u, 0u, 0u, 0u};
+  const int64_t K = a.K;
+  const float inv_base = a.inv_base;
+  for (int64_t wi = blockIdx.x; wi < n_work; wi += gridDim.x) {
+    const int64_t tile = wi / slabs;
+    const int64_t slab = wi - tile * slabs;
+    const int64_t k = slab * (int64_t)(kThreads * CPT) + (int64_t)threadIdx.x * CPT;
+    if (k >= K) continue;
+    const int64_t r0 = tile * T;
+    const int nrows = (int)((a.rows - r0) < T ? (a.rows - r0) : T);
+
+    // Δ = X_t − X_{t−1} for T rows × CPT channels (Eq. 1), kept in registers.
+    float d[T][CPT];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      if (t < nrows) {
+        float xt[CPT], xp[CPT];
+        load_vec<CPT>(a.x_t + (r0 + t) * K + k, xt);
+        load_vec<CPT>(a.x_prev + (r0 + t) * K + k, xp);
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) d[t][c] = __fsub_rn(xt[c], xp[c]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) d[t][c] = 0.0f;
+      }
+    }
+
+    uint32_t tagword = 0;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      // M: largest |Δ| of the sub-channel (QPU stage 1).
+      float m = 0.0f;
+#pragma unroll
+      for (int t = 0; t < T; ++t) m = fmaxf(m, fabsf(d[t][c]));
+      // PoT = number of bin edges base*2^j (j = 0..20) strictly below M, i.e.
+      // the smallest j with M <= base*2^j, capped at 21 (Eq. 3; QPU stage 2).
+      int pot = 0;
+#pragma unroll
+      for (int j = 0; j < DSTAR_FMDQ_POT_MAX; ++j) pot += (m > ldexpf(a.base, j)) ? 1 : 0;
+      // Precision from the thresholds base*2^(k0+2N): p = b - 2 = log2(PCeil).
+      const int p = pot <= a.k0 ? 0 : pot <= a.k0 + 2 ? 2 : pot <= a.k0 + 4 ? 4 : 6;
+      const int e = pot - p;                               // step = base * 2^e
+      const float scale = __int_as_float((127 - e) << 23);  // 2^-e, exact
+      const float pceil = (float)(1 << p);
+      int q[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        float r = __fmul_rn(__fmul_rn(d[t][c], inv_base), scale);
+        r = fminf(fmaxf(rintf(r), -pceil), pceil);
+        q[t] = (int)r;
+      }
+      hist[p >> 1] += 1u;
+      const uint32_t tag = (uint32_t)(DSTAR_FMDQ_TAG_OFFSET - e) | ((uint32_t)(p >> 1) << DSTAR_FMDQ_PREC_SHIFT);
+      tagword |= tag << (8 * c);
+      // Codes of channel k+c: T contiguous bytes at codes[(tile*K + k + c)*T].
+      int4* dst = reinterpret_cast<int4*>(a.codes + ((tile * K + k + c) * T));
+#pragma unroll
+      for (int v = 0; v < T / 16; ++v) {
+        int4 o;
+        o.x = (int)pack4(q[16 * v + 0], q[16 * v + 1], q[16 * v + 2], q[16 * v + 3]);
+        o.y = (int)pack4(q[16 * v + 4], q[16 * v + 5], q[16 * v + 6], q[16 * v + 7]);
+        o.z = (int)pack4(q[16 * v + 8], q[16 * v + 9], q[16 * v + 10], q[16 * v + 11]);
+        o.w = (int)pack4(q[16 * v + 12], q[16 * v + 13], q[16 * v + 14], q[16 * v + 15]);
+        dst[v] = o;
+      }
+    }
+    uint8_t* tp = a.tags + tile * K + k;
+    if constexpr (CPT == 4) {
+      *reinterpret_cast<uint32_t*>(tp) = tagword;
+    } else if constexpr (CPT == 2) {
+      *reinterpret_cast<uint16_t*>(tp) = (uint16_t)tagword;
+    } else {
+      *tp = (uint8_t)tagword;
+    }
+  }
+
+  if (a.bit_hist == nullptr) return;
+  // Block-wide histogram reduction, then at most four atomics per block.
+  __shared__ uint32_t part[kThreads / 64][4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    uint32_t v = hist[b];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6][b] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < 4) {
+    uint32_t v = 0;
+    for (int w = 0; w < kThreads / 64; ++w) v += part[w][threadIdx.x];
+    if (v) atomicAdd(a.bit_hist + threadIdx.x, v);
+  }
+}
+
+template <int T, int CPT>
+int launch_t(const QuantizeArgs& a, hipStream_t s) {
+  const int64_t nt = n_tiles(a.rows, T);
+  const int32_t slabs = (int32_t)((a.K + kThreads * CPT - 1) / (kThreads * CPT));
+  const int64_t n_work = nt * slabs;
+  const int64_t grid = n_work < 4096 ? n_work : 4096;
+  hipLaunchKernelGGL((quantize_kernel<T, CPT>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
+                     n_work, slabs);
+  return check_launch("fmdq_quantize");
+}
+
+}  // namespace
+
+int launch_quantize(const QuantizeArgs& a, hipStream_t s) {
+  if (a.rows == 0) return DSTAR_OK;
+  const bool vec4 = (a.K % 4) == 0;
+  const bool vec2 = (a.K % 2) == 0;
+  switch (a.T) {
+    case 16:
+      return vec4 ? launch_t<16, 4>(a, s) : vec2 ? launch_t<16, 2>(a, s) : launch_t<16, 1>(a, s);
+    case 32:
+      return vec4 ? launch_t<32, 4>(a, s) : vec2 ? launch_t<32, 2>(a, s) : launch_t<32, 1>(a, s);
+    case 64:
+      return vec2 ? launch_t<64, 2>(a, s) : launch_t<64, 1>(a, s);
+    default:
+      return set_error(DSTAR_EUNSUPPORTED, "token_tile %d not supported", a.T);
+  }
+}
+
+}  // namespace dstar

@@ -1,0 +1,149 @@
+/*
+ * dstar_fmdq.h — C ABI of the FMDQ differential linear layer on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Method: "DSTAR: Accelerating Diffusion Transformers via Spatial and Temporal
+ * Redundancy Reduction" (arXiv 2607.15846), cited as DSTAR.  For two adjacent
+ * denoising timesteps a linear layer y = W x is updated differentially
+ * (DSTAR §2.2, Eq. 1): Y_t = Y_{t-1} + W·(X_t − X_{t-1}).  The difference Δ is
+ * quantized per sub-channel (token tile × input channel) with power-of-two
+ * scales relative to a static base (DSTAR §3.1 step 1, Eq. 2–5), the channels
+ * of each token tile are grouped by their fused precision/scale tag (FPoT,
+ * DSTAR §3.1 step 3), each group is multiplied by int8 weights into its own
+ * integer accumulator, the group sums are aligned by left shifts (DSTAR §3.1
+ * steps 2 and 5, Fig. 6), dequantized and added to the cached Y_{t-1} (DSTAR
+ * §4.2 "Design of MPU", §4.3 "Linear Operation").
+ *
+ * The three entry points are the three stages; each launches HIP kernels on
+ * the caller's stream and returns without synchronizing.
+ *
+ * Conventions for every entry point
+ *   - All array arguments are DEVICE pointers (memory from hipMalloc, or
+ *     torch CUDA tensors on ROCm), owned by the caller.  The library keeps no
+ *     reference to them after the call returns and allocates no memory.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *   - Return value: DSTAR_OK (0), or a negative DSTAR_E* code.  On error no
+ *     kernel was launched (except DSTAR_EHIP, reported after a failed launch)
+ *     and dstar_fmdq_last_error() describes the cause (thread-local string).
+ *   - Argument checks happen on the host before any HIP call, so invalid
+ *     arguments are reported even on a machine without a GPU.
+ *   - Inputs must be finite; results for NaN/Inf inputs are unspecified.
+ *   - Only y_out may alias y_prev; no other arguments may overlap.
+ */
+#ifndef DSTAR_FMDQ_H
+#define DSTAR_FMDQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSTAR_FMDQ_ABI_VERSION 1
+
+/* Rule constants (DSTAR §3.1 step 1; readings in the design notes):
+ * PCeil of a b-bit sub-channel is 2^(b-2); PoT is capped at POT_MAX so that
+ * the tag (b-2) - PoT + TAG_OFFSET always lies in [0, NUM_TAGS). */
+#define DSTAR_FMDQ_NUM_TAGS 16
+#define DSTAR_FMDQ_TAG_OFFSET 15
+#define DSTAR_FMDQ_POT_MAX 21
+#define DSTAR_FMDQ_PREC_SHIFT 4
+#define DSTAR_FMDQ_MAX_K 65535
+
+/* Status codes. */
+#define DSTAR_OK 0
+#define DSTAR_EINVAL (-1)       /* a size or parameter is out of range       */
+#define DSTAR_ENULL (-2)        /* a required pointer is NULL                */
+#define DSTAR_EALIGN (-3)       /* a pointer is not aligned as required      */
+#define DSTAR_EUNSUPPORTED (-4) /* valid for the method, not supported here  */
+#define DSTAR_EHIP (-5)         /* the HIP runtime reported an error         */
+
+/* Layer parameters shared by the three stages.
+ *   rows            M = batch * tokens, rows of X and Y (batch-major), >= 0.
+ *   tokens_per_seq  tokens of one sequence; token tiles never straddle two
+ *                   sequences, so rows must equal tokens_per_seq (one
+ *                   sequence, last tile may be ragged) or be a multiple of it
+ *                   with tokens_per_seq % token_tile == 0.
+ *   K               input channels, 1..65535 (channel ids are uint16).
+ *   token_tile      T, rows per token tile: 16, 32 or 64 (DSTAR §3.1 step 1
+ *                   tiles Δ along the token dimension).
+ *   base            static per-layer base scale (DSTAR §3.1, "predefined
+ *                   static base"), a normal float in [2^-100, 2^100].
+ *   thr0_log2       k0 in Thr_0 = base * 2^k0, the 2-bit threshold of the
+ *                   precision bins Thr_0 * 4^N (DSTAR §3.1 step 1), 1..15.
+ * Tiles: n_t = ceil(rows / T); tile τ holds rows [τT, min(τT+T, rows)). */
+typedef struct {
+  int32_t rows;
+  int32_t tokens_per_seq;
+  int32_t K;
+  int32_t token_tile;
+  float base;
+  int32_t thr0_log2;
+} dstar_fmdq_params;
+
+/* Stage 1 — differential + sub-channel quantization (DSTAR Eq. 1; §3.1 step
+ * 1, Eq. 2-5; §4.2 QPU stages 1-3).
+ *   x_t, x_prev  [rows][K] float32 row-major, 16-byte aligned.
+ *   codes        [n_t][K][T] int8 (out): code of row τT+t, channel k at
+ *                codes[(τK + k)T + t]; rows past the end of a ragged last tile
+ *                are written 0.  16-byte aligned.
+ *   tags         [n_t][K] uint8 (out): bits 0-3 the FPoT tag g = (b-2) - PoT +
+ *                15 (ascending g = ascending FPoT; the sub-channel's step is
+ *                base * 2^(15-g)), bits 4-5 the precision code b/2 - 1.
+ *   bit_hist     uint32[4] or NULL: counts of sub-channels quantized at
+ *                2/4/6/8 bits are ADDED to it (the caller zeroes it).
+ * Per sub-channel: M = max |Δ| over the tile's rows; PoT = smallest j in
+ * [0, 21] with M <= base*2^j (21 if none); bits = 2/4/6/8 for PoT <= k0,
+ * k0+2, k0+4, else; e = PoT - (b-2); code = clip(rint(fl32(fl32(Δ *
+ * fl32(1/base)) * 2^-e)), ±2^(b-2)). */
+int dstar_fmdq_quantize(const dstar_fmdq_params* p, const float* x_t,
+                        const float* x_prev, int8_t* codes, uint8_t* tags,
+                        uint32_t* bit_hist, void* stream);
+
+/* Stage 2 — reorder the channels of every token tile by FPoT (DSTAR §3.1
+ * step 3; §4.2 QPU stage 4), as a stable counting sort.
+ *   tags       [n_t][K] uint8 from stage 1 (only bits 0-3 are read).
+ *   perm       [n_t][K] uint16 (out): channel ids of tile τ sorted by (tag
+ *              ascending, channel ascending).
+ *   group_off  [n_t][17] int32 (out): group_off[τ][g] = number of channels of
+ *              tile τ with tag < g; group g is perm[τ][group_off[τ][g] ..
+ *              group_off[τ][g+1]). */
+int dstar_fmdq_bucket(const dstar_fmdq_params* p, const uint8_t* tags,
+                      uint16_t* perm, int32_t* group_off, void* stream);
+
+/* Stage 3 — grouped int8 GEMM, shift alignment, dequantization and reverse
+ * differential (DSTAR §3.1 step 5, Fig. 6; §4.2 MPU, inverse quantization and
+ * accumulation units; §4.3 reverse differential fused into the GEMM).
+ *   N          output channels, a multiple of 4 in [4, 2^20].
+ *   codes      from stage 1; perm, group_off from stage 2.  Channel k of
+ *              group g of tile τ is multiplied at step 2^(15-g) * base.
+ *   w          [K][N] int8 row-major, 16-byte aligned.
+ *   w_scale    [N] float32, per-output-channel weight scale.
+ *   y_prev     [rows][N] float32, the cached output Y_{t-1}.
+ *   y_out      [rows][N] float32 (out), Y_t; may equal y_prev (in place).
+ *              y_prev and y_out are 16-byte aligned.
+ *   acc_dbg    NULL, or [dbg_tile_hi - dbg_tile_lo][16][T][N] int32 (out): the
+ *              group accumulators acc_g[t][n] = Σ over channels k of group g
+ *              of code(τT+t, k) * w[k][n] for tiles τ in [dbg_tile_lo,
+ *              dbg_tile_hi); groups absent from a tile and rows past a ragged
+ *              end are written 0.  Needs 0 <= lo < hi <= n_t.
+ * Per output: S = Σ_g acc_g * 2^(15-g) (int64, exact);
+ * y_out = fl32(f64(y_prev) + (f64(S) * f64(base)) * f64(w_scale[n])). */
+int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N,
+                      const int8_t* codes, const uint16_t* perm,
+                      const int32_t* group_off,
+                      const int8_t* w, const float* w_scale,
+                      const float* y_prev, float* y_out, int32_t* acc_dbg,
+                      int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream);
+
+/* Message describing the last error of the calling thread ("" if none). */
+const char* dstar_fmdq_last_error(void);
+
+/* DSTAR_FMDQ_ABI_VERSION of the library. */
+int dstar_fmdq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSTAR_FMDQ_H */

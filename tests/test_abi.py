@@ -1,0 +1,129 @@
+"""The C ABI library: it loads, exports every entry point the header declares,
+agrees with the oracle on the rule constants, and rejects invalid arguments on
+the host (no kernel is launched, so these run without a GPU)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dstar_fmdq.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from differential_mixed_precision_amd import _binding
+    if not os.path.exists(_binding.LIB_PATH):
+        from differential_mixed_precision_amd import build
+        build.build()
+    return _binding
+
+
+def _header():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def test_library_exports_every_declared_entry_point(lib):
+    text = _header()
+    declared = set(re.findall(r"^\s*(?:int|const char\*)\s+(dstar_fmdq_\w+)\s*\(", text, re.M))
+    assert declared == set(lib.SYMBOLS)
+    raw = ctypes.CDLL(lib.LIB_PATH)
+    for name in declared:
+        assert hasattr(raw, name), name
+    assert lib.load().dstar_fmdq_abi_version() == lib.ABI_VERSION
+
+
+def test_header_constants_match_oracle_and_binding(lib):
+    from oracle import fmdq
+    text = _header()
+    consts = dict(re.findall(r"#define\s+(DSTAR_\w+)\s+\(?(-?\d+)\)?", text))
+    assert int(consts["DSTAR_FMDQ_NUM_TAGS"]) == fmdq.N_TAGS == lib.NUM_TAGS
+    assert int(consts["DSTAR_FMDQ_TAG_OFFSET"]) == fmdq.TAG_OFF == lib.TAG_OFFSET
+    assert int(consts["DSTAR_FMDQ_POT_MAX"]) == fmdq.POT_HI == lib.POT_MAX
+    assert int(consts["DSTAR_FMDQ_PREC_SHIFT"]) == fmdq.PREC_SHIFT == lib.PREC_SHIFT
+    assert int(consts["DSTAR_FMDQ_ABI_VERSION"]) == lib.ABI_VERSION
+    for name, code in (("DSTAR_OK", lib.OK), ("DSTAR_EINVAL", lib.EINVAL), ("DSTAR_ENULL", lib.ENULL),
+                       ("DSTAR_EALIGN", lib.EALIGN), ("DSTAR_EUNSUPPORTED", lib.EUNSUPPORTED),
+                       ("DSTAR_EHIP", lib.EHIP)):
+        assert int(consts[name]) == code
+
+
+def test_params_struct_layout(lib):
+    assert ctypes.sizeof(lib.Params) == 24
+    assert [f[0] for f in lib.Params._fields_] == ["rows", "tokens_per_seq", "K", "token_tile",
+                                                    "base", "thr0_log2"]
+
+
+FAKE = 0x10000  # a 64 KiB-aligned address; never dereferenced (calls fail validation first)
+
+
+def _q(lib, p, x=FAKE, xp=FAKE, codes=FAKE, tags=FAKE, hist=None):
+    L = lib.load()
+    return L.dstar_fmdq_quantize(ctypes.byref(p) if p is not None else None, x, xp, codes, tags, hist, 0)
+
+
+def _l(lib, p, N=64, codes=FAKE, perm=FAKE, off=FAKE, w=FAKE, ws=FAKE, y0=FAKE, y1=FAKE, dbg=None,
+       lo=0, hi=0):
+    L = lib.load()
+    return L.dstar_fmdq_linear(ctypes.byref(p), N, codes, perm, off, w, ws, y0, y1, dbg, lo, hi, 0)
+
+
+@pytest.mark.parametrize("field,value", [
+    ("K", 0), ("K", 65536), ("token_tile", 8), ("token_tile", 48), ("rows", -1),
+    ("base", 0.0), ("base", -1.0), ("base", float("nan")), ("base", float("inf")),
+    ("base", 2.0 ** -110), ("thr0_log2", 0), ("thr0_log2", 16), ("tokens_per_seq", 0)])
+def test_invalid_params_rejected(lib, field, value):
+    p = lib.make_params(256, 64, 32, 0.05, 2)
+    setattr(p, field, value)
+    assert _q(lib, p) == lib.EINVAL
+    assert lib.load().dstar_fmdq_last_error().decode()
+    L = lib.load()
+    assert L.dstar_fmdq_bucket(ctypes.byref(p), FAKE, FAKE, FAKE, 0) == lib.EINVAL
+    assert _l(lib, p) == lib.EINVAL
+
+
+def test_sequences_must_tile_evenly(lib):
+    p = lib.make_params(2 * 100, 64, 32, 0.05, 2, tokens_per_seq=100)   # 100 % 32 != 0
+    assert _q(lib, p) == lib.EINVAL
+    p = lib.make_params(250, 64, 32, 0.05, 2, tokens_per_seq=128)       # not a multiple
+    assert _q(lib, p) == lib.EINVAL
+
+
+def test_null_and_alignment_errors(lib):
+    L = lib.load()
+    assert L.dstar_fmdq_quantize(None, FAKE, FAKE, FAKE, FAKE, None, 0) == lib.ENULL
+    p = lib.make_params(64, 64, 32, 0.05, 2)
+    assert _q(lib, p, x=None) == lib.ENULL
+    assert _q(lib, p, tags=None) == lib.ENULL
+    assert _q(lib, p, x=FAKE + 4) == lib.EALIGN
+    assert _q(lib, p, codes=FAKE + 8) == lib.EALIGN
+    assert _q(lib, p, hist=FAKE + 2) == lib.EALIGN
+    assert L.dstar_fmdq_bucket(ctypes.byref(p), FAKE, None, FAKE, 0) == lib.ENULL
+    assert L.dstar_fmdq_bucket(ctypes.byref(p), FAKE, FAKE + 1, FAKE, 0) == lib.EALIGN
+    assert _l(lib, p, w=None) == lib.ENULL
+    assert _l(lib, p, y1=FAKE + 4) == lib.EALIGN
+    assert _l(lib, p, w=FAKE + 8) == lib.EALIGN
+    assert _l(lib, p, N=66) == lib.EINVAL
+    assert _l(lib, p, N=0) == lib.EINVAL
+    assert _l(lib, p, dbg=FAKE, lo=1, hi=1) == lib.EINVAL
+    assert _l(lib, p, dbg=FAKE, lo=0, hi=3) == lib.EINVAL    # 64 rows / 32 = 2 tiles
+    assert "debug tile range" in L.dstar_fmdq_last_error().decode()
+
+
+def test_empty_input_is_a_no_op(lib):
+    p = lib.make_params(0, 64, 32, 0.05, 2, tokens_per_seq=1)
+    assert _q(lib, p, x=None, xp=None, codes=None, tags=None) == lib.OK
+    L = lib.load()
+    assert L.dstar_fmdq_bucket(ctypes.byref(p), None, None, None, 0) == lib.OK
+    assert _l(lib, p, codes=None, perm=None, off=None, w=None, ws=None, y0=None, y1=None) == lib.OK
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    from differential_mixed_precision_amd import _binding
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(_binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        _binding.load()

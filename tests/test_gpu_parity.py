@@ -1,0 +1,228 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Integer stages (codes, tags, bit histogram, bucket order, group offsets and the
+int32 group accumulators) must match bit for bit; Y_t must satisfy
+|y_gpu − y_oracle| ≤ 1e-5 · (|Y_{t−1}| + |Y_t − Y_{t−1}|) elementwise (the
+float32 combine tolerance), and the number of bit-identical outputs is
+reported.  Inputs come from the seeded generators in ``gen/``.
+"""
+import sys
+import time
+
+import numpy as np
+import pytest
+
+from gen import workloads as wl
+from oracle import fmdq
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 1e-5
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dm():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import differential_mixed_precision_amd as dm
+    dm.load()
+    return dm
+
+
+def gpu_layer(dm, d, dbg=None, inplace=False, y_prev_np=None):
+    """Runs the three stages on cuda:0; every output buffer starts as garbage."""
+    import torch
+    dev = torch.device("cuda:0")
+    rows, K, N, T = d["rows"], d["K"], d["N"], d["token_tile"]
+    nt = (rows + T - 1) // T
+    x_t = torch.from_numpy(d["x_t"]).to(dev)
+    x_p = torch.from_numpy(d["x_prev"]).to(dev)
+    w = torch.from_numpy(d["w"]).to(dev)
+    ws = torch.from_numpy(d["w_scale"]).to(dev)
+    y0 = torch.from_numpy(d["y_prev"] if y_prev_np is None else y_prev_np).to(dev)
+    p = dm.make_params(rows, K, T, float(d["base"]), d["k0"], d["tokens_per_seq"])
+    codes = torch.full((nt, K, T), 90, dtype=torch.int8, device=dev)
+    tags = torch.full((nt, K), 0xEE, dtype=torch.uint8, device=dev)
+    hist = torch.zeros(4, dtype=torch.int32, device=dev)
+    perm = torch.full((nt, K), -1, dtype=torch.int16, device=dev)
+    off = torch.full((nt, 17), -7, dtype=torch.int32, device=dev)
+    y1 = y0 if inplace else torch.full((rows, N), float("nan"), dtype=torch.float32, device=dev)
+    acc = None
+    lo, hi = (0, 0) if dbg is None else dbg
+    if dbg is not None:
+        acc = torch.full((hi - lo, 16, T, N), 0x7777, dtype=torch.int32, device=dev)
+    dm.quantize(p, x_t, x_p, codes, tags, hist)
+    dm.bucket(p, tags, perm, off)
+    dm.linear(p, N, codes, perm, off, w, ws, y0, y1, acc, lo, hi)
+    torch.cuda.synchronize()
+    out = dict(codes=codes.cpu().numpy(), tags=tags.cpu().numpy(), hist=hist.cpu().numpy(),
+               perm=perm.cpu().numpy().view(np.uint16), group_off=off.cpu().numpy(),
+               y=y1.cpu().numpy())
+    if acc is not None:
+        out["acc"] = acc.cpu().numpy()
+    return out
+
+
+def check_y(y_gpu, y_orc, y_prev, what=""):
+    y_gpu = y_gpu.astype(np.float64)
+    y_orc = y_orc.astype(np.float64)
+    y_prev = y_prev.astype(np.float64)
+    assert np.isfinite(y_gpu).all(), f"{what}: non-finite output"
+    den = np.abs(y_prev) + np.abs(y_orc - y_prev)
+    err = np.abs(y_gpu - y_orc)
+    rel = np.where(den > 0, err / np.where(den > 0, den, 1.0), np.where(err > 0, np.inf, 0.0))
+    exact = int((y_gpu == y_orc).sum())
+    log(f"  {what}: max rel err {rel.max():.3e}, bit-identical {exact}/{y_gpu.size}")
+    assert rel.max() <= REL_TOL, f"{what}: max rel err {rel.max()}"
+
+
+def check_integer_stages(g, codes, tags, hist, perm, off, what=""):
+    np.testing.assert_array_equal(g["codes"], codes, err_msg=f"{what}: codes")
+    np.testing.assert_array_equal(g["tags"], tags, err_msg=f"{what}: tags")
+    np.testing.assert_array_equal(g["hist"].astype(np.int64), hist, err_msg=f"{what}: bit histogram")
+    np.testing.assert_array_equal(g["perm"], perm, err_msg=f"{what}: bucket order")
+    np.testing.assert_array_equal(g["group_off"], off, err_msg=f"{what}: group offsets")
+
+
+def full_compare(dm, d, inplace=False):
+    rows, T = d["rows"], d["token_tile"]
+    nt = (rows + T - 1) // T
+    log(f"case {d['name']} rows={rows} K={d['K']} N={d['N']} T={T} inplace={inplace}")
+    g = gpu_layer(dm, d, dbg=(0, nt), inplace=inplace)
+    codes, tags, hist = fmdq.quantize(d["x_t"], d["x_prev"], T, d["base"], d["k0"])
+    perm, off = fmdq.bucket(tags)
+    check_integer_stages(g, codes, tags, hist, perm, off, d["name"])
+    y, accs = fmdq.linear(codes, tags, perm, off, d["w"], d["w_scale"], d["y_prev"], d["base"], T,
+                          return_acc=True)
+    for tau in range(nt):
+        np.testing.assert_array_equal(g["acc"][tau].astype(np.int64), accs[tau],
+                                      err_msg=f"{d['name']}: group accumulators of tile {tau}")
+    check_y(g["y"], y, d["y_prev"], d["name"])
+    return g, y
+
+
+SMALL = [
+    dict(rows=96, K=64, N=64, T=32, seed=1),
+    dict(rows=70, K=48, N=40, T=32, seed=2),                       # ragged last tile
+    dict(rows=128, K=36, N=36, T=64, seed=3),
+    dict(rows=40, K=33, N=20, T=16, seed=4),                       # odd K
+    dict(rows=200, K=130, N=24, T=32, seed=5),                     # K % 4 == 2
+    dict(rows=256, K=300, N=520, T=32, seed=6, heavy=0.3),
+    dict(rows=160, K=96, N=132, T=32, seed=7, heavy=0.5, c_range=(0.01, 3000.0)),  # many groups
+    dict(rows=128, K=64, N=48, T=32, seed=8, tokens_per_seq=64),   # batch of two sequences
+    dict(rows=300, K=1152, N=256, T=64, seed=9),                   # ragged T=64
+    dict(rows=33, K=2048, N=128, T=32, seed=10, heavy=0.1),        # one row in the last tile
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c['rows']}x{c['K']}x{c['N']}-T{c['T']}-s{c['seed']}")
+def test_small_layers_match_oracle(dm, case):
+    c = dict(case)
+    d = wl.make_custom(c.pop("rows"), c.pop("K"), c.pop("N"), c.pop("T"), c.pop("seed"), **c)
+    full_compare(dm, d)
+
+
+def test_zero_delta_gives_cached_output_bit_exact(dm):
+    d = wl.make_custom(96, 64, 40, 32, seed=12, zero_delta=True)
+    g, y = full_compare(dm, d)
+    np.testing.assert_array_equal(g["y"], d["y_prev"])
+
+
+def test_in_place_update(dm):
+    d = wl.make_custom(130, 80, 36, 32, seed=13, heavy=0.2)
+    full_compare(dm, d, inplace=True)
+
+
+def test_saturated_and_extreme_subchannels(dm):
+    rng = np.random.default_rng(14)
+    rows, K, N, T = 64, 40, 16, 32
+    base = np.float32(0.01)
+    x_prev = rng.standard_normal((rows, K)).astype(np.float32)
+    delta = rng.standard_normal((rows, K)) * 0.01
+    delta[3, 1] = base * 2.0 ** 23            # beyond base·2^21: PoT 21, clipped codes
+    delta[40, 2] = -base * 2.0 ** 21          # exactly at the last bin edge
+    delta[41, 3] = base * 2.0 ** 12
+    delta[:, 5] = 0.0                          # all-zero sub-channels
+    delta[7, 6] = base                         # exactly base: PoT 0
+    x_t = (x_prev.astype(np.float64) + delta).astype(np.float32)
+    d = dict(x_t=x_t, x_prev=x_prev, w=rng.integers(-127, 128, (K, N)).astype(np.int8),
+             w_scale=rng.uniform(1e-3, 1e-2, N).astype(np.float32),
+             y_prev=rng.standard_normal((rows, N)).astype(np.float32), base=base, k0=2,
+             token_tile=T, rows=rows, tokens_per_seq=rows, K=K, N=N, name="extreme")
+    for k0 in (1, 2, 6, 15):
+        d["k0"] = k0
+        d["name"] = f"extreme-k0={k0}"
+        full_compare(dm, d)
+
+
+def test_config0_full(dm):
+    d = wl.make_inputs(0, "fc1", 1)
+    t = time.time()
+    full_compare(dm, d)
+    log(f"  config 0 done in {time.time() - t:.1f}s")
+
+
+def test_determinism(dm):
+    d = wl.make_custom(512, 1152, 640, 32, seed=15, heavy=0.05)
+    a = gpu_layer(dm, d, dbg=(0, 16))
+    b = gpu_layer(dm, d, dbg=(0, 16))
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_timestep_chain_in_place(dm):
+    """Three consecutive pairs of config 1's random walk on its first 96 rows,
+    each implementation chaining its own cached output."""
+    import torch
+    y_orc = None
+    y_gpu = None
+    for pair in (1, 2, 3):
+        d = wl.make_inputs(1, "fc1", pair, rows=96)
+        d["tokens_per_seq"] = 96
+        if y_orc is None:
+            y_orc = d["y_prev"].copy()
+            y_gpu = d["y_prev"].copy()
+        r = fmdq.layer(d["x_t"], d["x_prev"], d["w"], d["w_scale"], y_orc, d["base"],
+                       d["token_tile"], d["k0"])
+        g = gpu_layer(dm, d, inplace=True, y_prev_np=y_gpu)
+        check_y(g["y"], r["y"], y_orc, f"chain pair {pair}")
+        y_orc, y_gpu = r["y"], g["y"]
+
+
+FULL = [(1, "fc1"), (1, "fc2"), (2, "qkv"), (2, "fc1"), (2, "fc2"), (3, "fc1"), (3, "fc2"),
+        (4, "fc1"), (4, "fc2")]
+
+
+@pytest.mark.parametrize("cfg,layer", FULL, ids=lambda v: str(v))
+def test_full_size_workloads(dm, cfg, layer):
+    """Full-size workload, pair 1: all integer stages compared in full; Y and
+    the group accumulators on sampled token tiles (first, second, middle,
+    last — ragged where the workload has one — and two seeded random tiles)."""
+    t0 = time.time()
+    d = wl.make_inputs(cfg, layer, 1)
+    rows, T = d["rows"], d["token_tile"]
+    nt = (rows + T - 1) // T
+    rng = np.random.default_rng(100 + cfg)
+    sample = sorted(set([0, 1, nt // 2, nt - 2, nt - 1] + [int(v) for v in rng.integers(0, nt, 2)]))
+    log(f"case config {cfg} {layer}: rows={rows} K={d['K']} N={d['N']} T={T} tiles={nt} "
+        f"sampled tiles {sample} (inputs {time.time() - t0:.1f}s)")
+    g = gpu_layer(dm, d, dbg=(nt - 2, nt))
+    log(f"  gpu done {time.time() - t0:.1f}s")
+    codes, tags, hist = fmdq.quantize(d["x_t"], d["x_prev"], T, d["base"], d["k0"])
+    perm, off = fmdq.bucket(tags)
+    log(f"  oracle quantize+bucket done {time.time() - t0:.1f}s")
+    check_integer_stages(g, codes, tags, hist, perm, off, d["name"])
+    y, accs = fmdq.linear(codes, tags, perm, off, d["w"], d["w_scale"], d["y_prev"], d["base"], T,
+                          tiles=sample, return_acc=True)
+    for tau in (nt - 2, nt - 1):
+        np.testing.assert_array_equal(g["acc"][tau - (nt - 2)].astype(np.int64), accs[tau],
+                                      err_msg=f"group accumulators of tile {tau}")
+    rows_s = np.concatenate([np.arange(tau * T, min(rows, tau * T + T)) for tau in sample])
+    check_y(g["y"][rows_s], y[rows_s], d["y_prev"][rows_s], d["name"])
+    log(f"  done {time.time() - t0:.1f}s")
