@@ -1,0 +1,240 @@
+"""Benchmark of the FMDQ differential linear on one MI355X.
+
+A step is one timestep pair through both MLP linears of the PixArt-alpha-style
+1024px workload (tokens 2 x 4096, fc1 1152->4608 and fc2 4608->1152, token
+tile 32): for each layer the three stages quantize -> bucket -> linear, with
+the cached output Y updated in place.  Inputs of a few consecutive pairs of
+the seeded random walk are made resident in HBM before timing and cycled.
+
+Prints one JSON line: whole-step dense-equivalent int8 TOPS (2*M*N*K per layer
+over the measured time), per-stage times from HIP events on the launch
+stream, the roofline of the dominant kernel, and the CPU oracle timed on the
+host as a baseline.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 1] [--pairs 2]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FMDQ differential linear: ms/layer, dense-equiv int8 TOPS, % MFMA & HBM peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
+STAGES = ("quantize", "bucket", "linear")
+KERNEL_SRC = {"quantize": "fmdq_quantize.hip", "bucket": "fmdq_bucket.hip",
+              "linear": "fmdq_linear.hip"}
+
+
+def algorithmic(stage: str, rows: int, K: int, N: int, T: int) -> dict:
+    """Compulsory HBM bytes (and int8 ops) of one launch of a stage."""
+    nt = (rows + T - 1) // T
+    codes = nt * T * K
+    if stage == "quantize":
+        return dict(bytes=8 * rows * K + codes + nt * K + 16, ops=0)
+    if stage == "bucket":
+        return dict(bytes=nt * K + 2 * nt * K + 68 * nt, ops=0)
+    return dict(bytes=codes + 2 * nt * K + 68 * nt + K * N + 4 * N + 8 * rows * N,
+                ops=2 * rows * N * K)
+
+
+def src_sha(stage: str) -> str:
+    path = os.path.join(ROOT, "differential_mixed_precision_amd", "csrc", KERNEL_SRC[stage])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(stage: str, layer: str, cfg: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    if there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tab = json.load(f)
+    e = tab.get(f"{stage}@c{cfg}-{layer}")
+    if not e or e.get("src_sha") != src_sha(stage):
+        return None
+    return e["bytes_per_launch"]
+
+
+def cpu_baseline(ins: list[dict]) -> dict:
+    """The oracle (untuned) on the host: one full step (pair 1, both layers)."""
+    from threadpoolctl import threadpool_info
+    from oracle import fmdq
+    t0 = time.perf_counter()
+    ops = 0
+    for d in ins:
+        fmdq.layer(d["x_t"], d["x_prev"], d["w"], d["w_scale"], d["y_prev"], d["base"],
+                   d["token_tile"], d["k0"])
+        ops += 2 * d["rows"] * d["N"] * d["K"]
+    dt = time.perf_counter() - t0
+    threads = max([i["num_threads"] for i in threadpool_info()] or [1])
+    return {"value": ops / dt / 1e12, "unit": "TOPS (dense-equiv int8)", "cores": threads,
+            "kind": "oracle", "seconds": dt,
+            "sample": f"one full step: pair 1, {ins[0]['rows']} rows, layers "
+                      f"{'+'.join(d['name'].split('/')[-1] for d in ins)}; numpy float64 "
+                      f"matmuls per tile and FPoT group"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--pairs", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the layer shards by token tiles with no "
+              f"inter-GPU exchange); --gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+
+    import torch
+    import differential_mixed_precision_amd as dm
+    from gen import workloads as wl
+
+    if not os.path.exists(dm._binding.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    dm.load()
+    dev = torch.device("cuda:0")
+    spec = wl.CONFIGS[args.config]
+    layers = list(spec["layers"])
+    print(f"[bench] generating config {args.config} ({spec['name']}) pairs 1..{args.pairs}",
+          file=sys.stderr, flush=True)
+    host = {L: [wl.make_inputs(args.config, L, p) for p in range(1, args.pairs + 1)] for L in layers}
+    rows, T = spec["rows"], spec["token_tile"]
+
+    # resident device state
+    state = {}
+    for L in layers:
+        d0 = host[L][0]
+        w = torch.from_numpy(d0["w"]).to(dev)
+        ws = torch.from_numpy(d0["w_scale"]).to(dev)
+        layer = dm.FmdqLayer(w, ws, rows, T, float(d0["base"]), d0["k0"], d0["tokens_per_seq"])
+        xs = [(torch.from_numpy(d["x_t"]).to(dev), torch.from_numpy(d["x_prev"]).to(dev))
+              for d in host[L]]
+        y = torch.from_numpy(d0["y_prev"]).to(dev)
+        state[L] = dict(layer=layer, xs=xs, y=y, K=d0["K"], N=d0["N"])
+    # a plain copy of known size (counter calibration for rocprofv3 --pmc runs)
+    cal_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(i, events=None):
+        for L in layers:
+            s = state[L]
+            lay = s["layer"]
+            x_t, x_p = s["xs"][i % len(s["xs"])]
+            ev = events[L] if events is not None else None
+            if ev is not None:
+                ev[0].record(stream)
+            dm.quantize(lay.p, x_t, x_p, lay.codes, lay.tags, lay.bit_hist)
+            if ev is not None:
+                ev[1].record(stream)
+            dm.bucket(lay.p, lay.tags, lay.perm, lay.group_off)
+            if ev is not None:
+                ev[2].record(stream)
+            dm.linear(lay.p, s["N"], lay.codes, lay.perm, lay.group_off, lay.w, lay.w_scale,
+                      s["y"], s["y"])
+            if ev is not None:
+                ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    for L in layers:
+        state[L]["layer"].bit_hist.zero_()
+    events = [{L: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for L in layers}
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {L: {s: [] for s in STAGES} for L in layers}
+    for i in range(args.steps):
+        for L in layers:
+            ev = events[i][L]
+            for j, s in enumerate(STAGES):
+                per[L][s].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)   # microseconds
+    ms_per_step = wall * 1e3 / args.steps
+    total_ops = sum(2 * rows * state[L]["N"] * state[L]["K"] for L in layers)
+    value = total_ops / (ms_per_step * 1e-3) / 1e12
+
+    kernels = {}
+    layer_out = {}
+    for L in layers:
+        K, N = state[L]["K"], state[L]["N"]
+        hist = state[L]["layer"].bit_hist.cpu().numpy().astype(np.int64) / max(args.steps, 1)
+        lay_us = 0.0
+        for s in STAGES:
+            us = float(np.mean(per[L][s]))
+            lay_us += us
+            alg = algorithmic(s, rows, K, N, T)
+            gbs = alg["bytes"] / (us * 1e-6) / 1e9
+            tops = alg["ops"] / (us * 1e-6) / 1e12 if alg["ops"] else 0.0
+            t_hbm = alg["bytes"] / (HBM_PEAK_GBS * 1e9)
+            t_mfma = alg["ops"] / (INT8_PEAK_TOPS * 1e12) if alg["ops"] else 0.0
+            bound = "mfma" if t_mfma > t_hbm else "hbm"
+            traffic = measured_traffic(s, L, args.config)
+            kernels[f"{s}@{L}"] = dict(
+                us_mean=us, us_p10=float(np.percentile(per[L][s], 10)),
+                us_p90=float(np.percentile(per[L][s], 90)), alg_bytes=alg["bytes"],
+                alg_ops=alg["ops"], gbs=gbs, tops=tops, bound=bound,
+                frac=(tops / INT8_PEAK_TOPS) if bound == "mfma" else gbs / HBM_PEAK_GBS,
+                traffic=traffic)
+        avg_bits = float((hist * np.array([2, 4, 6, 8])).sum() / max(hist.sum(), 1))
+        layer_out[L] = dict(K=K, N=N, us=lay_us, ms=lay_us / 1e3,
+                            tops=2 * rows * N * K / (lay_us * 1e-6) / 1e12,
+                            bits_hist_subchannels=[float(v) for v in hist], avg_bits=avg_bits)
+    dom = max(kernels, key=lambda k: kernels[k]["us_mean"])
+    kd = kernels[dom]
+    if kd["bound"] == "mfma":
+        roof = dict(bound="mfma", achieved=kd["tops"], peak=INT8_PEAK_TOPS, unit="TOP/s",
+                    frac=kd["tops"] / INT8_PEAK_TOPS)
+    else:
+        roof = dict(bound="hbm", achieved=kd["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=kd["gbs"] / HBM_PEAK_GBS)
+    roof["traffic"] = kd["traffic"]
+    roof["kernel"] = dom
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "TOPS (dense-equiv int8)", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic (seeded random walk of DiT-like activations; random int8 weights)",
+        "config": {"workload": f"config {args.config}: {spec['name']}, rows {rows}, "
+                               f"token tile {T}, layers " +
+                               ", ".join(f"{L} {state[L]['K']}->{state[L]['N']}" for L in layers),
+                   "rows": rows, "token_tile": T, "thr0_log2": wl.DEFAULT_K0,
+                   "pairs_cycled": args.pairs},
+        "layers": layer_out, "kernels": kernels, "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on one step", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline([host[L][0] for L in layers])
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
