@@ -77,8 +77,9 @@ int dstar_fmdq_quantize(const dstar_fmdq_params* p, const float* x_t, const floa
   if (p->rows == 0) return DSTAR_OK;
   if (!x_t || !x_prev || !codes || !tags)
     return set_error(DSTAR_ENULL, "quantize: x_t, x_prev, codes and tags must not be NULL");
-  if (!aligned(x_t, 16) || !aligned(x_prev, 16) || !aligned(codes, 16))
-    return set_error(DSTAR_EALIGN, "quantize: x_t, x_prev and codes must be 16-byte aligned");
+  if (!aligned(x_t, 16) || !aligned(x_prev, 16) || !aligned(codes, 16) || !aligned(tags, 4))
+    return set_error(DSTAR_EALIGN,
+                     "quantize: x_t, x_prev and codes must be 16-byte aligned, tags 4-byte aligned");
   if (bit_hist && !aligned(bit_hist, 4))
     return set_error(DSTAR_EALIGN, "quantize: bit_hist must be 4-byte aligned");
   QuantizeArgs a;

@@ -87,7 +87,7 @@ typedef struct {
  *   codes        [n_t][K][T] int8 (out): code of row τT+t, channel k at
  *                codes[(τK + k)T + t]; rows past the end of a ragged last tile
  *                are written 0.  16-byte aligned.
- *   tags         [n_t][K] uint8 (out): bits 0-3 the FPoT tag g = (b-2) - PoT +
+ *   tags         [n_t][K] uint8 (out), 4-byte aligned: bits 0-3 the FPoT tag g = (b-2) - PoT +
  *                15 (ascending g = ascending FPoT; the sub-channel's step is
  *                base * 2^(15-g)), bits 4-5 the precision code b/2 - 1.
  *   bit_hist     uint32[4] or NULL: counts of sub-channels quantized at

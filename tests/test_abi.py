@@ -101,6 +101,7 @@ def test_null_and_alignment_errors(lib):
     assert _q(lib, p, x=FAKE + 4) == lib.EALIGN
     assert _q(lib, p, codes=FAKE + 8) == lib.EALIGN
     assert _q(lib, p, hist=FAKE + 2) == lib.EALIGN
+    assert _q(lib, p, tags=FAKE + 2) == lib.EALIGN
     assert L.dstar_fmdq_bucket(ctypes.byref(p), FAKE, None, FAKE, 0) == lib.ENULL
     assert L.dstar_fmdq_bucket(ctypes.byref(p), FAKE, FAKE + 1, FAKE, 0) == lib.EALIGN
     assert _l(lib, p, w=None) == lib.ENULL
