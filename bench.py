@@ -150,7 +150,7 @@ def main() -> int:
             dm.bucket(lay.p, lay.tags, lay.perm, lay.group_off)
             if ev is not None:
                 ev[2].record(stream)
-            dm.linear(lay.p, s["N"], lay.codes, lay.perm, lay.group_off, lay.w, lay.w_scale,
+            dm.linear(lay.p, s["N"], lay.codes, lay.tags, lay.perm, lay.group_off, lay.w, lay.w_scale,
                       s["y"], s["y"])
             if ev is not None:
                 ev[3].record(stream)

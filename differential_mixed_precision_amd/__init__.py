@@ -49,6 +49,6 @@ class FmdqLayer:
                  self.bit_hist if hist else None, stream)
         bucket(self.p, self.tags, self.perm, self.group_off, stream)
         out = y if y_out is None else y_out
-        linear(self.p, self.N, self.codes, self.perm, self.group_off, self.w, self.w_scale,
+        linear(self.p, self.N, self.codes, self.tags, self.perm, self.group_off, self.w, self.w_scale,
                y, out, stream=stream)
         return out

@@ -19,7 +19,7 @@ TAG_OFFSET = 15
 POT_MAX = 21
 PREC_SHIFT = 4
 MAX_K = 65535
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 SYMBOLS = ("dstar_fmdq_quantize", "dstar_fmdq_bucket", "dstar_fmdq_linear",
            "dstar_fmdq_last_error", "dstar_fmdq_abi_version")
@@ -58,7 +58,7 @@ def load() -> ctypes.CDLL:
     lib.dstar_fmdq_quantize.restype = ctypes.c_int
     lib.dstar_fmdq_bucket.argtypes = [P, vp, vp, vp, vp]
     lib.dstar_fmdq_bucket.restype = ctypes.c_int
-    lib.dstar_fmdq_linear.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
+    lib.dstar_fmdq_linear.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
     lib.dstar_fmdq_linear.restype = ctypes.c_int
     lib.dstar_fmdq_last_error.argtypes = []
     lib.dstar_fmdq_last_error.restype = ctypes.c_char_p
@@ -110,10 +110,10 @@ def bucket(p: Params, tags, perm, group_off, stream=None) -> None:
                                     _stream(stream)))
 
 
-def linear(p: Params, N: int, codes, perm, group_off, w, w_scale, y_prev, y_out,
+def linear(p: Params, N: int, codes, tags, perm, group_off, w, w_scale, y_prev, y_out,
            acc_dbg=None, dbg_tile_lo: int = 0, dbg_tile_hi: int = 0, stream=None) -> None:
     """dstar_fmdq_linear."""
-    _check(load().dstar_fmdq_linear(ctypes.byref(p), int(N), _ptr(codes), _ptr(perm),
+    _check(load().dstar_fmdq_linear(ctypes.byref(p), int(N), _ptr(codes), _ptr(tags), _ptr(perm),
                                     _ptr(group_off), _ptr(w), _ptr(w_scale), _ptr(y_prev),
                                     _ptr(y_out), _ptr(acc_dbg), int(dbg_tile_lo),
                                     int(dbg_tile_hi), _stream(stream)))

@@ -8,8 +8,6 @@
 
 namespace dstar {
 
-int launch_linear_general(const LinearArgs& a, hipStream_t s);
-
 namespace {
 thread_local std::string g_error;
 
@@ -117,7 +115,7 @@ int dstar_fmdq_bucket(const dstar_fmdq_params* p, const uint8_t* tags, uint16_t*
 }
 
 int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N, const int8_t* codes,
-                      const uint16_t* perm, const int32_t* group_off, const int8_t* w,
+                      const uint8_t* tags, const uint16_t* perm, const int32_t* group_off, const int8_t* w,
                       const float* w_scale, const float* y_prev, float* y_out, int32_t* acc_dbg,
                       int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream) {
   clear_error();
@@ -129,16 +127,18 @@ int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N, const int8_t* codes
     return set_error(DSTAR_EINVAL, "linear: debug tile range [%d, %d) not within [0, %lld)",
                      dbg_tile_lo, dbg_tile_hi, (long long)nt);
   if (nt == 0) return DSTAR_OK;
-  if (!codes || !perm || !group_off || !w || !w_scale || !y_prev || !y_out)
-    return set_error(DSTAR_ENULL, "linear: codes, perm, group_off, w, w_scale, y_prev and y_out must not be NULL");
+  if (!codes || !tags || !perm || !group_off || !w || !w_scale || !y_prev || !y_out)
+    return set_error(DSTAR_ENULL,
+                     "linear: codes, tags, perm, group_off, w, w_scale, y_prev and y_out must not be NULL");
   if (!aligned(codes, 16) || !aligned(w, 16) || !aligned(y_prev, 16) || !aligned(y_out, 16) ||
-      !aligned(w_scale, 4) || !aligned(perm, 2) || !aligned(group_off, 4) ||
+      !aligned(tags, 4) || !aligned(w_scale, 4) || !aligned(perm, 2) || !aligned(group_off, 4) ||
       (acc_dbg && !aligned(acc_dbg, 4)))
     return set_error(DSTAR_EALIGN,
-                     "linear: codes, w, y_prev, y_out must be 16-byte aligned (w_scale, "
+                     "linear: codes, w, y_prev, y_out must be 16-byte aligned (tags, w_scale, "
                      "group_off, acc_dbg 4-byte, perm 2-byte)");
   LinearArgs a;
   a.codes = codes;
+  a.tags = tags;
   a.perm = perm;
   a.group_off = group_off;
   a.w = w;

@@ -15,7 +15,7 @@ void clear_error();
 // Checks hipGetLastError() after a launch; returns DSTAR_OK or DSTAR_EHIP.
 int check_launch(const char* what);
 
-inline int64_t n_tiles(int64_t rows, int64_t T) { return (rows + T - 1) / T; }
+__host__ __device__ inline int64_t n_tiles(int64_t rows, int64_t T) { return (rows + T - 1) / T; }
 
 // Validated launch descriptions (sizes already checked by the API layer).
 struct QuantizeArgs {
@@ -44,6 +44,7 @@ int launch_bucket(const BucketArgs& a, hipStream_t s);
 
 struct LinearArgs {
   const int8_t* codes;
+  const uint8_t* tags;
   const uint16_t* perm;
   const int32_t* group_off;
   const int8_t* w;
@@ -60,5 +61,8 @@ struct LinearArgs {
   double base;
 };
 int launch_linear(const LinearArgs& a, hipStream_t s);
+int launch_linear_general(const LinearArgs& a, hipStream_t s);
+bool linear_mfma_supported(const LinearArgs& a);
+int launch_linear_mfma(const LinearArgs& a, hipStream_t s);
 
 }  // namespace dstar

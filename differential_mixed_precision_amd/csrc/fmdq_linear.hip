@@ -1,10 +1,13 @@
-// Stage 3 dispatch.
+// Stage 3 dispatch: the MFMA kernel for token tiles of 32 or 64 rows (K a
+// multiple of 4); the general kernel for other shapes and whenever the group
+// accumulators are dumped.
 #include "fmdq_internal.h"
 
 namespace dstar {
 
-int launch_linear_general(const LinearArgs& a, hipStream_t s);
-
-int launch_linear(const LinearArgs& a, hipStream_t s) { return launch_linear_general(a, s); }
+int launch_linear(const LinearArgs& a, hipStream_t s) {
+  if (a.acc_dbg == nullptr && linear_mfma_supported(a)) return launch_linear_mfma(a, s);
+  return launch_linear_general(a, s);
+}
 
 }  // namespace dstar

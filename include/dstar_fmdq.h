@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DSTAR_FMDQ_ABI_VERSION 1
+#define DSTAR_FMDQ_ABI_VERSION 2
 
 /* Rule constants (DSTAR §3.1 step 1; readings in the design notes):
  * PCeil of a b-bit sub-channel is 2^(b-2); PoT is capped at POT_MAX so that
@@ -112,11 +112,13 @@ int dstar_fmdq_bucket(const dstar_fmdq_params* p, const uint8_t* tags,
                       uint16_t* perm, int32_t* group_off, void* stream);
 
 /* Stage 3 — grouped int8 GEMM, shift alignment, dequantization and reverse
- * differential (DSTAR §3.1 step 5, Fig. 6; §4.2 MPU, inverse quantization and
- * accumulation units; §4.3 reverse differential fused into the GEMM).
+ * differential (DSTAR §3.1 steps 3 and 5, Fig. 6; §4.2 MPU, inverse
+ * quantization and accumulation units; §4.3 reverse differential fused into
+ * the GEMM).
  *   N          output channels, a multiple of 4 in [4, 2^20].
- *   codes      from stage 1; perm, group_off from stage 2.  Channel k of
- *              group g of tile τ is multiplied at step 2^(15-g) * base.
+ *   codes      from stage 1; tags from stage 1 (4-byte aligned); perm,
+ *              group_off from stage 2.  Channel k of group g of tile τ is
+ *              multiplied at step 2^(15-g) * base.
  *   w          [K][N] int8 row-major, 16-byte aligned.
  *   w_scale    [N] float32, per-output-channel weight scale.
  *   y_prev     [rows][N] float32, the cached output Y_{t-1}.
@@ -126,11 +128,15 @@ int dstar_fmdq_bucket(const dstar_fmdq_params* p, const uint8_t* tags,
  *              group accumulators acc_g[t][n] = Σ over channels k of group g
  *              of code(τT+t, k) * w[k][n] for tiles τ in [dbg_tile_lo,
  *              dbg_tile_hi); groups absent from a tile and rows past a ragged
- *              end are written 0.  Needs 0 <= lo < hi <= n_t.
- * Per output: S = Σ_g acc_g * 2^(15-g) (int64, exact);
- * y_out = fl32(f64(y_prev) + (f64(S) * f64(base)) * f64(w_scale[n])). */
+ *              end are written 0.  Needs 0 <= lo < hi <= n_t.  With acc_dbg
+ *              the layer runs in the per-group kernel (slow; for checking).
+ * Per output: S = Σ_g acc_g * 2^(15-g) (an exact integer);
+ * y_out = fl32(f64(y_prev) + (f64(S) * f64(base)) * f64(w_scale[n])).
+ * perm and group_off are read only for token tiles where the fast kernel
+ * cannot prove its int32 accumulator exact (127 * Σ_k 2^PoT_k >= 2^31) or
+ * whose channels with PoT >= 7 exceed its LDS budget; tags are read always. */
 int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N,
-                      const int8_t* codes, const uint16_t* perm,
+                      const int8_t* codes, const uint8_t* tags, const uint16_t* perm,
                       const int32_t* group_off,
                       const int8_t* w, const float* w_scale,
                       const float* y_prev, float* y_out, int32_t* acc_dbg,

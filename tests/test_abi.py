@@ -65,10 +65,10 @@ def _q(lib, p, x=FAKE, xp=FAKE, codes=FAKE, tags=FAKE, hist=None):
     return L.dstar_fmdq_quantize(ctypes.byref(p) if p is not None else None, x, xp, codes, tags, hist, 0)
 
 
-def _l(lib, p, N=64, codes=FAKE, perm=FAKE, off=FAKE, w=FAKE, ws=FAKE, y0=FAKE, y1=FAKE, dbg=None,
-       lo=0, hi=0):
+def _l(lib, p, N=64, codes=FAKE, tags=FAKE, perm=FAKE, off=FAKE, w=FAKE, ws=FAKE, y0=FAKE, y1=FAKE,
+       dbg=None, lo=0, hi=0):
     L = lib.load()
-    return L.dstar_fmdq_linear(ctypes.byref(p), N, codes, perm, off, w, ws, y0, y1, dbg, lo, hi, 0)
+    return L.dstar_fmdq_linear(ctypes.byref(p), N, codes, tags, perm, off, w, ws, y0, y1, dbg, lo, hi, 0)
 
 
 @pytest.mark.parametrize("field,value", [
@@ -105,6 +105,8 @@ def test_null_and_alignment_errors(lib):
     assert L.dstar_fmdq_bucket(ctypes.byref(p), FAKE, None, FAKE, 0) == lib.ENULL
     assert L.dstar_fmdq_bucket(ctypes.byref(p), FAKE, FAKE + 1, FAKE, 0) == lib.EALIGN
     assert _l(lib, p, w=None) == lib.ENULL
+    assert _l(lib, p, tags=None) == lib.ENULL
+    assert _l(lib, p, tags=FAKE + 2) == lib.EALIGN
     assert _l(lib, p, y1=FAKE + 4) == lib.EALIGN
     assert _l(lib, p, w=FAKE + 8) == lib.EALIGN
     assert _l(lib, p, N=66) == lib.EINVAL

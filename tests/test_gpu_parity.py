@@ -36,7 +36,12 @@ def dm():
 
 
 def gpu_layer(dm, d, dbg=None, inplace=False, y_prev_np=None):
-    """Runs the three stages on cuda:0; every output buffer starts as garbage."""
+    """Runs the three stages on cuda:0; every output buffer starts as garbage.
+
+    Stage 3 runs twice from the same codes: once as the product path (no
+    accumulator dump: the MFMA kernel where the shape allows it) -> "y", and,
+    when ``dbg`` names a tile range, once more with the group accumulators
+    dumped (the per-group kernel) -> "y_dbg" and "acc"."""
     import torch
     dev = torch.device("cuda:0")
     rows, K, N, T = d["rows"], d["K"], d["N"], d["token_tile"]
@@ -45,7 +50,8 @@ def gpu_layer(dm, d, dbg=None, inplace=False, y_prev_np=None):
     x_p = torch.from_numpy(d["x_prev"]).to(dev)
     w = torch.from_numpy(d["w"]).to(dev)
     ws = torch.from_numpy(d["w_scale"]).to(dev)
-    y0 = torch.from_numpy(d["y_prev"] if y_prev_np is None else y_prev_np).to(dev)
+    y_np = d["y_prev"] if y_prev_np is None else y_prev_np
+    y0 = torch.from_numpy(y_np).to(dev)
     p = dm.make_params(rows, K, T, float(d["base"]), d["k0"], d["tokens_per_seq"])
     codes = torch.full((nt, K, T), 90, dtype=torch.int8, device=dev)
     tags = torch.full((nt, K), 0xEE, dtype=torch.uint8, device=dev)
@@ -53,19 +59,20 @@ def gpu_layer(dm, d, dbg=None, inplace=False, y_prev_np=None):
     perm = torch.full((nt, K), -1, dtype=torch.int16, device=dev)
     off = torch.full((nt, 17), -7, dtype=torch.int32, device=dev)
     y1 = y0 if inplace else torch.full((rows, N), float("nan"), dtype=torch.float32, device=dev)
-    acc = None
-    lo, hi = (0, 0) if dbg is None else dbg
-    if dbg is not None:
-        acc = torch.full((hi - lo, 16, T, N), 0x7777, dtype=torch.int32, device=dev)
     dm.quantize(p, x_t, x_p, codes, tags, hist)
     dm.bucket(p, tags, perm, off)
-    dm.linear(p, N, codes, perm, off, w, ws, y0, y1, acc, lo, hi)
+    dm.linear(p, N, codes, tags, perm, off, w, ws, y0, y1)
+    out = dict(codes=codes, tags=tags, hist=hist, perm=perm, group_off=off, y=y1)
+    if dbg is not None:
+        lo, hi = dbg
+        acc = torch.full((hi - lo, 16, T, N), 0x7777, dtype=torch.int32, device=dev)
+        y0b = torch.from_numpy(y_np).to(dev)
+        y2 = torch.full((rows, N), float("nan"), dtype=torch.float32, device=dev)
+        dm.linear(p, N, codes, tags, perm, off, w, ws, y0b, y2, acc, lo, hi)
+        out.update(acc=acc, y_dbg=y2)
     torch.cuda.synchronize()
-    out = dict(codes=codes.cpu().numpy(), tags=tags.cpu().numpy(), hist=hist.cpu().numpy(),
-               perm=perm.cpu().numpy().view(np.uint16), group_off=off.cpu().numpy(),
-               y=y1.cpu().numpy())
-    if acc is not None:
-        out["acc"] = acc.cpu().numpy()
+    out = {k: v.cpu().numpy() for k, v in out.items()}
+    out["perm"] = out["perm"].view(np.uint16)
     return out
 
 
@@ -80,6 +87,9 @@ def check_y(y_gpu, y_orc, y_prev, what=""):
     exact = int((y_gpu == y_orc).sum())
     log(f"  {what}: max rel err {rel.max():.3e}, bit-identical {exact}/{y_gpu.size}")
     assert rel.max() <= REL_TOL, f"{what}: max rel err {rel.max()}"
+    # S is an exact integer on both sides and the float64 combine is the same
+    # sequence of correctly rounded operations, so the outputs are identical.
+    assert exact == y_gpu.size, f"{what}: {y_gpu.size - exact} outputs differ from the oracle"
 
 
 def check_integer_stages(g, codes, tags, hist, perm, off, what=""):
@@ -103,7 +113,9 @@ def full_compare(dm, d, inplace=False):
     for tau in range(nt):
         np.testing.assert_array_equal(g["acc"][tau].astype(np.int64), accs[tau],
                                       err_msg=f"{d['name']}: group accumulators of tile {tau}")
-    check_y(g["y"], y, d["y_prev"], d["name"])
+    y_prev = d["y_prev"]
+    check_y(g["y_dbg"], y, y_prev, d["name"] + " (per-group kernel)")
+    check_y(g["y"], y, y_prev, d["name"])
     return g, y
 
 
@@ -118,6 +130,12 @@ SMALL = [
     dict(rows=128, K=64, N=48, T=32, seed=8, tokens_per_seq=64),   # batch of two sequences
     dict(rows=300, K=1152, N=256, T=64, seed=9),                   # ragged T=64
     dict(rows=33, K=2048, N=128, T=32, seed=10, heavy=0.1),        # one row in the last tile
+    # every sub-channel heavy: most channels need their own FPoT groups
+    dict(rows=96, K=4096, N=96, T=32, seed=21, heavy=1.0, c_range=(4.0, 8.0)),
+    dict(rows=128, K=8192, N=64, T=64, seed=22, heavy=1.0, c_range=(4.0, 8.0)),
+    # more such channels than the MFMA kernel stages: exact per-group fallback
+    dict(rows=64, K=8192, N=72, T=32, seed=20, heavy=1.0, c_range=(4.0, 8.0)),
+    dict(rows=200, K=1536, N=260, T=32, seed=23, heavy=0.2, c_range=(0.5, 64.0)),
 ]
 
 
