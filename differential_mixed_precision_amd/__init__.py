@@ -41,7 +41,7 @@ class FmdqLayer:
         self.codes = torch.empty((nt, self.K, token_tile), dtype=torch.int8, device=dev)
         self.tags = torch.empty((nt, self.K), dtype=torch.uint8, device=dev)
         self.perm = torch.empty((nt, self.K), dtype=torch.int16, device=dev)  # uint16 ids
-        self.group_off = torch.empty((nt, 17), dtype=torch.int32, device=dev)
+        self.group_off = torch.empty((nt, 65), dtype=torch.int32, device=dev)
         self.bit_hist = torch.zeros(4, dtype=torch.int32, device=dev)
 
     def step(self, x_t, x_prev, y, y_out=None, stream=None, hist: bool = True):

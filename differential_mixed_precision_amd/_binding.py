@@ -15,11 +15,12 @@ LIB_PATH = os.path.join(_PKG, "libdstar_fmdq.so")
 
 OK, EINVAL, ENULL, EALIGN, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5
 NUM_TAGS = 16
+NUM_BINS = 64
 TAG_OFFSET = 15
 POT_MAX = 21
 PREC_SHIFT = 4
 MAX_K = 65535
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 SYMBOLS = ("dstar_fmdq_quantize", "dstar_fmdq_bucket", "dstar_fmdq_linear",
            "dstar_fmdq_last_error", "dstar_fmdq_abi_version")

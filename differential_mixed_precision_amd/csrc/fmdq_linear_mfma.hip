@@ -27,11 +27,14 @@
 //
 // Exactness.  int32 arithmetic wraps modulo 2^32, so the final accumulator
 // equals S whenever |S| < 2^31; |S| ≤ 127 · Σ_k 2^PoT_k, so a token tile is
-// handled here only if 127 · Σ_k 2^PoT_k < 2^31 and its gathered channel list
-// fits the LDS budget.  Any other tile ("ineligible") is finished by an exact
-// scalar path in the same workgroup that walks the tile's FPoT-ordered channel
-// list (perm, group_off from stage 2) group by group with int32 group sums
-// shifted into an int64 sum.
+// handled here only if 127 · Σ_k 2^PoT_k < 2^31 (computed from stage 2's bin
+// counts).  Any other tile ("ineligible") is finished by an exact scalar path
+// in the same workgroup that walks the tile's FPoT groups in perm order with
+// int32 group sums shifted into an int64 sum.
+//
+// Stage 2 orders each FPoT group widest precision first, so the channels of a
+// group with PoT ≥ 7 are a prefix of the group in perm, found from the bin
+// offsets alone; the gathered steps read perm directly.
 //
 // Layout.  Workgroup = 256 threads = 4 waves, output block 128 rows × 128
 // columns, 2 × 2 waves of 64 × 64 (2 × 2 MFMA 32x32x32 int8 tiles each).
@@ -41,8 +44,9 @@
 // [channel][column] tiles (the code shift of a channel is one shift of each
 // 16-byte piece).  Each lane then assembles its 16-byte MFMA fragment (one
 // row or column, 16 consecutive channels) with two ds_read_b64_tr_b8
-// transpose reads.  Chunks are double-buffered in LDS with one barrier per
-// chunk, and the next chunk's global loads are in flight during the MFMAs.
+// transpose reads.  LDS stages are double-buffered with one barrier per step;
+// the dense loop keeps the global loads of three chunks in flight per thread,
+// the gathered loop fetches perm entries two steps and data one step ahead.
 #include "fmdq_internal.h"
 
 namespace dstar {
@@ -57,41 +61,35 @@ constexpr int kThreads = 256;
 constexpr int BM = 128;            // rows per workgroup
 constexpr int BN = 128;            // output columns per workgroup
 constexpr int BK = 64;             // channels per dense chunk (2 MFMA k-steps)
-constexpr int KS = 32;             // channels per MFMA k-step
+constexpr int KS = 32;             // channels per MFMA k-step (= per gathered step)
 constexpr int SA = BM + 32;        // LDS bytes per channel row of an A tile
 constexpr int SB = BN + 32;        // LDS bytes per channel row of a B tile
+constexpr int kDepth = 2;          // dense chunks whose loads are in flight per thread
+constexpr int kBand = 8;           // row blocks per band of the block order
 constexpr int kTags = DSTAR_FMDQ_NUM_TAGS;
+constexpr int kBins = DSTAR_FMDQ_NUM_BINS;
 constexpr int kAlignedPotMax = 6;  // q·2^e fits int8 when PoT ≤ 6
 constexpr uint64_t kBoundLimit = 2147483647ull / 127ull;  // Σ 2^PoT limit
-constexpr int kListBytes = 32768;  // gathered channel lists per workgroup
-constexpr uint16_t kPad = 0xFFFFu;
 
 template <int T>
 struct Cfg {
-  static constexpr int kTiles = BM / T;                   // token tiles per workgroup
-  static constexpr int kCap = kListBytes / 2 / kTiles;    // list entries per tile
-  static constexpr int kMaxSteps = kCap / KS;             // gathered k-steps per tile
+  static constexpr int kTiles = BM / T;   // token tiles per workgroup
 };
 
-// LDS carve-up (bytes): two A and two B chunk buffers, then the lists.
-constexpr int kSizeA = BK * SA;                            // 10240
-constexpr int kSizeB = BK * SB;                            // 10240
-constexpr int kOffA0 = 0;
-constexpr int kOffA1 = kOffA0 + kSizeA;
-constexpr int kOffB0 = kOffA1 + kSizeA;
-constexpr int kOffB1 = kOffB0 + kSizeB;
-constexpr int kOffList = kOffB1 + kSizeB;                  // uint16 lists
-constexpr int kOffStep = kOffList + kListBytes;            // uint8 step exponents
-constexpr int kSizeStep = 4 * 128;
-constexpr int kOffCnt = kOffStep + kSizeStep;              // uint32 [4][16] counters
-constexpr int kOffCur = kOffCnt + 4 * kTags * 4;           // uint32 [4][16] cursors
-constexpr int kOffBnd = kOffCur + 4 * kTags * 4;           // uint64 [4] bounds
-constexpr int kOffMeta = kOffBnd + 4 * 8;                  // int32 [4] steps, [4] eligible
-constexpr int kLdsBytes = kOffMeta + 8 * 4;
-static_assert(Cfg<32>::kMaxSteps * 4 <= kSizeStep && Cfg<64>::kMaxSteps * 2 <= kSizeStep, "steps");
-// Gathered steps keep A in buffer A0 (32 channel rows) and one B tile per
-// token tile (32 channel rows of SB bytes each) in B0..B1.
-static_assert(4 * KS * SB <= 2 * kSizeB, "gathered B tiles must fit");
+// LDS carve-up (bytes).  Dense: A0 A1 B0 B1 chunk buffers.  Gathered: two
+// stages of (A: 32 channel rows; B: one 32-row tile per token tile).  The two
+// phases reuse the same bytes.
+constexpr int kDenseBytes = 2 * BK * SA + 2 * BK * SB;     // 40960
+constexpr int kStageBytes = KS * SA + 4 * KS * SB;         // 25600
+constexpr int kDataBytes = kDenseBytes > 2 * kStageBytes ? kDenseBytes : 2 * kStageBytes;
+constexpr int kOffOff = kDataBytes;                         // int32 [4][65] bin offsets
+constexpr int kOffRs = kOffOff + 4 * (kBins + 1) * 4;      // int32 [4][16] prefix starts
+constexpr int kOffRc = kOffRs + 4 * kTags * 4;             // int32 [4][16] prefix lengths
+constexpr int kOffBp = kOffRc + 4 * kTags * 4;             // uint64 [4][16] bound parts
+constexpr int kOffSteps = kOffBp + 4 * kTags * 8;          // int32 [16] steps per group
+constexpr int kOffCum = kOffSteps + kTags * 4;             // int32 [17] cumulative steps
+constexpr int kOffElig = kOffCum + (kTags + 1) * 4;        // int32 [4]
+constexpr int kLdsBytes = kOffElig + 4 * 4;
 
 // Left shift of four packed int8 codes by e (0..6); each result fits int8.
 __device__ __forceinline__ uint32_t shift_codes(uint32_t x, int e) {
@@ -105,14 +103,42 @@ __device__ __forceinline__ int tag_pot(uint32_t byte) {
   return tag_e(byte) + 2 * (int)((byte >> DSTAR_FMDQ_PREC_SHIFT) & 3u);
 }
 
-__device__ __forceinline__ uint32_t ld_u32(const void* p) {
-  return *reinterpret_cast<const uint32_t*>(p);
-}
-__device__ __forceinline__ uint4 ld_u128(const void* p) {
-  return *reinterpret_cast<const uint4*>(p);
-}
 __device__ __forceinline__ void st_u128(uint8_t* p, uint4 v) {
   *reinterpret_cast<uint4*>(p) = v;
+}
+
+// Operand loads go through buffer resources: a load whose offset lies outside
+// the resource's byte range returns zeros, so every load is unconditional
+// (an invalid piece is given the offset kOob) and the compiler can count the
+// loads still in flight instead of waiting for all of them.
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOob = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// 16 bytes of W at byte offset `off` of the W resource; with VecW the piece is
+// one 16-byte load (N % 16 == 0, the piece lies wholly inside or outside W),
+// otherwise four 4-byte loads, each dropped past column N.
+template <bool VecW>
+__device__ __forceinline__ uint4 load_w16(rsrc_t rw, uint32_t off, int64_t n, int64_t N, bool valid) {
+  if constexpr (VecW) {
+    return bload16(rw, valid ? off : kOob);
+  } else {
+    uint32_t d[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) d[m] = bload4(rw, (valid && n + 4 * m < N) ? off + 4 * m : kOob);
+    return make_uint4(d[0], d[1], d[2], d[3]);
+  }
 }
 
 // MFMA fragment from a [channel][row] LDS tile with row stride S: the lane
@@ -133,20 +159,19 @@ __device__ __forceinline__ void shift_acc(v16i& acc, int s) {
   for (int r = 0; r < 16; ++r) acc[r] = (int)((uint32_t)acc[r] << s);
 }
 
-template <int T>
-__global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, int32_t col_blocks,
-                                                                  int32_t vec_w) {
+template <int T, bool VecW>
+__global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, int32_t row_blocks,
+                                                                  int32_t col_blocks) {
   using C = Cfg<T>;
+  constexpr int kTiles = C::kTiles;
   extern __shared__ __align__(16) uint8_t smem[];
-  auto Abuf = [&](int b) { return smem + kOffA0 + b * kSizeA; };
-  auto Bbuf = [&](int b) { return smem + kOffB0 + b * kSizeB; };
-  uint16_t* list = reinterpret_cast<uint16_t*>(smem + kOffList);       // [kTiles][kCap]
-  uint8_t* step_e = smem + kOffStep;                                    // [kTiles][kMaxSteps]
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(smem + kOffCnt);         // [kTiles][16]
-  uint32_t* cur = reinterpret_cast<uint32_t*>(smem + kOffCur);         // [kTiles][16]
-  unsigned long long* bnd = reinterpret_cast<unsigned long long*>(smem + kOffBnd);
-  int32_t* nsteps = reinterpret_cast<int32_t*>(smem + kOffMeta);       // [4]
-  int32_t* eligible = nsteps + 4;                                       // [4]
+  int32_t* off_s = reinterpret_cast<int32_t*>(smem + kOffOff);          // [kTiles][65]
+  int32_t* rstart = reinterpret_cast<int32_t*>(smem + kOffRs);          // [kTiles][16]
+  int32_t* rcount = reinterpret_cast<int32_t*>(smem + kOffRc);          // [kTiles][16]
+  unsigned long long* bpart = reinterpret_cast<unsigned long long*>(smem + kOffBp);
+  int32_t* steps_g = reinterpret_cast<int32_t*>(smem + kOffSteps);      // [16]
+  int32_t* cum = reinterpret_cast<int32_t*>(smem + kOffCum);            // [17]
+  int32_t* eligible = reinterpret_cast<int32_t*>(smem + kOffElig);      // [kTiles]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -154,103 +179,74 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   const int wr = wave >> 1, wc = wave & 1;
   const int64_t K = a.K, N = a.N;
   const int64_t nt = n_tiles(a.rows, T);
-  const int64_t mb = blockIdx.x / col_blocks;
-  const int64_t n0 = (int64_t)(blockIdx.x - mb * col_blocks) * BN;
-  const int64_t tile0 = mb * C::kTiles;
-  const int tiles_here = (int)min<int64_t>(C::kTiles, nt - tile0);
-
-  // ---- Prologue: per tile, the channels whose aligned codes exceed int8,
-  // grouped by tag in ascending FPoT, each group padded to a whole k-step.
-  if (tid < C::kTiles * kTags) cnt[tid] = 0u;
-  if (tid < C::kTiles) bnd[tid] = 0ull;
-  __syncthreads();
-  const int64_t kq_total = (K / 4) * tiles_here;   // tag words of this block's tiles
+  // Block order.  Workgroups are dealt to the 8 XCDs round-robin (XCD =
+  // blockIdx % 8), each with its own L2.  XCD x takes a contiguous range of a
+  // banded order of the (row block, column block) grid: bands of kBand row
+  // blocks, walked column block by column block, so the workgroups an XCD
+  // runs at the same time share their code rows and W columns in its L2.
+  int64_t mb, nb;
   {
-    unsigned long long b[C::kTiles];
-#pragma unroll
-    for (int i = 0; i < C::kTiles; ++i) b[i] = 0;
-    for (int64_t base = tid; base < kq_total; base += 4 * kThreads) {
-      uint32_t w[4];
-      int64_t idx[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        idx[u] = base + u * kThreads;
-        w[u] = idx[u] < kq_total ? ld_u32(a.tags + tile0 * K + 4 * idx[u]) : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (idx[u] >= kq_total) continue;
-        const int i = (int)(idx[u] / (K / 4));
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint32_t byte = (w[u] >> (8 * c)) & 0xFFu;
-          const int pot = tag_pot(byte);
-#pragma unroll
-          for (int ii = 0; ii < C::kTiles; ++ii)
-            if (ii == i) b[ii] += 1ull << pot;
-          if (pot > kAlignedPotMax) atomicAdd(&cnt[i * kTags + (byte & 15u)], 1u);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::kTiles; ++i) {
-      unsigned long long v = b[i];
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-      if (lane == 0 && i < tiles_here) atomicAdd(&bnd[i], v);
-    }
+    const int64_t G = (int64_t)row_blocks * col_blocks;
+    const int64_t x = blockIdx.x % 8, j = blockIdx.x / 8;
+    const int64_t L = x * (G / 8) + min<int64_t>(x, G % 8) + j;
+    const int64_t band = L / ((int64_t)kBand * col_blocks);
+    const int64_t Lb = L % ((int64_t)kBand * col_blocks);
+    const int64_t hgt = min<int64_t>(kBand, row_blocks - band * kBand);
+    mb = band * kBand + Lb % hgt;
+    nb = Lb / hgt;
+  }
+  const int64_t n0 = nb * BN;
+  const int64_t tile0 = mb * kTiles;
+  const int tiles_here = (int)min<int64_t>(kTiles, nt - tile0);
+  // This workgroup's tiles of codes, tags and perm; all of W.
+  const rsrc_t r_codes = make_rsrc(a.codes + tile0 * K * T, (uint32_t)(tiles_here * K * T));
+  const rsrc_t r_tags = make_rsrc(a.tags + tile0 * K, (uint32_t)(tiles_here * K));
+  const rsrc_t r_perm = make_rsrc(a.perm + tile0 * K, (uint32_t)(tiles_here * K * 2));
+  const rsrc_t r_w = make_rsrc(a.w, (uint32_t)(K * N));
+
+  // ---- Meta: per tile and FPoT group, the prefix of the group (in perm)
+  // whose channels have PoT ≥ 7, and the exactness bound Σ_k 2^PoT_k.
+  for (int idx = tid; idx < kTiles * (kBins + 1); idx += kThreads) {
+    const int i = idx / (kBins + 1);
+    off_s[idx] = i < tiles_here ? a.group_off[(tile0 + i) * (kBins + 1) + idx % (kBins + 1)] : 0;
   }
   __syncthreads();
-  if (tid < C::kTiles) {
-    const int i = tid;
-    int total = 0;
-    for (int g = 0; g < kTags; ++g) {
-      cur[i * kTags + g] = (uint32_t)total;
-      total += (int)((cnt[i * kTags + g] + KS - 1) / KS) * KS;
-    }
-    const bool ok = i < tiles_here && total <= C::kCap && bnd[i] <= kBoundLimit;
-    eligible[i] = ok ? 1 : 0;
-    nsteps[i] = ok ? total / KS : 0;
-    if (ok) {
-      for (int g = 0; g < kTags; ++g) {
-        const int s0 = (int)cur[i * kTags + g] / KS;
-        const int ns = (int)((cnt[i * kTags + g] + KS - 1) / KS);
-        for (int s = s0; s < s0 + ns; ++s) step_e[i * C::kMaxSteps + s] = (uint8_t)(DSTAR_FMDQ_TAG_OFFSET - g);
-      }
-    }
+  if (tid < kTiles * kTags) {
+    const int i = tid / kTags, g = tid % kTags;
+    const int e = DSTAR_FMDQ_TAG_OFFSET - g;
+    const int32_t* o = off_s + i * (kBins + 1);
+    // PoT = e + 2·pc ≥ 7  <=>  pc ≥ ceil((7 − e) / 2); bins of group g run
+    // from precision code 3 (bin 4g) down to 0 (bin 4g + 3).
+    const int pcmin = max(0, (8 - e) / 2);
+    rstart[tid] = o[4 * g];
+    rcount[tid] = pcmin <= 3 ? o[4 * g + 4 - pcmin] - o[4 * g] : 0;
+    unsigned long long b = 0;
+#pragma unroll
+    for (int pc = 0; pc < 4; ++pc)
+      b += (unsigned long long)(o[4 * g + 4 - pc] - o[4 * g + 3 - pc]) << (e + 2 * pc);
+    bpart[tid] = b;
   }
   __syncthreads();
-  for (int i = 0; i < C::kTiles; ++i) {
-    const int len = nsteps[i] * KS;
-    for (int j = tid; j < len; j += kThreads) list[i * C::kCap + j] = kPad;
+  if (tid < kTiles) {
+    unsigned long long b = 0;
+    for (int g = 0; g < kTags; ++g) b += bpart[tid * kTags + g];
+    eligible[tid] = (tid < tiles_here && b <= kBoundLimit) ? 1 : 0;
   }
   __syncthreads();
-  for (int64_t base = tid; base < kq_total; base += 4 * kThreads) {
-    uint32_t w[4];
-    int64_t idx[4];
+  if (tid < kTags) {
+    int m = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      idx[u] = base + u * kThreads;
-      const int i = idx[u] < kq_total ? (int)(idx[u] / (K / 4)) : 0;
-      w[u] = (idx[u] < kq_total && nsteps[i] > 0) ? ld_u32(a.tags + tile0 * K + 4 * idx[u]) : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (idx[u] >= kq_total) continue;
-      const int i = (int)(idx[u] / (K / 4));
-      if (nsteps[i] == 0) continue;
-      const int64_t k = 4 * (idx[u] - (int64_t)i * (K / 4));
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t byte = (w[u] >> (8 * c)) & 0xFFu;
-        if (tag_pot(byte) > kAlignedPotMax) {
-          const uint32_t slot = atomicAdd(&cur[i * kTags + (byte & 15u)], 1u);
-          list[i * C::kCap + slot] = (uint16_t)(k + c);
-        }
-      }
-    }
+    for (int i = 0; i < kTiles; ++i)
+      if (eligible[i]) m = max(m, (rcount[i * kTags + tid] + KS - 1) / KS);
+    steps_g[tid] = m;
   }
   __syncthreads();
+  if (tid == 0) {
+    cum[0] = 0;
+    for (int g = 0; g < kTags; ++g) cum[g + 1] = cum[g] + steps_g[g];
+  }
+  __syncthreads();
+  const int nsteps = cum[kTags];
 
   v16i acc[2][2];
 #pragma unroll
@@ -266,167 +262,187 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   for (int rb = 0; rb < 2; ++rb) rb_tile[rb] = (64 * wr + 32 * rb) / T;
 
   // ---- Gathered FPoT groups, Horner form: ascending tag = descending step.
-  int max_steps = 0;
+  // Step f of the workgroup covers entries 32·s .. 32·s + 31 of group g's
+  // prefix in every tile.  Thread roles: A piece (tile iA, entry jA, 16-byte
+  // piece subA of the channel's T codes); B pieces (entry jB, columns
+  // n0 + 16·c16 .. +15) of every tile.
+  {
+    constexpr int kPieces = T / 16;
+    const int iA = tid / (KS * kPieces), jA = (tid / kPieces) % KS, subA = tid % kPieces;
+    const int jB = tid >> 3, c16 = tid & 7;
+    auto step_group = [&](int f, int& g, int& s) {
+      g = 0;
+      while (cum[g + 1] <= f) ++g;
+      s = f - cum[g];
+    };
+    auto stage = [&](int b) { return smem + b * kStageBytes; };
+    // Entries: the channel id (low 16 bits) and a valid flag (bit 16).
+    uint32_t eA, eB[kTiles];
+    uint4 dA, dB[kTiles];
+    auto entry = [&](int i, int g, int j) -> uint32_t {
+      const int cnt = eligible[i] ? rcount[i * kTags + g] : 0;
+      const bool valid = j < cnt;
+      const uint32_t off = (uint32_t)(i * K + rstart[i * kTags + g] + j) * 2u;
+      return (__builtin_amdgcn_raw_buffer_load_b16(r_perm, valid ? off : kOob, 0, 0) & 0xFFFFu) |
+             (valid ? 0x10000u : 0u);
+    };
+    auto entries = [&](int f) {
+      int g, s;
+      step_group(f, g, s);
+      eA = entry(iA, g, KS * s + jA);
 #pragma unroll
-  for (int i = 0; i < C::kTiles; ++i) max_steps = max(max_steps, nsteps[i]);
-  for (int s = 0; s < max_steps; ++s) {
-    __syncthreads();
-    // A: per tile, 32 gathered channels × T rows -> Abuf(0)[entry][T·i + t].
-    {
-      constexpr int kPieces = T / 16;                  // 16-byte pieces per channel
-      const int p = tid;                               // kTiles · 32 · kPieces = 256
-      const int i = p / (KS * kPieces);
-      const int j = (p / kPieces) % KS;
-      const int sub = p % kPieces;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (s < nsteps[i]) {
-        const uint16_t ch = list[i * C::kCap + s * KS + j];
-        if (ch != kPad) v = ld_u128(a.codes + ((tile0 + i) * K + ch) * T + 16 * sub);
+      for (int i = 0; i < kTiles; ++i) eB[i] = entry(i, g, KS * s + jB);
+    };
+    auto data = [&]() {
+      const uint32_t chA = eA & 0xFFFFu;
+      dA = bload16(r_codes, (eA >> 16) ? (uint32_t)((iA * K + chA) * T + 16 * subA) : kOob);
+#pragma unroll
+      for (int i = 0; i < kTiles; ++i) {
+        const uint32_t ch = eB[i] & 0xFFFFu;
+        const int64_t n = n0 + 16 * c16;
+        dB[i] = load_w16<VecW>(r_w, (uint32_t)(ch * N + n), n, N, (eB[i] >> 16) && n < N);
       }
-      st_u128(Abuf(0) + j * SA + T * i + 16 * sub, v);
-    }
-    // B: per tile, 32 gathered W rows × 128 columns -> [entry][column].
+    };
+    auto store = [&](int b) {
+      uint8_t* st = stage(b);
+      st_u128(st + jA * SA + T * iA + 16 * subA, dA);
 #pragma unroll
-    for (int i = 0; i < C::kTiles; ++i) {
-      if (s >= nsteps[i]) continue;
-      const int j = tid >> 3, c16 = tid & 7;           // 32 rows × 8 pieces
-      const uint16_t ch = list[i * C::kCap + s * KS + j];
-      const int64_t n = n0 + 16 * c16;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (ch != kPad) {
-        const int8_t* src = a.w + (int64_t)ch * N + n;
-        if (vec_w && n + 16 <= N) {
-          v = ld_u128(src);
-        } else {
-          uint32_t d[4] = {0u, 0u, 0u, 0u};
+      for (int i = 0; i < kTiles; ++i) st_u128(st + KS * SA + i * KS * SB + jB * SB + 16 * c16, dB[i]);
+    };
+    int prev_e[2] = {-1, -1};
+    if (nsteps > 0) {
+      entries(0);
+      data();
+      if (nsteps > 1) entries(1);
+      store(0);
+      __syncthreads();
+      for (int f = 0; f < nsteps; ++f) {
+        const int b = f & 1;
+        if (f + 1 < nsteps) data();
+        if (f + 2 < nsteps) entries(f + 2);
+        int g, s;
+        step_group(f, g, s);
+        const int e = DSTAR_FMDQ_TAG_OFFSET - g;
+        const uint8_t* st = stage(b);
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
-            if (n + 4 * m < N) d[m] = ld_u32(src + 4 * m);
-          v = make_uint4(d[0], d[1], d[2], d[3]);
+        for (int rb = 0; rb < 2; ++rb) {
+          const int i = rb_tile[rb];
+          const int cnt = eligible[i] ? rcount[i * kTags + g] : 0;
+          if (KS * s >= cnt) continue;
+          if (s == 0) {
+            if (prev_e[rb] >= 0) {
+#pragma unroll
+              for (int cb = 0; cb < 2; ++cb) shift_acc(acc[rb][cb], prev_e[rb] - e);
+            }
+            prev_e[rb] = e;
+          }
+          const v4i af = tr_frag<SA>(st, 0, 64 * wr + 32 * rb, lane);
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb) {
+            const v4i bf = tr_frag<SB>(st + KS * SA + i * KS * SB, 0, 64 * wc + 32 * cb, lane);
+            acc[rb][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf, acc[rb][cb], 0, 0, 0);
+          }
         }
-      }
-      st_u128(smem + kOffB0 + i * KS * SB + j * SB + 16 * c16, v);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int i = rb_tile[rb];
-      if (s >= nsteps[i]) continue;
-      const int e = step_e[i * C::kMaxSteps + s];
-      if (s > 0) {
-        const int ep = step_e[i * C::kMaxSteps + s - 1];
-        if (ep != e) {
-#pragma unroll
-          for (int cb = 0; cb < 2; ++cb) shift_acc(acc[rb][cb], ep - e);
-        }
-      }
-      const v4i af = tr_frag<SA>(Abuf(0), 0, 64 * wr + 32 * rb, lane);
-      const uint8_t* Bt = smem + kOffB0 + i * KS * SB;
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const v4i bf = tr_frag<SB>(Bt, 0, 64 * wc + 32 * cb, lane);
-        acc[rb][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf, acc[rb][cb], 0, 0, 0);
+        if (f + 1 < nsteps) store(b ^ 1);
+        __syncthreads();
       }
     }
-  }
-  // Bring the gathered groups to units of the base (step 2^0).
+    // Bring the gathered groups to units of the base (step 2^0).
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int i = rb_tile[rb];
-    if (nsteps[i] > 0) {
-      const int e = step_e[i * C::kMaxSteps + nsteps[i] - 1];
+    for (int rb = 0; rb < 2; ++rb)
+      if (prev_e[rb] > 0) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) shift_acc(acc[rb][cb], e);
-    }
+        for (int cb = 0; cb < 2; ++cb) shift_acc(acc[rb][cb], prev_e[rb]);
+      }
   }
 
   // ---- Dense part: every other channel, natural order, codes shifted by e.
   // A chunk: per tile, 64 channels × T rows (contiguous in memory) as 16-byte
   // pieces; B chunk: 64 W rows × 128 columns as 16-byte pieces.
-  constexpr int kPiecesA = BK * BM / 16 / kThreads;    // 2
-  constexpr int kPiecesB = BK * BN / 16 / kThreads;    // 2
-  uint4 ra[kPiecesA], rbv[kPiecesB];
-  uint32_t rtag[kPiecesA];
-  auto load_chunk = [&](int64_t k0) {
+  {
+    constexpr int kPiecesA = BK * BM / 16 / kThreads;    // 2
+    constexpr int kPiecesB = BK * BN / 16 / kThreads;    // 2
+    auto Abuf = [&](int b) { return smem + b * BK * SA; };
+    auto Bbuf = [&](int b) { return smem + 2 * BK * SA + b * BK * SB; };
+    uint4 ra[kDepth][kPiecesA], rbv[kDepth][kPiecesB];
+    uint32_t rtag[kDepth][kPiecesA];
+    auto load_chunk = [&](int d, int64_t k0) {
 #pragma unroll
-    for (int u = 0; u < kPiecesA; ++u) {
-      const int p = tid + kThreads * u;
-      const int i = p / (BK * T / 16);
-      const int q = p % (BK * T / 16);
-      const int kk = q / (T / 16);
-      ra[u] = make_uint4(0u, 0u, 0u, 0u);
-      rtag[u] = 0xFFu;  // decodes to PoT > 6: contributes nothing
-      if (i < tiles_here && k0 + kk < K) {
-        ra[u] = ld_u128(a.codes + ((tile0 + i) * K + k0) * T + 16 * q);
-        rtag[u] = a.tags[(tile0 + i) * K + k0 + kk];
+      for (int u = 0; u < kPiecesA; ++u) {
+        const int p = tid + kThreads * u;
+        const int i = p / (BK * T / 16);
+        const int q = p % (BK * T / 16);
+        const int kk = q / (T / 16);
+        const bool valid = k0 + kk < K;   // tiles past the end lie outside r_codes
+        ra[d][u] = bload16(r_codes, valid ? (uint32_t)((i * K + k0) * T + 16 * q) : kOob);
+        // A zero tag byte (also what an invalid load returns) decodes to
+        // PoT = 15 > 6: the piece contributes nothing to the dense part.
+        rtag[d][u] = __builtin_amdgcn_raw_buffer_load_b8(r_tags, valid ? (uint32_t)(i * K + k0 + kk) : kOob, 0, 0);
       }
-    }
 #pragma unroll
-    for (int u = 0; u < kPiecesB; ++u) {
-      const int p = tid + kThreads * u;
-      const int kk = p / (BN / 16), c16 = p % (BN / 16);
-      const int64_t n = n0 + 16 * c16;
-      rbv[u] = make_uint4(0u, 0u, 0u, 0u);
-      if (k0 + kk < K) {
-        const int8_t* src = a.w + (k0 + kk) * N + n;
-        if (vec_w && n + 16 <= N) {
-          rbv[u] = ld_u128(src);
-        } else {
-          uint32_t d[4] = {0u, 0u, 0u, 0u};
+      for (int u = 0; u < kPiecesB; ++u) {
+        const int p = tid + kThreads * u;
+        const int kk = p / (BN / 16), c = p % (BN / 16);
+        const int64_t n = n0 + 16 * c;
+        rbv[d][u] = load_w16<VecW>(r_w, (uint32_t)((k0 + kk) * N + n), n, N, k0 + kk < K && n < N);
+      }
+    };
+    auto store_chunk = [&](int d, int b) {
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
-            if (n + 4 * m < N) d[m] = ld_u32(src + 4 * m);
-          rbv[u] = make_uint4(d[0], d[1], d[2], d[3]);
+      for (int u = 0; u < kPiecesA; ++u) {
+        const int p = tid + kThreads * u;
+        const int i = p / (BK * T / 16);
+        const int q = p % (BK * T / 16);
+        const int kk = q / (T / 16), sub = q % (T / 16);
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (tag_pot(rtag[d][u]) <= kAlignedPotMax) {
+          const int e = tag_e(rtag[d][u]);
+          v = make_uint4(shift_codes(ra[d][u].x, e), shift_codes(ra[d][u].y, e),
+                         shift_codes(ra[d][u].z, e), shift_codes(ra[d][u].w, e));
+        }
+        st_u128(Abuf(b) + kk * SA + T * i + 16 * sub, v);
+      }
+#pragma unroll
+      for (int u = 0; u < kPiecesB; ++u) {
+        const int p = tid + kThreads * u;
+        const int kk = p / (BN / 16), c = p % (BN / 16);
+        st_u128(Bbuf(b) + kk * SB + 16 * c, rbv[d][u]);
+      }
+    };
+    auto compute = [&](int b) {
+#pragma unroll
+      for (int ks = 0; ks < BK / KS; ++ks) {
+        v4i af[2], bf[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) af[rb] = tr_frag<SA>(Abuf(b), KS * ks, 64 * wr + 32 * rb, lane);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) bf[cb] = tr_frag<SB>(Bbuf(b), KS * ks, 64 * wc + 32 * cb, lane);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < 2; ++cb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[rb], bf[cb], acc[rb][cb], 0, 0, 0);
+      }
+    };
+
+    const int64_t nchunks = (K + BK - 1) / BK;
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d)
+      if (d < nchunks) load_chunk(d, d * BK);
+    store_chunk(0, 0);
+    __syncthreads();
+    for (int64_t c0 = 0; c0 < nchunks; c0 += kDepth) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        const int64_t c = c0 + d;
+        if (c < nchunks) {
+          if (c + kDepth < nchunks) load_chunk(d, (c + kDepth) * BK);
+          compute((int)(c & 1));
+          if (c + 1 < nchunks) store_chunk((d + 1) % kDepth, (int)((c + 1) & 1));
+          __syncthreads();
         }
       }
     }
-  };
-  auto store_chunk = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < kPiecesA; ++u) {
-      const int p = tid + kThreads * u;
-      const int i = p / (BK * T / 16);
-      const int q = p % (BK * T / 16);
-      const int kk = q / (T / 16), sub = q % (T / 16);
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (tag_pot(rtag[u]) <= kAlignedPotMax) {
-        const int e = tag_e(rtag[u]);
-        v = make_uint4(shift_codes(ra[u].x, e), shift_codes(ra[u].y, e), shift_codes(ra[u].z, e),
-                       shift_codes(ra[u].w, e));
-      }
-      st_u128(Abuf(buf) + kk * SA + T * i + 16 * sub, v);
-    }
-#pragma unroll
-    for (int u = 0; u < kPiecesB; ++u) {
-      const int p = tid + kThreads * u;
-      const int kk = p / (BN / 16), c16 = p % (BN / 16);
-      st_u128(Bbuf(buf) + kk * SB + 16 * c16, rbv[u]);
-    }
-  };
-
-  const int64_t nchunks = (K + BK - 1) / BK;
-  __syncthreads();  // the gathered steps are done with the buffers
-  load_chunk(0);
-  store_chunk(0);
-  __syncthreads();
-  for (int64_t c = 0; c < nchunks; ++c) {
-    const int buf = (int)(c & 1);
-    if (c + 1 < nchunks) load_chunk((c + 1) * BK);
-#pragma unroll
-    for (int ks = 0; ks < BK / KS; ++ks) {
-      v4i af[2], bf[2];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) af[rb] = tr_frag<SA>(Abuf(buf), KS * ks, 64 * wr + 32 * rb, lane);
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) bf[cb] = tr_frag<SB>(Bbuf(buf), KS * ks, 64 * wc + 32 * cb, lane);
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-          acc[rb][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[rb], bf[cb], acc[rb][cb], 0, 0, 0);
-    }
-    if (c + 1 < nchunks) store_chunk(buf ^ 1);
-    __syncthreads();
   }
 
   // ---- Epilogue: dequantize, add the cached output, store (float64 combine).
@@ -436,7 +452,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   const int h = lane >> 5, li = lane & 31;
   bool all_eligible = true;
 #pragma unroll
-  for (int i = 0; i < C::kTiles; ++i) all_eligible = all_eligible && eligible[i];
+  for (int i = 0; i < kTiles; ++i) all_eligible = all_eligible && eligible[i];
   const bool interior = all_eligible && (tile0 * T + BM <= a.rows) && (n0 + BN <= N);
   if (interior) {
     float yp[2][2][16];
@@ -485,8 +501,8 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     }
   }
 
-  // ---- Ineligible tiles: exact scalar path over the FPoT-ordered channels
-  // (stage 2's perm and group offsets), int32 group sums shifted into int64.
+  // ---- Ineligible tiles: exact scalar path over the FPoT groups in perm
+  // order, int32 group sums shifted into int64.
   for (int i = 0; i < tiles_here; ++i) {
     if (eligible[i]) continue;
     const int64_t tau = tile0 + i;
@@ -495,14 +511,14 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     const int64_t n = n0 + (tid % BN);
     const int t0 = (tid / BN) * kRows;
     if (n >= N) continue;
-    const int32_t* off = a.group_off + tau * (kTags + 1);
+    const int32_t* off = off_s + i * (kBins + 1);
     const uint16_t* pm = a.perm + tau * K;
     const int8_t* cd = a.codes + tau * K * T;
     int64_t sum[kRows];
 #pragma unroll
     for (int t = 0; t < kRows; ++t) sum[t] = 0;
     for (int g = 0; g < kTags; ++g) {
-      const int lo = off[g], hi = off[g + 1];
+      const int lo = off[4 * g], hi = off[4 * g + 4];
       if (lo == hi) continue;
       int32_t gs[kRows];
 #pragma unroll
@@ -534,32 +550,38 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   }
 }
 
-template <int T>
-int launch_t(const LinearArgs& a, hipStream_t s) {
+template <int T, bool VecW>
+int launch_tv(const LinearArgs& a, hipStream_t s) {
   const int64_t nt = n_tiles(a.rows, T);
   const int64_t row_blocks = (nt + Cfg<T>::kTiles - 1) / Cfg<T>::kTiles;
   const int32_t col_blocks = (int32_t)((a.N + BN - 1) / BN);
   const int64_t grid = row_blocks * col_blocks;
-  if (grid > 0x7FFFFFFF) return set_error(DSTAR_EUNSUPPORTED, "fmdq_linear: grid too large");
+  if (grid > 0x7FFFFFFF || row_blocks > 0x7FFFFFFF)
+    return set_error(DSTAR_EUNSUPPORTED, "fmdq_linear: grid too large");
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)linear_mfma_kernel<T>,
+    hipError_t e = hipFuncSetAttribute((const void*)linear_mfma_kernel<T, VecW>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess)
       return set_error(DSTAR_EHIP, "fmdq_linear: hipFuncSetAttribute: %s", hipGetErrorString(e));
     attr_set = true;
   }
-  const int32_t vec_w = (a.N % 16) == 0 ? 1 : 0;
-  hipLaunchKernelGGL(linear_mfma_kernel<T>, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, a,
-                     col_blocks, vec_w);
+  hipLaunchKernelGGL((linear_mfma_kernel<T, VecW>), dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s,
+                     a, (int32_t)row_blocks, col_blocks);
   return check_launch("fmdq_linear (mfma)");
+}
+
+template <int T>
+int launch_t(const LinearArgs& a, hipStream_t s) {
+  return (a.N % 16) == 0 ? launch_tv<T, true>(a, s) : launch_tv<T, false>(a, s);
 }
 
 }  // namespace
 
-// Handles token tiles of 32 or 64 rows with K a multiple of 4.
+// Handles token tiles of 32 or 64 rows with K a multiple of 4 and W below
+// 2^31 bytes (32-bit buffer offsets).
 bool linear_mfma_supported(const LinearArgs& a) {
-  return (a.T == 32 || a.T == 64) && (a.K % 4) == 0;
+  return (a.T == 32 || a.T == 64) && (a.K % 4) == 0 && (int64_t)a.K * a.N < (int64_t(1) << 31);
 }
 
 int launch_linear_mfma(const LinearArgs& a, hipStream_t s) {

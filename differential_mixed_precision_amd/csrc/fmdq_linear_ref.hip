@@ -25,7 +25,7 @@ __global__ __launch_bounds__(kThreads) void linear_general_kernel(LinearArgs a, 
     const int64_t tile = wi / col_blocks;
     const int64_t n = (wi - tile * col_blocks) * kThreads + threadIdx.x;
     const bool valid = n < N;
-    const int32_t* off = a.group_off + tile * (DSTAR_FMDQ_NUM_TAGS + 1);
+    const int32_t* off = a.group_off + tile * (DSTAR_FMDQ_NUM_BINS + 1);
     const uint16_t* pm = a.perm + tile * K;
     const int8_t* cd = a.codes + tile * K * T;
     const int64_t r0 = tile * T;
@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kThreads) void linear_general_kernel(LinearArgs a, 
 #pragma unroll
     for (int t = 0; t < T; ++t) s[t] = 0;
     for (int g = 0; g < DSTAR_FMDQ_NUM_TAGS; ++g) {
-      const int lo = off[g], hi = off[g + 1];
+      const int lo = off[4 * g], hi = off[4 * g + 4];
       if (lo == hi && !dump) continue;
       int32_t acc[T];
 #pragma unroll

@@ -39,12 +39,13 @@
 extern "C" {
 #endif
 
-#define DSTAR_FMDQ_ABI_VERSION 2
+#define DSTAR_FMDQ_ABI_VERSION 3
 
 /* Rule constants (DSTAR §3.1 step 1; readings in the design notes):
  * PCeil of a b-bit sub-channel is 2^(b-2); PoT is capped at POT_MAX so that
  * the tag (b-2) - PoT + TAG_OFFSET always lies in [0, NUM_TAGS). */
 #define DSTAR_FMDQ_NUM_TAGS 16
+#define DSTAR_FMDQ_NUM_BINS 64 /* (tag, precision) bins of the bucket order */
 #define DSTAR_FMDQ_TAG_OFFSET 15
 #define DSTAR_FMDQ_POT_MAX 21
 #define DSTAR_FMDQ_PREC_SHIFT 4
@@ -101,13 +102,16 @@ int dstar_fmdq_quantize(const dstar_fmdq_params* p, const float* x_t,
                         uint32_t* bit_hist, void* stream);
 
 /* Stage 2 — reorder the channels of every token tile by FPoT (DSTAR §3.1
- * step 3; §4.2 QPU stage 4), as a stable counting sort.
- *   tags       [n_t][K] uint8 from stage 1 (only bits 0-3 are read).
- *   perm       [n_t][K] uint16 (out): channel ids of tile τ sorted by (tag
- *              ascending, channel ascending).
- *   group_off  [n_t][17] int32 (out): group_off[τ][g] = number of channels of
- *              tile τ with tag < g; group g is perm[τ][group_off[τ][g] ..
- *              group_off[τ][g+1]). */
+ * step 3; §4.2 QPU stage 4), as a stable counting sort over the 64 bins
+ * bin = 4 * tag + (3 - precision code): FPoT tag ascending, inside one tag the
+ * precision descending, then the channel ascending.  (The pages fix only the
+ * FPoT order.  With the wider codes first, the sub-channels of a group whose
+ * shift-aligned codes exceed 8 bits form a prefix of that group.)
+ *   tags       [n_t][K] uint8 from stage 1.
+ *   perm       [n_t][K] uint16 (out): channel ids of tile τ in that order.
+ *   group_off  [n_t][65] int32 (out): group_off[τ][β] = number of channels of
+ *              tile τ with bin < β (group_off[τ][64] = K).  FPoT group g is
+ *              perm[τ][group_off[τ][4g] .. group_off[τ][4g+4]). */
 int dstar_fmdq_bucket(const dstar_fmdq_params* p, const uint8_t* tags,
                       uint16_t* perm, int32_t* group_off, void* stream);
 
@@ -117,7 +121,7 @@ int dstar_fmdq_bucket(const dstar_fmdq_params* p, const uint8_t* tags,
  * the GEMM).
  *   N          output channels, a multiple of 4 in [4, 2^20].
  *   codes      from stage 1; tags from stage 1 (4-byte aligned); perm,
- *              group_off from stage 2.  Channel k of group g of tile τ is
+ *              group_off ([n_t][65]) from stage 2.  Channel k of group g of tile τ is
  *              multiplied at step 2^(15-g) * base.
  *   w          [K][N] int8 row-major, 16-byte aligned.
  *   w_scale    [N] float32, per-output-channel weight scale.
@@ -132,9 +136,10 @@ int dstar_fmdq_bucket(const dstar_fmdq_params* p, const uint8_t* tags,
  *              the layer runs in the per-group kernel (slow; for checking).
  * Per output: S = Σ_g acc_g * 2^(15-g) (an exact integer);
  * y_out = fl32(f64(y_prev) + (f64(S) * f64(base)) * f64(w_scale[n])).
- * perm and group_off are read only for token tiles where the fast kernel
- * cannot prove its int32 accumulator exact (127 * Σ_k 2^PoT_k >= 2^31) or
- * whose channels with PoT >= 7 exceed its LDS budget; tags are read always. */
+ * The MFMA kernel reads the channels with PoT >= 7 of every FPoT group as the
+ * group's prefix in perm; a token tile whose int32 accumulator it cannot
+ * prove exact (127 * Σ_k 2^PoT_k >= 2^31) is finished by a per-group path
+ * over perm and group_off. */
 int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N,
                       const int8_t* codes, const uint8_t* tags, const uint16_t* perm,
                       const int32_t* group_off,

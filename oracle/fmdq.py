@@ -43,7 +43,12 @@ the design notes of this repository):
   once in float64; q = round-half-to-even(r) clipped to ±PCeil.  All of it is
   done in float32, the precision of the inputs, so that both implementations
   take the same integer decisions.
-* The bucket order is the stable one: (tag ascending, channel ascending).
+* The bucket order: tag ascending (ascending FPoT); inside one FPoT group,
+  precision descending, then channel ascending.  DSTAR leaves the order of
+  equal FPoTs free (a bitonic network, §3.1 ❸; the Fig. 11 meta table has
+  ties that are not index-ordered).  Putting the wider codes of a group first
+  makes the sub-channels whose shift-aligned codes exceed 8 bits a prefix of
+  every group.
 * The per-group sums are exact integers; S = Σ_g acc_g · 2^(15−g) in int64; the
   output is fl32(f64(Y_{t−1}) + (f64(S) · f64(base)) · f64(w_scale[n])).
 
@@ -67,6 +72,8 @@ TAG_OFF = 15
 N_TAGS = 16
 #: Precision code stored in bits 4-5 of a tag byte: b / 2 - 1.
 PREC_SHIFT = 4
+#: Bins of the bucket order: (tag, precision) pairs, four precisions per tag.
+N_BINS = 4 * N_TAGS
 
 
 # --------------------------------------------------------------------------- #
@@ -214,35 +221,53 @@ def bits_of(tags: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------- #
 # Step ❸ of DSTAR §3.1: reorder sub-channels of a tile by FPoT                  #
 # --------------------------------------------------------------------------- #
+def bucket_key(tags: np.ndarray) -> np.ndarray:
+    """Sort key of a sub-channel: 4 · tag + (3 − precision code).
+
+    Ascending key = ascending FPoT tag (DSTAR §3.1 ❸), and inside one tag
+    descending precision (a free choice: the pages fix only the FPoT order).
+    """
+    t = np.asarray(tags).astype(np.int64)
+    return 4 * (t & 0x0F) + (3 - ((t >> PREC_SHIFT) & 0x3))
+
+
+def group_bounds(off_tile: np.ndarray, g: int) -> tuple[int, int]:
+    """[first, last) positions of FPoT group g in a tile's bucket order."""
+    return int(off_tile[4 * g]), int(off_tile[4 * g + 4])
+
+
 def bucket(tags: np.ndarray):
     """Group the channels of every token tile by tag, in ascending FPoT.
 
     DSTAR §3.1 ❸ (sub-channels sharing an FPoT placed next to each other, in
-    ascending FPoT) and §4.2 QPU stage 4.  Written as a counting sort: count
-    the channels of each tag, take the exclusive prefix sum, then place the
-    channels in index order — which makes equal tags keep channel order.
+    ascending FPoT) and §4.2 QPU stage 4.  Written as a counting sort over the
+    64 (tag, precision) bins of ``bucket_key``: count the channels of each bin,
+    take the exclusive prefix sum, then place the channels in index order —
+    which keeps channel order inside a bin.
 
-    Returns perm uint16 [n_t][K] and group_off int32 [n_t][17], where the
-    channels of tag g are perm[τ][group_off[τ][g] : group_off[τ][g+1]].
+    Returns perm uint16 [n_t][K] and group_off int32 [n_t][65]:
+    group_off[τ][β] = number of channels of tile τ with key < β.  The channels
+    of FPoT group g are perm[τ][group_off[τ][4g] : group_off[τ][4g + 4]],
+    widest precision first.
     """
     tags = np.asarray(tags)
     nt, K = tags.shape
     perm = np.zeros((nt, K), dtype=np.uint16)
-    off = np.zeros((nt, N_TAGS + 1), dtype=np.int32)
+    off = np.zeros((nt, N_BINS + 1), dtype=np.int32)
     for tau in range(nt):
-        tg = tag_of(tags[tau])
-        count = np.zeros(N_TAGS, dtype=np.int64)
+        key = bucket_key(tags[tau])
+        count = np.zeros(N_BINS, dtype=np.int64)
         for k in range(K):
-            count[tg[k]] += 1
-        start = np.zeros(N_TAGS + 1, dtype=np.int64)
-        for g in range(N_TAGS):
-            start[g + 1] = start[g] + count[g]
+            count[key[k]] += 1
+        start = np.zeros(N_BINS + 1, dtype=np.int64)
+        for b in range(N_BINS):
+            start[b + 1] = start[b] + count[b]
         off[tau] = start
-        cursor = start[:N_TAGS].copy()
+        cursor = start[:N_BINS].copy()
         for k in range(K):
-            g = tg[k]
-            perm[tau, cursor[g]] = k
-            cursor[g] += 1
+            b = key[k]
+            perm[tau, cursor[b]] = k
+            cursor[b] += 1
     return perm, off
 
 
@@ -261,7 +286,7 @@ def group_accumulators(codes_tile: np.ndarray, perm_tile: np.ndarray,
     N = w.shape[1]
     acc = np.zeros((N_TAGS, T, N), dtype=np.int64)
     for g in range(N_TAGS):
-        lo, hi = int(off_tile[g]), int(off_tile[g + 1])
+        lo, hi = group_bounds(off_tile, g)
         if hi == lo:
             continue
         ch = perm_tile[lo:hi].astype(np.int64)

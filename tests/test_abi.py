@@ -41,6 +41,7 @@ def test_header_constants_match_oracle_and_binding(lib):
     text = _header()
     consts = dict(re.findall(r"#define\s+(DSTAR_\w+)\s+\(?(-?\d+)\)?", text))
     assert int(consts["DSTAR_FMDQ_NUM_TAGS"]) == fmdq.N_TAGS == lib.NUM_TAGS
+    assert int(consts["DSTAR_FMDQ_NUM_BINS"]) == fmdq.N_BINS == lib.NUM_BINS
     assert int(consts["DSTAR_FMDQ_TAG_OFFSET"]) == fmdq.TAG_OFF == lib.TAG_OFFSET
     assert int(consts["DSTAR_FMDQ_POT_MAX"]) == fmdq.POT_HI == lib.POT_MAX
     assert int(consts["DSTAR_FMDQ_PREC_SHIFT"]) == fmdq.PREC_SHIFT == lib.PREC_SHIFT

@@ -57,7 +57,7 @@ def gpu_layer(dm, d, dbg=None, inplace=False, y_prev_np=None):
     tags = torch.full((nt, K), 0xEE, dtype=torch.uint8, device=dev)
     hist = torch.zeros(4, dtype=torch.int32, device=dev)
     perm = torch.full((nt, K), -1, dtype=torch.int16, device=dev)
-    off = torch.full((nt, 17), -7, dtype=torch.int32, device=dev)
+    off = torch.full((nt, 65), -7, dtype=torch.int32, device=dev)
     y1 = y0 if inplace else torch.full((rows, N), float("nan"), dtype=torch.float32, device=dev)
     dm.quantize(p, x_t, x_p, codes, tags, hist)
     dm.bucket(p, tags, perm, off)

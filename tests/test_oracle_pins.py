@@ -367,9 +367,23 @@ def test_bucket_is_stable_sort_and_max_is_abs_max(seed):
     tags = raw.astype(np.uint8)
     perm, off = fmdq.bucket(tags)
     for tau in range(nt):
-        tg = tags[tau] & 0x0F
-        np.testing.assert_array_equal(perm[tau], np.argsort(tg, kind="stable"))
-        np.testing.assert_array_equal(off[tau], np.concatenate([[0], np.cumsum(np.bincount(tg, minlength=16))]))
+        tg = (tags[tau] & 0x0F).astype(np.int64)
+        pc = ((tags[tau] >> 4) & 0x3).astype(np.int64)
+        # the library routine on the same key: tag ascending, precision descending
+        key = np.lexsort((3 - pc, tg))       # last key is primary; lexsort is stable
+        np.testing.assert_array_equal(perm[tau], key)
+        bins = 4 * tg + 3 - pc
+        np.testing.assert_array_equal(off[tau], np.concatenate([[0], np.cumsum(np.bincount(bins, minlength=64))]))
+        # FPoT groups are contiguous and ascending; inside a group the precision
+        # never increases and, at equal precision, channel ids increase
+        t_sorted, p_sorted = tg[perm[tau]], pc[perm[tau]]
+        assert (np.diff(t_sorted) >= 0).all()
+        for g in range(16):
+            lo, hi = fmdq.group_bounds(off[tau], g)
+            assert (t_sorted[lo:hi] == g).all() and hi - lo == int((tg == g).sum())
+            assert (np.diff(p_sorted[lo:hi]) <= 0).all()
+            same = np.diff(p_sorted[lo:hi]) == 0
+            assert (np.diff(perm[tau][lo:hi].astype(int))[same] > 0).all()
     d = rng.standard_normal((70, 13)).astype(np.float32)
     m = fmdq.subchannel_max(d, 32)
     pad = np.zeros((96, 13), dtype=np.float32)
@@ -391,7 +405,8 @@ def test_fig11_meta_table_order():
     np.testing.assert_array_equal(fp[sh][perm[0].astype(int)], fp)
     # items of one FPoT keep their relative (stable) order
     for g in np.unique(fp):
-        idx = perm[0][off[0][g]:off[0][g + 1]]
+        lo, hi = fmdq.group_bounds(off[0], int(g))
+        idx = perm[0][lo:hi]
         assert (np.diff(idx.astype(int)) > 0).all()
 
 
