@@ -11,10 +11,10 @@ from __future__ import annotations
 
 from . import _binding
 from ._binding import (FmdqError, Params, bucket, linear, load, make_params,  # noqa: F401
-                       quantize)
+                       pack_weights, quantize)
 
 __all__ = ["FmdqError", "Params", "FmdqLayer", "bucket", "linear", "load", "make_params",
-           "quantize", "n_tiles"]
+           "pack_weights", "quantize", "n_tiles"]
 
 
 def n_tiles(rows: int, token_tile: int) -> int:
@@ -40,15 +40,18 @@ class FmdqLayer:
         dev = w.device
         self.codes = torch.empty((nt, self.K, token_tile), dtype=torch.int8, device=dev)
         self.tags = torch.empty((nt, self.K), dtype=torch.uint8, device=dev)
+        self.acodes = torch.empty((nt * token_tile, self.K), dtype=torch.int8, device=dev)
+        self.w_t = torch.empty((self.N, self.K), dtype=torch.int8, device=dev)
+        pack_weights(self.K, self.N, self.w, self.w_t)
         self.perm = torch.empty((nt, self.K), dtype=torch.int16, device=dev)  # uint16 ids
         self.group_off = torch.empty((nt, 65), dtype=torch.int32, device=dev)
         self.bit_hist = torch.zeros(4, dtype=torch.int32, device=dev)
 
     def step(self, x_t, x_prev, y, y_out=None, stream=None, hist: bool = True):
-        quantize(self.p, x_t, x_prev, self.codes, self.tags,
+        quantize(self.p, x_t, x_prev, self.codes, self.tags, self.acodes,
                  self.bit_hist if hist else None, stream)
         bucket(self.p, self.tags, self.perm, self.group_off, stream)
         out = y if y_out is None else y_out
-        linear(self.p, self.N, self.codes, self.tags, self.perm, self.group_off, self.w, self.w_scale,
-               y, out, stream=stream)
+        linear(self.p, self.N, self.codes, self.perm, self.group_off, self.acodes, self.w, self.w_t,
+               self.w_scale, y, out, stream=stream)
         return out

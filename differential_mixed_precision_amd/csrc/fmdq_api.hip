@@ -68,7 +68,8 @@ int dstar_fmdq_abi_version(void) { return DSTAR_FMDQ_ABI_VERSION; }
 const char* dstar_fmdq_last_error(void) { return g_error.c_str(); }
 
 int dstar_fmdq_quantize(const dstar_fmdq_params* p, const float* x_t, const float* x_prev,
-                        int8_t* codes, uint8_t* tags, uint32_t* bit_hist, void* stream) {
+                        int8_t* codes, uint8_t* tags, int8_t* acodes, uint32_t* bit_hist,
+                        void* stream) {
   clear_error();
   int64_t nt = 0;
   if (int rc = check_params(p, &nt)) return rc;
@@ -80,11 +81,14 @@ int dstar_fmdq_quantize(const dstar_fmdq_params* p, const float* x_t, const floa
                      "quantize: x_t, x_prev and codes must be 16-byte aligned, tags 4-byte aligned");
   if (bit_hist && !aligned(bit_hist, 4))
     return set_error(DSTAR_EALIGN, "quantize: bit_hist must be 4-byte aligned");
+  if (acodes && !aligned(acodes, 16))
+    return set_error(DSTAR_EALIGN, "quantize: acodes must be 16-byte aligned");
   QuantizeArgs a;
   a.x_t = x_t;
   a.x_prev = x_prev;
   a.codes = codes;
   a.tags = tags;
+  a.acodes = acodes;
   a.bit_hist = bit_hist;
   a.rows = p->rows;
   a.K = p->K;
@@ -114,8 +118,21 @@ int dstar_fmdq_bucket(const dstar_fmdq_params* p, const uint8_t* tags, uint16_t*
   return launch_bucket(a, (hipStream_t)stream);
 }
 
+int dstar_fmdq_pack_weights(int32_t K, int32_t N, const int8_t* w, int8_t* w_t, void* stream) {
+  clear_error();
+  if (K < 1 || K > DSTAR_FMDQ_MAX_K)
+    return set_error(DSTAR_EINVAL, "pack_weights: K = %d outside [1, %d]", K, DSTAR_FMDQ_MAX_K);
+  if (N < 1 || N > (1 << 20))
+    return set_error(DSTAR_EINVAL, "pack_weights: N = %d outside [1, 2^20]", N);
+  if (!w || !w_t) return set_error(DSTAR_ENULL, "pack_weights: w and w_t must not be NULL");
+  if (!aligned(w, 16) || !aligned(w_t, 16))
+    return set_error(DSTAR_EALIGN, "pack_weights: w and w_t must be 16-byte aligned");
+  return launch_pack_weights(K, N, w, w_t, (hipStream_t)stream);
+}
+
 int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N, const int8_t* codes,
-                      const uint8_t* tags, const uint16_t* perm, const int32_t* group_off, const int8_t* w,
+                      const uint16_t* perm, const int32_t* group_off,
+                      const int8_t* acodes, const int8_t* w, const int8_t* w_t,
                       const float* w_scale, const float* y_prev, float* y_out, int32_t* acc_dbg,
                       int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream) {
   clear_error();
@@ -127,21 +144,23 @@ int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N, const int8_t* codes
     return set_error(DSTAR_EINVAL, "linear: debug tile range [%d, %d) not within [0, %lld)",
                      dbg_tile_lo, dbg_tile_hi, (long long)nt);
   if (nt == 0) return DSTAR_OK;
-  if (!codes || !tags || !perm || !group_off || !w || !w_scale || !y_prev || !y_out)
+  if (!codes || !perm || !group_off || !w || !w_scale || !y_prev || !y_out)
     return set_error(DSTAR_ENULL,
-                     "linear: codes, tags, perm, group_off, w, w_scale, y_prev and y_out must not be NULL");
+                     "linear: codes, perm, group_off, w, w_scale, y_prev and y_out must not be NULL");
   if (!aligned(codes, 16) || !aligned(w, 16) || !aligned(y_prev, 16) || !aligned(y_out, 16) ||
-      !aligned(tags, 4) || !aligned(w_scale, 4) || !aligned(perm, 2) || !aligned(group_off, 4) ||
-      (acc_dbg && !aligned(acc_dbg, 4)))
+      !aligned(w_scale, 4) || !aligned(perm, 2) || !aligned(group_off, 4) ||
+      (acc_dbg && !aligned(acc_dbg, 4)) || (acodes && !aligned(acodes, 16)) ||
+      (w_t && !aligned(w_t, 16)))
     return set_error(DSTAR_EALIGN,
-                     "linear: codes, w, y_prev, y_out must be 16-byte aligned (tags, w_scale, "
-                     "group_off, acc_dbg 4-byte, perm 2-byte)");
+                     "linear: codes, acodes, w, w_t, y_prev, y_out must be 16-byte aligned "
+                     "(w_scale, group_off, acc_dbg 4-byte, perm 2-byte)");
   LinearArgs a;
   a.codes = codes;
-  a.tags = tags;
   a.perm = perm;
   a.group_off = group_off;
+  a.acodes = acodes;
   a.w = w;
+  a.w_t = w_t;
   a.w_scale = w_scale;
   a.y_prev = y_prev;
   a.y_out = y_out;

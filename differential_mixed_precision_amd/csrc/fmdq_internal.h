@@ -23,6 +23,7 @@ struct QuantizeArgs {
   const float* x_prev;
   int8_t* codes;
   uint8_t* tags;
+  int8_t* acodes;
   uint32_t* bit_hist;
   int64_t rows;
   int32_t K;
@@ -44,10 +45,11 @@ int launch_bucket(const BucketArgs& a, hipStream_t s);
 
 struct LinearArgs {
   const int8_t* codes;
-  const uint8_t* tags;
   const uint16_t* perm;
   const int32_t* group_off;
+  const int8_t* acodes;
   const int8_t* w;
+  const int8_t* w_t;
   const float* w_scale;
   const float* y_prev;
   float* y_out;
@@ -61,6 +63,7 @@ struct LinearArgs {
   double base;
 };
 int launch_linear(const LinearArgs& a, hipStream_t s);
+int launch_pack_weights(int32_t K, int32_t N, const int8_t* w, int8_t* w_t, hipStream_t s);
 int launch_linear_general(const LinearArgs& a, hipStream_t s);
 bool linear_mfma_supported(const LinearArgs& a);
 int launch_linear_mfma(const LinearArgs& a, hipStream_t s);

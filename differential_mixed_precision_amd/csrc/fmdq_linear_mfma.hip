@@ -38,15 +38,16 @@
 //
 // Layout.  Workgroup = 256 threads = 4 waves, output block 128 rows × 128
 // columns, 2 × 2 waves of 64 × 64 (2 × 2 MFMA 32x32x32 int8 tiles each).
-// Codes ([tile][K][T], channel-major) and W ([K][N], row-major) both have the
-// reduction index outermost, and so do their LDS copies: a chunk of 64
-// channels is copied with 16-byte coalesced loads into [channel][row] and
-// [channel][column] tiles (the code shift of a channel is one shift of each
-// 16-byte piece).  Each lane then assembles its 16-byte MFMA fragment (one
-// row or column, 16 consecutive channels) with two ds_read_b64_tr_b8
-// transpose reads.  LDS stages are double-buffered with one barrier per step;
-// the dense loop keeps the global loads of three chunks in flight per thread,
-// the gathered loop fetches perm entries two steps and data one step ahead.
+// The dense operands are stage 1's aligned codes [rows][K] and W^T [N][K],
+// both with the channel innermost: 16-byte copies into [row][channel] LDS
+// tiles and one ds_read_b128 per MFMA fragment.  The gathered operands are
+// the codes ([tile][K][T]) and W ([K][N]) rows of the gathered channels, with
+// the channel outermost: they are copied into [channel][row] and
+// [channel][column] tiles, and each lane assembles its fragment (one row or
+// column, 16 consecutive channels) with two ds_read_b64_tr_b8 transpose
+// reads.  LDS stages are double-buffered with one barrier per step; the next
+// dense chunk's loads are in flight during the MFMAs, and the gathered loop
+// fetches perm entries two steps and data one step ahead.
 #include "fmdq_internal.h"
 
 namespace dstar {
@@ -62,8 +63,9 @@ constexpr int BM = 128;            // rows per workgroup
 constexpr int BN = 128;            // output columns per workgroup
 constexpr int BK = 64;             // channels per dense chunk (2 MFMA k-steps)
 constexpr int KS = 32;             // channels per MFMA k-step (= per gathered step)
-constexpr int SA = BM + 32;        // LDS bytes per channel row of an A tile
-constexpr int SB = BN + 32;        // LDS bytes per channel row of a B tile
+constexpr int SA = BM + 32;        // LDS bytes per channel row of a gathered A tile
+constexpr int SB = BN + 32;        // LDS bytes per channel row of a gathered B tile
+constexpr int SD = BK + 16;        // LDS bytes per row of a dense tile ([row][channel])
 constexpr int kDepth = 2;          // dense chunks whose loads are in flight per thread
 constexpr int kBand = 8;           // row blocks per band of the block order
 constexpr int kTags = DSTAR_FMDQ_NUM_TAGS;
@@ -79,7 +81,7 @@ struct Cfg {
 // LDS carve-up (bytes).  Dense: A0 A1 B0 B1 chunk buffers.  Gathered: two
 // stages of (A: 32 channel rows; B: one 32-row tile per token tile).  The two
 // phases reuse the same bytes.
-constexpr int kDenseBytes = 2 * BK * SA + 2 * BK * SB;     // 40960
+constexpr int kDenseBytes = 2 * BM * SD + 2 * BN * SD;     // 40960
 constexpr int kStageBytes = KS * SA + 4 * KS * SB;         // 25600
 constexpr int kDataBytes = kDenseBytes > 2 * kStageBytes ? kDenseBytes : 2 * kStageBytes;
 constexpr int kOffOff = kDataBytes;                         // int32 [4][65] bin offsets
@@ -90,18 +92,6 @@ constexpr int kOffSteps = kOffBp + 4 * kTags * 8;          // int32 [16] steps p
 constexpr int kOffCum = kOffSteps + kTags * 4;             // int32 [17] cumulative steps
 constexpr int kOffElig = kOffCum + (kTags + 1) * 4;        // int32 [4]
 constexpr int kLdsBytes = kOffElig + 4 * 4;
-
-// Left shift of four packed int8 codes by e (0..6); each result fits int8.
-__device__ __forceinline__ uint32_t shift_codes(uint32_t x, int e) {
-  const uint32_t m = 0x01010101u * ((0xFFu << e) & 0xFFu);
-  return (x << e) & m;
-}
-
-// Decodes a tag byte: step exponent e = 15 − tag, PoT = e + (b − 2).
-__device__ __forceinline__ int tag_e(uint32_t byte) { return DSTAR_FMDQ_TAG_OFFSET - (int)(byte & 15u); }
-__device__ __forceinline__ int tag_pot(uint32_t byte) {
-  return tag_e(byte) + 2 * (int)((byte >> DSTAR_FMDQ_PREC_SHIFT) & 3u);
-}
 
 __device__ __forceinline__ void st_u128(uint8_t* p, uint4 v) {
   *reinterpret_cast<uint4*>(p) = v;
@@ -198,9 +188,8 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   const int64_t n0 = nb * BN;
   const int64_t tile0 = mb * kTiles;
   const int tiles_here = (int)min<int64_t>(kTiles, nt - tile0);
-  // This workgroup's tiles of codes, tags and perm; all of W.
+  // This workgroup's tiles of codes and perm; all of W.
   const rsrc_t r_codes = make_rsrc(a.codes + tile0 * K * T, (uint32_t)(tiles_here * K * T));
-  const rsrc_t r_tags = make_rsrc(a.tags + tile0 * K, (uint32_t)(tiles_here * K));
   const rsrc_t r_perm = make_rsrc(a.perm + tile0 * K, (uint32_t)(tiles_here * K * 2));
   const rsrc_t r_w = make_rsrc(a.w, (uint32_t)(K * N));
 
@@ -217,7 +206,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     const int32_t* o = off_s + i * (kBins + 1);
     // PoT = e + 2·pc ≥ 7  <=>  pc ≥ ceil((7 − e) / 2); bins of group g run
     // from precision code 3 (bin 4g) down to 0 (bin 4g + 3).
-    const int pcmin = max(0, (8 - e) / 2);
+    const int pcmin = max(0, (kAlignedPotMax + 2 - e) / 2);
     rstart[tid] = o[4 * g];
     rcount[tid] = pcmin <= 3 ? o[4 * g + 4 - pcmin] - o[4 * g] : 0;
     unsigned long long b = 0;
@@ -356,57 +345,46 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
       }
   }
 
-  // ---- Dense part: every other channel, natural order, codes shifted by e.
-  // A chunk: per tile, 64 channels × T rows (contiguous in memory) as 16-byte
-  // pieces; B chunk: 64 W rows × 128 columns as 16-byte pieces.
+  // ---- Dense part: every channel with PoT ≤ 6, natural order, from stage 1's
+  // aligned codes (already shifted to units of the base) and W^T.  Both are
+  // row-major with the channel index innermost: a chunk is 128 rows × 64
+  // bytes of each, copied in 16-byte pieces into [row][channel] LDS tiles
+  // (rows padded to 80 bytes), and each MFMA fragment is one ds_read_b128.
   {
-    constexpr int kPiecesA = BK * BM / 16 / kThreads;    // 2
-    constexpr int kPiecesB = BK * BN / 16 / kThreads;    // 2
-    auto Abuf = [&](int b) { return smem + b * BK * SA; };
-    auto Bbuf = [&](int b) { return smem + 2 * BK * SA + b * BK * SB; };
+    constexpr int kPieces = BK / 16;                     // 16-byte pieces per row (4)
+    constexpr int kPiecesA = BM * kPieces / kThreads;    // 2
+    constexpr int kPiecesB = BN * kPieces / kThreads;    // 2
+    auto Abuf = [&](int b) { return smem + b * BM * SD; };
+    auto Bbuf = [&](int b) { return smem + 2 * BM * SD + b * BN * SD; };
     uint4 ra[kDepth][kPiecesA], rbv[kDepth][kPiecesB];
-    uint32_t rtag[kDepth][kPiecesA];
+    const rsrc_t r_ac = make_rsrc(a.acodes + tile0 * T * K, (uint32_t)(tiles_here * T * K));
+    const rsrc_t r_wt = make_rsrc(a.w_t, (uint32_t)(N * K));
     auto load_chunk = [&](int d, int64_t k0) {
 #pragma unroll
       for (int u = 0; u < kPiecesA; ++u) {
         const int p = tid + kThreads * u;
-        const int i = p / (BK * T / 16);
-        const int q = p % (BK * T / 16);
-        const int kk = q / (T / 16);
-        const bool valid = k0 + kk < K;   // tiles past the end lie outside r_codes
-        ra[d][u] = bload16(r_codes, valid ? (uint32_t)((i * K + k0) * T + 16 * q) : kOob);
-        // A zero tag byte (also what an invalid load returns) decodes to
-        // PoT = 15 > 6: the piece contributes nothing to the dense part.
-        rtag[d][u] = __builtin_amdgcn_raw_buffer_load_b8(r_tags, valid ? (uint32_t)(i * K + k0 + kk) : kOob, 0, 0);
+        const int row = p / kPieces, c = p % kPieces;
+        const bool valid = k0 + 16 * c < K;     // rows past the last tile lie outside r_ac
+        ra[d][u] = bload16(r_ac, valid ? (uint32_t)(row * K + k0 + 16 * c) : kOob);
       }
 #pragma unroll
       for (int u = 0; u < kPiecesB; ++u) {
         const int p = tid + kThreads * u;
-        const int kk = p / (BN / 16), c = p % (BN / 16);
-        const int64_t n = n0 + 16 * c;
-        rbv[d][u] = load_w16<VecW>(r_w, (uint32_t)((k0 + kk) * N + n), n, N, k0 + kk < K && n < N);
+        const int col = p / kPieces, c = p % kPieces;
+        const bool valid = k0 + 16 * c < K && n0 + col < N;
+        rbv[d][u] = bload16(r_wt, valid ? (uint32_t)((n0 + col) * K + k0 + 16 * c) : kOob);
       }
     };
     auto store_chunk = [&](int d, int b) {
 #pragma unroll
       for (int u = 0; u < kPiecesA; ++u) {
         const int p = tid + kThreads * u;
-        const int i = p / (BK * T / 16);
-        const int q = p % (BK * T / 16);
-        const int kk = q / (T / 16), sub = q % (T / 16);
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (tag_pot(rtag[d][u]) <= kAlignedPotMax) {
-          const int e = tag_e(rtag[d][u]);
-          v = make_uint4(shift_codes(ra[d][u].x, e), shift_codes(ra[d][u].y, e),
-                         shift_codes(ra[d][u].z, e), shift_codes(ra[d][u].w, e));
-        }
-        st_u128(Abuf(b) + kk * SA + T * i + 16 * sub, v);
+        st_u128(Abuf(b) + (p / kPieces) * SD + 16 * (p % kPieces), ra[d][u]);
       }
 #pragma unroll
       for (int u = 0; u < kPiecesB; ++u) {
         const int p = tid + kThreads * u;
-        const int kk = p / (BN / 16), c = p % (BN / 16);
-        st_u128(Bbuf(b) + kk * SB + 16 * c, rbv[d][u]);
+        st_u128(Bbuf(b) + (p / kPieces) * SD + 16 * (p % kPieces), rbv[d][u]);
       }
     };
     auto compute = [&](int b) {
@@ -414,9 +392,11 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
       for (int ks = 0; ks < BK / KS; ++ks) {
         v4i af[2], bf[2];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) af[rb] = tr_frag<SA>(Abuf(b), KS * ks, 64 * wr + 32 * rb, lane);
+        for (int rb = 0; rb < 2; ++rb)
+          af[rb] = *reinterpret_cast<const v4i*>(Abuf(b) + (64 * wr + 32 * rb + (lane & 31)) * SD + KS * ks + 16 * (lane >> 5));
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) bf[cb] = tr_frag<SB>(Bbuf(b), KS * ks, 64 * wc + 32 * cb, lane);
+        for (int cb = 0; cb < 2; ++cb)
+          bf[cb] = *reinterpret_cast<const v4i*>(Bbuf(b) + (64 * wc + 32 * cb + (lane & 31)) * SD + KS * ks + 16 * (lane >> 5));
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -578,10 +558,12 @@ int launch_t(const LinearArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Handles token tiles of 32 or 64 rows with K a multiple of 4 and W below
-// 2^31 bytes (32-bit buffer offsets).
+// Handles token tiles of 32 or 64 rows, K a multiple of 16 (16-byte rows of
+// the aligned codes and W^T) and W below 2^31 bytes (32-bit buffer offsets),
+// given the aligned codes and W^T.
 bool linear_mfma_supported(const LinearArgs& a) {
-  return (a.T == 32 || a.T == 64) && (a.K % 4) == 0 && (int64_t)a.K * a.N < (int64_t(1) << 31);
+  return a.acodes != nullptr && a.w_t != nullptr && (a.T == 32 || a.T == 64) && (a.K % 16) == 0 &&
+         (int64_t)a.K * a.N < (int64_t(1) << 31);
 }
 
 int launch_linear_mfma(const LinearArgs& a, hipStream_t s) {

@@ -67,6 +67,11 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantizeArgs a, int6
     }
 
     uint32_t tagword = 0;
+    // Aligned codes of the CPT channels, one packed word per row (q·2^e when
+    // PoT ≤ 6, else 0): the 8-bit operand of stage 3's dense GEMM.
+    uint32_t arow[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) arow[t] = 0u;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       // M: largest |Δ| of the sub-channel (QPU stage 1).
@@ -90,6 +95,10 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantizeArgs a, int6
         r = fminf(fmaxf(rintf(r), -pceil), pceil);
         q[t] = (int)r;
       }
+      if (pot <= 6) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) arow[t] |= (((uint32_t)q[t] << e) & 0xFFu) << (8 * c);
+      }
       hist[p >> 1] += 1u;
       const uint32_t tag = (uint32_t)(DSTAR_FMDQ_TAG_OFFSET - e) | ((uint32_t)(p >> 1) << DSTAR_FMDQ_PREC_SHIFT);
       tagword |= tag << (8 * c);
@@ -103,6 +112,19 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantizeArgs a, int6
         o.z = (int)pack4(q[16 * v + 8], q[16 * v + 9], q[16 * v + 10], q[16 * v + 11]);
         o.w = (int)pack4(q[16 * v + 12], q[16 * v + 13], q[16 * v + 14], q[16 * v + 15]);
         dst[v] = o;
+      }
+    }
+    if (a.acodes != nullptr) {
+      int8_t* ap = a.acodes + r0 * K + k;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        if constexpr (CPT == 4) {
+          *reinterpret_cast<uint32_t*>(ap + t * K) = arow[t];
+        } else if constexpr (CPT == 2) {
+          *reinterpret_cast<uint16_t*>(ap + t * K) = (uint16_t)arow[t];
+        } else {
+          ap[t * K] = (int8_t)arow[t];
+        }
       }
     }
     uint8_t* tp = a.tags + tile * K + k;
@@ -148,15 +170,17 @@ int launch_t(const QuantizeArgs& a, hipStream_t s) {
 
 int launch_quantize(const QuantizeArgs& a, hipStream_t s) {
   if (a.rows == 0) return DSTAR_OK;
+  // Channels per thread: as many as keep three waves per SIMD resident
+  // (T·CPT floats of Δ live in registers), limited by K's divisibility.
   const bool vec4 = (a.K % 4) == 0;
   const bool vec2 = (a.K % 2) == 0;
   switch (a.T) {
     case 16:
       return vec4 ? launch_t<16, 4>(a, s) : vec2 ? launch_t<16, 2>(a, s) : launch_t<16, 1>(a, s);
     case 32:
-      return vec4 ? launch_t<32, 4>(a, s) : vec2 ? launch_t<32, 2>(a, s) : launch_t<32, 1>(a, s);
+      return vec2 ? launch_t<32, 2>(a, s) : launch_t<32, 1>(a, s);
     case 64:
-      return vec2 ? launch_t<64, 2>(a, s) : launch_t<64, 1>(a, s);
+      return launch_t<64, 1>(a, s);
     default:
       return set_error(DSTAR_EUNSUPPORTED, "token_tile %d not supported", a.T);
   }

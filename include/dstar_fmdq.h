@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DSTAR_FMDQ_ABI_VERSION 3
+#define DSTAR_FMDQ_ABI_VERSION 4
 
 /* Rule constants (DSTAR §3.1 step 1; readings in the design notes):
  * PCeil of a b-bit sub-channel is 2^(b-2); PoT is capped at POT_MAX so that
@@ -88,9 +88,17 @@ typedef struct {
  *   codes        [n_t][K][T] int8 (out): code of row τT+t, channel k at
  *                codes[(τK + k)T + t]; rows past the end of a ragged last tile
  *                are written 0.  16-byte aligned.
- *   tags         [n_t][K] uint8 (out), 4-byte aligned: bits 0-3 the FPoT tag g = (b-2) - PoT +
- *                15 (ascending g = ascending FPoT; the sub-channel's step is
- *                base * 2^(15-g)), bits 4-5 the precision code b/2 - 1.
+ *   tags         [n_t][K] uint8 (out), 4-byte aligned: bits 0-3 the FPoT tag
+ *                g = (b-2) - PoT + 15 (ascending g = ascending FPoT; the
+ *                sub-channel's step is base * 2^(15-g)), bits 4-5 the
+ *                precision code b/2 - 1.
+ *   acodes       NULL, or [n_t*T][K] int8 row-major (out), 16-byte aligned:
+ *                the shift-aligned operand of stage 3's dense GEMM (DSTAR
+ *                §3.1 step 5: partial sums of different FPoT are aligned by
+ *                left shifts; here the codes are shifted before the multiply
+ *                when the result still fits 8 bits).  acodes[τT+t][k] =
+ *                code * 2^(15-g) if PoT <= 6, else 0 (|value| <= 64); rows
+ *                past a ragged end are 0.
  *   bit_hist     uint32[4] or NULL: counts of sub-channels quantized at
  *                2/4/6/8 bits are ADDED to it (the caller zeroes it).
  * Per sub-channel: M = max |Δ| over the tile's rows; PoT = smallest j in
@@ -99,7 +107,7 @@ typedef struct {
  * fl32(1/base)) * 2^-e)), ±2^(b-2)). */
 int dstar_fmdq_quantize(const dstar_fmdq_params* p, const float* x_t,
                         const float* x_prev, int8_t* codes, uint8_t* tags,
-                        uint32_t* bit_hist, void* stream);
+                        int8_t* acodes, uint32_t* bit_hist, void* stream);
 
 /* Stage 2 — reorder the channels of every token tile by FPoT (DSTAR §3.1
  * step 3; §4.2 QPU stage 4), as a stable counting sort over the 64 bins
@@ -115,15 +123,24 @@ int dstar_fmdq_quantize(const dstar_fmdq_params* p, const float* x_t,
 int dstar_fmdq_bucket(const dstar_fmdq_params* p, const uint8_t* tags,
                       uint16_t* perm, int32_t* group_off, void* stream);
 
+/* Weight preparation, once per layer: w_t[n][k] = w[k][n] (the [out][in]
+ * layout of the weights), the operand of stage 3's dense GEMM.
+ *   w    [K][N] int8 row-major; w_t [N][K] int8 (out).  No alignment
+ *        requirement beyond 16 bytes for both. */
+int dstar_fmdq_pack_weights(int32_t K, int32_t N, const int8_t* w, int8_t* w_t,
+                            void* stream);
+
 /* Stage 3 — grouped int8 GEMM, shift alignment, dequantization and reverse
  * differential (DSTAR §3.1 steps 3 and 5, Fig. 6; §4.2 MPU, inverse
  * quantization and accumulation units; §4.3 reverse differential fused into
  * the GEMM).
  *   N          output channels, a multiple of 4 in [4, 2^20].
- *   codes      from stage 1; tags from stage 1 (4-byte aligned); perm,
- *              group_off ([n_t][65]) from stage 2.  Channel k of group g of tile τ is
- *              multiplied at step 2^(15-g) * base.
+ *   codes      from stage 1; perm, group_off ([n_t][65]) from stage 2.
+ *              Channel k of FPoT group g of tile τ is multiplied at step
+ *              2^(15-g) * base.
+ *   acodes     NULL, or stage 1's aligned codes.
  *   w          [K][N] int8 row-major, 16-byte aligned.
+ *   w_t        NULL, or the [N][K] copy made by dstar_fmdq_pack_weights.
  *   w_scale    [N] float32, per-output-channel weight scale.
  *   y_prev     [rows][N] float32, the cached output Y_{t-1}.
  *   y_out      [rows][N] float32 (out), Y_t; may equal y_prev (in place).
@@ -136,14 +153,17 @@ int dstar_fmdq_bucket(const dstar_fmdq_params* p, const uint8_t* tags,
  *              the layer runs in the per-group kernel (slow; for checking).
  * Per output: S = Σ_g acc_g * 2^(15-g) (an exact integer);
  * y_out = fl32(f64(y_prev) + (f64(S) * f64(base)) * f64(w_scale[n])).
- * The MFMA kernel reads the channels with PoT >= 7 of every FPoT group as the
- * group's prefix in perm; a token tile whose int32 accumulator it cannot
- * prove exact (127 * Σ_k 2^PoT_k >= 2^31) is finished by a per-group path
- * over perm and group_off. */
+ * With acodes and w_t given (T of 32 or 64, K % 16 == 0, K*N < 2^31) the MFMA
+ * kernel runs: acodes x w_t for every sub-channel with PoT <= 6, and the
+ * channels with PoT >= 7 of every FPoT group (the group's prefix in perm)
+ * gathered from codes and w, group by group with left shifts between groups;
+ * a token tile whose int32 accumulator it cannot prove exact
+ * (127 * Σ_k 2^PoT_k >= 2^31) is finished by a per-group path over perm and
+ * group_off.  Otherwise the per-group kernel runs. */
 int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N,
-                      const int8_t* codes, const uint8_t* tags, const uint16_t* perm,
-                      const int32_t* group_off,
-                      const int8_t* w, const float* w_scale,
+                      const int8_t* codes, const uint16_t* perm,
+                      const int32_t* group_off, const int8_t* acodes,
+                      const int8_t* w, const int8_t* w_t, const float* w_scale,
                       const float* y_prev, float* y_out, int32_t* acc_dbg,
                       int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream);
 

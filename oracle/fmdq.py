@@ -208,6 +208,27 @@ def quantize(x_t: np.ndarray, x_prev: np.ndarray, token_tile: int, base: float,
     return codes, tags, hist
 
 
+def aligned_codes(codes: np.ndarray, tags: np.ndarray) -> np.ndarray:
+    """The shift-aligned 8-bit operand of the dense GEMM, row-major [n_t·T][K].
+
+    DSTAR §3.1 ❺ aligns partial sums of different FPoT by left shifts of the
+    FPoT difference.  A code q at step base·2^e is q·2^e in units of the base,
+    and |q·2^e| ≤ 2^PoT; for PoT ≤ 6 that shifted code still fits 8 bits, so
+    it is stored shifted (the alignment done before the multiply).  Codes of
+    sub-channels with PoT ≥ 7 do not fit and are stored as 0 here; they keep
+    their own FPoT groups.  Row τ·T + t, column k holds the code of row t of
+    tile τ; rows past a ragged end are 0.
+    """
+    codes = np.asarray(codes)
+    nt, K, T = codes.shape
+    e = step_exponent(tag_of(tags))                              # [n_t][K]
+    pot = e + (bits_of(tags) - 2)
+    scaled = codes.astype(np.int64) * np.left_shift(np.int64(1), e)[:, :, None]
+    a = np.where((pot <= 6)[:, :, None], scaled, 0)              # [n_t][K][T]
+    assert np.abs(a).max(initial=0) <= 64
+    return np.ascontiguousarray(a.transpose(0, 2, 1).reshape(nt * T, K)).astype(np.int8)
+
+
 def tag_of(tags: np.ndarray) -> np.ndarray:
     """Tag (FPoT group) from a tag byte."""
     return (np.asarray(tags) & 0x0F).astype(np.int64)
@@ -355,4 +376,5 @@ def layer(x_t, x_prev, w, w_scale, y_prev, base, token_tile, k0):
     codes, tags, hist = quantize(x_t, x_prev, token_tile, base, k0)
     perm, off = bucket(tags)
     y = linear(codes, tags, perm, off, w, w_scale, y_prev, base, token_tile)
-    return dict(codes=codes, tags=tags, hist=hist, perm=perm, group_off=off, y=y)
+    return dict(codes=codes, tags=tags, acodes=aligned_codes(codes, tags), hist=hist, perm=perm,
+                group_off=off, y=y)

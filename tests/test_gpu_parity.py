@@ -55,20 +55,24 @@ def gpu_layer(dm, d, dbg=None, inplace=False, y_prev_np=None):
     p = dm.make_params(rows, K, T, float(d["base"]), d["k0"], d["tokens_per_seq"])
     codes = torch.full((nt, K, T), 90, dtype=torch.int8, device=dev)
     tags = torch.full((nt, K), 0xEE, dtype=torch.uint8, device=dev)
+    acodes = torch.full((nt * T, K), 77, dtype=torch.int8, device=dev)
+    w_t = torch.full((N, K), 55, dtype=torch.int8, device=dev)
     hist = torch.zeros(4, dtype=torch.int32, device=dev)
     perm = torch.full((nt, K), -1, dtype=torch.int16, device=dev)
     off = torch.full((nt, 65), -7, dtype=torch.int32, device=dev)
     y1 = y0 if inplace else torch.full((rows, N), float("nan"), dtype=torch.float32, device=dev)
-    dm.quantize(p, x_t, x_p, codes, tags, hist)
+    dm.pack_weights(K, N, w, w_t)
+    dm.quantize(p, x_t, x_p, codes, tags, acodes, hist)
     dm.bucket(p, tags, perm, off)
-    dm.linear(p, N, codes, tags, perm, off, w, ws, y0, y1)
-    out = dict(codes=codes, tags=tags, hist=hist, perm=perm, group_off=off, y=y1)
+    dm.linear(p, N, codes, perm, off, acodes, w, w_t, ws, y0, y1)
+    out = dict(codes=codes, tags=tags, acodes=acodes, w_t=w_t, hist=hist, perm=perm, group_off=off,
+               y=y1)
     if dbg is not None:
         lo, hi = dbg
         acc = torch.full((hi - lo, 16, T, N), 0x7777, dtype=torch.int32, device=dev)
         y0b = torch.from_numpy(y_np).to(dev)
         y2 = torch.full((rows, N), float("nan"), dtype=torch.float32, device=dev)
-        dm.linear(p, N, codes, tags, perm, off, w, ws, y0b, y2, acc, lo, hi)
+        dm.linear(p, N, codes, perm, off, acodes, w, w_t, ws, y0b, y2, acc, lo, hi)
         out.update(acc=acc, y_dbg=y2)
     torch.cuda.synchronize()
     out = {k: v.cpu().numpy() for k, v in out.items()}
@@ -92,9 +96,12 @@ def check_y(y_gpu, y_orc, y_prev, what=""):
     assert exact == y_gpu.size, f"{what}: {y_gpu.size - exact} outputs differ from the oracle"
 
 
-def check_integer_stages(g, codes, tags, hist, perm, off, what=""):
+def check_integer_stages(g, codes, tags, hist, perm, off, what="", w=None):
     np.testing.assert_array_equal(g["codes"], codes, err_msg=f"{what}: codes")
     np.testing.assert_array_equal(g["tags"], tags, err_msg=f"{what}: tags")
+    np.testing.assert_array_equal(g["acodes"], fmdq.aligned_codes(codes, tags), err_msg=f"{what}: aligned codes")
+    if w is not None:
+        np.testing.assert_array_equal(g["w_t"], w.T, err_msg=f"{what}: packed weights")
     np.testing.assert_array_equal(g["hist"].astype(np.int64), hist, err_msg=f"{what}: bit histogram")
     np.testing.assert_array_equal(g["perm"], perm, err_msg=f"{what}: bucket order")
     np.testing.assert_array_equal(g["group_off"], off, err_msg=f"{what}: group offsets")
@@ -107,7 +114,7 @@ def full_compare(dm, d, inplace=False):
     g = gpu_layer(dm, d, dbg=(0, nt), inplace=inplace)
     codes, tags, hist = fmdq.quantize(d["x_t"], d["x_prev"], T, d["base"], d["k0"])
     perm, off = fmdq.bucket(tags)
-    check_integer_stages(g, codes, tags, hist, perm, off, d["name"])
+    check_integer_stages(g, codes, tags, hist, perm, off, d["name"], d["w"])
     y, accs = fmdq.linear(codes, tags, perm, off, d["w"], d["w_scale"], d["y_prev"], d["base"], T,
                           return_acc=True)
     for tau in range(nt):
@@ -235,7 +242,7 @@ def test_full_size_workloads(dm, cfg, layer):
     codes, tags, hist = fmdq.quantize(d["x_t"], d["x_prev"], T, d["base"], d["k0"])
     perm, off = fmdq.bucket(tags)
     log(f"  oracle quantize+bucket done {time.time() - t0:.1f}s")
-    check_integer_stages(g, codes, tags, hist, perm, off, d["name"])
+    check_integer_stages(g, codes, tags, hist, perm, off, d["name"], d["w"])
     y, accs = fmdq.linear(codes, tags, perm, off, d["w"], d["w_scale"], d["y_prev"], d["base"], T,
                           tiles=sample, return_acc=True)
     for tau in (nt - 2, nt - 1):

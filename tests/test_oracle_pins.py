@@ -427,3 +427,29 @@ def test_code_rounding_is_half_to_even():
     codes, tags, _ = fmdq.quantize(x_t, x_prev, T, base, k0)
     assert int(fmdq.bits_of(tags)[0, 0]) == 4 and int(fmdq.step_exponent(fmdq.tag_of(tags))[0, 0]) == 2
     np.testing.assert_array_equal(codes[0, 0, :9], [round(v) for v in halves[:9]])
+
+
+# ------------------------------------------------------------------ P13 ------
+@pytest.mark.parametrize("seed,rows,K,N,T", [(31, 96, 64, 24, 32), (32, 70, 40, 8, 32), (33, 128, 36, 12, 64)])
+def test_aligned_codes_split_S_into_8_bit_part_and_wide_groups(seed, rows, K, N, T):
+    """S = (aligned codes) @ W + Σ over PoT ≥ 7 channels of q·2^e·W, exactly;
+    the aligned codes fit int8, equal q·2^e where PoT ≤ 6 and 0 elsewhere."""
+    d = wl.make_custom(rows, K, N, T, seed=seed, heavy=0.3, c_range=(0.5, 64.0))
+    codes, tags, _ = fmdq.quantize(d["x_t"], d["x_prev"], T, d["base"], d["k0"])
+    a = fmdq.aligned_codes(codes, tags)
+    nt = codes.shape[0]
+    assert a.shape == (nt * T, K) and a.dtype == np.int8
+    e = fmdq.step_exponent(fmdq.tag_of(tags))
+    pot = e + fmdq.bits_of(tags) - 2
+    assert (pot > 6).any() and (pot <= 6).any()
+    perm, off = fmdq.bucket(tags)
+    w = d["w"].astype(np.int64)
+    for tau in range(nt):
+        at = a[tau * T:(tau + 1) * T].astype(np.int64)                     # [T][K]
+        qt = codes[tau].T.astype(np.int64)                                   # [T][K]
+        wide = pot[tau] > 6
+        np.testing.assert_array_equal(at[:, wide], 0)
+        np.testing.assert_array_equal(at[:, ~wide], qt[:, ~wide] << e[tau][~wide])
+        wide_part = np.matmul(qt[:, wide] << e[tau][wide], w[wide])
+        s = fmdq.shift_combine(fmdq.group_accumulators(codes[tau], perm[tau], off[tau], d["w"]))
+        np.testing.assert_array_equal(np.matmul(at, w) + wide_part, s)
