@@ -36,18 +36,18 @@
 // group with PoT ≥ 7 are a prefix of the group in perm, found from the bin
 // offsets alone; the gathered steps read perm directly.
 //
-// Layout.  Workgroup = 256 threads = 4 waves, output block 128 rows × 128
-// columns, 2 × 2 waves of 64 × 64 (2 × 2 MFMA 32x32x32 int8 tiles each).
-// The dense operands are stage 1's aligned codes [rows][K] and W^T [N][K],
-// both with the channel innermost: 16-byte copies into [row][channel] LDS
-// tiles and one ds_read_b128 per MFMA fragment.  The gathered operands are
-// the codes ([tile][K][T]) and W ([K][N]) rows of the gathered channels, with
-// the channel outermost: they are copied into [channel][row] and
-// [channel][column] tiles, and each lane assembles its fragment (one row or
-// column, 16 consecutive channels) with two ds_read_b64_tr_b8 transpose
-// reads.  LDS stages are double-buffered with one barrier per step; the next
-// dense chunk's loads are in flight during the MFMAs, and the gathered loop
-// fetches perm entries two steps and data one step ahead.
+// Layout.  Workgroup = 256 threads = 4 waves, output block 128 rows × 256
+// columns; wave w owns all 128 rows and columns 64w .. 64w+63 (4 × 2 MFMA
+// 32x32x32 int8 tiles).  Dense part: the 128 rows of stage 1's aligned codes
+// ([rows][K], channel innermost) are shared by the four waves through LDS
+// ([row][channel] tiles, one ds_read_b128 per fragment); each wave streams its
+// own W^T fragments ([N][K], channel innermost) from global memory straight
+// into registers, one chunk ahead.  Gathered part: the codes ([tile][K][T])
+// and W ([K][N]) rows of the gathered channels have the channel outermost;
+// they are staged as [channel][row] and [channel][column] LDS tiles and each
+// lane assembles its fragment (one row or column, 16 consecutive channels)
+// with two ds_read_b64_tr_b8 transpose reads; perm entries are fetched two
+// steps and data one step ahead.
 #include "fmdq_internal.h"
 
 namespace dstar {
@@ -59,31 +59,35 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 
 constexpr int kThreads = 256;
+constexpr int kWaves = 4;
 constexpr int BM = 128;            // rows per workgroup
-constexpr int BN = 128;            // output columns per workgroup
+constexpr int WN = 64;             // output columns per wave
+constexpr int BN = kWaves * WN;    // output columns per workgroup (256)
+constexpr int RB = BM / 32;        // 32-row MFMA blocks per wave (4)
+constexpr int CB = WN / 32;        // 32-column MFMA blocks per wave (2)
 constexpr int BK = 64;             // channels per dense chunk (2 MFMA k-steps)
 constexpr int KS = 32;             // channels per MFMA k-step (= per gathered step)
-constexpr int SA = BM + 32;        // LDS bytes per channel row of a gathered A tile
+constexpr int SA = BM + 32;        // LDS bytes per channel row of the gathered A tile
 constexpr int SB = BN + 32;        // LDS bytes per channel row of a gathered B tile
-constexpr int SD = BK + 16;        // LDS bytes per row of a dense tile ([row][channel])
-constexpr int kDepth = 2;          // dense chunks whose loads are in flight per thread
-constexpr int kBand = 8;           // row blocks per band of the block order
 constexpr int kTags = DSTAR_FMDQ_NUM_TAGS;
 constexpr int kBins = DSTAR_FMDQ_NUM_BINS;
 constexpr int kAlignedPotMax = 6;  // q·2^e fits int8 when PoT ≤ 6
 constexpr uint64_t kBoundLimit = 2147483647ull / 127ull;  // Σ 2^PoT limit
+constexpr int kBand = 8;           // row blocks per band of the block order
 
 template <int T>
 struct Cfg {
   static constexpr int kTiles = BM / T;   // token tiles per workgroup
 };
 
-// LDS carve-up (bytes).  Dense: A0 A1 B0 B1 chunk buffers.  Gathered: two
-// stages of (A: 32 channel rows; B: one 32-row tile per token tile).  The two
-// phases reuse the same bytes.
-constexpr int kDenseBytes = 2 * BM * SD + 2 * BN * SD;     // 40960
-constexpr int kStageBytes = KS * SA + 4 * KS * SB;         // 25600
-constexpr int kDataBytes = kDenseBytes > 2 * kStageBytes ? kDenseBytes : 2 * kStageBytes;
+// LDS carve-up (bytes).  Dense: kStages stages of (A 128 rows + B 256 rows)
+// × 64 bytes.  Gathered: one stage of (A: 32 channel rows; B: one 32-row tile
+// per token tile).  The two phases reuse the same bytes.
+constexpr int kStages = 3;
+constexpr int kStageDense = (BM + BN) * BK;                // 24576
+constexpr int kDenseBytes = kStages * kStageDense;         // 73728
+constexpr int kStageBytes = KS * SA + 4 * KS * SB;         // 41984
+constexpr int kDataBytes = kDenseBytes > kStageBytes ? kDenseBytes : kStageBytes;
 constexpr int kOffOff = kDataBytes;                         // int32 [4][65] bin offsets
 constexpr int kOffRs = kOffOff + 4 * (kBins + 1) * 4;      // int32 [4][16] prefix starts
 constexpr int kOffRc = kOffRs + 4 * kTags * 4;             // int32 [4][16] prefix lengths
@@ -103,7 +107,13 @@ __device__ __forceinline__ void st_u128(uint8_t* p, uint4 v) {
 // loads still in flight instead of waiting for all of them.
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void* lds_ptr;
 constexpr uint32_t kOob = 0x80000000u;
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; the unused counters at their maximum): wait until no
+// vector-memory load is in flight, or at most one dense chunk's six loads.
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitVmChunk = 0x0F76;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
@@ -111,6 +121,10 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
 __device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
   const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ v4i bload16v(rsrc_t r, uint32_t off) {
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return v4i{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
 }
 __device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
@@ -152,8 +166,7 @@ __device__ __forceinline__ void shift_acc(v16i& acc, int s) {
 template <int T, bool VecW>
 __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, int32_t row_blocks,
                                                                   int32_t col_blocks) {
-  using C = Cfg<T>;
-  constexpr int kTiles = C::kTiles;
+  constexpr int kTiles = Cfg<T>::kTiles;
   extern __shared__ __align__(16) uint8_t smem[];
   int32_t* off_s = reinterpret_cast<int32_t*>(smem + kOffOff);          // [kTiles][65]
   int32_t* rstart = reinterpret_cast<int32_t*>(smem + kOffRs);          // [kTiles][16]
@@ -166,9 +179,10 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
+  const int li = lane & 31, h = lane >> 5;
   const int64_t K = a.K, N = a.N;
   const int64_t nt = n_tiles(a.rows, T);
+
   // Block order.  Workgroups are dealt to the 8 XCDs round-robin (XCD =
   // blockIdx % 8), each with its own L2.  XCD x takes a contiguous range of a
   // banded order of the (row block, column block) grid: bands of kBand row
@@ -186,12 +200,15 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     nb = Lb / hgt;
   }
   const int64_t n0 = nb * BN;
+  const int64_t nw = n0 + WN * wave;      // this wave's first column
   const int64_t tile0 = mb * kTiles;
   const int tiles_here = (int)min<int64_t>(kTiles, nt - tile0);
-  // This workgroup's tiles of codes and perm; all of W.
+  // This workgroup's tiles of codes, aligned codes and perm; all of W, W^T.
   const rsrc_t r_codes = make_rsrc(a.codes + tile0 * K * T, (uint32_t)(tiles_here * K * T));
   const rsrc_t r_perm = make_rsrc(a.perm + tile0 * K, (uint32_t)(tiles_here * K * 2));
+  const rsrc_t r_ac = make_rsrc(a.acodes + tile0 * T * K, (uint32_t)(tiles_here * T * K));
   const rsrc_t r_w = make_rsrc(a.w, (uint32_t)(K * N));
+  const rsrc_t r_wt = make_rsrc(a.w_t, (uint32_t)(N * K));
 
   // ---- Meta: per tile and FPoT group, the prefix of the group (in perm)
   // whose channels have PoT ≥ 7, and the exactness bound Σ_k 2^PoT_k.
@@ -237,37 +254,31 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   __syncthreads();
   const int nsteps = cum[kTags];
 
-  v16i acc[2][2];
+  v16i acc[RB][CB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0;
-
-  // Tile of each of this wave's two 32-row MFMA blocks.
-  int rb_tile[2];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) rb_tile[rb] = (64 * wr + 32 * rb) / T;
 
   // ---- Gathered FPoT groups, Horner form: ascending tag = descending step.
   // Step f of the workgroup covers entries 32·s .. 32·s + 31 of group g's
   // prefix in every tile.  Thread roles: A piece (tile iA, entry jA, 16-byte
   // piece subA of the channel's T codes); B pieces (entry jB, columns
-  // n0 + 16·c16 .. +15) of every tile.
+  // n0 + 16·cB .. +15 and n0 + 128 + 16·cB .. +15) of every tile.
   {
     constexpr int kPieces = T / 16;
     const int iA = tid / (KS * kPieces), jA = (tid / kPieces) % KS, subA = tid % kPieces;
-    const int jB = tid >> 3, c16 = tid & 7;
+    const int jB = tid >> 3, cB = tid & 7;
     auto step_group = [&](int f, int& g, int& s) {
       g = 0;
       while (cum[g + 1] <= f) ++g;
       s = f - cum[g];
     };
-    auto stage = [&](int b) { return smem + b * kStageBytes; };
     // Entries: the channel id (low 16 bits) and a valid flag (bit 16).
     uint32_t eA, eB[kTiles];
-    uint4 dA, dB[kTiles];
+    uint4 dA, dB[kTiles][2];
     auto entry = [&](int i, int g, int j) -> uint32_t {
       const int cnt = eligible[i] ? rcount[i * kTags + g] : 0;
       const bool valid = j < cnt;
@@ -288,193 +299,201 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
 #pragma unroll
       for (int i = 0; i < kTiles; ++i) {
         const uint32_t ch = eB[i] & 0xFFFFu;
-        const int64_t n = n0 + 16 * c16;
-        dB[i] = load_w16<VecW>(r_w, (uint32_t)(ch * N + n), n, N, (eB[i] >> 16) && n < N);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int64_t n = n0 + 128 * u + 16 * cB;
+          dB[i][u] = load_w16<VecW>(r_w, (uint32_t)(ch * N + n), n, N, (eB[i] >> 16) && n < N);
+        }
       }
     };
-    auto store = [&](int b) {
-      uint8_t* st = stage(b);
-      st_u128(st + jA * SA + T * iA + 16 * subA, dA);
+    auto store = [&]() {
+      st_u128(smem + jA * SA + T * iA + 16 * subA, dA);
 #pragma unroll
-      for (int i = 0; i < kTiles; ++i) st_u128(st + KS * SA + i * KS * SB + jB * SB + 16 * c16, dB[i]);
+      for (int i = 0; i < kTiles; ++i)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          st_u128(smem + KS * SA + i * KS * SB + jB * SB + 128 * u + 16 * cB, dB[i][u]);
     };
-    int prev_e[2] = {-1, -1};
+    int prev_e[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) prev_e[rb] = -1;
     if (nsteps > 0) {
       entries(0);
       data();
       if (nsteps > 1) entries(1);
-      store(0);
-      __syncthreads();
       for (int f = 0; f < nsteps; ++f) {
-        const int b = f & 1;
-        if (f + 1 < nsteps) data();
+        __syncthreads();                 // the previous step's fragments are read
+        store();
+        __syncthreads();
+        if (f + 1 < nsteps) data();      // entries of step f+1 arrived one step ago
         if (f + 2 < nsteps) entries(f + 2);
         int g, s;
         step_group(f, g, s);
         const int e = DSTAR_FMDQ_TAG_OFFSET - g;
-        const uint8_t* st = stage(b);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          const int i = rb_tile[rb];
+        for (int rb = 0; rb < RB; ++rb) {
+          const int i = (32 * rb) / T;
           const int cnt = eligible[i] ? rcount[i * kTags + g] : 0;
           if (KS * s >= cnt) continue;
           if (s == 0) {
             if (prev_e[rb] >= 0) {
 #pragma unroll
-              for (int cb = 0; cb < 2; ++cb) shift_acc(acc[rb][cb], prev_e[rb] - e);
+              for (int cb = 0; cb < CB; ++cb) shift_acc(acc[rb][cb], prev_e[rb] - e);
             }
             prev_e[rb] = e;
           }
-          const v4i af = tr_frag<SA>(st, 0, 64 * wr + 32 * rb, lane);
+          const v4i af = tr_frag<SA>(smem, 0, 32 * rb, lane);
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb) {
-            const v4i bf = tr_frag<SB>(st + KS * SA + i * KS * SB, 0, 64 * wc + 32 * cb, lane);
+          for (int cb = 0; cb < CB; ++cb) {
+            const v4i bf = tr_frag<SB>(smem + KS * SA + i * KS * SB, 0, WN * wave + 32 * cb, lane);
             acc[rb][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf, acc[rb][cb], 0, 0, 0);
           }
         }
-        if (f + 1 < nsteps) store(b ^ 1);
-        __syncthreads();
       }
     }
     // Bring the gathered groups to units of the base (step 2^0).
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
       if (prev_e[rb] > 0) {
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) shift_acc(acc[rb][cb], prev_e[rb]);
+        for (int cb = 0; cb < CB; ++cb) shift_acc(acc[rb][cb], prev_e[rb]);
       }
   }
 
-  // ---- Dense part: every channel with PoT ≤ 6, natural order, from stage 1's
-  // aligned codes (already shifted to units of the base) and W^T.  Both are
-  // row-major with the channel index innermost: a chunk is 128 rows × 64
-  // bytes of each, copied in 16-byte pieces into [row][channel] LDS tiles
-  // (rows padded to 80 bytes), and each MFMA fragment is one ds_read_b128.
+  // ---- Dense part: every channel with PoT ≤ 6, natural order, 64 channels
+  // per chunk through a ring of kStages LDS stages filled by direct
+  // global-to-LDS loads (no registers): A = the 128 rows of aligned codes,
+  // shared by the four waves; B = each wave's 64 columns of W^T.  Both tiles
+  // are [row][64 channels] with the 16-byte columns XOR-swizzled by row,
+  // (column ^ (row / 4) % 4), so the fragment reads (one ds_read_b128) are
+  // free of bank conflicts.  A direct load writes lane l's 16 bytes at
+  // base + 16·l: one wave instruction fills 16 rows.
   {
-    constexpr int kPieces = BK / 16;                     // 16-byte pieces per row (4)
-    constexpr int kPiecesA = BM * kPieces / kThreads;    // 2
-    constexpr int kPiecesB = BN * kPieces / kThreads;    // 2
-    auto Abuf = [&](int b) { return smem + b * BM * SD; };
-    auto Bbuf = [&](int b) { return smem + 2 * BM * SD + b * BN * SD; };
-    uint4 ra[kDepth][kPiecesA], rbv[kDepth][kPiecesB];
-    const rsrc_t r_ac = make_rsrc(a.acodes + tile0 * T * K, (uint32_t)(tiles_here * T * K));
-    const rsrc_t r_wt = make_rsrc(a.w_t, (uint32_t)(N * K));
-    auto load_chunk = [&](int d, int64_t k0) {
+    auto stageA = [&](int st) { return smem + st * kStageDense; };
+    auto stageB = [&](int st, int w) { return smem + st * kStageDense + BM * BK + w * WN * BK; };
+    const int r16 = lane >> 2;                       // row of this lane within a 16-row group
+    const int c16 = (lane & 3) ^ ((r16 >> 2) & 3);   // global 16-byte column it loads
+    // Each wave issues 2 A and 4 B instructions per chunk.
+    auto issue = [&](int64_t c, int st) {
+      const int64_t k0 = c * BK;
 #pragma unroll
-      for (int u = 0; u < kPiecesA; ++u) {
-        const int p = tid + kThreads * u;
-        const int row = p / kPieces, c = p % kPieces;
-        const bool valid = k0 + 16 * c < K;     // rows past the last tile lie outside r_ac
-        ra[d][u] = bload16(r_ac, valid ? (uint32_t)(row * K + k0 + 16 * c) : kOob);
+      for (int j = 0; j < 2; ++j) {
+        const int row = 16 * (2 * wave + j) + r16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_ac, (lds_ptr)(stageA(st) + 1024 * (2 * wave + j)), 16,
+                                                 (uint32_t)(row * K + k0 + 16 * c16), 0, 0, 0);
       }
 #pragma unroll
-      for (int u = 0; u < kPiecesB; ++u) {
-        const int p = tid + kThreads * u;
-        const int col = p / kPieces, c = p % kPieces;
-        const bool valid = k0 + 16 * c < K && n0 + col < N;
-        rbv[d][u] = bload16(r_wt, valid ? (uint32_t)((n0 + col) * K + k0 + 16 * c) : kOob);
+      for (int j = 0; j < 4; ++j) {
+        const int64_t n = nw + 16 * j + r16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_wt, (lds_ptr)(stageB(st, wave) + 1024 * j), 16,
+                                                 n < N ? (uint32_t)(n * K + k0 + 16 * c16) : kOob, 0, 0, 0);
       }
     };
-    auto store_chunk = [&](int d, int b) {
-#pragma unroll
-      for (int u = 0; u < kPiecesA; ++u) {
-        const int p = tid + kThreads * u;
-        st_u128(Abuf(b) + (p / kPieces) * SD + 16 * (p % kPieces), ra[d][u]);
-      }
-#pragma unroll
-      for (int u = 0; u < kPiecesB; ++u) {
-        const int p = tid + kThreads * u;
-        st_u128(Bbuf(b) + (p / kPieces) * SD + 16 * (p % kPieces), rbv[d][u]);
-      }
+    auto frag = [&](const uint8_t* tile, int row, int c) {
+      return *reinterpret_cast<const v4i*>(tile + row * BK + 16 * (c ^ ((row >> 2) & 3)));
     };
-    auto compute = [&](int b) {
+    auto compute = [&](int st) {
 #pragma unroll
       for (int ks = 0; ks < BK / KS; ++ks) {
-        v4i af[2], bf[2];
+        v4i af[RB], bf[CB];
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          af[rb] = *reinterpret_cast<const v4i*>(Abuf(b) + (64 * wr + 32 * rb + (lane & 31)) * SD + KS * ks + 16 * (lane >> 5));
+        for (int rb = 0; rb < RB; ++rb) af[rb] = frag(stageA(st), 32 * rb + li, 2 * ks + h);
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-          bf[cb] = *reinterpret_cast<const v4i*>(Bbuf(b) + (64 * wc + 32 * cb + (lane & 31)) * SD + KS * ks + 16 * (lane >> 5));
+        for (int cb = 0; cb < CB; ++cb) bf[cb] = frag(stageB(st, wave), 32 * cb + li, 2 * ks + h);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-          for (int cb = 0; cb < 2; ++cb)
+          for (int cb = 0; cb < CB; ++cb)
             acc[rb][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[rb], bf[cb], acc[rb][cb], 0, 0, 0);
       }
     };
 
-    const int64_t nchunks = (K + BK - 1) / BK;
+    const int64_t nchunks = K / BK;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // no other vector loads in flight
+    __syncthreads();                        // the gathered steps are done with LDS
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d)
-      if (d < nchunks) load_chunk(d, d * BK);
-    store_chunk(0, 0);
-    __syncthreads();
-    for (int64_t c0 = 0; c0 < nchunks; c0 += kDepth) {
-#pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        const int64_t c = c0 + d;
-        if (c < nchunks) {
-          if (c + kDepth < nchunks) load_chunk(d, (c + kDepth) * BK);
-          compute((int)(c & 1));
-          if (c + 1 < nchunks) store_chunk((d + 1) % kDepth, (int)((c + 1) & 1));
-          __syncthreads();
-        }
+    for (int c = 0; c < kStages - 1; ++c)
+      if (c < nchunks) issue(c, c);
+    for (int64_t c = 0; c < nchunks; ++c) {
+      // Chunk c's loads are done once at most one later chunk is in flight.
+      // A bare s_barrier then makes every wave's part of chunk c visible and
+      // guarantees every wave is done with chunk c - 1 (whose stage the next
+      // loads overwrite).  (__syncthreads would also wait for the loads still
+      // in flight, which is what the stages are there to avoid.)  The empty
+      // asm statements keep the compiler from moving LDS reads across.
+      if (c + 1 < nchunks) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmChunk);
+      } else {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
       }
+      __asm__ __volatile__("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      __asm__ __volatile__("" ::: "memory");
+      if (c + kStages - 1 < nchunks) issue(c + kStages - 1, (int)((c + kStages - 1) % kStages));
+      compute((int)(c % kStages));
     }
   }
 
   // ---- Epilogue: dequantize, add the cached output, store (float64 combine).
-  // Y is streamed once, so it bypasses the caches that hold W and the codes;
-  // every load of the cached output is issued before the first store.
+  // Y is streamed once: its loads and stores are non-temporal so they do not
+  // evict W and the codes from the caches.  In interior blocks the 32 loads
+  // of one 32-row block of the wave are issued before their stores.  Offsets
+  // are 32-bit, relative to this workgroup's first row.
   const double base = a.base;
-  const int h = lane >> 5, li = lane & 31;
   bool all_eligible = true;
 #pragma unroll
   for (int i = 0; i < kTiles; ++i) all_eligible = all_eligible && eligible[i];
-  const bool interior = all_eligible && (tile0 * T + BM <= a.rows) && (n0 + BN <= N);
+  const bool interior = all_eligible && (tile0 * T + BM <= a.rows) && (nw + WN <= N);
+  double ws[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int64_t n = nw + 32 * cb + li;
+    ws[cb] = n < N ? (double)a.w_scale[n] : 0.0;
+  }
   if (interior) {
-    float yp[2][2][16];
+    constexpr int kNt = 2;   // aux bit: non-temporal
+    const rsrc_t r_yp = make_rsrc(a.y_prev + tile0 * T * N, (uint32_t)(BM * N * 4));
+    const rsrc_t r_yo = make_rsrc(a.y_out + tile0 * T * N, (uint32_t)(BM * N * 4));
+    const uint32_t lane_off = (uint32_t)(((4 * h) * N + nw + li) * 4);
+    const uint32_t row4 = (uint32_t)(N * 4);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int rb = 0; rb < RB; ++rb) {
+      float yp[CB][16];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = tile0 * T + 64 * wr + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
-          yp[rb][cb][r] = __builtin_nontemporal_load(a.y_prev + row * N + n0 + 64 * wc + 32 * cb + li);
-        }
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int64_t n = n0 + 64 * wc + 32 * cb + li;
-      const double ws = (double)a.w_scale[n];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t row = tile0 * T + 64 * wr + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
-          const double d = __dmul_rn(__dmul_rn((double)acc[rb][cb][r], base), ws);
-          __builtin_nontemporal_store((float)__dadd_rn((double)yp[rb][cb][r], d), a.y_out + row * N + n);
+          const uint32_t off = lane_off + (uint32_t)(32 * rb + 8 * (r >> 2) + (r & 3)) * row4 + 128 * cb;
+          yp[cb][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_yp, off, 0, kNt));
         }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t off = lane_off + (uint32_t)(32 * rb + 8 * (r >> 2) + (r & 3)) * row4 + 128 * cb;
+          const double d = __dmul_rn(__dmul_rn((double)acc[rb][cb][r], base), ws[cb]);
+          const float y = (float)__dadd_rn((double)yp[cb][r], d);
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, y), r_yo, off, 0, kNt);
+        }
+      // keep each row block's loads, math and stores together (bounds the
+      // registers the epilogue holds at once)
+      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      const int64_t n = n0 + 64 * wc + 32 * cb + li;
+    for (int cb = 0; cb < CB; ++cb) {
+      const int64_t n = nw + 32 * cb + li;
       if (n >= N) continue;
-      const double ws = (double)a.w_scale[n];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int i = rb_tile[rb];
+      for (int rb = 0; rb < RB; ++rb) {
+        const int i = (32 * rb) / T;
         if (!eligible[i]) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = 64 * wr + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
-          const int64_t grow = tile0 * T + row;
+          const int64_t grow = tile0 * T + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
           if (grow >= a.rows) continue;
           const int64_t idx = grow * N + n;
-          const double d = __dmul_rn(__dmul_rn((double)acc[rb][cb][r], base), ws);
+          const double d = __dmul_rn(__dmul_rn((double)acc[rb][cb][r], base), ws[cb]);
           a.y_out[idx] = (float)__dadd_rn((double)a.y_prev[idx], d);
         }
       }
@@ -482,50 +501,49 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   }
 
   // ---- Ineligible tiles: exact scalar path over the FPoT groups in perm
-  // order, int32 group sums shifted into int64.
+  // order, int32 group sums shifted into int64.  Thread = one column.
   for (int i = 0; i < tiles_here; ++i) {
     if (eligible[i]) continue;
     const int64_t tau = tile0 + i;
-    constexpr int kRowSets = kThreads / BN;           // 2
-    constexpr int kRows = T / kRowSets;               // rows per thread
-    const int64_t n = n0 + (tid % BN);
-    const int t0 = (tid / BN) * kRows;
+    const int64_t n = n0 + tid;
     if (n >= N) continue;
     const int32_t* off = off_s + i * (kBins + 1);
     const uint16_t* pm = a.perm + tau * K;
     const int8_t* cd = a.codes + tau * K * T;
-    int64_t sum[kRows];
+    const double wsn = (double)a.w_scale[n];
+    for (int t0 = 0; t0 < T; t0 += 32) {
+      int64_t sum[32];
 #pragma unroll
-    for (int t = 0; t < kRows; ++t) sum[t] = 0;
-    for (int g = 0; g < kTags; ++g) {
-      const int lo = off[4 * g], hi = off[4 * g + 4];
-      if (lo == hi) continue;
-      int32_t gs[kRows];
+      for (int t = 0; t < 32; ++t) sum[t] = 0;
+      for (int g = 0; g < kTags; ++g) {
+        const int lo = off[4 * g], hi = off[4 * g + 4];
+        if (lo == hi) continue;
+        int32_t gs[32];
 #pragma unroll
-      for (int t = 0; t < kRows; ++t) gs[t] = 0;
-      for (int j = lo; j < hi; ++j) {
-        const int64_t k = pm[j];
-        const int32_t wv = (int32_t)a.w[k * N + n];
-        const int4* c4 = reinterpret_cast<const int4*>(cd + k * T + t0);
+        for (int t = 0; t < 32; ++t) gs[t] = 0;
+        for (int j = lo; j < hi; ++j) {
+          const int64_t k = pm[j];
+          const int32_t wv = (int32_t)a.w[k * N + n];
+          const int4* c4 = reinterpret_cast<const int4*>(cd + k * T + t0);
 #pragma unroll
-        for (int v = 0; v < kRows / 16; ++v) {
-          const int4 c = c4[v];
-          const int words[4] = {c.x, c.y, c.z, c.w};
+          for (int v = 0; v < 2; ++v) {
+            const int4 c = c4[v];
+            const int words[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
-          for (int b = 0; b < 16; ++b) gs[16 * v + b] += (int32_t)(int8_t)(words[b >> 2] >> (8 * (b & 3))) * wv;
+            for (int b = 0; b < 16; ++b) gs[16 * v + b] += (int32_t)(int8_t)(words[b >> 2] >> (8 * (b & 3))) * wv;
+          }
         }
+#pragma unroll
+        for (int t = 0; t < 32; ++t) sum[t] += (int64_t)gs[t] << (DSTAR_FMDQ_TAG_OFFSET - g);
       }
 #pragma unroll
-      for (int t = 0; t < kRows; ++t) sum[t] += (int64_t)gs[t] << (DSTAR_FMDQ_TAG_OFFSET - g);
-    }
-    const double ws = (double)a.w_scale[n];
-#pragma unroll
-    for (int t = 0; t < kRows; ++t) {
-      const int64_t grow = tau * T + t0 + t;
-      if (grow >= a.rows) continue;
-      const int64_t idx = grow * N + n;
-      const double d = __dmul_rn(__dmul_rn((double)sum[t], base), ws);
-      a.y_out[idx] = (float)__dadd_rn((double)a.y_prev[idx], d);
+      for (int t = 0; t < 32; ++t) {
+        const int64_t grow = tau * T + t0 + t;
+        if (grow >= a.rows) continue;
+        const int64_t idx = grow * N + n;
+        const double d = __dmul_rn(__dmul_rn((double)sum[t], base), wsn);
+        a.y_out[idx] = (float)__dadd_rn((double)a.y_prev[idx], d);
+      }
     }
   }
 }
@@ -558,11 +576,11 @@ int launch_t(const LinearArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Handles token tiles of 32 or 64 rows, K a multiple of 16 (16-byte rows of
-// the aligned codes and W^T) and W below 2^31 bytes (32-bit buffer offsets),
-// given the aligned codes and W^T.
+// Handles token tiles of 32 or 64 rows, K a multiple of 64 (whole dense
+// chunks) and W below 2^31 bytes (32-bit buffer offsets), given the aligned
+// codes and W^T.
 bool linear_mfma_supported(const LinearArgs& a) {
-  return a.acodes != nullptr && a.w_t != nullptr && (a.T == 32 || a.T == 64) && (a.K % 16) == 0 &&
+  return a.acodes != nullptr && a.w_t != nullptr && (a.T == 32 || a.T == 64) && (a.K % 64) == 0 &&
          (int64_t)a.K * a.N < (int64_t(1) << 31);
 }
 
