@@ -2,32 +2,39 @@
 // quantization (DSTAR, arXiv 2607.15846: §2.2 Eq. 1; §3.1 step 1 with Eq. 2-5;
 // §4.2 QPU stages 1-3).
 //
-// HBM-bound streaming kernel.  A thread owns CPT adjacent input channels of
-// one token tile: it reads the T rows of X_t and X_{t-1} for those channels
-// with CPT-wide vector loads (a wave reads 64*CPT*4 contiguous bytes per row),
-// keeps Δ in registers, reduces max|Δ| per channel, picks PoT / precision /
-// tag with exact float32 compares against base*2^j, and writes the T codes of
-// each channel as one contiguous run (codes are channel-major within a tile),
-// so every store is 16-byte and coalesced across the wave.
+// HBM-bound streaming kernel.  A pair of adjacent lanes owns CPT adjacent
+// input channels of one token tile; each lane of the pair reads half of the
+// tile's T rows of X_t and X_{t-1} for those channels with CPT-wide vector
+// loads (non-temporal: X is read once), keeps its Δ in registers and reduces
+// max|Δ| per channel; one lane-pair shuffle gives the sub-channel maximum M.
+// Both lanes then pick PoT / precision / tag with exact float32 compares
+// against base*2^j and quantize their rows.  Each lane writes its half of a
+// channel's T codes (codes are channel-major within a tile: a contiguous run
+// per lane), its rows of the aligned codes (one CPT-byte word per row), and
+// the even lane writes the tags and counts the bit histogram.
 #include "fmdq_internal.h"
 
 namespace dstar {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kGroups = kThreads / 2;   // channel groups per workgroup
 
+typedef float fv4 __attribute__((ext_vector_type(4)));
+typedef float fv2 __attribute__((ext_vector_type(2)));
 template <int CPT>
 struct FVec;
 template <>
-struct FVec<4> { using type = float4; };
+struct FVec<4> { using type = fv4; };
 template <>
-struct FVec<2> { using type = float2; };
+struct FVec<2> { using type = fv2; };
 template <>
 struct FVec<1> { using type = float; };
 
 template <int CPT>
 __device__ __forceinline__ void load_vec(const float* p, float (&v)[CPT]) {
-  typename FVec<CPT>::type t = *reinterpret_cast<const typename FVec<CPT>::type*>(p);
+  const typename FVec<CPT>::type t =
+      __builtin_nontemporal_load(reinterpret_cast<const typename FVec<CPT>::type*>(p));
   __builtin_memcpy(v, &t, sizeof(t));
 }
 
@@ -36,24 +43,48 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
          ((uint32_t(d) & 0xFFu) << 24);
 }
 
+// Stores the RT codes of one lane (RT = 8, 16 or 32 consecutive bytes).
+template <int RT>
+__device__ __forceinline__ void store_codes(int8_t* dst, const int (&q)[RT]) {
+  if constexpr (RT == 8) {
+    int2 o;
+    o.x = (int)pack4(q[0], q[1], q[2], q[3]);
+    o.y = (int)pack4(q[4], q[5], q[6], q[7]);
+    *reinterpret_cast<int2*>(dst) = o;
+  } else {
+#pragma unroll
+    for (int v = 0; v < RT / 16; ++v) {
+      int4 o;
+      o.x = (int)pack4(q[16 * v + 0], q[16 * v + 1], q[16 * v + 2], q[16 * v + 3]);
+      o.y = (int)pack4(q[16 * v + 4], q[16 * v + 5], q[16 * v + 6], q[16 * v + 7]);
+      o.z = (int)pack4(q[16 * v + 8], q[16 * v + 9], q[16 * v + 10], q[16 * v + 11]);
+      o.w = (int)pack4(q[16 * v + 12], q[16 * v + 13], q[16 * v + 14], q[16 * v + 15]);
+      reinterpret_cast<int4*>(dst)[v] = o;
+    }
+  }
+}
+
 template <int T, int CPT>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantizeArgs a, int64_t n_work,
                                                             int32_t slabs) {
+  constexpr int RT = T / 2;                  // rows per lane
   uint32_t hist[4] = {0u, 0u, 0u, 0u};
   const int64_t K = a.K;
   const float inv_base = a.inv_base;
+  const int half = threadIdx.x & 1;
+  const int grp = threadIdx.x >> 1;
   for (int64_t wi = blockIdx.x; wi < n_work; wi += gridDim.x) {
     const int64_t tile = wi / slabs;
     const int64_t slab = wi - tile * slabs;
-    const int64_t k = slab * (int64_t)(kThreads * CPT) + (int64_t)threadIdx.x * CPT;
-    if (k >= K) continue;
-    const int64_t r0 = tile * T;
-    const int nrows = (int)((a.rows - r0) < T ? (a.rows - r0) : T);
+    const int64_t k = slab * (int64_t)(kGroups * CPT) + (int64_t)grp * CPT;
+    if (k >= K) continue;                    // both lanes of a pair leave together
+    const int64_t r0 = tile * T + half * RT; // first row of this lane
+    const int64_t nrows = a.rows - r0;       // real rows from r0 (may be <= 0)
 
-    // Δ = X_t − X_{t−1} for T rows × CPT channels (Eq. 1), kept in registers.
-    float d[T][CPT];
+    // Δ = X_t − X_{t−1} for RT rows × CPT channels (Eq. 1), kept in registers.
+    float d[RT][CPT];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
+    for (int t = 0; t < RT; ++t) {
       if (t < nrows) {
         float xt[CPT], xp[CPT];
         load_vec<CPT>(a.x_t + (r0 + t) * K + k, xt);
@@ -69,15 +100,17 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantizeArgs a, int6
     uint32_t tagword = 0;
     // Aligned codes of the CPT channels, one packed word per row (q·2^e when
     // PoT ≤ 6, else 0): the 8-bit operand of stage 3's dense GEMM.
-    uint32_t arow[T];
+    uint32_t arow[RT];
 #pragma unroll
-    for (int t = 0; t < T; ++t) arow[t] = 0u;
+    for (int t = 0; t < RT; ++t) arow[t] = 0u;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      // M: largest |Δ| of the sub-channel (QPU stage 1).
+      // M: largest |Δ| of the sub-channel (QPU stage 1): this lane's rows,
+      // then the partner lane's.
       float m = 0.0f;
 #pragma unroll
-      for (int t = 0; t < T; ++t) m = fmaxf(m, fabsf(d[t][c]));
+      for (int t = 0; t < RT; ++t) m = fmaxf(m, fabsf(d[t][c]));
+      m = fmaxf(m, __shfl_xor(m, 1, 64));
       // PoT = number of bin edges base*2^j (j = 0..20) strictly below M, i.e.
       // the smallest j with M <= base*2^j, capped at 21 (Eq. 3; QPU stage 2).
       int pot = 0;
@@ -88,36 +121,28 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantizeArgs a, int6
       const int e = pot - p;                               // step = base * 2^e
       const float scale = __int_as_float((127 - e) << 23);  // 2^-e, exact
       const float pceil = (float)(1 << p);
-      int q[T];
+      int q[RT];
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
+      for (int t = 0; t < RT; ++t) {
         float r = __fmul_rn(__fmul_rn(d[t][c], inv_base), scale);
         r = fminf(fmaxf(rintf(r), -pceil), pceil);
         q[t] = (int)r;
       }
       if (pot <= 6) {
 #pragma unroll
-        for (int t = 0; t < T; ++t) arow[t] |= (((uint32_t)q[t] << e) & 0xFFu) << (8 * c);
+        for (int t = 0; t < RT; ++t) arow[t] |= (((uint32_t)q[t] << e) & 0xFFu) << (8 * c);
       }
-      hist[p >> 1] += 1u;
+      if (half == 0) hist[p >> 1] += 1u;
       const uint32_t tag = (uint32_t)(DSTAR_FMDQ_TAG_OFFSET - e) | ((uint32_t)(p >> 1) << DSTAR_FMDQ_PREC_SHIFT);
       tagword |= tag << (8 * c);
-      // Codes of channel k+c: T contiguous bytes at codes[(tile*K + k + c)*T].
-      int4* dst = reinterpret_cast<int4*>(a.codes + ((tile * K + k + c) * T));
-#pragma unroll
-      for (int v = 0; v < T / 16; ++v) {
-        int4 o;
-        o.x = (int)pack4(q[16 * v + 0], q[16 * v + 1], q[16 * v + 2], q[16 * v + 3]);
-        o.y = (int)pack4(q[16 * v + 4], q[16 * v + 5], q[16 * v + 6], q[16 * v + 7]);
-        o.z = (int)pack4(q[16 * v + 8], q[16 * v + 9], q[16 * v + 10], q[16 * v + 11]);
-        o.w = (int)pack4(q[16 * v + 12], q[16 * v + 13], q[16 * v + 14], q[16 * v + 15]);
-        dst[v] = o;
-      }
+      // This lane's RT codes of channel k+c: bytes half*RT .. half*RT+RT-1 of
+      // the channel's run at codes[(tile*K + k + c)*T].
+      store_codes<RT>(a.codes + ((tile * K + k + c) * T) + half * RT, q);
     }
     if (a.acodes != nullptr) {
       int8_t* ap = a.acodes + r0 * K + k;
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
+      for (int t = 0; t < RT; ++t) {
         if constexpr (CPT == 4) {
           *reinterpret_cast<uint32_t*>(ap + t * K) = arow[t];
         } else if constexpr (CPT == 2) {
@@ -127,13 +152,15 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantizeArgs a, int6
         }
       }
     }
-    uint8_t* tp = a.tags + tile * K + k;
-    if constexpr (CPT == 4) {
-      *reinterpret_cast<uint32_t*>(tp) = tagword;
-    } else if constexpr (CPT == 2) {
-      *reinterpret_cast<uint16_t*>(tp) = (uint16_t)tagword;
-    } else {
-      *tp = (uint8_t)tagword;
+    if (half == 0) {
+      uint8_t* tp = a.tags + tile * K + k;
+      if constexpr (CPT == 4) {
+        *reinterpret_cast<uint32_t*>(tp) = tagword;
+      } else if constexpr (CPT == 2) {
+        *reinterpret_cast<uint16_t*>(tp) = (uint16_t)tagword;
+      } else {
+        *tp = (uint8_t)tagword;
+      }
     }
   }
 
@@ -158,9 +185,9 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantizeArgs a, int6
 template <int T, int CPT>
 int launch_t(const QuantizeArgs& a, hipStream_t s) {
   const int64_t nt = n_tiles(a.rows, T);
-  const int32_t slabs = (int32_t)((a.K + kThreads * CPT - 1) / (kThreads * CPT));
+  const int32_t slabs = (int32_t)((a.K + kGroups * CPT - 1) / (kGroups * CPT));
   const int64_t n_work = nt * slabs;
-  const int64_t grid = n_work < 4096 ? n_work : 4096;
+  const int64_t grid = n_work < 8192 ? n_work : 8192;
   hipLaunchKernelGGL((quantize_kernel<T, CPT>), dim3((unsigned)grid), dim3(kThreads), 0, s, a,
                      n_work, slabs);
   return check_launch("fmdq_quantize");
@@ -170,17 +197,18 @@ int launch_t(const QuantizeArgs& a, hipStream_t s) {
 
 int launch_quantize(const QuantizeArgs& a, hipStream_t s) {
   if (a.rows == 0) return DSTAR_OK;
-  // Channels per thread: as many as keep three waves per SIMD resident
-  // (T·CPT floats of Δ live in registers), limited by K's divisibility.
+  // Channels per lane pair: as many as keep several waves per SIMD resident
+  // (T/2 · CPT floats of Δ live in each lane's registers), limited by K's
+  // divisibility.
   const bool vec4 = (a.K % 4) == 0;
   const bool vec2 = (a.K % 2) == 0;
   switch (a.T) {
     case 16:
       return vec4 ? launch_t<16, 4>(a, s) : vec2 ? launch_t<16, 2>(a, s) : launch_t<16, 1>(a, s);
     case 32:
-      return vec2 ? launch_t<32, 2>(a, s) : launch_t<32, 1>(a, s);
+      return vec4 ? launch_t<32, 4>(a, s) : vec2 ? launch_t<32, 2>(a, s) : launch_t<32, 1>(a, s);
     case 64:
-      return launch_t<64, 1>(a, s);
+      return vec2 ? launch_t<64, 2>(a, s) : launch_t<64, 1>(a, s);
     default:
       return set_error(DSTAR_EUNSUPPORTED, "token_tile %d not supported", a.T);
   }
