@@ -8,10 +8,19 @@ the seeded random walk are made resident in HBM before timing and cycled.
 
 Prints one JSON line: whole-step dense-equivalent int8 TOPS (2*M*N*K per layer
 over the measured time), per-stage times from HIP events on the launch
-stream, the roofline of the dominant kernel, and the CPU oracle timed on the
-host as a baseline.
+stream, the roofline of the dominant kernel (with the HBM traffic measured by
+rocprofv3 counters when a summary for the current kernel source exists under
+profiles/), and the CPU oracle timed on the host as a baseline.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 1] [--pairs 2]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload pixart-alpha-1024px]
+
+Traffic summary from two counter runs of this same command (run from the
+repository root; a plain 256 MiB device copy made before timing calibrates
+the counters):
+
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline
+    python bench.py --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write
 """
 from __future__ import annotations
 
@@ -32,59 +41,186 @@ METRIC = "FMDQ differential linear: ms/layer, dense-equiv int8 TOPS, % MFMA & HB
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
 STAGES = ("quantize", "bucket", "linear")
-KERNEL_SRC = {"quantize": "fmdq_quantize.hip", "bucket": "fmdq_bucket.hip",
-              "linear": "fmdq_linear.hip"}
+KERNEL_SRC = {"quantize": ["fmdq_quantize.hip"], "bucket": ["fmdq_bucket.hip"],
+              "linear": ["fmdq_linear.hip", "fmdq_linear_mfma.hip"]}
+# device kernel name of each stage (as rocprofv3 reports it)
+KERNEL_NAME = {"quantize": "quantize_kernel", "bucket": "bucket_kernel", "linear": "linear_mfma_kernel"}
+CAL_BYTES = 256 << 20     # the calibration copy
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "stage_traffic_pixart1024.md")
 
 
 def algorithmic(stage: str, rows: int, K: int, N: int, T: int) -> dict:
-    """Compulsory HBM bytes (and int8 ops) of one launch of a stage."""
+    """Compulsory HBM bytes (and int8 ops) of one launch of a stage: every array
+    the stage must read or write, once.  Re-reads of W or the codes by
+    several workgroups are not counted."""
     nt = (rows + T - 1) // T
     codes = nt * T * K
-    if stage == "quantize":
-        return dict(bytes=8 * rows * K + codes + nt * K + 16, ops=0)
-    if stage == "bucket":
-        return dict(bytes=nt * K + 2 * nt * K + 68 * nt, ops=0)
-    return dict(bytes=codes + 2 * nt * K + 68 * nt + K * N + 4 * N + 8 * rows * N,
+    if stage == "quantize":   # X_t, X_{t-1} in; codes, aligned codes, tags out
+        return dict(bytes=8 * rows * K + 2 * codes + nt * K + 16, ops=0)
+    if stage == "bucket":     # tags in; perm, bin offsets out
+        return dict(bytes=nt * K + 2 * nt * K + 260 * nt, ops=0)
+    # aligned codes, W^T, perm, bin offsets, w_scale in; Y_{t-1} in, Y_t out
+    return dict(bytes=codes + K * N + 2 * nt * K + 260 * nt + 4 * N + 8 * rows * N,
                 ops=2 * rows * N * K)
 
 
 def src_sha(stage: str) -> str:
-    path = os.path.join(ROOT, "differential_mixed_precision_amd", "csrc", KERNEL_SRC[stage])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRC[stage]:
+        with open(os.path.join(ROOT, "differential_mixed_precision_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(stage: str, layer: str, cfg: int):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
-    if there is none or the kernel source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+def measured_traffic(stage: str, grid: int):
+    """Calibrated HBM bytes per launch of a stage's kernel at a grid size, from
+    the committed counter summary; None if there is none or the kernel source
+    changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_MD):
         return None
-    with open(path) as f:
-        tab = json.load(f)
-    e = tab.get(f"{stage}@c{cfg}-{layer}")
-    if not e or e.get("src_sha") != src_sha(stage):
-        return None
-    return e["bytes_per_launch"]
+    for line in open(TRAFFIC_MD):
+        f = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(f) >= 7 and f[0] == stage and f[1] == str(grid) and f[2] == src_sha(stage):
+            return int(float(f[6]))
+    return None
 
 
-def cpu_baseline(ins: list[dict]) -> dict:
-    """The oracle (untuned) on the host: one full step (pair 1, both layers)."""
+def write_traffic(fetch_dir: str, write_dir: str) -> None:
+    """Summarizes two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of the
+    bench into the traffic table: per stage kernel and grid size, the mean
+    KiB per dispatch, scaled by what the counters read for the calibration
+    copy of known size."""
+    import csv
+
+    def read(d, counter):
+        rows = []
+        for root, _, files in os.walk(d):
+            for fn in files:
+                if fn.endswith("counter_collection.csv"):
+                    rows += [r for r in csv.DictReader(open(os.path.join(root, fn)))
+                             if r["Counter_Name"] == counter]
+        per = {}
+        for r in rows:
+            key = (r["Kernel_Name"], int(r["Grid_Size"]), r["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        return per
+
+    fetch, write = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
+
+    def mean(per, pred):
+        v = [x for (name, grid, _), x in per.items() if pred(name, grid)]
+        return sum(v) / len(v) if v else None
+
+    # the calibration copy is the largest device copy of the run
+    cal_grid = max((g for (n, g, _) in write if "copyBuffer" in n), default=None)
+    cal_f = mean(fetch, lambda n, g: "copyBuffer" in n and g == cal_grid)
+    cal_w = mean(write, lambda n, g: "copyBuffer" in n and g == cal_grid)
+    if not cal_f or not cal_w:
+        raise SystemExit("no calibration copy in the counter runs")
+    sf, sw = (CAL_BYTES / 1024) / cal_f, (CAL_BYTES / 1024) / cal_w
+    lines = ["# HBM traffic per launch, FMDQ differential linear, PixArt-alpha-style 1024px MLP",
+             "",
+             "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, rocprofv3 --pmc, one run each) of",
+             "`python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline` on one MI355X, scaled by what they read",
+             f"for a plain {CAL_BYTES >> 20} MiB device copy made in the same run (fetch x{sf:.4f}, write x{sw:.4f}).",
+             "Commands:",
+             "",
+             "```",
+             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+             "python bench.py --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write",
+             "```",
+             "",
+             "| stage | grid | source | fetch KiB | write KiB | scale | bytes per launch |",
+             "|---|---|---|---|---|---|---|"]
+    for stage, kname in KERNEL_NAME.items():
+        grids = sorted({g for (n, g, _) in fetch if kname in n})
+        for g in grids:
+            fk = mean(fetch, lambda n, gg: kname in n and gg == g)
+            wk = mean(write, lambda n, gg: kname in n and gg == g)
+            if fk is None or wk is None:
+                continue
+            b = fk * sf * 1024 + wk * sw * 1024
+            lines.append(f"| {stage} | {g} | {src_sha(stage)} | {fk:.0f} | {wk:.0f} | "
+                         f"{sf:.4f}/{sw:.4f} | {b:.0f} |")
+    with open(TRAFFIC_MD, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def cpu_baseline(ins: list[dict], budget_s: float = 10.0) -> dict:
+    """The oracle (untuned) on the host cores: whole steps (both layers, the
+    resident pairs in turn) until about budget_s seconds of work."""
     from threadpoolctl import threadpool_info
     from oracle import fmdq
     t0 = time.perf_counter()
     ops = 0
-    for d in ins:
-        fmdq.layer(d["x_t"], d["x_prev"], d["w"], d["w_scale"], d["y_prev"], d["base"],
-                   d["token_tile"], d["k0"])
-        ops += 2 * d["rows"] * d["N"] * d["K"]
+    steps = 0
+    while True:
+        for d in ins[steps % len(ins)]:
+            fmdq.layer(d["x_t"], d["x_prev"], d["w"], d["w_scale"], d["y_prev"], d["base"],
+                       d["token_tile"], d["k0"])
+            ops += 2 * d["rows"] * d["N"] * d["K"]
+        steps += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
     dt = time.perf_counter() - t0
     threads = max([i["num_threads"] for i in threadpool_info()] or [1])
     return {"value": ops / dt / 1e12, "unit": "TOPS (dense-equiv int8)", "cores": threads,
             "kind": "oracle", "seconds": dt,
-            "sample": f"one full step: pair 1, {ins[0]['rows']} rows, layers "
-                      f"{'+'.join(d['name'].split('/')[-1] for d in ins)}; numpy float64 "
-                      f"matmuls per tile and FPoT group"}
+            "sample": f"{steps} whole step(s) of the same workload ({ins[0][0]['rows']} rows, both "
+                      f"layers, timestep pairs 1..{min(steps, len(ins))}); numpy float64 matmuls "
+                      f"per token tile and FPoT group"}
+
+
+def write_kernel_summary(trace_dir: str) -> None:
+    """Summarizes a rocprofv3 --kernel-trace --stats run of the bench: the
+    tool's own per-kernel statistics, and the mean duration per kernel and
+    launch grid from the trace (fc1 and fc2 launch the same kernels with
+    different grids)."""
+    import csv
+    files = {}
+    for root, _, fs in os.walk(trace_dir):
+        for fn in fs:
+            files[fn] = os.path.join(root, fn)
+    stats = [r for f, p in files.items() if f.endswith("kernel_stats.csv") for r in csv.DictReader(open(p))]
+    trace = [r for f, p in files.items() if f.endswith("kernel_trace.csv") for r in csv.DictReader(open(p))]
+    lines = ["# Kernel time, FMDQ differential linear, PixArt-alpha-style 1024px MLP",
+             "",
+             "8192 rows (2 x 4096 tokens), fc1 1152->4608 and fc2 4608->1152, token tile 32; one MI355X.",
+             "Command (from the repository root), then the summary:",
+             "",
+             "```",
+             "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_bench -o run -- \\",
+             "    python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline",
+             "python bench.py --write-kernel-summary gpurun_out/prof_bench",
+             "```",
+             "",
+             "rocprofv3 statistics (13 steps x 2 layers; fc1 and fc2 pooled per kernel):",
+             "",
+             "| kernel | calls | total us | average us | min us | max us | % |",
+             "|---|---|---|---|---|---|---|"]
+    for r in stats:
+        name = r["Name"].replace("|", "/")
+        name = name if len(name) <= 80 else name[:80] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
+    per = {}
+    for r in trace:
+        name = r.get("Kernel_Name", "")
+        grid = r.get("Grid_Size") or r.get("Grid_Size_X") or "?"
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        per.setdefault((name, grid), []).append(dur)
+    lines += ["", "Per kernel and launch grid (threads), from the trace:", "",
+              "| kernel | grid | calls | mean us | min us | max us |", "|---|---|---|---|---|---|"]
+    for (name, grid), v in sorted(per.items(), key=lambda x: -sum(x[1])):
+        short = name.replace("dstar::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        lines.append(f"| `{short}` | {grid} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
+    out = os.path.join(ROOT, "profiles", "kernel_time_pixart1024.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def main() -> int:
@@ -92,10 +228,18 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--workload", default="pixart-alpha-1024px")
     ap.add_argument("--pairs", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--write-kernel-summary", metavar="TRACE_DIR")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return 0
+    if args.write_kernel_summary:
+        write_kernel_summary(args.write_kernel_summary)
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the layer shards by token tiles with no "
               f"inter-GPU exchange); --gpus {args.gpus} is not supported", file=sys.stderr)
@@ -110,11 +254,11 @@ def main() -> int:
         __graft_entry__.build()
     dm.load()
     dev = torch.device("cuda:0")
-    spec = wl.CONFIGS[args.config]
+    cfg = {v["name"]: c for c, v in wl.CONFIGS.items()}[args.workload]
+    spec = wl.CONFIGS[cfg]
     layers = list(spec["layers"])
-    print(f"[bench] generating config {args.config} ({spec['name']}) pairs 1..{args.pairs}",
-          file=sys.stderr, flush=True)
-    host = {L: [wl.make_inputs(args.config, L, p) for p in range(1, args.pairs + 1)] for L in layers}
+    print(f"[bench] generating {spec['name']} pairs 1..{args.pairs}", file=sys.stderr, flush=True)
+    host = {L: [wl.make_inputs(cfg, L, p) for p in range(1, args.pairs + 1)] for L in layers}
     rows, T = spec["rows"], spec["token_tile"]
 
     # resident device state
@@ -179,6 +323,14 @@ def main() -> int:
     total_ops = sum(2 * rows * state[L]["N"] * state[L]["K"] for L in layers)
     value = total_ops / (ms_per_step * 1e-3) / 1e12
 
+    # launch grid (threads) of each stage, as rocprofv3 reports it
+    nt = (rows + T - 1) // T
+    grids = {}
+    for L in layers:
+        K, N = state[L]["K"], state[L]["N"]
+        q_work = nt * ((K + 128 * 4 - 1) // (128 * 4))
+        grids[L] = {"quantize": 256 * min(q_work, 8192), "bucket": 256 * min(nt, 2048),
+                    "linear": 256 * ((nt + 128 // T - 1) // (128 // T)) * ((N + 255) // 256)}
     kernels = {}
     layer_out = {}
     for L in layers:
@@ -194,7 +346,7 @@ def main() -> int:
             t_hbm = alg["bytes"] / (HBM_PEAK_GBS * 1e9)
             t_mfma = alg["ops"] / (INT8_PEAK_TOPS * 1e12) if alg["ops"] else 0.0
             bound = "mfma" if t_mfma > t_hbm else "hbm"
-            traffic = measured_traffic(s, L, args.config)
+            traffic = measured_traffic(s, grids[L][s])
             kernels[f"{s}@{L}"] = dict(
                 us_mean=us, us_p10=float(np.percentile(per[L][s], 10)),
                 us_p90=float(np.percentile(per[L][s], 90)), alg_bytes=alg["bytes"],
@@ -221,16 +373,16 @@ def main() -> int:
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic (seeded random walk of DiT-like activations; random int8 weights)",
-        "config": {"workload": f"config {args.config}: {spec['name']}, rows {rows}, "
-                               f"token tile {T}, layers " +
+        "config": {"workload": f"{spec['name']}: {rows} rows ({rows // spec['tokens_per_seq']} x "
+                               f"{spec['tokens_per_seq']} tokens), token tile {T}, MLP " +
                                ", ".join(f"{L} {state[L]['K']}->{state[L]['N']}" for L in layers),
                    "rows": rows, "token_tile": T, "thr0_log2": wl.DEFAULT_K0,
                    "pairs_cycled": args.pairs},
         "layers": layer_out, "kernels": kernels, "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on one step", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline([host[L][0] for L in layers])
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline([[host[L][p] for L in layers] for p in range(args.pairs)])
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out))
