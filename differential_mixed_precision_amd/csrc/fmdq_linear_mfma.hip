@@ -38,16 +38,18 @@
 //
 // Layout.  Workgroup = 256 threads = 4 waves, output block 128 rows × 256
 // columns; wave w owns all 128 rows and columns 64w .. 64w+63 (4 × 2 MFMA
-// 32x32x32 int8 tiles).  Dense part: the 128 rows of stage 1's aligned codes
-// ([rows][K], channel innermost) are shared by the four waves through LDS
-// ([row][channel] tiles, one ds_read_b128 per fragment); each wave streams its
-// own W^T fragments ([N][K], channel innermost) from global memory straight
-// into registers, one chunk ahead.  Gathered part: the codes ([tile][K][T])
-// and W ([K][N]) rows of the gathered channels have the channel outermost;
-// they are staged as [channel][row] and [channel][column] LDS tiles and each
-// lane assembles its fragment (one row or column, 16 consecutive channels)
-// with two ds_read_b64_tr_b8 transpose reads; perm entries are fetched two
-// steps and data one step ahead.
+// 32x32x32 int8 tiles).  Dense part: 64-channel chunks of stage 1's aligned
+// codes ([rows][K]) and of W^T ([N][K]), both channel innermost, flow through
+// a 3-stage LDS ring filled by direct global-to-LDS buffer loads, two chunks
+// ahead of the MFMAs; the four 16-byte columns of every 64-byte row are
+// XOR-swizzled by (row / 4) mod 4 so that one ds_read_b128 per fragment is
+// free of bank conflicts.  The aligned-code rows are shared by the four waves,
+// each wave reads only its own 64 W^T rows.  Gathered part: the codes
+// ([tile][K][T]) and W ([K][N]) rows of the gathered channels have the channel
+// outermost; they are staged as [channel][row] and [channel][column] LDS tiles
+// and each lane assembles its fragment (one row or column, 16 consecutive
+// channels) with two ds_read_b64_tr_b8 transpose reads; perm entries are
+// fetched two steps and data one step ahead.
 #include "fmdq_internal.h"
 
 namespace dstar {

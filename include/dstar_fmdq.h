@@ -153,7 +153,7 @@ int dstar_fmdq_pack_weights(int32_t K, int32_t N, const int8_t* w, int8_t* w_t,
  *              the layer runs in the per-group kernel (slow; for checking).
  * Per output: S = Σ_g acc_g * 2^(15-g) (an exact integer);
  * y_out = fl32(f64(y_prev) + (f64(S) * f64(base)) * f64(w_scale[n])).
- * With acodes and w_t given (T of 32 or 64, K % 16 == 0, K*N < 2^31) the MFMA
+ * With acodes and w_t given (T of 32 or 64, K % 64 == 0, K*N < 2^31) the MFMA
  * kernel runs: acodes x w_t for every sub-channel with PoT <= 6, and the
  * channels with PoT >= 7 of every FPoT group (the group's prefix in perm)
  * gathered from codes and w, group by group with left shifts between groups;
