@@ -18,23 +18,24 @@
 // of them are summed by one natural-order int8 MFMA GEMM whose W chunks are
 // staged once in LDS and shared by every token tile of the workgroup.  The few
 // sub-channels with PoT ≥ 7 (only 8-bit ones at the default threshold) keep
-// their own FPoT groups: each tile's such channels are gathered, grouped by
-// tag in ascending FPoT, and multiplied group after group into the same int32
-// accumulator, which is shifted left by the FPoT difference at every group
-// change and finally to units of the base — the Horner form of the shift
-// alignment of §3.1 step 5 and Fig. 6.  The dense GEMM then accumulates on
-// top.
+// their own FPoT groups: after the dense GEMM, each 32-row block gathers its
+// token tile's such channels and multiplies them group after group, in
+// ascending FPoT, into a temporary int32 accumulator that is shifted left by
+// the FPoT difference at every group change — the Horner form of the shift
+// alignment of §3.1 step 5 and Fig. 6 — and finally added, shifted to units
+// of the base, to the dense sum.
 //
-// Exactness.  int32 arithmetic wraps modulo 2^32, so the final accumulator
-// equals S whenever |S| < 2^31; |S| ≤ 127 · Σ_k 2^PoT_k, so a token tile is
-// handled here only if 127 · Σ_k 2^PoT_k < 2^31 (computed from stage 2's bin
-// counts).  Any other tile ("ineligible") is finished by an exact scalar path
-// in the same workgroup that walks the tile's FPoT groups in perm order with
-// int32 group sums shifted into an int64 sum.
+// Exactness.  int32 arithmetic wraps modulo 2^32 (shifts and adds included),
+// so the final accumulator equals S whenever |S| < 2^31; |S| ≤ 127 · Σ_k
+// 2^PoT_k, so a token tile is handled here only if 127 · Σ_k 2^PoT_k < 2^31
+// (computed from stage 2's bin counts).  Any other tile ("ineligible") is
+// finished by an exact scalar path in the same workgroup that walks the
+// tile's FPoT groups in perm order with int32 group sums shifted into an int64
+// sum.
 //
 // Stage 2 orders each FPoT group widest precision first, so the channels of a
 // group with PoT ≥ 7 are a prefix of the group in perm, found from the bin
-// offsets alone; the gathered steps read perm directly.
+// offsets alone.
 //
 // Layout.  Workgroup = 256 threads = 4 waves, output block 128 rows × 256
 // columns; wave w owns all 128 rows and columns 64w .. 64w+63 (4 × 2 MFMA
@@ -44,12 +45,15 @@
 // ahead of the MFMAs; the four 16-byte columns of every 64-byte row are
 // XOR-swizzled by (row / 4) mod 4 so that one ds_read_b128 per fragment is
 // free of bank conflicts.  The aligned-code rows are shared by the four waves,
-// each wave reads only its own 64 W^T rows.  Gathered part: the codes
-// ([tile][K][T]) and W ([K][N]) rows of the gathered channels have the channel
-// outermost; they are staged as [channel][row] and [channel][column] LDS tiles
-// and each lane assembles its fragment (one row or column, 16 consecutive
-// channels) with two ds_read_b64_tr_b8 transpose reads; perm entries are
-// fetched two steps and data one step ahead.
+// each wave reads only its own 64 W^T rows.  Gathered part: one "unit" is 32
+// channels of one FPoT group for one 32-row block: their codes (32 bytes per
+// channel from the [tile][K][T] layout) and their W rows (256 bytes per
+// channel) are gathered by direct global-to-LDS loads into an 8-stage ring,
+// seven units ahead; the channel ids of up to 64 units at a time are staged in
+// LDS.  Both tiles have the channel outermost, so each lane assembles its
+// fragment with two ds_read_b64_tr_b8 transpose reads (W rows XOR-swizzled in
+// 16-byte pieces by channel mod 8).  The bin offsets and the unit schedule
+// are read while the first dense chunks are in flight.
 #include "fmdq_internal.h"
 
 namespace dstar {
@@ -67,10 +71,9 @@ constexpr int WN = 64;             // output columns per wave
 constexpr int BN = kWaves * WN;    // output columns per workgroup (256)
 constexpr int RB = BM / 32;        // 32-row MFMA blocks per wave (4)
 constexpr int CB = WN / 32;        // 32-column MFMA blocks per wave (2)
+static_assert(CB == 2, "the gathered step is written for two column blocks");
 constexpr int BK = 64;             // channels per dense chunk (2 MFMA k-steps)
-constexpr int KS = 32;             // channels per MFMA k-step (= per gathered step)
-constexpr int SA = BM + 32;        // LDS bytes per channel row of the gathered A tile
-constexpr int SB = BN + 32;        // LDS bytes per channel row of a gathered B tile
+constexpr int KS = 32;             // channels per MFMA k-step (= per gathered unit)
 constexpr int kTags = DSTAR_FMDQ_NUM_TAGS;
 constexpr int kBins = DSTAR_FMDQ_NUM_BINS;
 constexpr int kAlignedPotMax = 6;  // q·2^e fits int8 when PoT ≤ 6
@@ -82,26 +85,30 @@ struct Cfg {
   static constexpr int kTiles = BM / T;   // token tiles per workgroup
 };
 
-// LDS carve-up (bytes).  Dense: kStages stages of (A 128 rows + B 256 rows)
-// × 64 bytes.  Gathered: one stage of (A: 32 channel rows; B: one 32-row tile
-// per token tile).  The two phases reuse the same bytes.
+// LDS carve-up (bytes).  The data region holds either the dense ring
+// (kStages stages of (A 128 rows + B 256 rows) × 64 bytes) or, after the
+// dense loop, the gathered ring (kUnits stages of A 32 channels × 32 rows +
+// B 32 channels × 256 columns).  Both are 72 KiB, so two workgroups fit per CU.
 constexpr int kStages = 3;
 constexpr int kStageDense = (BM + BN) * BK;                // 24576
-constexpr int kDenseBytes = kStages * kStageDense;         // 73728
-constexpr int kStageBytes = KS * SA + 4 * KS * SB;         // 41984
-constexpr int kDataBytes = kDenseBytes > kStageBytes ? kDenseBytes : kStageBytes;
-constexpr int kOffOff = kDataBytes;                         // int32 [4][65] bin offsets
+constexpr int kUnitA = KS * 32;                            // 1024
+constexpr int kUnitB = KS * BN;                            // 8192
+constexpr int kUnitBytes = kUnitA + kUnitB;                // 9216
+constexpr int kUnits = 8;                                  // gathered ring stages
+constexpr int kAhead = kUnits - 1;                         // units in flight ahead
+constexpr int kBatch = 64;                                 // units whose ids are staged
+constexpr int kDataBytes = kStages * kStageDense;          // 73728
+static_assert(kUnits * kUnitBytes == kDataBytes, "the two rings share one region");
+constexpr int kOffEnt = kDataBytes;                        // uint16 [kBatch][32] channel ids
+constexpr int kOffBp = kOffEnt + kBatch * KS * 2;          // uint64 [4][16] bound parts
+constexpr int kOffOff = kOffBp + 4 * kTags * 8;            // int32 [4][65] bin offsets
 constexpr int kOffRs = kOffOff + 4 * (kBins + 1) * 4;      // int32 [4][16] prefix starts
 constexpr int kOffRc = kOffRs + 4 * kTags * 4;             // int32 [4][16] prefix lengths
-constexpr int kOffBp = kOffRc + 4 * kTags * 4;             // uint64 [4][16] bound parts
-constexpr int kOffSteps = kOffBp + 4 * kTags * 8;          // int32 [16] steps per group
-constexpr int kOffCum = kOffSteps + kTags * 4;             // int32 [17] cumulative steps
-constexpr int kOffElig = kOffCum + (kTags + 1) * 4;        // int32 [4]
+constexpr int kOffUs = kOffRc + 4 * kTags * 4;             // int32 [65] (+pad) unit starts
+constexpr int kOffUi = kOffUs + 68 * 4;                    // uint32 [kBatch] unit tile/rows
+constexpr int kOffElig = kOffUi + kBatch * 4;              // int32 [4]
 constexpr int kLdsBytes = kOffElig + 4 * 4;
-
-__device__ __forceinline__ void st_u128(uint8_t* p, uint4 v) {
-  *reinterpret_cast<uint4*>(p) = v;
-}
+static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per CU");
 
 // Operand loads go through buffer resources: a load whose offset lies outside
 // the resource's byte range returns zeros, so every load is unconditional
@@ -111,52 +118,67 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef __attribute__((address_space(3))) void* lds_ptr;
 constexpr uint32_t kOob = 0x80000000u;
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
-// 6:4, lgkmcnt 11:8; the unused counters at their maximum): wait until no
-// vector-memory load is in flight, or at most one dense chunk's six loads.
-constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitVmChunk = 0x0F76;
+// 6:4, lgkmcnt 11:8; the counters not waited on at their maximum).
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+constexpr int kWaitVm0 = wait_vm(0);
+constexpr int kWaitVmChunk = wait_vm(6);   // one dense chunk's six loads
+constexpr int kWaitVmChunkIds = wait_vm(14);  // ... and eight id loads
+constexpr int kWaitLgkm0 = 0xC07F;         // lgkmcnt(0)
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
-  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-__device__ __forceinline__ v4i bload16v(rsrc_t r, uint32_t off) {
-  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return v4i{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
-}
-__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+
+// Workgroup barrier that waits only for this wave's LDS accesses (not for
+// the direct-to-LDS loads in flight, which __syncthreads would also drain).
+__device__ __forceinline__ void bar_lds() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
 }
 
-// 16 bytes of W at byte offset `off` of the W resource; with VecW the piece is
-// one 16-byte load (N % 16 == 0, the piece lies wholly inside or outside W),
-// otherwise four 4-byte loads, each dropped past column N.
-template <bool VecW>
-__device__ __forceinline__ uint4 load_w16(rsrc_t rw, uint32_t off, int64_t n, int64_t N, bool valid) {
-  if constexpr (VecW) {
-    return bload16(rw, valid ? off : kOob);
-  } else {
-    uint32_t d[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) d[m] = bload4(rw, (valid && n + 4 * m < N) ? off + 4 * m : kOob);
-    return make_uint4(d[0], d[1], d[2], d[3]);
-  }
+// ds_read_b64_tr_b8 issued as inline assembly: the compiler cannot tell what
+// the intrinsic reads, so it would wait for every direct-to-LDS load in
+// flight before it.  The caller waits (lgkm_wait) before using the result.
+__device__ __forceinline__ v2i tr8(const uint8_t* p) {
+  v2i r;
+  const uint32_t addr = (uint32_t)(uintptr_t)(lds_ptr)p;
+  __asm__ __volatile__("ds_read_b64_tr_b8 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+// Waits for this wave's LDS reads; the fragments pass through the statement
+// so that no use of them can be scheduled before it.
+__device__ __forceinline__ void lgkm_wait(v4i& x, v4i& y, v4i& z) {
+  __asm__ __volatile__("s_waitcnt lgkmcnt(0)" : "+v"(x), "+v"(y), "+v"(z));
 }
 
 // MFMA fragment from a [channel][row] LDS tile with row stride S: the lane
-// gets row/column (lane % 32) and channels k0 + 16·(lane / 32) + 0..15.  Two
-// transpose reads; in each 16-lane group, lane r addresses channel row
-// k + r/2 at column offset 8·(r % 2) (+16 for the odd groups).
+// gets row/column (lane % 32) and channels 16·(lane / 32) + 0..15.  Two
+// transpose reads; in each 16-lane group, lane r addresses channel row r/2 (+8
+// for the second read) at column offset 8·(r % 2) (+16 for the odd groups).
 template <int S>
-__device__ __forceinline__ v4i tr_frag(const uint8_t* tile, int k0, int col0, int lane) {
+__device__ __forceinline__ v4i tr_frag(const uint8_t* tile, int col0, int lane) {
   const int q = lane >> 4, r = lane & 15;
-  const uint8_t* p = tile + (k0 + 16 * (q >> 1) + (r >> 1)) * S + col0 + 16 * (q & 1) + 8 * (r & 1);
-  const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)p);
-  const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(p + 8 * S));
+  const uint8_t* p = tile + (16 * (q >> 1) + (r >> 1)) * S + col0 + 16 * (q & 1) + 8 * (r & 1);
+  const v2i lo = tr8(p);
+  const v2i hi = tr8(p + 8 * S);
+  return v4i{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// The same from a gathered W tile [32 channels][256 columns] whose 16-byte
+// pieces are stored XOR-swizzled: column piece P of channel c sits at piece
+// P ^ (c mod 8), so the 8 channels one 16-lane group reads hit 8 different
+// pieces (no bank conflicts).  Channels c and c + 8 share the swizzle.
+__device__ __forceinline__ v4i tr_frag_wsw(const uint8_t* tile, int col0, int lane) {
+  const int q = lane >> 4, r = lane & 15;
+  const int c = 16 * (q >> 1) + (r >> 1);
+  const int piece = ((col0 >> 4) + (q & 1)) ^ (c & 7);
+  const uint8_t* p = tile + c * BN + 16 * piece + 8 * (r & 1);
+  const v2i lo = tr8(p);
+  const v2i hi = tr8(p + 8 * BN);
   return v4i{lo[0], lo[1], hi[0], hi[1]};
 }
 
@@ -165,17 +187,37 @@ __device__ __forceinline__ void shift_acc(v16i& acc, int s) {
   for (int r = 0; r < 16; ++r) acc[r] = (int)((uint32_t)acc[r] << s);
 }
 
+// Waits until at most `ops * after` vector-memory operations of this wave are
+// in flight (after = 0 .. kAhead - 1).
+template <int ops>
+__device__ __forceinline__ void wait_units(int after) {
+  switch (after) {
+    case 0: __builtin_amdgcn_s_waitcnt(wait_vm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(wait_vm(ops * 1)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(wait_vm(ops * 2)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(wait_vm(ops * 3)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(wait_vm(ops * 4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(wait_vm(ops * 5)); break;
+    default: __builtin_amdgcn_s_waitcnt(wait_vm(ops * 6)); break;
+  }
+}
+
 template <int T, bool VecW>
 __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, int32_t row_blocks,
                                                                   int32_t col_blocks) {
   constexpr int kTiles = Cfg<T>::kTiles;
+  // Direct-to-LDS loads per wave per gathered unit: one dword load of codes,
+  // and the W rows as two 16-byte or eight 4-byte loads.
+  constexpr int kOpsUnit = VecW ? 3 : 9;
+  static_assert(kOpsUnit * (kAhead - 1) <= 63, "vmcnt range");
   extern __shared__ __align__(16) uint8_t smem[];
+  uint16_t* ent = reinterpret_cast<uint16_t*>(smem + kOffEnt);         // [kBatch][32]
+  unsigned long long* bpart = reinterpret_cast<unsigned long long*>(smem + kOffBp);
   int32_t* off_s = reinterpret_cast<int32_t*>(smem + kOffOff);          // [kTiles][65]
   int32_t* rstart = reinterpret_cast<int32_t*>(smem + kOffRs);          // [kTiles][16]
   int32_t* rcount = reinterpret_cast<int32_t*>(smem + kOffRc);          // [kTiles][16]
-  unsigned long long* bpart = reinterpret_cast<unsigned long long*>(smem + kOffBp);
-  int32_t* steps_g = reinterpret_cast<int32_t*>(smem + kOffSteps);      // [16]
-  int32_t* cum = reinterpret_cast<int32_t*>(smem + kOffCum);            // [17]
+  int32_t* ustart = reinterpret_cast<int32_t*>(smem + kOffUs);          // [65]
+  uint32_t* uinfo = reinterpret_cast<uint32_t*>(smem + kOffUi);         // [kBatch]
   int32_t* eligible = reinterpret_cast<int32_t*>(smem + kOffElig);      // [kTiles]
 
   const int tid = threadIdx.x;
@@ -212,13 +254,58 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   const rsrc_t r_w = make_rsrc(a.w, (uint32_t)(K * N));
   const rsrc_t r_wt = make_rsrc(a.w_t, (uint32_t)(N * K));
 
-  // ---- Meta: per tile and FPoT group, the prefix of the group (in perm)
-  // whose channels have PoT ≥ 7, and the exactness bound Σ_k 2^PoT_k.
-  for (int idx = tid; idx < kTiles * (kBins + 1); idx += kThreads) {
-    const int i = idx / (kBins + 1);
-    off_s[idx] = i < tiles_here ? a.group_off[(tile0 + i) * (kBins + 1) + idx % (kBins + 1)] : 0;
+  // ---- Dense ring: every channel with PoT ≤ 6, natural order, 64 channels
+  // per chunk, filled by direct global-to-LDS loads (no registers): A = the
+  // 128 rows of aligned codes, shared by the four waves; B = each wave's 64
+  // columns of W^T.  Both tiles are [row][64 channels] with the 16-byte
+  // columns XOR-swizzled by row, (column ^ (row / 4) % 4), so the fragment
+  // reads (one ds_read_b128) are free of bank conflicts.  A direct load
+  // writes lane l's 16 bytes at base + 16·l: one wave instruction fills 16
+  // rows.  Each wave issues 2 A and 4 B instructions per chunk.
+  auto stageA = [&](int st) { return smem + st * kStageDense; };
+  auto stageB = [&](int st, int w) { return smem + st * kStageDense + BM * BK + w * WN * BK; };
+  const int r16 = lane >> 2;                       // row of this lane within a 16-row group
+  const int c16 = (lane & 3) ^ ((r16 >> 2) & 3);   // global 16-byte column it loads
+  const int64_t nchunks = K / BK;
+  auto issue = [&](int64_t c, int st) {
+    const int64_t k0 = c * BK;
+    const bool live = c < nchunks;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = 16 * (2 * wave + j) + r16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_ac, (lds_ptr)(stageA(st) + 1024 * (2 * wave + j)), 16,
+                                               live ? (uint32_t)(row * K + k0 + 16 * c16) : kOob, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = nw + 16 * j + r16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_wt, (lds_ptr)(stageB(st, wave) + 1024 * j), 16,
+                                               live && n < N ? (uint32_t)(n * K + k0 + 16 * c16) : kOob, 0, 0, 0);
+    }
+  };
+
+  // ---- Meta, overlapped with the first dense chunks: per tile and FPoT
+  // group the prefix of the group (in perm) whose channels have PoT ≥ 7, the
+  // exactness bound Σ_k 2^PoT_k, and the schedule of gathered units (32-row
+  // block major, then group, then 32-channel step).
+  // (Unconditional loads: the compiler then waits for exactly these, not for
+  // the dense loads issued after them.)
+  const rsrc_t r_off = make_rsrc(a.group_off + tile0 * (kBins + 1), (uint32_t)(tiles_here * (kBins + 1) * 4));
+  uint32_t go[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int idx = tid + kThreads * m;
+    go[m] = __builtin_amdgcn_raw_buffer_load_b32(r_off, idx < kTiles * (kBins + 1) ? (uint32_t)(4 * idx) : kOob, 0, 0);
   }
-  __syncthreads();
+  __asm__ __volatile__("" ::: "memory");   // keep these loads ahead of the dense ones
+#pragma unroll
+  for (int c = 0; c < kStages - 1; ++c) issue(c, c);   // a chunk past K loads zeros
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int idx = tid + kThreads * m;
+    if (idx < kTiles * (kBins + 1)) off_s[idx] = (int32_t)go[m];
+  }
+  bar_lds();
   if (tid < kTiles * kTags) {
     const int i = tid / kTags, g = tid % kTags;
     const int e = DSTAR_FMDQ_TAG_OFFSET - g;
@@ -234,27 +321,63 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
       b += (unsigned long long)(o[4 * g + 4 - pc] - o[4 * g + 3 - pc]) << (e + 2 * pc);
     bpart[tid] = b;
   }
-  __syncthreads();
-  if (tid < kTiles) {
+  bar_lds();
+  if (wave == 0) {
+    // lane = 16 · (32-row block) + group
+    const int rb = lane >> 4, g = lane & 15, i = (32 * rb) / T;
     unsigned long long b = 0;
-    for (int g = 0; g < kTags; ++g) b += bpart[tid * kTags + g];
-    eligible[tid] = (tid < tiles_here && b <= kBoundLimit) ? 1 : 0;
-  }
-  __syncthreads();
-  if (tid < kTags) {
-    int m = 0;
+    for (int g2 = 0; g2 < kTags; ++g2) b += bpart[i * kTags + g2];
+    const bool el = i < tiles_here && b <= kBoundLimit;
+    if (g == 0 && (32 * rb) % T == 0) eligible[i] = el ? 1 : 0;
+    int v = el ? (rcount[i * kTags + g] + KS - 1) / KS : 0;
 #pragma unroll
-    for (int i = 0; i < kTiles; ++i)
-      if (eligible[i]) m = max(m, (rcount[i * kTags + tid] + KS - 1) / KS);
-    steps_g[tid] = m;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int n = __shfl_up(v, o, 64);
+      if (lane >= o) v += n;
+    }
+    ustart[lane + 1] = v;
+    if (lane == 0) ustart[0] = 0;
   }
-  __syncthreads();
-  if (tid == 0) {
-    cum[0] = 0;
-    for (int g = 0; g < kTags; ++g) cum[g + 1] = cum[g] + steps_g[g];
-  }
-  __syncthreads();
-  const int nsteps = cum[kTags];
+  bar_lds();
+  const int U = ustart[RB * kTags];   // gathered units of this workgroup
+
+  // Channel ids of units [ubase, ubase + kBatch): thread → (unit, 8 ids).
+  // fetch() issues the loads into registers, commit() writes them to LDS.
+  uint32_t fid[8], fok, finfo;
+  auto fetch = [&](int ubase) {
+    const int uu = ubase + (tid >> 2), qq = tid & 3;
+    int lo = 0;
+#pragma unroll
+    for (int st = 32; st >= 1; st >>= 1)   // largest x with ustart[x] <= uu
+      if (lo + st < RB * kTags && ustart[lo + st] <= uu) lo += st;
+    const bool valid = uu < U;
+    const int rb = lo >> 4, g = lo & 15, i = (32 * rb) / T;
+    const int s = uu - ustart[lo];
+    const int cnt = valid ? rcount[i * kTags + g] : 0;
+    const int64_t base = (int64_t)i * K + rstart[i * kTags + g];
+    // (The loaded ids are only touched in commit(), so the loads stay in
+    // flight until then.)
+    fok = 0;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int pos = KS * s + 8 * qq + jj;
+      const bool ok = pos < cnt;
+      fid[jj] = __builtin_amdgcn_raw_buffer_load_b16(r_perm, ok ? (uint32_t)((base + pos) * 2) : kOob, 0, 0);
+      fok |= (ok ? 1u : 0u) << jj;
+    }
+    finfo = (uint32_t)i | ((uint32_t)(rb % (T / 32)) << 2);
+  };
+  auto commit = [&]() {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) fid[jj] = ((fok >> jj) & 1u) ? (fid[jj] & 0xFFFFu) : 0xFFFFu;
+    uint4 p;
+    p.x = fid[0] | (fid[1] << 16);
+    p.y = fid[2] | (fid[3] << 16);
+    p.z = fid[4] | (fid[5] << 16);
+    p.w = fid[6] | (fid[7] << 16);
+    *reinterpret_cast<uint4*>(ent + (tid >> 2) * KS + 8 * (tid & 3)) = p;
+    if ((tid & 3) == 0) uinfo[tid >> 2] = finfo;
+  };
 
   v16i acc[RB][CB];
 #pragma unroll
@@ -264,133 +387,14 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0;
 
-  // ---- Gathered FPoT groups, Horner form: ascending tag = descending step.
-  // Step f of the workgroup covers entries 32·s .. 32·s + 31 of group g's
-  // prefix in every tile.  Thread roles: A piece (tile iA, entry jA, 16-byte
-  // piece subA of the channel's T codes); B pieces (entry jB, columns
-  // n0 + 16·cB .. +15 and n0 + 128 + 16·cB .. +15) of every tile.
-  {
-    constexpr int kPieces = T / 16;
-    const int iA = tid / (KS * kPieces), jA = (tid / kPieces) % KS, subA = tid % kPieces;
-    const int jB = tid >> 3, cB = tid & 7;
-    auto step_group = [&](int f, int& g, int& s) {
-      g = 0;
-      while (cum[g + 1] <= f) ++g;
-      s = f - cum[g];
-    };
-    // Entries: the channel id (low 16 bits) and a valid flag (bit 16).
-    uint32_t eA, eB[kTiles];
-    uint4 dA, dB[kTiles][2];
-    auto entry = [&](int i, int g, int j) -> uint32_t {
-      const int cnt = eligible[i] ? rcount[i * kTags + g] : 0;
-      const bool valid = j < cnt;
-      const uint32_t off = (uint32_t)(i * K + rstart[i * kTags + g] + j) * 2u;
-      return (__builtin_amdgcn_raw_buffer_load_b16(r_perm, valid ? off : kOob, 0, 0) & 0xFFFFu) |
-             (valid ? 0x10000u : 0u);
-    };
-    auto entries = [&](int f) {
-      int g, s;
-      step_group(f, g, s);
-      eA = entry(iA, g, KS * s + jA);
-#pragma unroll
-      for (int i = 0; i < kTiles; ++i) eB[i] = entry(i, g, KS * s + jB);
-    };
-    auto data = [&]() {
-      const uint32_t chA = eA & 0xFFFFu;
-      dA = bload16(r_codes, (eA >> 16) ? (uint32_t)((iA * K + chA) * T + 16 * subA) : kOob);
-#pragma unroll
-      for (int i = 0; i < kTiles; ++i) {
-        const uint32_t ch = eB[i] & 0xFFFFu;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int64_t n = n0 + 128 * u + 16 * cB;
-          dB[i][u] = load_w16<VecW>(r_w, (uint32_t)(ch * N + n), n, N, (eB[i] >> 16) && n < N);
-        }
-      }
-    };
-    auto store = [&]() {
-      st_u128(smem + jA * SA + T * iA + 16 * subA, dA);
-#pragma unroll
-      for (int i = 0; i < kTiles; ++i)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          st_u128(smem + KS * SA + i * KS * SB + jB * SB + 128 * u + 16 * cB, dB[i][u]);
-    };
-    int prev_e[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) prev_e[rb] = -1;
-    if (nsteps > 0) {
-      entries(0);
-      data();
-      if (nsteps > 1) entries(1);
-      for (int f = 0; f < nsteps; ++f) {
-        __syncthreads();                 // the previous step's fragments are read
-        store();
-        __syncthreads();
-        if (f + 1 < nsteps) data();      // entries of step f+1 arrived one step ago
-        if (f + 2 < nsteps) entries(f + 2);
-        int g, s;
-        step_group(f, g, s);
-        const int e = DSTAR_FMDQ_TAG_OFFSET - g;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const int i = (32 * rb) / T;
-          const int cnt = eligible[i] ? rcount[i * kTags + g] : 0;
-          if (KS * s >= cnt) continue;
-          if (s == 0) {
-            if (prev_e[rb] >= 0) {
-#pragma unroll
-              for (int cb = 0; cb < CB; ++cb) shift_acc(acc[rb][cb], prev_e[rb] - e);
-            }
-            prev_e[rb] = e;
-          }
-          const v4i af = tr_frag<SA>(smem, 0, 32 * rb, lane);
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) {
-            const v4i bf = tr_frag<SB>(smem + KS * SA + i * KS * SB, 0, WN * wave + 32 * cb, lane);
-            acc[rb][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf, acc[rb][cb], 0, 0, 0);
-          }
-        }
-      }
-    }
-    // Bring the gathered groups to units of the base (step 2^0).
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      if (prev_e[rb] > 0) {
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) shift_acc(acc[rb][cb], prev_e[rb]);
-      }
-  }
+  // The ids of the first gathered units are loaded now and held in registers
+  // through the dense loop (eight loads, issued even when there is no unit,
+  // so that the loop's first two waits can count them).
+  fetch(0);
+  __asm__ __volatile__("" ::: "memory");
 
-  // ---- Dense part: every channel with PoT ≤ 6, natural order, 64 channels
-  // per chunk through a ring of kStages LDS stages filled by direct
-  // global-to-LDS loads (no registers): A = the 128 rows of aligned codes,
-  // shared by the four waves; B = each wave's 64 columns of W^T.  Both tiles
-  // are [row][64 channels] with the 16-byte columns XOR-swizzled by row,
-  // (column ^ (row / 4) % 4), so the fragment reads (one ds_read_b128) are
-  // free of bank conflicts.  A direct load writes lane l's 16 bytes at
-  // base + 16·l: one wave instruction fills 16 rows.
+  // ---- Dense loop.
   {
-    auto stageA = [&](int st) { return smem + st * kStageDense; };
-    auto stageB = [&](int st, int w) { return smem + st * kStageDense + BM * BK + w * WN * BK; };
-    const int r16 = lane >> 2;                       // row of this lane within a 16-row group
-    const int c16 = (lane & 3) ^ ((r16 >> 2) & 3);   // global 16-byte column it loads
-    // Each wave issues 2 A and 4 B instructions per chunk.
-    auto issue = [&](int64_t c, int st) {
-      const int64_t k0 = c * BK;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = 16 * (2 * wave + j) + r16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_ac, (lds_ptr)(stageA(st) + 1024 * (2 * wave + j)), 16,
-                                                 (uint32_t)(row * K + k0 + 16 * c16), 0, 0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t n = nw + 16 * j + r16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_wt, (lds_ptr)(stageB(st, wave) + 1024 * j), 16,
-                                                 n < N ? (uint32_t)(n * K + k0 + 16 * c16) : kOob, 0, 0, 0);
-      }
-    };
     auto frag = [&](const uint8_t* tile, int row, int c) {
       return *reinterpret_cast<const v4i*>(tile + row * BK + 16 * (c ^ ((row >> 2) & 3)));
     };
@@ -409,24 +413,19 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
             acc[rb][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[rb], bf[cb], acc[rb][cb], 0, 0, 0);
       }
     };
-
-    const int64_t nchunks = K / BK;
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // no other vector loads in flight
-    __syncthreads();                        // the gathered steps are done with LDS
-#pragma unroll
-    for (int c = 0; c < kStages - 1; ++c)
-      if (c < nchunks) issue(c, c);
     for (int64_t c = 0; c < nchunks; ++c) {
       // Chunk c's loads are done once at most one later chunk is in flight.
-      // A bare s_barrier then makes every wave's part of chunk c visible and
+      // The barrier then makes every wave's part of chunk c visible and
       // guarantees every wave is done with chunk c - 1 (whose stage the next
-      // loads overwrite).  (__syncthreads would also wait for the loads still
-      // in flight, which is what the stages are there to avoid.)  The empty
-      // asm statements keep the compiler from moving LDS reads across.
-      if (c + 1 < nchunks) {
-        __builtin_amdgcn_s_waitcnt(kWaitVmChunk);
-      } else {
+      // loads overwrite).
+      // (In the first two iterations the eight id loads issued after chunk 1
+      // may also be in flight.)
+      if (c + 1 >= nchunks) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      } else if (c < 2) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmChunkIds);
+      } else {
+        __builtin_amdgcn_s_waitcnt(kWaitVmChunk);
       }
       __asm__ __volatile__("" ::: "memory");
       __builtin_amdgcn_s_barrier();
@@ -436,16 +435,159 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     }
   }
 
-  // ---- Epilogue: dequantize, add the cached output, store (float64 combine).
-  // Y is streamed once: its loads and stores are non-temporal so they do not
-  // evict W and the codes from the caches.  In interior blocks the 32 loads
-  // of one 32-row block of the wave are issued before their stores.  Offsets
-  // are 32-bit, relative to this workgroup's first row.
+  // ---- Epilogue set-up.  Y is streamed once: its loads and stores are
+  // non-temporal so they do not evict W and the codes from the caches.  In
+  // interior blocks the epilogue runs over (32-row block, 32-column block)
+  // units, loading the next unit's Y_{t−1} before storing the current one;
+  // the first unit's loads are issued here, under the gathered phase.
+  // Offsets are 32-bit, relative to this workgroup's first row.
   const double base = a.base;
   bool all_eligible = true;
 #pragma unroll
   for (int i = 0; i < kTiles; ++i) all_eligible = all_eligible && eligible[i];
   const bool interior = all_eligible && (tile0 * T + BM <= a.rows) && (nw + WN <= N);
+  constexpr int kNt = 2;   // aux bit: non-temporal
+  const rsrc_t r_yp = make_rsrc(a.y_prev + tile0 * T * N, (uint32_t)(BM * N * 4));
+  const rsrc_t r_yo = make_rsrc(a.y_out + tile0 * T * N, (uint32_t)(BM * N * 4));
+  const uint32_t lane_off = (uint32_t)(((4 * h) * N + nw + li) * 4);
+  const uint32_t row4 = (uint32_t)(N * 4);
+  auto y_off = [&](int rb, int cb, int r) {
+    return lane_off + (uint32_t)(32 * rb + 8 * (r >> 2) + (r & 3)) * row4 + 128 * cb;
+  };
+  float ypa[16], ypb[16];
+  auto load_y = [&](float (&dst)[16], int rb, int cb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      dst[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_yp, y_off(rb, cb, r), 0, kNt));
+  };
+  if (interior) load_y(ypa, 0, 0);
+
+  // ---- Gathered FPoT groups (channels with PoT ≥ 7), per 32-row block.
+  // Unit v occupies ring stage v % kUnits: A = [32 channels][32 rows] codes,
+  // B = [32 channels][256 columns] of W, swizzled.  Each wave loads 256 bytes
+  // of A (dword loads: channel 8·wave + lane/8, dword lane % 8) and a quarter
+  // of B.  Columns past N only feed outputs that are never stored.
+  if (U > 0) {
+    commit();
+    bar_lds();   // ids visible; every wave is done with the dense ring
+    int ubase = 0, u = 0, issued = 0;
+    // Unit starts: lane x holds ustart[x] (x < 64), read with readlane.
+    const int us_lane = ustart[lane];
+    auto us_at = [&](int x) -> int { return x >= RB * kTags ? U : __builtin_amdgcn_readlane(us_lane, x); };
+    // The ids one wave needs for one unit's loads (all LDS reads first, so
+    // they share one wait).
+    constexpr int kNB = VecW ? 2 : 8;
+    struct UnitIds {
+      uint32_t inf, chA, chB[kNB];
+    };
+    auto load_ids = [&](int v, UnitIds& d) {
+      const uint16_t* en = ent + (v - ubase) * KS;
+      d.inf = uinfo[v - ubase];
+      d.chA = en[8 * wave + (lane >> 3)];
+#pragma unroll
+      for (int m = 0; m < kNB; ++m)
+        d.chB[m] = VecW ? en[4 * (2 * wave + m) + (lane >> 4)] : en[8 * wave + m];
+    };
+    auto issue_ids = [&](int v, const UnitIds& d) {
+      const int i = (int)(d.inf & 3u);
+      const int rowoff = 32 * (int)(d.inf >> 2);
+      uint8_t* sA = smem + (v % kUnits) * kUnitBytes;
+      uint8_t* sB = sA + kUnitA;
+      {
+        const uint32_t off =
+            d.chA != 0xFFFFu ? (uint32_t)(((int64_t)i * K + d.chA) * T + rowoff + 4 * (lane & 7)) : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_codes, (lds_ptr)(sA + 256 * wave), 4, off, 0, 0, 0);
+      }
+#pragma unroll
+      for (int m = 0; m < kNB; ++m) {
+        const uint32_t ch = d.chB[m];
+        if constexpr (VecW) {
+          const int jj = 2 * wave + m;            // channels 4·jj .. 4·jj + 3
+          const int c = 4 * jj + (lane >> 4);
+          const int piece = (lane & 15) ^ (c & 7);
+          const uint32_t off = ch != 0xFFFFu ? (uint32_t)((int64_t)ch * N + n0 + 16 * piece) : kOob;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr)(sB + 1024 * jj), 16, off, 0, 0, 0);
+        } else {
+          const int c = 8 * wave + m;             // one channel row of 256 bytes
+          const int piece = (lane >> 2) ^ (c & 7);
+          const uint32_t off =
+              ch != 0xFFFFu ? (uint32_t)((int64_t)ch * N + n0 + 16 * piece + 4 * (lane & 3)) : kOob;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr)(sB + BN * c), 4, off, 0, 0, 0);
+        }
+      }
+    };
+    auto issue_unit = [&](int v) {
+      UnitIds d;
+      load_ids(v, d);
+      issue_ids(v, d);
+    };
+    auto issue_upto = [&](int lim) {
+      for (; issued < lim; ++issued) issue_unit(issued);
+    };
+    issue_upto(min(U, min(ubase + kBatch, kAhead)));
+    // One gathered unit: wait for its loads, barrier, refill the ring, MFMA.
+    auto step = [&](v16i (&tmp)[CB]) {
+      if (u == ubase + kBatch) {
+        bar_lds();   // every wave is done with the previous ids (no loads in flight)
+        ubase = u;
+        fetch(ubase);
+        commit();
+        bar_lds();
+        issue_upto(min(U, min(ubase + kBatch, u + kAhead)));
+      }
+      const int hi = min(U, ubase + kBatch);
+      // The next unit's ids are read before the wait (their stage is only
+      // written after the barrier).
+      const bool more = issued < min(hi, u + kAhead + 1);
+      UnitIds nx;
+      if (more) load_ids(issued, nx);
+      wait_units<kOpsUnit>(min(kAhead - 1, hi - 1 - u));
+      __asm__ __volatile__("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      __asm__ __volatile__("" ::: "memory");
+      if (more) {
+        issue_ids(issued, nx);
+        ++issued;
+      }
+      const uint8_t* sA = smem + (u % kUnits) * kUnitBytes;
+      v4i af = tr_frag<32>(sA, 0, lane);
+      v4i bf0 = tr_frag_wsw(sA + kUnitA, WN * wave, lane);
+      v4i bf1 = tr_frag_wsw(sA + kUnitA, WN * wave + 32, lane);
+      lgkm_wait(af, bf0, bf1);
+      tmp[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf0, tmp[0], 0, 0, 0);
+      tmp[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf1, tmp[1], 0, 0, 0);
+      ++u;
+    };
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if (us_at((rb + 1) * kTags) == us_at(rb * kTags)) continue;
+      v16i tmp[CB];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tmp[cb][r] = 0;
+      int prev_e = -1;
+      for (int g = 0; g < kTags; ++g) {
+        const int nst = us_at(rb * kTags + g + 1) - us_at(rb * kTags + g);
+        if (nst == 0) continue;
+        const int e = DSTAR_FMDQ_TAG_OFFSET - g;
+        if (prev_e >= 0) {
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) shift_acc(tmp[cb], prev_e - e);
+        }
+        prev_e = e;
+        for (int s = 0; s < nst; ++s) step(tmp);
+      }
+      // Bring the gathered groups to units of the base and add them.
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[rb][cb][r] = (int)((uint32_t)acc[rb][cb][r] + ((uint32_t)tmp[cb][r] << prev_e));
+    }
+  }
+
+  // ---- Epilogue: dequantize, add the cached output, store (float64 combine).
   double ws[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
@@ -453,31 +595,19 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     ws[cb] = n < N ? (double)a.w_scale[n] : 0.0;
   }
   if (interior) {
-    constexpr int kNt = 2;   // aux bit: non-temporal
-    const rsrc_t r_yp = make_rsrc(a.y_prev + tile0 * T * N, (uint32_t)(BM * N * 4));
-    const rsrc_t r_yo = make_rsrc(a.y_out + tile0 * T * N, (uint32_t)(BM * N * 4));
-    const uint32_t lane_off = (uint32_t)(((4 * h) * N + nw + li) * 4);
-    const uint32_t row4 = (uint32_t)(N * 4);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float yp[CB][16];
+    for (int v = 0; v < RB * CB; ++v) {
+      const int rb = v / CB, cb = v % CB;
+      float (&cur)[16] = (v & 1) ? ypb : ypa;
+      float (&nxt)[16] = (v & 1) ? ypa : ypb;
+      if (v + 1 < RB * CB) load_y(nxt, (v + 1) / CB, (v + 1) % CB);
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t off = lane_off + (uint32_t)(32 * rb + 8 * (r >> 2) + (r & 3)) * row4 + 128 * cb;
-          yp[cb][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_yp, off, 0, kNt));
-        }
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t off = lane_off + (uint32_t)(32 * rb + 8 * (r >> 2) + (r & 3)) * row4 + 128 * cb;
-          const double d = __dmul_rn(__dmul_rn((double)acc[rb][cb][r], base), ws[cb]);
-          const float y = (float)__dadd_rn((double)yp[cb][r], d);
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, y), r_yo, off, 0, kNt);
-        }
-      // keep each row block's loads, math and stores together (bounds the
+      for (int r = 0; r < 16; ++r) {
+        const double d = __dmul_rn(__dmul_rn((double)acc[rb][cb][r], base), ws[cb]);
+        const float y = (float)__dadd_rn((double)cur[r], d);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, y), r_yo, y_off(rb, cb, r), 0, kNt);
+      }
+      // keep each unit's loads, math and stores in this order (bounds the
       // registers the epilogue holds at once)
       __builtin_amdgcn_sched_barrier(0);
     }
