@@ -430,26 +430,54 @@ def test_code_rounding_is_half_to_even():
 
 
 # ------------------------------------------------------------------ P13 ------
-@pytest.mark.parametrize("seed,rows,K,N,T", [(31, 96, 64, 24, 32), (32, 70, 40, 8, 32), (33, 128, 36, 12, 64)])
-def test_aligned_codes_split_S_into_8_bit_part_and_wide_groups(seed, rows, K, N, T):
-    """S = (aligned codes) @ W + Σ over PoT ≥ 7 channels of q·2^e·W, exactly;
-    the aligned codes fit int8, equal q·2^e where PoT ≤ 6 and 0 elsewhere."""
-    d = wl.make_custom(rows, K, N, T, seed=seed, heavy=0.3, c_range=(0.5, 64.0))
+def test_code_digits_reconstruct_every_shift_aligned_code():
+    """a = d0 + 2^7·d1 + 2^15·d2 for every value a code can take in units of
+    the base (|q·2^e| ≤ 2^PoT ≤ 2^21), with every digit in 8 bits, and no third
+    digit while |a| ≤ 2^13 (brute force over the whole range)."""
+    a = np.arange(-(1 << 21), (1 << 21) + 1, dtype=np.int64)
+    d0, d1, d2 = fmdq.code_digits(a)
+    np.testing.assert_array_equal(d0 + 128 * d1 + 32768 * d2, a)
+    assert d0.min() == -64 and d0.max() == 63
+    assert d1.min() >= -128 and d1.max() <= 127
+    assert d2.min() >= -64 and d2.max() <= 64
+    small = np.abs(a) <= (1 << 13)
+    assert not d2[small].any() and np.abs(d1[small]).max() <= 64
+    # a few values by hand: 64 = -64 + 2^7; 2^21 = 64·2^15; -65 = 63 - 2^7
+    for v, want in ((64, (-64, 1, 0)), (1 << 21, (0, 0, 64)), (-65, (63, -1, 0)), (-1, (-1, 0, 0))):
+        got = tuple(int(x[0]) for x in fmdq.code_digits(np.array([v])))
+        assert got == want, (v, got)
+
+
+@pytest.mark.parametrize("seed,rows,K,N,T,c_range", [(31, 96, 64, 24, 32, (0.5, 64.0)),
+                                                     (32, 70, 40, 8, 32, (0.5, 64.0)),
+                                                     (33, 128, 36, 12, 64, (0.5, 64.0)),
+                                                     (34, 64, 48, 16, 32, (0.02, 4000.0))])
+def test_aligned_codes_and_digit_planes_split_S_exactly(seed, rows, K, N, T, c_range):
+    """S = A·W + 2^7·(D1·W) + 2^15·(D2·W) per tile, exactly, against the
+    per-FPoT-group sum; A = q·2^e where PoT ≤ 6; digit planes zero where the
+    sub-channel does not need them."""
+    d = wl.make_custom(rows, K, N, T, seed=seed, heavy=0.3, c_range=c_range)
     codes, tags, _ = fmdq.quantize(d["x_t"], d["x_prev"], T, d["base"], d["k0"])
     a = fmdq.aligned_codes(codes, tags)
+    h = fmdq.heavy_digits(codes, tags)
     nt = codes.shape[0]
     assert a.shape == (nt * T, K) and a.dtype == np.int8
+    assert h.shape == (2, nt, K, T) and h.dtype == np.int8
     e = fmdq.step_exponent(fmdq.tag_of(tags))
     pot = e + fmdq.bits_of(tags) - 2
     assert (pot > 6).any() and (pot <= 6).any()
+    if c_range[1] > 1000:
+        assert (pot > 13).any()          # the third digit is exercised
     perm, off = fmdq.bucket(tags)
     w = d["w"].astype(np.int64)
     for tau in range(nt):
         at = a[tau * T:(tau + 1) * T].astype(np.int64)                     # [T][K]
         qt = codes[tau].T.astype(np.int64)                                   # [T][K]
-        wide = pot[tau] > 6
-        np.testing.assert_array_equal(at[:, wide], 0)
-        np.testing.assert_array_equal(at[:, ~wide], qt[:, ~wide] << e[tau][~wide])
-        wide_part = np.matmul(qt[:, wide] << e[tau][wide], w[wide])
+        light = pot[tau] <= 6
+        np.testing.assert_array_equal(at[:, light], qt[:, light] << e[tau][light])
+        d1 = h[0, tau].T.astype(np.int64)
+        d2 = h[1, tau].T.astype(np.int64)
+        np.testing.assert_array_equal(d1[:, light], 0)
+        np.testing.assert_array_equal(d2[:, pot[tau] <= 13], 0)
         s = fmdq.shift_combine(fmdq.group_accumulators(codes[tau], perm[tau], off[tau], d["w"]))
-        np.testing.assert_array_equal(np.matmul(at, w) + wide_part, s)
+        np.testing.assert_array_equal(at @ w + 128 * (d1 @ w) + 32768 * (d2 @ w), s)
