@@ -288,13 +288,14 @@ def main() -> int:
             ev = events[L] if events is not None else None
             if ev is not None:
                 ev[0].record(stream)
-            dm.quantize(lay.p, x_t, x_p, lay.codes, lay.tags, lay.acodes, lay.bit_hist)
+            dm.quantize(lay.p, x_t, x_p, lay.codes, lay.tags, lay.acodes, lay.hcodes, lay.bit_hist)
             if ev is not None:
                 ev[1].record(stream)
             dm.bucket(lay.p, lay.tags, lay.perm, lay.group_off)
             if ev is not None:
                 ev[2].record(stream)
-            dm.linear(lay.p, s["N"], lay.codes, lay.perm, lay.group_off, lay.acodes, lay.w, lay.w_t,
+            dm.linear(lay.p, s["N"], lay.codes, lay.perm, lay.group_off, lay.acodes, lay.hcodes, lay.w,
+                      lay.w_t,
                       lay.w_scale,
                       s["y"], s["y"])
             if ev is not None:

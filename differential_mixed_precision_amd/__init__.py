@@ -41,6 +41,7 @@ class FmdqLayer:
         self.codes = torch.empty((nt, self.K, token_tile), dtype=torch.int8, device=dev)
         self.tags = torch.empty((nt, self.K), dtype=torch.uint8, device=dev)
         self.acodes = torch.empty((nt * token_tile, self.K), dtype=torch.int8, device=dev)
+        self.hcodes = torch.empty((2, nt, self.K, token_tile), dtype=torch.int8, device=dev)
         self.w_t = torch.empty((self.N, self.K), dtype=torch.int8, device=dev)
         pack_weights(self.K, self.N, self.w, self.w_t)
         self.perm = torch.empty((nt, self.K), dtype=torch.int16, device=dev)  # uint16 ids
@@ -48,10 +49,10 @@ class FmdqLayer:
         self.bit_hist = torch.zeros(4, dtype=torch.int32, device=dev)
 
     def step(self, x_t, x_prev, y, y_out=None, stream=None, hist: bool = True):
-        quantize(self.p, x_t, x_prev, self.codes, self.tags, self.acodes,
+        quantize(self.p, x_t, x_prev, self.codes, self.tags, self.acodes, self.hcodes,
                  self.bit_hist if hist else None, stream)
         bucket(self.p, self.tags, self.perm, self.group_off, stream)
         out = y if y_out is None else y_out
-        linear(self.p, self.N, self.codes, self.perm, self.group_off, self.acodes, self.w, self.w_t,
-               self.w_scale, y, out, stream=stream)
+        linear(self.p, self.N, self.codes, self.perm, self.group_off, self.acodes, self.hcodes,
+               self.w, self.w_t, self.w_scale, y, out, stream=stream)
         return out

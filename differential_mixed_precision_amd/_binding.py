@@ -20,7 +20,7 @@ TAG_OFFSET = 15
 POT_MAX = 21
 PREC_SHIFT = 4
 MAX_K = 65535
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 SYMBOLS = ("dstar_fmdq_quantize", "dstar_fmdq_bucket", "dstar_fmdq_pack_weights",
            "dstar_fmdq_linear", "dstar_fmdq_last_error", "dstar_fmdq_abi_version")
@@ -55,13 +55,13 @@ def load() -> ctypes.CDLL:
     P = ctypes.POINTER(Params)
     vp = ctypes.c_void_p
     i32 = ctypes.c_int32
-    lib.dstar_fmdq_quantize.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    lib.dstar_fmdq_quantize.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.dstar_fmdq_quantize.restype = ctypes.c_int
     lib.dstar_fmdq_bucket.argtypes = [P, vp, vp, vp, vp]
     lib.dstar_fmdq_bucket.restype = ctypes.c_int
     lib.dstar_fmdq_pack_weights.argtypes = [i32, i32, vp, vp, vp]
     lib.dstar_fmdq_pack_weights.restype = ctypes.c_int
-    lib.dstar_fmdq_linear.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
+    lib.dstar_fmdq_linear.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
     lib.dstar_fmdq_linear.restype = ctypes.c_int
     lib.dstar_fmdq_last_error.argtypes = []
     lib.dstar_fmdq_last_error.restype = ctypes.c_char_p
@@ -101,10 +101,12 @@ def make_params(rows: int, K: int, token_tile: int, base: float, thr0_log2: int,
                   int(token_tile), float(base), int(thr0_log2))
 
 
-def quantize(p: Params, x_t, x_prev, codes, tags, acodes=None, bit_hist=None, stream=None) -> None:
+def quantize(p: Params, x_t, x_prev, codes, tags, acodes=None, hcodes=None, bit_hist=None,
+             stream=None) -> None:
     """dstar_fmdq_quantize."""
     _check(load().dstar_fmdq_quantize(ctypes.byref(p), _ptr(x_t), _ptr(x_prev), _ptr(codes),
-                                      _ptr(tags), _ptr(acodes), _ptr(bit_hist), _stream(stream)))
+                                      _ptr(tags), _ptr(acodes), _ptr(hcodes), _ptr(bit_hist),
+                                      _stream(stream)))
 
 
 def bucket(p: Params, tags, perm, group_off, stream=None) -> None:
@@ -118,10 +120,10 @@ def pack_weights(K: int, N: int, w, w_t, stream=None) -> None:
     _check(load().dstar_fmdq_pack_weights(int(K), int(N), _ptr(w), _ptr(w_t), _stream(stream)))
 
 
-def linear(p: Params, N: int, codes, perm, group_off, acodes, w, w_t, w_scale, y_prev, y_out,
-           acc_dbg=None, dbg_tile_lo: int = 0, dbg_tile_hi: int = 0, stream=None) -> None:
+def linear(p: Params, N: int, codes, perm, group_off, acodes, hcodes, w, w_t, w_scale, y_prev,
+           y_out, acc_dbg=None, dbg_tile_lo: int = 0, dbg_tile_hi: int = 0, stream=None) -> None:
     """dstar_fmdq_linear."""
     _check(load().dstar_fmdq_linear(ctypes.byref(p), int(N), _ptr(codes), _ptr(perm),
-                                    _ptr(group_off), _ptr(acodes), _ptr(w), _ptr(w_t),
+                                    _ptr(group_off), _ptr(acodes), _ptr(hcodes), _ptr(w), _ptr(w_t),
                                     _ptr(w_scale), _ptr(y_prev), _ptr(y_out), _ptr(acc_dbg),
                                     int(dbg_tile_lo), int(dbg_tile_hi), _stream(stream)))

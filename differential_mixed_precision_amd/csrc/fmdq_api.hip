@@ -68,8 +68,8 @@ int dstar_fmdq_abi_version(void) { return DSTAR_FMDQ_ABI_VERSION; }
 const char* dstar_fmdq_last_error(void) { return g_error.c_str(); }
 
 int dstar_fmdq_quantize(const dstar_fmdq_params* p, const float* x_t, const float* x_prev,
-                        int8_t* codes, uint8_t* tags, int8_t* acodes, uint32_t* bit_hist,
-                        void* stream) {
+                        int8_t* codes, uint8_t* tags, int8_t* acodes, int8_t* hcodes,
+                        uint32_t* bit_hist, void* stream) {
   clear_error();
   int64_t nt = 0;
   if (int rc = check_params(p, &nt)) return rc;
@@ -81,14 +81,18 @@ int dstar_fmdq_quantize(const dstar_fmdq_params* p, const float* x_t, const floa
                      "quantize: x_t, x_prev and codes must be 16-byte aligned, tags 4-byte aligned");
   if (bit_hist && !aligned(bit_hist, 4))
     return set_error(DSTAR_EALIGN, "quantize: bit_hist must be 4-byte aligned");
-  if (acodes && !aligned(acodes, 16))
-    return set_error(DSTAR_EALIGN, "quantize: acodes must be 16-byte aligned");
+  if ((acodes == nullptr) != (hcodes == nullptr))
+    return set_error(DSTAR_ENULL, "quantize: acodes and hcodes must both be given or both be NULL");
+  if ((acodes && !aligned(acodes, 16)) || (hcodes && !aligned(hcodes, 16)))
+    return set_error(DSTAR_EALIGN, "quantize: acodes and hcodes must be 16-byte aligned");
   QuantizeArgs a;
   a.x_t = x_t;
   a.x_prev = x_prev;
   a.codes = codes;
   a.tags = tags;
   a.acodes = acodes;
+  a.hcodes = hcodes;
+  a.plane = nt * (int64_t)p->K * p->token_tile;
   a.bit_hist = bit_hist;
   a.rows = p->rows;
   a.K = p->K;
@@ -132,7 +136,8 @@ int dstar_fmdq_pack_weights(int32_t K, int32_t N, const int8_t* w, int8_t* w_t, 
 
 int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N, const int8_t* codes,
                       const uint16_t* perm, const int32_t* group_off,
-                      const int8_t* acodes, const int8_t* w, const int8_t* w_t,
+                      const int8_t* acodes, const int8_t* hcodes, const int8_t* w,
+                      const int8_t* w_t,
                       const float* w_scale, const float* y_prev, float* y_out, int32_t* acc_dbg,
                       int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream) {
   clear_error();
@@ -150,15 +155,16 @@ int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N, const int8_t* codes
   if (!aligned(codes, 16) || !aligned(w, 16) || !aligned(y_prev, 16) || !aligned(y_out, 16) ||
       !aligned(w_scale, 4) || !aligned(perm, 2) || !aligned(group_off, 4) ||
       (acc_dbg && !aligned(acc_dbg, 4)) || (acodes && !aligned(acodes, 16)) ||
-      (w_t && !aligned(w_t, 16)))
+      (hcodes && !aligned(hcodes, 16)) || (w_t && !aligned(w_t, 16)))
     return set_error(DSTAR_EALIGN,
-                     "linear: codes, acodes, w, w_t, y_prev, y_out must be 16-byte aligned "
+                     "linear: codes, acodes, hcodes, w, w_t, y_prev, y_out must be 16-byte aligned "
                      "(w_scale, group_off, acc_dbg 4-byte, perm 2-byte)");
   LinearArgs a;
   a.codes = codes;
   a.perm = perm;
   a.group_off = group_off;
   a.acodes = acodes;
+  a.hcodes = hcodes;
   a.w = w;
   a.w_t = w_t;
   a.w_scale = w_scale;

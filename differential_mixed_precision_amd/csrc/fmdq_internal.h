@@ -24,6 +24,8 @@ struct QuantizeArgs {
   int8_t* codes;
   uint8_t* tags;
   int8_t* acodes;
+  int8_t* hcodes;     // digit planes [2][n_t][K][T] (with acodes)
+  int64_t plane;      // n_t * K * T: offset of the second plane
   uint32_t* bit_hist;
   int64_t rows;
   int32_t K;
@@ -48,6 +50,7 @@ struct LinearArgs {
   const uint16_t* perm;
   const int32_t* group_off;
   const int8_t* acodes;
+  const int8_t* hcodes;
   const int8_t* w;
   const int8_t* w_t;
   const float* w_scale;

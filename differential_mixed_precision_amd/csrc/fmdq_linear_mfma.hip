@@ -77,6 +77,7 @@ constexpr int KS = 32;             // channels per MFMA k-step (= per gathered u
 constexpr int kTags = DSTAR_FMDQ_NUM_TAGS;
 constexpr int kBins = DSTAR_FMDQ_NUM_BINS;
 constexpr int kAlignedPotMax = 6;  // q·2^e fits int8 when PoT ≤ 6
+constexpr int kTwoDigitPotMax = 13;  // q·2^e needs no third digit when PoT ≤ 13
 constexpr uint64_t kBoundLimit = 2147483647ull / 127ull;  // Σ 2^PoT limit
 constexpr int kBand = 8;           // row blocks per band of the block order
 
@@ -87,25 +88,27 @@ struct Cfg {
 
 // LDS carve-up (bytes).  The data region holds either the dense ring
 // (kStages stages of (A 128 rows + B 256 rows) × 64 bytes) or, after the
-// dense loop, the gathered ring (kUnits stages of A 32 channels × 32 rows +
-// B 32 channels × 256 columns).  Both are 72 KiB, so two workgroups fit per CU.
+// dense loop, the gathered ring (kUnits stages of A 64 channels × 32 rows +
+// B 64 channels × 256 columns).  Both are 72 KiB, so two workgroups fit per CU.
 constexpr int kStages = 3;
 constexpr int kStageDense = (BM + BN) * BK;                // 24576
-constexpr int kUnitA = KS * 32;                            // 1024
-constexpr int kUnitB = KS * BN;                            // 8192
-constexpr int kUnitBytes = kUnitA + kUnitB;                // 9216
-constexpr int kUnits = 8;                                  // gathered ring stages
+constexpr int KU = 64;                                     // channels per gathered unit
+constexpr int kUnitA = KU * 32;                            // 2048
+constexpr int kUnitB = KU * BN;                            // 16384
+constexpr int kUnitBytes = kUnitA + kUnitB;                // 18432
+constexpr int kUnits = 4;                                  // gathered ring stages
 constexpr int kAhead = kUnits - 1;                         // units in flight ahead
-constexpr int kBatch = 64;                                 // units whose ids are staged
+constexpr int kBatch = 32;                                 // units whose ids are staged
 constexpr int kDataBytes = kStages * kStageDense;          // 73728
 static_assert(kUnits * kUnitBytes == kDataBytes, "the two rings share one region");
-constexpr int kOffEnt = kDataBytes;                        // uint16 [kBatch][32] channel ids
-constexpr int kOffBp = kOffEnt + kBatch * KS * 2;          // uint64 [4][16] bound parts
+constexpr int kOffEnt = kDataBytes;                        // uint16 [kBatch][KU] channel ids
+constexpr int kOffBp = kOffEnt + kBatch * KU * 2;          // uint64 [4][16] bound parts
 constexpr int kOffOff = kOffBp + 4 * kTags * 8;            // int32 [4][65] bin offsets
-constexpr int kOffRs = kOffOff + 4 * (kBins + 1) * 4;      // int32 [4][16] prefix starts
-constexpr int kOffRc = kOffRs + 4 * kTags * 4;             // int32 [4][16] prefix lengths
-constexpr int kOffUs = kOffRc + 4 * kTags * 4;             // int32 [65] (+pad) unit starts
-constexpr int kOffUi = kOffUs + 68 * 4;                    // uint32 [kBatch] unit tile/rows
+constexpr int kOffRs = kOffOff + 4 * (kBins + 1) * 4;      // int32 [4][16] group starts in perm
+constexpr int kOffRc = kOffRs + 4 * kTags * 4;             // int32 [2][4][16] digit-list lengths
+constexpr int kOffPre = kOffRc + 2 * 4 * kTags * 4;        // int32 [2][4][17] their prefix sums
+constexpr int kOffUs = kOffPre + 2 * 4 * 17 * 4;           // int32 [9] (+pad) unit starts
+constexpr int kOffUi = kOffUs + 12 * 4;                    // uint32 [kBatch] unit tile/rows/plane
 constexpr int kOffElig = kOffUi + kBatch * 4;              // int32 [4]
 constexpr int kLdsBytes = kOffElig + 4 * 4;
 static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per CU");
@@ -187,36 +190,23 @@ __device__ __forceinline__ void shift_acc(v16i& acc, int s) {
   for (int r = 0; r < 16; ++r) acc[r] = (int)((uint32_t)acc[r] << s);
 }
 
-// Waits until at most `ops * after` vector-memory operations of this wave are
-// in flight (after = 0 .. kAhead - 1).
-template <int ops>
-__device__ __forceinline__ void wait_units(int after) {
-  switch (after) {
-    case 0: __builtin_amdgcn_s_waitcnt(wait_vm(0)); break;
-    case 1: __builtin_amdgcn_s_waitcnt(wait_vm(ops * 1)); break;
-    case 2: __builtin_amdgcn_s_waitcnt(wait_vm(ops * 2)); break;
-    case 3: __builtin_amdgcn_s_waitcnt(wait_vm(ops * 3)); break;
-    case 4: __builtin_amdgcn_s_waitcnt(wait_vm(ops * 4)); break;
-    case 5: __builtin_amdgcn_s_waitcnt(wait_vm(ops * 5)); break;
-    default: __builtin_amdgcn_s_waitcnt(wait_vm(ops * 6)); break;
-  }
-}
-
 template <int T, bool VecW>
 __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, int32_t row_blocks,
                                                                   int32_t col_blocks) {
   constexpr int kTiles = Cfg<T>::kTiles;
-  // Direct-to-LDS loads per wave per gathered unit: one dword load of codes,
-  // and the W rows as two 16-byte or eight 4-byte loads.
-  constexpr int kOpsUnit = VecW ? 3 : 9;
+  // Direct-to-LDS loads per wave per gathered unit: two dword loads of digit
+  // codes, and the W rows as four 16-byte or sixteen 4-byte loads.
+  constexpr int kOpsUnit = VecW ? 6 : 18;
+  constexpr int kWaitVmUnits = wait_vm(kOpsUnit * (kAhead - 1));   // unit u landed
   static_assert(kOpsUnit * (kAhead - 1) <= 63, "vmcnt range");
   extern __shared__ __align__(16) uint8_t smem[];
-  uint16_t* ent = reinterpret_cast<uint16_t*>(smem + kOffEnt);         // [kBatch][32]
+  uint16_t* ent = reinterpret_cast<uint16_t*>(smem + kOffEnt);         // [kBatch][KU]
   unsigned long long* bpart = reinterpret_cast<unsigned long long*>(smem + kOffBp);
   int32_t* off_s = reinterpret_cast<int32_t*>(smem + kOffOff);          // [kTiles][65]
   int32_t* rstart = reinterpret_cast<int32_t*>(smem + kOffRs);          // [kTiles][16]
-  int32_t* rcount = reinterpret_cast<int32_t*>(smem + kOffRc);          // [kTiles][16]
-  int32_t* ustart = reinterpret_cast<int32_t*>(smem + kOffUs);          // [65]
+  int32_t* rc = reinterpret_cast<int32_t*>(smem + kOffRc);              // [2][4][16]
+  int32_t* pre = reinterpret_cast<int32_t*>(smem + kOffPre);            // [2][4][17]
+  int32_t* ustart = reinterpret_cast<int32_t*>(smem + kOffUs);          // [9]
   uint32_t* uinfo = reinterpret_cast<uint32_t*>(smem + kOffUi);         // [kBatch]
   int32_t* eligible = reinterpret_cast<int32_t*>(smem + kOffElig);      // [kTiles]
 
@@ -285,9 +275,11 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   };
 
   // ---- Meta, overlapped with the first dense chunks: per tile and FPoT
-  // group the prefix of the group (in perm) whose channels have PoT ≥ 7, the
-  // exactness bound Σ_k 2^PoT_k, and the schedule of gathered units (32-row
-  // block major, then group, then 32-channel step).
+  // group the prefixes of the group (in perm) whose channels have PoT ≥ 7
+  // (second digit) and PoT ≥ 14 (third digit), the exactness bound
+  // Σ_k 2^PoT_k, and the schedule of gathered units: per 32-row block the
+  // third-digit list, then the second-digit list (each the concatenation of
+  // the tile's group prefixes), 64 channels per unit.
   // (Unconditional loads: the compiler then waits for exactly these, not for
   // the dense loads issued after them.)
   const rsrc_t r_off = make_rsrc(a.group_off + tile0 * (kBins + 1), (uint32_t)(tiles_here * (kBins + 1) * 4));
@@ -310,11 +302,14 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     const int i = tid / kTags, g = tid % kTags;
     const int e = DSTAR_FMDQ_TAG_OFFSET - g;
     const int32_t* o = off_s + i * (kBins + 1);
-    // PoT = e + 2·pc ≥ 7  <=>  pc ≥ ceil((7 − e) / 2); bins of group g run
-    // from precision code 3 (bin 4g) down to 0 (bin 4g + 3).
-    const int pcmin = max(0, (kAlignedPotMax + 2 - e) / 2);
+    // PoT = e + 2·pc.  Bins of group g run from precision code 3 (bin 4g)
+    // down to 0 (bin 4g + 3), so the channels with pc ≥ pcmin are the first
+    // o[4g + 4 − pcmin] − o[4g] of the group.
+    const int pc7 = max(0, (kAlignedPotMax + 2 - e) / 2);     // PoT ≥ 7
+    const int pc14 = max(0, (kTwoDigitPotMax + 2 - e) / 2);   // PoT ≥ 14
     rstart[tid] = o[4 * g];
-    rcount[tid] = pcmin <= 3 ? o[4 * g + 4 - pcmin] - o[4 * g] : 0;
+    rc[tid] = pc7 <= 3 ? o[4 * g + 4 - pc7] - o[4 * g] : 0;
+    rc[4 * kTags + tid] = pc14 <= 3 ? o[4 * g + 4 - pc14] - o[4 * g] : 0;
     unsigned long long b = 0;
 #pragma unroll
     for (int pc = 0; pc < 4; ++pc)
@@ -323,51 +318,81 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   }
   bar_lds();
   if (wave == 0) {
-    // lane = 16 · (32-row block) + group
-    const int rb = lane >> 4, g = lane & 15, i = (32 * rb) / T;
+    // lane = 16 · tile + group
+    const int i = lane >> 4, g = lane & 15;
+    const bool tile_ok = i < kTiles;
     unsigned long long b = 0;
-    for (int g2 = 0; g2 < kTags; ++g2) b += bpart[i * kTags + g2];
-    const bool el = i < tiles_here && b <= kBoundLimit;
-    if (g == 0 && (32 * rb) % T == 0) eligible[i] = el ? 1 : 0;
-    int v = el ? (rcount[i * kTags + g] + KS - 1) / KS : 0;
+    if (tile_ok)
+      for (int g2 = 0; g2 < kTags; ++g2) b += bpart[i * kTags + g2];
+    const bool el = tile_ok && i < tiles_here && b <= kBoundLimit;
+    if (tile_ok && g == 0) eligible[i] = el ? 1 : 0;
+    // Inclusive prefix sums of both list lengths over the tile's groups.
+    int s0 = tile_ok ? rc[lane] : 0, s1 = tile_ok ? rc[4 * kTags + lane] : 0;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
+    for (int o = 1; o < 16; o <<= 1) {
+      const int n0 = __shfl_up(s0, o, 16), n1 = __shfl_up(s1, o, 16);
+      if (g >= o) {
+        s0 += n0;
+        s1 += n1;
+      }
+    }
+    if (tile_ok) {
+      pre[i * 17 + g + 1] = s0;
+      pre[4 * 17 + i * 17 + g + 1] = s1;
+      if (g == 0) {
+        pre[i * 17] = 0;
+        pre[4 * 17 + i * 17] = 0;
+      }
+    }
+    // Units of (32-row block rb, slot x & 1): slot 0 = third digits, slot 1 =
+    // second digits; unit starts by an exclusive scan over x = 2·rb + slot.
+    const int x = lane & 7, ti = (32 * (x >> 1)) / T;
+    const int tot0 = __shfl(s0, ti * 16 + 15, 64), tot1 = __shfl(s1, ti * 16 + 15, 64);
+    const int elx = __shfl(el ? 1 : 0, ti * 16, 64);
+    int v = (lane < 8 && elx) ? (((x & 1) ? tot0 : tot1) + KU - 1) / KU : 0;
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
       const int n = __shfl_up(v, o, 64);
       if (lane >= o) v += n;
     }
-    ustart[lane + 1] = v;
+    if (lane < 8) ustart[lane + 1] = v;
     if (lane == 0) ustart[0] = 0;
   }
   bar_lds();
-  const int U = ustart[RB * kTags];   // gathered units of this workgroup
+  const int U = ustart[2 * RB];   // gathered units of this workgroup
 
   // Channel ids of units [ubase, ubase + kBatch): thread → (unit, 8 ids).
   // fetch() issues the loads into registers, commit() writes them to LDS.
   uint32_t fid[8], fok, finfo;
-  auto fetch = [&](int ubase) {
-    const int uu = ubase + (tid >> 2), qq = tid & 3;
-    int lo = 0;
+  auto fetch = [&](int ubase) __attribute__((always_inline)) {
+    const int uu = ubase + (tid >> 3), q8 = tid & 7;
+    int x = 0;
 #pragma unroll
-    for (int st = 32; st >= 1; st >>= 1)   // largest x with ustart[x] <= uu
-      if (lo + st < RB * kTags && ustart[lo + st] <= uu) lo += st;
+    for (int st = 4; st >= 1; st >>= 1)   // largest x with ustart[x] <= uu
+      if (x + st < 2 * RB && ustart[x + st] <= uu) x += st;
     const bool valid = uu < U;
-    const int rb = lo >> 4, g = lo & 15, i = (32 * rb) / T;
-    const int s = uu - ustart[lo];
-    const int cnt = valid ? rcount[i * kTags + g] : 0;
-    const int64_t base = (int64_t)i * K + rstart[i * kTags + g];
+    const int rb = x >> 1, lvl = (x & 1) ? 0 : 1, i = (32 * rb) / T;
+    const int32_t* pr = pre + lvl * 4 * 17 + i * 17;
+    const int total = valid ? pr[16] : 0;
+    int pos = KU * (uu - ustart[x]) + 8 * q8;
+    int g = 0;
+#pragma unroll
+    for (int st = 8; st >= 1; st >>= 1)   // group of pos: largest g with pr[g] <= pos
+      if (g + st < kTags && pr[g + st] <= pos) g += st;
     // (The loaded ids are only touched in commit(), so the loads stay in
     // flight until then.)
     fok = 0;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int pos = KS * s + 8 * qq + jj;
-      const bool ok = pos < cnt;
-      fid[jj] = __builtin_amdgcn_raw_buffer_load_b16(r_perm, ok ? (uint32_t)((base + pos) * 2) : kOob, 0, 0);
+    for (int jj = 0; jj < 8; ++jj, ++pos) {
+      while (g + 1 < kTags && pr[g + 1] <= pos) ++g;
+      const bool ok = pos < total;
+      const uint32_t off = ok ? (uint32_t)(((int64_t)i * K + rstart[i * kTags + g] + (pos - pr[g])) * 2) : kOob;
+      fid[jj] = __builtin_amdgcn_raw_buffer_load_b16(r_perm, off, 0, 0);
       fok |= (ok ? 1u : 0u) << jj;
     }
-    finfo = (uint32_t)i | ((uint32_t)(rb % (T / 32)) << 2);
+    finfo = (uint32_t)i | ((uint32_t)(rb % (T / 32)) << 2) | ((uint32_t)lvl << 3);
   };
-  auto commit = [&]() {
+  auto commit = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) fid[jj] = ((fok >> jj) & 1u) ? (fid[jj] & 0xFFFFu) : 0xFFFFu;
     uint4 p;
@@ -375,8 +400,8 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     p.y = fid[2] | (fid[3] << 16);
     p.z = fid[4] | (fid[5] << 16);
     p.w = fid[6] | (fid[7] << 16);
-    *reinterpret_cast<uint4*>(ent + (tid >> 2) * KS + 8 * (tid & 3)) = p;
-    if ((tid & 3) == 0) uinfo[tid >> 2] = finfo;
+    *reinterpret_cast<uint4*>(ent + (tid >> 3) * KU + 8 * (tid & 7)) = p;
+    if ((tid & 7) == 0) uinfo[tid >> 3] = finfo;
   };
 
   v16i acc[RB][CB];
@@ -438,8 +463,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   // ---- Epilogue set-up.  Y is streamed once: its loads and stores are
   // non-temporal so they do not evict W and the codes from the caches.  In
   // interior blocks the epilogue runs over (32-row block, 32-column block)
-  // units, loading the next unit's Y_{t−1} before storing the current one;
-  // the first unit's loads are issued here, under the gathered phase.
+  // units, loading the next unit's Y_{t−1} before storing the current one.
   // Offsets are 32-bit, relative to this workgroup's first row.
   const double base = a.base;
   bool all_eligible = true;
@@ -460,131 +484,142 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     for (int r = 0; r < 16; ++r)
       dst[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_yp, y_off(rb, cb, r), 0, kNt));
   };
-  if (interior) load_y(ypa, 0, 0);
 
-  // ---- Gathered FPoT groups (channels with PoT ≥ 7), per 32-row block.
-  // Unit v occupies ring stage v % kUnits: A = [32 channels][32 rows] codes,
-  // B = [32 channels][256 columns] of W, swizzled.  Each wave loads 256 bytes
-  // of A (dword loads: channel 8·wave + lane/8, dword lane % 8) and a quarter
-  // of B.  Columns past N only feed outputs that are never stored.
+  // ---- Channels with PoT ≥ 7, per 32-row block: their second digits
+  // (and, for PoT ≥ 14, third digits) times W, added to the dense sum at
+  // shifts 7 and 15.  Unit v (64 channels of one list) occupies ring stage
+  // v % kUnits: A = [64 channels][32 rows] digit codes, B = [64 channels][256
+  // columns] of W, swizzled.  Each wave loads 512 bytes of A (dword loads:
+  // channel 8·m + lane/8, dword lane % 8, for its two m) and a quarter of B.
+  // Every step issues exactly one unit (past the end of the list its loads
+  // read nothing and write zeros into a free stage), so every wait is the
+  // same count.  Columns past N only feed outputs that are never stored.
   if (U > 0) {
     commit();
     bar_lds();   // ids visible; every wave is done with the dense ring
-    int ubase = 0, u = 0, issued = 0;
-    // Unit starts: lane x holds ustart[x] (x < 64), read with readlane.
-    const int us_lane = ustart[lane];
-    auto us_at = [&](int x) -> int { return x >= RB * kTags ? U : __builtin_amdgcn_readlane(us_lane, x); };
+    int ubase = 0, u = 0;
+    // Unit starts: lane x holds ustart[x] (x ≤ 8), read with readlane.
+    const int us_lane = ustart[min(lane, 2 * RB)];
+    auto us_at = [&](int x) -> int { return __builtin_amdgcn_readlane(us_lane, x); };
+    // Both digit planes of this workgroup's tiles through one resource: the
+    // second plane starts plane_off bytes after the first (n_t·K·T < 2^31).
+    const uint32_t plane_off = (uint32_t)(nt * K * T);
+    const rsrc_t r_h = make_rsrc(a.hcodes + tile0 * K * T, plane_off + (uint32_t)(tiles_here * K * T));
     // The ids one wave needs for one unit's loads (all LDS reads first, so
     // they share one wait).
-    constexpr int kNB = VecW ? 2 : 8;
+    constexpr int kNB = VecW ? 4 : 16;
     struct UnitIds {
-      uint32_t inf, chA, chB[kNB];
+      uint32_t inf, chA[2], chB[kNB];
     };
-    auto load_ids = [&](int v, UnitIds& d) {
-      const uint16_t* en = ent + (v - ubase) * KS;
-      d.inf = uinfo[v - ubase];
-      d.chA = en[8 * wave + (lane >> 3)];
+    auto load_ids = [&](int v, UnitIds& d) __attribute__((always_inline)) {
+      const int vb = min(v - ubase, kBatch - 1);
+      const uint16_t* en = ent + vb * KU;
+      d.inf = uinfo[vb];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) d.chA[m] = en[8 * (2 * wave + m) + (lane >> 3)];
 #pragma unroll
       for (int m = 0; m < kNB; ++m)
-        d.chB[m] = VecW ? en[4 * (2 * wave + m) + (lane >> 4)] : en[8 * wave + m];
+        d.chB[m] = VecW ? en[4 * (4 * wave + m) + (lane >> 4)] : en[16 * wave + m];
     };
-    auto issue_ids = [&](int v, const UnitIds& d) {
+    auto issue_ids = [&](int v, const UnitIds& d, bool live) __attribute__((always_inline)) {
       const int i = (int)(d.inf & 3u);
-      const int rowoff = 32 * (int)(d.inf >> 2);
+      const int rowoff = 32 * (int)((d.inf >> 2) & 1u);
+      const uint32_t poff = (d.inf & 8u) ? plane_off : 0u;
       uint8_t* sA = smem + (v % kUnits) * kUnitBytes;
       uint8_t* sB = sA + kUnitA;
-      {
-        const uint32_t off =
-            d.chA != 0xFFFFu ? (uint32_t)(((int64_t)i * K + d.chA) * T + rowoff + 4 * (lane & 7)) : kOob;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_codes, (lds_ptr)(sA + 256 * wave), 4, off, 0, 0, 0);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int mm = 2 * wave + m;              // channels 8·mm .. 8·mm + 7
+        const uint32_t ch = d.chA[m];
+        const uint32_t off = live && ch != 0xFFFFu
+                                 ? poff + (uint32_t)(((int64_t)i * K + ch) * T + rowoff + 4 * (lane & 7)) : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_h, (lds_ptr)(sA + 256 * mm), 4, off, 0, 0, 0);
       }
 #pragma unroll
       for (int m = 0; m < kNB; ++m) {
         const uint32_t ch = d.chB[m];
         if constexpr (VecW) {
-          const int jj = 2 * wave + m;            // channels 4·jj .. 4·jj + 3
+          const int jj = 4 * wave + m;            // channels 4·jj .. 4·jj + 3
           const int c = 4 * jj + (lane >> 4);
           const int piece = (lane & 15) ^ (c & 7);
-          const uint32_t off = ch != 0xFFFFu ? (uint32_t)((int64_t)ch * N + n0 + 16 * piece) : kOob;
+          const uint32_t off = live && ch != 0xFFFFu ? (uint32_t)((int64_t)ch * N + n0 + 16 * piece) : kOob;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr)(sB + 1024 * jj), 16, off, 0, 0, 0);
         } else {
-          const int c = 8 * wave + m;             // one channel row of 256 bytes
+          const int c = 16 * wave + m;            // one channel row of 256 bytes
           const int piece = (lane >> 2) ^ (c & 7);
-          const uint32_t off =
-              ch != 0xFFFFu ? (uint32_t)((int64_t)ch * N + n0 + 16 * piece + 4 * (lane & 3)) : kOob;
+          const uint32_t off = live && ch != 0xFFFFu
+                                   ? (uint32_t)((int64_t)ch * N + n0 + 16 * piece + 4 * (lane & 3)) : kOob;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr)(sB + BN * c), 4, off, 0, 0, 0);
         }
       }
     };
-    auto issue_unit = [&](int v) {
+    auto issue_unit = [&](int v) __attribute__((always_inline)) {
       UnitIds d;
       load_ids(v, d);
-      issue_ids(v, d);
+      issue_ids(v, d, v < min(U, ubase + kBatch));
     };
-    auto issue_upto = [&](int lim) {
-      for (; issued < lim; ++issued) issue_unit(issued);
-    };
-    issue_upto(min(U, min(ubase + kBatch, kAhead)));
-    // One gathered unit: wait for its loads, barrier, refill the ring, MFMA.
-    auto step = [&](v16i (&tmp)[CB]) {
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) issue_unit(j);
+    // One unit: wait for its loads, barrier, refill the ring, MFMA.
+    auto step = [&](v16i (&tmp)[CB]) __attribute__((always_inline)) {
       if (u == ubase + kBatch) {
-        bar_lds();   // every wave is done with the previous ids (no loads in flight)
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        bar_lds();   // every wave is done with the previous ids
         ubase = u;
         fetch(ubase);
         commit();
         bar_lds();
-        issue_upto(min(U, min(ubase + kBatch, u + kAhead)));
+#pragma unroll
+        for (int j = 0; j < kAhead; ++j) issue_unit(u + j);
       }
-      const int hi = min(U, ubase + kBatch);
-      // The next unit's ids are read before the wait (their stage is only
+      // The ids of unit u + kAhead are read before the wait (its stage is only
       // written after the barrier).
-      const bool more = issued < min(hi, u + kAhead + 1);
       UnitIds nx;
-      if (more) load_ids(issued, nx);
-      wait_units<kOpsUnit>(min(kAhead - 1, hi - 1 - u));
+      load_ids(u + kAhead, nx);
+      const bool live = u + kAhead < min(U, ubase + kBatch);
+      __builtin_amdgcn_s_waitcnt(kWaitVmUnits);
       __asm__ __volatile__("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       __asm__ __volatile__("" ::: "memory");
-      if (more) {
-        issue_ids(issued, nx);
-        ++issued;
-      }
+      issue_ids(u + kAhead, nx, live);
       const uint8_t* sA = smem + (u % kUnits) * kUnitBytes;
-      v4i af = tr_frag<32>(sA, 0, lane);
-      v4i bf0 = tr_frag_wsw(sA + kUnitA, WN * wave, lane);
-      v4i bf1 = tr_frag_wsw(sA + kUnitA, WN * wave + 32, lane);
-      lgkm_wait(af, bf0, bf1);
-      tmp[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf0, tmp[0], 0, 0, 0);
-      tmp[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bf1, tmp[1], 0, 0, 0);
+      const uint8_t* sB = sA + kUnitA;
+#pragma unroll
+      for (int ks = 0; ks < KU / KS; ++ks) {
+        v4i af = tr_frag<32>(sA + ks * KS * 32, 0, lane);
+        v4i b0 = tr_frag_wsw(sB + ks * KS * BN, WN * wave, lane);
+        v4i b1 = tr_frag_wsw(sB + ks * KS * BN, WN * wave + 32, lane);
+        lgkm_wait(af, b0, b1);
+        tmp[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, b0, tmp[0], 0, 0, 0);
+        tmp[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, b1, tmp[1], 0, 0, 0);
+      }
       ++u;
     };
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      if (us_at((rb + 1) * kTags) == us_at(rb * kTags)) continue;
+      const int n2 = us_at(2 * rb + 1) - us_at(2 * rb);       // third-digit units
+      const int n1 = us_at(2 * rb + 2) - us_at(2 * rb + 1);   // second-digit units
+      if (n1 + n2 == 0) continue;
       v16i tmp[CB];
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) tmp[cb][r] = 0;
-      int prev_e = -1;
-      for (int g = 0; g < kTags; ++g) {
-        const int nst = us_at(rb * kTags + g + 1) - us_at(rb * kTags + g);
-        if (nst == 0) continue;
-        const int e = DSTAR_FMDQ_TAG_OFFSET - g;
-        if (prev_e >= 0) {
+      for (int s = 0; s < n2 + n1; ++s) {
+        if (s == n2 && n2 > 0) {   // third digits done: tmp = Σ d2·W · 2^8
 #pragma unroll
-          for (int cb = 0; cb < CB; ++cb) shift_acc(tmp[cb], prev_e - e);
+          for (int cb = 0; cb < CB; ++cb) shift_acc(tmp[cb], 8);
         }
-        prev_e = e;
-        for (int s = 0; s < nst; ++s) step(tmp);
+        step(tmp);
       }
-      // Bring the gathered groups to units of the base and add them.
+      // acc += (Σ d1·W + 2^8 Σ d2·W) · 2^7
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          acc[rb][cb][r] = (int)((uint32_t)acc[rb][cb][r] + ((uint32_t)tmp[cb][r] << prev_e));
+          acc[rb][cb][r] = (int)((uint32_t)acc[rb][cb][r] + ((uint32_t)tmp[cb][r] << 7));
     }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the loads issued past the last unit
   }
 
   // ---- Epilogue: dequantize, add the cached output, store (float64 combine).
@@ -595,6 +630,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     ws[cb] = n < N ? (double)a.w_scale[n] : 0.0;
   }
   if (interior) {
+    load_y(ypa, 0, 0);
 #pragma unroll
     for (int v = 0; v < RB * CB; ++v) {
       const int rb = v / CB, cb = v % CB;
@@ -712,7 +748,8 @@ int launch_t(const LinearArgs& a, hipStream_t s) {
 // chunks) and W below 2^31 bytes (32-bit buffer offsets), given the aligned
 // codes and W^T.
 bool linear_mfma_supported(const LinearArgs& a) {
-  return a.acodes != nullptr && a.w_t != nullptr && (a.T == 32 || a.T == 64) && (a.K % 64) == 0 &&
+  return a.acodes != nullptr && a.hcodes != nullptr && a.w_t != nullptr && (a.T == 32 || a.T == 64) &&
+         (a.K % 64) == 0 && n_tiles(a.rows, a.T) * a.K * a.T < (int64_t(1) << 31) &&
          (int64_t)a.K * a.N < (int64_t(1) << 31);
 }
 

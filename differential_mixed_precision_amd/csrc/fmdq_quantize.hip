@@ -11,7 +11,11 @@
 // against base*2^j and quantize their rows.  Each lane writes its half of a
 // channel's T codes (codes are channel-major within a tile: a contiguous run
 // per lane), its rows of the aligned codes (one CPT-byte word per row), and
-// the even lane writes the tags and counts the bit histogram.
+// the even lane writes the tags and counts the bit histogram.  A code in units
+// of the base, a = q·2^e, is the aligned code itself when PoT ≤ 6; otherwise
+// it is split into signed digits a = d0 + 2^7·d1 + 2^15·d2: d0 goes to the
+// aligned codes, d1 (PoT ≥ 7) and d2 (PoT ≥ 14) to the two digit planes, laid
+// out like the codes.
 #include "fmdq_internal.h"
 
 namespace dstar {
@@ -64,8 +68,20 @@ __device__ __forceinline__ void store_codes(int8_t* dst, const int (&q)[RT]) {
   }
 }
 
+// Stores RT bytes packed four to a word (RT = 8, 16 or 32).
+template <int RT>
+__device__ __forceinline__ void store_words(int8_t* dst, const uint32_t (&w)[RT / 4]) {
+  if constexpr (RT == 8) {
+    *reinterpret_cast<int2*>(dst) = make_int2((int)w[0], (int)w[1]);
+  } else {
+#pragma unroll
+    for (int v = 0; v < RT / 16; ++v)
+      reinterpret_cast<int4*>(dst)[v] = make_int4((int)w[4 * v], (int)w[4 * v + 1], (int)w[4 * v + 2], (int)w[4 * v + 3]);
+  }
+}
+
 template <int T, int CPT>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantizeArgs a, int64_t n_work,
+__global__ __launch_bounds__(kThreads, (T == 64 ? 1 : 3)) void quantize_kernel(QuantizeArgs a, int64_t n_work,
                                                             int32_t slabs) {
   constexpr int RT = T / 2;                  // rows per lane
   uint32_t hist[4] = {0u, 0u, 0u, 0u};
@@ -99,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantizeArgs a, int6
 
     uint32_t tagword = 0;
     // Aligned codes of the CPT channels, one packed word per row (q·2^e when
-    // PoT ≤ 6, else 0): the 8-bit operand of stage 3's dense GEMM.
+    // PoT ≤ 6, else its low digit): the 8-bit operand of stage 3's dense GEMM.
     uint32_t arow[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) arow[t] = 0u;
@@ -128,16 +144,36 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantizeArgs a, int6
         r = fminf(fmaxf(rintf(r), -pceil), pceil);
         q[t] = (int)r;
       }
+      // This lane's RT codes of channel k+c: bytes half*RT .. half*RT+RT-1 of
+      // the channel's run at codes[(tile*K + k + c)*T].
+      const int64_t run = (tile * K + k + c) * T + half * RT;
+      store_codes<RT>(a.codes + run, q);
       if (pot <= 6) {
 #pragma unroll
         for (int t = 0; t < RT; ++t) arow[t] |= (((uint32_t)q[t] << e) & 0xFFu) << (8 * c);
+      } else if (a.acodes != nullptr) {
+        // Digits of a = q·2^e (|a| ≤ 2^21): d0 in [−64, 63], d1 in
+        // [−128, 127], d2 (0 unless PoT ≥ 14), packed as they are formed.
+        uint32_t w1[RT / 4], w2[RT / 4];
+#pragma unroll
+        for (int v = 0; v < RT / 4; ++v) w1[v] = w2[v] = 0u;
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          const int av = q[t] * (1 << e);
+          const int d0 = ((av + 64) & 127) - 64;
+          const int r1 = (av - d0) >> 7;
+          const int d1 = ((r1 + 128) & 255) - 128;
+          const int d2 = (r1 - d1) >> 8;
+          arow[t] |= ((uint32_t)d0 & 0xFFu) << (8 * c);
+          w1[t / 4] |= ((uint32_t)d1 & 0xFFu) << (8 * (t % 4));
+          w2[t / 4] |= ((uint32_t)d2 & 0xFFu) << (8 * (t % 4));
+        }
+        store_words<RT>(a.hcodes + run, w1);
+        if (pot > 13) store_words<RT>(a.hcodes + a.plane + run, w2);
       }
       if (half == 0) hist[p >> 1] += 1u;
       const uint32_t tag = (uint32_t)(DSTAR_FMDQ_TAG_OFFSET - e) | ((uint32_t)(p >> 1) << DSTAR_FMDQ_PREC_SHIFT);
       tagword |= tag << (8 * c);
-      // This lane's RT codes of channel k+c: bytes half*RT .. half*RT+RT-1 of
-      // the channel's run at codes[(tile*K + k + c)*T].
-      store_codes<RT>(a.codes + ((tile * K + k + c) * T) + half * RT, q);
     }
     if (a.acodes != nullptr) {
       int8_t* ap = a.acodes + r0 * K + k;

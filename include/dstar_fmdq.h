@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DSTAR_FMDQ_ABI_VERSION 4
+#define DSTAR_FMDQ_ABI_VERSION 5
 
 /* Rule constants (DSTAR §3.1 step 1; readings in the design notes):
  * PCeil of a b-bit sub-channel is 2^(b-2); PoT is capped at POT_MAX so that
@@ -95,10 +95,17 @@ typedef struct {
  *   acodes       NULL, or [n_t*T][K] int8 row-major (out), 16-byte aligned:
  *                the shift-aligned operand of stage 3's dense GEMM (DSTAR
  *                §3.1 step 5: partial sums of different FPoT are aligned by
- *                left shifts; here the codes are shifted before the multiply
- *                when the result still fits 8 bits).  acodes[τT+t][k] =
- *                code * 2^(15-g) if PoT <= 6, else 0 (|value| <= 64); rows
- *                past a ragged end are 0.
+ *                left shifts; here the codes are shifted before the multiply).
+ *                With a = code * 2^(15-g), the code in units of the base
+ *                (|a| <= 2^PoT), split into signed digits
+ *                a = d0 + 2^7*d1 + 2^15*d2 (d0 in [-64, 63], d1 in
+ *                [-128, 127], d2 in [-64, 64]): acodes[τT+t][k] = a if
+ *                PoT <= 6, else d0.  Rows past a ragged end are 0.
+ *   hcodes       NULL (exactly when acodes is NULL), or [2][n_t][K][T] int8
+ *                (out), 16-byte aligned, laid out like codes: plane 0 holds d1
+ *                of every sub-channel with PoT >= 7, plane 1 holds d2 of
+ *                every sub-channel with PoT >= 14.  All other entries are
+ *                left unwritten.
  *   bit_hist     uint32[4] or NULL: counts of sub-channels quantized at
  *                2/4/6/8 bits are ADDED to it (the caller zeroes it).
  * Per sub-channel: M = max |Δ| over the tile's rows; PoT = smallest j in
@@ -107,7 +114,8 @@ typedef struct {
  * fl32(1/base)) * 2^-e)), ±2^(b-2)). */
 int dstar_fmdq_quantize(const dstar_fmdq_params* p, const float* x_t,
                         const float* x_prev, int8_t* codes, uint8_t* tags,
-                        int8_t* acodes, uint32_t* bit_hist, void* stream);
+                        int8_t* acodes, int8_t* hcodes, uint32_t* bit_hist,
+                        void* stream);
 
 /* Stage 2 — reorder the channels of every token tile by FPoT (DSTAR §3.1
  * step 3; §4.2 QPU stage 4), as a stable counting sort over the 64 bins
@@ -139,6 +147,7 @@ int dstar_fmdq_pack_weights(int32_t K, int32_t N, const int8_t* w, int8_t* w_t,
  *              Channel k of FPoT group g of tile τ is multiplied at step
  *              2^(15-g) * base.
  *   acodes     NULL, or stage 1's aligned codes.
+ *   hcodes     NULL, or stage 1's digit planes (given with acodes).
  *   w          [K][N] int8 row-major, 16-byte aligned.
  *   w_t        NULL, or the [N][K] copy made by dstar_fmdq_pack_weights.
  *   w_scale    [N] float32, per-output-channel weight scale.
@@ -153,17 +162,18 @@ int dstar_fmdq_pack_weights(int32_t K, int32_t N, const int8_t* w, int8_t* w_t,
  *              the layer runs in the per-group kernel (slow; for checking).
  * Per output: S = Σ_g acc_g * 2^(15-g) (an exact integer);
  * y_out = fl32(f64(y_prev) + (f64(S) * f64(base)) * f64(w_scale[n])).
- * With acodes and w_t given (T of 32 or 64, K % 64 == 0, K*N < 2^31) the MFMA
- * kernel runs: acodes x w_t for every sub-channel with PoT <= 6, and the
- * channels with PoT >= 7 of every FPoT group (the group's prefix in perm)
- * gathered from codes and w, group by group with left shifts between groups;
- * a token tile whose int32 accumulator it cannot prove exact
- * (127 * Σ_k 2^PoT_k >= 2^31) is finished by a per-group path over perm and
- * group_off.  Otherwise the per-group kernel runs. */
+ * With acodes, hcodes and w_t given (T of 32 or 64, K % 64 == 0, K*N and
+ * n_t*K*T below 2^31) the MFMA kernel runs: S = acodes x w_t + 2^7 * (d1
+ * digits x w) + 2^15 * (d2 digits x w), the digit terms over the channels
+ * with PoT >= 7 (resp. >= 14) of each token tile, which are prefixes of the
+ * FPoT groups in perm; a token tile whose int32 accumulator it cannot prove
+ * exact (127 * Σ_k 2^PoT_k >= 2^31) is finished by a per-group path over perm
+ * and group_off.  Otherwise the per-group kernel runs. */
 int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N,
                       const int8_t* codes, const uint16_t* perm,
                       const int32_t* group_off, const int8_t* acodes,
-                      const int8_t* w, const int8_t* w_t, const float* w_scale,
+                      const int8_t* hcodes, const int8_t* w, const int8_t* w_t,
+                      const float* w_scale,
                       const float* y_prev, float* y_out, int32_t* acc_dbg,
                       int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream);
 

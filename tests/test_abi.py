@@ -61,17 +61,17 @@ def test_params_struct_layout(lib):
 FAKE = 0x10000  # a 64 KiB-aligned address; never dereferenced (calls fail validation first)
 
 
-def _q(lib, p, x=FAKE, xp=FAKE, codes=FAKE, tags=FAKE, acodes=None, hist=None):
+def _q(lib, p, x=FAKE, xp=FAKE, codes=FAKE, tags=FAKE, acodes=None, hcodes=None, hist=None):
     L = lib.load()
     return L.dstar_fmdq_quantize(ctypes.byref(p) if p is not None else None, x, xp, codes, tags, acodes,
-                                 hist, 0)
+                                 hcodes, hist, 0)
 
 
-def _l(lib, p, N=64, codes=FAKE, perm=FAKE, off=FAKE, acodes=None, w=FAKE, w_t=None, ws=FAKE, y0=FAKE,
-       y1=FAKE, dbg=None, lo=0, hi=0):
+def _l(lib, p, N=64, codes=FAKE, perm=FAKE, off=FAKE, acodes=None, hcodes=None, w=FAKE, w_t=None,
+       ws=FAKE, y0=FAKE, y1=FAKE, dbg=None, lo=0, hi=0):
     L = lib.load()
-    return L.dstar_fmdq_linear(ctypes.byref(p), N, codes, perm, off, acodes, w, w_t, ws, y0, y1, dbg, lo,
-                               hi, 0)
+    return L.dstar_fmdq_linear(ctypes.byref(p), N, codes, perm, off, acodes, hcodes, w, w_t, ws, y0, y1,
+                               dbg, lo, hi, 0)
 
 
 @pytest.mark.parametrize("field,value", [
@@ -97,7 +97,7 @@ def test_sequences_must_tile_evenly(lib):
 
 def test_null_and_alignment_errors(lib):
     L = lib.load()
-    assert L.dstar_fmdq_quantize(None, FAKE, FAKE, FAKE, FAKE, None, None, 0) == lib.ENULL
+    assert L.dstar_fmdq_quantize(None, FAKE, FAKE, FAKE, FAKE, None, None, None, 0) == lib.ENULL
     p = lib.make_params(64, 64, 32, 0.05, 2)
     assert _q(lib, p, x=None) == lib.ENULL
     assert _q(lib, p, tags=None) == lib.ENULL
@@ -108,9 +108,13 @@ def test_null_and_alignment_errors(lib):
     assert L.dstar_fmdq_bucket(ctypes.byref(p), FAKE, None, FAKE, 0) == lib.ENULL
     assert L.dstar_fmdq_bucket(ctypes.byref(p), FAKE, FAKE + 1, FAKE, 0) == lib.EALIGN
     assert _l(lib, p, w=None) == lib.ENULL
-    assert _q(lib, p, acodes=FAKE + 4) == lib.EALIGN
-    assert _l(lib, p, acodes=FAKE + 8, w_t=FAKE) == lib.EALIGN
-    assert _l(lib, p, acodes=FAKE, w_t=FAKE + 4) == lib.EALIGN
+    assert _q(lib, p, acodes=FAKE + 4, hcodes=FAKE) == lib.EALIGN
+    assert _q(lib, p, acodes=FAKE, hcodes=FAKE + 8) == lib.EALIGN
+    assert _q(lib, p, acodes=FAKE) == lib.ENULL          # the digit planes come with acodes
+    assert _q(lib, p, hcodes=FAKE) == lib.ENULL
+    assert _l(lib, p, acodes=FAKE + 8, hcodes=FAKE, w_t=FAKE) == lib.EALIGN
+    assert _l(lib, p, acodes=FAKE, hcodes=FAKE + 4, w_t=FAKE) == lib.EALIGN
+    assert _l(lib, p, acodes=FAKE, hcodes=FAKE, w_t=FAKE + 4) == lib.EALIGN
     assert L.dstar_fmdq_pack_weights(0, 16, FAKE, FAKE, 0) == lib.EINVAL
     assert L.dstar_fmdq_pack_weights(16, 0, FAKE, FAKE, 0) == lib.EINVAL
     assert L.dstar_fmdq_pack_weights(16, 16, None, FAKE, 0) == lib.ENULL

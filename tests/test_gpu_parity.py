@@ -56,23 +56,24 @@ def gpu_layer(dm, d, dbg=None, inplace=False, y_prev_np=None):
     codes = torch.full((nt, K, T), 90, dtype=torch.int8, device=dev)
     tags = torch.full((nt, K), 0xEE, dtype=torch.uint8, device=dev)
     acodes = torch.full((nt * T, K), 77, dtype=torch.int8, device=dev)
+    hcodes = torch.full((2, nt, K, T), 66, dtype=torch.int8, device=dev)
     w_t = torch.full((N, K), 55, dtype=torch.int8, device=dev)
     hist = torch.zeros(4, dtype=torch.int32, device=dev)
     perm = torch.full((nt, K), -1, dtype=torch.int16, device=dev)
     off = torch.full((nt, 65), -7, dtype=torch.int32, device=dev)
     y1 = y0 if inplace else torch.full((rows, N), float("nan"), dtype=torch.float32, device=dev)
     dm.pack_weights(K, N, w, w_t)
-    dm.quantize(p, x_t, x_p, codes, tags, acodes, hist)
+    dm.quantize(p, x_t, x_p, codes, tags, acodes, hcodes, hist)
     dm.bucket(p, tags, perm, off)
-    dm.linear(p, N, codes, perm, off, acodes, w, w_t, ws, y0, y1)
-    out = dict(codes=codes, tags=tags, acodes=acodes, w_t=w_t, hist=hist, perm=perm, group_off=off,
-               y=y1)
+    dm.linear(p, N, codes, perm, off, acodes, hcodes, w, w_t, ws, y0, y1)
+    out = dict(codes=codes, tags=tags, acodes=acodes, hcodes=hcodes, w_t=w_t, hist=hist, perm=perm,
+               group_off=off, y=y1)
     if dbg is not None:
         lo, hi = dbg
         acc = torch.full((hi - lo, 16, T, N), 0x7777, dtype=torch.int32, device=dev)
         y0b = torch.from_numpy(y_np).to(dev)
         y2 = torch.full((rows, N), float("nan"), dtype=torch.float32, device=dev)
-        dm.linear(p, N, codes, perm, off, acodes, w, w_t, ws, y0b, y2, acc, lo, hi)
+        dm.linear(p, N, codes, perm, off, acodes, hcodes, w, w_t, ws, y0b, y2, acc, lo, hi)
         out.update(acc=acc, y_dbg=y2)
     torch.cuda.synchronize()
     out = {k: v.cpu().numpy() for k, v in out.items()}
@@ -100,6 +101,13 @@ def check_integer_stages(g, codes, tags, hist, perm, off, what="", w=None):
     np.testing.assert_array_equal(g["codes"], codes, err_msg=f"{what}: codes")
     np.testing.assert_array_equal(g["tags"], tags, err_msg=f"{what}: tags")
     np.testing.assert_array_equal(g["acodes"], fmdq.aligned_codes(codes, tags), err_msg=f"{what}: aligned codes")
+    # digit planes: only the entries stage 1 defines (PoT >= 7, resp. >= 14)
+    pot = fmdq.step_exponent(fmdq.tag_of(tags)) + fmdq.bits_of(tags) - 2
+    h = fmdq.heavy_digits(codes, tags)
+    for plane, lo_pot in ((0, 7), (1, 14)):
+        m = np.broadcast_to((pot >= lo_pot)[:, :, None], codes.shape)
+        np.testing.assert_array_equal(g["hcodes"][plane][m], h[plane][m],
+                                      err_msg=f"{what}: digit plane {plane}")
     if w is not None:
         np.testing.assert_array_equal(g["w_t"], w.T, err_msg=f"{what}: packed weights")
     np.testing.assert_array_equal(g["hist"].astype(np.int64), hist, err_msg=f"{what}: bit histogram")
