@@ -228,6 +228,54 @@ def test_timestep_chain_in_place(dm):
         y_orc, y_gpu = r["y"], g["y"]
 
 
+def test_graph_replay_matches_eager(dm):
+    """One layer step captured in a HIP graph and replayed three times, with
+    eager work and synchronizations between the replays, gives after every
+    replay the same output (bit for bit) as the same number of eager steps;
+    and the eager steps match the oracle's chained outputs."""
+    import torch
+    dev = torch.device("cuda:0")
+    d = wl.make_custom(rows=300, K=1152, N=512, token_tile=32, seed=11, heavy=0.1)
+    rows, T = d["rows"], d["token_tile"]
+    w = torch.from_numpy(d["w"]).to(dev)
+    ws = torch.from_numpy(d["w_scale"]).to(dev)
+    x_t = torch.from_numpy(d["x_t"]).to(dev)
+    x_p = torch.from_numpy(d["x_prev"]).to(dev)
+    layer = dm.FmdqLayer(w, ws, rows, T, float(d["base"]), d["k0"])
+    # eager reference: the output after 1, 2, 3 in-place steps
+    y_e = torch.from_numpy(d["y_prev"]).to(dev)
+    refs = []
+    for _ in range(3):
+        layer.step(x_t, x_p, y_e)
+        refs.append(y_e.cpu().numpy().copy())
+    y_orc = d["y_prev"]
+    for r in range(3):
+        y_orc = fmdq.layer(d["x_t"], d["x_prev"], d["w"], d["w_scale"], y_orc, d["base"], T,
+                           d["k0"])["y"]
+        np.testing.assert_array_equal(refs[r], y_orc, err_msg=f"eager step {r + 1}")
+    # graph: warm up on a side stream, capture one step, replay
+    y_g = torch.from_numpy(d["y_prev"]).to(dev)
+    scratch = torch.empty_like(y_g)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.step(x_t, x_p, y_g.clone(), y_out=scratch)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.step(x_t, x_p, y_g)
+    other = dm.FmdqLayer(w, ws, rows, T, float(d["base"]), d["k0"])
+    for r in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        # eager work between replays, on the same kind of buffers
+        other.step(x_p, x_t, scratch)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y_g.cpu().numpy(), refs[r], err_msg=f"graph replay {r + 1}")
+        log(f"  graph replay {r + 1}: bit-identical to {r + 1} eager steps")
+
+
 FULL = [(1, "fc1"), (1, "fc2"), (2, "qkv"), (2, "fc1"), (2, "fc2"), (3, "fc1"), (3, "fc2"),
         (4, "fc1"), (4, "fc2")]
 
