@@ -2,16 +2,17 @@
 // quantization (DSTAR, arXiv 2607.15846: §2.2 Eq. 1; §3.1 step 1 with Eq. 2-5;
 // §4.2 QPU stages 1-3).
 //
-// HBM-bound streaming kernel.  A pair of adjacent lanes owns CPT adjacent
-// input channels of one token tile; each lane of the pair reads half of the
-// tile's T rows of X_t and X_{t-1} for those channels with CPT-wide vector
-// loads (non-temporal: X is read once), keeps its Δ in registers and reduces
-// max|Δ| per channel; one lane-pair shuffle gives the sub-channel maximum M.
-// Both lanes then pick PoT / precision / tag with exact float32 compares
-// against base*2^j and quantize their rows.  Each lane writes its half of a
-// channel's T codes (codes are channel-major within a tile: a contiguous run
-// per lane), its rows of the aligned codes (one CPT-byte word per row), and
-// the even lane writes the tags and counts the bit histogram.  A code in units
+// HBM-bound streaming kernel.  A group of G = T/16 adjacent lanes (one lane
+// at T = 16) owns CPT adjacent input channels of one token tile; each lane of
+// the group reads 16 of the tile's T rows of X_t and X_{t-1} for those
+// channels with CPT-wide vector loads (non-temporal: X is read once), keeps
+// its Δ in registers and reduces max|Δ| per channel; shuffles within the
+// group give the sub-channel maximum M.  Every lane then picks PoT /
+// precision / tag with exact float32 compares against base*2^j and quantizes
+// its rows.  Each lane writes its 16 of a channel's T codes (codes are
+// channel-major within a tile: a contiguous run per lane), its rows of the
+// aligned codes (one CPT-byte word per row), and the group's first lane
+// writes the tags and counts the bit histogram.  A code in units
 // of the base, a = q·2^e, is the aligned code itself when PoT ≤ 6; otherwise
 // it is split into signed digits a = d0 + 2^7·d1 + 2^15·d2: d0 goes to the
 // aligned codes, d1 (PoT ≥ 7) and d2 (PoT ≥ 14) to the two digit planes, laid
@@ -22,7 +23,7 @@ namespace dstar {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kGroups = kThreads / 2;   // channel groups per workgroup
+constexpr int RT = 16;                  // rows per lane
 
 typedef float fv4 __attribute__((ext_vector_type(4)));
 typedef float fv2 __attribute__((ext_vector_type(2)));
@@ -81,20 +82,21 @@ __device__ __forceinline__ void store_words(int8_t* dst, const uint32_t (&w)[RT 
 }
 
 template <int T, int CPT>
-__global__ __launch_bounds__(kThreads, (T == 64 ? 1 : 3)) void quantize_kernel(QuantizeArgs a, int64_t n_work,
+__global__ __launch_bounds__(kThreads, 3) void quantize_kernel(QuantizeArgs a, int64_t n_work,
                                                             int32_t slabs) {
-  constexpr int RT = T / 2;                  // rows per lane
+  constexpr int G = T / RT;                  // lanes per (tile, channels) group
+  constexpr int kGroups = kThreads / G;      // channel groups per workgroup
   uint32_t hist[4] = {0u, 0u, 0u, 0u};
   const int64_t K = a.K;
   const float inv_base = a.inv_base;
-  const int half = threadIdx.x & 1;
-  const int grp = threadIdx.x >> 1;
+  const int sub = threadIdx.x % G;           // which 16 rows of the tile
+  const int grp = threadIdx.x / G;
   for (int64_t wi = blockIdx.x; wi < n_work; wi += gridDim.x) {
     const int64_t tile = wi / slabs;
     const int64_t slab = wi - tile * slabs;
     const int64_t k = slab * (int64_t)(kGroups * CPT) + (int64_t)grp * CPT;
-    if (k >= K) continue;                    // both lanes of a pair leave together
-    const int64_t r0 = tile * T + half * RT; // first row of this lane
+    if (k >= K) continue;                    // the lanes of a group leave together
+    const int64_t r0 = tile * T + sub * RT;  // first row of this lane
     const int64_t nrows = a.rows - r0;       // real rows from r0 (may be <= 0)
 
     // Δ = X_t − X_{t−1} for RT rows × CPT channels (Eq. 1), kept in registers.
@@ -122,11 +124,12 @@ __global__ __launch_bounds__(kThreads, (T == 64 ? 1 : 3)) void quantize_kernel(Q
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       // M: largest |Δ| of the sub-channel (QPU stage 1): this lane's rows,
-      // then the partner lane's.
+      // then the other lanes' of the group.
       float m = 0.0f;
 #pragma unroll
       for (int t = 0; t < RT; ++t) m = fmaxf(m, fabsf(d[t][c]));
-      m = fmaxf(m, __shfl_xor(m, 1, 64));
+#pragma unroll
+      for (int o = 1; o < G; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
       // PoT = number of bin edges base*2^j (j = 0..20) strictly below M, i.e.
       // the smallest j with M <= base*2^j, capped at 21 (Eq. 3; QPU stage 2).
       int pot = 0;
@@ -144,9 +147,9 @@ __global__ __launch_bounds__(kThreads, (T == 64 ? 1 : 3)) void quantize_kernel(Q
         r = fminf(fmaxf(rintf(r), -pceil), pceil);
         q[t] = (int)r;
       }
-      // This lane's RT codes of channel k+c: bytes half*RT .. half*RT+RT-1 of
+      // This lane's RT codes of channel k+c: bytes sub*RT .. sub*RT+RT-1 of
       // the channel's run at codes[(tile*K + k + c)*T].
-      const int64_t run = (tile * K + k + c) * T + half * RT;
+      const int64_t run = (tile * K + k + c) * T + sub * RT;
       store_codes<RT>(a.codes + run, q);
       if (pot <= 6) {
 #pragma unroll
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(kThreads, (T == 64 ? 1 : 3)) void quantize_kernel(Q
         store_words<RT>(a.hcodes + run, w1);
         if (pot > 13) store_words<RT>(a.hcodes + a.plane + run, w2);
       }
-      if (half == 0) hist[p >> 1] += 1u;
+      if (sub == 0) hist[p >> 1] += 1u;
       const uint32_t tag = (uint32_t)(DSTAR_FMDQ_TAG_OFFSET - e) | ((uint32_t)(p >> 1) << DSTAR_FMDQ_PREC_SHIFT);
       tagword |= tag << (8 * c);
     }
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(kThreads, (T == 64 ? 1 : 3)) void quantize_kernel(Q
         }
       }
     }
-    if (half == 0) {
+    if (sub == 0) {
       uint8_t* tp = a.tags + tile * K + k;
       if constexpr (CPT == 4) {
         *reinterpret_cast<uint32_t*>(tp) = tagword;
@@ -220,6 +223,7 @@ __global__ __launch_bounds__(kThreads, (T == 64 ? 1 : 3)) void quantize_kernel(Q
 
 template <int T, int CPT>
 int launch_t(const QuantizeArgs& a, hipStream_t s) {
+  constexpr int kGroups = kThreads / (T / RT);
   const int64_t nt = n_tiles(a.rows, T);
   const int32_t slabs = (int32_t)((a.K + kGroups * CPT - 1) / (kGroups * CPT));
   const int64_t n_work = nt * slabs;
@@ -233,8 +237,8 @@ int launch_t(const QuantizeArgs& a, hipStream_t s) {
 
 int launch_quantize(const QuantizeArgs& a, hipStream_t s) {
   if (a.rows == 0) return DSTAR_OK;
-  // Channels per lane pair: as many as keep several waves per SIMD resident
-  // (T/2 · CPT floats of Δ live in each lane's registers), limited by K's
+  // Channels per lane group: as many as keep three waves per SIMD resident
+  // (16 · CPT floats of Δ live in each lane's registers), limited by K's
   // divisibility.
   const bool vec4 = (a.K % 4) == 0;
   const bool vec2 = (a.K % 2) == 0;
@@ -244,7 +248,7 @@ int launch_quantize(const QuantizeArgs& a, hipStream_t s) {
     case 32:
       return vec4 ? launch_t<32, 4>(a, s) : vec2 ? launch_t<32, 2>(a, s) : launch_t<32, 1>(a, s);
     case 64:
-      return vec2 ? launch_t<64, 2>(a, s) : launch_t<64, 1>(a, s);
+      return vec4 ? launch_t<64, 4>(a, s) : vec2 ? launch_t<64, 2>(a, s) : launch_t<64, 1>(a, s);
     default:
       return set_error(DSTAR_EUNSUPPORTED, "token_tile %d not supported", a.T);
   }
