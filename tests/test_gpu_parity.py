@@ -151,6 +151,10 @@ SMALL = [
     # more such channels than the MFMA kernel stages: exact per-group fallback
     dict(rows=64, K=8192, N=72, T=32, seed=20, heavy=1.0, c_range=(4.0, 8.0)),
     dict(rows=200, K=1536, N=260, T=32, seed=23, heavy=0.2, c_range=(0.5, 64.0)),
+    # channels with PoT >= 14 (third digits) through the MFMA kernel
+    dict(rows=160, K=1152, N=132, T=32, seed=24, heavy=0.3, c_range=(0.02, 4000.0)),  # N % 16 != 0
+    dict(rows=192, K=640, N=256, T=64, seed=25, heavy=0.3, c_range=(0.02, 4000.0)),
+    dict(rows=128, K=1152, N=144, T=32, seed=26, heavy=0.15, c_range=(0.05, 2000.0)),
 ]
 
 
