@@ -41,16 +41,19 @@
 // columns; wave w owns all 128 rows and columns 64w .. 64w+63 (4 × 2 MFMA
 // 32x32x32 int8 tiles).  Dense part: 64-channel chunks of stage 1's aligned
 // codes ([rows][K]) and of W^T ([N][K]), both channel innermost, flow through
-// a 3-stage LDS ring filled by direct global-to-LDS buffer loads, two chunks
-// ahead of the MFMAs; the four 16-byte columns of every 64-byte row are
-// XOR-swizzled by (row / 4) mod 4 so that one ds_read_b128 per fragment is
-// free of bank conflicts.  The aligned-code rows are shared by the four waves,
-// each wave reads only its own 64 W^T rows.  Gathered part: one "unit" is 32
-// channels of one FPoT group for one 32-row block: their codes (32 bytes per
-// channel from the [tile][K][T] layout) and their W rows (256 bytes per
-// channel) are gathered by direct global-to-LDS loads into an 8-stage ring,
-// seven units ahead; the channel ids of up to 64 units at a time are staged in
-// LDS.  Both tiles have the channel outermost, so each lane assembles its
+// a 3-stage LDS ring filled by direct global-to-LDS buffer loads; a chunk's
+// stage is refilled as soon as every wave holds the fragments of its second
+// k-step, so three chunks are in flight, and each k-step's six fragment reads
+// are interleaved with the previous k-step's MFMAs.  The four 16-byte columns
+// of every 64-byte row are XOR-swizzled by (row / 4) mod 4 so that one
+// ds_read_b128 per fragment is free of bank conflicts.  The aligned-code rows
+// are shared by the four waves, each wave reads only its own 64 W^T rows.
+// Gathered part (digits of the channels with PoT ≥ 7): one "unit" is 64
+// channels of one 32-row block's digit list; their digit codes (32 bytes per
+// channel from the [tile][K][T] digit planes) and W rows (256 bytes per
+// channel) are gathered by direct global-to-LDS loads into a 4-stage ring,
+// three units ahead; the channel ids of up to 32 units at a time are staged
+// in LDS.  Both tiles have the channel outermost, so each lane assembles its
 // fragment with two ds_read_b64_tr_b8 transpose reads (W rows XOR-swizzled in
 // 16-byte pieces by channel mod 8).  The bin offsets and the unit schedule
 // are read while the first dense chunks are in flight.
@@ -128,6 +131,7 @@ constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00
 constexpr int kWaitVm0 = wait_vm(0);
 constexpr int kWaitVmChunk = wait_vm(6);   // one dense chunk's six loads
 constexpr int kWaitVmChunkIds = wait_vm(14);  // ... and eight id loads
+constexpr int kWaitVmFirst = wait_vm(20);  // two chunks and the eight id loads
 constexpr int kWaitLgkm0 = 0xC07F;         // lgkmcnt(0)
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
@@ -291,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   }
   __asm__ __volatile__("" ::: "memory");   // keep these loads ahead of the dense ones
 #pragma unroll
-  for (int c = 0; c < kStages - 1; ++c) issue(c, c);   // a chunk past K loads zeros
+  for (int c = 0; c < kStages; ++c) issue(c, c);   // a chunk past K loads zeros
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const int idx = tid + kThreads * m;
@@ -423,41 +427,59 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     auto frag = [&](const uint8_t* tile, int row, int c) {
       return *reinterpret_cast<const v4i*>(tile + row * BK + 16 * (c ^ ((row >> 2) & 3)));
     };
-    auto compute = [&](int st) {
+    // One k-step's fragments: 4 row blocks of codes, 2 column blocks of W^T.
+    struct Frags { v4i a[RB], b[CB]; };
+    auto read = [&](Frags& f, int st, int ks) __attribute__((always_inline)) {
 #pragma unroll
-      for (int ks = 0; ks < BK / KS; ++ks) {
-        v4i af[RB], bf[CB];
+      for (int cb = 0; cb < CB; ++cb) f.b[cb] = frag(stageB(st, wave), 32 * cb + li, 2 * ks + h);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) af[rb] = frag(stageA(st), 32 * rb + li, 2 * ks + h);
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) bf[cb] = frag(stageB(st, wave), 32 * cb + li, 2 * ks + h);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb)
-            acc[rb][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[rb], bf[cb], acc[rb][cb], 0, 0, 0);
-      }
+      for (int rb = 0; rb < RB; ++rb) f.a[rb] = frag(stageA(st), 32 * rb + li, 2 * ks + h);
     };
+    // The MFMAs of one k-step with the six fragment reads of the next one
+    // interleaved (one read after each of the first six MFMAs), so the reads
+    // are in flight while the matrix core works.
+    auto mma = [&](const Frags& f) __attribute__((always_inline)) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[rb], f.b[cb], acc[rb][cb], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < RB + CB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, RB * CB - RB - CB, 0);
+    };
+    // Chunk c's stage is free once every wave holds its second k-step's
+    // fragments, so the wait for chunk c + 1 and the barrier sit between the
+    // two k-steps of chunk c, and chunk c + 3 is issued into that stage right
+    // after: three chunks are in flight.  Chunks past K load zeros (their
+    // fragments are read but never used), so every wait has the same count;
+    // in the first two waits the eight id loads (issued after chunk 2) may
+    // also be in flight.
+    Frags f0, f1;
+    __builtin_amdgcn_s_waitcnt(kWaitVmFirst);
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+    read(f0, 0, 0);
     for (int64_t c = 0; c < nchunks; ++c) {
-      // Chunk c's loads are done once at most one later chunk is in flight.
-      // The barrier then makes every wave's part of chunk c visible and
-      // guarantees every wave is done with chunk c - 1 (whose stage the next
-      // loads overwrite).
-      // (In the first two iterations the eight id loads issued after chunk 1
-      // may also be in flight.)
-      if (c + 1 >= nchunks) {
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      } else if (c < 2) {
+      const int st = (int)(c % kStages);
+      const int st1 = (int)((c + 1) % kStages);
+      read(f1, st, 1);
+      mma(f0);
+      if (c < 2) {
         __builtin_amdgcn_s_waitcnt(kWaitVmChunkIds);
       } else {
         __builtin_amdgcn_s_waitcnt(kWaitVmChunk);
       }
-      __asm__ __volatile__("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      __asm__ __volatile__("" ::: "memory");
-      if (c + kStages - 1 < nchunks) issue(c + kStages - 1, (int)((c + kStages - 1) % kStages));
-      compute((int)(c % kStages));
+      bar_lds();
+      issue(c + kStages, st);
+      read(f0, st1, 0);
+      mma(f1);
     }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the chunks issued past K
   }
 
   // ---- Epilogue set-up.  Y is streamed once: its loads and stores are
