@@ -424,6 +424,40 @@ def linear(codes: np.ndarray, tags: np.ndarray, perm: np.ndarray,
     return y
 
 
+#: The range a layer's base is held to: the library rejects a static base
+#: outside it, and a dynamic base is clamped into it.
+BASE_MIN = 2.0 ** -100
+BASE_MAX = 2.0 ** 100
+
+
+def dynamic_base(x_t: np.ndarray, x_prev: np.ndarray, token_tile: int, fallback: float) -> np.float32:
+    """The base as DSTAR §3.1 ❶ defines it before the static-base shortcut:
+    the smallest sub-channel maximum M_{τk} of the layer input, found in a
+    first pass over X (the "DS-FMDQ-DYN" variant of DSTAR §5.2, Table 2).
+
+    Readings of what the page leaves open: sub-channels whose Δ is zero in
+    every row are left out (their codes are 0 whatever the base, and a zero
+    base has no Eq. 2 scale); if every sub-channel is zero the static base
+    ``fallback`` is kept; the minimum is clamped to [BASE_MIN, BASE_MAX].  The
+    minimum of float32 values is exact, so both implementations agree bit for
+    bit.
+    """
+    m = subchannel_max(differential(x_t, x_prev), token_tile)
+    pos = m[m > 0]
+    if pos.size == 0:
+        return F32(fallback)
+    return F32(min(max(F64(pos.min()), BASE_MIN), BASE_MAX))
+
+
+def layer_dynamic(x_t, x_prev, w, w_scale, y_prev, fallback_base, token_tile, k0):
+    """The layer with the dynamic base: pass 1 finds the base (dynamic_base),
+    pass 2 is the static pipeline run with it.  The result carries "base"."""
+    base = dynamic_base(x_t, x_prev, token_tile, fallback_base)
+    out = layer(x_t, x_prev, w, w_scale, y_prev, base, token_tile, k0)
+    out["base"] = base
+    return out
+
+
 def layer(x_t, x_prev, w, w_scale, y_prev, base, token_tile, k0):
     """The whole FMDQ differential linear: quantize, bucket, grouped GEMM."""
     codes, tags, hist = quantize(x_t, x_prev, token_tile, base, k0)
