@@ -20,10 +20,11 @@ TAG_OFFSET = 15
 POT_MAX = 21
 PREC_SHIFT = 4
 MAX_K = 65535
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 SYMBOLS = ("dstar_fmdq_quantize", "dstar_fmdq_bucket", "dstar_fmdq_pack_weights",
-           "dstar_fmdq_linear", "dstar_fmdq_last_error", "dstar_fmdq_abi_version")
+           "dstar_fmdq_linear", "dstar_fmdq_dynamic_base", "dstar_fmdq_quantize_dyn",
+           "dstar_fmdq_linear_dyn", "dstar_fmdq_last_error", "dstar_fmdq_abi_version")
 
 
 class FmdqError(RuntimeError):
@@ -63,6 +64,13 @@ def load() -> ctypes.CDLL:
     lib.dstar_fmdq_pack_weights.restype = ctypes.c_int
     lib.dstar_fmdq_linear.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
     lib.dstar_fmdq_linear.restype = ctypes.c_int
+    lib.dstar_fmdq_dynamic_base.argtypes = [P, vp, vp, vp, vp]
+    lib.dstar_fmdq_dynamic_base.restype = ctypes.c_int
+    lib.dstar_fmdq_quantize_dyn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.dstar_fmdq_quantize_dyn.restype = ctypes.c_int
+    lib.dstar_fmdq_linear_dyn.argtypes = [P, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                          i32, vp]
+    lib.dstar_fmdq_linear_dyn.restype = ctypes.c_int
     lib.dstar_fmdq_last_error.argtypes = []
     lib.dstar_fmdq_last_error.restype = ctypes.c_char_p
     lib.dstar_fmdq_abi_version.argtypes = []
@@ -127,3 +135,29 @@ def linear(p: Params, N: int, codes, perm, group_off, acodes, hcodes, w, w_t, w_
                                     _ptr(group_off), _ptr(acodes), _ptr(hcodes), _ptr(w), _ptr(w_t),
                                     _ptr(w_scale), _ptr(y_prev), _ptr(y_out), _ptr(acc_dbg),
                                     int(dbg_tile_lo), int(dbg_tile_hi), _stream(stream)))
+
+
+def dynamic_base(p: Params, x_t, x_prev, base, stream=None) -> None:
+    """dstar_fmdq_dynamic_base: base (a 1-element float32 device tensor) = the
+    smallest positive sub-channel maximum of |x_t - x_prev|."""
+    _check(load().dstar_fmdq_dynamic_base(ctypes.byref(p), _ptr(x_t), _ptr(x_prev), _ptr(base),
+                                          _stream(stream)))
+
+
+def quantize_dyn(p: Params, base, x_t, x_prev, codes, tags, acodes=None, hcodes=None, bit_hist=None,
+                 stream=None) -> None:
+    """dstar_fmdq_quantize_dyn: stage 1 with the base read from the device tensor `base`."""
+    _check(load().dstar_fmdq_quantize_dyn(ctypes.byref(p), _ptr(base), _ptr(x_t), _ptr(x_prev),
+                                          _ptr(codes), _ptr(tags), _ptr(acodes), _ptr(hcodes),
+                                          _ptr(bit_hist), _stream(stream)))
+
+
+def linear_dyn(p: Params, base, N: int, codes, perm, group_off, acodes, hcodes, w, w_t, w_scale,
+               y_prev, y_out, acc_dbg=None, dbg_tile_lo: int = 0, dbg_tile_hi: int = 0,
+               stream=None) -> None:
+    """dstar_fmdq_linear_dyn: stage 3 with the base read from the device tensor `base`."""
+    _check(load().dstar_fmdq_linear_dyn(ctypes.byref(p), _ptr(base), int(N), _ptr(codes), _ptr(perm),
+                                        _ptr(group_off), _ptr(acodes), _ptr(hcodes), _ptr(w),
+                                        _ptr(w_t), _ptr(w_scale), _ptr(y_prev), _ptr(y_out),
+                                        _ptr(acc_dbg), int(dbg_tile_lo), int(dbg_tile_hi),
+                                        _stream(stream)))

@@ -67,9 +67,13 @@ int dstar_fmdq_abi_version(void) { return DSTAR_FMDQ_ABI_VERSION; }
 
 const char* dstar_fmdq_last_error(void) { return g_error.c_str(); }
 
-int dstar_fmdq_quantize(const dstar_fmdq_params* p, const float* x_t, const float* x_prev,
-                        int8_t* codes, uint8_t* tags, int8_t* acodes, int8_t* hcodes,
-                        uint32_t* bit_hist, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int quantize_impl(const dstar_fmdq_params* p, const float* base_dev, const float* x_t,
+                  const float* x_prev, int8_t* codes, uint8_t* tags, int8_t* acodes,
+                  int8_t* hcodes, uint32_t* bit_hist, void* stream) {
   clear_error();
   int64_t nt = 0;
   if (int rc = check_params(p, &nt)) return rc;
@@ -99,8 +103,61 @@ int dstar_fmdq_quantize(const dstar_fmdq_params* p, const float* x_t, const floa
   a.T = p->token_tile;
   a.base = p->base;
   a.inv_base = (float)(1.0 / (double)p->base);
+  a.base_dev = base_dev;
   a.k0 = p->thr0_log2;
   return launch_quantize(a, (hipStream_t)stream);
+}
+
+int linear_impl(const dstar_fmdq_params* p, const float* base_dev, int32_t N, const int8_t* codes,
+                const uint16_t* perm, const int32_t* group_off, const int8_t* acodes,
+                const int8_t* hcodes, const int8_t* w, const int8_t* w_t, const float* w_scale,
+                const float* y_prev, float* y_out, int32_t* acc_dbg, int32_t dbg_tile_lo,
+                int32_t dbg_tile_hi, void* stream);
+
+// Checks the device base pointer of the _dyn entry points.
+int check_base_dev(const float* base_dev, const char* what) {
+  if (base_dev == nullptr) return set_error(DSTAR_ENULL, "%s: base must not be NULL", what);
+  if (!aligned(base_dev, 4)) return set_error(DSTAR_EALIGN, "%s: base must be 4-byte aligned", what);
+  return DSTAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dstar_fmdq_quantize(const dstar_fmdq_params* p, const float* x_t, const float* x_prev,
+                        int8_t* codes, uint8_t* tags, int8_t* acodes, int8_t* hcodes,
+                        uint32_t* bit_hist, void* stream) {
+  return quantize_impl(p, nullptr, x_t, x_prev, codes, tags, acodes, hcodes, bit_hist, stream);
+}
+
+int dstar_fmdq_quantize_dyn(const dstar_fmdq_params* p, const float* base, const float* x_t,
+                            const float* x_prev, int8_t* codes, uint8_t* tags, int8_t* acodes,
+                            int8_t* hcodes, uint32_t* bit_hist, void* stream) {
+  clear_error();
+  if (int rc = check_base_dev(base, "quantize_dyn")) return rc;
+  return quantize_impl(p, base, x_t, x_prev, codes, tags, acodes, hcodes, bit_hist, stream);
+}
+
+int dstar_fmdq_dynamic_base(const dstar_fmdq_params* p, const float* x_t, const float* x_prev,
+                            float* base, void* stream) {
+  clear_error();
+  int64_t nt = 0;
+  if (int rc = check_params(p, &nt)) return rc;
+  if (!base || (p->rows > 0 && (!x_t || !x_prev)))
+    return set_error(DSTAR_ENULL, "dynamic_base: x_t, x_prev and base must not be NULL");
+  if (!aligned(base, 4) || (p->rows > 0 && (!aligned(x_t, 16) || !aligned(x_prev, 16))))
+    return set_error(DSTAR_EALIGN,
+                     "dynamic_base: x_t and x_prev must be 16-byte aligned, base 4-byte aligned");
+  BaseArgs a;
+  a.x_t = x_t;
+  a.x_prev = x_prev;
+  a.base_bits = reinterpret_cast<uint32_t*>(base);
+  a.rows = p->rows;
+  a.K = p->K;
+  a.T = p->token_tile;
+  a.fallback = p->base;
+  return launch_dynamic_base(a, (hipStream_t)stream);
 }
 
 int dstar_fmdq_bucket(const dstar_fmdq_params* p, const uint8_t* tags, uint16_t* perm,
@@ -141,6 +198,31 @@ int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N, const int8_t* codes
                       const float* w_scale, const float* y_prev, float* y_out, int32_t* acc_dbg,
                       int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream) {
   clear_error();
+  return linear_impl(p, nullptr, N, codes, perm, group_off, acodes, hcodes, w, w_t, w_scale, y_prev,
+                     y_out, acc_dbg, dbg_tile_lo, dbg_tile_hi, stream);
+}
+
+int dstar_fmdq_linear_dyn(const dstar_fmdq_params* p, const float* base, int32_t N,
+                          const int8_t* codes, const uint16_t* perm, const int32_t* group_off,
+                          const int8_t* acodes, const int8_t* hcodes, const int8_t* w,
+                          const int8_t* w_t, const float* w_scale, const float* y_prev,
+                          float* y_out, int32_t* acc_dbg, int32_t dbg_tile_lo,
+                          int32_t dbg_tile_hi, void* stream) {
+  clear_error();
+  if (int rc = check_base_dev(base, "linear_dyn")) return rc;
+  return linear_impl(p, base, N, codes, perm, group_off, acodes, hcodes, w, w_t, w_scale, y_prev,
+                     y_out, acc_dbg, dbg_tile_lo, dbg_tile_hi, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int linear_impl(const dstar_fmdq_params* p, const float* base_dev, int32_t N, const int8_t* codes,
+                const uint16_t* perm, const int32_t* group_off, const int8_t* acodes,
+                const int8_t* hcodes, const int8_t* w, const int8_t* w_t, const float* w_scale,
+                const float* y_prev, float* y_out, int32_t* acc_dbg, int32_t dbg_tile_lo,
+                int32_t dbg_tile_hi, void* stream) {
   int64_t nt = 0;
   if (int rc = check_params(p, &nt)) return rc;
   if (N < 1 || N > (1 << 20) || N % 4 != 0)
@@ -178,7 +260,8 @@ int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N, const int8_t* codes
   a.N = N;
   a.T = p->token_tile;
   a.base = (double)p->base;
+  a.base_dev = base_dev;
   return launch_linear(a, (hipStream_t)stream);
 }
 
-}  // extern "C"
+}  // namespace

@@ -1,0 +1,98 @@
+// Dynamic base of the FMDQ differential linear: the first of the two passes
+// over X that a base taken from the data needs (DSTAR, arXiv 2607.15846: §3.1
+// step 1 defines the base of Eq. 2-3 as the smallest sub-channel maximum M_i;
+// the static base of the method removes this pass, and §5.2 Table 2 evaluates
+// the dynamic variant as DS-FMDQ-DYN).
+//
+// base = min over sub-channels (token tile × channel) with M > 0 of
+// M = max |X_t − X_{t−1}| over the tile's rows, clamped to [2^-100, 2^100];
+// the static base when every M is 0.  M and its minimum are exact in float32,
+// and a positive float32 orders like its bit pattern, so the minimum is an
+// atomicMin over 32-bit patterns: one kernel writes +inf, the reduction
+// lowers it (one atomic per wave), a last one-thread kernel applies the
+// fallback and the clamp.  No memset, so the sequence can be captured in a
+// HIP graph.
+#include "fmdq_internal.h"
+
+namespace dstar {
+namespace {
+
+constexpr int kThreads = 256;
+typedef float f4 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kInfBits = 0x7F800000u;
+
+__global__ void base_init_kernel(uint32_t* bits) {
+  if (threadIdx.x == 0) *bits = kInfBits;
+}
+
+// Workgroup = one token tile × kThreads·V channels; thread j owns channels
+// [V·(slab·kThreads + j), +V) and walks the tile's rows (float4 loads when
+// V = 4: K % 4 == 0 and 16-byte aligned rows).
+template <int V>
+__global__ __launch_bounds__(kThreads) void base_min_kernel(BaseArgs a, int32_t slabs) {
+  const int64_t tile = blockIdx.x / slabs;
+  const int64_t slab = blockIdx.x - tile * slabs;
+  const int64_t k = (slab * kThreads + threadIdx.x) * V;
+  const int64_t r0 = tile * a.T;
+  const int64_t r1 = min(r0 + (int64_t)a.T, a.rows);
+  const int64_t K = a.K;
+  uint32_t best = kInfBits;
+  if (k < K) {
+    float m[V];
+#pragma unroll
+    for (int c = 0; c < V; ++c) m[c] = 0.0f;
+    for (int64_t r = r0; r < r1; ++r) {
+      float xt[V], xp[V];
+      if constexpr (V == 4) {
+        const f4 u = __builtin_nontemporal_load(reinterpret_cast<const f4*>(a.x_t + r * K + k));
+        const f4 v = __builtin_nontemporal_load(reinterpret_cast<const f4*>(a.x_prev + r * K + k));
+        xt[0] = u.x; xt[1] = u.y; xt[2] = u.z; xt[3] = u.w;
+        xp[0] = v.x; xp[1] = v.y; xp[2] = v.z; xp[3] = v.w;
+      } else {
+        xt[0] = __builtin_nontemporal_load(a.x_t + r * K + k);
+        xp[0] = __builtin_nontemporal_load(a.x_prev + r * K + k);
+      }
+#pragma unroll
+      for (int c = 0; c < V; ++c) m[c] = fmaxf(m[c], fabsf(__fsub_rn(xt[c], xp[c])));
+    }
+#pragma unroll
+    for (int c = 0; c < V; ++c)
+      if (m[c] > 0.0f) best = min(best, __float_as_uint(m[c]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) best = min(best, (uint32_t)__shfl_xor((int)best, o, 64));
+  if ((threadIdx.x & 63) == 0 && best != kInfBits) atomicMin(a.base_bits, best);
+}
+
+__global__ void base_final_kernel(uint32_t* bits, float fallback) {
+  if (threadIdx.x != 0) return;
+  const uint32_t b = *bits;
+  const float v = b == kInfBits ? fallback : fminf(fmaxf(__uint_as_float(b), 0x1p-100f), 0x1p100f);
+  *reinterpret_cast<float*>(bits) = v;
+}
+
+template <int V>
+int launch_v(const BaseArgs& a, hipStream_t s) {
+  const int64_t nt = n_tiles(a.rows, a.T);
+  const int64_t per = (int64_t)kThreads * V;
+  const int32_t slabs = (int32_t)((a.K + per - 1) / per);
+  const int64_t grid = nt * slabs;
+  if (grid > 0x7FFFFFFF) return set_error(DSTAR_EUNSUPPORTED, "dynamic_base: grid too large");
+  hipLaunchKernelGGL(base_min_kernel<V>, dim3((unsigned)grid), dim3(kThreads), 0, s, a, slabs);
+  return check_launch("fmdq_dynamic_base (min)");
+}
+
+}  // namespace
+
+int launch_dynamic_base(const BaseArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(base_init_kernel, dim3(1), dim3(64), 0, s, a.base_bits);
+  if (int rc = check_launch("fmdq_dynamic_base (init)")) return rc;
+  if (a.rows > 0) {
+    const int rc = (a.K % 4) == 0 ? launch_v<4>(a, s) : launch_v<1>(a, s);
+    if (rc) return rc;
+  }
+  hipLaunchKernelGGL(base_final_kernel, dim3(1), dim3(64), 0, s, a.base_bits, a.fallback);
+  return check_launch("fmdq_dynamic_base (final)");
+}
+
+}  // namespace dstar

@@ -32,6 +32,7 @@ struct QuantizeArgs {
   int32_t T;
   float base;
   float inv_base;
+  const float* base_dev;   // non-NULL: base read from device memory (dynamic base)
   int32_t k0;
 };
 int launch_quantize(const QuantizeArgs& a, hipStream_t s);
@@ -64,8 +65,19 @@ struct LinearArgs {
   int32_t N;
   int32_t T;
   double base;
+  const float* base_dev;   // non-NULL: base read from device memory (dynamic base)
 };
 int launch_linear(const LinearArgs& a, hipStream_t s);
+struct BaseArgs {
+  const float* x_t;
+  const float* x_prev;
+  uint32_t* base_bits;     // the float32 result, handled as its bit pattern
+  int64_t rows;
+  int32_t K;
+  int32_t T;
+  float fallback;
+};
+int launch_dynamic_base(const BaseArgs& a, hipStream_t s);
 int launch_pack_weights(int32_t K, int32_t N, const int8_t* w, int8_t* w_t, hipStream_t s);
 int launch_linear_general(const LinearArgs& a, hipStream_t s);
 bool linear_mfma_supported(const LinearArgs& a);

@@ -487,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   // interior blocks the epilogue runs over (32-row block, 32-column block)
   // units, loading the next unit's Y_{t−1} before storing the current one.
   // Offsets are 32-bit, relative to this workgroup's first row.
-  const double base = a.base;
+  const double base = a.base_dev != nullptr ? (double)*a.base_dev : a.base;
   bool all_eligible = true;
 #pragma unroll
   for (int i = 0; i < kTiles; ++i) all_eligible = all_eligible && eligible[i];

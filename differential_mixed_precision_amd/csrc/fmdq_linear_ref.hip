@@ -64,12 +64,13 @@ __global__ __launch_bounds__(kThreads) void linear_general_kernel(LinearArgs a, 
       }
     }
     if (!valid) continue;
+    const double base = a.base_dev != nullptr ? (double)*a.base_dev : a.base;
     const double ws = (double)a.w_scale[n];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       if (t < nrows) {
         const int64_t idx = (r0 + t) * N + n;
-        const double d = __dmul_rn(__dmul_rn((double)s[t], a.base), ws);
+        const double d = __dmul_rn(__dmul_rn((double)s[t], base), ws);
         a.y_out[idx] = (float)__dadd_rn((double)a.y_prev[idx], d);
       }
     }

@@ -88,7 +88,13 @@ __global__ __launch_bounds__(kThreads, 3) void quantize_kernel(QuantizeArgs a, i
   constexpr int kGroups = kThreads / G;      // channel groups per workgroup
   uint32_t hist[4] = {0u, 0u, 0u, 0u};
   const int64_t K = a.K;
-  const float inv_base = a.inv_base;
+  // The base: static (from the host), or the dynamic one in device memory,
+  // whose reciprocal is formed here exactly as the host forms it.
+  float base = a.base, inv_base = a.inv_base;
+  if (a.base_dev != nullptr) {
+    base = *a.base_dev;
+    inv_base = (float)(1.0 / (double)base);
+  }
   const int sub = threadIdx.x % G;           // which 16 rows of the tile
   const int grp = threadIdx.x / G;
   for (int64_t wi = blockIdx.x; wi < n_work; wi += gridDim.x) {
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(kThreads, 3) void quantize_kernel(QuantizeArgs a, i
       // the smallest j with M <= base*2^j, capped at 21 (Eq. 3; QPU stage 2).
       int pot = 0;
 #pragma unroll
-      for (int j = 0; j < DSTAR_FMDQ_POT_MAX; ++j) pot += (m > ldexpf(a.base, j)) ? 1 : 0;
+      for (int j = 0; j < DSTAR_FMDQ_POT_MAX; ++j) pot += (m > ldexpf(base, j)) ? 1 : 0;
       // Precision from the thresholds base*2^(k0+2N): p = b - 2 = log2(PCeil).
       const int p = pot <= a.k0 ? 0 : pot <= a.k0 + 2 ? 2 : pot <= a.k0 + 4 ? 4 : 6;
       const int e = pot - p;                               // step = base * 2^e

@@ -14,8 +14,9 @@
  * steps 2 and 5, Fig. 6), dequantized and added to the cached Y_{t-1} (DSTAR
  * §4.2 "Design of MPU", §4.3 "Linear Operation").
  *
- * The three entry points are the three stages; each launches HIP kernels on
- * the caller's stream and returns without synchronizing.
+ * The entry points are the three stages, the weight preparation and the
+ * dynamic-base variant; each launches HIP kernels on the caller's stream and
+ * returns without synchronizing.
  *
  * Conventions for every entry point
  *   - All array arguments are DEVICE pointers (memory from hipMalloc, or
@@ -39,7 +40,7 @@
 extern "C" {
 #endif
 
-#define DSTAR_FMDQ_ABI_VERSION 5
+#define DSTAR_FMDQ_ABI_VERSION 6
 
 /* Rule constants (DSTAR §3.1 step 1; readings in the design notes):
  * PCeil of a b-bit sub-channel is 2^(b-2); PoT is capped at POT_MAX so that
@@ -176,6 +177,40 @@ int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N,
                       const float* w_scale,
                       const float* y_prev, float* y_out, int32_t* acc_dbg,
                       int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream);
+
+/* Dynamic base, pass 1 of the variant that takes the base from the data
+ * (DSTAR §3.1 step 1 defines the base of Eq. 2-3 as the smallest sub-channel
+ * maximum M_i over the whole tensor, which costs a second pass over X; the
+ * method's static base removes it, and DSTAR §5.2, Table 2 evaluates the
+ * dynamic variant as DS-FMDQ-DYN).
+ *   x_t, x_prev  as for stage 1 (may be NULL when rows == 0).
+ *   base         float32[1], DEVICE memory, 4-byte aligned (out): the smallest
+ *                M = max |Δ| over the rows of a token tile, over every
+ *                sub-channel with M > 0, clamped to [2^-100, 2^100]; p->base
+ *                when no sub-channel has M > 0.
+ * The result stays on the device for the _dyn entry points below (three
+ * kernels; no memset, so the sequence can be captured in a HIP graph). */
+int dstar_fmdq_dynamic_base(const dstar_fmdq_params* p, const float* x_t,
+                            const float* x_prev, float* base, void* stream);
+
+/* Stage 1 and stage 3 with the base read from device memory: `base` is a
+ * float32[1] written by dstar_fmdq_dynamic_base (or any float in
+ * [2^-100, 2^100]), 4-byte aligned, not NULL.  Every other argument, check
+ * and result is that of dstar_fmdq_quantize, resp. dstar_fmdq_linear, with
+ * p->base replaced by *base (p->base must still be valid).  Stage 2 does not
+ * depend on the base. */
+int dstar_fmdq_quantize_dyn(const dstar_fmdq_params* p, const float* base,
+                            const float* x_t, const float* x_prev,
+                            int8_t* codes, uint8_t* tags, int8_t* acodes,
+                            int8_t* hcodes, uint32_t* bit_hist, void* stream);
+int dstar_fmdq_linear_dyn(const dstar_fmdq_params* p, const float* base,
+                          int32_t N, const int8_t* codes, const uint16_t* perm,
+                          const int32_t* group_off, const int8_t* acodes,
+                          const int8_t* hcodes, const int8_t* w,
+                          const int8_t* w_t, const float* w_scale,
+                          const float* y_prev, float* y_out, int32_t* acc_dbg,
+                          int32_t dbg_tile_lo, int32_t dbg_tile_hi,
+                          void* stream);
 
 /* Message describing the last error of the calling thread ("" if none). */
 const char* dstar_fmdq_last_error(void);

@@ -86,6 +86,9 @@ def test_invalid_params_rejected(lib, field, value):
     L = lib.load()
     assert L.dstar_fmdq_bucket(ctypes.byref(p), FAKE, FAKE, FAKE, 0) == lib.EINVAL
     assert _l(lib, p) == lib.EINVAL
+    assert L.dstar_fmdq_dynamic_base(ctypes.byref(p), FAKE, FAKE, FAKE, 0) == lib.EINVAL
+    assert L.dstar_fmdq_quantize_dyn(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None,
+                                     0) == lib.EINVAL
 
 
 def test_sequences_must_tile_evenly(lib):
@@ -126,6 +129,21 @@ def test_null_and_alignment_errors(lib):
     assert _l(lib, p, dbg=FAKE, lo=1, hi=1) == lib.EINVAL
     assert _l(lib, p, dbg=FAKE, lo=0, hi=3) == lib.EINVAL    # 64 rows / 32 = 2 tiles
     assert "debug tile range" in L.dstar_fmdq_last_error().decode()
+    # dynamic base and the _dyn stages
+    assert L.dstar_fmdq_dynamic_base(ctypes.byref(p), FAKE, FAKE, None, 0) == lib.ENULL
+    assert L.dstar_fmdq_dynamic_base(ctypes.byref(p), None, FAKE, FAKE, 0) == lib.ENULL
+    assert L.dstar_fmdq_dynamic_base(ctypes.byref(p), FAKE, FAKE, FAKE + 2, 0) == lib.EALIGN
+    assert L.dstar_fmdq_dynamic_base(ctypes.byref(p), FAKE + 4, FAKE, FAKE, 0) == lib.EALIGN
+    assert L.dstar_fmdq_quantize_dyn(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, None, None, None,
+                                     0) == lib.ENULL
+    assert L.dstar_fmdq_quantize_dyn(ctypes.byref(p), FAKE + 1, FAKE, FAKE, FAKE, FAKE, None, None,
+                                     None, 0) == lib.EALIGN
+    assert L.dstar_fmdq_quantize_dyn(ctypes.byref(p), FAKE, None, FAKE, FAKE, FAKE, None, None, None,
+                                     0) == lib.ENULL
+    assert L.dstar_fmdq_linear_dyn(ctypes.byref(p), None, 64, FAKE, FAKE, FAKE, None, None, FAKE, None,
+                                   FAKE, FAKE, FAKE, None, 0, 0, 0) == lib.ENULL
+    assert L.dstar_fmdq_linear_dyn(ctypes.byref(p), FAKE, 66, FAKE, FAKE, FAKE, None, None, FAKE, None,
+                                   FAKE, FAKE, FAKE, None, 0, 0, 0) == lib.EINVAL
 
 
 def test_empty_input_is_a_no_op(lib):

@@ -35,13 +35,15 @@ def dm():
     return dm
 
 
-def gpu_layer(dm, d, dbg=None, inplace=False, y_prev_np=None):
+def gpu_layer(dm, d, dbg=None, inplace=False, y_prev_np=None, dynamic=False):
     """Runs the three stages on cuda:0; every output buffer starts as garbage.
 
     Stage 3 runs twice from the same codes: once as the product path (no
     accumulator dump: the MFMA kernel where the shape allows it) -> "y", and,
     when ``dbg`` names a tile range, once more with the group accumulators
-    dumped (the per-group kernel) -> "y_dbg" and "acc"."""
+    dumped (the per-group kernel) -> "y_dbg" and "acc".  With ``dynamic`` the
+    base is found on the device first (dynamic_base -> "base") and stages 1
+    and 3 read it from there (quantize_dyn, linear_dyn)."""
     import torch
     dev = torch.device("cuda:0")
     rows, K, N, T = d["rows"], d["K"], d["N"], d["token_tile"]
@@ -63,17 +65,28 @@ def gpu_layer(dm, d, dbg=None, inplace=False, y_prev_np=None):
     off = torch.full((nt, 65), -7, dtype=torch.int32, device=dev)
     y1 = y0 if inplace else torch.full((rows, N), float("nan"), dtype=torch.float32, device=dev)
     dm.pack_weights(K, N, w, w_t)
-    dm.quantize(p, x_t, x_p, codes, tags, acodes, hcodes, hist)
+    base = torch.full((1,), float("nan"), dtype=torch.float32, device=dev)
+    if dynamic:
+        dm.dynamic_base(p, x_t, x_p, base)
+        dm.quantize_dyn(p, base, x_t, x_p, codes, tags, acodes, hcodes, hist)
+    else:
+        dm.quantize(p, x_t, x_p, codes, tags, acodes, hcodes, hist)
     dm.bucket(p, tags, perm, off)
-    dm.linear(p, N, codes, perm, off, acodes, hcodes, w, w_t, ws, y0, y1)
+    if dynamic:
+        dm.linear_dyn(p, base, N, codes, perm, off, acodes, hcodes, w, w_t, ws, y0, y1)
+    else:
+        dm.linear(p, N, codes, perm, off, acodes, hcodes, w, w_t, ws, y0, y1)
     out = dict(codes=codes, tags=tags, acodes=acodes, hcodes=hcodes, w_t=w_t, hist=hist, perm=perm,
-               group_off=off, y=y1)
+               group_off=off, y=y1, base=base)
     if dbg is not None:
         lo, hi = dbg
         acc = torch.full((hi - lo, 16, T, N), 0x7777, dtype=torch.int32, device=dev)
         y0b = torch.from_numpy(y_np).to(dev)
         y2 = torch.full((rows, N), float("nan"), dtype=torch.float32, device=dev)
-        dm.linear(p, N, codes, perm, off, acodes, hcodes, w, w_t, ws, y0b, y2, acc, lo, hi)
+        if dynamic:
+            dm.linear_dyn(p, base, N, codes, perm, off, acodes, hcodes, w, w_t, ws, y0b, y2, acc, lo, hi)
+        else:
+            dm.linear(p, N, codes, perm, off, acodes, hcodes, w, w_t, ws, y0b, y2, acc, lo, hi)
         out.update(acc=acc, y_dbg=y2)
     torch.cuda.synchronize()
     out = {k: v.cpu().numpy() for k, v in out.items()}
@@ -310,4 +323,91 @@ def test_full_size_workloads(dm, cfg, layer):
                                       err_msg=f"group accumulators of tile {tau}")
     rows_s = np.concatenate([np.arange(tau * T, min(rows, tau * T + T)) for tau in sample])
     check_y(g["y"][rows_s], y[rows_s], d["y_prev"][rows_s], d["name"])
+    log(f"  done {time.time() - t0:.1f}s")
+
+
+# ---------------------------------------------------------------- dynamic base
+DYN = [
+    dict(rows=96, K=64, N=64, T=32, seed=41),
+    dict(rows=70, K=44, N=40, T=32, seed=42),                      # ragged last tile
+    dict(rows=128, K=37, N=36, T=64, seed=43),                     # K % 4 != 0: scalar loads
+    dict(rows=64, K=128, N=96, T=16, seed=44),
+    dict(rows=320, K=256, N=264, T=32, seed=45, heavy=0.2),        # MFMA kernel, digit planes
+    dict(rows=192, K=192, N=128, T=64, seed=46, c_range=(0.02, 4000.0)),
+]
+
+
+def dyn_compare(dm, d, what):
+    rows, T = d["rows"], d["token_tile"]
+    nt = (rows + T - 1) // T
+    b = fmdq.dynamic_base(d["x_t"], d["x_prev"], T, d["base"])
+    log(f"case {what} rows={rows} K={d['K']} N={d['N']} T={T}: oracle base {float(b)!r}")
+    g = gpu_layer(dm, d, dbg=(0, nt), dynamic=True)
+    assert g["base"].view(np.uint32)[0] == np.asarray(b, dtype=np.float32).view(np.uint32), \
+        f"{what}: base {g['base'][0]!r} != {float(b)!r}"
+    codes, tags, hist = fmdq.quantize(d["x_t"], d["x_prev"], T, b, d["k0"])
+    perm, off = fmdq.bucket(tags)
+    check_integer_stages(g, codes, tags, hist, perm, off, what, d["w"])
+    y, accs = fmdq.linear(codes, tags, perm, off, d["w"], d["w_scale"], d["y_prev"], b, T,
+                          return_acc=True)
+    for tau in range(nt):
+        np.testing.assert_array_equal(g["acc"][tau].astype(np.int64), accs[tau],
+                                      err_msg=f"{what}: group accumulators of tile {tau}")
+    check_y(g["y_dbg"], y, d["y_prev"], what + " (per-group kernel)")
+    check_y(g["y"], y, d["y_prev"], what)
+
+
+@pytest.mark.parametrize("case", DYN, ids=lambda c: f"{c['rows']}x{c['K']}x{c['N']}-T{c['T']}-s{c['seed']}")
+def test_dynamic_base_layers_match_oracle(dm, case):
+    c = dict(case)
+    d = wl.make_custom(c.pop("rows"), c.pop("K"), c.pop("N"), c.pop("T"), seed=c.pop("seed"), **c)
+    dyn_compare(dm, d, d["name"] + " dyn")
+
+
+def test_dynamic_base_special_cases(dm):
+    """All-zero Δ keeps the static base; a zero sub-channel is left out; the
+    clamp to [2^-100, 2^100] (base only)."""
+    import torch
+    dev = torch.device("cuda:0")
+    d = wl.make_custom(64, 12, 8, 32, seed=47)
+    x_t = d["x_t"].copy()
+    x_t[32:64, 3] = d["x_prev"][32:64, 3]
+    d2 = dict(d, x_t=x_t, name="zero-subchannel")
+    dyn_compare(dm, d2, "zero sub-channel dyn")
+    d3 = dict(d, x_t=d["x_prev"].copy(), name="zero-delta")
+    dyn_compare(dm, d3, "all-zero delta dyn")
+    delta = d["x_t"].astype(np.float64) - d["x_prev"].astype(np.float64)
+    for scale, expect in ((-130, 2.0 ** -100), (110, 2.0 ** 100)):
+        xt = torch.from_numpy((delta * 2.0 ** scale).astype(np.float32)).to(dev)
+        xp = torch.zeros_like(xt)
+        base = torch.full((1,), float("nan"), dtype=torch.float32, device=dev)
+        p = dm.make_params(64, 12, 32, float(d["base"]), d["k0"])
+        log(f"clamp case 2^{scale}")
+        dm.dynamic_base(p, xt, xp, base)
+        torch.cuda.synchronize()
+        got = base.cpu().numpy()[0]
+        orc = fmdq.dynamic_base(xt.cpu().numpy(), xp.cpu().numpy(), 32, d["base"])
+        assert got == np.float32(expect) == orc
+
+
+@pytest.mark.parametrize("cfg,layer", [(1, "fc1"), (2, "fc2")], ids=lambda v: str(v))
+def test_dynamic_base_full_size(dm, cfg, layer):
+    """Full-size workload with the dynamic base: the base bit for bit, every
+    integer stage in full, Y on sampled token tiles."""
+    t0 = time.time()
+    d = wl.make_inputs(cfg, layer, 1)
+    rows, T = d["rows"], d["token_tile"]
+    nt = (rows + T - 1) // T
+    sample = sorted(set([0, 1, nt // 2, nt - 1]))
+    b = fmdq.dynamic_base(d["x_t"], d["x_prev"], T, d["base"])
+    log(f"case config {cfg} {layer} dyn: rows={rows} K={d['K']} N={d['N']} base {float(b)!r} "
+        f"(static {float(d['base'])!r})")
+    g = gpu_layer(dm, d, dynamic=True)
+    assert g["base"].view(np.uint32)[0] == np.asarray(b, dtype=np.float32).view(np.uint32)
+    codes, tags, hist = fmdq.quantize(d["x_t"], d["x_prev"], T, b, d["k0"])
+    perm, off = fmdq.bucket(tags)
+    check_integer_stages(g, codes, tags, hist, perm, off, d["name"] + " dyn", d["w"])
+    y = fmdq.linear(codes, tags, perm, off, d["w"], d["w_scale"], d["y_prev"], b, T, tiles=sample)
+    rows_s = np.concatenate([np.arange(tau * T, min(rows, tau * T + T)) for tau in sample])
+    check_y(g["y"][rows_s], y[rows_s], d["y_prev"][rows_s], d["name"] + " dyn")
     log(f"  done {time.time() - t0:.1f}s")
