@@ -11,7 +11,8 @@ pair; --eager launches kernel by kernel).  Prints one JSON line: whole-step
 dense-equivalent int8 TOPS (2*M*N*K per layer over the measured time), per-stage times from HIP events on the launch
 stream, the roofline of the dominant kernel (with the HBM traffic measured by
 rocprofv3 counters when a summary for the current kernel source exists under
-profiles/), and the CPU oracle timed on the host as a baseline.
+profiles/), the CPU oracle timed on the host as a baseline, and the same steps
+with the dynamic base (an extra pass over X; --no-dynamic skips it).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload pixart-alpha-1024px]
 
@@ -19,8 +20,8 @@ Traffic summary from two counter runs of this same command (run from the
 repository root; a plain 256 MiB device copy made before timing calibrates
 the counters):
 
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline
-    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic
     python bench.py --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write
 """
 from __future__ import annotations
@@ -122,13 +123,13 @@ def write_traffic(fetch_dir: str, write_dir: str) -> None:
     lines = ["# HBM traffic per launch, FMDQ differential linear, PixArt-alpha-style 1024px MLP",
              "",
              "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, rocprofv3 --pmc, one run each) of",
-             "`python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline` on one MI355X, scaled by what they read",
+             "`python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic` on one MI355X, scaled by what they read",
              f"for a plain {CAL_BYTES >> 20} MiB device copy made in the same run (fetch x{sf:.4f}, write x{sw:.4f}).",
              "Commands:",
              "",
              "```",
-             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
-             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic",
+             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic",
              "python bench.py --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write",
              "```",
              "",
@@ -193,11 +194,11 @@ def write_kernel_summary(trace_dir: str) -> None:
              "",
              "```",
              "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_bench -o run -- \\",
-             "    python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline",
+             "    python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline --no-dynamic",
              "python bench.py --write-kernel-summary gpurun_out/prof_bench",
              "```",
              "",
-             "rocprofv3 statistics (13 steps x 2 layers; fc1 and fc2 pooled per kernel):",
+             "rocprofv3 statistics over every launch of the run (eager warm-up steps, graph warm-up and timed replays, and the eager pass that times the stages; fc1 and fc2 pooled per kernel):",
              "",
              "| kernel | calls | total us | average us | min us | max us | % |",
              "|---|---|---|---|---|---|---|"]
@@ -224,6 +225,89 @@ def write_kernel_summary(trace_dir: str) -> None:
     print("\n".join(lines))
 
 
+def dynamic_variant(dm, torch, state, layers, rows, args, stream, ms_static) -> dict:
+    """The same steps with the dynamic base (DSTAR §3.1 step 1 / §5.2
+    DS-FMDQ-DYN): an extra pass over X finds the smallest positive sub-channel
+    maximum, and stages 1 and 3 read it from device memory.  Timed the same
+    way as the static steps (graph replays unless --eager), with per-stage
+    times and bit histograms from an eager pass."""
+    def step(i, events=None):
+        for L in layers:
+            s = state[L]
+            lay = s["layer"]
+            x_t, x_p = s["xs"][i % len(s["xs"])]
+            ev = events[L] if events is not None else None
+            if ev is not None:
+                ev[0].record(stream)
+            dm.dynamic_base(lay.p, x_t, x_p, lay.base_dev)
+            if ev is not None:
+                ev[1].record(stream)
+            dm.quantize_dyn(lay.p, lay.base_dev, x_t, x_p, lay.codes, lay.tags, lay.acodes, lay.hcodes,
+                            lay.bit_hist)
+            if ev is not None:
+                ev[2].record(stream)
+            dm.bucket(lay.p, lay.tags, lay.perm, lay.group_off)
+            if ev is not None:
+                ev[3].record(stream)
+            dm.linear_dyn(lay.p, lay.base_dev, s["N"], lay.codes, lay.perm, lay.group_off, lay.acodes,
+                          lay.hcodes, lay.w, lay.w_t, lay.w_scale, s["y"], s["y"])
+            if ev is not None:
+                ev[4].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    graphs = []
+    if not args.eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for i in range(args.pairs):
+                step(i)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        for p in range(args.pairs):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(p)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % args.pairs].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if graphs:
+            graphs[(args.warmup + i) % args.pairs].replay()
+        else:
+            step(args.warmup + i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    for L in layers:
+        state[L]["layer"].bit_hist.zero_()
+    events = [{L: [torch.cuda.Event(enable_timing=True) for _ in range(5)] for L in layers}
+              for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i, events[i])
+    torch.cuda.synchronize()
+    total_ops = sum(2 * rows * state[L]["N"] * state[L]["K"] for L in layers)
+    out = {"ms_per_step": ms, "value": total_ops / (ms * 1e-3) / 1e12, "vs_static_time": ms / ms_static,
+           "layers": {}}
+    for L in layers:
+        lay = state[L]["layer"]
+        hist = lay.bit_hist.cpu().numpy().astype(np.float64) / max(args.steps, 1)
+        st = {}
+        for j, name in enumerate(("base_pass", "quantize", "bucket", "linear")):
+            st[name + "_us"] = float(np.mean([events[i][L][j].elapsed_time(events[i][L][j + 1]) * 1e3
+                                              for i in range(args.steps)]))
+        K = state[L]["K"]
+        st["base_pass_gbs"] = 8.0 * rows * K / (st["base_pass_us"] * 1e-6) / 1e9
+        st["base_last"] = float(lay.base_dev.cpu()[0])
+        st["base_static"] = float(lay.p.base)
+        st["bits_hist_subchannels"] = [float(v) for v in hist]
+        st["avg_bits"] = float((hist * np.array([2, 4, 6, 8])).sum() / max(hist.sum(), 1))
+        out["layers"][L] = st
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,6 +317,7 @@ def main() -> int:
     ap.add_argument("--pairs", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch kernel by kernel instead of graph replays")
+    ap.add_argument("--no-dynamic", action="store_true", help="skip the dynamic-base comparison")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--write-kernel-summary", metavar="TRACE_DIR")
     args = ap.parse_args()
@@ -410,6 +495,9 @@ def main() -> int:
                    "pairs_cycled": args.pairs},
         "layers": layer_out, "kernels": kernels, "roofline": roof,
     }
+    if not args.no_dynamic:
+        print("[bench] dynamic-base variant", file=sys.stderr, flush=True)
+        out["dynamic_base"] = dynamic_variant(dm, torch, state, layers, rows, args, stream, ms_per_step)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline([[host[L][p] for L in layers] for p in range(args.pairs)])

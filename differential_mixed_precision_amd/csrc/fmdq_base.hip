@@ -25,22 +25,25 @@ __global__ void base_init_kernel(uint32_t* bits) {
   if (threadIdx.x == 0) *bits = kInfBits;
 }
 
-// Workgroup = one token tile × kThreads·V channels; thread j owns channels
-// [V·(slab·kThreads + j), +V) and walks the tile's rows (float4 loads when
-// V = 4: K % 4 == 0 and 16-byte aligned rows).
+// Workgroup = one token tile × 64·V channels; lane l of every wave owns
+// channels [V·(64·slab + l), +V) (float4 loads when V = 4: K % 4 == 0 and
+// 16-byte aligned rows), and wave w the rows [w·T/4, (w+1)·T/4) of the tile.
+// The four partial maxima meet in LDS; wave 0 forms M and the minimum.
 template <int V>
 __global__ __launch_bounds__(kThreads) void base_min_kernel(BaseArgs a, int32_t slabs) {
+  __shared__ float part[kThreads / 64][64 * V];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t tile = blockIdx.x / slabs;
   const int64_t slab = blockIdx.x - tile * slabs;
-  const int64_t k = (slab * kThreads + threadIdx.x) * V;
-  const int64_t r0 = tile * a.T;
-  const int64_t r1 = min(r0 + (int64_t)a.T, a.rows);
   const int64_t K = a.K;
-  uint32_t best = kInfBits;
-  if (k < K) {
-    float m[V];
+  const int64_t k = (slab * 64 + lane) * V;
+  const int64_t r0 = tile * a.T + (int64_t)wave * (a.T / 4);
+  const int64_t r1 = min(r0 + (int64_t)(a.T / 4), a.rows);
+  float m[V];
 #pragma unroll
-    for (int c = 0; c < V; ++c) m[c] = 0.0f;
+  for (int c = 0; c < V; ++c) m[c] = 0.0f;
+  if (k < K) {
+#pragma unroll 8
     for (int64_t r = r0; r < r1; ++r) {
       float xt[V], xp[V];
       if constexpr (V == 4) {
@@ -55,13 +58,24 @@ __global__ __launch_bounds__(kThreads) void base_min_kernel(BaseArgs a, int32_t 
 #pragma unroll
       for (int c = 0; c < V; ++c) m[c] = fmaxf(m[c], fabsf(__fsub_rn(xt[c], xp[c])));
     }
+  }
 #pragma unroll
-    for (int c = 0; c < V; ++c)
-      if (m[c] > 0.0f) best = min(best, __float_as_uint(m[c]));
+  for (int c = 0; c < V; ++c) part[wave][lane * V + c] = m[c];
+  __syncthreads();
+  if (wave != 0) return;
+  uint32_t best = kInfBits;
+  if (k < K) {
+#pragma unroll
+    for (int c = 0; c < V; ++c) {
+      float mc = part[0][lane * V + c];
+#pragma unroll
+      for (int w = 1; w < kThreads / 64; ++w) mc = fmaxf(mc, part[w][lane * V + c]);
+      if (mc > 0.0f) best = min(best, __float_as_uint(mc));
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) best = min(best, (uint32_t)__shfl_xor((int)best, o, 64));
-  if ((threadIdx.x & 63) == 0 && best != kInfBits) atomicMin(a.base_bits, best);
+  if (lane == 0 && best != kInfBits) atomicMin(a.base_bits, best);
 }
 
 __global__ void base_final_kernel(uint32_t* bits, float fallback) {
@@ -73,10 +87,8 @@ __global__ void base_final_kernel(uint32_t* bits, float fallback) {
 
 template <int V>
 int launch_v(const BaseArgs& a, hipStream_t s) {
-  const int64_t nt = n_tiles(a.rows, a.T);
-  const int64_t per = (int64_t)kThreads * V;
-  const int32_t slabs = (int32_t)((a.K + per - 1) / per);
-  const int64_t grid = nt * slabs;
+  const int32_t slabs = (int32_t)((a.K + 64 * V - 1) / (64 * V));
+  const int64_t grid = n_tiles(a.rows, a.T) * slabs;
   if (grid > 0x7FFFFFFF) return set_error(DSTAR_EUNSUPPORTED, "dynamic_base: grid too large");
   hipLaunchKernelGGL(base_min_kernel<V>, dim3((unsigned)grid), dim3(kThreads), 0, s, a, slabs);
   return check_launch("fmdq_dynamic_base (min)");
