@@ -69,8 +69,8 @@ extern "C" {
  *   K               input channels, 1..65535 (channel ids are uint16).
  *   token_tile      T, rows per token tile: 16, 32 or 64 (DSTAR §3.1 step 1
  *                   tiles Δ along the token dimension).
- *   base            static per-layer base scale (DSTAR §3.1, "predefined
- *                   static base"), a normal float in [2^-100, 2^100].
+ *   base            static per-layer base scale (DSTAR §3.1: fixed ahead of
+ *                   time instead of taken from the data), a normal float in [2^-100, 2^100].
  *   thr0_log2       k0 in Thr_0 = base * 2^k0, the 2-bit threshold of the
  *                   precision bins Thr_0 * 4^N (DSTAR §3.1 step 1), 1..15.
  * Tiles: n_t = ceil(rows / T); tile τ holds rows [τT, min(τT+T, rows)). */

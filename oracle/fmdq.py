@@ -102,7 +102,7 @@ def tile_rows(tile: int, rows: int, token_tile: int) -> tuple[int, int]:
 def subchannel_max(delta: np.ndarray, token_tile: int) -> np.ndarray:
     """M_{τk}: the largest |Δ| of each sub-channel (tile τ × channel k).
 
-    DSTAR §3.1 ❶ ("maximum absolute value of each sub-channel") and §4.2 QPU
+    DSTAR §3.1 ❶ (the largest magnitude within a sub-channel) and §4.2 QPU
     stage 1.  A running maximum over the rows of the tile, in float32.
     """
     rows, K = delta.shape
