@@ -128,14 +128,18 @@ def check_integer_stages(g, codes, tags, hist, perm, off, what="", w=None):
     np.testing.assert_array_equal(g["group_off"], off, err_msg=f"{what}: group offsets")
 
 
-def full_compare(dm, d, inplace=False):
+def full_compare(dm, d, inplace=False, dump=True):
     rows, T = d["rows"], d["token_tile"]
     nt = (rows + T - 1) // T
     log(f"case {d['name']} rows={rows} K={d['K']} N={d['N']} T={T} inplace={inplace}")
-    g = gpu_layer(dm, d, dbg=(0, nt), inplace=inplace)
+    g = gpu_layer(dm, d, dbg=(0, nt) if dump else None, inplace=inplace)
     codes, tags, hist = fmdq.quantize(d["x_t"], d["x_prev"], T, d["base"], d["k0"])
     perm, off = fmdq.bucket(tags)
     check_integer_stages(g, codes, tags, hist, perm, off, d["name"], d["w"])
+    if not dump:
+        y = fmdq.linear(codes, tags, perm, off, d["w"], d["w_scale"], d["y_prev"], d["base"], T)
+        check_y(g["y"], y, d["y_prev"], d["name"])
+        return g, y
     y, accs = fmdq.linear(codes, tags, perm, off, d["w"], d["w_scale"], d["y_prev"], d["base"], T,
                           return_acc=True)
     for tau in range(nt):
@@ -170,12 +174,31 @@ SMALL = [
     dict(rows=128, K=1152, N=144, T=32, seed=26, heavy=0.15, c_range=(0.05, 2000.0)),
 ]
 
+# Limits of the ABI: the largest K (the bucket's global-memory variant above
+# K = 32768), the largest K that the MFMA kernel takes, the largest N, one row.
+EDGE = [
+    dict(rows=32, K=65535, N=16, T=32, seed=30),
+    dict(rows=40, K=40000, N=20, T=16, seed=31, heavy=0.1),
+    dict(rows=64, K=65472, N=32, T=32, seed=32, heavy=0.05),
+    dict(rows=32, K=64, N=1 << 20, T=32, seed=33),
+    dict(rows=1, K=64, N=64, T=32, seed=34),
+    dict(rows=1, K=5, N=4, T=64, seed=35),
+]
+
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c['rows']}x{c['K']}x{c['N']}-T{c['T']}-s{c['seed']}")
 def test_small_layers_match_oracle(dm, case):
     c = dict(case)
     d = wl.make_custom(c.pop("rows"), c.pop("K"), c.pop("N"), c.pop("T"), c.pop("seed"), **c)
     full_compare(dm, d)
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: f"{c['rows']}x{c['K']}x{c['N']}-T{c['T']}-s{c['seed']}")
+def test_abi_limits_match_oracle(dm, case):
+    """(The group-accumulator dump is skipped at N = 2^20: it would be 2 GiB.)"""
+    c = dict(case)
+    d = wl.make_custom(c.pop("rows"), c.pop("K"), c.pop("N"), c.pop("T"), seed=c.pop("seed"), **c)
+    full_compare(dm, d, dump=d["N"] <= 65536)
 
 
 def test_zero_delta_gives_cached_output_bit_exact(dm):
@@ -245,11 +268,14 @@ def test_timestep_chain_in_place(dm):
         y_orc, y_gpu = r["y"], g["y"]
 
 
-def test_graph_replay_matches_eager(dm):
+@pytest.mark.parametrize("dynamic", [False, True], ids=["static", "dynamic"])
+def test_graph_replay_matches_eager(dm, dynamic):
     """One layer step captured in a HIP graph and replayed three times, with
     eager work and synchronizations between the replays, gives after every
     replay the same output (bit for bit) as the same number of eager steps;
-    and the eager steps match the oracle's chained outputs."""
+    and the eager steps match the oracle's chained outputs.  The dynamic-base
+    step (three more kernels, which reset and finalize the base in device
+    memory) is captured the same way."""
     import torch
     dev = torch.device("cuda:0")
     d = wl.make_custom(rows=300, K=1152, N=512, token_tile=32, seed=11, heavy=0.1)
@@ -259,15 +285,18 @@ def test_graph_replay_matches_eager(dm):
     x_t = torch.from_numpy(d["x_t"]).to(dev)
     x_p = torch.from_numpy(d["x_prev"]).to(dev)
     layer = dm.FmdqLayer(w, ws, rows, T, float(d["base"]), d["k0"])
+    run = (lambda lay, *a, **k: lay.step_dynamic(*a, **k)) if dynamic else \
+        (lambda lay, *a, **k: lay.step(*a, **k))
+    base = fmdq.dynamic_base(d["x_t"], d["x_prev"], T, d["base"]) if dynamic else d["base"]
     # eager reference: the output after 1, 2, 3 in-place steps
     y_e = torch.from_numpy(d["y_prev"]).to(dev)
     refs = []
     for _ in range(3):
-        layer.step(x_t, x_p, y_e)
+        run(layer, x_t, x_p, y_e)
         refs.append(y_e.cpu().numpy().copy())
     y_orc = d["y_prev"]
     for r in range(3):
-        y_orc = fmdq.layer(d["x_t"], d["x_prev"], d["w"], d["w_scale"], y_orc, d["base"], T,
+        y_orc = fmdq.layer(d["x_t"], d["x_prev"], d["w"], d["w_scale"], y_orc, base, T,
                            d["k0"])["y"]
         np.testing.assert_array_equal(refs[r], y_orc, err_msg=f"eager step {r + 1}")
     # graph: warm up on a side stream, capture one step, replay
@@ -276,18 +305,18 @@ def test_graph_replay_matches_eager(dm):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        layer.step(x_t, x_p, y_g.clone(), y_out=scratch)
+        run(layer, x_t, x_p, y_g.clone(), y_out=scratch)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        layer.step(x_t, x_p, y_g)
+        run(layer, x_t, x_p, y_g)
     other = dm.FmdqLayer(w, ws, rows, T, float(d["base"]), d["k0"])
     for r in range(3):
         g.replay()
         torch.cuda.synchronize()
         # eager work between replays, on the same kind of buffers
-        other.step(x_p, x_t, scratch)
+        run(other, x_p, x_t, scratch)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(y_g.cpu().numpy(), refs[r], err_msg=f"graph replay {r + 1}")
         log(f"  graph replay {r + 1}: bit-identical to {r + 1} eager steps")
