@@ -82,7 +82,7 @@ __device__ __forceinline__ void store_words(int8_t* dst, const uint32_t (&w)[RT 
 }
 
 template <int T, int CPT>
-__global__ __launch_bounds__(kThreads, 3) void quantize_kernel(QuantizeArgs a, int64_t n_work,
+__global__ __launch_bounds__(kThreads, 2) void quantize_kernel(QuantizeArgs a, int64_t n_work,
                                                             int32_t slabs) {
   constexpr int G = T / RT;                  // lanes per (tile, channels) group
   constexpr int kGroups = kThreads / G;      // channel groups per workgroup
@@ -106,19 +106,17 @@ __global__ __launch_bounds__(kThreads, 3) void quantize_kernel(QuantizeArgs a, i
     const int64_t nrows = a.rows - r0;       // real rows from r0 (may be <= 0)
 
     // Δ = X_t − X_{t−1} for RT rows × CPT channels (Eq. 1), kept in registers.
+    // The loads are unconditional (a row past the end reads the last row and
+    // is zeroed after), so all 2·RT of them are in flight together.
     float d[RT][CPT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      if (t < nrows) {
-        float xt[CPT], xp[CPT];
-        load_vec<CPT>(a.x_t + (r0 + t) * K + k, xt);
-        load_vec<CPT>(a.x_prev + (r0 + t) * K + k, xp);
+      const int64_t r = min(r0 + t, a.rows - 1);
+      float xt[CPT], xp[CPT];
+      load_vec<CPT>(a.x_t + r * K + k, xt);
+      load_vec<CPT>(a.x_prev + r * K + k, xp);
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) d[t][c] = __fsub_rn(xt[c], xp[c]);
-      } else {
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) d[t][c] = 0.0f;
-      }
+      for (int c = 0; c < CPT; ++c) d[t][c] = t < nrows ? __fsub_rn(xt[c], xp[c]) : 0.0f;
     }
 
     uint32_t tagword = 0;
