@@ -241,17 +241,16 @@ int launch_t(const QuantizeArgs& a, hipStream_t s) {
 
 int launch_quantize(const QuantizeArgs& a, hipStream_t s) {
   if (a.rows == 0) return DSTAR_OK;
-  // Channels per lane group (16 · CPT floats of Δ live in each lane's
-  // registers), limited by K's divisibility: 4 at T = 16 and 64; 2 at T = 32,
-  // where the smaller workgroup slabs (256 channels) measured faster on every
-  // workload (more workgroups, less of the last slab idle).
+  // Channels per lane group: as many as keep three waves per SIMD resident
+  // (16 · CPT floats of Δ live in each lane's registers), limited by K's
+  // divisibility.
   const bool vec4 = (a.K % 4) == 0;
   const bool vec2 = (a.K % 2) == 0;
   switch (a.T) {
     case 16:
       return vec4 ? launch_t<16, 4>(a, s) : vec2 ? launch_t<16, 2>(a, s) : launch_t<16, 1>(a, s);
     case 32:
-      return vec2 ? launch_t<32, 2>(a, s) : launch_t<32, 1>(a, s);
+      return vec4 ? launch_t<32, 4>(a, s) : vec2 ? launch_t<32, 2>(a, s) : launch_t<32, 1>(a, s);
     case 64:
       return vec4 ? launch_t<64, 4>(a, s) : vec2 ? launch_t<64, 2>(a, s) : launch_t<64, 1>(a, s);
     default:
