@@ -241,9 +241,10 @@ int launch_t(const QuantizeArgs& a, hipStream_t s) {
 
 int launch_quantize(const QuantizeArgs& a, hipStream_t s) {
   if (a.rows == 0) return DSTAR_OK;
-  // Channels per lane group: as many as keep three waves per SIMD resident
-  // (16 · CPT floats of Δ live in each lane's registers), limited by K's
-  // divisibility.
+  // Channels per lane group: up to 4 as K's divisibility allows (16 · CPT
+  // floats of Δ live in each lane's registers; two waves per SIMD).  At T = 32
+  // two channels per group (smaller slabs, more workgroups) measured slower in
+  // the pipelined step.
   const bool vec4 = (a.K % 4) == 0;
   const bool vec2 = (a.K % 2) == 0;
   switch (a.T) {
