@@ -7,8 +7,19 @@
 // makes the sub-channels whose shift-aligned codes need more than 8 bits a
 // prefix of every FPoT group, which the GEMM of stage 3 reads directly.)
 //
-// One workgroup per token tile runs an LDS counting sort.  Thread j owns the
-// contiguous channel range [j*per, (j+1)*per).  It counts its keys into column
+// One workgroup per token tile runs an LDS counting sort.
+//
+// For K <= 16384 (every workload) the count is a wave-level split: a wave
+// takes 64 consecutive channels ("chunk"), and for each lane the lanes with
+// the same bin are found with six ballots (one per bit of the bin); the
+// lowest of them writes the group's size into a [64 bins][chunks] table, and
+// a lane's rank among its peers is the number of lower peers.  One exclusive
+// scan over the table in (bin, chunk) order then gives every (bin, chunk) its
+// first output slot — the stable order, since chunks and lanes both run in
+// channel order — and each lane places its channel at slot + rank.  No step
+// is a chain of dependent LDS updates.
+//
+// Otherwise thread j owns the contiguous channel range [j*per, (j+1)*per).  It counts its keys into column
 // j of a [64][256] uint16 LDS table; one exclusive scan over that table, read
 // in row-major order, gives every (bin, thread) pair its first output slot,
 // which is exactly the stable order.  The threads then place their channels
@@ -60,6 +71,86 @@ __device__ void exclusive_scan_table(uint16_t* tab, uint32_t* wave_tot) {
     row[i] = (lo & 0xFFFFu) | (hi << 16);
   }
   __syncthreads();
+}
+
+constexpr int kBallotMaxK = 16384;
+constexpr int kBallotThreads = 1024;   // 16 waves: the chunks of one tile spread over them
+
+// Lanes of this wave whose 6-bit bin equals this lane's (active lanes only).
+__device__ __forceinline__ uint64_t peers_of(int bin, uint64_t active) {
+  uint64_t m = active;
+#pragma unroll
+  for (int bit = 0; bit < 6; ++bit) {
+    const uint64_t b = __ballot((bin >> bit) & 1);
+    m &= ((bin >> bit) & 1) ? b : ~b;
+  }
+  return m;
+}
+
+__global__ __launch_bounds__(kBallotThreads) void bucket_ballot_kernel(BucketArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int K = a.K;
+  const int C = (K + 63) / 64;                  // chunks of 64 channels
+  const int E = kBins * C;                      // table entries, bin-major
+  const int epad = (E + 7) & ~7;
+  uint16_t* cnt = reinterpret_cast<uint16_t*>(smem);                   // [64][C]
+  uint32_t* wave_tot = reinterpret_cast<uint32_t*>(smem + 2 * epad);   // [16]
+  uint8_t* tags_s = smem + 2 * epad + 64;                              // [K]
+  const int kpad = (K + 15) & ~15;
+  uint16_t* perm_s = reinterpret_cast<uint16_t*>(tags_s + kpad);       // [K]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int per = (E + kBallotThreads - 1) / kBallotThreads;   // scan entries per thread
+  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+
+  for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+    const uint8_t* tg = a.tags + tile * (int64_t)K;
+    uint16_t* out = a.perm + tile * (int64_t)K;
+    for (int i = tid; i < K; i += kBallotThreads) tags_s[i] = tg[i];
+    for (int i = tid; i < epad / 8; i += kBallotThreads) reinterpret_cast<uint4*>(cnt)[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+    for (int c = wave; c < C; c += kBallotThreads / 64) {
+      const int k = 64 * c + lane;
+      const bool act = k < K;
+      const uint64_t active = __ballot(act);
+      const int bin = act ? bin_of(tags_s[k]) : 0;
+      const uint64_t peers = peers_of(bin, active);
+      if (act && (peers & below) == 0) cnt[bin * C + c] = (uint16_t)__popcll(peers);
+    }
+    __syncthreads();
+    // exclusive scan of cnt in (bin, chunk) order
+    uint32_t sum = 0;
+    for (int e = e0; e < e1; ++e) sum += cnt[e];
+    uint32_t inc = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t n = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += n;
+    }
+    if (lane == 63) wave_tot[wave] = inc;
+    __syncthreads();
+    uint32_t run = inc - sum;
+    for (int w = 0; w < wave; ++w) run += wave_tot[w];
+    for (int e = e0; e < e1; ++e) {
+      const uint32_t v = cnt[e];
+      cnt[e] = (uint16_t)run;
+      run += v;
+    }
+    __syncthreads();
+    if (tid < kBins) a.group_off[tile * (kBins + 1) + tid] = (int32_t)cnt[tid * C];
+    if (tid == kBins) a.group_off[tile * (kBins + 1) + kBins] = K;
+    for (int c = wave; c < C; c += kBallotThreads / 64) {
+      const int k = 64 * c + lane;
+      const bool act = k < K;
+      const uint64_t active = __ballot(act);
+      const int bin = act ? bin_of(tags_s[k]) : 0;
+      const uint64_t peers = peers_of(bin, active);
+      if (act) perm_s[cnt[bin * C + c] + __popcll(peers & below)] = (uint16_t)k;
+    }
+    __syncthreads();
+    for (int i = tid; i < K; i += kBallotThreads) out[i] = perm_s[i];
+    __syncthreads();
+  }
 }
 
 template <bool kInLds>
@@ -115,6 +206,18 @@ __global__ __launch_bounds__(kThreads) void bucket_kernel(BucketArgs a) {
 int launch_bucket(const BucketArgs& a, hipStream_t s) {
   if (a.n_tiles == 0) return DSTAR_OK;
   const int64_t grid = a.n_tiles < 2048 ? a.n_tiles : 2048;
+  if (a.K <= kBallotMaxK) {
+    const size_t E = (size_t)kBins * ((a.K + 63) / 64);
+    const size_t lds = 2 * ((E + 7) & ~(size_t)7) + 64 + 3 * (size_t)((a.K + 15) & ~15);
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute((const void*)bucket_ballot_kernel,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess)
+        return set_error(DSTAR_EHIP, "fmdq_bucket: hipFuncSetAttribute: %s", hipGetErrorString(e));
+    }
+    hipLaunchKernelGGL(bucket_ballot_kernel, dim3((unsigned)grid), dim3(kBallotThreads), lds, s, a);
+    return check_launch("fmdq_bucket");
+  }
   const size_t base = (size_t)kBins * kThreads * 2 + 64;
   size_t lds = base;
   const void* fn = (const void*)bucket_kernel<false>;
