@@ -424,6 +424,41 @@ def linear(codes: np.ndarray, tags: np.ndarray, perm: np.ndarray,
     return y
 
 
+#: Constants of the tanh form of GELU: sqrt(2/pi) and the cubic coefficient.
+GELU_C = 0.7978845608028654
+GELU_A = 0.044715
+
+
+def gelu(y: np.ndarray) -> np.ndarray:
+    """GELU of the MLP between the two linears, the activation DSTAR fuses
+    into the linear through its vector unit (§4.2 "Design of VPU", §4.3
+    "Linear Operation").  The page gives no formula (its unit uses piecewise
+    cubics); the reading here is the tanh form used by the DiT MLPs,
+    0.5·y·(1 + tanh(u)) with u = c·(y + a·y³), written as y / (1 + exp(−2u))
+    (the same function without the cancellation of 1 + tanh(u) at negative
+    y) and evaluated in float64, then rounded once to float32.  The cube is
+    (y·y)·y.
+    """
+    y64 = np.asarray(y, dtype=F32).astype(F64)
+    u = GELU_C * (y64 + GELU_A * ((y64 * y64) * y64))
+    with np.errstate(over="ignore"):
+        return (y64 / (1.0 + np.exp(-2.0 * u))).astype(F32)
+
+
+def mlp_step(x_t, x_prev, y1_prev, g_prev, y2_prev, fc1, fc2, token_tile, k0):
+    """One timestep pair through fc1 → GELU → fc2 with every output cached:
+    fc1 updates its output Y1 differentially (layer); G = GELU(Y1) is fc2's
+    input at this step and G_prev its input at the previous one, so fc2
+    updates Y2 from the difference G − G_prev (DSTAR §2.2 Eq. 1 applied to
+    both linears of the MLP; §4.3 fuses the GELU into the first).
+    ``fc1``/``fc2`` are dicts with w, w_scale and base.  Returns (y1, g, y2,
+    hist1, hist2)."""
+    r1 = layer(x_t, x_prev, fc1["w"], fc1["w_scale"], y1_prev, fc1["base"], token_tile, k0)
+    g = gelu(r1["y"])
+    r2 = layer(g, g_prev, fc2["w"], fc2["w_scale"], y2_prev, fc2["base"], token_tile, k0)
+    return r1["y"], g, r2["y"], r1["hist"], r2["hist"]
+
+
 #: The range a layer's base is held to: the library rejects a static base
 #: outside it, and a dynamic base is clamped into it.
 BASE_MIN = 2.0 ** -100
