@@ -11,8 +11,10 @@ pair; --eager launches kernel by kernel).  Prints one JSON line: whole-step
 dense-equivalent int8 TOPS (2*M*N*K per layer over the measured time), per-stage times from HIP events on the launch
 stream, the roofline of the dominant kernel (with the HBM traffic measured by
 rocprofv3 counters when a summary for the current kernel source exists under
-profiles/), the CPU oracle timed on the host as a baseline, and the same steps
-with the dynamic base (an extra pass over X; --no-dynamic skips it).
+profiles/), the CPU oracle timed on the host as a baseline, the same steps
+with the dynamic base (an extra pass over X; --no-dynamic skips it), and the
+MLP chained over all timestep pairs with the GELU fused into fc1 (bits per
+step; --no-chain skips it).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload pixart-alpha-1024px]
 
@@ -20,8 +22,8 @@ Traffic summary from two counter runs of this same command (run from the
 repository root; a plain 256 MiB device copy made before timing calibrates
 the counters):
 
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic
-    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain
     python bench.py --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write
 """
 from __future__ import annotations
@@ -123,13 +125,13 @@ def write_traffic(fetch_dir: str, write_dir: str) -> None:
     lines = ["# HBM traffic per launch, FMDQ differential linear, PixArt-alpha-style 1024px MLP",
              "",
              "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, rocprofv3 --pmc, one run each) of",
-             "`python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic` on one MI355X, scaled by what they read",
+             "`python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain` on one MI355X, scaled by what they read",
              f"for a plain {CAL_BYTES >> 20} MiB device copy made in the same run (fetch x{sf:.4f}, write x{sw:.4f}).",
              "Commands:",
              "",
              "```",
-             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic",
-             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic",
+             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain",
+             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain",
              "python bench.py --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write",
              "```",
              "",
@@ -194,7 +196,7 @@ def write_kernel_summary(trace_dir: str) -> None:
              "",
              "```",
              "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_bench -o run -- \\",
-             "    python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline --no-dynamic",
+             "    python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline --no-dynamic --no-chain",
              "python bench.py --write-kernel-summary gpurun_out/prof_bench",
              "```",
              "",
@@ -223,6 +225,62 @@ def write_kernel_summary(trace_dir: str) -> None:
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def mlp_chain(dm, torch, cfg, spec, stream) -> dict:
+    """The MLP as it runs inside a denoising loop: fc1 with the GELU fused into
+    its stage 3, then fc2 on G_t − G_{t−1}, over all the workload's timestep
+    pairs with both outputs cached on the device (DSTAR §4.3; the bit widths
+    per step are the trend of DSTAR §5.4, Fig. 22).  fc2's static base is
+    profiled on the first step (host side, before the chain).  Steps run
+    eagerly (each pair has its own inputs); per-step times from HIP events."""
+    from gen import workloads as wl
+    rows, T = spec["rows"], spec["token_tile"]
+    pairs = spec["pairs"]
+    xs = [torch.from_numpy(x).to(torch.device("cuda:0")) for x in wl.make_walk(cfg, "fc1", pairs)]
+    d1 = wl.make_inputs(cfg, "fc1", 1)
+    d2 = wl.make_inputs(cfg, "fc2", 1)
+    dev = xs[0].device
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    mlp = dm.FmdqMLP(t(d1["w"]), t(d1["w_scale"]), float(d1["base"]), t(d2["w"]), t(d2["w_scale"]),
+                     1.0, rows, T, d1["k0"], d1["tokens_per_seq"])
+    y1_0, y2_0 = t(d1["y_prev"]), t(d2["y_prev"])
+    # profile fc2's base on step 1: RMS of G_1 - G_0 (a throw-away first pass)
+    mlp.start(y1_0.clone(), y2_0.clone())
+    g0 = mlp.g_cur.clone()
+    mlp.step(xs[1], xs[0])
+    torch.cuda.synchronize()
+    base2 = wl.profiled_base((mlp.g_cur.double() - g0.double()).cpu().numpy())
+    mlp.fc2.p.base = float(base2)
+    mlp.start(y1_0.clone(), y2_0.clone())
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(pairs)]
+    bits1, bits2 = [], []
+    w = np.array([2, 4, 6, 8])
+    for p in range(1, pairs + 1):
+        mlp.fc1.bit_hist.zero_()
+        mlp.fc2.bit_hist.zero_()
+        e = ev[p - 1]
+        e[0].record(stream)
+        nxt = 1 - mlp.cur
+        mlp.fc1.step(xs[p], xs[p - 1], mlp.y1, gelu_out=mlp.g[nxt])
+        e[1].record(stream)
+        mlp.fc2.step(mlp.g[nxt], mlp.g[mlp.cur], mlp.y2)
+        mlp.cur = nxt
+        e[2].record(stream)
+        h1 = mlp.fc1.bit_hist.cpu().numpy().astype(np.float64)
+        h2 = mlp.fc2.bit_hist.cpu().numpy().astype(np.float64)
+        bits1.append(float((h1 * w).sum() / h1.sum()))
+        bits2.append(float((h2 * w).sum() / h2.sum()))
+    torch.cuda.synchronize()
+    fc1_us = [a.elapsed_time(b) * 1e3 for a, b, _ in ev]
+    fc2_us = [b.elapsed_time(c) * 1e3 for _, b, c in ev]
+    return {"pairs": pairs, "launch": "eager, one step per pair",
+            "ms_per_step": float(np.mean(np.array(fc1_us) + np.array(fc2_us))) / 1e3,
+            "fc1_with_gelu_us": float(np.mean(fc1_us)), "fc2_us": float(np.mean(fc2_us)),
+            "fc2_base_profiled": float(base2),
+            "avg_bits_fc1_per_step": [round(b, 4) for b in bits1],
+            "avg_bits_fc2_per_step": [round(b, 4) for b in bits2]}
 
 
 def dynamic_variant(dm, torch, state, layers, rows, args, stream, ms_static) -> dict:
@@ -318,6 +376,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch kernel by kernel instead of graph replays")
     ap.add_argument("--no-dynamic", action="store_true", help="skip the dynamic-base comparison")
+    ap.add_argument("--no-chain", action="store_true", help="skip the fc1 -> GELU -> fc2 timestep chain")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--write-kernel-summary", metavar="TRACE_DIR")
     args = ap.parse_args()
@@ -498,6 +557,9 @@ def main() -> int:
                    "pairs_cycled": args.pairs},
         "layers": layer_out, "kernels": kernels, "roofline": roof,
     }
+    if not args.no_chain and set(layers) >= {"fc1", "fc2"}:
+        print("[bench] fc1 -> GELU -> fc2 chain", file=sys.stderr, flush=True)
+        out["mlp_chain"] = mlp_chain(dm, torch, cfg, spec, stream)
     if not args.no_dynamic:
         print("[bench] dynamic-base variant", file=sys.stderr, flush=True)
         out["dynamic_base"] = dynamic_variant(dm, torch, state, layers, rows, args, stream, ms_per_step)

@@ -5,18 +5,22 @@ The layer runs in three HIP kernels behind a C ABI (include/dstar_fmdq.h):
 channels by FPoT tag) and ``linear`` (grouped int8 GEMM with shift alignment,
 dequantization and the reverse differential).  ``dynamic_base`` with
 ``quantize_dyn`` / ``linear_dyn`` is the variant whose base is the smallest
-sub-channel maximum of the data instead of a static one.  This package is the
-thin Python binding; ``FmdqLayer`` allocates the buffers of one layer with
-torch and calls the stages on the current stream.
+sub-channel maximum of the data instead of a static one; ``linear_gelu`` fuses
+the MLP's GELU into stage 3 and ``gelu`` is the same activation on its own.
+This package is the thin Python binding; ``FmdqLayer`` allocates the buffers of
+one layer with torch and calls the stages on the current stream, and
+``FmdqMLP`` chains two of them (fc1 → GELU → fc2) over timesteps.
 """
 from __future__ import annotations
 
 from . import _binding
-from ._binding import (FmdqError, Params, bucket, dynamic_base, linear, linear_dyn,  # noqa: F401
-                       load, make_params, pack_weights, quantize, quantize_dyn)
+from ._binding import (FmdqError, Params, bucket, dynamic_base, gelu, linear,  # noqa: F401
+                       linear_dyn, linear_gelu, load, make_params, pack_weights, quantize,
+                       quantize_dyn)
 
-__all__ = ["FmdqError", "Params", "FmdqLayer", "bucket", "dynamic_base", "linear", "linear_dyn",
-           "load", "make_params", "pack_weights", "quantize", "quantize_dyn", "n_tiles"]
+__all__ = ["FmdqError", "Params", "FmdqLayer", "FmdqMLP", "bucket", "dynamic_base", "gelu", "linear",
+           "linear_dyn", "linear_gelu", "load", "make_params", "pack_weights", "quantize",
+           "quantize_dyn", "n_tiles"]
 
 
 def n_tiles(rows: int, token_tile: int) -> int:
@@ -53,13 +57,18 @@ class FmdqLayer:
         self.bit_hist = torch.zeros(4, dtype=torch.int32, device=dev)
         self.base_dev = torch.empty(1, dtype=torch.float32, device=dev)
 
-    def step(self, x_t, x_prev, y, y_out=None, stream=None, hist: bool = True):
+    def step(self, x_t, x_prev, y, y_out=None, stream=None, hist: bool = True, gelu_out=None):
+        """One timestep pair; with ``gelu_out`` stage 3 also stores GELU(Y_t) there."""
         quantize(self.p, x_t, x_prev, self.codes, self.tags, self.acodes, self.hcodes,
                  self.bit_hist if hist else None, stream)
         bucket(self.p, self.tags, self.perm, self.group_off, stream)
         out = y if y_out is None else y_out
-        linear(self.p, self.N, self.codes, self.perm, self.group_off, self.acodes, self.hcodes,
-               self.w, self.w_t, self.w_scale, y, out, stream=stream)
+        if gelu_out is None:
+            linear(self.p, self.N, self.codes, self.perm, self.group_off, self.acodes, self.hcodes,
+                   self.w, self.w_t, self.w_scale, y, out, stream=stream)
+        else:
+            linear_gelu(self.p, self.N, self.codes, self.perm, self.group_off, self.acodes,
+                        self.hcodes, self.w, self.w_t, self.w_scale, y, out, gelu_out, stream=stream)
         return out
 
     def step_dynamic(self, x_t, x_prev, y, y_out=None, stream=None, hist: bool = True):
@@ -71,3 +80,44 @@ class FmdqLayer:
         linear_dyn(self.p, self.base_dev, self.N, self.codes, self.perm, self.group_off, self.acodes,
                    self.hcodes, self.w, self.w_t, self.w_scale, y, out, stream=stream)
         return out
+
+
+class FmdqMLP:
+    """The MLP of a DiT block, fc1 → GELU → fc2, run differentially over
+    timesteps (DSTAR Eq. 1 for both linears; the GELU fused into fc1's stage 3
+    as in DSTAR §4.3).
+
+    State kept on the device between steps: Y1 (fc1's cached output, updated
+    in place), G_t and G_{t−1} = GELU(Y1) at this and the previous step (two
+    buffers used in turn; they are fc2's X_t and X_{t−1}) and Y2 (fc2's cached
+    output, updated in place).  ``start(y1, y2)`` takes the cached outputs of
+    the last full step and forms G from Y1; each ``step(x_t, x_prev)`` then
+    runs fc1 with the fused GELU and fc2 on G_t − G_{t−1}.
+    """
+
+    def __init__(self, w1, ws1, base1: float, w2, ws2, base2: float, rows: int, token_tile: int,
+                 thr0_log2: int, tokens_per_seq: int | None = None):
+        import torch
+        self.fc1 = FmdqLayer(w1, ws1, rows, token_tile, base1, thr0_log2, tokens_per_seq)
+        self.fc2 = FmdqLayer(w2, ws2, rows, token_tile, base2, thr0_log2, tokens_per_seq)
+        assert self.fc1.N == self.fc2.K
+        self.g = [torch.empty((rows, self.fc1.N), dtype=torch.float32, device=w1.device) for _ in range(2)]
+        self.cur = 0
+        self.y1 = self.y2 = None
+
+    def start(self, y1, y2, stream=None) -> None:
+        self.y1, self.y2 = y1, y2
+        self.cur = 0
+        gelu(y1, self.g[0], stream=stream)
+
+    @property
+    def g_cur(self):
+        """GELU(Y1) of the latest step (fc2's latest input)."""
+        return self.g[self.cur]
+
+    def step(self, x_t, x_prev, stream=None, hist: bool = True):
+        nxt = 1 - self.cur
+        self.fc1.step(x_t, x_prev, self.y1, stream=stream, hist=hist, gelu_out=self.g[nxt])
+        self.fc2.step(self.g[nxt], self.g[self.cur], self.y2, stream=stream, hist=hist)
+        self.cur = nxt
+        return self.y2

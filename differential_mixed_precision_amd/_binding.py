@@ -20,10 +20,11 @@ TAG_OFFSET = 15
 POT_MAX = 21
 PREC_SHIFT = 4
 MAX_K = 65535
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 SYMBOLS = ("dstar_fmdq_quantize", "dstar_fmdq_bucket", "dstar_fmdq_pack_weights",
-           "dstar_fmdq_linear", "dstar_fmdq_dynamic_base", "dstar_fmdq_quantize_dyn",
+           "dstar_fmdq_linear", "dstar_fmdq_linear_gelu", "dstar_fmdq_gelu",
+           "dstar_fmdq_dynamic_base", "dstar_fmdq_quantize_dyn",
            "dstar_fmdq_linear_dyn", "dstar_fmdq_last_error", "dstar_fmdq_abi_version")
 
 
@@ -64,6 +65,10 @@ def load() -> ctypes.CDLL:
     lib.dstar_fmdq_pack_weights.restype = ctypes.c_int
     lib.dstar_fmdq_linear.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
     lib.dstar_fmdq_linear.restype = ctypes.c_int
+    lib.dstar_fmdq_linear_gelu.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.dstar_fmdq_linear_gelu.restype = ctypes.c_int
+    lib.dstar_fmdq_gelu.argtypes = [vp, vp, ctypes.c_int64, vp]
+    lib.dstar_fmdq_gelu.restype = ctypes.c_int
     lib.dstar_fmdq_dynamic_base.argtypes = [P, vp, vp, vp, vp]
     lib.dstar_fmdq_dynamic_base.restype = ctypes.c_int
     lib.dstar_fmdq_quantize_dyn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -161,3 +166,17 @@ def linear_dyn(p: Params, base, N: int, codes, perm, group_off, acodes, hcodes, 
                                         _ptr(w_t), _ptr(w_scale), _ptr(y_prev), _ptr(y_out),
                                         _ptr(acc_dbg), int(dbg_tile_lo), int(dbg_tile_hi),
                                         _stream(stream)))
+
+
+def linear_gelu(p: Params, N: int, codes, perm, group_off, acodes, hcodes, w, w_t, w_scale, y_prev,
+                y_out, gelu_out, stream=None) -> None:
+    """dstar_fmdq_linear_gelu: stage 3 that also stores GELU(Y_t) in gelu_out."""
+    _check(load().dstar_fmdq_linear_gelu(ctypes.byref(p), int(N), _ptr(codes), _ptr(perm),
+                                         _ptr(group_off), _ptr(acodes), _ptr(hcodes), _ptr(w),
+                                         _ptr(w_t), _ptr(w_scale), _ptr(y_prev), _ptr(y_out),
+                                         _ptr(gelu_out), _stream(stream)))
+
+
+def gelu(y, g, n: int | None = None, stream=None) -> None:
+    """dstar_fmdq_gelu: g = GELU(y) elementwise (n defaults to y.numel())."""
+    _check(load().dstar_fmdq_gelu(_ptr(y), _ptr(g), int(y.numel() if n is None else n), _stream(stream)))

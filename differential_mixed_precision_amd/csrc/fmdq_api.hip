@@ -111,8 +111,8 @@ int quantize_impl(const dstar_fmdq_params* p, const float* base_dev, const float
 int linear_impl(const dstar_fmdq_params* p, const float* base_dev, int32_t N, const int8_t* codes,
                 const uint16_t* perm, const int32_t* group_off, const int8_t* acodes,
                 const int8_t* hcodes, const int8_t* w, const int8_t* w_t, const float* w_scale,
-                const float* y_prev, float* y_out, int32_t* acc_dbg, int32_t dbg_tile_lo,
-                int32_t dbg_tile_hi, void* stream);
+                const float* y_prev, float* y_out, float* gelu_out, int32_t* acc_dbg,
+                int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream);
 
 // Checks the device base pointer of the _dyn entry points.
 int check_base_dev(const float* base_dev, const char* what) {
@@ -199,7 +199,30 @@ int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N, const int8_t* codes
                       int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream) {
   clear_error();
   return linear_impl(p, nullptr, N, codes, perm, group_off, acodes, hcodes, w, w_t, w_scale, y_prev,
-                     y_out, acc_dbg, dbg_tile_lo, dbg_tile_hi, stream);
+                     y_out, nullptr, acc_dbg, dbg_tile_lo, dbg_tile_hi, stream);
+}
+
+int dstar_fmdq_linear_gelu(const dstar_fmdq_params* p, int32_t N, const int8_t* codes,
+                           const uint16_t* perm, const int32_t* group_off, const int8_t* acodes,
+                           const int8_t* hcodes, const int8_t* w, const int8_t* w_t,
+                           const float* w_scale, const float* y_prev, float* y_out,
+                           float* gelu_out, void* stream) {
+  clear_error();
+  if (gelu_out == nullptr) return set_error(DSTAR_ENULL, "linear_gelu: gelu_out must not be NULL");
+  if (!aligned(gelu_out, 16)) return set_error(DSTAR_EALIGN, "linear_gelu: gelu_out must be 16-byte aligned");
+  if (gelu_out == y_out || gelu_out == y_prev)
+    return set_error(DSTAR_EINVAL, "linear_gelu: gelu_out must not alias y_prev or y_out");
+  return linear_impl(p, nullptr, N, codes, perm, group_off, acodes, hcodes, w, w_t, w_scale, y_prev,
+                     y_out, gelu_out, nullptr, 0, 0, stream);
+}
+
+int dstar_fmdq_gelu(const float* y, float* g, int64_t n, void* stream) {
+  clear_error();
+  if (n < 0) return set_error(DSTAR_EINVAL, "gelu: n = %lld < 0", (long long)n);
+  if (n == 0) return DSTAR_OK;
+  if (!y || !g) return set_error(DSTAR_ENULL, "gelu: y and g must not be NULL");
+  if (!aligned(y, 16) || !aligned(g, 16)) return set_error(DSTAR_EALIGN, "gelu: y and g must be 16-byte aligned");
+  return launch_gelu(y, g, n, (hipStream_t)stream);
 }
 
 int dstar_fmdq_linear_dyn(const dstar_fmdq_params* p, const float* base, int32_t N,
@@ -211,7 +234,7 @@ int dstar_fmdq_linear_dyn(const dstar_fmdq_params* p, const float* base, int32_t
   clear_error();
   if (int rc = check_base_dev(base, "linear_dyn")) return rc;
   return linear_impl(p, base, N, codes, perm, group_off, acodes, hcodes, w, w_t, w_scale, y_prev,
-                     y_out, acc_dbg, dbg_tile_lo, dbg_tile_hi, stream);
+                     y_out, nullptr, acc_dbg, dbg_tile_lo, dbg_tile_hi, stream);
 }
 
 }  // extern "C"
@@ -221,8 +244,8 @@ namespace {
 int linear_impl(const dstar_fmdq_params* p, const float* base_dev, int32_t N, const int8_t* codes,
                 const uint16_t* perm, const int32_t* group_off, const int8_t* acodes,
                 const int8_t* hcodes, const int8_t* w, const int8_t* w_t, const float* w_scale,
-                const float* y_prev, float* y_out, int32_t* acc_dbg, int32_t dbg_tile_lo,
-                int32_t dbg_tile_hi, void* stream) {
+                const float* y_prev, float* y_out, float* gelu_out, int32_t* acc_dbg,
+                int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream) {
   int64_t nt = 0;
   if (int rc = check_params(p, &nt)) return rc;
   if (N < 1 || N > (1 << 20) || N % 4 != 0)
@@ -261,6 +284,7 @@ int linear_impl(const dstar_fmdq_params* p, const float* base_dev, int32_t N, co
   a.T = p->token_tile;
   a.base = (double)p->base;
   a.base_dev = base_dev;
+  a.gelu_out = gelu_out;
   return launch_linear(a, (hipStream_t)stream);
 }
 

@@ -66,6 +66,7 @@ struct LinearArgs {
   int32_t T;
   double base;
   const float* base_dev;   // non-NULL: base read from device memory (dynamic base)
+  float* gelu_out;         // non-NULL: GELU(Y_t) is stored here as well
 };
 int launch_linear(const LinearArgs& a, hipStream_t s);
 struct BaseArgs {
@@ -78,6 +79,16 @@ struct BaseArgs {
   float fallback;
 };
 int launch_dynamic_base(const BaseArgs& a, hipStream_t s);
+// GELU in its tanh form, y / (1 + exp(-2u)) with u = c·(y + a·y³), evaluated
+// in float64 (the cube as (y·y)·y) and rounded once to float32: the activation
+// between the two linears of the MLP, fused into the first one's epilogue.
+__device__ __forceinline__ float gelu_of(float yf) {
+  const double y = (double)yf;
+  const double u = __dmul_rn(0.7978845608028654,
+                             __dadd_rn(y, __dmul_rn(0.044715, __dmul_rn(__dmul_rn(y, y), y))));
+  return (float)__ddiv_rn(y, __dadd_rn(1.0, exp(__dmul_rn(-2.0, u))));
+}
+int launch_gelu(const float* y, float* g, int64_t n, hipStream_t s);
 int launch_pack_weights(int32_t K, int32_t N, const int8_t* w, int8_t* w_t, hipStream_t s);
 int launch_linear_general(const LinearArgs& a, hipStream_t s);
 bool linear_mfma_supported(const LinearArgs& a);

@@ -194,7 +194,9 @@ __device__ __forceinline__ void shift_acc(v16i& acc, int s) {
   for (int r = 0; r < 16; ++r) acc[r] = (int)((uint32_t)acc[r] << s);
 }
 
-template <int T, bool VecW>
+// Gelu: the epilogue also stores GELU(Y_t) (a separate instantiation, so the
+// plain kernel carries none of its code).
+template <int T, bool VecW, bool Gelu>
 __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, int32_t row_blocks,
                                                                   int32_t col_blocks) {
   constexpr int kTiles = Cfg<T>::kTiles;
@@ -495,6 +497,8 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   constexpr int kNt = 2;   // aux bit: non-temporal
   const rsrc_t r_yp = make_rsrc(a.y_prev + tile0 * T * N, (uint32_t)(BM * N * 4));
   const rsrc_t r_yo = make_rsrc(a.y_out + tile0 * T * N, (uint32_t)(BM * N * 4));
+  constexpr bool has_gelu = Gelu;
+  const rsrc_t r_go = make_rsrc(Gelu ? a.gelu_out + tile0 * T * N : a.y_out, (uint32_t)(BM * N * 4));
   const uint32_t lane_off = (uint32_t)(((4 * h) * N + nw + li) * 4);
   const uint32_t row4 = (uint32_t)(N * 4);
   auto y_off = [&](int rb, int cb, int r) {
@@ -664,6 +668,8 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
         const double d = __dmul_rn(__dmul_rn((double)acc[rb][cb][r], base), ws[cb]);
         const float y = (float)__dadd_rn((double)cur[r], d);
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, y), r_yo, y_off(rb, cb, r), 0, kNt);
+        if constexpr (has_gelu)
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gelu_of(y)), r_go, y_off(rb, cb, r), 0, kNt);
       }
       // keep each unit's loads, math and stores in this order (bounds the
       // registers the epilogue holds at once)
@@ -684,7 +690,9 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
           if (grow >= a.rows) continue;
           const int64_t idx = grow * N + n;
           const double d = __dmul_rn(__dmul_rn((double)acc[rb][cb][r], base), ws[cb]);
-          a.y_out[idx] = (float)__dadd_rn((double)a.y_prev[idx], d);
+          const float y = (float)__dadd_rn((double)a.y_prev[idx], d);
+          a.y_out[idx] = y;
+          if constexpr (has_gelu) a.gelu_out[idx] = gelu_of(y);
         }
       }
     }
@@ -732,13 +740,15 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
         if (grow >= a.rows) continue;
         const int64_t idx = grow * N + n;
         const double d = __dmul_rn(__dmul_rn((double)sum[t], base), wsn);
-        a.y_out[idx] = (float)__dadd_rn((double)a.y_prev[idx], d);
+        const float y = (float)__dadd_rn((double)a.y_prev[idx], d);
+        a.y_out[idx] = y;
+        if constexpr (has_gelu) a.gelu_out[idx] = gelu_of(y);
       }
     }
   }
 }
 
-template <int T, bool VecW>
+template <int T, bool VecW, bool Gelu>
 int launch_tv(const LinearArgs& a, hipStream_t s) {
   const int64_t nt = n_tiles(a.rows, T);
   const int64_t row_blocks = (nt + Cfg<T>::kTiles - 1) / Cfg<T>::kTiles;
@@ -748,20 +758,22 @@ int launch_tv(const LinearArgs& a, hipStream_t s) {
     return set_error(DSTAR_EUNSUPPORTED, "fmdq_linear: grid too large");
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)linear_mfma_kernel<T, VecW>,
+    hipError_t e = hipFuncSetAttribute((const void*)linear_mfma_kernel<T, VecW, Gelu>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess)
       return set_error(DSTAR_EHIP, "fmdq_linear: hipFuncSetAttribute: %s", hipGetErrorString(e));
     attr_set = true;
   }
-  hipLaunchKernelGGL((linear_mfma_kernel<T, VecW>), dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s,
+  hipLaunchKernelGGL((linear_mfma_kernel<T, VecW, Gelu>), dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s,
                      a, (int32_t)row_blocks, col_blocks);
   return check_launch("fmdq_linear (mfma)");
 }
 
 template <int T>
 int launch_t(const LinearArgs& a, hipStream_t s) {
-  return (a.N % 16) == 0 ? launch_tv<T, true>(a, s) : launch_tv<T, false>(a, s);
+  if (a.gelu_out != nullptr)
+    return (a.N % 16) == 0 ? launch_tv<T, true, true>(a, s) : launch_tv<T, false, true>(a, s);
+  return (a.N % 16) == 0 ? launch_tv<T, true, false>(a, s) : launch_tv<T, false, false>(a, s);
 }
 
 }  // namespace

@@ -71,7 +71,9 @@ __global__ __launch_bounds__(kThreads) void linear_general_kernel(LinearArgs a, 
       if (t < nrows) {
         const int64_t idx = (r0 + t) * N + n;
         const double d = __dmul_rn(__dmul_rn((double)s[t], base), ws);
-        a.y_out[idx] = (float)__dadd_rn((double)a.y_prev[idx], d);
+        const float y = (float)__dadd_rn((double)a.y_prev[idx], d);
+        a.y_out[idx] = y;
+        if (a.gelu_out != nullptr) a.gelu_out[idx] = gelu_of(y);
       }
     }
   }

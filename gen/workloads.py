@@ -158,3 +158,32 @@ def make_custom(rows: int, K: int, N: int, token_tile: int, seed: int,
                 base=base, k0=k0, token_tile=token_tile, rows=rows,
                 tokens_per_seq=rows if tokens_per_seq is None else tokens_per_seq,
                 K=K, N=N, name=f"custom-{rows}x{K}x{N}-T{token_tile}-s{seed}")
+
+
+def make_walk(cfg: int, layer: str, pairs: int) -> list:
+    """X_0, X_1, ..., X_pairs of the random walk of one layer of workload
+    ``cfg``, drawn once (make_inputs(cfg, layer, p) has X_{p-1} and X_p)."""
+    spec = CONFIGS[cfg]
+    names = list(spec["layers"])
+    li = names.index(layer)
+    K, _ = spec["layers"][layer]
+    full_rows = spec["rows"]
+    lo, hi = spec["c_range"]
+    c = np.exp(rng(cfg, li, 0, S_C).uniform(np.log(lo), np.log(hi), size=K))
+    x = (rng(cfg, li, 0, S_X0).standard_normal((full_rows, K)) * c[None, :]).astype(np.float32)
+    xs = [x]
+    for p in range(1, pairs + 1):
+        x = (x.astype(np.float64) + _delta(spec, cfg, li, p, full_rows, K, c)).astype(np.float32)
+        xs.append(x)
+    return xs
+
+
+def profiled_base(delta: np.ndarray) -> np.float32:
+    """A static base "profiled" from one observed difference, by the same rule
+    as the workloads' own base: half the median over channels of the
+    per-channel RMS of Δ (the workloads draw Δ with RMS σ = 0.03·c_k and use
+    0.03·median(c)/2).  For layers whose input is produced by another layer
+    (the second linear of an MLP), where no c_k is drawn."""
+    d = np.asarray(delta, dtype=np.float64)
+    rms = np.sqrt(np.mean(d * d, axis=0))
+    return np.float32(float(np.median(rms)) / 2.0)

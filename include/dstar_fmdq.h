@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define DSTAR_FMDQ_ABI_VERSION 6
+#define DSTAR_FMDQ_ABI_VERSION 7
 
 /* Rule constants (DSTAR §3.1 step 1; readings in the design notes):
  * PCeil of a b-bit sub-channel is 2^(b-2); PoT is capped at POT_MAX so that
@@ -177,6 +177,32 @@ int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N,
                       const float* w_scale,
                       const float* y_prev, float* y_out, int32_t* acc_dbg,
                       int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream);
+
+/* Stage 3 with the MLP activation fused into its epilogue (DSTAR §4.3
+ * "Linear Operation": the GELU that follows the first linear of a DiT MLP is
+ * applied by the vector unit as the output is produced; §4.2 "Design of
+ * VPU").  Arguments and results as for dstar_fmdq_linear (without the
+ * accumulator dump), plus
+ *   gelu_out  [rows][N] float32 (out), 16-byte aligned, not aliasing y_prev or
+ *             y_out: GELU(Y_t) for every output written to y_out, in the tanh
+ *             form y / (1 + exp(-2u)), u = 0.7978845608028654 * (y + 0.044715 *
+ *             (y*y)*y), evaluated in float64 and rounded once to float32 (the
+ *             pages give no formula; their unit uses piecewise cubics).
+ * In a chain of timesteps gelu_out is the second linear's X_t, and the
+ * previous step's gelu_out its X_{t-1}. */
+int dstar_fmdq_linear_gelu(const dstar_fmdq_params* p, int32_t N,
+                           const int8_t* codes, const uint16_t* perm,
+                           const int32_t* group_off, const int8_t* acodes,
+                           const int8_t* hcodes, const int8_t* w,
+                           const int8_t* w_t, const float* w_scale,
+                           const float* y_prev, float* y_out, float* gelu_out,
+                           void* stream);
+
+/* Elementwise GELU, the same function as dstar_fmdq_linear_gelu's:
+ * g[i] = GELU(y[i]) for i < n (n >= 0).  y and g are 16-byte aligned device
+ * arrays; g may equal y.  For the GELU of a cached output, e.g. the second
+ * linear's X_{t-1} when a chain of timesteps starts. */
+int dstar_fmdq_gelu(const float* y, float* g, int64_t n, void* stream);
 
 /* Dynamic base, pass 1 of the variant that takes the base from the data
  * (DSTAR §3.1 step 1 defines the base of Eq. 2-3 as the smallest sub-channel

@@ -129,6 +129,17 @@ def test_null_and_alignment_errors(lib):
     assert _l(lib, p, dbg=FAKE, lo=1, hi=1) == lib.EINVAL
     assert _l(lib, p, dbg=FAKE, lo=0, hi=3) == lib.EINVAL    # 64 rows / 32 = 2 tiles
     assert "debug tile range" in L.dstar_fmdq_last_error().decode()
+    # fused GELU and the stand-alone GELU
+    lg = lambda go, y0=FAKE, y1=FAKE: L.dstar_fmdq_linear_gelu(ctypes.byref(p), 64, FAKE, FAKE, FAKE, None, None,
+                                                               FAKE, None, FAKE, y0, y1, go, 0)
+    assert lg(None) == lib.ENULL
+    assert lg(FAKE + 4) == lib.EALIGN
+    assert lg(FAKE + 0x1000, y1=FAKE + 0x1000) == lib.EINVAL      # gelu_out aliases y_out
+    assert lg(FAKE + 0x1000, y0=FAKE + 0x1000) == lib.EINVAL      # ... or y_prev
+    assert L.dstar_fmdq_gelu(FAKE, FAKE, -1, 0) == lib.EINVAL
+    assert L.dstar_fmdq_gelu(None, FAKE, 8, 0) == lib.ENULL
+    assert L.dstar_fmdq_gelu(FAKE + 4, FAKE, 8, 0) == lib.EALIGN
+    assert L.dstar_fmdq_gelu(None, None, 0, 0) == lib.OK           # empty: no launch
     # dynamic base and the _dyn stages
     assert L.dstar_fmdq_dynamic_base(ctypes.byref(p), FAKE, FAKE, None, 0) == lib.ENULL
     assert L.dstar_fmdq_dynamic_base(ctypes.byref(p), None, FAKE, FAKE, 0) == lib.ENULL

@@ -440,3 +440,96 @@ def test_dynamic_base_full_size(dm, cfg, layer):
     rows_s = np.concatenate([np.arange(tau * T, min(rows, tau * T + T)) for tau in sample])
     check_y(g["y"][rows_s], y[rows_s], d["y_prev"][rows_s], d["name"] + " dyn")
     log(f"  done {time.time() - t0:.1f}s")
+
+
+# ------------------------------------------------------------------- GELU / MLP
+def ulp_distance(a, b):
+    """|a - b| in float32 ulps (both arrays float32; signed zeros are equal)."""
+    def ordered(x):
+        i = np.asarray(x, dtype=np.float32).view(np.int32).astype(np.int64)
+        return np.where(i < 0, -(i & 0x7FFFFFFF), i)
+    return np.abs(ordered(a) - ordered(b))
+
+
+def check_gelu(g_gpu, y, what):
+    """GELU is evaluated in float64 on both sides (exp from different
+    libraries, each within an ulp of float64) and rounded once to float32, so
+    the outputs may differ only where the float64 values straddle a float32
+    rounding boundary: by one ulp, rarely."""
+    d = ulp_distance(g_gpu, fmdq.gelu(y))
+    log(f"  {what}: GELU max {int(d.max())} ulp, identical {int((d == 0).sum())}/{d.size}")
+    assert d.max() <= 1, f"{what}: GELU differs by {int(d.max())} ulp"
+
+
+def test_gelu_kernel(dm):
+    import torch
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(61)
+    special = np.float32([0.0, -0.0, 1e-30, -1e-30, 1e-45, 30.0, -30.0, 1e30, -1e30, -3.0, -5.0, -10.0,
+                          -15.0, -20.0, -40.0, 3.4e38, -3.4e38])
+    y = np.concatenate([(rng.standard_normal(100003) * 4).astype(np.float32), special])
+    g = torch.full((y.size,), float("nan"), dtype=torch.float32, device=dev)
+    dm.gelu(torch.from_numpy(y).to(dev), g)
+    torch.cuda.synchronize()
+    check_gelu(g.cpu().numpy(), y, "gelu kernel")
+
+
+@pytest.mark.parametrize("case", [SMALL[0], SMALL[2], SMALL[3], SMALL[5], SMALL[8], SMALL[14]],
+                         ids=lambda c: f"{c['rows']}x{c['K']}x{c['N']}-T{c['T']}-s{c['seed']}")
+def test_linear_gelu_matches_oracle(dm, case):
+    """Stage 3 with the fused GELU: Y_t bit for bit, GELU(Y_t) within an ulp."""
+    import torch
+    dev = torch.device("cuda:0")
+    c = dict(case)
+    d = wl.make_custom(c.pop("rows"), c.pop("K"), c.pop("N"), c.pop("T"), seed=c.pop("seed"), **c)
+    rows, K, N, T = d["rows"], d["K"], d["N"], d["token_tile"]
+    log(f"case {d['name']} (fused GELU)")
+    w = torch.from_numpy(d["w"]).to(dev)
+    lay = dm.FmdqLayer(w, torch.from_numpy(d["w_scale"]).to(dev), rows, T, float(d["base"]), d["k0"],
+                       d["tokens_per_seq"])
+    y = torch.from_numpy(d["y_prev"]).to(dev)
+    g = torch.full((rows, N), float("nan"), dtype=torch.float32, device=dev)
+    lay.step(torch.from_numpy(d["x_t"]).to(dev), torch.from_numpy(d["x_prev"]).to(dev), y, gelu_out=g)
+    torch.cuda.synchronize()
+    r = fmdq.layer(d["x_t"], d["x_prev"], d["w"], d["w_scale"], d["y_prev"], d["base"], T, d["k0"])
+    check_y(y.cpu().numpy(), r["y"], d["y_prev"], d["name"])
+    check_gelu(g.cpu().numpy(), r["y"], d["name"])
+
+
+def test_mlp_chain_matches_oracle(dm):
+    """Three timestep pairs through fc1 (fused GELU) → fc2 of the PixArt-alpha
+    MLP at 256 rows: Y1 and Y2 bit for bit, G within an ulp.  The oracle's
+    second linear takes the GPU's G (an ulp apart at most), so its integer
+    decisions are made on the same inputs."""
+    import torch
+    dev = torch.device("cuda:0")
+    R, T = 256, 32
+    d1 = [wl.make_inputs(1, "fc1", p, rows=R) for p in (1, 2, 3)]
+    d2 = wl.make_inputs(1, "fc2", 1, rows=R)
+    k0 = d1[0]["k0"]
+    y1_0, y2_0 = d1[0]["y_prev"], d2["y_prev"]
+    # static base of the second linear, profiled on the first step (oracle)
+    g0 = fmdq.gelu(y1_0)
+    y1_1 = fmdq.layer(d1[0]["x_t"], d1[0]["x_prev"], d1[0]["w"], d1[0]["w_scale"], y1_0, d1[0]["base"],
+                      T, k0)["y"]
+    base2 = wl.profiled_base(fmdq.gelu(y1_1).astype(np.float64) - g0.astype(np.float64))
+    log(f"MLP chain: fc2 base {float(base2)!r}")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    mlp = dm.FmdqMLP(t(d1[0]["w"]), t(d1[0]["w_scale"]), float(d1[0]["base"]), t(d2["w"]),
+                     t(d2["w_scale"]), float(base2), R, T, k0, tokens_per_seq=R)
+    mlp.start(t(y1_0), t(y2_0))
+    torch.cuda.synchronize()
+    g_prev = mlp.g_cur.cpu().numpy().copy()
+    check_gelu(g_prev, y1_0, "start")
+    y1o, y2o = y1_0, y2_0
+    for s, d in enumerate(d1):
+        mlp.step(t(d["x_t"]), t(d["x_prev"]))
+        torch.cuda.synchronize()
+        y1g, gg, y2g = mlp.y1.cpu().numpy(), mlp.g_cur.cpu().numpy().copy(), mlp.y2.cpu().numpy()
+        r1 = fmdq.layer(d["x_t"], d["x_prev"], d["w"], d["w_scale"], y1o, d["base"], T, k0)
+        check_y(y1g, r1["y"], y1o, f"step {s + 1} fc1")
+        check_gelu(gg, r1["y"], f"step {s + 1}")
+        r2 = fmdq.layer(gg, g_prev, d2["w"], d2["w_scale"], y2o, base2, T, k0)
+        check_y(y2g, r2["y"], y2o, f"step {s + 1} fc2")
+        log(f"  step {s + 1}: bits fc1 {r1['hist'].tolist()} fc2 {r2['hist'].tolist()}")
+        y1o, y2o, g_prev = r1["y"], r2["y"], gg
