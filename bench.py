@@ -48,7 +48,7 @@ STAGES = ("quantize", "bucket", "linear")
 KERNEL_SRC = {"quantize": ["fmdq_quantize.hip"], "bucket": ["fmdq_bucket.hip"],
               "linear": ["fmdq_linear.hip", "fmdq_linear_mfma.hip"]}
 # device kernel name of each stage (as rocprofv3 reports it)
-KERNEL_NAME = {"quantize": "quantize_kernel", "bucket": "bucket_kernel", "linear": "linear_mfma_kernel"}
+KERNEL_NAME = {"quantize": "quantize_kernel", "bucket": "bucket_", "linear": "linear_mfma_kernel"}
 CAL_BYTES = 256 << 20     # the calibration copy
 TRAFFIC_MD = os.path.join(ROOT, "profiles", "stage_traffic_pixart1024.md")
 
@@ -505,7 +505,7 @@ def main() -> int:
         kgroups = 256 // (T // 16)
         cpt = 4 if K % 4 == 0 else 2 if K % 2 == 0 else 1
         q_work = nt * ((K + kgroups * cpt - 1) // (kgroups * cpt))
-        grids[L] = {"quantize": 256 * min(q_work, 8192), "bucket": 256 * min(nt, 2048),
+        grids[L] = {"quantize": 256 * min(q_work, 8192), "bucket": (1024 if K <= 16384 else 256) * min(nt, 2048),
                     "linear": 256 * ((nt + 128 // T - 1) // (128 // T)) * ((N + 255) // 256)}
     kernels = {}
     layer_out = {}
