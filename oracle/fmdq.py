@@ -424,6 +424,75 @@ def linear(codes: np.ndarray, tags: np.ndarray, perm: np.ndarray,
     return y
 
 
+#: 2-bit slices (DSTAR §3.1 ❷): slice n of a code sits at FPoT − 2n, i.e.
+#: slice tag tag − 2n in [−6, 15]; bin = slice tag + SLICE_TAG_OFF.
+SLICE_TAG_OFF = 6
+SLICE_BINS = 22
+
+
+def code_slices(q: np.ndarray, bits: np.ndarray):
+    """The 2-bit slices of b-bit codes (DSTAR §3.1 ❷: a code is the sum of its
+    slices shifted by 2n), least significant first, b/2 of them.
+
+    Reading for signed codes (the page's example is unsigned): the radix-4
+    digits of the two's-complement code — slices below the top one in 0..3,
+    the top slice in −2..1 — so q = Σ_n slice_n · 4^n exactly and every slice
+    is the 2-bit field (q >> 2n) & 3 (the top one read as signed).
+    Returns a list of b_max/2 int64 arrays (zero above a code's own count).
+    """
+    q = np.asarray(q, dtype=np.int64)
+    nsl = np.asarray(bits, dtype=np.int64) // 2
+    out = []
+    for n in range(4):
+        field = (q >> (2 * n)) & 3
+        top = (n == nsl - 1)
+        val = np.where(top & (field >= 2), field - 4, field)
+        out.append(np.where(n < nsl, val, 0))
+    return out
+
+
+def slice_encode(codes: np.ndarray, tags: np.ndarray):
+    """Steps ❷ ❸ ❹ of DSTAR §3.1 as a stream per token tile.
+
+    Every b-bit sub-channel becomes b/2 entries (channel k, slice n), the
+    slice at slice tag tag − 2n (its FPoT lowered by 2n).  The entries of a
+    tile are ordered by slice tag ascending (ascending FPoT), ties by channel
+    ascending, and each carries the number of left shifts to apply to the
+    running partial sum before it — the slice-tag difference to the previous
+    entry (0 for the first), the encoding of ❹.  Returns
+      ent   uint32 [n_t][4K]   k | n << 16 | shift << 24 (entries past the
+                               tile's count are 0xFFFFFFFF)
+      data  uint8  [n_t][4K][T/4]  the slice's 2-bit fields of rows t, four
+                               rows per byte (row t at bits 2·(t mod 4))
+      off   int32  [n_t][23]   off[τ][β] = entries of tile τ with bin < β
+    """
+    codes = np.asarray(codes)
+    nt, K, T = codes.shape
+    tag = tag_of(tags)
+    bits = bits_of(tags)
+    ent = np.full((nt, 4 * K), 0xFFFFFFFF, dtype=np.uint32)
+    data = np.zeros((nt, 4 * K, T // 4), dtype=np.uint8)
+    off = np.zeros((nt, SLICE_BINS + 1), dtype=np.int32)
+    for tau in range(nt):
+        items = []                     # (bin, k, n)
+        for k in range(K):
+            for n in range(int(bits[tau, k]) // 2):
+                items.append((int(tag[tau, k]) - 2 * n + SLICE_TAG_OFF, k, n))
+        items.sort()
+        slices = code_slices(codes[tau].astype(np.int64), bits[tau][:, None])
+        prev = None
+        for j, (b, k, n) in enumerate(items):
+            shift = 0 if prev is None else b - prev
+            prev = b
+            ent[tau, j] = k | (n << 16) | (shift << 24)
+            field = slices[n][k] & 3                      # the 2-bit pattern
+            packed = field.reshape(T // 4, 4) << (2 * np.arange(4))
+            data[tau, j] = packed.sum(axis=1).astype(np.uint8)
+        for beta in range(SLICE_BINS + 1):
+            off[tau, beta] = sum(1 for it in items if it[0] < beta)
+    return ent, data, off
+
+
 #: Constants of the tanh form of GELU: sqrt(2/pi) and the cubic coefficient.
 GELU_C = 0.7978845608028654
 GELU_A = 0.044715
