@@ -16,11 +16,11 @@ from __future__ import annotations
 from . import _binding
 from ._binding import (FmdqError, Params, bucket, dynamic_base, gelu, linear,  # noqa: F401
                        linear_dyn, linear_gelu, load, make_params, pack_weights, quantize,
-                       quantize_dyn)
+                       quantize_dyn, slice_encode)
 
 __all__ = ["FmdqError", "Params", "FmdqLayer", "FmdqMLP", "bucket", "dynamic_base", "gelu", "linear",
            "linear_dyn", "linear_gelu", "load", "make_params", "pack_weights", "quantize",
-           "quantize_dyn", "n_tiles"]
+           "quantize_dyn", "slice_encode", "n_tiles"]
 
 
 def n_tiles(rows: int, token_tile: int) -> int:

@@ -20,9 +20,9 @@ TAG_OFFSET = 15
 POT_MAX = 21
 PREC_SHIFT = 4
 MAX_K = 65535
-ABI_VERSION = 7
+ABI_VERSION = 8
 
-SYMBOLS = ("dstar_fmdq_quantize", "dstar_fmdq_bucket", "dstar_fmdq_pack_weights",
+SYMBOLS = ("dstar_fmdq_quantize", "dstar_fmdq_bucket", "dstar_fmdq_slice_encode", "dstar_fmdq_pack_weights",
            "dstar_fmdq_linear", "dstar_fmdq_linear_gelu", "dstar_fmdq_gelu",
            "dstar_fmdq_dynamic_base", "dstar_fmdq_quantize_dyn",
            "dstar_fmdq_linear_dyn", "dstar_fmdq_last_error", "dstar_fmdq_abi_version")
@@ -61,6 +61,8 @@ def load() -> ctypes.CDLL:
     lib.dstar_fmdq_quantize.restype = ctypes.c_int
     lib.dstar_fmdq_bucket.argtypes = [P, vp, vp, vp, vp]
     lib.dstar_fmdq_bucket.restype = ctypes.c_int
+    lib.dstar_fmdq_slice_encode.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.dstar_fmdq_slice_encode.restype = ctypes.c_int
     lib.dstar_fmdq_pack_weights.argtypes = [i32, i32, vp, vp, vp]
     lib.dstar_fmdq_pack_weights.restype = ctypes.c_int
     lib.dstar_fmdq_linear.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
@@ -180,3 +182,9 @@ def linear_gelu(p: Params, N: int, codes, perm, group_off, acodes, hcodes, w, w_
 def gelu(y, g, n: int | None = None, stream=None) -> None:
     """dstar_fmdq_gelu: g = GELU(y) elementwise (n defaults to y.numel())."""
     _check(load().dstar_fmdq_gelu(_ptr(y), _ptr(g), int(y.numel() if n is None else n), _stream(stream)))
+
+
+def slice_encode(p: Params, codes, tags, entries, slices, slice_off, stream=None) -> None:
+    """dstar_fmdq_slice_encode: the 2-bit slice stream of every token tile."""
+    _check(load().dstar_fmdq_slice_encode(ctypes.byref(p), _ptr(codes), _ptr(tags), _ptr(entries),
+                                          _ptr(slices), _ptr(slice_off), _stream(stream)))

@@ -179,6 +179,30 @@ int dstar_fmdq_bucket(const dstar_fmdq_params* p, const uint8_t* tags, uint16_t*
   return launch_bucket(a, (hipStream_t)stream);
 }
 
+int dstar_fmdq_slice_encode(const dstar_fmdq_params* p, const int8_t* codes, const uint8_t* tags,
+                            uint32_t* entries, uint8_t* slices, int32_t* slice_off, void* stream) {
+  clear_error();
+  int64_t nt = 0;
+  if (int rc = check_params(p, &nt)) return rc;
+  if (p->K > DSTAR_FMDQ_SLICE_MAX_K)
+    return set_error(DSTAR_EUNSUPPORTED, "slice_encode: K = %d above %d", p->K, DSTAR_FMDQ_SLICE_MAX_K);
+  if (nt == 0) return DSTAR_OK;
+  if (!codes || !tags || !entries || !slices || !slice_off)
+    return set_error(DSTAR_ENULL, "slice_encode: codes, tags, entries, slices and slice_off must not be NULL");
+  if (!aligned(codes, 16) || !aligned(entries, 4) || !aligned(slice_off, 4))
+    return set_error(DSTAR_EALIGN, "slice_encode: codes must be 16-byte aligned, entries and slice_off 4-byte");
+  SliceArgs a;
+  a.codes = codes;
+  a.tags = tags;
+  a.entries = entries;
+  a.slices = slices;
+  a.slice_off = slice_off;
+  a.n_tiles = nt;
+  a.K = p->K;
+  a.T = p->token_tile;
+  return launch_slices(a, (hipStream_t)stream);
+}
+
 int dstar_fmdq_pack_weights(int32_t K, int32_t N, const int8_t* w, int8_t* w_t, void* stream) {
   clear_error();
   if (K < 1 || K > DSTAR_FMDQ_MAX_K)

@@ -45,6 +45,17 @@ struct BucketArgs {
   int32_t K;
 };
 int launch_bucket(const BucketArgs& a, hipStream_t s);
+struct SliceArgs {
+  const int8_t* codes;
+  const uint8_t* tags;
+  uint32_t* entries;
+  uint8_t* slices;
+  int32_t* slice_off;
+  int64_t n_tiles;
+  int32_t K;
+  int32_t T;
+};
+int launch_slices(const SliceArgs& a, hipStream_t s);
 
 struct LinearArgs {
   const int8_t* codes;

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define DSTAR_FMDQ_ABI_VERSION 7
+#define DSTAR_FMDQ_ABI_VERSION 8
 
 /* Rule constants (DSTAR §3.1 step 1; readings in the design notes):
  * PCeil of a b-bit sub-channel is 2^(b-2); PoT is capped at POT_MAX so that
@@ -51,6 +51,9 @@ extern "C" {
 #define DSTAR_FMDQ_POT_MAX 21
 #define DSTAR_FMDQ_PREC_SHIFT 4
 #define DSTAR_FMDQ_MAX_K 65535
+#define DSTAR_FMDQ_SLICE_BINS 22     /* slice tags -6..15 of the 2-bit stream */
+#define DSTAR_FMDQ_SLICE_TAG_OFFSET 6
+#define DSTAR_FMDQ_SLICE_MAX_K 16384
 
 /* Status codes. */
 #define DSTAR_OK 0
@@ -131,6 +134,31 @@ int dstar_fmdq_quantize(const dstar_fmdq_params* p, const float* x_t,
  *              perm[τ][group_off[τ][4g] .. group_off[τ][4g+4]). */
 int dstar_fmdq_bucket(const dstar_fmdq_params* p, const uint8_t* tags,
                       uint16_t* perm, int32_t* group_off, void* stream);
+
+/* The 2-bit slice stream of DSTAR's accelerator (§3.1 steps 2-4: sub-channel
+ * decomposition into 2-bit slices, reordering by FPoT, encoding of channel
+ * indices and shift counts; §4.2 QPU stages 3-4).  For inspection and for a
+ * 2-bit datapath: dstar_fmdq_linear does not read it.  K <= 16384.
+ *   codes, tags  from stage 1.
+ *   entries    [n_t][4K] uint32 (out), 4-byte aligned: the entries of tile τ,
+ *              channel k | slice n << 16 | shift << 24, ordered by bin =
+ *              tag - 2n + 6 (the slice's FPoT lowered by 2n) ascending, then
+ *              channel ascending; shift = bin - previous entry's bin (0 for
+ *              the first) = the left shift applied to the running partial sum
+ *              before adding this entry's product.  A b-bit sub-channel gives
+ *              b/2 entries (n = 0 .. b/2-1); entries past the tile's count are
+ *              0xFFFFFFFF.
+ *   slices     [n_t][4K][T/4] uint8 (out): entry j's 2-bit fields for rows t,
+ *              four rows per byte (row t at bits 2*(t mod 4)); field = (code >>
+ *              2n) & 3, i.e. the radix-4 digits of the two's-complement code,
+ *              the top one (n = b/2-1) read as signed (-2..1), the others
+ *              unsigned.  code = sum_n digit_n * 4^n.
+ *   slice_off  [n_t][23] int32 (out): entries of tile τ with bin < β.
+ * Decoding: acc <<= shift; acc += digits * W[k]; after the last entry
+ * S = acc * 2^(15 - (bin_last - 6)). */
+int dstar_fmdq_slice_encode(const dstar_fmdq_params* p, const int8_t* codes,
+                            const uint8_t* tags, uint32_t* entries,
+                            uint8_t* slices, int32_t* slice_off, void* stream);
 
 /* Weight preparation, once per layer: w_t[n][k] = w[k][n] (the [out][in]
  * layout of the weights), the operand of stage 3's dense GEMM.

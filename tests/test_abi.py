@@ -129,6 +129,13 @@ def test_null_and_alignment_errors(lib):
     assert _l(lib, p, dbg=FAKE, lo=1, hi=1) == lib.EINVAL
     assert _l(lib, p, dbg=FAKE, lo=0, hi=3) == lib.EINVAL    # 64 rows / 32 = 2 tiles
     assert "debug tile range" in L.dstar_fmdq_last_error().decode()
+    # 2-bit slice stream
+    se = lambda q, **kw: L.dstar_fmdq_slice_encode(ctypes.byref(q), kw.get("c", FAKE), FAKE, kw.get("e", FAKE),
+                                                   FAKE, kw.get("o", FAKE), 0)
+    assert se(p, c=None) == lib.ENULL
+    assert se(p, c=FAKE + 4) == lib.EALIGN
+    assert se(p, e=FAKE + 2) == lib.EALIGN
+    assert se(lib.make_params(64, 16385, 32, 0.05, 2)) == lib.EUNSUPPORTED
     # fused GELU and the stand-alone GELU
     lg = lambda go, y0=FAKE, y1=FAKE: L.dstar_fmdq_linear_gelu(ctypes.byref(p), 64, FAKE, FAKE, FAKE, None, None,
                                                                FAKE, None, FAKE, y0, y1, go, 0)

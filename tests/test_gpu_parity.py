@@ -533,3 +533,59 @@ def test_mlp_chain_matches_oracle(dm):
         check_y(y2g, r2["y"], y2o, f"step {s + 1} fc2")
         log(f"  step {s + 1}: bits fc1 {r1['hist'].tolist()} fc2 {r2['hist'].tolist()}")
         y1o, y2o, g_prev = r1["y"], r2["y"], gg
+
+
+# ------------------------------------------------------------- 2-bit slice stream
+SLICE_CASES = [
+    dict(rows=96, K=40, N=8, T=32, seed=71, heavy=0.2, c_range=(0.05, 500.0)),
+    dict(rows=70, K=33, N=8, T=32, seed=72, heavy=0.5, c_range=(0.05, 500.0)),    # ragged, odd K
+    dict(rows=128, K=64, N=8, T=64, seed=73, heavy=0.3),
+    dict(rows=40, K=17, N=8, T=16, seed=74, heavy=0.1),
+    dict(rows=64, K=2000, N=8, T=32, seed=75, heavy=1.0, c_range=(4.0, 8.0)),     # every channel 8-bit
+]
+
+
+def gpu_slices(dm, d):
+    import torch
+    dev = torch.device("cuda:0")
+    rows, K, T = d["rows"], d["K"], d["token_tile"]
+    nt = (rows + T - 1) // T
+    p = dm.make_params(rows, K, T, float(d["base"]), d["k0"], d["tokens_per_seq"])
+    codes = torch.full((nt, K, T), 90, dtype=torch.int8, device=dev)
+    tags = torch.full((nt, K), 0xEE, dtype=torch.uint8, device=dev)
+    dm.quantize(p, torch.from_numpy(d["x_t"]).to(dev), torch.from_numpy(d["x_prev"]).to(dev), codes, tags)
+    ent = torch.full((nt, 4 * K), 0x1234, dtype=torch.int32, device=dev)
+    sl = torch.full((nt, 4 * K, T // 4), 0xAB, dtype=torch.uint8, device=dev)
+    off = torch.full((nt, 23), -3, dtype=torch.int32, device=dev)
+    dm.slice_encode(p, codes, tags, ent, sl, off)
+    torch.cuda.synchronize()
+    return (codes.cpu().numpy(), tags.cpu().numpy(), ent.cpu().numpy().view(np.uint32), sl.cpu().numpy(),
+            off.cpu().numpy())
+
+
+@pytest.mark.parametrize("case", SLICE_CASES, ids=lambda c: f"{c['rows']}x{c['K']}-T{c['T']}-s{c['seed']}")
+def test_slice_stream_matches_oracle(dm, case):
+    c = dict(case)
+    d = wl.make_custom(c.pop("rows"), c.pop("K"), c.pop("N"), c.pop("T"), seed=c.pop("seed"), **c)
+    log(f"case {d['name']} (slice stream)")
+    codes, tags, ent, sl, off = gpu_slices(dm, d)
+    e_o, s_o, off_o = fmdq.slice_encode(codes, tags)
+    np.testing.assert_array_equal(off, off_o, err_msg="slice offsets")
+    np.testing.assert_array_equal(ent, e_o, err_msg="entries")
+    for tau in range(codes.shape[0]):
+        E = int(off_o[tau, -1])
+        np.testing.assert_array_equal(sl[tau, :E], s_o[tau, :E], err_msg=f"slices of tile {tau}")
+    log(f"  entries per tile {off_o[:, -1].tolist()[:8]} ...: identical")
+
+
+def test_slice_stream_full_workload_rows(dm):
+    """The PixArt-alpha fc1 input at 256 rows (8 token tiles, K = 1152)."""
+    d = wl.make_inputs(1, "fc1", 1, rows=256)
+    codes, tags, ent, sl, off = gpu_slices(dm, d)
+    e_o, s_o, off_o = fmdq.slice_encode(codes, tags)
+    np.testing.assert_array_equal(off, off_o)
+    np.testing.assert_array_equal(ent, e_o)
+    for tau in range(codes.shape[0]):
+        E = int(off_o[tau, -1])
+        np.testing.assert_array_equal(sl[tau, :E], s_o[tau, :E])
+    log(f"  slice stream of {codes.shape[0]} tiles identical; entries per tile {off_o[:, -1].tolist()}")
