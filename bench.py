@@ -22,8 +22,8 @@ Traffic summary from two counter runs of this same command (run from the
 repository root; a plain 256 MiB device copy made before timing calibrates
 the counters):
 
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain
-    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices
     python bench.py --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write
 """
 from __future__ import annotations
@@ -125,13 +125,13 @@ def write_traffic(fetch_dir: str, write_dir: str) -> None:
     lines = ["# HBM traffic per launch, FMDQ differential linear, PixArt-alpha-style 1024px MLP",
              "",
              "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, rocprofv3 --pmc, one run each) of",
-             "`python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain` on one MI355X, scaled by what they read",
+             "`python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices` on one MI355X, scaled by what they read",
              f"for a plain {CAL_BYTES >> 20} MiB device copy made in the same run (fetch x{sf:.4f}, write x{sw:.4f}).",
              "Commands:",
              "",
              "```",
-             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain",
-             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain",
+             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices",
+             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices",
              "python bench.py --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write",
              "```",
              "",
@@ -196,7 +196,7 @@ def write_kernel_summary(trace_dir: str) -> None:
              "",
              "```",
              "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_bench -o run -- \\",
-             "    python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline --no-dynamic --no-chain",
+             "    python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline --no-dynamic --no-chain --no-slices",
              "python bench.py --write-kernel-summary gpurun_out/prof_bench",
              "```",
              "",
@@ -225,6 +225,33 @@ def write_kernel_summary(trace_dir: str) -> None:
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def slice_stream(dm, torch, state, layers, rows, T, stream) -> dict:
+    """The 2-bit slice stream (DSTAR §3.1 steps 2-4) of each layer's latest
+    codes, timed with HIP events (it is not part of the step: the MFMA path
+    multiplies whole codes)."""
+    out = {}
+    nt = (rows + T - 1) // T
+    for L in layers:
+        lay = state[L]["layer"]
+        K = state[L]["K"]
+        ent = torch.empty((nt, 4 * K), dtype=torch.int32, device=lay.codes.device)
+        sl = torch.empty((nt, 4 * K, T // 4), dtype=torch.uint8, device=lay.codes.device)
+        off = torch.empty((nt, 23), dtype=torch.int32, device=lay.codes.device)
+        for _ in range(3):
+            dm.slice_encode(lay.p, lay.codes, lay.tags, ent, sl, off)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(10):
+            dm.slice_encode(lay.p, lay.codes, lay.tags, ent, sl, off)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        us = ev[0].elapsed_time(ev[1]) * 1e3 / 10
+        E = off[:, -1].double()
+        moved = nt * K * (1 + T) + float(E.sum()) * (4 + T // 4) + nt * 23 * 4
+        out[L] = {"us": us, "entries_per_tile": float(E.mean()), "gbs": moved / (us * 1e-6) / 1e9}
+    return out
 
 
 def mlp_chain(dm, torch, cfg, spec, stream) -> dict:
@@ -377,6 +404,7 @@ def main() -> int:
     ap.add_argument("--eager", action="store_true", help="launch kernel by kernel instead of graph replays")
     ap.add_argument("--no-dynamic", action="store_true", help="skip the dynamic-base comparison")
     ap.add_argument("--no-chain", action="store_true", help="skip the fc1 -> GELU -> fc2 timestep chain")
+    ap.add_argument("--no-slices", action="store_true", help="skip timing the 2-bit slice stream")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--write-kernel-summary", metavar="TRACE_DIR")
     args = ap.parse_args()
@@ -557,6 +585,9 @@ def main() -> int:
                    "pairs_cycled": args.pairs},
         "layers": layer_out, "kernels": kernels, "roofline": roof,
     }
+    if not args.no_slices:
+        print("[bench] 2-bit slice stream", file=sys.stderr, flush=True)
+        out["slice_stream"] = slice_stream(dm, torch, state, layers, rows, T, stream)
     if not args.no_chain and set(layers) >= {"fc1", "fc2"}:
         print("[bench] fc1 -> GELU -> fc2 chain", file=sys.stderr, flush=True)
         out["mlp_chain"] = mlp_chain(dm, torch, cfg, spec, stream)
