@@ -10,17 +10,24 @@ the MLP's GELU into stage 3 and ``gelu`` is the same activation on its own.
 This package is the thin Python binding; ``FmdqLayer`` allocates the buffers of
 one layer with torch and calls the stages on the current stream, and
 ``FmdqMLP`` chains two of them (fc1 → GELU → fc2) over timesteps.
+
+``SarAttention`` is Sparse Attention Reuse with FMDQ-INT8 operands (DSTAR
+§3.2, §4.3; include/dstar_sar.h): a cached step that quantizes Q, K and V and
+stores the block-sparse attention weights, and reused steps that apply them to
+the current V.
 """
 from __future__ import annotations
 
 from . import _binding
 from ._binding import (FmdqError, Params, bucket, dynamic_base, gelu, linear,  # noqa: F401
                        linear_dyn, linear_gelu, load, make_params, pack_weights, quantize,
-                       quantize_dyn, slice_encode)
+                       quantize_dyn, slice_encode, sar_padded_dim, sar_pv, sar_quantize_k,
+                       sar_quantize_q, sar_quantize_v, sar_scores)
 
 __all__ = ["FmdqError", "Params", "FmdqLayer", "FmdqMLP", "bucket", "dynamic_base", "gelu", "linear",
            "linear_dyn", "linear_gelu", "load", "make_params", "pack_weights", "quantize",
-           "quantize_dyn", "slice_encode", "n_tiles"]
+           "quantize_dyn", "slice_encode", "n_tiles", "SarAttention", "sar_padded_dim", "sar_pv",
+           "sar_quantize_k", "sar_quantize_q", "sar_quantize_v", "sar_scores"]
 
 
 def n_tiles(rows: int, token_tile: int) -> int:
@@ -121,3 +128,68 @@ class FmdqMLP:
         self.fc2.step(self.g[nxt], self.g[self.cur], self.y2, stream=stream, hist=hist)
         self.cur = nxt
         return self.y2
+
+
+class SarAttention:
+    """One attention layer under Sparse Attention Reuse with FMDQ-INT8 operands
+    (DSTAR §3.2 Fig. 8, §4.3 Fig. 13).
+
+    ``mask`` is the static block mask, bool [heads][L/64][L/64] (numpy or
+    torch); it is turned into compressed rows once, here.  Every buffer of the
+    layer (codes, scales, the P cache, the output) is allocated once on
+    ``device``.  ``cached_step(q, k, v)`` quantizes the three operands, fills the
+    cache and returns O; ``reused_step(v)`` quantizes the current V and returns
+    O = P_cache V.  q, k, v: float32 [batch·heads][L][d] on the device.
+    """
+
+    def __init__(self, mask, batch: int, heads: int, tokens: int, head_dim: int, base_q: float,
+                 base_p: float, sm_scale: float, device="cuda"):
+        import numpy as np
+        import torch
+
+        m = mask.cpu().numpy() if hasattr(mask, "cpu") else np.asarray(mask)
+        nb = tokens // _binding.SAR_BLOCK
+        if m.shape != (heads, nb, nb):
+            raise ValueError(f"mask shape {m.shape} != {(heads, nb, nb)}")
+        rows = m.astype(bool).reshape(heads * nb, nb)
+        row_ptr = np.zeros(heads * nb + 1, dtype=np.int32)
+        row_ptr[1:] = np.cumsum(rows.sum(axis=1))
+        cols = np.nonzero(rows)[1].astype(np.int32)
+        self.nnz = int(len(cols))
+        self.p = _binding.make_sar_params(batch, heads, tokens, head_dim, base_q, base_p, sm_scale)
+        dev = torch.device(device)
+        BH, L, d = batch * heads, tokens, head_dim
+        dp = sar_padded_dim(d)
+        self.row_ptr = torch.from_numpy(row_ptr).to(dev)
+        self.cols = torch.from_numpy(cols if len(cols) else np.zeros(1, np.int32)).to(dev)
+        self.qcodes = torch.empty((BH, L, dp), dtype=torch.int8, device=dev)
+        self.qpot = torch.empty((BH, L // _binding.SAR_TILE, dp), dtype=torch.uint8, device=dev)
+        self.kcodes = torch.empty((BH, L, dp), dtype=torch.int8, device=dev)
+        self.kscale = torch.empty((BH, L), dtype=torch.float32, device=dev)
+        self.vcodes_t = torch.empty((BH, dp, L), dtype=torch.int8, device=dev)
+        self.vscale = torch.empty((BH, d), dtype=torch.float32, device=dev)
+        blocks = max(self.nnz, 1)
+        self.pcodes = torch.empty((batch, blocks, 64, 64), dtype=torch.int8, device=dev)
+        self.ppot = torch.empty((batch, blocks, 2, 64), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((BH, L, d), dtype=torch.float32, device=dev)
+
+    def scores(self, q, k, stream=None):
+        """Quantizes Q and K and fills the P cache."""
+        sar_quantize_q(self.p, q, self.qcodes, self.qpot, stream)
+        sar_quantize_k(self.p, k, self.kcodes, self.kscale, stream)
+        sar_scores(self.p, self.row_ptr, self.cols, self.nnz, self.qcodes, self.qpot, self.kcodes,
+                   self.kscale, self.pcodes, self.ppot, stream)
+
+    def apply(self, v, stream=None):
+        """Quantizes V and computes O = P_cache V into self.out."""
+        sar_quantize_v(self.p, v, self.vcodes_t, self.vscale, stream)
+        sar_pv(self.p, self.row_ptr, self.cols, self.nnz, self.pcodes, self.ppot, self.vcodes_t,
+               self.vscale, self.out, stream)
+        return self.out
+
+    def cached_step(self, q, k, v, stream=None):
+        self.scores(q, k, stream)
+        return self.apply(v, stream)
+
+    def reused_step(self, v, stream=None):
+        return self.apply(v, stream)

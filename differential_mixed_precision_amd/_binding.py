@@ -1,4 +1,5 @@
-"""ctypes binding of libdstar_fmdq.so (the C ABI declared in include/dstar_fmdq.h).
+"""ctypes binding of libdstar_fmdq.so (the C ABI declared in include/dstar_fmdq.h
+and include/dstar_sar.h).
 
 Argument marshalling only: every step of the layer runs in the HIP kernels of
 the library.  Tensors are torch tensors on the GPU (their data_ptr() is passed
@@ -20,12 +21,20 @@ TAG_OFFSET = 15
 POT_MAX = 21
 PREC_SHIFT = 4
 MAX_K = 65535
-ABI_VERSION = 8
+ABI_VERSION = 9
+SAR_BLOCK = 64
+SAR_TILE = 32
+SAR_PAD = 32
+SAR_MAX_D = 128
+SAR_MAX_L = 65536
+SAR_EXP_FRAC = 36
 
 SYMBOLS = ("dstar_fmdq_quantize", "dstar_fmdq_bucket", "dstar_fmdq_slice_encode", "dstar_fmdq_pack_weights",
            "dstar_fmdq_linear", "dstar_fmdq_linear_gelu", "dstar_fmdq_gelu",
            "dstar_fmdq_dynamic_base", "dstar_fmdq_quantize_dyn",
            "dstar_fmdq_linear_dyn", "dstar_fmdq_last_error", "dstar_fmdq_abi_version")
+SAR_SYMBOLS = ("dstar_sar_quantize_q", "dstar_sar_quantize_k", "dstar_sar_quantize_v", "dstar_sar_scores",
+               "dstar_sar_pv")
 
 
 class FmdqError(RuntimeError):
@@ -39,6 +48,13 @@ class Params(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int32), ("tokens_per_seq", ctypes.c_int32),
                 ("K", ctypes.c_int32), ("token_tile", ctypes.c_int32),
                 ("base", ctypes.c_float), ("thr0_log2", ctypes.c_int32)]
+
+
+class SarParams(ctypes.Structure):
+    """dstar_sar_params."""
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("tokens", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("base_q", ctypes.c_float), ("base_p", ctypes.c_float),
+                ("sm_scale", ctypes.c_float)]
 
 
 _lib = None
@@ -78,6 +94,14 @@ def load() -> ctypes.CDLL:
     lib.dstar_fmdq_linear_dyn.argtypes = [P, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                           i32, vp]
     lib.dstar_fmdq_linear_dyn.restype = ctypes.c_int
+    S = ctypes.POINTER(SarParams)
+    lib.dstar_sar_quantize_q.argtypes = [S, vp, vp, vp, vp]
+    lib.dstar_sar_quantize_k.argtypes = [S, vp, vp, vp, vp]
+    lib.dstar_sar_quantize_v.argtypes = [S, vp, vp, vp, vp]
+    lib.dstar_sar_scores.argtypes = [S, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.dstar_sar_pv.argtypes = [S, vp, vp, i32, vp, vp, vp, vp, vp, vp]
+    for name in SAR_SYMBOLS:
+        getattr(lib, name).restype = ctypes.c_int
     lib.dstar_fmdq_last_error.argtypes = []
     lib.dstar_fmdq_last_error.restype = ctypes.c_char_p
     lib.dstar_fmdq_abi_version.argtypes = []
@@ -188,3 +212,45 @@ def slice_encode(p: Params, codes, tags, entries, slices, slice_off, stream=None
     """dstar_fmdq_slice_encode: the 2-bit slice stream of every token tile."""
     _check(load().dstar_fmdq_slice_encode(ctypes.byref(p), _ptr(codes), _ptr(tags), _ptr(entries),
                                           _ptr(slices), _ptr(slice_off), _stream(stream)))
+
+
+# ---------------------------------------------------------------- SAR attention
+
+def sar_padded_dim(d: int) -> int:
+    """dp = d rounded up to a multiple of SAR_PAD (the codes' row length)."""
+    return (int(d) + SAR_PAD - 1) // SAR_PAD * SAR_PAD
+
+
+def make_sar_params(batch: int, heads: int, tokens: int, head_dim: int, base_q: float, base_p: float,
+                    sm_scale: float) -> SarParams:
+    return SarParams(int(batch), int(heads), int(tokens), int(head_dim), float(base_q), float(base_p),
+                     float(sm_scale))
+
+
+def sar_quantize_q(p: SarParams, q, qcodes, qpot, stream=None) -> None:
+    """dstar_sar_quantize_q."""
+    _check(load().dstar_sar_quantize_q(ctypes.byref(p), _ptr(q), _ptr(qcodes), _ptr(qpot), _stream(stream)))
+
+
+def sar_quantize_k(p: SarParams, k, kcodes, kscale, stream=None) -> None:
+    """dstar_sar_quantize_k."""
+    _check(load().dstar_sar_quantize_k(ctypes.byref(p), _ptr(k), _ptr(kcodes), _ptr(kscale), _stream(stream)))
+
+
+def sar_quantize_v(p: SarParams, v, vcodes_t, vscale, stream=None) -> None:
+    """dstar_sar_quantize_v."""
+    _check(load().dstar_sar_quantize_v(ctypes.byref(p), _ptr(v), _ptr(vcodes_t), _ptr(vscale), _stream(stream)))
+
+
+def sar_scores(p: SarParams, row_ptr, cols, nnz: int, qcodes, qpot, kcodes, kscale, pcodes, ppot,
+               stream=None) -> None:
+    """dstar_sar_scores."""
+    _check(load().dstar_sar_scores(ctypes.byref(p), _ptr(row_ptr), _ptr(cols), int(nnz), _ptr(qcodes),
+                                   _ptr(qpot), _ptr(kcodes), _ptr(kscale), _ptr(pcodes), _ptr(ppot),
+                                   _stream(stream)))
+
+
+def sar_pv(p: SarParams, row_ptr, cols, nnz: int, pcodes, ppot, vcodes_t, vscale, out, stream=None) -> None:
+    """dstar_sar_pv."""
+    _check(load().dstar_sar_pv(ctypes.byref(p), _ptr(row_ptr), _ptr(cols), int(nnz), _ptr(pcodes), _ptr(ppot),
+                               _ptr(vcodes_t), _ptr(vscale), _ptr(out), _stream(stream)))

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define DSTAR_FMDQ_ABI_VERSION 8
+#define DSTAR_FMDQ_ABI_VERSION 9   /* also covers the entry points of dstar_sar.h */
 
 /* Rule constants (DSTAR §3.1 step 1; readings in the design notes):
  * PCeil of a b-bit sub-channel is 2^(b-2); PoT is capped at POT_MAX so that

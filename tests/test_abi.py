@@ -10,6 +10,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dstar_fmdq.h")
+SAR_HEADER = os.path.join(ROOT, "include", "dstar_sar.h")
 
 
 @pytest.fixture(scope="module")
@@ -178,3 +179,51 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(_binding, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         _binding.load()
+
+
+def test_library_exports_every_sar_entry_point(lib):
+    with open(SAR_HEADER) as f:
+        text = f.read()
+    declared = set(re.findall(r"^\s*int\s+(dstar_sar_\w+)\s*\(", text, re.M))
+    assert declared == set(lib.SAR_SYMBOLS)
+    raw = ctypes.CDLL(lib.LIB_PATH)
+    for name in declared:
+        assert hasattr(raw, name), name
+    consts = dict(re.findall(r"#define\s+(DSTAR_SAR_\w+)\s+(\d+)", text))
+    from oracle import sar
+    assert int(consts["DSTAR_SAR_BLOCK"]) == sar.SAR_BLOCK == lib.SAR_BLOCK
+    assert int(consts["DSTAR_SAR_TILE"]) == sar.SAR_TILE == lib.SAR_TILE
+    assert int(consts["DSTAR_SAR_EXP_FRAC"]) == sar.EXP_FRAC == lib.SAR_EXP_FRAC
+    assert int(consts["DSTAR_SAR_PAD"]) == lib.SAR_PAD
+    assert int(consts["DSTAR_SAR_MAX_D"]) == lib.SAR_MAX_D
+    assert int(consts["DSTAR_SAR_MAX_L"]) == lib.SAR_MAX_L
+    assert ctypes.sizeof(lib.SarParams) == 28
+
+
+def test_sar_rejects_invalid_arguments_on_the_host(lib):
+    """Argument checks run before any launch: bad shapes, bases, NULL and
+    misaligned pointers, and an impossible nnz."""
+    L = lib.load()
+    good = lib.make_sar_params(2, 3, 256, 72, 0.01, 2.0 ** -15, 0.125)
+    fake = 1 << 20                                  # aligned, never dereferenced on the host
+    cases = [
+        (lib.make_sar_params(0, 3, 256, 72, 0.01, 1.0, 0.1), lib.EINVAL),
+        (lib.make_sar_params(2, 3, 200, 72, 0.01, 1.0, 0.1), lib.EINVAL),
+        (lib.make_sar_params(2, 3, 256, 0, 0.01, 1.0, 0.1), lib.EINVAL),
+        (lib.make_sar_params(2, 3, 256, 129, 0.01, 1.0, 0.1), lib.EINVAL),
+        (lib.make_sar_params(2, 3, 256, 72, 0.0, 1.0, 0.1), lib.EINVAL),
+        (lib.make_sar_params(2, 3, 256, 72, 0.01, float("inf"), 0.1), lib.EINVAL),
+        (lib.make_sar_params(2, 3, 256, 72, 0.01, 1.0, -1.0), lib.EINVAL),
+    ]
+    for p, code in cases:
+        assert L.dstar_sar_quantize_q(ctypes.byref(p), fake, fake, fake, None) == code
+    assert L.dstar_sar_quantize_q(None, fake, fake, fake, None) == lib.ENULL
+    assert L.dstar_sar_quantize_q(ctypes.byref(good), None, fake, fake, None) == lib.ENULL
+    assert L.dstar_sar_quantize_k(ctypes.byref(good), fake, fake + 8, fake, None) == lib.EALIGN
+    assert L.dstar_sar_quantize_v(ctypes.byref(good), fake + 2, fake, fake, None) == lib.EALIGN
+    # nnz beyond heads·(L/64)^2 = 48
+    assert L.dstar_sar_scores(ctypes.byref(good), fake, fake, 49, fake, fake, fake, fake, fake, fake,
+                              None) == lib.EINVAL
+    assert L.dstar_sar_pv(ctypes.byref(good), fake, fake, -1, fake, fake, fake, fake, fake, None) == lib.EINVAL
+    assert L.dstar_sar_pv(ctypes.byref(good), None, fake, 4, fake, fake, fake, fake, fake, None) == lib.ENULL
+    assert "nnz" in L.dstar_fmdq_last_error().decode() or "row_ptr" in L.dstar_fmdq_last_error().decode()
