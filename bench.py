@@ -22,8 +22,8 @@ Traffic summary from two counter runs of this same command (run from the
 repository root; a plain 256 MiB device copy made before timing calibrates
 the counters):
 
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices
-    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention
     python bench.py --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write
 """
 from __future__ import annotations
@@ -125,13 +125,13 @@ def write_traffic(fetch_dir: str, write_dir: str) -> None:
     lines = ["# HBM traffic per launch, FMDQ differential linear, PixArt-alpha-style 1024px MLP",
              "",
              "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, rocprofv3 --pmc, one run each) of",
-             "`python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices` on one MI355X, scaled by what they read",
+             "`python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention` on one MI355X, scaled by what they read",
              f"for a plain {CAL_BYTES >> 20} MiB device copy made in the same run (fetch x{sf:.4f}, write x{sw:.4f}).",
              "Commands:",
              "",
              "```",
-             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices",
-             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices",
+             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention",
+             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention",
              "python bench.py --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write",
              "```",
              "",
@@ -196,7 +196,7 @@ def write_kernel_summary(trace_dir: str) -> None:
              "",
              "```",
              "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_bench -o run -- \\",
-             "    python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline --no-dynamic --no-chain --no-slices",
+             "    python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention",
              "python bench.py --write-kernel-summary gpurun_out/prof_bench",
              "```",
              "",
@@ -393,6 +393,81 @@ def dynamic_variant(dm, torch, state, layers, rows, args, stream, ms_static) -> 
     return out
 
 
+def sar_attention(dm, torch, stream, reps: int = 10) -> dict:
+    """Sparse Attention Reuse with FMDQ-INT8 operands (DSTAR §3.2 Fig. 8,
+    §4.3 Fig. 13) on the PixArt-alpha 1024px self-attention shape: 2 images x
+    16 heads, 4096 tokens, 72 channels, 37% of the 64 x 64 blocks pruned.  The
+    cached step runs every kernel (Q, K, V quantizers, scores to the P cache,
+    P.V); the reused step only quantizes V and runs P_cache.V.  HIP events on
+    the launch stream around each kernel, averaged over `reps` eager steps.
+    Algorithmic bytes count each array once; ops are one dense-equivalent
+    int8 product over the kept blocks (2 * 64 * 64 * d per block and image)."""
+    from gen import attention as ga
+    spec = ga.ATTN_CONFIGS["pixart-alpha-1024px-attn"]
+    d = ga.make_config("pixart-alpha-1024px-attn", seed=1)
+    dev = torch.device("cuda:0")
+    B, H, L, D = spec["batch"], spec["heads"], spec["L"], spec["d"]
+    BH, dp = B * H, dm.sar_padded_dim(spec["d"])
+    att = dm.SarAttention(d["mask"], B, H, L, D, float(d["base_q"]), float(d["base_p"]),
+                          float(d["sm_scale"]), device=dev)
+    q, k, v, vn = (torch.from_numpy(d[n]).to(dev) for n in ("q", "k", "v", "v_next"))
+    nnz = att.nnz
+    names = ("quantize_q", "quantize_k", "quantize_v", "scores", "pv")
+
+    def run(vv, events=None):
+        calls = (lambda: dm.sar_quantize_q(att.p, q, att.qcodes, att.qpot),
+                 lambda: dm.sar_quantize_k(att.p, k, att.kcodes, att.kscale),
+                 lambda: dm.sar_quantize_v(att.p, vv, att.vcodes_t, att.vscale),
+                 lambda: dm.sar_scores(att.p, att.row_ptr, att.cols, nnz, att.qcodes, att.qpot, att.kcodes,
+                                       att.kscale, att.pcodes, att.ppot),
+                 lambda: dm.sar_pv(att.p, att.row_ptr, att.cols, nnz, att.pcodes, att.ppot, att.vcodes_t,
+                                   att.vscale, att.out))
+        for j, c in enumerate(calls):
+            if events is not None:
+                events[j].record(stream)
+            c()
+        if events is not None:
+            events[len(calls)].record(stream)
+
+    for _ in range(3):
+        run(v)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(reps)]
+    for i in range(reps):
+        run(v if i % 2 == 0 else vn, ev[i])
+    # reused steps: V of the next timestep against the cached P
+    er = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        er[i][0].record(stream)
+        att.reused_step(vn if i % 2 == 0 else v)
+        er[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) * 1e3 for e in ev])) for j, n in enumerate(names)}
+    prod_ops = 2.0 * B * nnz * 64 * 64 * D
+    pc_bytes = B * nnz * (64 * 64 + 2 * 64)          # P codes + PoTs of the cache
+    x_bytes = 4 * BH * L * D                         # one float32 operand
+    alg = {"quantize_q": (x_bytes + BH * L * dp + BH * (L // 32) * dp, 0.0),
+           "quantize_k": (x_bytes + BH * L * dp + 4 * BH * L, 0.0),
+           "quantize_v": (x_bytes + BH * L * dp + 4 * BH * D, 0.0),
+           "scores": (BH * L * dp * 2 + BH * (L // 32) * dp + 4 * BH * L + pc_bytes, prod_ops),
+           "pv": (pc_bytes + BH * L * dp + 4 * BH * D + x_bytes, prod_ops)}
+    kern = {}
+    for n in names:
+        b, o = alg[n]
+        t = us[n] * 1e-6
+        t_hbm, t_mfma = b / (HBM_PEAK_GBS * 1e9), o / (INT8_PEAK_TOPS * 1e12)
+        bound = "mfma" if t_mfma > t_hbm else "hbm"
+        gbs, tops = b / t / 1e9, o / t / 1e12
+        kern[n] = dict(us=us[n], alg_bytes=b, alg_ops=o, gbs=gbs, tops=tops, bound=bound,
+                       frac=tops / INT8_PEAK_TOPS if bound == "mfma" else gbs / HBM_PEAK_GBS)
+    cached = sum(us.values())
+    reused = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in er]))
+    return {"workload": f"pixart-alpha-1024px-attn: {B} images x {H} heads, {L} tokens, head dim {D}, "
+                        f"64x64 blocks, kept {nnz} of {H * (L // 64) ** 2} per image",
+            "launch": "eager", "cached_step_us": cached, "reused_step_us": reused,
+            "kept_fraction": nnz / (H * (L // 64) ** 2),
+            "dense_equiv_tops_cached": 2 * prod_ops / (cached * 1e-6) / 1e12, "kernels": kern}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -405,6 +480,7 @@ def main() -> int:
     ap.add_argument("--no-dynamic", action="store_true", help="skip the dynamic-base comparison")
     ap.add_argument("--no-chain", action="store_true", help="skip the fc1 -> GELU -> fc2 timestep chain")
     ap.add_argument("--no-slices", action="store_true", help="skip timing the 2-bit slice stream")
+    ap.add_argument("--no-attention", action="store_true", help="skip the SAR attention workload")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--write-kernel-summary", metavar="TRACE_DIR")
     args = ap.parse_args()
@@ -594,6 +670,9 @@ def main() -> int:
     if not args.no_dynamic:
         print("[bench] dynamic-base variant", file=sys.stderr, flush=True)
         out["dynamic_base"] = dynamic_variant(dm, torch, state, layers, rows, args, stream, ms_per_step)
+    if not args.no_attention:
+        print("[bench] SAR attention", file=sys.stderr, flush=True)
+        out["sar_attention"] = sar_attention(dm, torch, stream)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline([[host[L][p] for L in layers] for p in range(args.pairs)])

@@ -12,9 +12,14 @@
 //   scores  cached step: one wave per (image·head, 32-row token tile); three
 //           sweeps over the kept key blocks of its query block (row maximum of
 //           the logits, sum of the fixed-point exponentials, then P and its
-//           FMDQ-INT8 codes), each recomputing the exact integer scores.
+//           FMDQ-INT8 codes), each recomputing the exact integer scores; the
+//           next block's K fragments are loaded while one is computed.
 //   pv      cached and reused steps: one wave per (image·head, token tile),
-//           int64 accumulators of the exact O_int over the kept key blocks.
+//           one int32 MFMA accumulator per (column tile, digit plane) over all
+//           kept keys, combined in int64 at the end.
+// Both run two waves per SIMD: the number of digit planes a wave needs is
+// found first and selects a templated body, so the common cases (two planes
+// of a_Q, three of a_P) keep few registers.
 //
 // Exact integer products on int8 MFMAs.  An FMDQ operand value in integer
 // units is a = code·2^PoT (|code| ≤ 64, PoT ≤ 21, so |a| ≤ 2^27).  It is split
@@ -43,7 +48,6 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kBlock = DSTAR_SAR_BLOCK;
 constexpr int kTile = DSTAR_SAR_TILE;
-constexpr int kMaxKs = DSTAR_SAR_MAX_D / 32;   // k-steps over the head channels
 constexpr int kPlanes = 4;                     // digit planes of |a| ≤ 2^27
 constexpr int kP8 = 6;                         // log2 of the 8-bit ceiling 64
 constexpr int kPotMax = DSTAR_FMDQ_POT_MAX;    // 21
@@ -72,12 +76,6 @@ __device__ __forceinline__ float exp32(float x) {
   p = __fadd_rn(__fmul_rn(p, r), 1.0f);
   p = __fadd_rn(__fmul_rn(p, r), 1.0f);
   return ldexpf(p, (int)n);
-}
-
-// E = rint(exp32(x)·2^36): e ≤ 1, so the scaled value is at most 2^36 and
-// converts to int64 exactly.
-__device__ __forceinline__ int64_t exp_fixed(float x) {
-  return (int64_t)rintf(ldexpf(exp32(x), DSTAR_SAR_EXP_FRAC));
 }
 
 // PoT: the number of bin edges base·2^j (j = 0..20) strictly below m.
@@ -112,52 +110,15 @@ __device__ __forceinline__ int wave_max_i(int v) {
   for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
   return v;
 }
-// Maximum / int64 sum over the 32 lanes of one half of the wave.
+// Maximum over the 32 lanes of one half of the wave.
 __device__ __forceinline__ float half_max(float v) {
 #pragma unroll
   for (int o = 16; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
-__device__ __forceinline__ int64_t half_sum(int64_t v) {
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) {
-    const int lo = __shfl_xor((int)(uint32_t)(uint64_t)v, o, 64);
-    const int hi = __shfl_xor((int)(uint32_t)((uint64_t)v >> 32), o, 64);
-    v += (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
-  }
-  return v;
-}
-
 // Planes needed for |code·2^pmax| with |code| ≤ 64.
 __device__ __forceinline__ int planes_for(int pmax) {
   return 1 + (pmax >= 1 ? 1 : 0) + (pmax >= 9 ? 1 : 0) + (pmax >= 17 ? 1 : 0);
-}
-
-// Digit planes of 16 values a_i = code_i·2^pot_i (codes: signed bytes of cw,
-// PoTs: bytes of pw); dig[j] holds digit j of the 16 values, 4 per int.
-// Returns the largest PoT seen.
-__device__ __forceinline__ int digits16(const v4i cw, const v4i pw, v4i (&dig)[kPlanes]) {
-  int pmax = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    uint32_t o[kPlanes] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int code = (int)(int8_t)(((uint32_t)cw[w] >> (8 * i)) & 0xFFu);
-      const int pot = (int)(((uint32_t)pw[w] >> (8 * i)) & 0xFFu);
-      pmax = max(pmax, pot);
-      int a = code * (1 << pot);
-#pragma unroll
-      for (int j = 0; j < kPlanes; ++j) {
-        const int dj = (int)(int8_t)(a & 0xFF);
-        o[j] |= ((uint32_t)dj & 0xFFu) << (8 * i);
-        a = (a - dj) >> 8;   // exact: a − dj is a multiple of 256
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kPlanes; ++j) dig[j][w] = (int)o[j];
-  }
-  return pmax;
 }
 
 struct Dims {
@@ -300,41 +261,199 @@ __device__ __forceinline__ void block_range(const int32_t* row_ptr, int64_t r, i
   j1 = min(max(row_ptr[r + 1], j0), nnz);
 }
 
-// Logits z of one kept key block for the wave's 32 rows: z[ct][r] at row
-// 8·(r/4) + 4·(lane/32) + r%4 of the tile and key 32·ct + lane%32 of the block.
-__device__ __forceinline__ void block_logits(const ScoreArgs& a, int64_t bh, int kb, const v4i (&A)[kMaxKs][kPlanes],
-                                             int np, int nks, float (&z)[2][16]) {
-  const int lane = threadIdx.x & 63, li = lane & 31, hi = lane >> 5;
-  const int8_t* kbase = a.kc + (bh * a.m.L + (int64_t)kb * kBlock) * a.m.dp;
+// Digit planes 0..NP-1 of 16 values a_i = code_i·2^pot_i (codes: signed
+// bytes of cw, PoTs: bytes of pw); dig[j] holds digit j of the 16 values, 4
+// per int.  The caller guarantees that the higher digits are 0.
+template <int NP>
+__device__ __forceinline__ void digits_np(const v4i cw, const v4i pw, v4i (&dig)[NP]) {
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    v4i Bf[kMaxKs];
+  for (int w = 0; w < 4; ++w) {
+    uint32_t o[NP];
 #pragma unroll
-    for (int ks = 0; ks < kMaxKs; ++ks)
-      if (ks < nks) Bf[ks] = *reinterpret_cast<const v4i*>(kbase + (int64_t)(32 * ct + li) * a.m.dp + 32 * ks + 16 * hi);
-    const double f = (double)a.ks[bh * a.m.L + (int64_t)kb * kBlock + 32 * ct + li] * a.g;
+    for (int j = 0; j < NP; ++j) o[j] = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int code = (int)(int8_t)(((uint32_t)cw[w] >> (8 * i)) & 0xFFu);
+      const int pot = (int)(((uint32_t)pw[w] >> (8 * i)) & 0xFFu);
+      int a = code * (1 << pot);
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        const int dj = (int)(int8_t)(a & 0xFF);
+        o[j] |= ((uint32_t)dj & 0xFFu) << (8 * i);
+        a = (a - dj) >> 8;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) dig[j][w] = (int)o[j];
+  }
+}
+
+// Largest PoT byte of a 16-byte vector.
+__device__ __forceinline__ int max_pot16(const v4i pw) {
+  int m = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, (int)(((uint32_t)pw[w] >> (8 * i)) & 0xFFu));
+  return m;
+}
+
+// Logits z of one 32-key column tile of a kept block for the wave's 32 rows:
+// z[r] at row 8·(r/4) + 4·(lane/32) + r%4 of the tile and key lane%32 of the
+// column tile.  The exact integer score is Σ_j 2^(8j)·(digit plane j · K);
+// with two planes every partial sum and the total stay below 2^30, so int32
+// holds it exactly, otherwise the planes are combined in int64.
+template <int NKS, int NP>
+__device__ __forceinline__ void tile_logits(const v4i (&A)[NKS][NP], const v4i (&B)[NKS], double f, float (&z)[16]) {
+  if constexpr (NP <= 2) {
+    v16i acc[NP];
+#pragma unroll
+    for (int jp = 0; jp < NP; ++jp) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[jp][r] = 0;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) acc[jp] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ks][jp], B[ks], acc[jp], 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int s = NP == 2 ? acc[0][r] + acc[1][r] * 256 : acc[0][r];
+      z[r] = (float)((double)s * f);
+    }
+  } else {
+    // one plane at a time into an int64 sum (fewer live registers)
     int64_t s[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0;
 #pragma unroll
-    for (int jp = 0; jp < kPlanes; ++jp) {
-      if (jp < np) {
-        v16i acc;
+    for (int jp = 0; jp < NP; ++jp) {
+      v16i acc;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0;
+      for (int r = 0; r < 16; ++r) acc[r] = 0;
 #pragma unroll
-        for (int ks = 0; ks < kMaxKs; ++ks)
-          if (ks < nks) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ks][jp], Bf[ks], acc, 0, 0, 0);
+      for (int ks = 0; ks < NKS; ++ks) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[ks][jp], B[ks], acc, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] += (int64_t)acc[r] * ((int64_t)1 << (8 * jp));
-      }
+      for (int r = 0; r < 16; ++r) s[r] += (int64_t)acc[r] * ((int64_t)1 << (8 * jp));
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) z[ct][r] = (float)((double)s[r] * f);
+    for (int r = 0; r < 16; ++r) z[r] = (float)((double)s[r] * f);
   }
 }
 
-__global__ __launch_bounds__(kThreads) void scores_kernel(ScoreArgs a) {
+// E = rint(exp32(x)·2^36) as a double: e ≤ 1 and the scaled value is exact,
+// so E is an integer below 2^37 and sums of up to 2^16 of them stay exact.
+__device__ __forceinline__ double exp_fixed_d(float x) {
+  return rint(ldexp((double)exp32(x), DSTAR_SAR_EXP_FRAC));
+}
+
+__device__ __forceinline__ double half_sum_d(double v) {
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// One sweep over the kept blocks [j0, j1) of the wave's query block: the
+// logits of every 32-key column tile are handed to fn(j, ct, z).  With two
+// digit planes the K fragments and scales of block j+1 are loaded while
+// block j is computed (with four there are no registers left for that).
+template <int NKS, int NP, typename F>
+__device__ __forceinline__ void sweep_blocks(const ScoreArgs& a, int64_t bh, int j0, int j1,
+                                             const v4i (&A)[NKS][NP], F&& fn) {
+  const int lane = threadIdx.x & 63, li = lane & 31, hi = lane >> 5;
+  const int8_t* kbh = a.kc + bh * a.m.L * (int64_t)a.m.dp + (int64_t)li * a.m.dp + 16 * hi;
+  const float* sbh = a.ks + bh * a.m.L + li;
+  v4i Bn[2][NKS];
+  float sn[2];
+  auto fetch = [&](int j) {
+    int kb = a.cols[j];
+    kb = (kb < 0 || kb >= a.m.nb) ? 0 : kb;     // skipped below; any block in range
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        Bn[ct][ks] = *reinterpret_cast<const v4i*>(kbh + (int64_t)(kb * kBlock + 32 * ct) * a.m.dp + 32 * ks);
+      sn[ct] = sbh[kb * kBlock + 32 * ct];
+    }
+  };
+  constexpr bool kPrefetch = NP <= 2;
+  if (kPrefetch) fetch(j0);
+  for (int j = j0; j < j1; ++j) {
+    const int kb = a.cols[j];
+    if (!kPrefetch) fetch(j);
+    v4i B[2][NKS];
+    float sc[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      sc[ct] = sn[ct];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) B[ct][ks] = Bn[ct][ks];
+    }
+    if (kPrefetch && j + 1 < j1) fetch(j + 1);
+    if (kb < 0 || kb >= a.m.nb) continue;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      float z[16];
+      tile_logits<NKS, NP>(A, B[ct], (double)sc[ct] * a.g, z);
+      fn(j, ct, z);
+    }
+  }
+}
+
+// The three sweeps of one 32-row query tile (a wave) with NP digit planes of
+// a_Q: row maxima of the logits, exact sums of the fixed-point exponentials,
+// then P, its FMDQ-INT8 codes per (tile, key) sub-channel and the cache.
+template <int NKS, int NP>
+__device__ __forceinline__ void scores_tile(const ScoreArgs& a, int64_t bh, int tau, int b, int half, int j0, int j1,
+                                            const v4i (&cw)[NKS], const v4i (&pw)[NKS]) {
+  const int lane = threadIdx.x & 63, li = lane & 31, hi = lane >> 5;
+  v4i A[NKS][NP];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) digits_np<NP>(cw[ks], pw[ks], A[ks]);
+
+  float mrow[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mrow[r] = -INFINITY;
+  sweep_blocks<NKS, NP>(a, bh, j0, j1, A, [&](int, int, const float (&z)[16]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mrow[r] = fmaxf(mrow[r], z[r]);
+  });
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mrow[r] = half_max(mrow[r]);
+
+  double inv[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) inv[r] = 0.0;
+  sweep_blocks<NKS, NP>(a, bh, j0, j1, A, [&](int, int, const float (&z)[16]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) inv[r] += exp_fixed_d(__fsub_rn(z[r], mrow[r]));
+  });
+#pragma unroll
+  for (int r = 0; r < 16; ++r) inv[r] = 1.0 / half_sum_d(inv[r]);
+
+  sweep_blocks<NKS, NP>(a, bh, j0, j1, A, [&](int j, int ct, const float (&z)[16]) {
+    const int64_t blk = (int64_t)b * a.nnz + j;
+    float P[16];
+    float mx = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      P[r] = (float)(exp_fixed_d(__fsub_rn(z[r], mrow[r])) * inv[r]);
+      mx = fmaxf(mx, P[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));    // the other 16 rows of the column
+    const int pot = pot_of(mx, a.base_p);
+    int8_t* dst = a.pc + (blk * kBlock + 32 * half) * kBlock + 32 * ct + li;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      dst[(8 * (r >> 2) + 4 * hi + (r & 3)) * kBlock] = (int8_t)code8(P[r], a.inv_base_p, pot);
+    if (hi == 0) a.ppot[(blk * 2 + half) * kBlock + 32 * ct + li] = (uint8_t)pot;
+  });
+}
+
+// One wave per (image·head, 32-row token tile); NKS = dp/32 k-steps.  Two
+// waves per SIMD: the digit planes of a_Q the tile needs (two unless some
+// PoT exceeds 8) select the instantiation, so the common case keeps few
+// registers.
+template <int NKS>
+__global__ __launch_bounds__(kThreads, 2) void scores_kernel(ScoreArgs a) {
   const int lane = threadIdx.x & 63, li = lane & 31, hi = lane >> 5;
   const int tpb = a.m.L / kTile;
   const int64_t tile = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
@@ -346,85 +465,23 @@ __global__ __launch_bounds__(kThreads) void scores_kernel(ScoreArgs a) {
   int j0, j1;
   block_range(a.row_ptr, (int64_t)h * a.m.nb + qb, a.nnz, j0, j1);
   if (j0 >= j1) return;
-  const int nks = a.m.dp / 32;
 
-  // Digit planes of a_Q for the tile (A operand, kept in registers).
-  v4i A[kMaxKs][kPlanes];
+  v4i cw[NKS], pw[NKS];
   int pmax = 0;
   {
     const int8_t* qrow = a.qc + (bh * a.m.L + (int64_t)tau * kTile + li) * a.m.dp;
     const uint8_t* prow = a.qpot + (bh * tpb + tau) * a.m.dp;
 #pragma unroll
-    for (int ks = 0; ks < kMaxKs; ++ks) {
-      if (ks < nks) {
-        const v4i cw = *reinterpret_cast<const v4i*>(qrow + 32 * ks + 16 * hi);
-        const v4i pw = *reinterpret_cast<const v4i*>(prow + 32 * ks + 16 * hi);
-        pmax = max(pmax, digits16(cw, pw, A[ks]));
-      } else {
-#pragma unroll
-        for (int j = 0; j < kPlanes; ++j) A[ks][j] = v4i{0, 0, 0, 0};
-      }
+    for (int ks = 0; ks < NKS; ++ks) {
+      cw[ks] = *reinterpret_cast<const v4i*>(qrow + 32 * ks + 16 * hi);
+      pw[ks] = *reinterpret_cast<const v4i*>(prow + 32 * ks + 16 * hi);
+      pmax = max(pmax, max_pot16(pw[ks]));
     }
   }
-  const int np = planes_for(wave_max_i(pmax));
-
-  // Sweep 1: row maxima of the logits over every kept key.
-  float mrow[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) mrow[r] = -INFINITY;
-  for (int j = j0; j < j1; ++j) {
-    const int kb = a.cols[j];
-    if (kb < 0 || kb >= a.m.nb) continue;
-    float z[2][16];
-    block_logits(a, bh, kb, A, np, nks, z);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mrow[r] = fmaxf(mrow[r], fmaxf(z[0][r], z[1][r]));
-  }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) mrow[r] = half_max(mrow[r]);
-
-  // Sweep 2: exact sums of the fixed-point exponentials.
-  int64_t srow[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) srow[r] = 0;
-  for (int j = j0; j < j1; ++j) {
-    const int kb = a.cols[j];
-    if (kb < 0 || kb >= a.m.nb) continue;
-    float z[2][16];
-    block_logits(a, bh, kb, A, np, nks, z);
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      srow[r] += exp_fixed(__fsub_rn(z[0][r], mrow[r])) + exp_fixed(__fsub_rn(z[1][r], mrow[r]));
-  }
-  double inv[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) inv[r] = 1.0 / (double)half_sum(srow[r]);
-
-  // Sweep 3: P, its FMDQ-INT8 codes per (tile, key) sub-channel, the cache.
-  for (int j = j0; j < j1; ++j) {
-    const int kb = a.cols[j];
-    if (kb < 0 || kb >= a.m.nb) continue;
-    float z[2][16];
-    block_logits(a, bh, kb, A, np, nks, z);
-    const int64_t blk = (int64_t)b * a.nnz + j;
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      float P[16];
-      float mx = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        P[r] = (float)((double)exp_fixed(__fsub_rn(z[ct][r], mrow[r])) * inv[r]);
-        mx = fmaxf(mx, P[r]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));    // the other 16 rows of the column
-      const int pot = pot_of(mx, a.base_p);
-      int8_t* dst = a.pc + (blk * kBlock + 32 * half) * kBlock + 32 * ct + li;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        dst[(8 * (r >> 2) + 4 * hi + (r & 3)) * kBlock] = (int8_t)code8(P[r], a.inv_base_p, pot);
-      if (hi == 0) a.ppot[(blk * 2 + half) * kBlock + 32 * ct + li] = (uint8_t)pot;
-    }
-  }
+  if (planes_for(wave_max_i(pmax)) <= 2)
+    scores_tile<NKS, 2>(a, bh, tau, b, half, j0, j1, cw, pw);
+  else
+    scores_tile<NKS, kPlanes>(a, bh, tau, b, half, j0, j1, cw, pw);
 }
 
 // ---------------------------------------------------------------- P·V
@@ -442,8 +499,98 @@ struct PvArgs {
   double hp;         // base_p·2^-6
 };
 
-__global__ __launch_bounds__(kThreads) void pv_kernel(PvArgs a) {
+// One pass over the kept blocks of the wave's query block for the column
+// tiles ct0 .. ct0+CG-1 (those below ncg): a_P is split into NP digit planes
+// (NP covers every kept block's largest PoT); each (column tile, plane) keeps
+// one int32 MFMA accumulator over all kept keys.  |digit| ≤ 128, |V code| ≤
+// 127 and at most 2^16 keys, so each stays below 2^31 and is exact; the
+// planes are combined in int64 once, at the end.  The P codes and PoTs of
+// block j+1 are loaded while block j is multiplied.
+template <int CG, int NP>
+__device__ __forceinline__ void pv_pass(const PvArgs& a, int64_t bh, int tau, int b, int half, int j0, int j1,
+                                        int ct0, int ncg) {
   const int lane = threadIdx.x & 63, li = lane & 31, hi = lane >> 5;
+  v16i acc[CG][NP];
+#pragma unroll
+  for (int c = 0; c < CG; ++c)
+#pragma unroll
+    for (int jp = 0; jp < NP; ++jp)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[c][jp][r] = 0;
+
+  v4i cn[2], pn[2];
+  auto fetch = [&](int j) {
+    const int64_t blk = (int64_t)b * a.nnz + j;
+    const int8_t* prow = a.pc + (blk * kBlock + 32 * half + li) * kBlock + 16 * hi;
+    const uint8_t* pp = a.ppot + (blk * 2 + half) * kBlock + 16 * hi;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      cn[ks] = *reinterpret_cast<const v4i*>(prow + 32 * ks);
+      pn[ks] = *reinterpret_cast<const v4i*>(pp + 32 * ks);
+    }
+  };
+  const int8_t* vbh = a.vct + (bh * a.m.dp + li) * (int64_t)a.m.L + 16 * hi;
+  if (j0 < j1) fetch(j0);
+  for (int j = j0; j < j1; ++j) {
+    const int kb = a.cols[j];
+    const v4i cw0 = cn[0], cw1 = cn[1], pw0 = pn[0], pw1 = pn[1];
+    if (j + 1 < j1) fetch(j + 1);
+    if (kb < 0 || kb >= a.m.nb) continue;
+    v4i Bv[CG][2];
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+      if (c < ncg) {
+        const int8_t* vrow = vbh + (int64_t)(32 * (ct0 + c)) * a.m.L + (int64_t)kb * kBlock;
+        Bv[c][0] = *reinterpret_cast<const v4i*>(vrow);
+        Bv[c][1] = *reinterpret_cast<const v4i*>(vrow + 32);
+      }
+    }
+    v4i A0[NP], A1[NP];
+    digits_np<NP>(cw0, pw0, A0);
+    digits_np<NP>(cw1, pw1, A1);
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+      if (c < ncg) {
+#pragma unroll
+        for (int jp = 0; jp < NP; ++jp) {
+          acc[c][jp] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A0[jp], Bv[c][0], acc[c][jp], 0, 0, 0);
+          acc[c][jp] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A1[jp], Bv[c][1], acc[c][jp], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int c = 0; c < CG; ++c) {
+    const int ch = 32 * (ct0 + c) + li;
+    if (c < ncg && ch < a.m.d) {
+      const double hc = (double)a.vscale[bh * a.m.d + ch] * a.hp;
+      float* dst = a.out + (bh * a.m.L + (int64_t)tau * kTile) * a.m.d + ch;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        int64_t o = 0;
+#pragma unroll
+        for (int jp = 0; jp < NP; ++jp) o += (int64_t)acc[c][jp][r] * ((int64_t)1 << (8 * jp));
+        dst[(int64_t)(8 * (r >> 2) + 4 * hi + (r & 3)) * a.m.d] = (float)((double)o * hc);
+      }
+    }
+  }
+}
+
+// All column tiles of one wave's rows, CG at a time.
+template <int NCT, int CG, int NP>
+__device__ __forceinline__ void pv_tile(const PvArgs& a, int64_t bh, int tau, int b, int half, int j0, int j1) {
+#pragma unroll
+  for (int ct0 = 0; ct0 < NCT; ct0 += CG) pv_pass<CG, NP>(a, bh, tau, b, half, j0, j1, ct0, min(CG, NCT - ct0));
+}
+
+// One wave per (image·head, 32-row token tile); NCT = dp/32 column tiles.
+// A first pass over the kept blocks' PoTs of the tile's rows gives the digit
+// planes a_P needs (P ≤ 1: three planes while every PoT ≤ 16), which select
+// the instantiation; two waves per SIMD.
+template <int NCT>
+__global__ __launch_bounds__(kThreads, 2) void pv_kernel(PvArgs a) {
+  const int lane = threadIdx.x & 63;
   const int tpb = a.m.L / kTile;
   const int64_t tile = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (tile >= a.m.BH * tpb) return;
@@ -451,63 +598,22 @@ __global__ __launch_bounds__(kThreads) void pv_kernel(PvArgs a) {
   const int tau = (int)(tile % tpb);
   const int b = (int)(bh / a.m.heads), h = (int)(bh % a.m.heads);
   const int qb = tau >> 1, half = tau & 1;
-  const int nct = a.m.dp / 32;
   int j0, j1;
   block_range(a.row_ptr, (int64_t)h * a.m.nb + qb, a.nnz, j0, j1);
 
-  int64_t o[kMaxKs][16];
-#pragma unroll
-  for (int ct = 0; ct < kMaxKs; ++ct)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[ct][r] = 0;
-
+  int pmax = 0;
   for (int j = j0; j < j1; ++j) {
     const int kb = a.cols[j];
     if (kb < 0 || kb >= a.m.nb) continue;
-    const int64_t blk = (int64_t)b * a.nnz + j;
-    const int8_t* prow = a.pc + (blk * kBlock + 32 * half + li) * kBlock;
-    const uint8_t* pp = a.ppot + (blk * 2 + half) * kBlock;
-    v4i A[2][kPlanes];
-    int pmax = 0;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const v4i cw = *reinterpret_cast<const v4i*>(prow + 32 * ks + 16 * hi);
-      const v4i pw = *reinterpret_cast<const v4i*>(pp + 32 * ks + 16 * hi);
-      pmax = max(pmax, digits16(cw, pw, A[ks]));
-    }
-    const int np = planes_for(wave_max_i(pmax));
-#pragma unroll
-    for (int ct = 0; ct < kMaxKs; ++ct) {
-      if (ct < nct) {
-        const int8_t* vrow = a.vct + (bh * a.m.dp + 32 * ct + li) * a.m.L + (int64_t)kb * kBlock + 16 * hi;
-        const v4i B0 = *reinterpret_cast<const v4i*>(vrow);
-        const v4i B1 = *reinterpret_cast<const v4i*>(vrow + 32);
-#pragma unroll
-        for (int jp = 0; jp < kPlanes; ++jp) {
-          if (jp < np) {
-            v16i acc;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = 0;
-            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[0][jp], B0, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[1][jp], B1, acc, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[ct][r] += (int64_t)acc[r] * ((int64_t)1 << (8 * jp));
-          }
-        }
-      }
-    }
+    pmax = max(pmax, (int)a.ppot[(((int64_t)b * a.nnz + j) * 2 + half) * kBlock + lane]);
   }
-
-#pragma unroll
-  for (int ct = 0; ct < kMaxKs; ++ct) {
-    const int c = 32 * ct + li;
-    if (ct < nct && c < a.m.d) {
-      const double hc = (double)a.vscale[bh * a.m.d + c] * a.hp;
-      float* dst = a.out + (bh * a.m.L + (int64_t)tau * kTile) * a.m.d + c;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dst[(int64_t)(8 * (r >> 2) + 4 * hi + (r & 3)) * a.m.d] = (float)((double)o[ct][r] * hc);
-    }
-  }
+  const int np = planes_for(min(wave_max_i(pmax), 31));
+  if (np <= 2)
+    pv_tile<NCT, (NCT < 3 ? NCT : 3), 2>(a, bh, tau, b, half, j0, j1);
+  else if (np == 3)
+    pv_tile<NCT, (NCT < 3 ? NCT : 3), 3>(a, bh, tau, b, half, j0, j1);
+  else
+    pv_tile<NCT, (NCT < 2 ? NCT : 2), kPlanes>(a, bh, tau, b, half, j0, j1);
 }
 
 // ---------------------------------------------------------------- host checks
@@ -627,8 +733,14 @@ int dstar_sar_scores(const dstar_sar_params* p, const int32_t* row_ptr, const in
   a.base_p = p->base_p;
   a.inv_base_p = (float)(1.0 / (double)p->base_p);
   if (nnz == 0) return DSTAR_OK;
-  hipLaunchKernelGGL(scores_kernel, dim3(waves_grid(a.m.BH * (a.m.L / kTile))), dim3(kThreads), 0,
-                     (hipStream_t)stream, a);
+  const dim3 grid(waves_grid(a.m.BH * (a.m.L / kTile)));
+  const hipStream_t s = (hipStream_t)stream;
+  switch (a.m.dp / 32) {
+    case 1: hipLaunchKernelGGL(scores_kernel<1>, grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(scores_kernel<2>, grid, dim3(kThreads), 0, s, a); break;
+    case 3: hipLaunchKernelGGL(scores_kernel<3>, grid, dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL(scores_kernel<4>, grid, dim3(kThreads), 0, s, a); break;
+  }
   return check_launch("sar_scores");
 }
 
@@ -653,7 +765,14 @@ int dstar_sar_pv(const dstar_sar_params* p, const int32_t* row_ptr, const int32_
   a.vscale = vscale;
   a.out = out;
   a.hp = (double)p->base_p * 0x1p-6;
-  hipLaunchKernelGGL(pv_kernel, dim3(waves_grid(a.m.BH * (a.m.L / kTile))), dim3(kThreads), 0, (hipStream_t)stream, a);
+  const dim3 grid(waves_grid(a.m.BH * (a.m.L / kTile)));
+  const hipStream_t s = (hipStream_t)stream;
+  switch (a.m.dp / 32) {
+    case 1: hipLaunchKernelGGL(pv_kernel<1>, grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(pv_kernel<2>, grid, dim3(kThreads), 0, s, a); break;
+    case 3: hipLaunchKernelGGL(pv_kernel<3>, grid, dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL(pv_kernel<4>, grid, dim3(kThreads), 0, s, a); break;
+  }
   return check_launch("sar_pv");
 }
 

@@ -109,6 +109,42 @@ def test_sar_cached_and_reused_step_match_oracle(dm, case):
     np.testing.assert_array_equal(g["o_reused"], u["o"])
 
 
+PLANE_CASES = [
+    # (d, q_outlier, log2 base_p, seed): outliers in Q raise its PoTs past 8
+    # (more than two digit planes of a_Q); a small base_p raises P's PoTs past
+    # 16 (four planes of a_P), a large one keeps them at or below 8 (two)
+    (72, 2000.0, -15, 11),
+    (128, 300.0, -28, 12),
+    (72, 1.0, -28, 13),
+    (40, 1.0, -4, 14),
+    (1, 5000.0, -30, 15),
+    (96, 1.0, -6, 16),
+]
+
+
+@pytest.mark.parametrize("case", PLANE_CASES, ids=[f"d{c[0]}q{c[1]:g}p{c[2]}" for c in PLANE_CASES])
+def test_sar_digit_plane_counts_match_oracle(dm, case):
+    """Every digit-plane count of a_Q (scores) and a_P (P·V), at several head
+    widths: bit-equal to the oracle in every stage."""
+    dd, qo, lbp, seed = case
+    d = ga.make_attention(1, 2, 256, dd, 0.63, seed)
+    rng = np.random.default_rng(seed)
+    if qo != 1.0:
+        hot = rng.random(d["q"].shape) < 0.002
+        hot[0, 37, 0] = True
+        d["q"] = np.where(hot, d["q"] * np.float32(qo), d["q"]).astype(np.float32)
+    d["base_p"] = np.float32(2.0 ** lbp)
+    log(f"case d={dd} q_outlier={qo} base_p=2^{lbp} seed={seed}")
+    g = run_gpu(dm, d, reuse_v=d["v_next"])
+    row_ptr, cols = sar.mask_to_csr(d["mask"])
+    r = sar.cached_step(d["q"], d["k"], d["v"], row_ptr, cols, 2, d["base_q"], d["sm_scale"], d["base_p"])
+    if qo != 1.0:
+        assert r["qpot"].max() > 8
+    compare(g, r, d)
+    u = sar.reused_step(r["pcodes"], r["ppot"], d["v_next"], row_ptr, cols, 2, d["base_p"])
+    np.testing.assert_array_equal(g["o_reused"], u["o"])
+
+
 def test_sar_empty_query_blocks_and_sparse_rows(dm):
     """Query blocks without any kept key block get O = 0; single kept blocks
     far from the diagonal work."""
