@@ -177,30 +177,48 @@ def cpu_baseline(ins: list[dict], budget_s: float = 10.0) -> dict:
                       f"per token tile and FPoT group"}
 
 
-def write_kernel_summary(trace_dir: str) -> None:
+SUMMARIES = {
+    "linear": ("kernel_time_pixart1024.md",
+               "# Kernel time, FMDQ differential linear, PixArt-alpha-style 1024px MLP",
+               "8192 rows (2 x 4096 tokens), fc1 1152->4608 and fc2 4608->1152, token tile 32; one MI355X.",
+               "python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline --no-dynamic --no-chain --no-slices "
+               "--no-attention",
+               "rocprofv3 statistics over every launch of the run (eager warm-up steps, graph warm-up and timed "
+               "replays, and the eager pass that times the stages; fc1 and fc2 pooled per kernel):"),
+    "attention": ("kernel_time_sar_attention_pixart1024.md",
+                  "# Kernel time, SAR attention with FMDQ-INT8 operands, PixArt-alpha-style 1024px",
+                  "2 images x 16 heads, 4096 tokens, head dim 72, 64 x 64 blocks (63% kept); one MI355X.",
+                  "python3 bench.py --only-attention",
+                  "rocprofv3 statistics over every launch of the run (three warm-up cached steps, ten timed "
+                  "cached steps and ten reused steps):"),
+}
+
+
+def write_kernel_summary(trace_dir: str, which: str = "linear") -> None:
     """Summarizes a rocprofv3 --kernel-trace --stats run of the bench: the
     tool's own per-kernel statistics, and the mean duration per kernel and
     launch grid from the trace (fc1 and fc2 launch the same kernels with
     different grids)."""
     import csv
+    fname, title, shape, cmd, stats_note = SUMMARIES[which]
     files = {}
     for root, _, fs in os.walk(trace_dir):
         for fn in fs:
             files[fn] = os.path.join(root, fn)
     stats = [r for f, p in files.items() if f.endswith("kernel_stats.csv") for r in csv.DictReader(open(p))]
     trace = [r for f, p in files.items() if f.endswith("kernel_trace.csv") for r in csv.DictReader(open(p))]
-    lines = ["# Kernel time, FMDQ differential linear, PixArt-alpha-style 1024px MLP",
+    lines = [title,
              "",
-             "8192 rows (2 x 4096 tokens), fc1 1152->4608 and fc2 4608->1152, token tile 32; one MI355X.",
+             shape,
              "Command (from the repository root), then the summary:",
              "",
              "```",
-             "rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_bench -o run -- \\",
-             "    python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention",
-             "python bench.py --write-kernel-summary gpurun_out/prof_bench",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_{which} -o run -- \\",
+             f"    {cmd}",
+             f"python bench.py --write-kernel-summary gpurun_out/prof_{which} --summary {which}",
              "```",
              "",
-             "rocprofv3 statistics over every launch of the run (eager warm-up steps, graph warm-up and timed replays, and the eager pass that times the stages; fc1 and fc2 pooled per kernel):",
+             stats_note,
              "",
              "| kernel | calls | total us | average us | min us | max us | % |",
              "|---|---|---|---|---|---|---|"]
@@ -221,7 +239,7 @@ def write_kernel_summary(trace_dir: str) -> None:
     for (name, grid), v in sorted(per.items(), key=lambda x: -sum(x[1])):
         short = name.replace("dstar::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
         lines.append(f"| `{short}` | {grid} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
-    out = os.path.join(ROOT, "profiles", "kernel_time_pixart1024.md")
+    out = os.path.join(ROOT, "profiles", fname)
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -393,6 +411,28 @@ def dynamic_variant(dm, torch, state, layers, rows, args, stream, ms_static) -> 
     return out
 
 
+def library_gemm(torch, layers: dict, rows: int, reps: int = 20) -> dict:
+    """Context only: the vendor library's plain int8 GEMM (torch._int_mm, int32
+    out) on each layer's shape, M = rows, K, N as the layer's; it computes
+    neither the quantization, the FPoT alignment nor the float32 Y update."""
+    out = {}
+    dev = torch.device("cuda:0")
+    for L, (K, N) in layers.items():
+        a = torch.randint(-127, 128, (rows, K), dtype=torch.int8, device=dev)
+        b = torch.randint(-127, 128, (N, K), dtype=torch.int8, device=dev).t()
+        for _ in range(3):
+            torch._int_mm(a, b)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch._int_mm(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        out[L] = {"M": rows, "K": K, "N": N, "us": us, "tops": 2 * rows * K * N / (us * 1e-6) / 1e12}
+    return out
+
+
 def sar_attention(dm, torch, stream, reps: int = 10) -> dict:
     """Sparse Attention Reuse with FMDQ-INT8 operands (DSTAR §3.2 Fig. 8,
     §4.3 Fig. 13) on the PixArt-alpha 1024px self-attention shape: 2 images x
@@ -483,12 +523,15 @@ def main() -> int:
     ap.add_argument("--no-attention", action="store_true", help="skip the SAR attention workload")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--write-kernel-summary", metavar="TRACE_DIR")
+    ap.add_argument("--summary", choices=sorted(SUMMARIES), default="linear",
+                    help="which kernel-time summary --write-kernel-summary writes")
+    ap.add_argument("--only-attention", action="store_true", help="time only the SAR attention workload")
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(*args.write_traffic)
         return 0
     if args.write_kernel_summary:
-        write_kernel_summary(args.write_kernel_summary)
+        write_kernel_summary(args.write_kernel_summary, args.summary)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the layer shards by token tiles with no "
@@ -503,6 +546,10 @@ def main() -> int:
         import __graft_entry__
         __graft_entry__.build()
     dm.load()
+    if args.only_attention:
+        print("[bench] SAR attention", file=sys.stderr, flush=True)
+        print(json.dumps({"sar_attention": sar_attention(dm, torch, torch.cuda.current_stream())}))
+        return 0
     dev = torch.device("cuda:0")
     cfg = {v["name"]: c for c, v in wl.CONFIGS.items()}[args.workload]
     spec = wl.CONFIGS[cfg]
@@ -670,6 +717,11 @@ def main() -> int:
     if not args.no_dynamic:
         print("[bench] dynamic-base variant", file=sys.stderr, flush=True)
         out["dynamic_base"] = dynamic_variant(dm, torch, state, layers, rows, args, stream, ms_per_step)
+    print("[bench] library int8 GEMM (context)", file=sys.stderr, flush=True)
+    try:
+        out["library_int8_gemm"] = library_gemm(torch, {L: (state[L]["K"], state[L]["N"]) for L in layers}, rows)
+    except RuntimeError as ex:                # not every build exposes it
+        out["library_int8_gemm"] = {"error": str(ex)[:200]}
     if not args.no_attention:
         print("[bench] SAR attention", file=sys.stderr, flush=True)
         out["sar_attention"] = sar_attention(dm, torch, stream)

@@ -263,28 +263,31 @@ __device__ __forceinline__ void block_range(const int32_t* row_ptr, int64_t r, i
 
 // Digit planes 0..NP-1 of 16 values a_i = code_i·2^pot_i (codes: signed
 // bytes of cw, PoTs: bytes of pw); dig[j] holds digit j of the 16 values, 4
-// per int.  The caller guarantees that the higher digits are 0.
+// per int.  The caller guarantees that the higher digits are 0.  Adding
+// Σ_j 128·256^j to a makes every digit non-negative (d_j + 128 in [0, 255]),
+// so the bytes of a + 0x80808080, each XORed with 0x80, are the signed
+// digits of a (|a| ≤ 2^27); a 4 × 4 byte transpose then gathers digit j of
+// four values into one word.
 template <int NP>
 __device__ __forceinline__ void digits_np(const v4i cw, const v4i pw, v4i (&dig)[NP]) {
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint32_t o[NP];
-#pragma unroll
-    for (int j = 0; j < NP; ++j) o[j] = 0u;
+    uint32_t d[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int code = (int)(int8_t)(((uint32_t)cw[w] >> (8 * i)) & 0xFFu);
       const int pot = (int)(((uint32_t)pw[w] >> (8 * i)) & 0xFFu);
-      int a = code * (1 << pot);
-#pragma unroll
-      for (int j = 0; j < NP; ++j) {
-        const int dj = (int)(int8_t)(a & 0xFF);
-        o[j] |= ((uint32_t)dj & 0xFFu) << (8 * i);
-        a = (a - dj) >> 8;
-      }
+      d[i] = ((uint32_t)(code * (1 << pot)) + 0x80808080u) ^ 0x80808080u;
     }
+    // d[i] = bytes (d0, d1, d2, d3) of value i → plane words
+    const uint32_t a0 = __builtin_amdgcn_perm(d[1], d[0], 0x05010400u);
+    const uint32_t a1 = __builtin_amdgcn_perm(d[1], d[0], 0x07030602u);
+    const uint32_t b0 = __builtin_amdgcn_perm(d[3], d[2], 0x05010400u);
+    const uint32_t b1 = __builtin_amdgcn_perm(d[3], d[2], 0x07030602u);
+    const uint32_t pl[4] = {__builtin_amdgcn_perm(b0, a0, 0x05040100u), __builtin_amdgcn_perm(b0, a0, 0x07060302u),
+                            __builtin_amdgcn_perm(b1, a1, 0x05040100u), __builtin_amdgcn_perm(b1, a1, 0x07060302u)};
 #pragma unroll
-    for (int j = 0; j < NP; ++j) dig[j][w] = (int)o[j];
+    for (int j = 0; j < NP; ++j) dig[j][w] = (int)pl[j];
   }
 }
 
