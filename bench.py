@@ -652,11 +652,12 @@ def main() -> int:
     grids = {}
     for L in layers:
         K, N = state[L]["K"], state[L]["N"]
-        # stage 1: 16 rows per lane, T/16 lanes per group, CPT channels per group
+        # stage 1: 16 rows per lane, T/16 lanes per group, CPT channels per
+        # group; items of kgroups flattened (tile, group) pairs; 512 workgroups
         kgroups = 256 // (T // 16)
         cpt = 4 if K % 4 == 0 else 2 if K % 2 == 0 else 1
-        q_work = nt * ((K + kgroups * cpt - 1) // (kgroups * cpt))
-        grids[L] = {"quantize": 256 * min(q_work, 8192), "bucket": (1024 if K <= 16384 else 256) * min(nt, 2048),
+        q_work = (nt * (K // cpt) + kgroups - 1) // kgroups
+        grids[L] = {"quantize": 256 * min(q_work, 512), "bucket": (1024 if K <= 16384 else 256) * min(nt, 2048),
                     "linear": 256 * ((nt + 128 // T - 1) // (128 // T)) * ((N + 255) // 256)}
     kernels = {}
     layer_out = {}
