@@ -4,7 +4,7 @@
 // Kernels:
 //   qquant  FMDQ-INT8 of Q: one wave per 32-row token tile, a lane per channel
 //           (two channel passes), the tile's rows streamed with coalesced loads.
-//   kquant  int8 of K with a scale per key: one wave per key row.
+//   kquant  int8 of K with a scale per key: one wave per 8 key rows.
 //   vquant  int8 of V with a scale per channel: a column-maximum pass (partial
 //           maxima of 256-row chunks lowered into the scale buffer by atomic
 //           max on the float bits), a quantize pass that writes the codes
@@ -152,8 +152,10 @@ __global__ __launch_bounds__(kThreads) void qquant_kernel(const float* q, int8_t
     float x[kTile];
     float mx = 0.0f;
 #pragma unroll
+    for (int t = 0; t < kTile; ++t) x[t] = q[(row0 + t) * m.d + min(c, m.d - 1)];   // unconditional
+#pragma unroll
     for (int t = 0; t < kTile; ++t) {
-      x[t] = c < m.d ? q[(row0 + t) * m.d + c] : 0.0f;
+      x[t] = c < m.d ? x[t] : 0.0f;
       mx = fmaxf(mx, fabsf(x[t]));
     }
     const int pot = pot_of(mx, base);
@@ -163,17 +165,32 @@ __global__ __launch_bounds__(kThreads) void qquant_kernel(const float* q, int8_t
   }
 }
 
+// One wave per kKRows consecutive key rows: every row's loads are issued
+// before the first maximum is taken (one row per wave left each wave with a
+// single row's latency to hide).
+constexpr int kKRows = 8;
 __global__ __launch_bounds__(kThreads) void kquant_kernel(const float* k, int8_t* kc, float* ks, Dims m) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (row >= m.BH * m.L) return;
-  const float x0 = lane < m.d ? k[row * m.d + lane] : 0.0f;
-  const float x1 = lane + 64 < m.d ? k[row * m.d + lane + 64] : 0.0f;
-  const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
-  const float s = (float)((double)amax / 127.0);
-  if (lane < m.dp) kc[row * m.dp + lane] = (int8_t)code_w(x0, s);
-  if (lane + 64 < m.dp) kc[row * m.dp + lane + 64] = (int8_t)code_w(x1, s);
-  if (lane == 0) ks[row] = s;
+  const int64_t row0 = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * kKRows;
+  const int64_t rows = m.BH * m.L;
+  if (row0 >= rows) return;
+  float x0[kKRows], x1[kKRows];
+#pragma unroll
+  for (int i = 0; i < kKRows; ++i) {
+    const int64_t row = min(row0 + i, rows - 1);   // rows past the end are never stored
+    x0[i] = lane < m.d ? k[row * m.d + lane] : 0.0f;
+    x1[i] = lane + 64 < m.d ? k[row * m.d + lane + 64] : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < kKRows; ++i) {
+    const int64_t row = row0 + i;
+    if (row >= rows) break;
+    const float amax = wave_max(fmaxf(fabsf(x0[i]), fabsf(x1[i])));
+    const float s = (float)((double)amax / 127.0);
+    if (lane < m.dp) kc[row * m.dp + lane] = (int8_t)code_w(x0[i], s);
+    if (lane + 64 < m.dp) kc[row * m.dp + lane + 64] = (int8_t)code_w(x1[i], s);
+    if (lane == 0) ks[row] = s;
+  }
 }
 
 __global__ void vinit_kernel(uint32_t* bits, int64_t n) {
@@ -194,8 +211,17 @@ __global__ __launch_bounds__(kThreads) void vmax_kernel(const float* v, uint32_t
   for (int cc = 0; cc < 2; ++cc) {
     const int c = lane + 64 * cc;
     float mx = 0.0f;
-    if (c < m.d)
-      for (int r = ch * kVChunk + rg; r < r_end; r += kWaves) mx = fmaxf(mx, fabsf(v[(bh * m.L + r) * m.d + c]));
+    if (c < m.d) {
+      // sixteen rows' loads in flight per step
+      for (int r = ch * kVChunk + rg; r < r_end; r += 16 * kWaves) {
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)   // unconditional (clamped row), so all are in flight
+          x[i] = v[(bh * m.L + min(r + i * kWaves, r_end - 1)) * m.d + c];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, r + i * kWaves < r_end ? fabsf(x[i]) : 0.0f);
+      }
+    }
     part[rg][c] = mx;
   }
   __syncthreads();
@@ -222,12 +248,12 @@ __global__ __launch_bounds__(kThreads) void vquant_kernel(const float* v, const 
     if (c >= m.dp) break;
     const float s = c < m.d ? (float)((double)__uint_as_float(vmax[bh * m.d + c]) / 127.0) : 0.0f;
     uint32_t w[4] = {0u, 0u, 0u, 0u};
+    float x[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t key = (int64_t)kc * 64 + 16 * q4 + i;
-      const float x = c < m.d ? v[(bh * m.L + key) * m.d + c] : 0.0f;
-      w[i / 4] |= ((uint32_t)code_w(x, s) & 0xFFu) << (8 * (i % 4));
-    }
+    for (int i = 0; i < 16; ++i)   // unconditional (clamped channel; s = 0 gives code 0 there)
+      x[i] = v[(bh * m.L + (int64_t)kc * 64 + 16 * q4 + i) * m.d + min(c, m.d - 1)];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i / 4] |= ((uint32_t)code_w(x[i], s) & 0xFFu) << (8 * (i % 4));
     *reinterpret_cast<uint4*>(vct + (bh * m.dp + c) * m.L + (int64_t)kc * 64 + 16 * q4) =
         make_uint4(w[0], w[1], w[2], w[3]);
   }
@@ -390,7 +416,10 @@ __device__ __forceinline__ void sweep_blocks(const ScoreArgs& a, int64_t bh, int
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) B[ct][ks] = Bn[ct][ks];
     }
-    if (kPrefetch && j + 1 < j1) fetch(j + 1);
+    if (kPrefetch) {
+      fetch(min(j + 1, j1 - 1));   // unconditional: a constant load count
+      __asm__ __volatile__("" ::: "memory");   // issue it here, not where it is used
+    }
     if (kb < 0 || kb >= a.m.nb) continue;
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
@@ -459,7 +488,9 @@ template <int NKS>
 __global__ __launch_bounds__(kThreads, 2) void scores_kernel(ScoreArgs a) {
   const int lane = threadIdx.x & 63, li = lane & 31, hi = lane >> 5;
   const int tpb = a.m.L / kTile;
-  const int64_t tile = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  // wave-uniform (readfirstlane): the index and mask loads below become
+  // scalar loads, which the vector-load counts do not include
+  const int64_t tile = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWaves + (threadIdx.x >> 6)));
   if (tile >= a.m.BH * tpb) return;
   const int64_t bh = tile / tpb;
   const int tau = (int)(tile % tpb);
@@ -536,18 +567,22 @@ __device__ __forceinline__ void pv_pass(const PvArgs& a, int64_t bh, int tau, in
   if (j0 < j1) fetch(j0);
   for (int j = j0; j < j1; ++j) {
     const int kb = a.cols[j];
+    const bool valid = kb >= 0 && kb < a.m.nb;
     const v4i cw0 = cn[0], cw1 = cn[1], pw0 = pn[0], pw1 = pn[1];
-    if (j + 1 < j1) fetch(j + 1);
-    if (kb < 0 || kb >= a.m.nb) continue;
+    // V fragments of this block first, then the next block's P: vector loads
+    // complete in order, so waiting for V leaves the prefetch in flight.
     v4i Bv[CG][2];
+    const int kbc = valid ? kb : 0;
 #pragma unroll
     for (int c = 0; c < CG; ++c) {
-      if (c < ncg) {
-        const int8_t* vrow = vbh + (int64_t)(32 * (ct0 + c)) * a.m.L + (int64_t)kb * kBlock;
-        Bv[c][0] = *reinterpret_cast<const v4i*>(vrow);
-        Bv[c][1] = *reinterpret_cast<const v4i*>(vrow + 32);
-      }
+      const int8_t* vrow = vbh + (int64_t)(32 * (ct0 + min(c, ncg - 1))) * a.m.L + (int64_t)kbc * kBlock;
+      Bv[c][0] = *reinterpret_cast<const v4i*>(vrow);
+      Bv[c][1] = *reinterpret_cast<const v4i*>(vrow + 32);
     }
+    __asm__ __volatile__("" ::: "memory");
+    fetch(min(j + 1, j1 - 1));   // unconditional: a constant load count
+    __asm__ __volatile__("" ::: "memory");
+    if (!valid) continue;
     v4i A0[NP], A1[NP];
     digits_np<NP>(cw0, pw0, A0);
     digits_np<NP>(cw1, pw1, A1);
@@ -595,7 +630,9 @@ template <int NCT>
 __global__ __launch_bounds__(kThreads, 2) void pv_kernel(PvArgs a) {
   const int lane = threadIdx.x & 63;
   const int tpb = a.m.L / kTile;
-  const int64_t tile = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  // wave-uniform (readfirstlane): the index and mask loads below become
+  // scalar loads, which the vector-load counts do not include
+  const int64_t tile = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWaves + (threadIdx.x >> 6)));
   if (tile >= a.m.BH * tpb) return;
   const int64_t bh = tile / tpb;
   const int tau = (int)(tile % tpb);
@@ -605,10 +642,16 @@ __global__ __launch_bounds__(kThreads, 2) void pv_kernel(PvArgs a) {
   block_range(a.row_ptr, (int64_t)h * a.m.nb + qb, a.nnz, j0, j1);
 
   int pmax = 0;
-  for (int j = j0; j < j1; ++j) {
-    const int kb = a.cols[j];
-    if (kb < 0 || kb >= a.m.nb) continue;
-    pmax = max(pmax, (int)a.ppot[(((int64_t)b * a.nnz + j) * 2 + half) * kBlock + lane]);
+  for (int j = j0; j < j1; j += 8) {
+    int pt[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)   // eight loads in flight (indices clamped, extras ignored)
+      pt[i] = a.ppot[(((int64_t)b * a.nnz + min(j + i, j1 - 1)) * 2 + half) * kBlock + lane];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int kb = a.cols[min(j + i, j1 - 1)];
+      if (j + i < j1 && kb >= 0 && kb < a.m.nb) pmax = max(pmax, pt[i]);
+    }
   }
   const int np = planes_for(min(wave_max_i(pmax), 31));
   if (np <= 2)
@@ -687,8 +730,8 @@ int dstar_sar_quantize_k(const dstar_sar_params* p, const float* k, int8_t* kcod
   if (int rc = check(p)) return rc;
   if (int rc = check_ptrs({{k, 4}, {kcodes, 16}, {kscale, 4}})) return rc;
   const Dims m = dims_of(p);
-  hipLaunchKernelGGL(kquant_kernel, dim3(waves_grid(m.BH * m.L)), dim3(kThreads), 0, (hipStream_t)stream, k, kcodes,
-                     kscale, m);
+  hipLaunchKernelGGL(kquant_kernel, dim3(waves_grid((m.BH * m.L + kKRows - 1) / kKRows)), dim3(kThreads), 0,
+                     (hipStream_t)stream, k, kcodes, kscale, m);
   return check_launch("sar_quantize_k");
 }
 
