@@ -76,16 +76,30 @@ def src_sha(stage: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(stage: str, grid: int):
-    """Calibrated HBM bytes per launch of a stage's kernel at a grid size, from
-    the committed counter summary; None if there is none or the kernel source
-    changed since the counters were taken."""
+def layer_keys(dispatches):
+    """dispatches: (dispatch id, kernel name, grid).  Returns {dispatch id:
+    grid of the next stage-3 launch} (a stage-3 launch keys itself): stages 1
+    and 2 launch with the same grid at fc1 and fc2, so a launch is attributed
+    to its layer by the stage-3 launch that follows it."""
+    out, nxt = {}, None
+    for did, name, grid in sorted(dispatches, key=lambda x: -x[0]):
+        if KERNEL_NAME["linear"] in name:
+            nxt = grid
+        out[did] = nxt
+    return out
+
+
+def measured_traffic(stage: str, layer_grid: int):
+    """Calibrated HBM bytes per launch of a stage's kernel in the layer whose
+    stage-3 launch grid is layer_grid, from the committed counter summary;
+    None if there is none or the kernel source changed since the counters
+    were taken."""
     if not os.path.exists(TRAFFIC_MD):
         return None
     for line in open(TRAFFIC_MD):
         f = [c.strip() for c in line.strip().strip("|").split("|")]
-        if len(f) >= 7 and f[0] == stage and f[1] == str(grid) and f[2] == src_sha(stage):
-            return int(float(f[6]))
+        if len(f) >= 8 and f[0] == stage and f[1] == str(layer_grid) and f[3] == src_sha(stage):
+            return int(float(f[7]))
     return None
 
 
@@ -105,15 +119,22 @@ def write_traffic(fetch_dir: str, write_dir: str) -> None:
                              if r["Counter_Name"] == counter]
         per = {}
         for r in rows:
-            key = (r["Kernel_Name"], int(r["Grid_Size"]), r["Dispatch_Id"])
+            key = (r["Kernel_Name"], int(r["Grid_Size"]), int(r["Dispatch_Id"]))
             per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
         return per
 
     fetch, write = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
 
+    lay = {w: layer_keys([(did, n, g) for (n, g, did) in per]) for w, per in (("fetch", fetch), ("write", write))}
+
     def mean(per, pred):
         v = [x for (name, grid, _), x in per.items() if pred(name, grid)]
         return sum(v) / len(v) if v else None
+
+    def mean_layer(per, which, kname, lg):
+        v = [x for (name, grid, did), x in per.items() if kname in name and lay[which][did] == lg]
+        return (sum(v) / len(v), sorted({grid for (name, grid, did) in per if kname in name and
+                                         lay[which][did] == lg})) if v else (None, [])
 
     # the calibration copy is the largest device copy of the run
     cal_grid = max((g for (n, g, _) in write if "copyBuffer" in n), default=None)
@@ -135,17 +156,20 @@ def write_traffic(fetch_dir: str, write_dir: str) -> None:
              "python bench.py --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write",
              "```",
              "",
-             "| stage | grid | source | fetch KiB | write KiB | scale | bytes per launch |",
-             "|---|---|---|---|---|---|---|"]
+             "Launches are attributed to their layer by the stage-3 launch that follows them (stages 1 and 2",
+             "launch with the same grid at fc1 and fc2); the layer is named by its stage-3 launch grid.",
+             "",
+             "| stage | layer (stage-3 grid) | launch grid | source | fetch KiB | write KiB | scale | bytes per launch |",
+             "|---|---|---|---|---|---|---|---|"]
+    layer_grids = sorted({g for (n, g, _) in fetch if KERNEL_NAME["linear"] in n})
     for stage, kname in KERNEL_NAME.items():
-        grids = sorted({g for (n, g, _) in fetch if kname in n})
-        for g in grids:
-            fk = mean(fetch, lambda n, gg: kname in n and gg == g)
-            wk = mean(write, lambda n, gg: kname in n and gg == g)
+        for lg in layer_grids:
+            fk, g1 = mean_layer(fetch, "fetch", kname, lg)
+            wk, _ = mean_layer(write, "write", kname, lg)
             if fk is None or wk is None:
                 continue
             b = fk * sf * 1024 + wk * sw * 1024
-            lines.append(f"| {stage} | {g} | {src_sha(stage)} | {fk:.0f} | {wk:.0f} | "
+            lines.append(f"| {stage} | {lg} | {'/'.join(map(str, g1))} | {src_sha(stage)} | {fk:.0f} | {wk:.0f} | "
                          f"{sf:.4f}/{sw:.4f} | {b:.0f} |")
     with open(TRAFFIC_MD, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -229,16 +253,23 @@ def write_kernel_summary(trace_dir: str, which: str = "linear") -> None:
                      f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
     per = {}
+    grid_of = lambda r: int(r.get("Grid_Size") or r.get("Grid_Size_X") or 0)
+    lay = layer_keys([(int(r["Dispatch_Id"]), r.get("Kernel_Name", ""), grid_of(r)) for r in trace])
     for r in trace:
         name = r.get("Kernel_Name", "")
-        grid = r.get("Grid_Size") or r.get("Grid_Size_X") or "?"
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        per.setdefault((name, grid), []).append(dur)
-    lines += ["", "Per kernel and launch grid (threads), from the trace:", "",
-              "| kernel | grid | calls | mean us | min us | max us |", "|---|---|---|---|---|---|"]
-    for (name, grid), v in sorted(per.items(), key=lambda x: -sum(x[1])):
+        lg = lay[int(r["Dispatch_Id"])] if which == "linear" else None
+        per.setdefault((name, grid_of(r), lg), []).append(dur)
+    lines += ["", "Per kernel and launch grid (threads), from the trace" +
+              (" (launches attributed to their layer by the stage-3 launch that follows them: stages 1 and 2"
+               " launch with the same grid at fc1 and fc2):" if which == "linear" else ":"), "",
+              "| kernel | grid | layer (stage-3 grid) | calls | mean us | min us | max us |",
+              "|---|---|---|---|---|---|---|"]
+    for (name, grid, lg), v in sorted(per.items(), key=lambda x: -sum(x[1])):
         short = name.replace("dstar::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
-        lines.append(f"| `{short}` | {grid} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
+        short = short if len(short) <= 80 else short[:80] + "..."
+        lines.append(f"| `{short}` | {grid} | {lg if lg is not None else '-'} | {len(v)} | {sum(v) / len(v):.1f} | "
+                     f"{min(v):.1f} | {max(v):.1f} |")
     out = os.path.join(ROOT, "profiles", fname)
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -674,7 +705,7 @@ def main() -> int:
             t_hbm = alg["bytes"] / (HBM_PEAK_GBS * 1e9)
             t_mfma = alg["ops"] / (INT8_PEAK_TOPS * 1e12) if alg["ops"] else 0.0
             bound = "mfma" if t_mfma > t_hbm else "hbm"
-            traffic = measured_traffic(s, grids[L][s])
+            traffic = measured_traffic(s, grids[L]["linear"])
             kernels[f"{s}@{L}"] = dict(
                 us_mean=us, us_p10=float(np.percentile(per[L][s], 10)),
                 us_p90=float(np.percentile(per[L][s], 90)), alg_bytes=alg["bytes"],
