@@ -487,7 +487,8 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   // ---- Epilogue set-up.  Y is streamed once: its loads and stores are
   // non-temporal so they do not evict W and the codes from the caches.  In
   // interior blocks the epilogue runs over (32-row block, 32-column block)
-  // units, loading the next unit's Y_{t−1} before storing the current one.
+  // units, loading the Y_{t−1} of the two next units before storing the
+  // current one.
   // Offsets are 32-bit, relative to this workgroup's first row.
   const double base = a.base_dev != nullptr ? (double)*a.base_dev : a.base;
   bool all_eligible = true;
@@ -504,7 +505,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   auto y_off = [&](int rb, int cb, int r) {
     return lane_off + (uint32_t)(32 * rb + 8 * (r >> 2) + (r & 3)) * row4 + 128 * cb;
   };
-  float ypa[16], ypb[16];
+  float ypa[16], ypb[16], ypc[16];
   auto load_y = [&](float (&dst)[16], int rb, int cb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
@@ -656,13 +657,16 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     ws[cb] = n < N ? (double)a.w_scale[n] : 0.0;
   }
   if (interior) {
+    // three buffers: the loads of the two next units are in flight while
+    // one unit is combined and stored
     load_y(ypa, 0, 0);
+    load_y(ypb, 1 / CB, 1 % CB);
 #pragma unroll
     for (int v = 0; v < RB * CB; ++v) {
       const int rb = v / CB, cb = v % CB;
-      float (&cur)[16] = (v & 1) ? ypb : ypa;
-      float (&nxt)[16] = (v & 1) ? ypa : ypb;
-      if (v + 1 < RB * CB) load_y(nxt, (v + 1) / CB, (v + 1) % CB);
+      float (&cur)[16] = v % 3 == 0 ? ypa : v % 3 == 1 ? ypb : ypc;
+      float (&nxt)[16] = v % 3 == 0 ? ypc : v % 3 == 1 ? ypa : ypb;
+      if (v + 2 < RB * CB) load_y(nxt, (v + 2) / CB, (v + 2) % CB);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const double d = __dmul_rn(__dmul_rn((double)acc[rb][cb][r], base), ws[cb]);
