@@ -78,12 +78,16 @@ __device__ __forceinline__ float exp32(float x) {
   return ldexpf(p, (int)n);
 }
 
-// PoT: the number of bin edges base·2^j (j = 0..20) strictly below m.
+// PoT: the number of bin edges base·2^j (j = 0..20) strictly below m, i.e.
+// the smallest j in [0, 21] with m ≤ base·2^j (21 if none).  For m ≥ 0 and a
+// normal base it follows from the float fields: with m = 1.f_m·2^e_m and
+// base = 1.f_b·2^e_b, m ≤ base·2^j holds exactly when j ≥ e_m − e_b + [f_m >
+// f_b]; zero and subnormal m give j ≤ 0.  Equal to the 21 compares for every
+// non-negative float and every base in [2^-100, 2^100].
 __device__ __forceinline__ int pot_of(float m, float base) {
-  int pot = 0;
-#pragma unroll
-  for (int j = 0; j < kPotMax; ++j) pot += (m > ldexpf(base, j)) ? 1 : 0;
-  return pot;
+  const uint32_t bm = __float_as_uint(m), bb = __float_as_uint(base);
+  const int j = (int)(bm >> 23) - (int)(bb >> 23) + ((bm & 0x7FFFFFu) > (bb & 0x7FFFFFu) ? 1 : 0);
+  return min(max(j, 0), kPotMax);
 }
 
 // FMDQ-INT8 code of x in a sub-channel of this PoT.
