@@ -61,10 +61,11 @@ constexpr int kWaves = kThreads / 64;
 constexpr float kLog2e = 0x1.715476p+0f;
 constexpr float kLn2Hi = 0x1.63p-1f;
 constexpr float kLn2Lo = -0x1.bd0106p-13f;
-constexpr float kExpXMin = -26.0f;
 
-__device__ __forceinline__ float exp32(float x) {
-  if (x < kExpXMin) return 0.0f;
+// exp32 without its final power of two: e^x = p·2^n (Cody–Waite reduction,
+// then the Taylor polynomial of e^r by Horner's rule, each step rounded to
+// float32).  Branch-free; see exp_fixed_d for the cut-off.
+__device__ __forceinline__ float exp32_poly(float x, int& n_out) {
   const float n = rintf(__fmul_rn(x, kLog2e));
   const float r = __fsub_rn(__fsub_rn(x, __fmul_rn(n, kLn2Hi)), __fmul_rn(n, kLn2Lo));
   float p = 0x1.a01a02p-13f;                       // 1/5040
@@ -75,7 +76,8 @@ __device__ __forceinline__ float exp32(float x) {
   p = __fadd_rn(__fmul_rn(p, r), 0.5f);
   p = __fadd_rn(__fmul_rn(p, r), 1.0f);
   p = __fadd_rn(__fmul_rn(p, r), 1.0f);
-  return ldexpf(p, (int)n);
+  n_out = (int)n;
+  return p;
 }
 
 // PoT: the number of bin edges base·2^j (j = 0..20) strictly below m, i.e.
@@ -372,10 +374,17 @@ __device__ __forceinline__ void tile_logits(const v4i (&A)[NKS][NP], const v4i (
   }
 }
 
-// E = rint(exp32(x)·2^36) as a double: e ≤ 1 and the scaled value is exact,
-// so E is an integer below 2^37 and sums of up to 2^16 of them stay exact.
+// E = rint(exp32(x)·2^36) as a double, x ≤ 0.  For x ≥ −26 (the cut-off),
+// exp32(x) = p·2^n is a normal float (n ≥ −38), so e·2^36 = p·2^(n+36) is
+// formed exactly in float32 (at most 2^36, as e ≤ 1) and its float32 rint is
+// the integer E.  Below the cut-off exp32 is 0, and so is this: e^x·2^36 <
+// 0.36 there, p·2^(n+36) is that within a few ulps (or flushes to 0 for very
+// negative x), and rint gives 0; no clamp or select is needed.  E ≤ 2^36, so
+// sums of up to 2^16 of them stay exact in float64.
 __device__ __forceinline__ double exp_fixed_d(float x) {
-  return rint(ldexp((double)exp32(x), DSTAR_SAR_EXP_FRAC));
+  int n;
+  const float p = exp32_poly(x, n);
+  return (double)rintf(ldexpf(p, n + DSTAR_SAR_EXP_FRAC));
 }
 
 __device__ __forceinline__ double half_sum_d(double v) {
