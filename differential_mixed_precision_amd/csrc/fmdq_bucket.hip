@@ -102,11 +102,20 @@ __global__ __launch_bounds__(kBallotThreads) void bucket_ballot_kernel(BucketArg
   const uint64_t below = (1ull << lane) - 1ull;
   const int per = (E + kBallotThreads - 1) / kBallotThreads;   // scan entries per thread
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+  // Tags in 4-byte words and ids in 16-byte pieces when every tile's row is
+  // so aligned (the staging buffers in LDS always are).
+  const bool tags4 = ((reinterpret_cast<uintptr_t>(a.tags) | (uintptr_t)K) & 3u) == 0;
+  const bool perm16 = ((reinterpret_cast<uintptr_t>(a.perm) | (uintptr_t)(2 * K)) & 15u) == 0;
 
   for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
     const uint8_t* tg = a.tags + tile * (int64_t)K;
     uint16_t* out = a.perm + tile * (int64_t)K;
-    for (int i = tid; i < K; i += kBallotThreads) tags_s[i] = tg[i];
+    if (tags4) {
+      for (int i = tid; i < K / 4; i += kBallotThreads)
+        reinterpret_cast<uint32_t*>(tags_s)[i] = reinterpret_cast<const uint32_t*>(tg)[i];
+    } else {
+      for (int i = tid; i < K; i += kBallotThreads) tags_s[i] = tg[i];
+    }
     for (int i = tid; i < epad / 8; i += kBallotThreads) reinterpret_cast<uint4*>(cnt)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
     for (int c = wave; c < C; c += kBallotThreads / 64) {
@@ -148,7 +157,12 @@ __global__ __launch_bounds__(kBallotThreads) void bucket_ballot_kernel(BucketArg
       if (act) perm_s[cnt[bin * C + c] + __popcll(peers & below)] = (uint16_t)k;
     }
     __syncthreads();
-    for (int i = tid; i < K; i += kBallotThreads) out[i] = perm_s[i];
+    if (perm16) {
+      for (int i = tid; i < K / 8; i += kBallotThreads)
+        reinterpret_cast<uint4*>(out)[i] = reinterpret_cast<const uint4*>(perm_s)[i];
+    } else {
+      for (int i = tid; i < K; i += kBallotThreads) out[i] = perm_s[i];
+    }
     __syncthreads();
   }
 }
