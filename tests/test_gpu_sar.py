@@ -222,3 +222,58 @@ def test_sar_full_size_sampled_heads(dm):
         np.testing.assert_array_equal(g["ppot"][b, j0:j1], r["ppot"][0])
         np.testing.assert_array_equal(g["o"][sl], r["o"])
         np.testing.assert_array_equal(g["o_reused"][sl], u["o"])
+
+
+def test_sar_out_of_range_columns_are_ignored(dm):
+    """Compressed-row entries outside [0, L/64) are skipped, as the header
+    says: O, and the cache of every valid block, equal the oracle's on the mask
+    without them; the cache entries of the skipped blocks are not written."""
+    import torch
+    dev = torch.device("cuda:0")
+    B, H, L, dd = 1, 2, 256, 72
+    nb = L // 64
+    d = ga.make_attention(B, H, L, dd, 0.63, seed=17)
+    row_ptr, cols = sar.mask_to_csr(d["mask"])
+    rows = [list(cols[row_ptr[r]:row_ptr[r + 1]]) for r in range(H * nb)]
+    rows[1] = [-1] + rows[1]                 # before the first kept block
+    rows[5] = rows[5] + [nb + 3]             # after the last one
+    rows[7] = rows[7] + [1000, 1 << 30]
+    new_ptr = np.zeros(H * nb + 1, dtype=np.int32)
+    new_ptr[1:] = np.cumsum([len(r) for r in rows])
+    new_cols = np.array([c for r in rows for c in r], dtype=np.int32)
+    valid = (new_cols >= 0) & (new_cols < nb)
+    assert (~valid).sum() == 4 and valid.sum() == len(cols)
+    nnz = len(new_cols)
+    dp = dm.sar_padded_dim(dd)
+    p = dm._binding.make_sar_params(B, H, L, dd, float(d["base_q"]), float(d["base_p"]), float(d["sm_scale"]))
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q, k, v, vn = t(d["q"]), t(d["k"]), t(d["v"]), t(d["v_next"])
+    qc = torch.empty((B * H, L, dp), dtype=torch.int8, device=dev)
+    qp = torch.empty((B * H, L // 32, dp), dtype=torch.uint8, device=dev)
+    kc = torch.empty((B * H, L, dp), dtype=torch.int8, device=dev)
+    ks = torch.empty((B * H, L), dtype=torch.float32, device=dev)
+    vc = torch.empty((B * H, dp, L), dtype=torch.int8, device=dev)
+    vs = torch.empty((B * H, dd), dtype=torch.float32, device=dev)
+    pc = torch.full((B, nnz, 64, 64), 93, dtype=torch.int8, device=dev)
+    pp = torch.full((B, nnz, 2, 64), 0xAB, dtype=torch.uint8, device=dev)
+    out = torch.full((B * H, L, dd), float("nan"), dtype=torch.float32, device=dev)
+    rp, cl = t(new_ptr), t(new_cols)
+    log(f"  gpu cached step with {nnz - len(cols)} out-of-range column entries")
+    dm.sar_quantize_q(p, q, qc, qp)
+    dm.sar_quantize_k(p, k, kc, ks)
+    dm.sar_quantize_v(p, v, vc, vs)
+    dm.sar_scores(p, rp, cl, nnz, qc, qp, kc, ks, pc, pp)
+    dm.sar_pv(p, rp, cl, nnz, pc, pp, vc, vs, out)
+    torch.cuda.synchronize()
+    g_out, g_pc, g_pp = out.cpu().numpy().copy(), pc.cpu().numpy(), pp.cpu().numpy()
+    dm.sar_quantize_v(p, vn, vc, vs)
+    dm.sar_pv(p, rp, cl, nnz, pc, pp, vc, vs, out)
+    torch.cuda.synchronize()
+    g_reused = out.cpu().numpy()
+    r = sar.cached_step(d["q"], d["k"], d["v"], row_ptr, cols, H, d["base_q"], d["sm_scale"], d["base_p"])
+    u = sar.reused_step(r["pcodes"], r["ppot"], d["v_next"], row_ptr, cols, H, d["base_p"])
+    np.testing.assert_array_equal(g_out, r["o"])
+    np.testing.assert_array_equal(g_reused, u["o"])
+    np.testing.assert_array_equal(g_pc[:, valid], r["pcodes"])
+    np.testing.assert_array_equal(g_pp[:, valid], r["ppot"])
+    assert (g_pc[:, ~valid] == 93).all() and (g_pp[:, ~valid] == 0xAB).all()
