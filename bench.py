@@ -22,8 +22,8 @@ Traffic summary from two counter runs of this same command (run from the
 repository root; a plain 256 MiB device copy made before timing calibrates
 the counters):
 
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention
-    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention --no-cold
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention --no-cold
     python bench.py --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write
 """
 from __future__ import annotations
@@ -146,13 +146,13 @@ def write_traffic(fetch_dir: str, write_dir: str) -> None:
     lines = ["# HBM traffic per launch, FMDQ differential linear, PixArt-alpha-style 1024px MLP",
              "",
              "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, rocprofv3 --pmc, one run each) of",
-             "`python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention` on one MI355X, scaled by what they read",
+             "`python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention --no-cold` on one MI355X, scaled by what they read",
              f"for a plain {CAL_BYTES >> 20} MiB device copy made in the same run (fetch x{sf:.4f}, write x{sw:.4f}).",
              "Commands:",
              "",
              "```",
-             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention",
-             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention",
+             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention --no-cold",
+             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention --no-cold",
              "python bench.py --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write",
              "```",
              "",
@@ -552,6 +552,7 @@ def main() -> int:
     ap.add_argument("--no-chain", action="store_true", help="skip the fc1 -> GELU -> fc2 timestep chain")
     ap.add_argument("--no-slices", action="store_true", help="skip timing the 2-bit slice stream")
     ap.add_argument("--no-attention", action="store_true", help="skip the SAR attention workload")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache pass")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--write-kernel-summary", metavar="TRACE_DIR")
     ap.add_argument("--summary", choices=sorted(SUMMARIES), default="linear",
@@ -674,6 +675,35 @@ def main() -> int:
             ev = events[i][L]
             for j, s in enumerate(STAGES):
                 per[L][s].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)   # microseconds
+    # Cold runs: before each layer a 512 MiB write evicts the 256 MB
+    # Infinity Cache (and the L2s), so every operand comes from HBM.
+    cold_reps = 0 if args.no_cold else 5
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold_ev = [{L: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for L in layers}
+               for _ in range(cold_reps)]
+    for i in range(cold_reps):
+        for L in layers:
+            flush.fill_(i + 1)
+            sl = state[L]
+            x_t, x_p = sl["xs"][i % len(sl["xs"])]
+            lay, ev = sl["layer"], cold_ev[i][L]
+            ev[0].record(stream)
+            dm.quantize(lay.p, x_t, x_p, lay.codes, lay.tags, lay.acodes, lay.hcodes, lay.bit_hist)
+            ev[1].record(stream)
+            dm.bucket(lay.p, lay.tags, lay.perm, lay.group_off)
+            ev[2].record(stream)
+            dm.linear(lay.p, sl["N"], lay.codes, lay.perm, lay.group_off, lay.acodes, lay.hcodes, lay.w,
+                      lay.w_t, lay.w_scale, sl["y"], sl["y"])
+            ev[3].record(stream)
+    torch.cuda.synchronize()
+    del flush
+    cold = {}
+    for L in layers:
+        for j, s_ in enumerate(STAGES):
+            v = [cold_ev[i][L][j].elapsed_time(cold_ev[i][L][j + 1]) * 1e3 for i in range(cold_reps)]
+            if v:
+                cold[f"{s_}@{L}"] = {"us_median": float(np.median(v)), "us_mean": float(np.mean(v))}
+    cold_ms = sum(v["us_median"] for v in cold.values()) / 1e3
     ms_per_step = wall * 1e3 / args.steps
     total_ops = sum(2 * rows * state[L]["N"] * state[L]["K"] for L in layers)
     value = total_ops / (ms_per_step * 1e-3) / 1e12
@@ -707,7 +737,7 @@ def main() -> int:
             bound = "mfma" if t_mfma > t_hbm else "hbm"
             traffic = measured_traffic(s, grids[L]["linear"])
             kernels[f"{s}@{L}"] = dict(
-                us_mean=us, us_p10=float(np.percentile(per[L][s], 10)),
+                us_mean=us, us_median=float(np.median(per[L][s])), us_p10=float(np.percentile(per[L][s], 10)),
                 us_p90=float(np.percentile(per[L][s], 90)), alg_bytes=alg["bytes"],
                 alg_ops=alg["ops"], gbs=gbs, tops=tops, bound=bound,
                 frac=(tops / INT8_PEAK_TOPS) if bound == "mfma" else gbs / HBM_PEAK_GBS,
@@ -739,6 +769,9 @@ def main() -> int:
                    "rows": rows, "token_tile": T, "thr0_log2": wl.DEFAULT_K0,
                    "pairs_cycled": args.pairs},
         "layers": layer_out, "kernels": kernels, "roofline": roof,
+        "cold": None if not cold else {
+            "note": "eager, 512 MiB write before each layer (caches flushed); medians of 5",
+            "ms_per_step": cold_ms, "tops": total_ops / (cold_ms * 1e-3) / 1e12, "kernels": cold},
     }
     if not args.no_slices:
         print("[bench] 2-bit slice stream", file=sys.stderr, flush=True)
