@@ -22,9 +22,9 @@ Traffic summary from two counter runs of this same command (run from the
 repository root; a plain 256 MiB device copy made before timing calibrates
 the counters):
 
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention --no-cold
-    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention --no-cold
-    python bench.py --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention --no-cold
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention --no-cold
+    python bench.py --write-traffic OUT/pmc_fetch OUT/pmc_write
 """
 from __future__ import annotations
 
@@ -51,6 +51,8 @@ KERNEL_SRC = {"quantize": ["fmdq_quantize.hip"], "bucket": ["fmdq_bucket.hip"],
 KERNEL_NAME = {"quantize": "quantize_kernel", "bucket": "bucket_", "linear": "linear_mfma_kernel"}
 CAL_BYTES = 256 << 20     # the calibration copy
 TRAFFIC_MD = os.path.join(ROOT, "profiles", "stage_traffic_pixart1024.md")
+# bench.py arguments of the counter runs (the static step only)
+PMC_ARGS = "--steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention --no-cold"
 
 
 def algorithmic(stage: str, rows: int, K: int, N: int, T: int) -> dict:
@@ -146,14 +148,14 @@ def write_traffic(fetch_dir: str, write_dir: str) -> None:
     lines = ["# HBM traffic per launch, FMDQ differential linear, PixArt-alpha-style 1024px MLP",
              "",
              "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, rocprofv3 --pmc, one run each) of",
-             "`python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention --no-cold` on one MI355X, scaled by what they read",
+             f"`python3 bench.py {PMC_ARGS}` on one MI355X, scaled by what they read",
              f"for a plain {CAL_BYTES >> 20} MiB device copy made in the same run (fetch x{sf:.4f}, write x{sw:.4f}).",
              "Commands:",
              "",
              "```",
-             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention --no-cold",
-             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention --no-cold",
-             "python bench.py --write-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write",
+             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- python3 bench.py {PMC_ARGS}",
+             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- python3 bench.py {PMC_ARGS}",
+             f"python bench.py --write-traffic {fetch_dir} {write_dir}",
              "```",
              "",
              "Launches are attributed to their layer by the stage-3 launch that follows them (stages 1 and 2",
@@ -237,9 +239,9 @@ def write_kernel_summary(trace_dir: str, which: str = "linear") -> None:
              "Command (from the repository root), then the summary:",
              "",
              "```",
-             f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_{which} -o run -- \\",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o run -- \\",
              f"    {cmd}",
-             f"python bench.py --write-kernel-summary gpurun_out/prof_{which} --summary {which}",
+             f"python bench.py --write-kernel-summary {trace_dir} --summary {which}",
              "```",
              "",
              stats_note,
