@@ -466,6 +466,42 @@ def library_gemm(torch, layers: dict, rows: int, reps: int = 20) -> dict:
     return out
 
 
+def measured_peaks(torch) -> dict:
+    """The two ceilings re-measured on this GPU: HBM bandwidth of a plain
+    1 GiB device copy (bytes read + written over time) and the dense int8
+    rate of the vendor library's GEMM on a square 8192^3 product."""
+    dev = torch.device("cuda:0")
+    out = {}
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    out["hbm_copy_gbs"] = 2 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3 / 10) / 1e9
+    del src, dst
+    try:
+        n = 8192
+        a = torch.randint(-127, 128, (n, n), dtype=torch.int8, device=dev)
+        b = torch.randint(-127, 128, (n, n), dtype=torch.int8, device=dev).t()
+        for _ in range(2):
+            torch._int_mm(a, b)
+        e0.record()
+        for _ in range(5):
+            torch._int_mm(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        out["int8_gemm_8192_tops"] = 2 * n ** 3 / (e0.elapsed_time(e1) * 1e-3 / 5) / 1e12
+    except RuntimeError as ex:               # not every build exposes it
+        out["int8_gemm_8192_tops"] = None
+        out["error"] = str(ex)[:200]
+    return out
+
+
 def sar_attention(dm, torch, stream, reps: int = 10) -> dict:
     """Sparse Attention Reuse with FMDQ-INT8 operands (DSTAR §3.2 Fig. 8,
     §4.3 Fig. 13) on the PixArt-alpha 1024px self-attention shape: 2 images x
@@ -748,6 +784,11 @@ def main() -> int:
         layer_out[L] = dict(K=K, N=N, us=lay_us, ms=lay_us / 1e3,
                             tops=2 * rows * N * K / (lay_us * 1e-6) / 1e12,
                             bits_hist_subchannels=[float(v) for v in hist], avg_bits=avg_bits)
+    print("[bench] measured peaks (copy, library int8 GEMM)", file=sys.stderr, flush=True)
+    peaks = measured_peaks(torch)
+    for kd in kernels.values():
+        ref = peaks["hbm_copy_gbs"] if kd["bound"] == "hbm" else peaks.get("int8_gemm_8192_tops")
+        kd["frac_measured"] = (kd["gbs"] if kd["bound"] == "hbm" else kd["tops"]) / ref if ref else None
     dom = max(kernels, key=lambda k: kernels[k]["us_mean"])
     kd = kernels[dom]
     if kd["bound"] == "mfma":
@@ -758,6 +799,8 @@ def main() -> int:
                     frac=kd["gbs"] / HBM_PEAK_GBS)
     roof["traffic"] = kd["traffic"]
     roof["kernel"] = dom
+    roof["peak_measured"] = peaks["hbm_copy_gbs"] if kd["bound"] == "hbm" else peaks.get("int8_gemm_8192_tops")
+    roof["frac_measured"] = kd["frac_measured"]
 
     out = {
         "metric": METRIC, "value": value, "unit": "TOPS (dense-equiv int8)", "n_gpus": 1,
@@ -770,7 +813,7 @@ def main() -> int:
                                ", ".join(f"{L} {state[L]['K']}->{state[L]['N']}" for L in layers),
                    "rows": rows, "token_tile": T, "thr0_log2": wl.DEFAULT_K0,
                    "pairs_cycled": args.pairs},
-        "layers": layer_out, "kernels": kernels, "roofline": roof,
+        "layers": layer_out, "kernels": kernels, "roofline": roof, "measured_peaks": peaks,
         "cold": None if not cold else {
             "note": "eager, 512 MiB write before each layer (caches flushed); medians of 5",
             "ms_per_step": cold_ms, "tops": total_ops / (cold_ms * 1e-3) / 1e12, "kernels": cold},
