@@ -178,18 +178,31 @@ def write_traffic(fetch_dir: str, write_dir: str) -> None:
     print("\n".join(lines))
 
 
-def cpu_baseline(ins: list[dict], budget_s: float = 10.0) -> dict:
+def cpu_baseline(ins: list[dict], layer_names: list[str], budget_s: float = 10.0) -> dict:
     """The oracle (untuned) on the host cores: whole steps (both layers, the
-    resident pairs in turn) until about budget_s seconds of work."""
+    resident pairs in turn) until about budget_s seconds of work.  Each layer
+    runs the oracle's three stages (stage 1 with the aligned codes and digit
+    planes the GPU's stage 1 also writes), timed separately."""
     from threadpoolctl import threadpool_info
     from oracle import fmdq
     t0 = time.perf_counter()
     ops = 0
     steps = 0
+    stage_s = {}
     while True:
-        for d in ins[steps % len(ins)]:
-            fmdq.layer(d["x_t"], d["x_prev"], d["w"], d["w_scale"], d["y_prev"], d["base"],
-                       d["token_tile"], d["k0"])
+        for L, d in zip(layer_names, ins[steps % len(ins)]):
+            T, base = d["token_tile"], d["base"]
+            ta = time.perf_counter()
+            codes, tags, _ = fmdq.quantize(d["x_t"], d["x_prev"], T, base, d["k0"])
+            fmdq.aligned_codes(codes, tags)
+            fmdq.heavy_digits(codes, tags)
+            tb = time.perf_counter()
+            perm, off = fmdq.bucket(tags)
+            tc = time.perf_counter()
+            fmdq.linear(codes, tags, perm, off, d["w"], d["w_scale"], d["y_prev"], base, T)
+            td = time.perf_counter()
+            for name, dt in (("quantize", tb - ta), ("bucket", tc - tb), ("linear", td - tc)):
+                stage_s.setdefault(f"{name}@{L}", []).append(dt)
             ops += 2 * d["rows"] * d["N"] * d["K"]
         steps += 1
         if time.perf_counter() - t0 > budget_s:
@@ -198,6 +211,7 @@ def cpu_baseline(ins: list[dict], budget_s: float = 10.0) -> dict:
     threads = max([i["num_threads"] for i in threadpool_info()] or [1])
     return {"value": ops / dt / 1e12, "unit": "TOPS (dense-equiv int8)", "cores": threads,
             "kind": "oracle", "seconds": dt,
+            "stage_ms": {k: float(np.median(v)) * 1e3 for k, v in stage_s.items()},
             "sample": f"{steps} whole step(s) of the same workload ({ins[0][0]['rows']} rows, both "
                       f"layers, timestep pairs 1..{min(steps, len(ins))}); numpy float64 matmuls "
                       f"per token tile and FPoT group"}
@@ -837,7 +851,10 @@ def main() -> int:
         out["sar_attention"] = sar_attention(dm, torch, stream)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline([[host[L][p] for L in layers] for p in range(args.pairs)])
+        cb = cpu_baseline([[host[L][p] for L in layers] for p in range(args.pairs)], layers)
+        cb["gpu_speedup_per_stage"] = {k: v / (kernels[k]["us_mean"] / 1e3) for k, v in cb["stage_ms"].items()
+                                       if k in kernels}
+        out["cpu_baseline"] = cb
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out))
