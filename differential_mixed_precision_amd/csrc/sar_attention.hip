@@ -25,8 +25,11 @@
 // units is a = code·2^PoT (|code| ≤ 64, PoT ≤ 21, so |a| ≤ 2^27).  It is split
 // into signed base-256 digits a = Σ_j 2^(8j)·d_j (d_j in [-128, 127]); each
 // digit plane is an int8 matrix, and one v_mfma_i32_32x32x32_i8 chain per
-// plane gives an exact int32 partial product (|Σ| ≤ 128·127·128 < 2^22) that
-// is shifted into an int64 sum.  The planes a tile needs follow from its
+// plane gives an exact int32 partial product (|Σ| ≤ 128·127·128 < 2^22 per
+// block of keys).  scores combines two planes in int32 (|S| < 2^30) and more
+// in int64; pv keeps one int32 accumulator per plane over all kept keys
+// (|Σ| ≤ 128·127·2^16 < 2^31) and combines them in int64 once.  The planes a
+// tile needs follow from its
 // largest PoT (one for PoT 0, two up to 8, three up to 16, four beyond), so
 // typical Q tiles take two and P tiles two or three.  The MFMA operands are
 // loaded straight from global memory in the fragment layout (16 consecutive
