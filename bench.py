@@ -565,6 +565,30 @@ def sar_attention(dm, torch, stream, reps: int = 10) -> dict:
         er[i][1].record(stream)
     torch.cuda.synchronize()
     us = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) * 1e3 for e in ev])) for j, n in enumerate(names)}
+    # the same steps as HIP graph replays (no host gaps between the launches)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        run(v)
+        att.reused_step(vn)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g_cached, g_reused = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_cached):
+        run(v)
+    with torch.cuda.graph(g_reused):
+        att.reused_step(vn)
+    graph_us = {}
+    for name, g in (("cached", g_cached), ("reused", g_reused)):
+        for _ in range(3):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_us[name] = e0.elapsed_time(e1) * 1e3 / reps
     prod_ops = 2.0 * B * nnz * 64 * 64 * D
     pc_bytes = B * nnz * (64 * 64 + 2 * 64)          # P codes + PoTs of the cache
     x_bytes = 4 * BH * L * D                         # one float32 operand
@@ -586,7 +610,9 @@ def sar_attention(dm, torch, stream, reps: int = 10) -> dict:
     reused = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in er]))
     return {"workload": f"pixart-alpha-1024px-attn: {B} images x {H} heads, {L} tokens, head dim {D}, "
                         f"64x64 blocks, kept {nnz} of {H * (L // 64) ** 2} per image",
-            "launch": "eager", "cached_step_us": cached, "reused_step_us": reused,
+            "launch": "eager (per-kernel HIP events); graph replays for the step times below",
+            "cached_step_us": cached, "reused_step_us": reused,
+            "cached_step_us_graph": graph_us["cached"], "reused_step_us_graph": graph_us["reused"],
             "kept_fraction": nnz / (H * (L // 64) ** 2),
             "dense_equiv_tops_cached": 2 * prod_ops / (cached * 1e-6) / 1e12, "kernels": kern}
 
