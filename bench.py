@@ -1,30 +1,33 @@
 """Benchmark of the FMDQ differential linear on one MI355X.
 
-A step is one timestep pair through both MLP linears of the PixArt-alpha-style
-1024px workload (tokens 2 x 4096, fc1 1152->4608 and fc2 4608->1152, token
-tile 32): for each layer the three stages quantize -> bucket -> linear, with
-the cached output Y updated in place.  Inputs of a few consecutive pairs of
-the seeded random walk are made resident in HBM before timing and cycled.
+A step is one timestep pair through both MLP linears of the FLUX-style
+workload (4608 rows = 4096 image + 512 text tokens, fc1 3072->12288 and fc2
+12288->3072, token tile 32), the largest that fits one GPU: for each layer
+the three stages quantize -> bucket -> linear, with the cached output Y
+updated in place.  Inputs of a few consecutive pairs of the seeded random
+walk are made resident in HBM before timing and cycled.  --workload NAME
+times another workload instead; by default the other four are also timed
+(10 steps each) into the "per_workload" block of the same JSON line.
 
 Steps are launched as HIP graph replays (one captured step per cycled input
 pair; --eager launches kernel by kernel).  Prints one JSON line: whole-step
-dense-equivalent int8 TOPS (2*M*N*K per layer over the measured time), per-stage times from HIP events on the launch
-stream, the roofline of the dominant kernel (with the HBM traffic measured by
-rocprofv3 counters when a summary for the current kernel source exists under
-profiles/), the CPU oracle timed on the host as a baseline, the same steps
-with the dynamic base (an extra pass over X; --no-dynamic skips it), and the
-MLP chained over all timestep pairs with the GELU fused into fc1 (bits per
-step; --no-chain skips it).
+dense-equivalent int8 TOPS (2*M*N*K per layer over the measured time),
+per-stage times from HIP events on the launch stream, the roofline of the
+dominant kernel (with the HBM traffic measured by rocprofv3 counters when a
+summary for the current kernel source exists under profiles/), the CPU oracle
+timed on the host as a baseline, the same steps with the dynamic base (an
+extra pass over X; --no-dynamic skips it), and the MLP chained over all
+timestep pairs with the GELU fused into fc1 (bits per step; --no-chain skips
+it).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload pixart-alpha-1024px]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload flux-large]
 
-Traffic summary from two counter runs of this same command (run from the
-repository root; a plain 256 MiB device copy made before timing calibrates
-the counters):
+Traffic summary from two counter runs (run from the repository root; a plain
+256 MiB device copy made before timing calibrates the counters):
 
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention --no-cold
-    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention --no-cold
-    python bench.py --write-traffic OUT/pmc_fetch OUT/pmc_write
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o run -- python3 bench.py --workload W --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention --no-cold --no-per-workload
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o run -- python3 bench.py (same arguments)
+    python bench.py --workload W --write-traffic OUT/pmc_fetch OUT/pmc_write
 """
 from __future__ import annotations
 
@@ -50,24 +53,38 @@ KERNEL_SRC = {"quantize": ["fmdq_quantize.hip"], "bucket": ["fmdq_bucket.hip"],
 # device kernel name of each stage (as rocprofv3 reports it)
 KERNEL_NAME = {"quantize": "quantize_kernel", "bucket": "bucket_", "linear": "linear_mfma_kernel"}
 CAL_BYTES = 256 << 20     # the calibration copy
-TRAFFIC_MD = os.path.join(ROOT, "profiles", "stage_traffic_pixart1024.md")
-# bench.py arguments of the counter runs (the static step only)
-PMC_ARGS = "--steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention --no-cold"
+HEADLINE = "flux-large"        # the largest workload that fits one GPU
+
+
+def traffic_md(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"stage_traffic_{workload}.md")
+
+
+def pmc_args(workload: str) -> str:
+    """bench.py arguments of the counter runs (the static step only)."""
+    return (f"--workload {workload} --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain "
+            f"--no-slices --no-attention --no-cold --no-per-workload")
 
 
 def algorithmic(stage: str, rows: int, K: int, N: int, T: int) -> dict:
     """Compulsory HBM bytes (and int8 ops) of one launch of a stage: every array
-    the stage must read or write, once.  Re-reads of W or the codes by
-    several workgroups are not counted."""
+    the stage must read or write, once, by the formulas of the layer's scope
+    (M = rows, n_t token tiles):
+      quantize  8·M·K (X_t, X_{t-1}) + M·K (codes) + n_t·K (tags) + 16 (histogram)
+      bucket    3·n_t·K (tags in, uint16 ids out) + 68·n_t (17 group offsets)
+      linear    M·K (codes) + K·N (weights) + 2·n_t·K (ids) + 68·n_t + 4·N
+                (w_scale) + 8·M·N (Y_{t-1} in, Y_t out); 2·M·N·K int8 ops.
+    Re-reads of W or the codes by several workgroups are not counted.  Stage
+    1 also writes the shift-aligned operand of stage 3 (M·K more bytes) and
+    the digit planes of the wide sub-channels; ``extra_bytes`` reports the
+    former, which the formula leaves out."""
     nt = (rows + T - 1) // T
-    codes = nt * T * K
-    if stage == "quantize":   # X_t, X_{t-1} in; codes, aligned codes, tags out
-        return dict(bytes=8 * rows * K + 2 * codes + nt * K + 16, ops=0)
-    if stage == "bucket":     # tags in; perm, bin offsets out
-        return dict(bytes=nt * K + 2 * nt * K + 260 * nt, ops=0)
-    # aligned codes, W^T, perm, bin offsets, w_scale in; Y_{t-1} in, Y_t out
-    return dict(bytes=codes + K * N + 2 * nt * K + 260 * nt + 4 * N + 8 * rows * N,
-                ops=2 * rows * N * K)
+    if stage == "quantize":
+        return dict(bytes=8 * rows * K + rows * K + nt * K + 16, ops=0, extra_bytes=rows * K)
+    if stage == "bucket":
+        return dict(bytes=3 * nt * K + 68 * nt, ops=0, extra_bytes=0)
+    return dict(bytes=rows * K + K * N + 2 * nt * K + 68 * nt + 4 * N + 8 * rows * N,
+                ops=2 * rows * N * K, extra_bytes=0)
 
 
 def src_sha(stage: str) -> str:
@@ -91,21 +108,22 @@ def layer_keys(dispatches):
     return out
 
 
-def measured_traffic(stage: str, layer_grid: int):
+def measured_traffic(stage: str, layer_grid: int, workload: str):
     """Calibrated HBM bytes per launch of a stage's kernel in the layer whose
-    stage-3 launch grid is layer_grid, from the committed counter summary;
-    None if there is none or the kernel source changed since the counters
-    were taken."""
-    if not os.path.exists(TRAFFIC_MD):
+    stage-3 launch grid is layer_grid, from the committed counter summary of
+    the workload; None if there is none or the kernel source changed since
+    the counters were taken."""
+    md = traffic_md(workload)
+    if not os.path.exists(md):
         return None
-    for line in open(TRAFFIC_MD):
+    for line in open(md):
         f = [c.strip() for c in line.strip().strip("|").split("|")]
         if len(f) >= 8 and f[0] == stage and f[1] == str(layer_grid) and f[3] == src_sha(stage):
             return int(float(f[7]))
     return None
 
 
-def write_traffic(fetch_dir: str, write_dir: str) -> None:
+def write_traffic(fetch_dir: str, write_dir: str, workload: str) -> None:
     """Summarizes two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of the
     bench into the traffic table: per stage kernel and grid size, the mean
     KiB per dispatch, scaled by what the counters read for the calibration
@@ -145,17 +163,18 @@ def write_traffic(fetch_dir: str, write_dir: str) -> None:
     if not cal_f or not cal_w:
         raise SystemExit("no calibration copy in the counter runs")
     sf, sw = (CAL_BYTES / 1024) / cal_f, (CAL_BYTES / 1024) / cal_w
-    lines = ["# HBM traffic per launch, FMDQ differential linear, PixArt-alpha-style 1024px MLP",
+    args = pmc_args(workload)
+    lines = [f"# HBM traffic per launch, FMDQ differential linear, {workload} MLP",
              "",
              "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, rocprofv3 --pmc, one run each) of",
-             f"`python3 bench.py {PMC_ARGS}` on one MI355X, scaled by what they read",
+             f"`python3 bench.py {args}` on one MI355X, scaled by what they read",
              f"for a plain {CAL_BYTES >> 20} MiB device copy made in the same run (fetch x{sf:.4f}, write x{sw:.4f}).",
              "Commands:",
              "",
              "```",
-             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- python3 bench.py {PMC_ARGS}",
-             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- python3 bench.py {PMC_ARGS}",
-             f"python bench.py --write-traffic {fetch_dir} {write_dir}",
+             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- python3 bench.py {args}",
+             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- python3 bench.py {args}",
+             f"python bench.py --workload {workload} --write-traffic {fetch_dir} {write_dir}",
              "```",
              "",
              "Launches are attributed to their layer by the stage-3 launch that follows them (stages 1 and 2",
@@ -173,7 +192,7 @@ def write_traffic(fetch_dir: str, write_dir: str) -> None:
             b = fk * sf * 1024 + wk * sw * 1024
             lines.append(f"| {stage} | {lg} | {'/'.join(map(str, g1))} | {src_sha(stage)} | {fk:.0f} | {wk:.0f} | "
                          f"{sf:.4f}/{sw:.4f} | {b:.0f} |")
-    with open(TRAFFIC_MD, "w") as f:
+    with open(traffic_md(workload), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -181,8 +200,7 @@ def write_traffic(fetch_dir: str, write_dir: str) -> None:
 def cpu_baseline(ins: list[dict], layer_names: list[str], budget_s: float = 10.0) -> dict:
     """The oracle (untuned) on the host cores: whole steps (both layers, the
     resident pairs in turn) until about budget_s seconds of work.  Each layer
-    runs the oracle's three stages (stage 1 with the aligned codes and digit
-    planes the GPU's stage 1 also writes), timed separately."""
+    runs the oracle's three stages, timed separately."""
     from threadpoolctl import threadpool_info
     from oracle import fmdq
     t0 = time.perf_counter()
@@ -194,8 +212,6 @@ def cpu_baseline(ins: list[dict], layer_names: list[str], budget_s: float = 10.0
             T, base = d["token_tile"], d["base"]
             ta = time.perf_counter()
             codes, tags, _ = fmdq.quantize(d["x_t"], d["x_prev"], T, base, d["k0"])
-            fmdq.aligned_codes(codes, tags)
-            fmdq.heavy_digits(codes, tags)
             tb = time.perf_counter()
             perm, off = fmdq.bucket(tags)
             tc = time.perf_counter()
@@ -217,30 +233,39 @@ def cpu_baseline(ins: list[dict], layer_names: list[str], budget_s: float = 10.0
                       f"per token tile and FPoT group"}
 
 
-SUMMARIES = {
-    "linear": ("kernel_time_pixart1024.md",
-               "# Kernel time, FMDQ differential linear, PixArt-alpha-style 1024px MLP",
-               "8192 rows (2 x 4096 tokens), fc1 1152->4608 and fc2 4608->1152, token tile 32; one MI355X.",
-               "python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline --no-dynamic --no-chain --no-slices "
-               "--no-attention",
-               "rocprofv3 statistics over every launch of the run (eager warm-up steps, graph warm-up and timed "
-               "replays, and the eager pass that times the stages; fc1 and fc2 pooled per kernel):"),
-    "attention": ("kernel_time_sar_attention_pixart1024.md",
-                  "# Kernel time, SAR attention with FMDQ-INT8 operands, PixArt-alpha-style 1024px",
-                  "2 images x 16 heads, 4096 tokens, head dim 72, 64 x 64 blocks (63% kept); one MI355X.",
-                  "python3 bench.py --only-attention",
-                  "rocprofv3 statistics over every launch of the run (three warm-up cached steps, ten timed "
-                  "cached steps and ten reused steps):"),
-}
+def kernel_trace_args(workload: str) -> str:
+    return (f"--workload {workload} --steps 10 --warmup 3 --no-cpu-baseline --no-dynamic --no-chain "
+            f"--no-slices --no-attention --no-per-workload")
 
 
-def write_kernel_summary(trace_dir: str, which: str = "linear") -> None:
+def summary_spec(which: str, workload: str):
+    """File name, title, shape line, bench arguments and note of a kernel-time
+    summary."""
+    if which == "attention":
+        return ("kernel_time_sar_attention_pixart1024.md",
+                "# Kernel time, SAR attention with FMDQ-INT8 operands, PixArt-alpha-style 1024px",
+                "2 images x 16 heads, 4096 tokens, head dim 72, 64 x 64 blocks (63% kept); one MI355X.",
+                "--only-attention",
+                "rocprofv3 statistics over every launch of the run (three warm-up cached steps, ten timed "
+                "cached steps and ten reused steps):")
+    from gen import workloads as wl
+    spec = next(v for v in wl.CONFIGS.values() if v["name"] == workload)
+    shape = (f"{spec['rows']} rows, " + ", ".join(f"{L} {k}->{n}" for L, (k, n) in spec["layers"].items()) +
+             f", token tile {spec['token_tile']}; one MI355X.")
+    return (f"kernel_time_{workload}.md",
+            f"# Kernel time, FMDQ differential linear, {workload} workload", shape, kernel_trace_args(workload),
+            "rocprofv3 statistics over every launch of the run (eager warm-up steps, graph warm-up and timed "
+            "replays, and the eager pass that times the stages; the layers pooled per kernel):")
+
+
+def write_kernel_summary(trace_dir: str, which: str = "linear", workload: str = HEADLINE) -> None:
     """Summarizes a rocprofv3 --kernel-trace --stats run of the bench: the
     tool's own per-kernel statistics, and the mean duration per kernel and
-    launch grid from the trace (fc1 and fc2 launch the same kernels with
+    launch grid from the trace (the layers launch the same kernels with
     different grids)."""
     import csv
-    fname, title, shape, cmd, stats_note = SUMMARIES[which]
+    fname, title, shape, args, stats_note = summary_spec(which, workload)
+    cmd = f"python3 bench.py {args}"
     files = {}
     for root, _, fs in os.walk(trace_dir):
         for fn in fs:
@@ -255,7 +280,7 @@ def write_kernel_summary(trace_dir: str, which: str = "linear") -> None:
              "```",
              f"rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o run -- \\",
              f"    {cmd}",
-             f"python bench.py --write-kernel-summary {trace_dir} --summary {which}",
+             f"python bench.py --write-kernel-summary {trace_dir} --summary {which} --workload {workload}",
              "```",
              "",
              stats_note,
@@ -617,12 +642,177 @@ def sar_attention(dm, torch, stream, reps: int = 10) -> dict:
             "dense_equiv_tops_cached": 2 * prod_ops / (cached * 1e-6) / 1e12, "kernels": kern}
 
 
+def layer_grids(rows: int, T: int, K: int, N: int) -> dict:
+    """Launch grid (threads) of each stage, as rocprofv3 reports it."""
+    nt = (rows + T - 1) // T
+    # stage 1: 16 rows per lane, T/16 lanes per group, CPT channels per
+    # group; items of kgroups flattened (tile, group) pairs; 512 workgroups
+    kgroups = 256 // (T // 16)
+    cpt = 4 if K % 4 == 0 else 2 if K % 2 == 0 else 1
+    q_work = (nt * (K // cpt) + kgroups - 1) // kgroups
+    return {"quantize": 256 * min(q_work, 512), "bucket": (1024 if K <= 16384 else 256) * min(nt, 2048),
+            "linear": 256 * ((nt + 128 // T - 1) // (128 // T)) * ((N + 255) // 256)}
+
+
+class Workload:
+    """The device state of one workload's step (every layer: its buffers, the
+    resident input pairs, its cached output) and the step itself."""
+
+    def __init__(self, dm, torch, wl, cfg: int, pairs: int, host=None):
+        self.dm, self.torch = dm, torch
+        self.spec = wl.CONFIGS[cfg]
+        self.cfg = cfg
+        self.layers = list(self.spec["layers"])
+        self.rows, self.T = self.spec["rows"], self.spec["token_tile"]
+        self.pairs = pairs
+        if host is None:
+            host = {L: [wl.make_inputs(cfg, L, p) for p in range(1, pairs + 1)] for L in self.layers}
+        self.host = host
+        dev = torch.device("cuda:0")
+        self.state = {}
+        for L in self.layers:
+            d0 = host[L][0]
+            w = torch.from_numpy(d0["w"]).to(dev)
+            ws = torch.from_numpy(d0["w_scale"]).to(dev)
+            layer = dm.FmdqLayer(w, ws, self.rows, self.T, float(d0["base"]), d0["k0"], d0["tokens_per_seq"])
+            xs = [(torch.from_numpy(d["x_t"]).to(dev), torch.from_numpy(d["x_prev"]).to(dev)) for d in host[L]]
+            y = torch.from_numpy(d0["y_prev"]).to(dev)
+            self.state[L] = dict(layer=layer, xs=xs, y=y, K=d0["K"], N=d0["N"])
+        self.stream = torch.cuda.current_stream()
+
+    def step(self, i, events=None):
+        dm, stream = self.dm, self.stream
+        for L in self.layers:
+            s = self.state[L]
+            lay = s["layer"]
+            x_t, x_p = s["xs"][i % len(s["xs"])]
+            ev = events[L] if events is not None else None
+            if ev is not None:
+                ev[0].record(stream)
+            dm.quantize(lay.p, x_t, x_p, lay.codes, lay.tags, lay.acodes, lay.hcodes, lay.bit_hist)
+            if ev is not None:
+                ev[1].record(stream)
+            dm.bucket(lay.p, lay.tags, lay.perm, lay.group_off)
+            if ev is not None:
+                ev[2].record(stream)
+            dm.linear(lay.p, s["N"], lay.codes, lay.perm, lay.group_off, lay.acodes, lay.hcodes, lay.w,
+                      lay.w_t, lay.w_scale, s["y"], s["y"])
+            if ev is not None:
+                ev[3].record(stream)
+
+    def measure(self, steps: int, warmup: int, eager: bool) -> dict:
+        """W eager warm-up steps; then K timed steps (HIP graph replays of one
+        captured step per resident pair unless eager) between two device
+        synchronizations; then the same steps once more eagerly with HIP events
+        between the kernels for the per-stage times (diagnostic)."""
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        graphs = []
+        if not eager:
+            side = torch.cuda.Stream()
+            side.wait_stream(self.stream)
+            with torch.cuda.stream(side):
+                for i in range(self.pairs):
+                    self.step(i)
+            self.stream.wait_stream(side)
+            torch.cuda.synchronize()
+            for p in range(self.pairs):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    self.step(p)
+                graphs.append(g)
+            for i in range(warmup):
+                graphs[i % self.pairs].replay()
+        for L in self.layers:
+            self.state[L]["layer"].bit_hist.zero_()
+        events = [{L: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for L in self.layers}
+                  for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            if graphs:
+                graphs[(warmup + i) % self.pairs].replay()
+            else:
+                self.step(warmup + i, events[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        hists = {L: self.state[L]["layer"].bit_hist.cpu().numpy().astype(np.int64) for L in self.layers}
+        if graphs:
+            for i in range(steps):
+                self.step(warmup + steps + i, events[i])
+            torch.cuda.synchronize()
+        per = {L: {s: [] for s in STAGES} for L in self.layers}
+        for i in range(steps):
+            for L in self.layers:
+                ev = events[i][L]
+                for j, s in enumerate(STAGES):
+                    per[L][s].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)   # microseconds
+        ms_per_step = wall * 1e3 / steps
+        total_ops = sum(2 * self.rows * self.state[L]["N"] * self.state[L]["K"] for L in self.layers)
+        kernels, layer_out = {}, {}
+        for L in self.layers:
+            K, N = self.state[L]["K"], self.state[L]["N"]
+            grid = layer_grids(self.rows, self.T, K, N)
+            hist = hists[L] / max(steps, 1)
+            lay_us = 0.0
+            for s in STAGES:
+                us = float(np.mean(per[L][s]))
+                lay_us += us
+                alg = algorithmic(s, self.rows, K, N, self.T)
+                gbs = alg["bytes"] / (us * 1e-6) / 1e9
+                tops = alg["ops"] / (us * 1e-6) / 1e12 if alg["ops"] else 0.0
+                t_hbm = alg["bytes"] / (HBM_PEAK_GBS * 1e9)
+                t_mfma = alg["ops"] / (INT8_PEAK_TOPS * 1e12) if alg["ops"] else 0.0
+                bound = "mfma" if t_mfma > t_hbm else "hbm"
+                kd = dict(us_mean=us, us_median=float(np.median(per[L][s])),
+                          us_p10=float(np.percentile(per[L][s], 10)), us_p90=float(np.percentile(per[L][s], 90)),
+                          alg_bytes=alg["bytes"], alg_ops=alg["ops"], gbs=gbs, tops=tops, bound=bound,
+                          frac=(tops / INT8_PEAK_TOPS) if bound == "mfma" else gbs / HBM_PEAK_GBS,
+                          traffic=measured_traffic(s, grid["linear"], self.spec["name"]), grid=grid[s])
+                if alg["extra_bytes"]:
+                    kd["extra_bytes"] = alg["extra_bytes"]
+                    kd["gbs_with_extra"] = (alg["bytes"] + alg["extra_bytes"]) / (us * 1e-6) / 1e9
+                kernels[f"{s}@{L}"] = kd
+            avg_bits = float((hist * np.array([2, 4, 6, 8])).sum() / max(hist.sum(), 1))
+            layer_out[L] = dict(K=K, N=N, us=lay_us, ms=lay_us / 1e3,
+                                tops=2 * self.rows * N * K / (lay_us * 1e-6) / 1e12,
+                                bits_hist_subchannels=[float(v) for v in hist], avg_bits=avg_bits)
+        return dict(ms_per_step=ms_per_step, value=total_ops / (ms_per_step * 1e-3) / 1e12,
+                    total_ops=total_ops, kernels=kernels, layers=layer_out,
+                    launch="eager" if eager else "HIP graph replay of one captured step per input pair")
+
+    def describe(self) -> str:
+        sp = self.spec
+        return (f"{sp['name']}: {self.rows} rows ({self.rows // sp['tokens_per_seq']} x {sp['tokens_per_seq']} "
+                f"tokens), token tile {self.T}, " +
+                ", ".join(f"{L} {self.state[L]['K']}->{self.state[L]['N']}" for L in self.layers))
+
+
+def roofline_of(kernels: dict) -> dict:
+    """The roofline object of the stage with the largest mean time."""
+    dom = max(kernels, key=lambda k: kernels[k]["us_mean"])
+    kd = kernels[dom]
+    if kd["bound"] == "mfma":
+        roof = dict(bound="mfma", achieved=kd["tops"], peak=INT8_PEAK_TOPS, unit="TOP/s",
+                    frac=kd["tops"] / INT8_PEAK_TOPS)
+    else:
+        roof = dict(bound="hbm", achieved=kd["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=kd["gbs"] / HBM_PEAK_GBS)
+    roof["traffic"] = kd["traffic"]
+    roof["kernel"] = dom
+    roof["us_per_launch"] = kd["us_mean"]
+    roof["alg_bytes_per_launch"] = kd["alg_bytes"]
+    roof["alg_ops_per_launch"] = kd["alg_ops"]
+    return roof
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="pixart-alpha-1024px")
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--pairs", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch kernel by kernel instead of graph replays")
@@ -631,17 +821,18 @@ def main() -> int:
     ap.add_argument("--no-slices", action="store_true", help="skip timing the 2-bit slice stream")
     ap.add_argument("--no-attention", action="store_true", help="skip the SAR attention workload")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache pass")
+    ap.add_argument("--no-per-workload", action="store_true", help="skip the other workloads' steps")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--write-kernel-summary", metavar="TRACE_DIR")
-    ap.add_argument("--summary", choices=sorted(SUMMARIES), default="linear",
+    ap.add_argument("--summary", choices=["linear", "attention"], default="linear",
                     help="which kernel-time summary --write-kernel-summary writes")
     ap.add_argument("--only-attention", action="store_true", help="time only the SAR attention workload")
     args = ap.parse_args()
     if args.write_traffic:
-        write_traffic(*args.write_traffic)
+        write_traffic(*args.write_traffic, args.workload)
         return 0
     if args.write_kernel_summary:
-        write_kernel_summary(args.write_kernel_summary, args.summary)
+        write_kernel_summary(args.write_kernel_summary, args.summary, args.workload)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the layer shards by token tiles with no "
@@ -663,100 +854,25 @@ def main() -> int:
     dev = torch.device("cuda:0")
     cfg = {v["name"]: c for c, v in wl.CONFIGS.items()}[args.workload]
     spec = wl.CONFIGS[cfg]
-    layers = list(spec["layers"])
     print(f"[bench] generating {spec['name']} pairs 1..{args.pairs}", file=sys.stderr, flush=True)
-    host = {L: [wl.make_inputs(cfg, L, p) for p in range(1, args.pairs + 1)] for L in layers}
-    rows, T = spec["rows"], spec["token_tile"]
-
-    # resident device state
-    state = {}
-    for L in layers:
-        d0 = host[L][0]
-        w = torch.from_numpy(d0["w"]).to(dev)
-        ws = torch.from_numpy(d0["w_scale"]).to(dev)
-        layer = dm.FmdqLayer(w, ws, rows, T, float(d0["base"]), d0["k0"], d0["tokens_per_seq"])
-        xs = [(torch.from_numpy(d["x_t"]).to(dev), torch.from_numpy(d["x_prev"]).to(dev))
-              for d in host[L]]
-        y = torch.from_numpy(d0["y_prev"]).to(dev)
-        state[L] = dict(layer=layer, xs=xs, y=y, K=d0["K"], N=d0["N"])
+    work = Workload(dm, torch, wl, cfg, args.pairs)
+    layers, rows, T, state = work.layers, work.rows, work.T, work.state
     # a plain copy of known size (counter calibration for rocprofv3 --pmc runs)
-    cal_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    cal_src = torch.empty(CAL_BYTES, dtype=torch.uint8, device=dev)
     cal_dst = torch.empty_like(cal_src)
     cal_dst.copy_(cal_src)
     torch.cuda.synchronize()
+    del cal_src, cal_dst
+    stream = work.stream
 
-    stream = torch.cuda.current_stream()
+    print(f"[bench] timing {spec['name']}", file=sys.stderr, flush=True)
+    head = work.measure(args.steps, args.warmup, args.eager)
+    kernels = head["kernels"]
 
-    def step(i, events=None):
-        for L in layers:
-            s = state[L]
-            lay = s["layer"]
-            x_t, x_p = s["xs"][i % len(s["xs"])]
-            ev = events[L] if events is not None else None
-            if ev is not None:
-                ev[0].record(stream)
-            dm.quantize(lay.p, x_t, x_p, lay.codes, lay.tags, lay.acodes, lay.hcodes, lay.bit_hist)
-            if ev is not None:
-                ev[1].record(stream)
-            dm.bucket(lay.p, lay.tags, lay.perm, lay.group_off)
-            if ev is not None:
-                ev[2].record(stream)
-            dm.linear(lay.p, s["N"], lay.codes, lay.perm, lay.group_off, lay.acodes, lay.hcodes, lay.w,
-                      lay.w_t, lay.w_scale, s["y"], s["y"])
-            if ev is not None:
-                ev[3].record(stream)
-
-    for i in range(args.warmup):
-        step(i)
-    # Steps are launched as HIP graphs: one captured step per cycled input pair
-    # (the same six kernels, without the host launch gaps between them).
-    graphs = []
-    if not args.eager:
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            for i in range(args.pairs):
-                step(i)
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        for p in range(args.pairs):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(p)
-            graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % args.pairs].replay()
-    for L in layers:
-        state[L]["layer"].bit_hist.zero_()
-    events = [{L: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for L in layers}
-              for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if graphs:
-            graphs[(args.warmup + i) % args.pairs].replay()
-        else:
-            step(args.warmup + i, events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    hists = {L: state[L]["layer"].bit_hist.cpu().numpy().astype(np.int64) for L in layers}
-    if graphs:
-        # per-stage times: the same steps once more, eagerly, with HIP events
-        # between the kernels (diagnostic; not part of the timed region above)
-        for i in range(args.steps):
-            step(args.warmup + args.steps + i, events[i])
-        torch.cuda.synchronize()
-
-    per = {L: {s: [] for s in STAGES} for L in layers}
-    for i in range(args.steps):
-        for L in layers:
-            ev = events[i][L]
-            for j, s in enumerate(STAGES):
-                per[L][s].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)   # microseconds
     # Cold runs: before each layer a 512 MiB write evicts the 256 MB
     # Infinity Cache (and the L2s), so every operand comes from HBM.
     cold_reps = 0 if args.no_cold else 5
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if cold_reps else None
     cold_ev = [{L: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for L in layers}
                for _ in range(cold_reps)]
     for i in range(cold_reps):
@@ -782,81 +898,26 @@ def main() -> int:
             if v:
                 cold[f"{s_}@{L}"] = {"us_median": float(np.median(v)), "us_mean": float(np.mean(v))}
     cold_ms = sum(v["us_median"] for v in cold.values()) / 1e3
-    ms_per_step = wall * 1e3 / args.steps
-    total_ops = sum(2 * rows * state[L]["N"] * state[L]["K"] for L in layers)
-    value = total_ops / (ms_per_step * 1e-3) / 1e12
 
-    # launch grid (threads) of each stage, as rocprofv3 reports it
-    nt = (rows + T - 1) // T
-    grids = {}
-    for L in layers:
-        K, N = state[L]["K"], state[L]["N"]
-        # stage 1: 16 rows per lane, T/16 lanes per group, CPT channels per
-        # group; items of kgroups flattened (tile, group) pairs; 512 workgroups
-        kgroups = 256 // (T // 16)
-        cpt = 4 if K % 4 == 0 else 2 if K % 2 == 0 else 1
-        q_work = (nt * (K // cpt) + kgroups - 1) // kgroups
-        grids[L] = {"quantize": 256 * min(q_work, 512), "bucket": (1024 if K <= 16384 else 256) * min(nt, 2048),
-                    "linear": 256 * ((nt + 128 // T - 1) // (128 // T)) * ((N + 255) // 256)}
-    kernels = {}
-    layer_out = {}
-    for L in layers:
-        K, N = state[L]["K"], state[L]["N"]
-        hist = hists[L] / max(args.steps, 1)
-        lay_us = 0.0
-        for s in STAGES:
-            us = float(np.mean(per[L][s]))
-            lay_us += us
-            alg = algorithmic(s, rows, K, N, T)
-            gbs = alg["bytes"] / (us * 1e-6) / 1e9
-            tops = alg["ops"] / (us * 1e-6) / 1e12 if alg["ops"] else 0.0
-            t_hbm = alg["bytes"] / (HBM_PEAK_GBS * 1e9)
-            t_mfma = alg["ops"] / (INT8_PEAK_TOPS * 1e12) if alg["ops"] else 0.0
-            bound = "mfma" if t_mfma > t_hbm else "hbm"
-            traffic = measured_traffic(s, grids[L]["linear"])
-            kernels[f"{s}@{L}"] = dict(
-                us_mean=us, us_median=float(np.median(per[L][s])), us_p10=float(np.percentile(per[L][s], 10)),
-                us_p90=float(np.percentile(per[L][s], 90)), alg_bytes=alg["bytes"],
-                alg_ops=alg["ops"], gbs=gbs, tops=tops, bound=bound,
-                frac=(tops / INT8_PEAK_TOPS) if bound == "mfma" else gbs / HBM_PEAK_GBS,
-                traffic=traffic)
-        avg_bits = float((hist * np.array([2, 4, 6, 8])).sum() / max(hist.sum(), 1))
-        layer_out[L] = dict(K=K, N=N, us=lay_us, ms=lay_us / 1e3,
-                            tops=2 * rows * N * K / (lay_us * 1e-6) / 1e12,
-                            bits_hist_subchannels=[float(v) for v in hist], avg_bits=avg_bits)
     print("[bench] measured peaks (copy, library int8 GEMM)", file=sys.stderr, flush=True)
     peaks = measured_peaks(torch)
     for kd in kernels.values():
         ref = peaks["hbm_copy_gbs"] if kd["bound"] == "hbm" else peaks.get("int8_gemm_8192_tops")
         kd["frac_measured"] = (kd["gbs"] if kd["bound"] == "hbm" else kd["tops"]) / ref if ref else None
-    dom = max(kernels, key=lambda k: kernels[k]["us_mean"])
-    kd = kernels[dom]
-    if kd["bound"] == "mfma":
-        roof = dict(bound="mfma", achieved=kd["tops"], peak=INT8_PEAK_TOPS, unit="TOP/s",
-                    frac=kd["tops"] / INT8_PEAK_TOPS)
-    else:
-        roof = dict(bound="hbm", achieved=kd["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=kd["gbs"] / HBM_PEAK_GBS)
-    roof["traffic"] = kd["traffic"]
-    roof["kernel"] = dom
-    roof["peak_measured"] = peaks["hbm_copy_gbs"] if kd["bound"] == "hbm" else peaks.get("int8_gemm_8192_tops")
-    roof["frac_measured"] = kd["frac_measured"]
+    roof = roofline_of(kernels)
 
     out = {
-        "metric": METRIC, "value": value, "unit": "TOPS (dense-equiv int8)", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "metric": METRIC, "value": head["value"], "unit": "TOPS (dense-equiv int8)", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
-        "launch": "eager" if args.eager else "HIP graph replay of one captured step per input pair",
+        "launch": head["launch"],
         "data": "synthetic (seeded random walk of DiT-like activations; random int8 weights)",
-        "config": {"workload": f"{spec['name']}: {rows} rows ({rows // spec['tokens_per_seq']} x "
-                               f"{spec['tokens_per_seq']} tokens), token tile {T}, MLP " +
-                               ", ".join(f"{L} {state[L]['K']}->{state[L]['N']}" for L in layers),
-                   "rows": rows, "token_tile": T, "thr0_log2": wl.DEFAULT_K0,
+        "config": {"workload": work.describe(), "rows": rows, "token_tile": T, "thr0_log2": wl.DEFAULT_K0,
                    "pairs_cycled": args.pairs},
-        "layers": layer_out, "kernels": kernels, "roofline": roof, "measured_peaks": peaks,
+        "layers": head["layers"], "kernels": kernels, "roofline": roof, "measured_peaks": peaks,
         "cold": None if not cold else {
             "note": "eager, 512 MiB write before each layer (caches flushed); medians of 5",
-            "ms_per_step": cold_ms, "tops": total_ops / (cold_ms * 1e-3) / 1e12, "kernels": cold},
+            "ms_per_step": cold_ms, "tops": head["total_ops"] / (cold_ms * 1e-3) / 1e12, "kernels": cold},
     }
     if not args.no_slices:
         print("[bench] 2-bit slice stream", file=sys.stderr, flush=True)
@@ -866,12 +927,29 @@ def main() -> int:
         out["mlp_chain"] = mlp_chain(dm, torch, cfg, spec, stream)
     if not args.no_dynamic:
         print("[bench] dynamic-base variant", file=sys.stderr, flush=True)
-        out["dynamic_base"] = dynamic_variant(dm, torch, state, layers, rows, args, stream, ms_per_step)
+        out["dynamic_base"] = dynamic_variant(dm, torch, state, layers, rows, args, stream, head["ms_per_step"])
     print("[bench] library int8 GEMM (context)", file=sys.stderr, flush=True)
     try:
         out["library_int8_gemm"] = library_gemm(torch, {L: (state[L]["K"], state[L]["N"]) for L in layers}, rows)
     except RuntimeError as ex:                # not every build exposes it
         out["library_int8_gemm"] = {"error": str(ex)[:200]}
+    host = work.host
+    del work, state
+    torch.cuda.empty_cache()
+    if not args.no_per_workload:
+        # the other workloads: parity cases, timed the same way (context)
+        pw = {}
+        for c, sp in wl.CONFIGS.items():
+            if c == cfg:
+                continue
+            print(f"[bench] workload {sp['name']}", file=sys.stderr, flush=True)
+            wk = Workload(dm, torch, wl, c, 1)
+            r = wk.measure(10, 3, args.eager)
+            pw[sp["name"]] = {"config": wk.describe(), "ms_per_step": r["ms_per_step"], "tops": r["value"],
+                              "layers": r["layers"], "kernels": r["kernels"], "roofline": roofline_of(r["kernels"])}
+            del wk
+            torch.cuda.empty_cache()
+        out["per_workload"] = pw
     if not args.no_attention:
         print("[bench] SAR attention", file=sys.stderr, flush=True)
         out["sar_attention"] = sar_attention(dm, torch, stream)

@@ -19,12 +19,13 @@ the current V.
 from __future__ import annotations
 
 from . import _binding
-from ._binding import (FmdqError, Params, bucket, dynamic_base, gelu, linear,  # noqa: F401
-                       linear_dyn, linear_gelu, load, make_params, pack_weights, quantize,
+from ._binding import (FmdqError, Params, bucket, dynamic_base, gelu, layer, layer_workspace_size,  # noqa: F401
+                       linear, linear_dyn, linear_gelu, load, make_params, pack_weights, quantize,
                        quantize_dyn, slice_encode, sar_padded_dim, sar_pv, sar_quantize_k,
                        sar_quantize_q, sar_quantize_v, sar_scores)
 
-__all__ = ["FmdqError", "Params", "FmdqLayer", "FmdqMLP", "bucket", "dynamic_base", "gelu", "linear",
+__all__ = ["FmdqError", "Params", "FmdqLayer", "FmdqMLP", "bucket", "dynamic_base", "gelu", "layer",
+           "layer_workspace_size", "linear",
            "linear_dyn", "linear_gelu", "load", "make_params", "pack_weights", "quantize",
            "quantize_dyn", "slice_encode", "n_tiles", "SarAttention", "sar_padded_dim", "sar_pv",
            "sar_quantize_k", "sar_quantize_q", "sar_quantize_v", "sar_scores"]

@@ -21,7 +21,7 @@ TAG_OFFSET = 15
 POT_MAX = 21
 PREC_SHIFT = 4
 MAX_K = 65535
-ABI_VERSION = 9
+ABI_VERSION = 10
 SAR_BLOCK = 64
 SAR_TILE = 32
 SAR_PAD = 32
@@ -32,7 +32,8 @@ SAR_EXP_FRAC = 36
 SYMBOLS = ("dstar_fmdq_quantize", "dstar_fmdq_bucket", "dstar_fmdq_slice_encode", "dstar_fmdq_pack_weights",
            "dstar_fmdq_linear", "dstar_fmdq_linear_gelu", "dstar_fmdq_gelu",
            "dstar_fmdq_dynamic_base", "dstar_fmdq_quantize_dyn",
-           "dstar_fmdq_linear_dyn", "dstar_fmdq_last_error", "dstar_fmdq_abi_version")
+           "dstar_fmdq_linear_dyn", "dstar_fmdq_layer", "dstar_fmdq_layer_workspace_size",
+           "dstar_fmdq_last_error", "dstar_fmdq_abi_version")
 SAR_SYMBOLS = ("dstar_sar_quantize_q", "dstar_sar_quantize_k", "dstar_sar_quantize_v", "dstar_sar_scores",
                "dstar_sar_pv")
 
@@ -81,7 +82,7 @@ def load() -> ctypes.CDLL:
     lib.dstar_fmdq_slice_encode.restype = ctypes.c_int
     lib.dstar_fmdq_pack_weights.argtypes = [i32, i32, vp, vp, vp]
     lib.dstar_fmdq_pack_weights.restype = ctypes.c_int
-    lib.dstar_fmdq_linear.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
+    lib.dstar_fmdq_linear.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp]
     lib.dstar_fmdq_linear.restype = ctypes.c_int
     lib.dstar_fmdq_linear_gelu.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.dstar_fmdq_linear_gelu.restype = ctypes.c_int
@@ -91,9 +92,13 @@ def load() -> ctypes.CDLL:
     lib.dstar_fmdq_dynamic_base.restype = ctypes.c_int
     lib.dstar_fmdq_quantize_dyn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.dstar_fmdq_quantize_dyn.restype = ctypes.c_int
-    lib.dstar_fmdq_linear_dyn.argtypes = [P, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
-                                          i32, vp]
+    lib.dstar_fmdq_linear_dyn.argtypes = [P, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                          i32, i32, vp]
     lib.dstar_fmdq_linear_dyn.restype = ctypes.c_int
+    lib.dstar_fmdq_layer.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp]
+    lib.dstar_fmdq_layer.restype = ctypes.c_int
+    lib.dstar_fmdq_layer_workspace_size.argtypes = [P]
+    lib.dstar_fmdq_layer_workspace_size.restype = ctypes.c_int64
     S = ctypes.POINTER(SarParams)
     lib.dstar_sar_quantize_q.argtypes = [S, vp, vp, vp, vp]
     lib.dstar_sar_quantize_k.argtypes = [S, vp, vp, vp, vp]
@@ -160,12 +165,30 @@ def pack_weights(K: int, N: int, w, w_t, stream=None) -> None:
 
 
 def linear(p: Params, N: int, codes, perm, group_off, acodes, hcodes, w, w_t, w_scale, y_prev,
-           y_out, acc_dbg=None, dbg_tile_lo: int = 0, dbg_tile_hi: int = 0, stream=None) -> None:
+           y_out, acc_dbg=None, dbg_tile_lo: int = 0, dbg_tile_hi: int = 0, stream=None,
+           s_dbg=None) -> None:
     """dstar_fmdq_linear."""
     _check(load().dstar_fmdq_linear(ctypes.byref(p), int(N), _ptr(codes), _ptr(perm),
                                     _ptr(group_off), _ptr(acodes), _ptr(hcodes), _ptr(w), _ptr(w_t),
                                     _ptr(w_scale), _ptr(y_prev), _ptr(y_out), _ptr(acc_dbg),
-                                    int(dbg_tile_lo), int(dbg_tile_hi), _stream(stream)))
+                                    _ptr(s_dbg), int(dbg_tile_lo), int(dbg_tile_hi), _stream(stream)))
+
+
+def layer_workspace_size(p: Params) -> int:
+    """dstar_fmdq_layer_workspace_size: bytes of workspace the one-call layer needs."""
+    n = load().dstar_fmdq_layer_workspace_size(ctypes.byref(p))
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def layer(p: Params, N: int, x_t, x_prev, w, w_t, w_scale, y_prev, y_out, workspace, bit_hist=None,
+          stream=None) -> None:
+    """dstar_fmdq_layer: the three stages in one call; ``workspace`` is a uint8
+    device tensor of at least layer_workspace_size(p) bytes."""
+    _check(load().dstar_fmdq_layer(ctypes.byref(p), int(N), _ptr(x_t), _ptr(x_prev), _ptr(w), _ptr(w_t),
+                                   _ptr(w_scale), _ptr(y_prev), _ptr(y_out), _ptr(bit_hist), _ptr(workspace),
+                                   int(workspace.numel() * workspace.element_size()), _stream(stream)))
 
 
 def dynamic_base(p: Params, x_t, x_prev, base, stream=None) -> None:
@@ -185,12 +208,12 @@ def quantize_dyn(p: Params, base, x_t, x_prev, codes, tags, acodes=None, hcodes=
 
 def linear_dyn(p: Params, base, N: int, codes, perm, group_off, acodes, hcodes, w, w_t, w_scale,
                y_prev, y_out, acc_dbg=None, dbg_tile_lo: int = 0, dbg_tile_hi: int = 0,
-               stream=None) -> None:
+               stream=None, s_dbg=None) -> None:
     """dstar_fmdq_linear_dyn: stage 3 with the base read from the device tensor `base`."""
     _check(load().dstar_fmdq_linear_dyn(ctypes.byref(p), _ptr(base), int(N), _ptr(codes), _ptr(perm),
                                         _ptr(group_off), _ptr(acodes), _ptr(hcodes), _ptr(w),
                                         _ptr(w_t), _ptr(w_scale), _ptr(y_prev), _ptr(y_out),
-                                        _ptr(acc_dbg), int(dbg_tile_lo), int(dbg_tile_hi),
+                                        _ptr(acc_dbg), _ptr(s_dbg), int(dbg_tile_lo), int(dbg_tile_hi),
                                         _stream(stream)))
 
 

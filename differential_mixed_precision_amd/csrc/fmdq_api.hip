@@ -112,7 +112,7 @@ int linear_impl(const dstar_fmdq_params* p, const float* base_dev, int32_t N, co
                 const uint16_t* perm, const int32_t* group_off, const int8_t* acodes,
                 const int8_t* hcodes, const int8_t* w, const int8_t* w_t, const float* w_scale,
                 const float* y_prev, float* y_out, float* gelu_out, int32_t* acc_dbg,
-                int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream);
+                int64_t* s_dbg, int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream);
 
 // Checks the device base pointer of the _dyn entry points.
 int check_base_dev(const float* base_dev, const char* what) {
@@ -220,10 +220,10 @@ int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N, const int8_t* codes
                       const int8_t* acodes, const int8_t* hcodes, const int8_t* w,
                       const int8_t* w_t,
                       const float* w_scale, const float* y_prev, float* y_out, int32_t* acc_dbg,
-                      int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream) {
+                      int64_t* s_dbg, int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream) {
   clear_error();
   return linear_impl(p, nullptr, N, codes, perm, group_off, acodes, hcodes, w, w_t, w_scale, y_prev,
-                     y_out, nullptr, acc_dbg, dbg_tile_lo, dbg_tile_hi, stream);
+                     y_out, nullptr, acc_dbg, s_dbg, dbg_tile_lo, dbg_tile_hi, stream);
 }
 
 int dstar_fmdq_linear_gelu(const dstar_fmdq_params* p, int32_t N, const int8_t* codes,
@@ -234,10 +234,20 @@ int dstar_fmdq_linear_gelu(const dstar_fmdq_params* p, int32_t N, const int8_t* 
   clear_error();
   if (gelu_out == nullptr) return set_error(DSTAR_ENULL, "linear_gelu: gelu_out must not be NULL");
   if (!aligned(gelu_out, 16)) return set_error(DSTAR_EALIGN, "linear_gelu: gelu_out must be 16-byte aligned");
-  if (gelu_out == y_out || gelu_out == y_prev)
-    return set_error(DSTAR_EINVAL, "linear_gelu: gelu_out must not alias y_prev or y_out");
+  // Workgroups read Y_{t-1} and write Y_t and GELU(Y_t) of their own block
+  // only, so gelu_out may not share a byte with either (not even shifted by a
+  // row: another block's GELU store would race with this block's loads).
+  if (p != nullptr && p->rows > 0 && N > 0) {
+    const uintptr_t bytes = (uintptr_t)p->rows * (uintptr_t)N * sizeof(float);
+    auto overlap = [bytes](const void* x, const void* y) {
+      const uintptr_t a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(y);
+      return x != nullptr && y != nullptr && a < b + bytes && b < a + bytes;
+    };
+    if (overlap(gelu_out, y_out) || overlap(gelu_out, y_prev))
+      return set_error(DSTAR_EINVAL, "linear_gelu: gelu_out overlaps y_prev or y_out");
+  }
   return linear_impl(p, nullptr, N, codes, perm, group_off, acodes, hcodes, w, w_t, w_scale, y_prev,
-                     y_out, gelu_out, nullptr, 0, 0, stream);
+                     y_out, gelu_out, nullptr, nullptr, 0, 0, stream);
 }
 
 int dstar_fmdq_gelu(const float* y, float* g, int64_t n, void* stream) {
@@ -253,12 +263,12 @@ int dstar_fmdq_linear_dyn(const dstar_fmdq_params* p, const float* base, int32_t
                           const int8_t* codes, const uint16_t* perm, const int32_t* group_off,
                           const int8_t* acodes, const int8_t* hcodes, const int8_t* w,
                           const int8_t* w_t, const float* w_scale, const float* y_prev,
-                          float* y_out, int32_t* acc_dbg, int32_t dbg_tile_lo,
+                          float* y_out, int32_t* acc_dbg, int64_t* s_dbg, int32_t dbg_tile_lo,
                           int32_t dbg_tile_hi, void* stream) {
   clear_error();
   if (int rc = check_base_dev(base, "linear_dyn")) return rc;
   return linear_impl(p, base, N, codes, perm, group_off, acodes, hcodes, w, w_t, w_scale, y_prev,
-                     y_out, nullptr, acc_dbg, dbg_tile_lo, dbg_tile_hi, stream);
+                     y_out, nullptr, acc_dbg, s_dbg, dbg_tile_lo, dbg_tile_hi, stream);
 }
 
 }  // extern "C"
@@ -269,12 +279,12 @@ int linear_impl(const dstar_fmdq_params* p, const float* base_dev, int32_t N, co
                 const uint16_t* perm, const int32_t* group_off, const int8_t* acodes,
                 const int8_t* hcodes, const int8_t* w, const int8_t* w_t, const float* w_scale,
                 const float* y_prev, float* y_out, float* gelu_out, int32_t* acc_dbg,
-                int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream) {
+                int64_t* s_dbg, int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream) {
   int64_t nt = 0;
   if (int rc = check_params(p, &nt)) return rc;
   if (N < 1 || N > (1 << 20) || N % 4 != 0)
     return set_error(DSTAR_EINVAL, "linear: N = %d must be a multiple of 4 in [4, 2^20]", N);
-  if (acc_dbg && (dbg_tile_lo < 0 || dbg_tile_lo >= dbg_tile_hi || dbg_tile_hi > nt))
+  if ((acc_dbg || s_dbg) && (dbg_tile_lo < 0 || dbg_tile_lo >= dbg_tile_hi || dbg_tile_hi > nt))
     return set_error(DSTAR_EINVAL, "linear: debug tile range [%d, %d) not within [0, %lld)",
                      dbg_tile_lo, dbg_tile_hi, (long long)nt);
   if (nt == 0) return DSTAR_OK;
@@ -283,11 +293,12 @@ int linear_impl(const dstar_fmdq_params* p, const float* base_dev, int32_t N, co
                      "linear: codes, perm, group_off, w, w_scale, y_prev and y_out must not be NULL");
   if (!aligned(codes, 16) || !aligned(w, 16) || !aligned(y_prev, 16) || !aligned(y_out, 16) ||
       !aligned(w_scale, 4) || !aligned(perm, 2) || !aligned(group_off, 4) ||
-      (acc_dbg && !aligned(acc_dbg, 4)) || (acodes && !aligned(acodes, 16)) ||
+      (acc_dbg && !aligned(acc_dbg, 4)) || (s_dbg && !aligned(s_dbg, 8)) ||
+      (acodes && !aligned(acodes, 16)) ||
       (hcodes && !aligned(hcodes, 16)) || (w_t && !aligned(w_t, 16)))
     return set_error(DSTAR_EALIGN,
                      "linear: codes, acodes, hcodes, w, w_t, y_prev, y_out must be 16-byte aligned "
-                     "(w_scale, group_off, acc_dbg 4-byte, perm 2-byte)");
+                     "(s_dbg 8-byte, w_scale, group_off, acc_dbg 4-byte, perm 2-byte)");
   LinearArgs a;
   a.codes = codes;
   a.perm = perm;
@@ -300,6 +311,7 @@ int linear_impl(const dstar_fmdq_params* p, const float* base_dev, int32_t N, co
   a.y_prev = y_prev;
   a.y_out = y_out;
   a.acc_dbg = acc_dbg;
+  a.s_dbg = s_dbg;
   a.dbg_lo = dbg_tile_lo;
   a.dbg_hi = dbg_tile_hi;
   a.rows = p->rows;
@@ -313,3 +325,75 @@ int linear_impl(const dstar_fmdq_params* p, const float* base_dev, int32_t N, co
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// The whole layer in one call, with the intermediates in a caller workspace.
+
+namespace dstar {
+
+namespace {
+inline int64_t round256(int64_t v) { return (v + 255) & ~int64_t(255); }
+}  // namespace
+
+LayerWorkspace layer_workspace(int64_t nt, int64_t K, int64_t T) {
+  LayerWorkspace w;
+  int64_t o = 0;
+  w.codes = o;  o += round256(nt * K * T);
+  w.acodes = o; o += round256(nt * T * K);
+  w.hcodes = o; o += round256(2 * nt * K * T);
+  w.tags = o;   o += round256(nt * K);
+  w.perm = o;   o += round256(2 * nt * K);
+  w.off = o;    o += round256(4 * nt * (DSTAR_FMDQ_NUM_BINS + 1));
+  w.total = o;
+  return w;
+}
+
+int layer_impl(const dstar_fmdq_params* p, int32_t N, const float* x_t, const float* x_prev,
+               const int8_t* w, const int8_t* w_t, const float* w_scale, const float* y_prev,
+               float* y_out, uint32_t* bit_hist, void* workspace, int64_t workspace_bytes,
+               void* stream) {
+  int64_t nt = 0;
+  if (int rc = check_params(p, &nt)) return rc;
+  if (N < 1 || N > (1 << 20) || N % 4 != 0)
+    return set_error(DSTAR_EINVAL, "layer: N = %d must be a multiple of 4 in [4, 2^20]", N);
+  if (nt == 0) return DSTAR_OK;
+  const LayerWorkspace ws = layer_workspace(nt, p->K, p->token_tile);
+  if (workspace == nullptr) return set_error(DSTAR_ENULL, "layer: workspace must not be NULL");
+  if (!aligned(workspace, 256)) return set_error(DSTAR_EALIGN, "layer: workspace must be 256-byte aligned");
+  if (workspace_bytes < ws.total)
+    return set_error(DSTAR_EINVAL, "layer: workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                     (long long)ws.total);
+  uint8_t* b = static_cast<uint8_t*>(workspace);
+  int8_t* codes = reinterpret_cast<int8_t*>(b + ws.codes);
+  int8_t* acodes = reinterpret_cast<int8_t*>(b + ws.acodes);
+  int8_t* hcodes = reinterpret_cast<int8_t*>(b + ws.hcodes);
+  uint8_t* tags = b + ws.tags;
+  uint16_t* perm = reinterpret_cast<uint16_t*>(b + ws.perm);
+  int32_t* off = reinterpret_cast<int32_t*>(b + ws.off);
+  if (int rc = quantize_impl(p, nullptr, x_t, x_prev, codes, tags, acodes, hcodes, bit_hist, stream)) return rc;
+  if (int rc = dstar_fmdq_bucket(p, tags, perm, off, stream)) return rc;
+  return linear_impl(p, nullptr, N, codes, perm, off, acodes, hcodes, w, w_t, w_scale, y_prev, y_out, nullptr,
+                     nullptr, nullptr, 0, 0, stream);
+}
+
+}  // namespace dstar
+
+extern "C" {
+
+int64_t dstar_fmdq_layer_workspace_size(const dstar_fmdq_params* p) {
+  clear_error();
+  int64_t nt = 0;
+  if (int rc = check_params(p, &nt)) return rc;
+  return layer_workspace(nt, p->K, p->token_tile).total;
+}
+
+int dstar_fmdq_layer(const dstar_fmdq_params* p, int32_t N, const float* x_t, const float* x_prev,
+                     const int8_t* w, const int8_t* w_t, const float* w_scale, const float* y_prev,
+                     float* y_out, uint32_t* bit_hist, void* workspace, int64_t workspace_bytes,
+                     void* stream) {
+  clear_error();
+  return layer_impl(p, N, x_t, x_prev, w, w_t, w_scale, y_prev, y_out, bit_hist, workspace,
+                    workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -68,7 +68,8 @@ struct LinearArgs {
   const float* w_scale;
   const float* y_prev;
   float* y_out;
-  int32_t* acc_dbg;
+  int32_t* acc_dbg;        // per-group accumulator dump (general kernel only)
+  int64_t* s_dbg;          // exact S dump, written by whichever kernel runs
   int32_t dbg_lo;
   int32_t dbg_hi;
   int64_t rows;
@@ -102,6 +103,20 @@ __device__ __forceinline__ float gelu_of(float yf) {
 int launch_gelu(const float* y, float* g, int64_t n, hipStream_t s);
 int launch_pack_weights(int32_t K, int32_t N, const int8_t* w, int8_t* w_t, hipStream_t s);
 int launch_linear_general(const LinearArgs& a, hipStream_t s);
+
+// Byte offsets of the intermediates in the workspace of the one-call layer
+// (each 256-byte aligned): codes, aligned codes, digit planes, tags, bucket
+// ids, bin offsets.
+struct LayerWorkspace {
+  int64_t codes, acodes, hcodes, tags, perm, off, total;
+};
+LayerWorkspace layer_workspace(int64_t nt, int64_t K, int64_t T);
+// The three stages on the caller's stream with the intermediates in
+// `workspace` (checked: non-NULL, 256-byte aligned, large enough).
+int layer_impl(const dstar_fmdq_params* p, int32_t N, const float* x_t, const float* x_prev,
+               const int8_t* w, const int8_t* w_t, const float* w_scale, const float* y_prev,
+               float* y_out, uint32_t* bit_hist, void* workspace, int64_t workspace_bytes,
+               void* stream);
 bool linear_mfma_supported(const LinearArgs& a);
 int launch_linear_mfma(const LinearArgs& a, hipStream_t s);
 

@@ -1,6 +1,8 @@
-// Stage 3 dispatch: the MFMA kernel for token tiles of 32 or 64 rows (K a
-// multiple of 4); the general kernel for other shapes and whenever the group
-// accumulators are dumped.
+// Stage 3 dispatch: the MFMA kernel for token tiles of 32 or 64 rows, K a
+// multiple of 64, with the aligned codes, digit planes and W^T given; the
+// general kernel for other shapes and whenever the per-group accumulators are
+// dumped (only the general kernel has them).  The S dump is written by
+// whichever kernel runs.
 #include "fmdq_internal.h"
 
 namespace dstar {

@@ -26,9 +26,10 @@
 // of the base, to the dense sum.
 //
 // Exactness.  int32 arithmetic wraps modulo 2^32 (shifts and adds included),
-// so the final accumulator equals S whenever |S| < 2^31; |S| ≤ 127 · Σ_k
-// 2^PoT_k, so a token tile is handled here only if 127 · Σ_k 2^PoT_k < 2^31
-// (computed from stage 2's bin counts).  Any other tile ("ineligible") is
+// so the final accumulator equals S whenever |S| < 2^31; |W| ≤ 128 (any
+// int8, −128 included) gives |S| ≤ 128 · Σ_k 2^PoT_k, so a token tile is
+// handled here only if 128 · Σ_k 2^PoT_k < 2^31 (computed from stage 2's bin
+// counts).  Any other tile ("ineligible") is
 // finished by an exact scalar path in the same workgroup that walks the
 // tile's FPoT groups in perm order with int32 group sums shifted into an int64
 // sum.
@@ -81,7 +82,7 @@ constexpr int kTags = DSTAR_FMDQ_NUM_TAGS;
 constexpr int kBins = DSTAR_FMDQ_NUM_BINS;
 constexpr int kAlignedPotMax = 6;  // q·2^e fits int8 when PoT ≤ 6
 constexpr int kTwoDigitPotMax = 13;  // q·2^e needs no third digit when PoT ≤ 13
-constexpr uint64_t kBoundLimit = 2147483647ull / 127ull;  // Σ 2^PoT limit
+constexpr uint64_t kBoundLimit = 2147483647ull / 128ull;  // Σ 2^PoT limit (|W| ≤ 128)
 constexpr int kBand = 8;           // row blocks per band of the block order
 
 template <int T>
@@ -243,8 +244,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   const int64_t nw = n0 + WN * wave;      // this wave's first column
   const int64_t tile0 = mb * kTiles;
   const int tiles_here = (int)min<int64_t>(kTiles, nt - tile0);
-  // This workgroup's tiles of codes, aligned codes and perm; all of W, W^T.
-  const rsrc_t r_codes = make_rsrc(a.codes + tile0 * K * T, (uint32_t)(tiles_here * K * T));
+  // This workgroup's tiles of aligned codes and perm; all of W, W^T.
   const rsrc_t r_perm = make_rsrc(a.perm + tile0 * K, (uint32_t)(tiles_here * K * 2));
   const rsrc_t r_ac = make_rsrc(a.acodes + tile0 * T * K, (uint32_t)(tiles_here * T * K));
   const rsrc_t r_w = make_rsrc(a.w, (uint32_t)(K * N));
@@ -649,6 +649,29 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the loads issued past the last unit
   }
 
+  // ---- Optional dump of the exact integer S of the eligible tiles in
+  // [dbg_lo, dbg_hi) (for checking; the ineligible ones are dumped by the
+  // scalar path below).  Lane layout of a 32x32 MFMA result: row
+  // 8·(r / 4) + 4·h + r % 4, column li.
+  if (a.s_dbg != nullptr) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int i = (32 * rb) / T;
+      const int64_t tau = tile0 + i;
+      if (i >= tiles_here || !eligible[i] || tau < a.dbg_lo || tau >= a.dbg_hi) continue;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int64_t n = nw + 32 * cb + li;
+        if (n >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t t = (32 * rb) % T + 8 * (r >> 2) + 4 * h + (r & 3);
+          a.s_dbg[((tau - a.dbg_lo) * T + t) * N + n] = (int64_t)acc[rb][cb][r];
+        }
+      }
+    }
+  }
+
   // ---- Epilogue: dequantize, add the cached output, store (float64 combine).
   double ws[CB];
 #pragma unroll
@@ -738,6 +761,10 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
 #pragma unroll
         for (int t = 0; t < 32; ++t) sum[t] += (int64_t)gs[t] << (DSTAR_FMDQ_TAG_OFFSET - g);
       }
+      if (a.s_dbg != nullptr && tau >= a.dbg_lo && tau < a.dbg_hi) {
+#pragma unroll
+        for (int t = 0; t < 32; ++t) a.s_dbg[((tau - a.dbg_lo) * T + t0 + t) * N + n] = sum[t];
+      }
 #pragma unroll
       for (int t = 0; t < 32; ++t) {
         const int64_t grow = tau * T + t0 + t;
@@ -760,14 +787,12 @@ int launch_tv(const LinearArgs& a, hipStream_t s) {
   const int64_t grid = row_blocks * col_blocks;
   if (grid > 0x7FFFFFFF || row_blocks > 0x7FFFFFFF)
     return set_error(DSTAR_EUNSUPPORTED, "fmdq_linear: grid too large");
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)linear_mfma_kernel<T, VecW, Gelu>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess)
-      return set_error(DSTAR_EHIP, "fmdq_linear: hipFuncSetAttribute: %s", hipGetErrorString(e));
-    attr_set = true;
-  }
+  // The LDS limit is a per-device property of the kernel: set it on every
+  // launch (a host-side call; cheap, thread-safe, right on any device).
+  hipError_t e = hipFuncSetAttribute((const void*)linear_mfma_kernel<T, VecW, Gelu>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  if (e != hipSuccess)
+    return set_error(DSTAR_EHIP, "fmdq_linear: hipFuncSetAttribute: %s", hipGetErrorString(e));
   hipLaunchKernelGGL((linear_mfma_kernel<T, VecW, Gelu>), dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s,
                      a, (int32_t)row_blocks, col_blocks);
   return check_launch("fmdq_linear (mfma)");

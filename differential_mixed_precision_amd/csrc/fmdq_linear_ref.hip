@@ -64,6 +64,11 @@ __global__ __launch_bounds__(kThreads) void linear_general_kernel(LinearArgs a, 
       }
     }
     if (!valid) continue;
+    if (a.s_dbg != nullptr && tile >= a.dbg_lo && tile < a.dbg_hi) {
+      int64_t* dst = a.s_dbg + (tile - a.dbg_lo) * (int64_t)T * N + n;
+#pragma unroll
+      for (int t = 0; t < T; ++t) dst[t * N] = s[t];
+    }
     const double base = a.base_dev != nullptr ? (double)*a.base_dev : a.base;
     const double ws = (double)a.w_scale[n];
 #pragma unroll

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define DSTAR_FMDQ_ABI_VERSION 9   /* also covers the entry points of dstar_sar.h */
+#define DSTAR_FMDQ_ABI_VERSION 10  /* also covers the entry points of dstar_sar.h */
 
 /* Rule constants (DSTAR §3.1 step 1; readings in the design notes):
  * PCeil of a b-bit sub-channel is 2^(b-2); PoT is capped at POT_MAX so that
@@ -177,7 +177,8 @@ int dstar_fmdq_pack_weights(int32_t K, int32_t N, const int8_t* w, int8_t* w_t,
  *              2^(15-g) * base.
  *   acodes     NULL, or stage 1's aligned codes.
  *   hcodes     NULL, or stage 1's digit planes (given with acodes).
- *   w          [K][N] int8 row-major, 16-byte aligned.
+ *   w          [K][N] int8 row-major, 16-byte aligned; any int8 value
+ *              (-128 included).
  *   w_t        NULL, or the [N][K] copy made by dstar_fmdq_pack_weights.
  *   w_scale    [N] float32, per-output-channel weight scale.
  *   y_prev     [rows][N] float32, the cached output Y_{t-1}.
@@ -188,7 +189,14 @@ int dstar_fmdq_pack_weights(int32_t K, int32_t N, const int8_t* w, int8_t* w_t,
  *              of code(τT+t, k) * w[k][n] for tiles τ in [dbg_tile_lo,
  *              dbg_tile_hi); groups absent from a tile and rows past a ragged
  *              end are written 0.  Needs 0 <= lo < hi <= n_t.  With acc_dbg
- *              the layer runs in the per-group kernel (slow; for checking).
+ *              the layer runs in the per-group kernel (slow; for checking):
+ *              only that kernel keeps one accumulator per FPoT group.
+ *   s_dbg      NULL, or [dbg_tile_hi - dbg_tile_lo][T][N] int64 (out),
+ *              8-byte aligned: the exact integer S of every output of the
+ *              tiles in [dbg_tile_lo, dbg_tile_hi) (0 on rows past a ragged
+ *              end), as the kernel that computes the layer holds it before
+ *              the dequantization: the MFMA kernel when acc_dbg is NULL and
+ *              the shape allows it, else the per-group kernel.  For checking.
  * Per output: S = Σ_g acc_g * 2^(15-g) (an exact integer);
  * y_out = fl32(f64(y_prev) + (f64(S) * f64(base)) * f64(w_scale[n])).
  * With acodes, hcodes and w_t given (T of 32 or 64, K % 64 == 0, K*N and
@@ -196,7 +204,7 @@ int dstar_fmdq_pack_weights(int32_t K, int32_t N, const int8_t* w, int8_t* w_t,
  * digits x w) + 2^15 * (d2 digits x w), the digit terms over the channels
  * with PoT >= 7 (resp. >= 14) of each token tile, which are prefixes of the
  * FPoT groups in perm; a token tile whose int32 accumulator it cannot prove
- * exact (127 * Σ_k 2^PoT_k >= 2^31) is finished by a per-group path over perm
+ * exact (128 * Σ_k 2^PoT_k >= 2^31; |W| <= 128) is finished by a per-group path over perm
  * and group_off.  Otherwise the per-group kernel runs. */
 int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N,
                       const int8_t* codes, const uint16_t* perm,
@@ -204,15 +212,16 @@ int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N,
                       const int8_t* hcodes, const int8_t* w, const int8_t* w_t,
                       const float* w_scale,
                       const float* y_prev, float* y_out, int32_t* acc_dbg,
-                      int32_t dbg_tile_lo, int32_t dbg_tile_hi, void* stream);
+                      int64_t* s_dbg, int32_t dbg_tile_lo, int32_t dbg_tile_hi,
+                      void* stream);
 
 /* Stage 3 with the MLP activation fused into its epilogue (DSTAR §4.3
  * "Linear Operation": the GELU that follows the first linear of a DiT MLP is
  * applied by the vector unit as the output is produced; §4.2 "Design of
  * VPU").  Arguments and results as for dstar_fmdq_linear (without the
  * accumulator dump), plus
- *   gelu_out  [rows][N] float32 (out), 16-byte aligned, not aliasing y_prev or
- *             y_out: GELU(Y_t) for every output written to y_out, in the tanh
+ *   gelu_out  [rows][N] float32 (out), 16-byte aligned, sharing no byte with
+ *             y_prev or y_out (DSTAR_EINVAL otherwise): GELU(Y_t) for every output written to y_out, in the tanh
  *             form y / (1 + exp(-2u)), u = 0.7978845608028654 * (y + 0.044715 *
  *             (y*y)*y), evaluated in float64 and rounded once to float32 (the
  *             pages give no formula; their unit uses piecewise cubics).
@@ -263,8 +272,32 @@ int dstar_fmdq_linear_dyn(const dstar_fmdq_params* p, const float* base,
                           const int8_t* hcodes, const int8_t* w,
                           const int8_t* w_t, const float* w_scale,
                           const float* y_prev, float* y_out, int32_t* acc_dbg,
-                          int32_t dbg_tile_lo, int32_t dbg_tile_hi,
-                          void* stream);
+                          int64_t* s_dbg, int32_t dbg_tile_lo,
+                          int32_t dbg_tile_hi, void* stream);
+
+/* The whole layer in one call: stages 1, 2 and 3 (dstar_fmdq_quantize with
+ * the aligned codes and digit planes, dstar_fmdq_bucket, dstar_fmdq_linear)
+ * on `stream`, with every intermediate (codes, tags, aligned codes, digit
+ * planes, bucket ids and bin offsets) in a caller workspace (DSTAR §3.1 steps
+ * 1-5; §4.3 "Linear Operation": quantization, reorder and the GEMM with its
+ * fused reverse differential as one pipelined operation).
+ *   x_t, x_prev, w, w_t, w_scale, y_prev, y_out, bit_hist  as for the stages
+ *              (w_t may be NULL: then the per-group kernel runs).
+ *   workspace  device memory, 256-byte aligned, of at least
+ *              dstar_fmdq_layer_workspace_size(p) bytes; its contents on entry
+ *              do not matter, and it holds the intermediates afterwards.
+ *              Two calls that share a workspace must not overlap in time.
+ * Errors as for the stages, plus DSTAR_EINVAL when workspace_bytes is too
+ * small.  The library allocates nothing. */
+int dstar_fmdq_layer(const dstar_fmdq_params* p, int32_t N, const float* x_t,
+                     const float* x_prev, const int8_t* w, const int8_t* w_t,
+                     const float* w_scale, const float* y_prev, float* y_out,
+                     uint32_t* bit_hist, void* workspace, int64_t workspace_bytes,
+                     void* stream);
+
+/* Bytes of workspace dstar_fmdq_layer needs for these parameters (>= 0), or a
+ * negative DSTAR_E* code for invalid parameters. */
+int64_t dstar_fmdq_layer_workspace_size(const dstar_fmdq_params* p);
 
 /* Message describing the last error of the calling thread ("" if none). */
 const char* dstar_fmdq_last_error(void);

@@ -51,10 +51,6 @@ the design notes of this repository):
   every group.
 * The per-group sums are exact integers; S = Σ_g acc_g · 2^(15−g) in int64; the
   output is fl32(f64(Y_{t−1}) + (f64(S) · f64(base)) · f64(w_scale[n])).
-* The GPU path's 8-bit operands (aligned codes and digit planes) are a
-  re-association of the same exact sum: a code shifted to units of the base,
-  a = q·2^e, is split into signed digits a = d0 + 2^7·d1 + 2^15·d2 (the left
-  shifts of §3.1 ❺ at three fixed offsets).
 
 Parity of every function here is pinned by tests against values printed in
 DSTAR, closed forms, library routines and brute force (``tests/test_oracle_*``).
@@ -210,76 +206,6 @@ def quantize(x_t: np.ndarray, x_prev: np.ndarray, token_tile: int, base: float,
     tags = (tag | (((bits // 2) - 1) << PREC_SHIFT)).astype(np.uint8)
     hist = np.array([(bits == b).sum() for b in (2, 4, 6, 8)], dtype=np.int64)
     return codes, tags, hist
-
-
-#: Shifts of the three signed digits a shift-aligned code is split into.
-DIGIT_SHIFTS = (0, 7, 15)
-#: Largest PoT whose shift-aligned codes fit 8 bits (|q·2^e| ≤ 2^PoT ≤ 64).
-ALIGNED_POT_MAX = 6
-#: Largest PoT whose shift-aligned codes need no third digit (|q·2^e| ≤ 2^13).
-TWO_DIGIT_POT_MAX = 13
-
-
-def shifted_codes(codes: np.ndarray, tags: np.ndarray) -> np.ndarray:
-    """a = q·2^e: every code in units of the base, int64 [n_t][K][T].
-
-    DSTAR §3.1 ❺ aligns partial sums of different FPoT by left shifts of the
-    FPoT difference; shifting each code by its own step exponent e brings all
-    of them to the common unit (the base), where they can be summed directly.
-    """
-    e = step_exponent(tag_of(tags))                              # [n_t][K]
-    return np.asarray(codes).astype(np.int64) * np.left_shift(np.int64(1), e)[:, :, None]
-
-
-def code_digits(a: np.ndarray):
-    """Signed digits of a shift-aligned code: a = d0 + 2^7·d1 + 2^15·d2.
-
-    d0 is the residue of a modulo 2^7 taken in [−64, 63]; d1 is the residue of
-    the remaining multiple of 2^7 (divided by 2^7) modulo 2^8, in [−128, 127];
-    d2 is what is left, divided by 2^15.  For |a| ≤ 2^21 (PoT ≤ 21) every
-    digit fits 8 bits.
-    """
-    a = np.asarray(a).astype(np.int64)
-    d0 = ((a + 64) % 128) - 64
-    r1 = (a - d0) // 128
-    d1 = ((r1 + 128) % 256) - 128
-    d2 = (r1 - d1) // 256
-    return d0, d1, d2
-
-
-def aligned_codes(codes: np.ndarray, tags: np.ndarray) -> np.ndarray:
-    """The 8-bit operand of the dense GEMM, row-major [n_t·T][K].
-
-    Row τ·T + t, column k: a = q·2^e (the code in units of the base) when the
-    sub-channel's PoT ≤ 6, where |a| ≤ 2^PoT ≤ 64 fits 8 bits; for PoT ≥ 7 the
-    low digit d0 of a (``code_digits``).  Rows past a ragged end are 0.
-    """
-    codes = np.asarray(codes)
-    nt, K, T = codes.shape
-    pot = step_exponent(tag_of(tags)) + (bits_of(tags) - 2)
-    a = shifted_codes(codes, tags)
-    d0, _, _ = code_digits(a)
-    out = np.where((pot <= ALIGNED_POT_MAX)[:, :, None], a, d0)   # [n_t][K][T]
-    assert np.abs(out).max(initial=0) <= 64
-    return np.ascontiguousarray(out.transpose(0, 2, 1).reshape(nt * T, K)).astype(np.int8)
-
-
-def heavy_digits(codes: np.ndarray, tags: np.ndarray) -> np.ndarray:
-    """Digit planes of the wide shift-aligned codes, int8 [2][n_t][K][T].
-
-    Plane 0 holds d1 of every sub-channel with PoT ≥ 7, plane 1 holds d2 of
-    every sub-channel with PoT ≥ 14 (``code_digits``); all other entries are 0
-    (for 7 ≤ PoT ≤ 13, |a| ≤ 2^13 makes d2 = 0).  Together with the aligned
-    codes, S = A·W + 2^7·(D1·W) + 2^15·(D2·W) over a tile's channels.
-    """
-    codes = np.asarray(codes)
-    pot = (step_exponent(tag_of(tags)) + (bits_of(tags) - 2))[:, :, None]
-    _, d1, d2 = code_digits(shifted_codes(codes, tags))
-    assert not np.any((d2 != 0) & (pot <= TWO_DIGIT_POT_MAX))
-    planes = np.stack([np.where(pot > ALIGNED_POT_MAX, d1, 0),
-                       np.where(pot > TWO_DIGIT_POT_MAX, d2, 0)])
-    assert np.abs(planes).max(initial=0) <= 128
-    return planes.astype(np.int8)
 
 
 def tag_of(tags: np.ndarray) -> np.ndarray:
@@ -567,5 +493,4 @@ def layer(x_t, x_prev, w, w_scale, y_prev, base, token_tile, k0):
     codes, tags, hist = quantize(x_t, x_prev, token_tile, base, k0)
     perm, off = bucket(tags)
     y = linear(codes, tags, perm, off, w, w_scale, y_prev, base, token_tile)
-    return dict(codes=codes, tags=tags, acodes=aligned_codes(codes, tags),
-                hcodes=heavy_digits(codes, tags), hist=hist, perm=perm, group_off=off, y=y)
+    return dict(codes=codes, tags=tags, hist=hist, perm=perm, group_off=off, y=y)

@@ -29,7 +29,7 @@ def _header():
 
 def test_library_exports_every_declared_entry_point(lib):
     text = _header()
-    declared = set(re.findall(r"^\s*(?:int|const char\*)\s+(dstar_fmdq_\w+)\s*\(", text, re.M))
+    declared = set(re.findall(r"^\s*(?:int64_t|int|const char\*)\s+(dstar_fmdq_\w+)\s*\(", text, re.M))
     assert declared == set(lib.SYMBOLS)
     raw = ctypes.CDLL(lib.LIB_PATH)
     for name in declared:
@@ -69,10 +69,10 @@ def _q(lib, p, x=FAKE, xp=FAKE, codes=FAKE, tags=FAKE, acodes=None, hcodes=None,
 
 
 def _l(lib, p, N=64, codes=FAKE, perm=FAKE, off=FAKE, acodes=None, hcodes=None, w=FAKE, w_t=None,
-       ws=FAKE, y0=FAKE, y1=FAKE, dbg=None, lo=0, hi=0):
+       ws=FAKE, y0=FAKE, y1=FAKE, dbg=None, lo=0, hi=0, sdbg=None):
     L = lib.load()
     return L.dstar_fmdq_linear(ctypes.byref(p), N, codes, perm, off, acodes, hcodes, w, w_t, ws, y0, y1,
-                               dbg, lo, hi, 0)
+                               dbg, sdbg, lo, hi, 0)
 
 
 @pytest.mark.parametrize("field,value", [
@@ -130,6 +130,8 @@ def test_null_and_alignment_errors(lib):
     assert _l(lib, p, dbg=FAKE, lo=1, hi=1) == lib.EINVAL
     assert _l(lib, p, dbg=FAKE, lo=0, hi=3) == lib.EINVAL    # 64 rows / 32 = 2 tiles
     assert "debug tile range" in L.dstar_fmdq_last_error().decode()
+    assert _l(lib, p, sdbg=FAKE, lo=0, hi=3) == lib.EINVAL   # the S dump shares the range check
+    assert _l(lib, p, sdbg=FAKE + 4, lo=0, hi=1) == lib.EALIGN   # int64: 8-byte aligned
     # 2-bit slice stream
     se = lambda q, **kw: L.dstar_fmdq_slice_encode(ctypes.byref(q), kw.get("c", FAKE), FAKE, kw.get("e", FAKE),
                                                    FAKE, kw.get("o", FAKE), 0)
@@ -144,6 +146,10 @@ def test_null_and_alignment_errors(lib):
     assert lg(FAKE + 4) == lib.EALIGN
     assert lg(FAKE + 0x1000, y1=FAKE + 0x1000) == lib.EINVAL      # gelu_out aliases y_out
     assert lg(FAKE + 0x1000, y0=FAKE + 0x1000) == lib.EINVAL      # ... or y_prev
+    # any shared byte is rejected: one row (64 floats) apart overlaps for 64 rows
+    assert lg(FAKE + 0x1000 + 256, y1=FAKE + 0x1000) == lib.EINVAL
+    assert lg(FAKE + 0x1000, y0=FAKE + 0x1000 + 256) == lib.EINVAL
+    assert "overlaps" in L.dstar_fmdq_last_error().decode()
     assert L.dstar_fmdq_gelu(FAKE, FAKE, -1, 0) == lib.EINVAL
     assert L.dstar_fmdq_gelu(None, FAKE, 8, 0) == lib.ENULL
     assert L.dstar_fmdq_gelu(FAKE + 4, FAKE, 8, 0) == lib.EALIGN
@@ -160,9 +166,34 @@ def test_null_and_alignment_errors(lib):
     assert L.dstar_fmdq_quantize_dyn(ctypes.byref(p), FAKE, None, FAKE, FAKE, FAKE, None, None, None,
                                      0) == lib.ENULL
     assert L.dstar_fmdq_linear_dyn(ctypes.byref(p), None, 64, FAKE, FAKE, FAKE, None, None, FAKE, None,
-                                   FAKE, FAKE, FAKE, None, 0, 0, 0) == lib.ENULL
+                                   FAKE, FAKE, FAKE, None, None, 0, 0, 0) == lib.ENULL
     assert L.dstar_fmdq_linear_dyn(ctypes.byref(p), FAKE, 66, FAKE, FAKE, FAKE, None, None, FAKE, None,
-                                   FAKE, FAKE, FAKE, None, 0, 0, 0) == lib.EINVAL
+                                   FAKE, FAKE, FAKE, None, None, 0, 0, 0) == lib.EINVAL
+
+
+def test_layer_workspace_and_its_checks(lib):
+    """The one-call layer: its workspace size is the sum of the intermediates
+    (each rounded up to 256 bytes), and a missing, misaligned or short
+    workspace is rejected before any launch."""
+    L = lib.load()
+    r256 = lambda v: (v + 255) // 256 * 256
+    for rows, K, T in ((8192, 1152, 32), (300, 1152, 64), (40, 33, 16)):
+        p = lib.make_params(rows, K, T, 0.05, 2)
+        nt = (rows + T - 1) // T
+        want = (r256(nt * K * T) * 2 + r256(2 * nt * K * T) + r256(nt * K) + r256(2 * nt * K) +
+                r256(4 * nt * 65))
+        assert lib.layer_workspace_size(p) == want
+    bad = lib.make_params(64, 64, 48, 0.05, 2)
+    assert L.dstar_fmdq_layer_workspace_size(ctypes.byref(bad)) == lib.EINVAL
+    p = lib.make_params(64, 64, 32, 0.05, 2)
+    need = lib.layer_workspace_size(p)
+    lay = lambda ws, nb, N=64: L.dstar_fmdq_layer(ctypes.byref(p), N, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                  FAKE, None, ws, nb, 0)
+    assert lay(None, need) == lib.ENULL
+    assert lay(FAKE + 16, need) == lib.EALIGN
+    assert lay(FAKE, need - 1) == lib.EINVAL
+    assert "needed" in L.dstar_fmdq_last_error().decode()
+    assert lay(FAKE, need, N=66) == lib.EINVAL
 
 
 def test_empty_input_is_a_no_op(lib):

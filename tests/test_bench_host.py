@@ -33,10 +33,34 @@ def test_launches_are_attributed_to_the_following_stage3_launch():
 
 
 def test_stage_algorithmic_bytes_count_each_array_once():
-    rows, K, N, T = 8192, 1152, 4608, 32
+    """The per-launch byte counts are the scope's formulas: stage 1 reads both
+    float32 inputs and writes codes and tags (the aligned-operand write is
+    reported apart), stage 2 reads tags and writes ids and 17 offsets per
+    tile, stage 3 reads codes, W, ids, offsets and w_scale and streams Y."""
+    rows, K, N, T = 4608, 3072, 12288, 32
     nt = rows // T
     q = bench.algorithmic("quantize", rows, K, N, T)
-    assert q == dict(bytes=8 * rows * K + 2 * nt * T * K + nt * K + 16, ops=0)
+    assert q == dict(bytes=8 * rows * K + rows * K + nt * K + 16, ops=0, extra_bytes=rows * K)
+    b = bench.algorithmic("bucket", rows, K, N, T)
+    assert b["bytes"] == 3 * nt * K + 68 * nt
     lin = bench.algorithmic("linear", rows, K, N, T)
     assert lin["ops"] == 2 * rows * N * K
-    assert lin["bytes"] == nt * T * K + K * N + 2 * nt * K + 260 * nt + 4 * N + 8 * rows * N
+    assert lin["bytes"] == rows * K + K * N + 2 * nt * K + 68 * nt + 4 * N + 8 * rows * N
+    # the table of the scope: FLUX-style fc1 stage 3 moves 506 MB for 348 G ops
+    assert round(lin["bytes"] / 1e6) == 506 and round(lin["ops"] / 1e9) == 348
+
+
+def test_headline_is_the_largest_single_gpu_workload():
+    from gen import workloads as wl
+    big = max(wl.CONFIGS.values(), key=lambda c: sum(2 * c["rows"] * k * n for k, n in c["layers"].values()))
+    assert bench.HEADLINE == big["name"] == "flux-large"
+
+
+def test_roofline_takes_the_longest_stage():
+    kernels = {"quantize@fc1": dict(us_mean=40.0, bound="hbm", gbs=3000.0, tops=0.0, traffic=None,
+                                    alg_bytes=1, alg_ops=0),
+               "linear@fc1": dict(us_mean=200.0, bound="mfma", gbs=2500.0, tops=1740.0, traffic=123,
+                                  alg_bytes=2, alg_ops=3)}
+    r = bench.roofline_of(kernels)
+    assert r["kernel"] == "linear@fc1" and r["bound"] == "mfma" and r["unit"] == "TOP/s"
+    assert abs(r["frac"] - 1740.0 / bench.INT8_PEAK_TOPS) < 1e-12 and r["traffic"] == 123

@@ -14,6 +14,7 @@ import pytest
 
 from gen import workloads as wl
 from oracle import fmdq
+from tests import digits
 
 pytestmark = pytest.mark.gpu
 
@@ -35,15 +36,17 @@ def dm():
     return dm
 
 
-def gpu_layer(dm, d, dbg=None, inplace=False, y_prev_np=None, dynamic=False):
+def gpu_layer(dm, d, dbg=None, inplace=False, y_prev_np=None, dynamic=False, sdump=None):
     """Runs the three stages on cuda:0; every output buffer starts as garbage.
 
     Stage 3 runs twice from the same codes: once as the product path (no
-    accumulator dump: the MFMA kernel where the shape allows it) -> "y", and,
-    when ``dbg`` names a tile range, once more with the group accumulators
-    dumped (the per-group kernel) -> "y_dbg" and "acc".  With ``dynamic`` the
-    base is found on the device first (dynamic_base -> "base") and stages 1
-    and 3 read it from there (quantize_dyn, linear_dyn)."""
+    accumulator dump: the MFMA kernel where the shape allows it) -> "y", with
+    the exact S of the tiles in ``sdump`` (default: ``dbg``) dumped by that
+    same kernel -> "s"; and, when ``dbg`` names a tile range, once more with
+    the group accumulators dumped (the per-group kernel) -> "y_dbg" and
+    "acc".  With ``dynamic`` the base is found on the device first
+    (dynamic_base -> "base") and stages 1 and 3 read it from there
+    (quantize_dyn, linear_dyn)."""
     import torch
     dev = torch.device("cuda:0")
     rows, K, N, T = d["rows"], d["K"], d["N"], d["token_tile"]
@@ -72,12 +75,21 @@ def gpu_layer(dm, d, dbg=None, inplace=False, y_prev_np=None, dynamic=False):
     else:
         dm.quantize(p, x_t, x_p, codes, tags, acodes, hcodes, hist)
     dm.bucket(p, tags, perm, off)
+    sd = sdump if sdump is not None else dbg
+    s_dbg, slo, shi = None, 0, 0
+    if sd is not None:
+        slo, shi = sd
+        s_dbg = torch.full((shi - slo, T, N), 0x5A5A5A5A5A5A, dtype=torch.int64, device=dev)
     if dynamic:
-        dm.linear_dyn(p, base, N, codes, perm, off, acodes, hcodes, w, w_t, ws, y0, y1)
+        dm.linear_dyn(p, base, N, codes, perm, off, acodes, hcodes, w, w_t, ws, y0, y1,
+                      dbg_tile_lo=slo, dbg_tile_hi=shi, s_dbg=s_dbg)
     else:
-        dm.linear(p, N, codes, perm, off, acodes, hcodes, w, w_t, ws, y0, y1)
+        dm.linear(p, N, codes, perm, off, acodes, hcodes, w, w_t, ws, y0, y1,
+                  dbg_tile_lo=slo, dbg_tile_hi=shi, s_dbg=s_dbg)
     out = dict(codes=codes, tags=tags, acodes=acodes, hcodes=hcodes, w_t=w_t, hist=hist, perm=perm,
                group_off=off, y=y1, base=base)
+    if s_dbg is not None:
+        out["s"] = s_dbg
     if dbg is not None:
         lo, hi = dbg
         acc = torch.full((hi - lo, 16, T, N), 0x7777, dtype=torch.int32, device=dev)
@@ -92,6 +104,29 @@ def gpu_layer(dm, d, dbg=None, inplace=False, y_prev_np=None, dynamic=False):
     out = {k: v.cpu().numpy() for k, v in out.items()}
     out["perm"] = out["perm"].view(np.uint16)
     return out
+
+
+def par_linear(codes, tags, perm, off, w, w_scale, y_prev, base, T):
+    """fmdq.linear over every token tile, run on chunks of tiles in parallel
+    threads (one BLAS thread each): the oracle's own function, called per
+    chunk; the rows of each chunk are taken from its call."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    rows = y_prev.shape[0]
+    nt = (rows + T - 1) // T
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    chunks = [c for c in np.array_split(np.arange(nt), 2 * workers) if len(c)]
+    y = np.array(y_prev, dtype=np.float32, copy=True)
+
+    def run(ch):
+        return ch, fmdq.linear(codes, tags, perm, off, w, w_scale, y_prev, base, T, tiles=ch)
+
+    with threadpool_limits(limits=1), ThreadPoolExecutor(workers) as ex:
+        for ch, yy in ex.map(run, chunks):
+            r0, r1 = int(ch[0]) * T, min((int(ch[-1]) + 1) * T, rows)
+            y[r0:r1] = yy[r0:r1]
+    return y
 
 
 def check_y(y_gpu, y_orc, y_prev, what=""):
@@ -113,14 +148,8 @@ def check_y(y_gpu, y_orc, y_prev, what=""):
 def check_integer_stages(g, codes, tags, hist, perm, off, what="", w=None):
     np.testing.assert_array_equal(g["codes"], codes, err_msg=f"{what}: codes")
     np.testing.assert_array_equal(g["tags"], tags, err_msg=f"{what}: tags")
-    np.testing.assert_array_equal(g["acodes"], fmdq.aligned_codes(codes, tags), err_msg=f"{what}: aligned codes")
-    # digit planes: only the entries stage 1 defines (PoT >= 7, resp. >= 14)
-    pot = fmdq.step_exponent(fmdq.tag_of(tags)) + fmdq.bits_of(tags) - 2
-    h = fmdq.heavy_digits(codes, tags)
-    for plane, lo_pot in ((0, 7), (1, 14)):
-        m = np.broadcast_to((pot >= lo_pot)[:, :, None], codes.shape)
-        np.testing.assert_array_equal(g["hcodes"][plane][m], h[plane][m],
-                                      err_msg=f"{what}: digit plane {plane}")
+    # stage 3's 8-bit operands, by identity against the oracle's codes and tags
+    digits.check_operands(g["acodes"], g["hcodes"], codes, tags, what)
     if w is not None:
         np.testing.assert_array_equal(g["w_t"], w.T, err_msg=f"{what}: packed weights")
     np.testing.assert_array_equal(g["hist"].astype(np.int64), hist, err_msg=f"{what}: bit histogram")
@@ -145,10 +174,20 @@ def full_compare(dm, d, inplace=False, dump=True):
     for tau in range(nt):
         np.testing.assert_array_equal(g["acc"][tau].astype(np.int64), accs[tau],
                                       err_msg=f"{d['name']}: group accumulators of tile {tau}")
+    check_s(g["s"], accs, range(nt), 0, d["name"])
     y_prev = d["y_prev"]
     check_y(g["y_dbg"], y, y_prev, d["name"] + " (per-group kernel)")
     check_y(g["y"], y, y_prev, d["name"])
     return g, y
+
+
+def check_s(s_gpu, accs, tiles, lo, what=""):
+    """The product kernel's exact integer S of each tile against the oracle's
+    per-FPoT-group accumulators aligned by shifts (shift_combine)."""
+    for tau in tiles:
+        np.testing.assert_array_equal(s_gpu[tau - lo], fmdq.shift_combine(accs[tau]),
+                                      err_msg=f"{what}: S of tile {tau} (product kernel)")
+    log(f"  {what}: S of {len(list(tiles))} tiles bit-exact (product kernel)")
 
 
 SMALL = [
@@ -201,6 +240,45 @@ def test_abi_limits_match_oracle(dm, case):
     full_compare(dm, d, dump=d["N"] <= 65536)
 
 
+def aligned_workspace(torch, nbytes, dev):
+    """A uint8 device tensor of nbytes whose data pointer is 256-byte aligned."""
+    raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+    off = (-raw.data_ptr()) % 256
+    return raw[off:off + nbytes]
+
+
+@pytest.mark.parametrize("case", [SMALL[0], SMALL[1], SMALL[3], SMALL[8], SMALL[13], SMALL[14]],
+                         ids=lambda c: f"{c['rows']}x{c['K']}x{c['N']}-T{c['T']}-s{c['seed']}")
+def test_one_call_layer_matches_oracle(dm, case):
+    """dstar_fmdq_layer (the three stages in one call, intermediates in a
+    caller workspace): Y_t bit for bit and the bit histogram, against the
+    oracle; the workspace holds the codes and tags afterwards."""
+    import torch
+    dev = torch.device("cuda:0")
+    c = dict(case)
+    d = wl.make_custom(c.pop("rows"), c.pop("K"), c.pop("N"), c.pop("T"), seed=c.pop("seed"), **c)
+    rows, K, N, T = d["rows"], d["K"], d["N"], d["token_tile"]
+    log(f"case {d['name']} (one-call layer)")
+    p = dm.make_params(rows, K, T, float(d["base"]), d["k0"], d["tokens_per_seq"])
+    need = dm.layer_workspace_size(p)
+    ws = aligned_workspace(torch, need, dev)
+    ws.fill_(0xA5)
+    w = torch.from_numpy(d["w"]).to(dev)
+    w_t = torch.empty((N, K), dtype=torch.int8, device=dev)
+    dm.pack_weights(K, N, w, w_t)
+    y0 = torch.from_numpy(d["y_prev"]).to(dev)
+    y1 = torch.full((rows, N), float("nan"), dtype=torch.float32, device=dev)
+    hist = torch.zeros(4, dtype=torch.int32, device=dev)
+    dm.layer(p, N, torch.from_numpy(d["x_t"]).to(dev), torch.from_numpy(d["x_prev"]).to(dev), w, w_t,
+             torch.from_numpy(d["w_scale"]).to(dev), y0, y1, ws, hist)
+    torch.cuda.synchronize()
+    r = fmdq.layer(d["x_t"], d["x_prev"], d["w"], d["w_scale"], d["y_prev"], d["base"], T, d["k0"])
+    check_y(y1.cpu().numpy(), r["y"], d["y_prev"], d["name"] + " (one call)")
+    np.testing.assert_array_equal(hist.cpu().numpy().astype(np.int64), r["hist"])
+    nt = (rows + T - 1) // T
+    np.testing.assert_array_equal(ws[:nt * K * T].cpu().numpy().view(np.int8).reshape(nt, K, T), r["codes"])
+
+
 def test_zero_delta_gives_cached_output_bit_exact(dm):
     d = wl.make_custom(96, 64, 40, 32, seed=12, zero_delta=True)
     g, y = full_compare(dm, d)
@@ -242,11 +320,62 @@ def test_config0_full(dm):
 
 
 def test_determinism(dm):
+    """Ten runs of the same layer give the same bits in every output (the
+    stages have no atomics whose order could change a result)."""
     d = wl.make_custom(512, 1152, 640, 32, seed=15, heavy=0.05)
     a = gpu_layer(dm, d, dbg=(0, 16))
-    b = gpu_layer(dm, d, dbg=(0, 16))
-    for k in a:
-        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+    for r in range(9):
+        b = gpu_layer(dm, d, dbg=(0, 16))
+        for k in a:
+            np.testing.assert_array_equal(a[k], b[k], err_msg=f"run {r + 2}: {k}")
+    log("  10 runs bit-identical")
+
+
+def w_minus_128_case(K, T, pot_heavy, n_heavy, seed):
+    """One token tile at the int32 exactness bound of the product kernel:
+    n_heavy channels whose Δ is −base·2^pot_heavy in every row (code −64 at
+    step 2^(pot_heavy−6), a = −2^pot_heavy), the other channels small, and W
+    = −128 on the heavy channels of column 0 (|S| reaches 128·Σ 2^PoT there).
+    """
+    rng = np.random.default_rng(seed)
+    N = 64
+    base = np.float32(2.0 ** -6)
+    x_prev = np.zeros((T, K), dtype=np.float32)
+    delta = rng.standard_normal((T, K)) * float(base) * 0.3        # PoT 0 .. 1
+    delta[:, :n_heavy] = -float(base) * 2.0 ** pot_heavy
+    x_t = delta.astype(np.float32)
+    w = rng.integers(-127, 128, (K, N)).astype(np.int8)
+    w[:n_heavy, 0] = -128
+    w[:n_heavy, 1] = 127
+    return dict(x_t=x_t, x_prev=x_prev, w=w, w_scale=rng.uniform(1e-3, 1e-2, N).astype(np.float32),
+                y_prev=rng.standard_normal((T, N)).astype(np.float32), base=base, k0=2, token_tile=T,
+                rows=T, tokens_per_seq=T, K=K, N=N, name=f"w=-128 K={K} PoT={pot_heavy}x{n_heavy}")
+
+
+@pytest.mark.parametrize("K,pot,n_heavy", [(1024, 14, 1024), (64, 21, 8), (1024, 14, 1016)],
+                         ids=["at-2^24", "pot21-at-bound", "just-under"])
+def test_int32_bound_with_w_minus_128(dm, K, pot, n_heavy):
+    """The product kernel proves a tile exact only when 128·Σ_k 2^PoT_k < 2^31
+    (|W| ≤ 128: int8 includes −128).  At Σ 2^PoT = 2^24 a column of −128 makes
+    S = +2^31, which int32 cannot hold: that tile must take the exact per-group
+    path.  Just under the bound the MFMA path holds S exactly.  Y_t and S are
+    compared with the oracle bit for bit."""
+    d = w_minus_128_case(K, 32, pot, n_heavy, seed=K + pot + n_heavy)
+    codes, tags, hist = fmdq.quantize(d["x_t"], d["x_prev"], 32, d["base"], d["k0"])
+    pot_all = digits.pot_of(tags)
+    bound = int((1 << pot_all.astype(np.int64)).sum())
+    perm, off = fmdq.bucket(tags)
+    y, accs = fmdq.linear(codes, tags, perm, off, d["w"], d["w_scale"], d["y_prev"], d["base"], 32,
+                          return_acc=True)
+    s0 = fmdq.shift_combine(accs[0])
+    log(f"case {d['name']}: sum 2^PoT = {bound} (limit {(2 ** 31 - 1) // 128}), "
+        f"S[0][0] = {int(s0[0, 0])}, max |S| = {int(np.abs(s0).max())}")
+    if n_heavy == K or pot == 21:
+        assert bound >= (1 << 24) - (1 << 10) and abs(int(s0[0, 0])) >= (1 << 31) - (1 << 20)
+    g = gpu_layer(dm, d, sdump=(0, 1))
+    check_integer_stages(g, codes, tags, hist, perm, off, d["name"], d["w"])
+    check_s(g["s"], accs, [0], 0, d["name"])
+    check_y(g["y"], y, d["y_prev"], d["name"])
 
 
 def test_timestep_chain_in_place(dm):
@@ -328,31 +457,68 @@ FULL = [(1, "fc1"), (1, "fc2"), (2, "qkv"), (2, "fc1"), (2, "fc2"), (3, "fc1"), 
 
 @pytest.mark.parametrize("cfg,layer", FULL, ids=lambda v: str(v))
 def test_full_size_workloads(dm, cfg, layer):
-    """Full-size workload, pair 1: all integer stages compared in full; Y and
-    the group accumulators on sampled token tiles (first, second, middle,
-    last — ragged where the workload has one — and two seeded random tiles)."""
+    """Full-size workload, pair 1: every integer stage in full; Y_t of every
+    token tile against the oracle's whole layer, bit for bit, from both the
+    product kernel and the per-group kernel; the product kernel's exact S on
+    the last eight tiles (the ragged one included where the workload has one)
+    and the per-group kernel's accumulators on the last two."""
     t0 = time.time()
     d = wl.make_inputs(cfg, layer, 1)
     rows, T = d["rows"], d["token_tile"]
     nt = (rows + T - 1) // T
-    rng = np.random.default_rng(100 + cfg)
-    sample = sorted(set([0, 1, nt // 2, nt - 2, nt - 1] + [int(v) for v in rng.integers(0, nt, 2)]))
+    s_lo = max(0, nt - 8)
     log(f"case config {cfg} {layer}: rows={rows} K={d['K']} N={d['N']} T={T} tiles={nt} "
-        f"sampled tiles {sample} (inputs {time.time() - t0:.1f}s)")
-    g = gpu_layer(dm, d, dbg=(nt - 2, nt))
+        f"(inputs {time.time() - t0:.1f}s)")
+    g = gpu_layer(dm, d, dbg=(nt - 2, nt), sdump=(s_lo, nt))
     log(f"  gpu done {time.time() - t0:.1f}s")
     codes, tags, hist = fmdq.quantize(d["x_t"], d["x_prev"], T, d["base"], d["k0"])
     perm, off = fmdq.bucket(tags)
     log(f"  oracle quantize+bucket done {time.time() - t0:.1f}s")
     check_integer_stages(g, codes, tags, hist, perm, off, d["name"], d["w"])
-    y, accs = fmdq.linear(codes, tags, perm, off, d["w"], d["w_scale"], d["y_prev"], d["base"], T,
-                          tiles=sample, return_acc=True)
+    y = par_linear(codes, tags, perm, off, d["w"], d["w_scale"], d["y_prev"], d["base"], T)
+    log(f"  oracle linear (all {nt} tiles) done {time.time() - t0:.1f}s")
+    check_y(g["y"], y, d["y_prev"], d["name"])
+    check_y(g["y_dbg"], y, d["y_prev"], d["name"] + " (per-group kernel)")
+    _, accs = fmdq.linear(codes, tags, perm, off, d["w"], d["w_scale"], d["y_prev"], d["base"], T,
+                          tiles=range(s_lo, nt), return_acc=True)
     for tau in (nt - 2, nt - 1):
         np.testing.assert_array_equal(g["acc"][tau - (nt - 2)].astype(np.int64), accs[tau],
                                       err_msg=f"group accumulators of tile {tau}")
-    rows_s = np.concatenate([np.arange(tau * T, min(rows, tau * T + T)) for tau in sample])
-    check_y(g["y"][rows_s], y[rows_s], d["y_prev"][rows_s], d["name"])
+    check_s(g["s"], accs, range(s_lo, nt), s_lo, d["name"])
     log(f"  done {time.time() - t0:.1f}s")
+
+
+CHAIN = [(1, "fc1"), (1, "fc2"), (4, "fc1"), (4, "fc2")]
+
+
+@pytest.mark.parametrize("cfg,layer", CHAIN, ids=lambda v: str(v))
+def test_full_size_chain_in_place(dm, cfg, layer):
+    """Timestep pairs 1-3 of the workload's random walk at full rows through
+    FmdqLayer.step, Y updated in place (each step's Y_t is the next step's
+    Y_{t-1}), each implementation chaining its own output (DSTAR Eq. 1 over
+    consecutive steps): Y_t of every step bit for bit."""
+    import torch
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    d = wl.make_inputs(cfg, layer, 1)
+    xs = wl.make_walk(cfg, layer, 3)
+    rows, T = d["rows"], d["token_tile"]
+    log(f"case chain config {cfg} {layer}: rows={rows} K={d['K']} N={d['N']} pairs 1-3 "
+        f"(inputs {time.time() - t0:.1f}s)")
+    lay = dm.FmdqLayer(torch.from_numpy(d["w"]).to(dev), torch.from_numpy(d["w_scale"]).to(dev), rows, T,
+                       float(d["base"]), d["k0"], d["tokens_per_seq"])
+    y = torch.from_numpy(d["y_prev"]).to(dev)
+    y_orc = d["y_prev"]
+    for pair in (1, 2, 3):
+        lay.step(torch.from_numpy(xs[pair]).to(dev), torch.from_numpy(xs[pair - 1]).to(dev), y)
+        torch.cuda.synchronize()
+        # the oracle's layer: quantize, bucket, then linear on chunks of tiles
+        codes, tags, hist = fmdq.quantize(xs[pair], xs[pair - 1], T, d["base"], d["k0"])
+        perm, off = fmdq.bucket(tags)
+        y_new = par_linear(codes, tags, perm, off, d["w"], d["w_scale"], y_orc, d["base"], T)
+        check_y(y.cpu().numpy(), y_new, y_orc, f"{d['name']} pair {pair}")
+        y_orc = y_new
+        log(f"  pair {pair} done {time.time() - t0:.1f}s, bits {hist.tolist()}")
 
 
 # ---------------------------------------------------------------- dynamic base
@@ -382,6 +548,7 @@ def dyn_compare(dm, d, what):
     for tau in range(nt):
         np.testing.assert_array_equal(g["acc"][tau].astype(np.int64), accs[tau],
                                       err_msg=f"{what}: group accumulators of tile {tau}")
+    check_s(g["s"], accs, range(nt), 0, what)
     check_y(g["y_dbg"], y, d["y_prev"], what + " (per-group kernel)")
     check_y(g["y"], y, d["y_prev"], what)
 

@@ -16,6 +16,7 @@ import pytest
 
 from gen import workloads as wl
 from oracle import fmdq
+from tests import digits
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "dstar_examples.json")
 with open(GOLDEN) as f:
@@ -435,7 +436,7 @@ def test_code_digits_reconstruct_every_shift_aligned_code():
     the base (|q·2^e| ≤ 2^PoT ≤ 2^21), with every digit in 8 bits, and no third
     digit while |a| ≤ 2^13 (brute force over the whole range)."""
     a = np.arange(-(1 << 21), (1 << 21) + 1, dtype=np.int64)
-    d0, d1, d2 = fmdq.code_digits(a)
+    d0, d1, d2 = digits.code_digits(a)
     np.testing.assert_array_equal(d0 + 128 * d1 + 32768 * d2, a)
     assert d0.min() == -64 and d0.max() == 63
     assert d1.min() >= -128 and d1.max() <= 127
@@ -444,7 +445,7 @@ def test_code_digits_reconstruct_every_shift_aligned_code():
     assert not d2[small].any() and np.abs(d1[small]).max() <= 64
     # a few values by hand: 64 = -64 + 2^7; 2^21 = 64·2^15; -65 = 63 - 2^7
     for v, want in ((64, (-64, 1, 0)), (1 << 21, (0, 0, 64)), (-65, (63, -1, 0)), (-1, (-1, 0, 0))):
-        got = tuple(int(x[0]) for x in fmdq.code_digits(np.array([v])))
+        got = tuple(int(x[0]) for x in digits.code_digits(np.array([v])))
         assert got == want, (v, got)
 
 
@@ -458,8 +459,8 @@ def test_aligned_codes_and_digit_planes_split_S_exactly(seed, rows, K, N, T, c_r
     sub-channel does not need them."""
     d = wl.make_custom(rows, K, N, T, seed=seed, heavy=0.3, c_range=c_range)
     codes, tags, _ = fmdq.quantize(d["x_t"], d["x_prev"], T, d["base"], d["k0"])
-    a = fmdq.aligned_codes(codes, tags)
-    h = fmdq.heavy_digits(codes, tags)
+    a = digits.aligned_codes(codes, tags)
+    h = digits.heavy_digits(codes, tags)
     nt = codes.shape[0]
     assert a.shape == (nt * T, K) and a.dtype == np.int8
     assert h.shape == (2, nt, K, T) and h.dtype == np.int8
