@@ -49,9 +49,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA
 STAGES = ("quantize", "bucket", "linear")
 KERNEL_SRC = {"quantize": ["fmdq_quantize.hip"], "bucket": ["fmdq_bucket.hip"],
-              "linear": ["fmdq_linear.hip", "fmdq_linear_mfma.hip"]}
+              "linear": ["fmdq_linear.hip", "fmdq_linear_mfma.hip", "fmdq_linear_pp.hip"]}
 # device kernel name of each stage (as rocprofv3 reports it)
-KERNEL_NAME = {"quantize": "quantize_kernel", "bucket": "bucket_", "linear": "linear_mfma_kernel"}
+KERNEL_NAME = {"quantize": "quantize_kernel", "bucket": "bucket_", "linear": "linear_"}
 CAL_BYTES = 256 << 20     # the calibration copy
 HEADLINE = "flux-large"        # the largest workload that fits one GPU
 
@@ -642,6 +642,13 @@ def sar_attention(dm, torch, stream, reps: int = 10) -> dict:
             "dense_equiv_tops_cached": 2 * prod_ops / (cached * 1e-6) / 1e12, "kernels": kern}
 
 
+def uses_ping_pong(rows: int, T: int, K: int, N: int, cus: int = 256) -> bool:
+    """Whether the library's stage-3 dispatch picks the ping-pong kernel
+    (the rule of csrc/fmdq_linear.hip)."""
+    nt = (rows + T - 1) // T
+    return T == 32 and K % 64 == 0 and K >= 4096 and 2 * ((nt + 7) // 8) * ((N + 255) // 256) >= cus
+
+
 def layer_grids(rows: int, T: int, K: int, N: int) -> dict:
     """Launch grid (threads) of each stage, as rocprofv3 reports it."""
     nt = (rows + T - 1) // T
@@ -650,8 +657,12 @@ def layer_grids(rows: int, T: int, K: int, N: int) -> dict:
     kgroups = 256 // (T // 16)
     cpt = 4 if K % 4 == 0 else 2 if K % 2 == 0 else 1
     q_work = (nt * (K // cpt) + kgroups - 1) // kgroups
+    if uses_ping_pong(rows, T, K, N):
+        lin = 512 * ((nt + 256 // T - 1) // (256 // T)) * ((N + 255) // 256)
+    else:
+        lin = 256 * ((nt + 128 // T - 1) // (128 // T)) * ((N + 255) // 256)
     return {"quantize": 256 * min(q_work, 512), "bucket": (1024 if K <= 16384 else 256) * min(nt, 2048),
-            "linear": 256 * ((nt + 128 // T - 1) // (128 // T)) * ((N + 255) // 256)}
+            "linear": lin}
 
 
 class Workload:

@@ -119,5 +119,7 @@ int layer_impl(const dstar_fmdq_params* p, int32_t N, const float* x_t, const fl
                void* stream);
 bool linear_mfma_supported(const LinearArgs& a);
 int launch_linear_mfma(const LinearArgs& a, hipStream_t s);
+bool linear_pp_supported(const LinearArgs& a);
+int launch_linear_pp(const LinearArgs& a, hipStream_t s);
 
 }  // namespace dstar

@@ -1,13 +1,42 @@
-// Stage 3 dispatch: the MFMA kernel for token tiles of 32 or 64 rows, K a
-// multiple of 64, with the aligned codes, digit planes and W^T given; the
-// general kernel for other shapes and whenever the per-group accumulators are
-// dumped (only the general kernel has them).  The S dump is written by
-// whichever kernel runs.
+// Stage 3 dispatch.  Two MFMA kernels compute the same exact integer sum:
+//   - the ping-pong kernel (256 × 256 output blocks, one workgroup of eight
+//     waves per CU, the two waves of each SIMD alternating matrix and memory
+//     phases): the faster dense loop, but its Y_{t-1}/Y_t stream cannot
+//     overlap another workgroup's matrix work on the same CU;
+//   - the two-workgroups-per-CU kernel (128 × 256 blocks of four waves),
+//     whose workgroups hide each other's Y stream.
+// Measured on MI355X over the five workloads: the ping-pong kernel is faster
+// where the reduction is long (K ≥ 4096, so the matrix work dominates the Y
+// stream) and its blocks fill at least half of the CUs; the other kernel
+// everywhere else.  Both need T of 32 (the ping-pong one) or 32/64, K a
+// multiple of 64, the aligned codes, digit planes and W^T.  The general
+// kernel runs for other shapes and whenever the per-group accumulators are
+// dumped (only it keeps one accumulator per FPoT group).  The S dump is
+// written by whichever kernel runs.
 #include "fmdq_internal.h"
 
 namespace dstar {
 
+namespace {
+// Compute units of the current device (looked up once per device).
+int cu_count() {
+  static int counts[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (counts[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    counts[dev] = n;
+  }
+  return counts[dev];
+}
+}  // namespace
+
 int launch_linear(const LinearArgs& a, hipStream_t s) {
+  if (a.acc_dbg == nullptr && linear_pp_supported(a) && a.T == 32 && a.K >= 4096) {
+    const int64_t blocks = ((n_tiles(a.rows, a.T) + 7) / 8) * ((a.N + 255) / 256);
+    if (2 * blocks >= cu_count()) return launch_linear_pp(a, s);
+  }
   if (a.acc_dbg == nullptr && linear_mfma_supported(a)) return launch_linear_mfma(a, s);
   return launch_linear_general(a, s);
 }

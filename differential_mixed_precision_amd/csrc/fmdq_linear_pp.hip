@@ -1,0 +1,850 @@
+// Stage 3 of the FMDQ differential linear, MFMA kernel for gfx950 (DSTAR, arXiv
+// 2607.15846: §3.1 steps 3 and 5 with Fig. 6; §4.2 MPU with its inverse
+// quantization and accumulation units; §4.3 reverse differential fused into
+// the GEMM).
+//
+// What is computed.  For an output (row t of token tile τ, column n)
+//     S = Σ_k q[t][k] · 2^e_k · W[k][n]              (e_k = 15 − tag_k)
+//     Y_t = fl32(f64(Y_{t−1}) + (f64(S) · f64(base)) · f64(w_scale[n]))
+// which is the sum of the FPoT-group partial sums aligned by left shifts
+// (§3.1 step 5: Σ_g acc_g · 2^(15−g)), dequantized and added to the cached
+// output.  S is an exact integer; this kernel computes it exactly, so Y_t is
+// the same float as the per-group formulation gives.
+//
+// How.  A sub-channel's code q (|q| ≤ 2^p, p = b − 2) at step 2^e has the
+// value a = q·2^e in units of the base, and |a| ≤ 2^PoT.  When PoT ≤ 6 that
+// shifted code still fits in int8: these sub-channels are "aligned" by the
+// left shift of §3.1 step 5 before the multiply instead of after it, and all
+// of them are summed by one natural-order int8 MFMA GEMM whose operand chunks
+// are staged once in LDS and shared by every token tile of the workgroup.  A
+// sub-channel with PoT ≥ 7 is split by stage 1 into signed digits
+// a = d0 + 2^7·d1 + 2^15·d2: d0 sits in the dense operand, and d1 (d2 where
+// PoT ≥ 14) are multiplied after the dense loop over the tile's list of such
+// channels (prefixes of its FPoT groups in stage 2's order) into a temporary
+// accumulator that is shifted into the sum: tmp = Σ d2·W, tmp ≪= 8,
+// tmp += Σ d1·W, acc += tmp ≪ 7.
+//
+// Exactness.  int32 arithmetic wraps modulo 2^32 (shifts and adds included),
+// so the final accumulator equals S whenever |S| < 2^31; |W| ≤ 128 (any
+// int8, −128 included) gives |S| ≤ 128 · Σ_k 2^PoT_k, so a token tile is
+// handled here only if 128 · Σ_k 2^PoT_k < 2^31 (computed from stage 2's bin
+// counts).  Any other tile ("ineligible") is finished by an exact scalar path
+// in the same workgroup that walks the tile's FPoT groups in perm order with
+// int32 group sums shifted into an int64 sum.
+//
+// Layout.  Workgroup = 512 threads = 8 waves (two per SIMD: waves w and w+4
+// share one), output block 256 rows × 256 columns, one workgroup per CU.  The
+// block is two halves of 128 rows; wave w works in half h = w / 4 and owns its
+// 128 rows × columns 64·(w mod 4) .. +63 (4 × 2 MFMA 32x32x32 int8 tiles, 128
+// accumulator registers per lane).
+//
+// Dense loop, "ping-pong".  64-channel chunks of the aligned codes (256 rows)
+// and of W^T (256 columns), both channel innermost, flow through a 4-stage
+// LDS ring filled by direct global-to-LDS buffer loads; the 16-byte columns of
+// every 64-byte row are XOR-swizzled by (row / 4) mod 4 so that each fragment
+// is one conflict-free ds_read_b128.  The two halves run one slot apart: in
+// each slot one half multiplies a whole chunk from registers (16 MFMAs per
+// wave, at raised wave priority) while the other reads the next chunk's
+// fragments and issues the global loads of a chunk three ahead; every slot
+// ends with a workgroup barrier, so each SIMD always has one wave issuing
+// matrix instructions.  (Measured on this GPU: the same tile with both waves
+// of a SIMD in step spends its barriers with the matrix cores idle.)
+//
+// Gathered part (digits of the channels with PoT ≥ 7): one "unit" is 64
+// channels of one 32-row block's digit list; their digit codes (32 bytes per
+// channel from the [tile][K][T] digit planes) and W rows (256 bytes per
+// channel) are gathered by direct global-to-LDS loads into a 4-stage ring per
+// half, three units ahead; the channel ids of up to 32 units per half are staged
+// in LDS.  Both tiles have the channel outermost, so each lane assembles its
+// fragment with two ds_read_b64_tr_b8 transpose reads (W rows XOR-swizzled in
+// 16-byte pieces by channel mod 8).  The two halves step through their own
+// unit lists in one loop of max(U_0, U_1) steps (a half past its end loads
+// nothing), so both execute the same barriers.
+#include "fmdq_internal.h"
+
+namespace dstar {
+namespace {
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 512;
+constexpr int BM = 256;            // rows per workgroup
+constexpr int HM = 128;            // rows per half
+constexpr int WN = 64;             // output columns per wave
+constexpr int BN = 4 * WN;         // output columns per workgroup (256)
+constexpr int RB = HM / 32;        // 32-row MFMA blocks per wave (4)
+constexpr int CB = WN / 32;        // 32-column MFMA blocks per wave (2)
+static_assert(CB == 2, "the gathered step is written for two column blocks");
+constexpr int BK = 64;             // channels per dense chunk (2 MFMA k-steps)
+constexpr int KS = 32;             // channels per MFMA k-step
+constexpr int kTags = DSTAR_FMDQ_NUM_TAGS;
+constexpr int kBins = DSTAR_FMDQ_NUM_BINS;
+constexpr int kAlignedPotMax = 6;  // q·2^e fits int8 when PoT ≤ 6
+constexpr int kTwoDigitPotMax = 13;  // q·2^e needs no third digit when PoT ≤ 13
+constexpr uint64_t kBoundLimit = 2147483647ull / 128ull;  // Σ 2^PoT limit (|W| ≤ 128)
+constexpr int kBand = 8;           // row blocks per band of the block order
+
+template <int T>
+struct Cfg {
+  static constexpr int kTiles = BM / T;    // token tiles per workgroup
+  static constexpr int kTilesH = HM / T;   // token tiles per half
+};
+constexpr int kMaxTiles = BM / 32;
+
+// LDS carve-up (bytes).  The data region holds either the dense ring
+// (kStages stages of (A 256 rows + B 256 columns) × 64 bytes) or, after the
+// dense loop, the two halves' gathered rings (kUnits stages each of A 64
+// channels × 32 rows + B 64 channels × 256 columns).
+constexpr int kStages = 4;
+constexpr int kStageDense = (BM + BN) * BK;                // 32768
+constexpr int KU = 64;                                     // channels per gathered unit
+constexpr int kUnitA = KU * 32;                            // 2048
+constexpr int kUnitB = KU * BN;                            // 16384
+constexpr int kUnitBytes = kUnitA + kUnitB;                // 18432
+constexpr int kUnits = 4;                                  // gathered ring stages per half
+constexpr int kAhead = kUnits - 1;                         // units in flight ahead
+constexpr int kBatch = 32;                                 // units whose ids are staged
+constexpr int kDataBytes = 2 * kUnits * kUnitBytes;        // 147456 (the dense ring: 131072)
+static_assert(kStages * kStageDense <= kDataBytes, "the rings share one region");
+constexpr int kOffEnt = kDataBytes;                        // uint16 [2][kBatch][KU] channel ids
+constexpr int kOffBp = kOffEnt + 2 * kBatch * KU * 2;      // uint64 [8][16] bound parts
+constexpr int kOffOff = kOffBp + kMaxTiles * kTags * 8;    // int32 [8][65] bin offsets
+constexpr int kOffRs = kOffOff + kMaxTiles * (kBins + 1) * 4;  // int32 [8][16] group starts in perm
+constexpr int kOffRc = kOffRs + kMaxTiles * kTags * 4;     // int32 [2][8][16] digit-list lengths
+constexpr int kOffPre = kOffRc + 2 * kMaxTiles * kTags * 4;  // int32 [2][8][17] their prefix sums
+constexpr int kOffUs = kOffPre + 2 * kMaxTiles * 17 * 4;   // int32 [2][12] unit starts per half
+constexpr int kOffUi = kOffUs + 2 * 12 * 4;                // uint32 [2][kBatch] unit tile/rows/plane
+constexpr int kOffElig = kOffUi + 2 * kBatch * 4;          // int32 [8]
+constexpr int kLdsBytes = kOffElig + kMaxTiles * 4;
+static_assert(kLdsBytes <= 160 * 1024, "one workgroup per CU");
+
+// Operand loads go through buffer resources: a load whose offset lies outside
+// the resource's byte range returns zeros, so every load is unconditional
+// (an invalid piece is given the offset kOob) and the compiler can count the
+// loads still in flight instead of waiting for all of them.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void* lds_ptr;
+constexpr uint32_t kOob = 0x80000000u;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; the counters not waited on at their maximum).
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+constexpr int kWaitVm0 = wait_vm(0);
+constexpr int kWaitLgkm0 = 0xC07F;         // lgkmcnt(0)
+constexpr int kPerChunk = 4;               // direct loads per wave per dense chunk
+constexpr int kIdLoads = 8;                // id loads of the first gathered batch
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// Workgroup barrier that waits only for this wave's LDS accesses (not for
+// the direct-to-LDS loads in flight, which __syncthreads would also drain).
+__device__ __forceinline__ void bar_lds() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+__device__ __forceinline__ void bar_only() {
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// ds_read_b64_tr_b8 issued as inline assembly: the compiler cannot tell what
+// the intrinsic reads, so it would wait for every direct-to-LDS load in
+// flight before it.  The caller waits (lgkm_wait) before using the result.
+__device__ __forceinline__ v2i tr8(const uint8_t* p) {
+  v2i r;
+  const uint32_t addr = (uint32_t)(uintptr_t)(lds_ptr)p;
+  __asm__ __volatile__("ds_read_b64_tr_b8 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+// Waits for this wave's LDS reads; the fragments pass through the statement
+// so that no use of them can be scheduled before it.
+__device__ __forceinline__ void lgkm_wait(v4i& x, v4i& y, v4i& z) {
+  __asm__ __volatile__("s_waitcnt lgkmcnt(0)" : "+v"(x), "+v"(y), "+v"(z));
+}
+
+// MFMA fragment from a [channel][row] LDS tile with row stride S: the lane
+// gets row/column (lane % 32) and channels 16·(lane / 32) + 0..15.  Two
+// transpose reads; in each 16-lane group, lane r addresses channel row r/2 (+8
+// for the second read) at column offset 8·(r % 2) (+16 for the odd groups).
+template <int S>
+__device__ __forceinline__ v4i tr_frag(const uint8_t* tile, int col0, int lane) {
+  const int q = lane >> 4, r = lane & 15;
+  const uint8_t* p = tile + (16 * (q >> 1) + (r >> 1)) * S + col0 + 16 * (q & 1) + 8 * (r & 1);
+  const v2i lo = tr8(p);
+  const v2i hi = tr8(p + 8 * S);
+  return v4i{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// The same from a gathered W tile [32 channels][256 columns] whose 16-byte
+// pieces are stored XOR-swizzled: column piece P of channel c sits at piece
+// P ^ (c mod 8), so the 8 channels one 16-lane group reads hit 8 different
+// pieces (no bank conflicts).  Channels c and c + 8 share the swizzle.
+__device__ __forceinline__ v4i tr_frag_wsw(const uint8_t* tile, int col0, int lane) {
+  const int q = lane >> 4, r = lane & 15;
+  const int c = 16 * (q >> 1) + (r >> 1);
+  const int piece = ((col0 >> 4) + (q & 1)) ^ (c & 7);
+  const uint8_t* p = tile + c * BN + 16 * piece + 8 * (r & 1);
+  const v2i lo = tr8(p);
+  const v2i hi = tr8(p + 8 * BN);
+  return v4i{lo[0], lo[1], hi[0], hi[1]};
+}
+
+__device__ __forceinline__ void shift_acc(v16i& acc, int s) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = (int)((uint32_t)acc[r] << s);
+}
+
+// Gelu: the epilogue also stores GELU(Y_t) (a separate instantiation, so the
+// plain kernel carries none of its code).
+template <int T, bool VecW, bool Gelu>
+__global__ __launch_bounds__(kThreads, 1) void linear_pp_kernel(LinearArgs a, int32_t row_blocks,
+                                                                  int32_t col_blocks) {
+  constexpr int kTiles = Cfg<T>::kTiles;
+  constexpr int kTilesH = Cfg<T>::kTilesH;
+  // Direct-to-LDS loads per wave per gathered unit: two dword loads of digit
+  // codes, and the W rows as four 16-byte or sixteen 4-byte loads.
+  constexpr int kOpsUnit = VecW ? 6 : 18;
+  constexpr int kWaitVmUnits = wait_vm(kOpsUnit * (kAhead - 1));   // unit u landed
+  static_assert(kOpsUnit * (kAhead - 1) <= 63, "vmcnt range");
+  extern __shared__ __align__(16) uint8_t smem[];
+  unsigned long long* bpart = reinterpret_cast<unsigned long long*>(smem + kOffBp);
+  int32_t* off_s = reinterpret_cast<int32_t*>(smem + kOffOff);          // [kTiles][65]
+  int32_t* rstart = reinterpret_cast<int32_t*>(smem + kOffRs);          // [kTiles][16]
+  int32_t* rc = reinterpret_cast<int32_t*>(smem + kOffRc);              // [2][kMaxTiles][16]
+  int32_t* pre = reinterpret_cast<int32_t*>(smem + kOffPre);            // [2][kMaxTiles][17]
+  int32_t* eligible = reinterpret_cast<int32_t*>(smem + kOffElig);      // [kTiles]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = wave >> 2;          // ping-pong group and 128-row half
+  const int w4 = wave & 3;             // column group within the half
+  const int htid = tid & 255;          // thread index within the half
+  const int li = lane & 31, h = lane >> 5;
+  const int64_t K = a.K, N = a.N;
+  const int64_t nt = n_tiles(a.rows, T);
+  uint16_t* ent = reinterpret_cast<uint16_t*>(smem + kOffEnt) + half * kBatch * KU;   // [kBatch][KU]
+  int32_t* ustart = reinterpret_cast<int32_t*>(smem + kOffUs) + half * 12;          // [9]
+  uint32_t* uinfo = reinterpret_cast<uint32_t*>(smem + kOffUi) + half * kBatch;     // [kBatch]
+
+  // Block order.  Workgroups are dealt to the 8 XCDs round-robin (XCD =
+  // blockIdx % 8), each with its own L2.  XCD x takes a contiguous range of a
+  // banded order of the (row block, column block) grid: bands of kBand row
+  // blocks, walked column block by column block, so the workgroups an XCD
+  // runs at the same time share their code rows and W columns in its L2.
+  int64_t mb, nb;
+  {
+    const int64_t G = (int64_t)row_blocks * col_blocks;
+    const int64_t x = blockIdx.x % 8, j = blockIdx.x / 8;
+    const int64_t L = x * (G / 8) + min<int64_t>(x, G % 8) + j;
+    const int64_t band = L / ((int64_t)kBand * col_blocks);
+    const int64_t Lb = L % ((int64_t)kBand * col_blocks);
+    const int64_t hgt = min<int64_t>(kBand, row_blocks - band * kBand);
+    mb = band * kBand + Lb % hgt;
+    nb = Lb / hgt;
+  }
+  const int64_t n0 = nb * BN;
+  const int64_t nw = n0 + WN * w4;        // this wave's first column
+  const int64_t tile0 = mb * kTiles;
+  const int tiles_here = (int)min<int64_t>(kTiles, nt - tile0);
+  // This workgroup's tiles of aligned codes and perm; all of W, W^T.
+  const rsrc_t r_perm = make_rsrc(a.perm + tile0 * K, (uint32_t)(tiles_here * K * 2));
+  const rsrc_t r_ac = make_rsrc(a.acodes + tile0 * T * K, (uint32_t)(tiles_here * T * K));
+  const rsrc_t r_w = make_rsrc(a.w, (uint32_t)(K * N));
+  const rsrc_t r_wt = make_rsrc(a.w_t, (uint32_t)(N * K));
+
+  // ---- Dense ring: every channel, natural order, 64 channels per chunk,
+  // filled by direct global-to-LDS loads (no registers): A = the 256 rows of
+  // aligned codes, B = the 256 columns of W^T.  Both tiles are [row][64
+  // channels] with the 16-byte columns XOR-swizzled by row, (column ^ (row /
+  // 4) % 4).  A direct load writes lane l's 16 bytes at base + 16·l: one wave
+  // instruction fills 16 rows.  Each wave issues 2 A and 2 B instructions per
+  // chunk.
+  auto stageA = [&](int st) { return smem + st * kStageDense; };
+  auto stageB = [&](int st) { return smem + st * kStageDense + BM * BK; };
+  const int r16 = lane >> 2;                       // row of this lane within a 16-row group
+  const int c16 = (lane & 3) ^ ((r16 >> 2) & 3);   // global 16-byte column it loads
+  const int64_t nchunks = K / BK;
+  const uint32_t a_off = (uint32_t)((16 * (2 * wave) + r16) * K + 16 * c16);
+  const uint32_t b_off = (uint32_t)((n0 + 16 * (2 * wave) + r16) * K + 16 * c16);
+  const bool b_ok0 = n0 + 16 * (2 * wave) + r16 < N, b_ok1 = n0 + 16 * (2 * wave + 1) + r16 < N;
+  const uint32_t row16 = (uint32_t)(16 * K);
+  auto issue = [&](int64_t c, int st) {
+    const uint32_t k0 = (uint32_t)(c * BK);
+    const bool live = c < nchunks;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_ac, (lds_ptr)(stageA(st) + 1024 * (2 * wave + j)), 16,
+                                               live ? a_off + j * row16 + k0 : kOob, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_wt, (lds_ptr)(stageB(st) + 1024 * (2 * wave + j)), 16,
+                                               live && (j ? b_ok1 : b_ok0) ? b_off + j * row16 + k0 : kOob,
+                                               0, 0, 0);
+  };
+
+  // ---- Meta, overlapped with the first dense chunks: per tile and FPoT
+  // group the prefixes of the group (in perm) whose channels have PoT ≥ 7
+  // (second digit) and PoT ≥ 14 (third digit), the exactness bound
+  // Σ_k 2^PoT_k, and per half the schedule of gathered units: per 32-row
+  // block the third-digit list, then the second-digit list (each the
+  // concatenation of the tile's group prefixes), 64 channels per unit.
+  // (Unconditional loads: the compiler then waits for exactly these, not for
+  // the dense loads issued after them.)
+  const rsrc_t r_off = make_rsrc(a.group_off + tile0 * (kBins + 1), (uint32_t)(tiles_here * (kBins + 1) * 4));
+  uint32_t go[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int idx = tid + kThreads * m;
+    go[m] = __builtin_amdgcn_raw_buffer_load_b32(r_off, idx < kTiles * (kBins + 1) ? (uint32_t)(4 * idx) : kOob, 0, 0);
+  }
+  __asm__ __volatile__("" ::: "memory");   // keep these loads ahead of the dense ones
+#pragma unroll
+  for (int c = 0; c < kStages; ++c) issue(c, c);   // a chunk past K loads zeros
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int idx = tid + kThreads * m;
+    if (idx < kTiles * (kBins + 1)) off_s[idx] = (int32_t)go[m];
+  }
+  bar_lds();
+  if (tid < kTiles * kTags) {
+    const int i = tid / kTags, g = tid % kTags;
+    const int e = DSTAR_FMDQ_TAG_OFFSET - g;
+    const int32_t* o = off_s + i * (kBins + 1);
+    // PoT = e + 2·pc.  Bins of group g run from precision code 3 (bin 4g)
+    // down to 0 (bin 4g + 3), so the channels with pc ≥ pcmin are the first
+    // o[4g + 4 − pcmin] − o[4g] of the group.
+    const int pc7 = max(0, (kAlignedPotMax + 2 - e) / 2);     // PoT ≥ 7
+    const int pc14 = max(0, (kTwoDigitPotMax + 2 - e) / 2);   // PoT ≥ 14
+    rstart[tid] = o[4 * g];
+    rc[tid] = pc7 <= 3 ? o[4 * g + 4 - pc7] - o[4 * g] : 0;
+    rc[kMaxTiles * kTags + tid] = pc14 <= 3 ? o[4 * g + 4 - pc14] - o[4 * g] : 0;
+    unsigned long long b = 0;
+#pragma unroll
+    for (int pc = 0; pc < 4; ++pc)
+      b += (unsigned long long)(o[4 * g + 4 - pc] - o[4 * g + 3 - pc]) << (e + 2 * pc);
+    bpart[tid] = b;
+  }
+  bar_lds();
+  if (w4 == 0) {
+    // One wave per half; lane = 16 · (tile of the half) + group.
+    const int il = lane >> 4, g = lane & 15;
+    const int i = half * kTilesH + il;          // tile within the workgroup
+    const bool tile_ok = il < kTilesH;
+    unsigned long long b = 0;
+    if (tile_ok)
+      for (int g2 = 0; g2 < kTags; ++g2) b += bpart[i * kTags + g2];
+    const bool el = tile_ok && i < tiles_here && b <= kBoundLimit;
+    if (tile_ok && g == 0) eligible[i] = el ? 1 : 0;
+    // Inclusive prefix sums of both list lengths over the tile's groups.
+    int s0 = tile_ok ? rc[i * kTags + g] : 0, s1 = tile_ok ? rc[kMaxTiles * kTags + i * kTags + g] : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int u0 = __shfl_up(s0, o, 16), u1 = __shfl_up(s1, o, 16);
+      if (g >= o) {
+        s0 += u0;
+        s1 += u1;
+      }
+    }
+    if (tile_ok) {
+      pre[i * 17 + g + 1] = s0;
+      pre[kMaxTiles * 17 + i * 17 + g + 1] = s1;
+      if (g == 0) {
+        pre[i * 17] = 0;
+        pre[kMaxTiles * 17 + i * 17] = 0;
+      }
+    }
+    // Units of (32-row block rb of the half, slot x & 1): slot 0 = third
+    // digits, slot 1 = second digits; unit starts by an exclusive scan over
+    // x = 2·rb + slot.
+    const int x = lane & 7, til = (32 * (x >> 1)) / T;
+    const int tot0 = __shfl(s0, til * 16 + 15, 64), tot1 = __shfl(s1, til * 16 + 15, 64);
+    const int elx = __shfl(el ? 1 : 0, til * 16, 64);
+    int v = (lane < 8 && elx) ? (((x & 1) ? tot0 : tot1) + KU - 1) / KU : 0;
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      const int vu = __shfl_up(v, o, 64);
+      if (lane >= o) v += vu;
+    }
+    if (lane < 8) ustart[lane + 1] = v;
+    if (lane == 0) ustart[0] = 0;
+  }
+  bar_lds();
+  const int U = ustart[2 * RB];                  // gathered units of this half
+  const int Umax = max(ustart[2 * RB], reinterpret_cast<int32_t*>(smem + kOffUs)[(1 - half) * 12 + 2 * RB]);
+
+  // Channel ids of this half's units [ubase, ubase + kBatch): thread of the
+  // half → (unit, 8 ids).  fetch() issues the loads into registers, commit()
+  // writes them to LDS.
+  uint32_t fid[8], fok, finfo;
+  auto fetch = [&](int ubase) __attribute__((always_inline)) {
+    const int uu = ubase + (htid >> 3), q8 = htid & 7;
+    int x = 0;
+#pragma unroll
+    for (int st = 4; st >= 1; st >>= 1)   // largest x with ustart[x] <= uu
+      if (x + st < 2 * RB && ustart[x + st] <= uu) x += st;
+    const bool valid = uu < U;
+    const int rb = x >> 1, lvl = (x & 1) ? 0 : 1, i = half * kTilesH + (32 * rb) / T;
+    const int32_t* pr = pre + lvl * kMaxTiles * 17 + i * 17;
+    const int total = valid ? pr[16] : 0;
+    int pos = KU * (uu - ustart[x]) + 8 * q8;
+    int g = 0;
+#pragma unroll
+    for (int st = 8; st >= 1; st >>= 1)   // group of pos: largest g with pr[g] <= pos
+      if (g + st < kTags && pr[g + st] <= pos) g += st;
+    // (The loaded ids are only touched in commit(), so the loads stay in
+    // flight until then.)
+    fok = 0;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj, ++pos) {
+      while (g + 1 < kTags && pr[g + 1] <= pos) ++g;
+      const bool ok = pos < total;
+      const uint32_t off = ok ? (uint32_t)(((int64_t)i * K + rstart[i * kTags + g] + (pos - pr[g])) * 2) : kOob;
+      fid[jj] = __builtin_amdgcn_raw_buffer_load_b16(r_perm, off, 0, 0);
+      fok |= (ok ? 1u : 0u) << jj;
+    }
+    finfo = (uint32_t)i | ((uint32_t)(rb % (T / 32)) << 3) | ((uint32_t)lvl << 4);
+  };
+  auto commit = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) fid[jj] = ((fok >> jj) & 1u) ? (fid[jj] & 0xFFFFu) : 0xFFFFu;
+    uint4 p;
+    p.x = fid[0] | (fid[1] << 16);
+    p.y = fid[2] | (fid[3] << 16);
+    p.z = fid[4] | (fid[5] << 16);
+    p.w = fid[6] | (fid[7] << 16);
+    *reinterpret_cast<uint4*>(ent + (htid >> 3) * KU + 8 * (htid & 7)) = p;
+    if ((htid & 7) == 0) uinfo[htid >> 3] = finfo;
+  };
+
+  v16i acc[RB][CB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0;
+
+  // The ids of the first gathered units are loaded now and held in registers
+  // through the dense loop (eight loads, issued even when there is no unit,
+  // so that the loop's first waits can count them).
+  fetch(0);
+  __asm__ __volatile__("" ::: "memory");
+
+  // ---- Dense loop (ping-pong).  Wave (half, w4) reads its rows 128·half +
+  // 32·rb + lane and its columns 64·w4 + 32·cb + lane of each chunk.
+  {
+    auto frag = [&](const uint8_t* tile, int row, int c) {
+      return *reinterpret_cast<const v4i*>(tile + row * BK + 16 * (c ^ ((row >> 2) & 3)));
+    };
+    v4i fa[2][RB], fb[2][CB];
+    // Chunk 0 landed in every wave's share, then one barrier: visible.  (The
+    // eight id loads issued after the chunks may still be in flight.)
+    __builtin_amdgcn_s_waitcnt(wait_vm((kStages - 1) * kPerChunk + kIdLoads));
+    bar_only();
+    if (half == 1) bar_only();   // the second half runs one slot behind
+    for (int64_t j = 0; j < nchunks; ++j) {
+      const int st = (int)(j % kStages);
+      // Memory phase: this chunk's fragments into registers; the loads of
+      // chunk j − 1 + kStages into the stage chunk j − 1 used (both halves
+      // have finished reading it: the first half two slots ago, the second
+      // one slot ago, each waiting for its reads before its barrier); then
+      // this wave's share of chunk j + 1 (chunks j + 2 .. j + 3 may stay in
+      // flight, and while j ≤ 2 also the id loads, issued after chunk 3).
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) fb[ks][cb] = frag(stageB(st), WN * w4 + 32 * cb + li, 2 * ks + h);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) fa[ks][rb] = frag(stageA(st), HM * half + 32 * rb + li, 2 * ks + h);
+      }
+      if (j >= 1) issue(j - 1 + kStages, (int)((j - 1) % kStages));
+      if (j <= kStages - 2) {
+        __builtin_amdgcn_s_waitcnt(wait_vm((kStages - 2) * kPerChunk + kIdLoads));
+      } else {
+        __builtin_amdgcn_s_waitcnt(wait_vm((kStages - 2) * kPerChunk));
+      }
+      bar_lds();
+      // Compute phase: the whole chunk from registers, at raised priority so
+      // that this SIMD's other wave (in its memory phase) issues around it.
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[ks][rb], fb[ks][cb], acc[rb][cb], 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
+      bar_only();
+    }
+    if (half == 0) bar_only();
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the chunks issued past K
+  }
+
+  // ---- Epilogue set-up.  Y is streamed once: its loads and stores are
+  // non-temporal so they do not evict W and the codes from the caches.  In
+  // interior blocks the epilogue runs over (32-row block, 32-column block)
+  // units, loading the Y_{t−1} of the two next units before storing the
+  // current one.  Offsets are 32-bit, relative to this half's first row.
+  const double base = a.base_dev != nullptr ? (double)*a.base_dev : a.base;
+  bool all_eligible = true;
+#pragma unroll
+  for (int il = 0; il < kTilesH; ++il) all_eligible = all_eligible && eligible[half * kTilesH + il];
+  const int64_t row0 = tile0 * T + HM * half;      // this half's first row
+  const bool interior = all_eligible && (row0 + HM <= a.rows) && (nw + WN <= N);
+  constexpr int kNt = 2;   // aux bit: non-temporal
+  const rsrc_t r_yp = make_rsrc(a.y_prev + row0 * N, (uint32_t)(HM * N * 4));
+  const rsrc_t r_yo = make_rsrc(a.y_out + row0 * N, (uint32_t)(HM * N * 4));
+  constexpr bool has_gelu = Gelu;
+  const rsrc_t r_go = make_rsrc(Gelu ? a.gelu_out + row0 * N : a.y_out, (uint32_t)(HM * N * 4));
+  const uint32_t lane_off = (uint32_t)(((4 * h) * N + nw + li) * 4);
+  const uint32_t row4 = (uint32_t)(N * 4);
+  auto y_off = [&](int rb, int cb, int r) {
+    return lane_off + (uint32_t)(32 * rb + 8 * (r >> 2) + (r & 3)) * row4 + 128 * cb;
+  };
+  float ypa[16], ypb[16], ypc[16];
+  auto load_y = [&](float (&dst)[16], int rb, int cb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      dst[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_yp, y_off(rb, cb, r), 0, kNt));
+  };
+
+  // ---- Channels with PoT ≥ 7, per 32-row block: their second digits
+  // (and, for PoT ≥ 14, third digits) times W, added to the dense sum at
+  // shifts 7 and 15.  Unit v of a half occupies its ring stage v % kUnits: A =
+  // [64 channels][32 rows] digit codes, B = [64 channels][256 columns] of W,
+  // swizzled.  Each wave loads 512 bytes of A (dword loads: channel 8·m +
+  // lane/8, dword lane % 8, for its two m) and a quarter of B.  Every step
+  // issues exactly one unit per half (past the end of a list its loads read
+  // nothing and write zeros into a free stage), so every wait is the same
+  // count.  Columns past N only feed outputs that are never stored.
+  if (Umax > 0) {
+    commit();
+    bar_lds();   // ids visible; every wave is done with the dense ring
+    int ubase = 0;
+    // Unit starts of this half: lane x holds ustart[x] (x ≤ 8), read with readlane.
+    const int us_lane = ustart[min(lane, 2 * RB)];
+    auto us_at = [&](int x) -> int { return __builtin_amdgcn_readlane(us_lane, x); };
+    // Both digit planes of this workgroup's tiles through one resource: the
+    // second plane starts plane_off bytes after the first (n_t·K·T < 2^31).
+    const uint32_t plane_off = (uint32_t)(nt * K * T);
+    const rsrc_t r_h = make_rsrc(a.hcodes + tile0 * K * T, plane_off + (uint32_t)(tiles_here * K * T));
+    uint8_t* ring = smem + half * kUnits * kUnitBytes;
+    // The ids one wave needs for one unit's loads (all LDS reads first, so
+    // they share one wait).
+    constexpr int kNB = VecW ? 4 : 16;
+    struct UnitIds {
+      uint32_t inf, chA[2], chB[kNB];
+    };
+    auto load_ids = [&](int v, UnitIds& d) __attribute__((always_inline)) {
+      const int vb = min(v - ubase, kBatch - 1);
+      const uint16_t* en = ent + vb * KU;
+      d.inf = uinfo[vb];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) d.chA[m] = en[8 * (2 * w4 + m) + (lane >> 3)];
+#pragma unroll
+      for (int m = 0; m < kNB; ++m)
+        d.chB[m] = VecW ? en[4 * (4 * w4 + m) + (lane >> 4)] : en[16 * w4 + m];
+    };
+    auto issue_ids = [&](int v, const UnitIds& d, bool live) __attribute__((always_inline)) {
+      const int i = (int)(d.inf & 7u);
+      const int rowoff = 32 * (int)((d.inf >> 3) & 1u);
+      const uint32_t poff = (d.inf & 16u) ? plane_off : 0u;
+      uint8_t* sA = ring + (v % kUnits) * kUnitBytes;
+      uint8_t* sB = sA + kUnitA;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int mm = 2 * w4 + m;                // channels 8·mm .. 8·mm + 7
+        const uint32_t ch = d.chA[m];
+        const uint32_t off = live && ch != 0xFFFFu
+                                 ? poff + (uint32_t)(((int64_t)i * K + ch) * T + rowoff + 4 * (lane & 7)) : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_h, (lds_ptr)(sA + 256 * mm), 4, off, 0, 0, 0);
+      }
+#pragma unroll
+      for (int m = 0; m < kNB; ++m) {
+        const uint32_t ch = d.chB[m];
+        if constexpr (VecW) {
+          const int jj = 4 * w4 + m;              // channels 4·jj .. 4·jj + 3
+          const int c = 4 * jj + (lane >> 4);
+          const int piece = (lane & 15) ^ (c & 7);
+          const uint32_t off = live && ch != 0xFFFFu ? (uint32_t)((int64_t)ch * N + n0 + 16 * piece) : kOob;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr)(sB + 1024 * jj), 16, off, 0, 0, 0);
+        } else {
+          const int c = 16 * w4 + m;              // one channel row of 256 bytes
+          const int piece = (lane >> 2) ^ (c & 7);
+          const uint32_t off = live && ch != 0xFFFFu
+                                   ? (uint32_t)((int64_t)ch * N + n0 + 16 * piece + 4 * (lane & 3)) : kOob;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr)(sB + BN * c), 4, off, 0, 0, 0);
+        }
+      }
+    };
+    auto issue_unit = [&](int v) __attribute__((always_inline)) {
+      UnitIds d;
+      load_ids(v, d);
+      issue_ids(v, d, v < min(U, ubase + kBatch));
+    };
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) issue_unit(j);
+    // The units of a half, in order, are the third-digit then the
+    // second-digit lists of its row blocks 0..3; tmp collects the current
+    // row block's (third digits first, shifted by 8 when the second begin).
+    v16i tmp[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tmp[cb][r] = 0;
+    int cur_x = -1;   // x-slot (2·rb + slot) of the last unit multiplied
+    // acc[rb] += tmp · 2^7 for the row block of x-slot cur_x (tmp = Σ d1·W +
+    // 2^8 Σ d2·W), then tmp = 0.
+    auto flush = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if ((cur_x >> 1) == rb) {
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              acc[rb][cb][r] = (int)((uint32_t)acc[rb][cb][r] + ((uint32_t)tmp[cb][r] << 7));
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tmp[cb][r] = 0;
+    };
+    for (int u = 0; u < Umax; ++u) {
+      if (u == ubase + kBatch) {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        bar_lds();   // every wave is done with the previous ids
+        ubase = u;
+        fetch(ubase);
+        commit();
+        bar_lds();
+#pragma unroll
+        for (int j = 0; j < kAhead; ++j) issue_unit(u + j);
+      }
+      // The ids of unit u + kAhead are read before the wait (its stage is only
+      // written after the barrier).
+      UnitIds nx;
+      load_ids(u + kAhead, nx);
+      const bool live = u + kAhead < min(U, ubase + kBatch);
+      __builtin_amdgcn_s_waitcnt(kWaitVmUnits);
+      bar_only();
+      issue_ids(u + kAhead, nx, live);
+      if (u < U) {
+        // x-slot of unit u: largest x with ustart[x] <= u (wave-uniform)
+        int x = 0;
+#pragma unroll
+        for (int xx = 1; xx < 2 * RB; ++xx) x = us_at(xx) <= u ? xx : x;
+        if (x != cur_x) {
+          if ((x >> 1) != (cur_x >> 1)) {
+            if (cur_x >= 0) flush();
+          } else {   // third digits of this row block done: tmp = Σ d2·W · 2^8
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) shift_acc(tmp[cb], 8);
+          }
+          cur_x = x;
+        }
+        const uint8_t* sA = ring + (u % kUnits) * kUnitBytes;
+        const uint8_t* sB = sA + kUnitA;
+#pragma unroll
+        for (int ks = 0; ks < KU / KS; ++ks) {
+          v4i af = tr_frag<32>(sA + ks * KS * 32, 0, lane);
+          v4i b0 = tr_frag_wsw(sB + ks * KS * BN, WN * w4, lane);
+          v4i b1 = tr_frag_wsw(sB + ks * KS * BN, WN * w4 + 32, lane);
+          lgkm_wait(af, b0, b1);
+          tmp[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, b0, tmp[0], 0, 0, 0);
+          tmp[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, b1, tmp[1], 0, 0, 0);
+        }
+      }
+    }
+    if (cur_x >= 0) flush();
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the loads issued past the last unit
+  }
+
+  // ---- Optional dump of the exact integer S of the eligible tiles in
+  // [dbg_lo, dbg_hi) (for checking; the ineligible ones are dumped by the
+  // scalar path below).  Lane layout of a 32x32 MFMA result: row
+  // 8·(r / 4) + 4·h + r % 4, column li.
+  if (a.s_dbg != nullptr) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int i = half * kTilesH + (32 * rb) / T;
+      const int64_t tau = tile0 + i;
+      if (i >= tiles_here || !eligible[i] || tau < a.dbg_lo || tau >= a.dbg_hi) continue;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int64_t n = nw + 32 * cb + li;
+        if (n >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t t = (32 * rb) % T + 8 * (r >> 2) + 4 * h + (r & 3);
+          a.s_dbg[((tau - a.dbg_lo) * T + t) * N + n] = (int64_t)acc[rb][cb][r];
+        }
+      }
+    }
+  }
+
+  // ---- Epilogue: dequantize, add the cached output, store (float64 combine).
+  double ws[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int64_t n = nw + 32 * cb + li;
+    ws[cb] = n < N ? (double)a.w_scale[n] : 0.0;
+  }
+  if (interior) {
+    // three buffers: the loads of the two next units are in flight while
+    // one unit is combined and stored
+    load_y(ypa, 0, 0);
+    load_y(ypb, 1 / CB, 1 % CB);
+#pragma unroll
+    for (int v = 0; v < RB * CB; ++v) {
+      const int rb = v / CB, cb = v % CB;
+      float (&cur)[16] = v % 3 == 0 ? ypa : v % 3 == 1 ? ypb : ypc;
+      float (&nxt)[16] = v % 3 == 0 ? ypc : v % 3 == 1 ? ypa : ypb;
+      if (v + 2 < RB * CB) load_y(nxt, (v + 2) / CB, (v + 2) % CB);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const double d = __dmul_rn(__dmul_rn((double)acc[rb][cb][r], base), ws[cb]);
+        const float y = (float)__dadd_rn((double)cur[r], d);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, y), r_yo, y_off(rb, cb, r), 0, kNt);
+        if constexpr (has_gelu)
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gelu_of(y)), r_go, y_off(rb, cb, r), 0, kNt);
+      }
+      // keep each unit's loads, math and stores in this order (bounds the
+      // registers the epilogue holds at once)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int64_t n = nw + 32 * cb + li;
+      if (n >= N) continue;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int i = half * kTilesH + (32 * rb) / T;
+        if (!eligible[i]) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t grow = row0 + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (grow >= a.rows) continue;
+          const int64_t idx = grow * N + n;
+          const double d = __dmul_rn(__dmul_rn((double)acc[rb][cb][r], base), ws[cb]);
+          const float y = (float)__dadd_rn((double)a.y_prev[idx], d);
+          a.y_out[idx] = y;
+          if constexpr (has_gelu) a.gelu_out[idx] = gelu_of(y);
+        }
+      }
+    }
+  }
+
+  // ---- Ineligible tiles: exact scalar path over the FPoT groups in perm
+  // order, int32 group sums shifted into int64.  Thread of the half = one
+  // column.
+  for (int il = 0; il < kTilesH; ++il) {
+    const int i = half * kTilesH + il;
+    if (i >= tiles_here || eligible[i]) continue;
+    const int64_t tau = tile0 + i;
+    const int64_t n = n0 + htid;
+    if (n >= N) continue;
+    const int32_t* off = off_s + i * (kBins + 1);
+    const uint16_t* pm = a.perm + tau * K;
+    const int8_t* cd = a.codes + tau * K * T;
+    const double wsn = (double)a.w_scale[n];
+    for (int t0 = 0; t0 < T; t0 += 32) {
+      int64_t sum[32];
+#pragma unroll
+      for (int t = 0; t < 32; ++t) sum[t] = 0;
+      for (int g = 0; g < kTags; ++g) {
+        const int lo = off[4 * g], hi = off[4 * g + 4];
+        if (lo == hi) continue;
+        int32_t gs[32];
+#pragma unroll
+        for (int t = 0; t < 32; ++t) gs[t] = 0;
+        for (int j = lo; j < hi; ++j) {
+          const int64_t k = pm[j];
+          const int32_t wv = (int32_t)a.w[k * N + n];
+          const int4* c4 = reinterpret_cast<const int4*>(cd + k * T + t0);
+#pragma unroll
+          for (int v = 0; v < 2; ++v) {
+            const int4 c = c4[v];
+            const int words[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+            for (int b = 0; b < 16; ++b) gs[16 * v + b] += (int32_t)(int8_t)(words[b >> 2] >> (8 * (b & 3))) * wv;
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 32; ++t) sum[t] += (int64_t)gs[t] << (DSTAR_FMDQ_TAG_OFFSET - g);
+      }
+      if (a.s_dbg != nullptr && tau >= a.dbg_lo && tau < a.dbg_hi) {
+#pragma unroll
+        for (int t = 0; t < 32; ++t) a.s_dbg[((tau - a.dbg_lo) * T + t0 + t) * N + n] = sum[t];
+      }
+#pragma unroll
+      for (int t = 0; t < 32; ++t) {
+        const int64_t grow = tau * T + t0 + t;
+        if (grow >= a.rows) continue;
+        const int64_t idx = grow * N + n;
+        const double d = __dmul_rn(__dmul_rn((double)sum[t], base), wsn);
+        const float y = (float)__dadd_rn((double)a.y_prev[idx], d);
+        a.y_out[idx] = y;
+        if constexpr (has_gelu) a.gelu_out[idx] = gelu_of(y);
+      }
+    }
+  }
+}
+
+template <int T, bool VecW, bool Gelu>
+int launch_tv(const LinearArgs& a, hipStream_t s) {
+  const int64_t nt = n_tiles(a.rows, T);
+  const int64_t row_blocks = (nt + Cfg<T>::kTiles - 1) / Cfg<T>::kTiles;
+  const int32_t col_blocks = (int32_t)((a.N + BN - 1) / BN);
+  const int64_t grid = row_blocks * col_blocks;
+  if (grid > 0x7FFFFFFF || row_blocks > 0x7FFFFFFF)
+    return set_error(DSTAR_EUNSUPPORTED, "fmdq_linear: grid too large");
+  // The LDS limit is a per-device property of the kernel: set it on every
+  // launch (a host-side call; cheap, thread-safe, right on any device).
+  hipError_t e = hipFuncSetAttribute((const void*)linear_pp_kernel<T, VecW, Gelu>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  if (e != hipSuccess)
+    return set_error(DSTAR_EHIP, "fmdq_linear: hipFuncSetAttribute: %s", hipGetErrorString(e));
+  hipLaunchKernelGGL((linear_pp_kernel<T, VecW, Gelu>), dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s,
+                     a, (int32_t)row_blocks, col_blocks);
+  return check_launch("fmdq_linear (ping-pong)");
+}
+
+template <int T>
+int launch_t(const LinearArgs& a, hipStream_t s) {
+  if (a.gelu_out != nullptr)
+    return (a.N % 16) == 0 ? launch_tv<T, true, true>(a, s) : launch_tv<T, false, true>(a, s);
+  return (a.N % 16) == 0 ? launch_tv<T, true, false>(a, s) : launch_tv<T, false, false>(a, s);
+}
+
+}  // namespace
+
+// Handles token tiles of 32 or 64 rows, K a multiple of 64 (whole dense
+// chunks) and W below 2^31 bytes (32-bit buffer offsets), given the aligned
+// codes and W^T.
+bool linear_pp_supported(const LinearArgs& a) {
+  return a.acodes != nullptr && a.hcodes != nullptr && a.w_t != nullptr && (a.T == 32 || a.T == 64) &&
+         (a.K % 64) == 0 && n_tiles(a.rows, a.T) * a.K * a.T < (int64_t(1) << 31) &&
+         (int64_t)a.K * a.N < (int64_t(1) << 31);
+}
+
+int launch_linear_pp(const LinearArgs& a, hipStream_t s) {
+  switch (a.T) {
+    case 32: return launch_t<32>(a, s);
+    case 64: return launch_t<64>(a, s);
+    default: return set_error(DSTAR_EUNSUPPORTED, "fmdq_linear (ping-pong): token_tile %d", a.T);
+  }
+}
+
+}  // namespace dstar

@@ -488,6 +488,75 @@ def test_full_size_workloads(dm, cfg, layer):
     log(f"  done {time.time() - t0:.1f}s")
 
 
+def par_linear_s(codes, tags, perm, off, w, w_scale, y_prev, base, T):
+    """Y of every tile and S of every tile ([n_t][T][N] int64), the oracle's
+    linear and shift_combine(group_accumulators) called per tile in parallel
+    threads."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    rows, N = y_prev.shape[0], w.shape[1]
+    nt = (rows + T - 1) // T
+    y = np.array(y_prev, dtype=np.float32, copy=True)
+    s_all = np.zeros((nt, T, N), dtype=np.int64)
+
+    def run(tau):
+        yy, accs = fmdq.linear(codes, tags, perm, off, w, w_scale, y_prev, base, T, tiles=[tau],
+                               return_acc=True)
+        return tau, yy, fmdq.shift_combine(accs[tau])
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with threadpool_limits(limits=1), ThreadPoolExecutor(workers) as ex:
+        for tau, yy, st in ex.map(run, range(nt)):
+            r0, r1 = tau * T, min(rows, tau * T + T)
+            y[r0:r1] = yy[r0:r1]
+            s_all[tau] = st
+    return y, s_all
+
+
+# Shapes large enough for the dispatch to take the ping-pong kernel (T = 32,
+# K >= 4096, its 256 x 256 blocks filling at least half of the CUs).
+PP_CASES = [
+    dict(rows=2041, K=4096, N=4096, T=32, seed=91, heavy=0.2, c_range=(0.5, 64.0)),      # ragged last tile
+    dict(rows=2048, K=4096, N=4100, T=32, seed=92, heavy=0.3, c_range=(0.02, 4000.0)),   # N % 16 != 0, d2
+    dict(rows=2048, K=4160, N=4096, T=32, seed=93, heavy=1.0, c_range=(4.0, 8.0)),       # every channel 8-bit
+    # two tiles whose first 1024 channels sit at PoT 14: Σ 2^PoT ≥ 2^24, the
+    # exact per-group path inside the kernel; every other tile eligible
+    dict(rows=2048, K=4096, N=4096, T=32, seed=94, heavy=0.05, c_range=(0.5, 64.0), wide_tiles=(5, 40)),
+]
+
+
+@pytest.mark.parametrize("case", PP_CASES, ids=lambda c: f"{c['rows']}x{c['K']}x{c['N']}-s{c['seed']}")
+def test_ping_pong_kernel_matches_oracle(dm, case):
+    """The ping-pong stage-3 kernel (taken at these shapes): every integer
+    stage, S of every tile and Y_t of every output bit for bit, and the
+    per-group accumulators of the last two tiles."""
+    t0 = time.time()
+    c = dict(case)
+    wide = c.pop("wide_tiles", ())
+    d = wl.make_custom(c.pop("rows"), c.pop("K"), c.pop("N"), c.pop("T"), seed=c.pop("seed"), **c)
+    rows, T = d["rows"], d["token_tile"]
+    nt = (rows + T - 1) // T
+    for tau in wide:
+        x = d["x_prev"][tau * T:(tau + 1) * T, :1024].astype(np.float64)
+        d["x_t"][tau * T:(tau + 1) * T, :1024] = (x - float(d["base"]) * 2.0 ** 14).astype(np.float32)
+    log(f"case {d['name']} (ping-pong kernel), tiles at the bound: {list(wide)}")
+    g = gpu_layer(dm, d, dbg=(nt - 2, nt), sdump=(0, nt))
+    codes, tags, hist = fmdq.quantize(d["x_t"], d["x_prev"], T, d["base"], d["k0"])
+    perm, off = fmdq.bucket(tags)
+    check_integer_stages(g, codes, tags, hist, perm, off, d["name"], d["w"])
+    y, s_all = par_linear_s(codes, tags, perm, off, d["w"], d["w_scale"], d["y_prev"], d["base"], T)
+    log(f"  oracle done {time.time() - t0:.1f}s")
+    np.testing.assert_array_equal(g["s"], s_all, err_msg=f"{d['name']}: S (product kernel)")
+    check_y(g["y"], y, d["y_prev"], d["name"])
+    check_y(g["y_dbg"], y, d["y_prev"], d["name"] + " (per-group kernel)")
+    _, accs = fmdq.linear(codes, tags, perm, off, d["w"], d["w_scale"], d["y_prev"], d["base"], T,
+                          tiles=[nt - 2, nt - 1], return_acc=True)
+    for tau in (nt - 2, nt - 1):
+        np.testing.assert_array_equal(g["acc"][tau - (nt - 2)].astype(np.int64), accs[tau])
+    log(f"  done {time.time() - t0:.1f}s")
+
+
 CHAIN = [(1, "fc1"), (1, "fc2"), (4, "fc1"), (4, "fc2")]
 
 
