@@ -19,13 +19,14 @@ the current V.
 from __future__ import annotations
 
 from . import _binding
-from ._binding import (FmdqError, Params, bucket, dynamic_base, gelu, layer, layer_workspace_size,  # noqa: F401
+from ._binding import (FmdqError, Params, bucket, dynamic_base, gelu, layer, layer_noalloc,  # noqa: F401
+                       layer_workspace_size,
                        linear, linear_dyn, linear_gelu, load, make_params, pack_weights, quantize,
                        quantize_dyn, slice_encode, sar_padded_dim, sar_pv, sar_quantize_k,
                        sar_quantize_q, sar_quantize_v, sar_scores)
 
 __all__ = ["FmdqError", "Params", "FmdqLayer", "FmdqMLP", "bucket", "dynamic_base", "gelu", "layer",
-           "layer_workspace_size", "linear",
+           "layer_noalloc", "layer_workspace_size", "linear",
            "linear_dyn", "linear_gelu", "load", "make_params", "pack_weights", "quantize",
            "quantize_dyn", "slice_encode", "n_tiles", "SarAttention", "sar_padded_dim", "sar_pv",
            "sar_quantize_k", "sar_quantize_q", "sar_quantize_v", "sar_scores"]

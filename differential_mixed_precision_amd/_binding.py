@@ -28,11 +28,13 @@ SAR_PAD = 32
 SAR_MAX_D = 128
 SAR_MAX_L = 65536
 SAR_EXP_FRAC = 36
+NOALLOC_MAX_BYTES = 64 << 20
 
 SYMBOLS = ("dstar_fmdq_quantize", "dstar_fmdq_bucket", "dstar_fmdq_slice_encode", "dstar_fmdq_pack_weights",
            "dstar_fmdq_linear", "dstar_fmdq_linear_gelu", "dstar_fmdq_gelu",
            "dstar_fmdq_dynamic_base", "dstar_fmdq_quantize_dyn",
            "dstar_fmdq_linear_dyn", "dstar_fmdq_layer", "dstar_fmdq_layer_workspace_size",
+           "dstar_fmdq_layer_noalloc",
            "dstar_fmdq_last_error", "dstar_fmdq_abi_version")
 SAR_SYMBOLS = ("dstar_sar_quantize_q", "dstar_sar_quantize_k", "dstar_sar_quantize_v", "dstar_sar_scores",
                "dstar_sar_pv")
@@ -97,6 +99,8 @@ def load() -> ctypes.CDLL:
     lib.dstar_fmdq_linear_dyn.restype = ctypes.c_int
     lib.dstar_fmdq_layer.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp]
     lib.dstar_fmdq_layer.restype = ctypes.c_int
+    lib.dstar_fmdq_layer_noalloc.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.dstar_fmdq_layer_noalloc.restype = ctypes.c_int
     lib.dstar_fmdq_layer_workspace_size.argtypes = [P]
     lib.dstar_fmdq_layer_workspace_size.restype = ctypes.c_int64
     S = ctypes.POINTER(SarParams)
@@ -189,6 +193,16 @@ def layer(p: Params, N: int, x_t, x_prev, w, w_t, w_scale, y_prev, y_out, worksp
     _check(load().dstar_fmdq_layer(ctypes.byref(p), int(N), _ptr(x_t), _ptr(x_prev), _ptr(w), _ptr(w_t),
                                    _ptr(w_scale), _ptr(y_prev), _ptr(y_out), _ptr(bit_hist), _ptr(workspace),
                                    int(workspace.numel() * workspace.element_size()), _stream(stream)))
+
+
+def layer_noalloc(p: Params, N: int, x_t, x_prev, w, w_t, w_scale, y_prev, y_out, bit_hist=None,
+                  stream=None) -> None:
+    """dstar_fmdq_layer_noalloc: the three stages in one call with the
+    intermediates in the library's own per-GPU scratch (at most
+    NOALLOC_MAX_BYTES of them; calls that overlap in time on one GPU race)."""
+    _check(load().dstar_fmdq_layer_noalloc(ctypes.byref(p), int(N), _ptr(x_t), _ptr(x_prev), _ptr(w), _ptr(w_t),
+                                           _ptr(w_scale), _ptr(y_prev), _ptr(y_out), _ptr(bit_hist),
+                                           _stream(stream)))
 
 
 def dynamic_base(p: Params, x_t, x_prev, base, stream=None) -> None:

@@ -54,6 +54,7 @@ extern "C" {
 #define DSTAR_FMDQ_SLICE_BINS 22     /* slice tags -6..15 of the 2-bit stream */
 #define DSTAR_FMDQ_SLICE_TAG_OFFSET 6
 #define DSTAR_FMDQ_SLICE_MAX_K 16384
+#define DSTAR_FMDQ_NOALLOC_MAX_BYTES (64 << 20) /* scratch of dstar_fmdq_layer_noalloc */
 
 /* Status codes. */
 #define DSTAR_OK 0
@@ -298,6 +299,24 @@ int dstar_fmdq_layer(const dstar_fmdq_params* p, int32_t N, const float* x_t,
 /* Bytes of workspace dstar_fmdq_layer needs for these parameters (>= 0), or a
  * negative DSTAR_E* code for invalid parameters. */
 int64_t dstar_fmdq_layer_workspace_size(const dstar_fmdq_params* p);
+
+/* dstar_fmdq_layer without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The intermediates live in the library's
+ * own device array of DSTAR_FMDQ_NOALLOC_MAX_BYTES (64 MiB), one per GPU, held
+ * until the process ends; its address on a device is looked up once, on the
+ * first call there.  Arguments, results and errors as for dstar_fmdq_layer,
+ * plus DSTAR_EINVAL (before any HIP call) when
+ * dstar_fmdq_layer_workspace_size(p) exceeds that size.  Nothing is
+ * allocated.  Every call on one GPU uses the same array: calls that overlap in
+ * time on one GPU (on different streams, or from different threads) race and
+ * must be serialized by the caller.  Nothing needs clearing between calls:
+ * the stages write every intermediate they read. */
+int dstar_fmdq_layer_noalloc(const dstar_fmdq_params* p, int32_t N,
+                             const float* x_t, const float* x_prev,
+                             const int8_t* w, const int8_t* w_t,
+                             const float* w_scale, const float* y_prev,
+                             float* y_out, uint32_t* bit_hist, void* stream);
 
 /* Message describing the last error of the calling thread ("" if none). */
 const char* dstar_fmdq_last_error(void);

@@ -196,6 +196,23 @@ def test_layer_workspace_and_its_checks(lib):
     assert lay(FAKE, need, N=66) == lib.EINVAL
 
 
+def test_noalloc_layer_rejects_sizes_above_its_scratch_on_the_host(lib):
+    """The no-allocation layer checks its size against the library's scratch
+    before any HIP call (so this runs without a GPU)."""
+    L = lib.load()
+    p = lib.make_params(8192, 4608, 32, 0.05, 2, 4096)      # ~151 MB of intermediates
+    assert lib.layer_workspace_size(p) > lib.NOALLOC_MAX_BYTES
+    rc = L.dstar_fmdq_layer_noalloc(ctypes.byref(p), 1152, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0)
+    assert rc == lib.EINVAL
+    assert "scratch" in L.dstar_fmdq_last_error().decode()
+    bad = lib.make_params(64, 64, 48, 0.05, 2)
+    assert L.dstar_fmdq_layer_noalloc(ctypes.byref(bad), 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                      0) == lib.EINVAL
+    text = _header()
+    m = re.search(r"#define\s+DSTAR_FMDQ_NOALLOC_MAX_BYTES\s+\((\d+)\s*<<\s*(\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == lib.NOALLOC_MAX_BYTES
+
+
 def test_empty_input_is_a_no_op(lib):
     p = lib.make_params(0, 64, 32, 0.05, 2, tokens_per_seq=1)
     assert _q(lib, p, x=None, xp=None, codes=None, tags=None) == lib.OK
