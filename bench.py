@@ -22,8 +22,8 @@ it).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload flux-large]
 
-Traffic summary from two counter runs (run from the repository root; a plain
-256 MiB device copy made before timing calibrates the counters):
+Traffic summary from two counter runs (run from the repository root; the
+library GELU over 256 MiB of float32, run before timing, calibrates the counters):
 
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/pmc_fetch -o run -- python3 bench.py --workload W --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain --no-slices --no-attention --no-cold --no-per-workload
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/pmc_write -o run -- python3 bench.py (same arguments)
@@ -52,7 +52,8 @@ KERNEL_SRC = {"quantize": ["fmdq_quantize.hip"], "bucket": ["fmdq_bucket.hip"],
               "linear": ["fmdq_linear.hip", "fmdq_linear_mfma.hip", "fmdq_linear_pp.hip"]}
 # device kernel name of each stage (as rocprofv3 reports it)
 KERNEL_NAME = {"quantize": "quantize_kernel", "bucket": "bucket_", "linear": "linear_"}
-CAL_BYTES = 256 << 20     # the calibration copy
+CAL_BYTES = 256 << 20     # bytes the calibration kernel reads (and writes)
+CAL_KERNEL = "gelu_kernel"  # the library's elementwise GELU: reads and writes 4 bytes per element
 HEADLINE = "flux-large"        # the largest workload that fits one GPU
 
 
@@ -156,19 +157,20 @@ def write_traffic(fetch_dir: str, write_dir: str, workload: str) -> None:
         return (sum(v) / len(v), sorted({grid for (name, grid, did) in per if kname in name and
                                          lay[which][did] == lg})) if v else (None, [])
 
-    # the calibration copy is the largest device copy of the run
-    cal_grid = max((g for (n, g, _) in write if "copyBuffer" in n), default=None)
-    cal_f = mean(fetch, lambda n, g: "copyBuffer" in n and g == cal_grid)
-    cal_w = mean(write, lambda n, g: "copyBuffer" in n and g == cal_grid)
+    # the calibration pass: the library's GELU over CAL_BYTES / 4 floats (a
+    # kernel no step launches), which reads and writes CAL_BYTES each
+    cal_f = mean(fetch, lambda n, g: CAL_KERNEL in n)
+    cal_w = mean(write, lambda n, g: CAL_KERNEL in n)
     if not cal_f or not cal_w:
-        raise SystemExit("no calibration copy in the counter runs")
+        raise SystemExit("no calibration pass in the counter runs")
     sf, sw = (CAL_BYTES / 1024) / cal_f, (CAL_BYTES / 1024) / cal_w
     args = pmc_args(workload)
     lines = [f"# HBM traffic per launch, FMDQ differential linear, {workload} MLP",
              "",
              "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, rocprofv3 --pmc, one run each) of",
              f"`python3 bench.py {args}` on one MI355X, scaled by what they read",
-             f"for a plain {CAL_BYTES >> 20} MiB device copy made in the same run (fetch x{sf:.4f}, write x{sw:.4f}).",
+             f"for a plain stream of known size made in the same run: the library's elementwise GELU over",
+             f"{CAL_BYTES >> 20} MiB of float32 (reads and writes {CAL_BYTES >> 20} MiB; fetch x{sf:.4f}, write x{sw:.4f}).",
              "Commands:",
              "",
              "```",
@@ -868,10 +870,10 @@ def main() -> int:
     print(f"[bench] generating {spec['name']} pairs 1..{args.pairs}", file=sys.stderr, flush=True)
     work = Workload(dm, torch, wl, cfg, args.pairs)
     layers, rows, T, state = work.layers, work.rows, work.T, work.state
-    # a plain copy of known size (counter calibration for rocprofv3 --pmc runs)
-    cal_src = torch.empty(CAL_BYTES, dtype=torch.uint8, device=dev)
+    # a plain stream of known size (counter calibration for rocprofv3 --pmc runs)
+    cal_src = torch.zeros(CAL_BYTES // 4, dtype=torch.float32, device=dev)
     cal_dst = torch.empty_like(cal_src)
-    cal_dst.copy_(cal_src)
+    dm.gelu(cal_src, cal_dst)
     torch.cuda.synchronize()
     del cal_src, cal_dst
     stream = work.stream
