@@ -14,9 +14,26 @@
  * steps 2 and 5, Fig. 6), dequantized and added to the cached Y_{t-1} (DSTAR
  * §4.2 "Design of MPU", §4.3 "Linear Operation").
  *
- * The entry points are the three stages, the weight preparation and the
- * dynamic-base variant; each launches HIP kernels on the caller's stream and
- * returns without synchronizing.
+ * The entry points are the three stages, the weight preparation, the
+ * one-call layer (with a workspace, or without one) and the variants (dynamic
+ * base, fused GELU, 2-bit slice stream); each launches HIP kernels on the
+ * caller's stream and returns without synchronizing.
+ *
+ * Compared with a minimal three-call interface (stage 1 writing codes and
+ * tags; stage 2 writing channel ids sorted by (tag, channel) with 17 tag
+ * offsets; stage 3 taking codes, tags, ids, offsets and W):
+ *   - stage 1 also writes the shift-aligned codes and their high digits
+ *     (acodes, hcodes), the operands of the MFMA kernels (DSTAR §3.1 step 5:
+ *     the alignment is applied to the codes before the multiply);
+ *   - stage 2 orders ties inside one tag by precision, widest first, then by
+ *     channel, and writes 65 offsets, one per (tag, precision) bin plus the
+ *     end (DSTAR §3.1 step 3 fixes only the tag order);
+ *   - stage 3 takes no tags (a channel's group and precision follow from its
+ *     position in perm against the bin offsets), takes acodes, hcodes and a
+ *     once-per-layer W^T (dstar_fmdq_pack_weights), accepts any int8 weight,
+ *     -128 included, and can dump its exact integer S (s_dbg);
+ *   - the stream is a hipStream_t passed as void*, so this header needs no
+ *     HIP header.
  *
  * Conventions for every entry point
  *   - All array arguments are DEVICE pointers (memory from hipMalloc, or
