@@ -12,7 +12,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libdstar_fmdq.so")
+# DSTAR_FMDQ_LIB names another build of the same library (the host-sanitized
+# one); by default the in-tree build next to this file is loaded.
+LIB_PATH = os.environ.get("DSTAR_FMDQ_LIB") or os.path.join(_PKG, "libdstar_fmdq.so")
 
 OK, EINVAL, ENULL, EALIGN, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5
 NUM_TAGS = 16

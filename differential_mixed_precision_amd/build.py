@@ -1,8 +1,13 @@
 """Builds libdstar_fmdq.so (HIP kernels + C ABI) for gfx950 with hipcc.
 
-Usage: python -m differential_mixed_precision_amd.build [-v]
+Usage: python -m differential_mixed_precision_amd.build [-v] [--sanitize]
 
-Objects go to <repo>/_build/, the shared library next to this file.
+Objects go to <repo>/_build/, the shared library next to this file.  With
+--sanitize the host code (the C ABI's argument checks and launch set-up) is
+built with AddressSanitizer and UndefinedBehaviorSanitizer into
+<repo>/_build/sanitize/libdstar_fmdq.so; the device code is built as usual.
+That library needs the sanitizer runtime preloaded (SANITIZER_RUNTIME) and is
+loaded through DSTAR_FMDQ_LIB.
 """
 from __future__ import annotations
 
@@ -34,13 +39,36 @@ CFLAGS = [
 ]
 
 
+# host-only sanitizers: each -fsanitize= is scoped to the host compilation
+SANITIZE_FLAGS = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-g",
+]
+SANITIZE_DIR = os.path.join(BUILD, "sanitize")
+SANITIZE_LIB = os.path.join(SANITIZE_DIR, LIB_NAME)
+
+
+def sanitizer_runtime() -> str | None:
+    """The shared ASan runtime of the ROCm clang that compiles the library."""
+    base = "/opt/rocm/llvm/lib/clang"
+    if not os.path.isdir(base):
+        return None
+    for ver in sorted(os.listdir(base), reverse=True):
+        p = os.path.join(base, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(p):
+            return p
+    return None
+
+
 def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+def _compile(src: str, verbose: bool, sanitize: bool = False) -> str:
+    out = SANITIZE_DIR if sanitize else BUILD
+    obj = os.path.join(out, os.path.basename(src)[:-4] + ".o")
+    cmd = [HIPCC, *CFLAGS, *(SANITIZE_FLAGS if sanitize else []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,24 +81,27 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compiles every source under csrc/ and links the shared library."""
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compiles every source under csrc/ and links the shared library (the
+    sanitized host build into _build/sanitize/ when `sanitize`)."""
     if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(BUILD, exist_ok=True)
+    out = SANITIZE_DIR if sanitize else BUILD
+    lib_path = SANITIZE_LIB if sanitize else LIB_PATH
+    os.makedirs(out, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, sanitize), srcs))
+    tmp = lib_path + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))
