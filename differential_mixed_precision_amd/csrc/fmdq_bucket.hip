@@ -13,11 +13,13 @@
 // takes 64 consecutive channels ("chunk"), and for each lane the lanes with
 // the same bin are found with six ballots (one per bit of the bin); the
 // lowest of them writes the group's size into a [64 bins][chunks] table, and
-// a lane's rank among its peers is the number of lower peers.  One exclusive
-// scan over the table in (bin, chunk) order then gives every (bin, chunk) its
-// first output slot — the stable order, since chunks and lanes both run in
-// channel order — and each lane places its channel at slot + rank.  No step
-// is a chain of dependent LDS updates.
+// a lane's rank among its peers is the number of lower peers.  The ballots
+// are the kernel's main cost (vector ALU, one workgroup per tile), so each
+// lane keeps its bin and rank in a register from the count to the placement.
+// One exclusive scan over the table in (bin, chunk) order then gives every
+// (bin, chunk) its first output slot — the stable order, since chunks and
+// lanes both run in channel order — and each lane places its channel at
+// slot + rank.  No step is a chain of dependent LDS updates.
 //
 // Otherwise thread j owns the contiguous channel range [j*per, (j+1)*per).  It counts its keys into column
 // j of a [64][256] uint16 LDS table; one exclusive scan over that table, read
@@ -76,6 +78,15 @@ __device__ void exclusive_scan_table(uint16_t* tab, uint32_t* wave_tot) {
 constexpr int kBallotMaxK = 16384;
 constexpr int kBallotThreads = 1024;   // 16 waves: the chunks of one tile spread over them
 
+// Row stride (uint16 entries) of the [64 bins][C chunks] count table: C
+// rounded up so that a row spans an odd number of 4-byte words, which puts
+// the entries of one chunk for different bins in different LDS banks (with C
+// a multiple of 64, every bin of a chunk fell in the same bank).
+__host__ __device__ __forceinline__ int count_row(int C) {
+  const int w = (C + 1) / 2;
+  return 2 * (w % 2 == 1 ? w : w + 1);
+}
+
 // Lanes of this wave whose 6-bit bin equals this lane's (active lanes only).
 __device__ __forceinline__ uint64_t peers_of(int bin, uint64_t active) {
   uint64_t m = active;
@@ -92,12 +103,14 @@ __global__ __launch_bounds__(kBallotThreads) void bucket_ballot_kernel(BucketArg
   const int K = a.K;
   const int C = (K + 63) / 64;                  // chunks of 64 channels
   const int E = kBins * C;                      // table entries, bin-major
-  const int epad = (E + 7) & ~7;
-  uint16_t* cnt = reinterpret_cast<uint16_t*>(smem);                   // [64][C]
+  const int CP = count_row(C);                  // row stride of the table
+  const int epad = (kBins * CP + 7) & ~7;
+  uint16_t* cnt = reinterpret_cast<uint16_t*>(smem);                   // [64][CP]
   uint32_t* wave_tot = reinterpret_cast<uint32_t*>(smem + 2 * epad);   // [16]
   uint8_t* tags_s = smem + 2 * epad + 64;                              // [K]
   const int kpad = (K + 15) & ~15;
   uint16_t* perm_s = reinterpret_cast<uint16_t*>(tags_s + kpad);       // [K]
+  uint16_t* br_s = perm_s + kpad;                                      // [K]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t below = (1ull << lane) - 1ull;
   const int per = (E + kBallotThreads - 1) / kBallotThreads;   // scan entries per thread
@@ -118,18 +131,31 @@ __global__ __launch_bounds__(kBallotThreads) void bucket_ballot_kernel(BucketArg
     }
     for (int i = tid; i < epad / 8; i += kBallotThreads) reinterpret_cast<uint4*>(cnt)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
+    // Count.  The lane's bin and its rank among the lanes of its chunk with
+    // the same bin are kept (bin | rank << 8, at the channel's own index) for
+    // the placement, so the ballots run once per chunk.
     for (int c = wave; c < C; c += kBallotThreads / 64) {
       const int k = 64 * c + lane;
       const bool act = k < K;
       const uint64_t active = __ballot(act);
       const int bin = act ? bin_of(tags_s[k]) : 0;
       const uint64_t peers = peers_of(bin, active);
-      if (act && (peers & below) == 0) cnt[bin * C + c] = (uint16_t)__popcll(peers);
+      const uint32_t rank = (uint32_t)__popcll(peers & below);
+      if (act) {
+        if (rank == 0u) cnt[bin * CP + c] = (uint16_t)__popcll(peers);
+        br_s[k] = (uint16_t)((uint32_t)bin | (rank << 8));
+      }
     }
     __syncthreads();
     // exclusive scan of cnt in (bin, chunk) order
     uint32_t sum = 0;
-    for (int e = e0; e < e1; ++e) sum += cnt[e];
+    {
+      int b = e0 / max(C, 1), c = e0 - b * C;
+      for (int e = e0; e < e1; ++e) {
+        sum += cnt[b * CP + c];
+        if (++c == C) { c = 0; ++b; }
+      }
+    }
     uint32_t inc = sum;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -140,21 +166,21 @@ __global__ __launch_bounds__(kBallotThreads) void bucket_ballot_kernel(BucketArg
     __syncthreads();
     uint32_t run = inc - sum;
     for (int w = 0; w < wave; ++w) run += wave_tot[w];
-    for (int e = e0; e < e1; ++e) {
-      const uint32_t v = cnt[e];
-      cnt[e] = (uint16_t)run;
-      run += v;
+    {
+      int b = e0 / max(C, 1), c = e0 - b * C;
+      for (int e = e0; e < e1; ++e) {
+        const uint32_t v = cnt[b * CP + c];
+        cnt[b * CP + c] = (uint16_t)run;
+        run += v;
+        if (++c == C) { c = 0; ++b; }
+      }
     }
     __syncthreads();
-    if (tid < kBins) a.group_off[tile * (kBins + 1) + tid] = (int32_t)cnt[tid * C];
+    if (tid < kBins) a.group_off[tile * (kBins + 1) + tid] = (int32_t)cnt[tid * CP];
     if (tid == kBins) a.group_off[tile * (kBins + 1) + kBins] = K;
-    for (int c = wave; c < C; c += kBallotThreads / 64) {
-      const int k = 64 * c + lane;
-      const bool act = k < K;
-      const uint64_t active = __ballot(act);
-      const int bin = act ? bin_of(tags_s[k]) : 0;
-      const uint64_t peers = peers_of(bin, active);
-      if (act) perm_s[cnt[bin * C + c] + __popcll(peers & below)] = (uint16_t)k;
+    for (int k = tid; k < K; k += kBallotThreads) {
+      const uint32_t v = br_s[k];
+      perm_s[cnt[(int)(v & 0xFFu) * CP + (k >> 6)] + (v >> 8)] = (uint16_t)k;
     }
     __syncthreads();
     if (perm16) {
@@ -221,8 +247,8 @@ int launch_bucket(const BucketArgs& a, hipStream_t s) {
   if (a.n_tiles == 0) return DSTAR_OK;
   const int64_t grid = a.n_tiles < 2048 ? a.n_tiles : 2048;
   if (a.K <= kBallotMaxK) {
-    const size_t E = (size_t)kBins * ((a.K + 63) / 64);
-    const size_t lds = 2 * ((E + 7) & ~(size_t)7) + 64 + 3 * (size_t)((a.K + 15) & ~15);
+    const size_t E = (size_t)kBins * count_row((a.K + 63) / 64);
+    const size_t lds = 2 * ((E + 7) & ~(size_t)7) + 64 + 5 * (size_t)((a.K + 15) & ~15);
     if (lds > 65536) {
       hipError_t e = hipFuncSetAttribute((const void*)bucket_ballot_kernel,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
