@@ -262,10 +262,13 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   auto stageB = [&](int st, int w) { return smem + st * kStageDense + BM * BK + w * WN * BK; };
   const int r16 = lane >> 2;                       // row of this lane within a 16-row group
   const int c16 = (lane & 3) ^ ((r16 >> 2) & 3);   // global 16-byte column it loads
-  const int64_t nchunks = K / BK;
+  // K a multiple of 16: the last chunk may hold fewer than 64 channels; a
+  // lane whose 16-byte column starts at K loads from the out-of-range offset,
+  // which writes zeros into LDS, so those columns add nothing.
+  const int64_t nchunks = (K + BK - 1) / BK;
   auto issue = [&](int64_t c, int st) {
     const int64_t k0 = c * BK;
-    const bool live = c < nchunks;
+    const bool live = c < nchunks && k0 + 16 * c16 < K;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int row = 16 * (2 * wave + j) + r16;
@@ -807,12 +810,12 @@ int launch_t(const LinearArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Handles token tiles of 32 or 64 rows, K a multiple of 64 (whole dense
-// chunks) and W below 2^31 bytes (32-bit buffer offsets), given the aligned
-// codes and W^T.
+// Handles token tiles of 32 or 64 rows, K a multiple of 16 (whole 16-byte
+// columns of a dense chunk) and W below 2^31 bytes (32-bit buffer offsets),
+// given the aligned codes and W^T.
 bool linear_mfma_supported(const LinearArgs& a) {
   return a.acodes != nullptr && a.hcodes != nullptr && a.w_t != nullptr && (a.T == 32 || a.T == 64) &&
-         (a.K % 64) == 0 && n_tiles(a.rows, a.T) * a.K * a.T < (int64_t(1) << 31) &&
+         (a.K % 16) == 0 && n_tiles(a.rows, a.T) * a.K * a.T < (int64_t(1) << 31) &&
          (int64_t)a.K * a.N < (int64_t(1) << 31);
 }
 

@@ -211,6 +211,10 @@ SMALL = [
     dict(rows=160, K=1152, N=132, T=32, seed=24, heavy=0.3, c_range=(0.02, 4000.0)),  # N % 16 != 0
     dict(rows=192, K=640, N=256, T=64, seed=25, heavy=0.3, c_range=(0.02, 4000.0)),
     dict(rows=128, K=1152, N=144, T=32, seed=26, heavy=0.15, c_range=(0.05, 2000.0)),
+    # K % 64 != 0 (a multiple of 16): the product kernels' partial last chunk
+    dict(rows=64, K=16, N=64, T=32, seed=27),
+    dict(rows=300, K=1040, N=264, T=32, seed=28, heavy=0.2, c_range=(0.02, 4000.0)),
+    dict(rows=256, K=1072, N=132, T=64, seed=29, heavy=0.3, c_range=(0.02, 4000.0)),
 ]
 
 # Limits of the ABI: the largest K (the bucket's global-memory variant above
@@ -523,6 +527,9 @@ PP_CASES = [
     # two tiles whose first 1024 channels sit at PoT 14: Σ 2^PoT ≥ 2^24, the
     # exact per-group path inside the kernel; every other tile eligible
     dict(rows=2048, K=4096, N=4096, T=32, seed=94, heavy=0.05, c_range=(0.5, 64.0), wide_tiles=(5, 40)),
+    # K % 64 = 16 and 48: a partial last dense chunk
+    dict(rows=2048, K=4112, N=4096, T=32, seed=95, heavy=0.2, c_range=(0.02, 4000.0)),
+    dict(rows=1999, K=4144, N=4100, T=32, seed=96, heavy=0.1, c_range=(0.5, 64.0)),
 ]
 
 
