@@ -86,6 +86,18 @@ __device__ __forceinline__ void store_words(int8_t* dst, const uint32_t (&w)[RT 
   }
 }
 
+// PoT of a sub-channel maximum m ≥ 0 against a normal base in [2^-100, 2^100]:
+// the smallest j in [0, 21] with m ≤ base·2^j (21 if none).  With
+// m = 1.f_m·2^e_m and base = 1.f_b·2^e_b (base·2^j stays normal for j ≤ 21),
+// m ≤ base·2^j holds exactly when j ≥ e_m − e_b + [f_m > f_b]; a zero or
+// subnormal m gives j ≤ 0.  The same integer as counting the edges
+// base·2^j (j = 0..20) below m.
+__device__ __forceinline__ int pot_of(float m, float base) {
+  const uint32_t bm = __float_as_uint(m), bb = __float_as_uint(base);
+  const int j = (int)(bm >> 23) - (int)(bb >> 23) + ((bm & 0x7FFFFFu) > (bb & 0x7FFFFFu) ? 1 : 0);
+  return min(max(j, 0), DSTAR_FMDQ_POT_MAX);
+}
+
 // A work item is kGroups consecutive (tile, channel group) pairs of the
 // flattened [n_t][K / CPT] space, so no lane idles at the end of a tile's
 // channels (with 512-channel slabs, K = 1152 left a quarter of the lanes idle).
@@ -144,10 +156,9 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kernel(QuantizeArgs a, i
 #pragma unroll
       for (int o = 1; o < G; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
       // PoT = number of bin edges base*2^j (j = 0..20) strictly below M, i.e.
-      // the smallest j with M <= base*2^j, capped at 21 (Eq. 3; QPU stage 2).
-      int pot = 0;
-#pragma unroll
-      for (int j = 0; j < DSTAR_FMDQ_POT_MAX; ++j) pot += (m > ldexpf(base, j)) ? 1 : 0;
+      // the smallest j with M <= base*2^j, capped at 21 (Eq. 3; QPU stage 2),
+      // read from the float fields instead of 21 compares.
+      const int pot = pot_of(m, base);
       // Precision from the thresholds base*2^(k0+2N): p = b - 2 = log2(PCeil).
       const int p = pot <= a.k0 ? 0 : pot <= a.k0 + 2 ? 2 : pot <= a.k0 + 4 ? 4 : 6;
       const int e = pot - p;                               // step = base * 2^e
