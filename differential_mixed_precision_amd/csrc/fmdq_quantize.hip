@@ -48,9 +48,18 @@ __device__ __forceinline__ void load_vec(const float* p, float (&v)[CPT]) {
   __builtin_memcpy(v, &t, sizeof(t));
 }
 
+// The low bytes of a, b, c, d as one word, a lowest (byte selects: v_perm_b32
+// takes bytes 0-3 from its second operand, 4-7 from its first, 0x0c = zero).
 __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
-  return (uint32_t(a) & 0xFFu) | ((uint32_t(b) & 0xFFu) << 8) | ((uint32_t(c) & 0xFFu) << 16) |
-         ((uint32_t(d) & 0xFFu) << 24);
+  const uint32_t lo = __builtin_amdgcn_perm((uint32_t)b, (uint32_t)a, 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm((uint32_t)d, (uint32_t)c, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// w with its byte c (0..3; a constant after unrolling) replaced by the low
+// byte of v: select 4 + i (w's byte i) everywhere but byte c, which selects 0.
+__device__ __forceinline__ uint32_t put_byte(uint32_t w, uint32_t v, int c) {
+  return __builtin_amdgcn_perm(w, v, 0x07060504u & ~(0xFFu << (8 * c)));
 }
 
 // Stores the RT codes of one lane (RT = 8, 16 or 32 consecutive bytes).
@@ -127,17 +136,37 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kernel(QuantizeArgs a, i
     const int64_t nrows = a.rows - r0;       // real rows from r0 (may be <= 0)
 
     // Δ = X_t − X_{t−1} for RT rows × CPT channels (Eq. 1), kept in registers.
-    // The loads are unconditional (a row past the end reads the last row and
-    // is zeroed after), so all 2·RT of them are in flight together.
+    // The loads are unconditional, so all 2·RT of them are in flight together:
+    // in a ragged last tile a row past the end reads the last row and is
+    // zeroed after; every other tile takes the path without those selects.
     float d[RT][CPT];
+    if (nrows >= RT) {
+      const float* pt = a.x_t + r0 * K + k;
+      const float* pp = a.x_prev + r0 * K + k;
+      float xt[RT][CPT], xp[RT][CPT];
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const int64_t r = min(r0 + t, a.rows - 1);
-      float xt[CPT], xp[CPT];
-      load_vec<CPT>(a.x_t + r * K + k, xt);
-      load_vec<CPT>(a.x_prev + r * K + k, xp);
+      for (int t = 0; t < RT; ++t) {
+        load_vec<CPT>(pt + t * K, xt[t]);
+        load_vec<CPT>(pp + t * K, xp[t]);
+      }
+      // every load issued before the first use (otherwise the compiler waits
+      // for each row's pair before issuing the next)
+      __asm__ __volatile__("" ::: "memory");
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) d[t][c] = t < nrows ? __fsub_rn(xt[c], xp[c]) : 0.0f;
+      for (int t = 0; t < RT; ++t) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) d[t][c] = __fsub_rn(xt[t][c], xp[t][c]);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const int64_t r = min(r0 + t, a.rows - 1);
+        float xt[CPT], xp[CPT];
+        load_vec<CPT>(a.x_t + r * K + k, xt);
+        load_vec<CPT>(a.x_prev + r * K + k, xp);
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) d[t][c] = t < nrows ? __fsub_rn(xt[c], xp[c]) : 0.0f;
+      }
     }
 
     uint32_t tagword = 0;
@@ -168,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kernel(QuantizeArgs a, i
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         float r = __fmul_rn(__fmul_rn(d[t][c], inv_base), scale);
-        r = fminf(fmaxf(rintf(r), -pceil), pceil);
+        r = __builtin_amdgcn_fmed3f(rintf(r), -pceil, pceil);   // clip to ±PCeil (r is finite)
         q[t] = (int)r;
       }
       // This lane's RT codes of channel k+c: bytes sub*RT .. sub*RT+RT-1 of
@@ -177,7 +206,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kernel(QuantizeArgs a, i
       store_codes<RT>(a.codes + run, q);
       if (pot <= 6) {
 #pragma unroll
-        for (int t = 0; t < RT; ++t) arow[t] |= (((uint32_t)q[t] << e) & 0xFFu) << (8 * c);
+        for (int t = 0; t < RT; ++t) arow[t] = put_byte(arow[t], (uint32_t)q[t] << e, c);
       } else if (a.acodes != nullptr) {
         // Digits of a = q·2^e (|a| ≤ 2^21): d0 in [−64, 63], d1 in
         // [−128, 127], d2 (0 unless PoT ≥ 14), packed as they are formed.
