@@ -66,19 +66,20 @@ constexpr float kLn2Hi = 0x1.63p-1f;
 constexpr float kLn2Lo = -0x1.bd0106p-13f;
 
 // exp32 without its final power of two: e^x = p·2^n (Cody–Waite reduction,
-// then the Taylor polynomial of e^r by Horner's rule, each step rounded to
-// float32).  Branch-free; see exp_fixed_d for the cut-off.
+// then the Taylor polynomial of e^r by Horner's rule, one fused multiply-add
+// per step, each rounded once to float32).  x − n·ln2_hi is exact (n·ln2_hi
+// is exact and close to x).  Branch-free; see exp_fixed_d for the cut-off.
 __device__ __forceinline__ float exp32_poly(float x, int& n_out) {
   const float n = rintf(__fmul_rn(x, kLog2e));
-  const float r = __fsub_rn(__fsub_rn(x, __fmul_rn(n, kLn2Hi)), __fmul_rn(n, kLn2Lo));
+  const float r = __builtin_fmaf(-n, kLn2Lo, __fsub_rn(x, __fmul_rn(n, kLn2Hi)));
   float p = 0x1.a01a02p-13f;                       // 1/5040
-  p = __fadd_rn(__fmul_rn(p, r), 0x1.6c16c2p-10f);  // 1/720
-  p = __fadd_rn(__fmul_rn(p, r), 0x1.111112p-7f);   // 1/120
-  p = __fadd_rn(__fmul_rn(p, r), 0x1.555556p-5f);   // 1/24
-  p = __fadd_rn(__fmul_rn(p, r), 0x1.555556p-3f);   // 1/6
-  p = __fadd_rn(__fmul_rn(p, r), 0.5f);
-  p = __fadd_rn(__fmul_rn(p, r), 1.0f);
-  p = __fadd_rn(__fmul_rn(p, r), 1.0f);
+  p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);       // 1/720
+  p = __builtin_fmaf(p, r, 0x1.111112p-7f);        // 1/120
+  p = __builtin_fmaf(p, r, 0x1.555556p-5f);        // 1/24
+  p = __builtin_fmaf(p, r, 0x1.555556p-3f);        // 1/6
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
   n_out = (int)n;
   return p;
 }

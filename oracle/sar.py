@@ -44,7 +44,8 @@ Readings of points the page leaves open (each listed in the design notes):
   (the P codes) from the same bits: x = fl32(z − max_row z); e = exp32(x), a
   float32 exponential by Cody and Waite's range reduction (W. J. Cody, W.
   Waite, "Software Manual for the Elementary Functions", 1980) and a degree-7
-  Taylor polynomial, every operation rounded to float32 in a fixed order;
+  Taylor polynomial by Horner's rule in fused multiply-adds (one rounding to
+  float32 per step, IEEE 754 fusedMultiplyAdd), every step in a fixed order;
   E = rint(e·2^36) as an integer (x < −26 gives 0), summed exactly per row;
   P = fl32(f64(E) · (1 / f64(ΣE))).
 * Outputs: O = fl32(f64(O_int) · h_c) with O_int = Σ_s (q_P·2^PoT_P)·vq[s][c]
@@ -94,18 +95,45 @@ def mask_to_csr(mask: np.ndarray):
 
 # ---------------------------------------------------------------- exp32
 
+def fma32(a, b, c) -> np.ndarray:
+    """fl32(a·b + c) with a single rounding (IEEE 754 fusedMultiplyAdd, round to
+    nearest, ties to even) for float32 a, b, c of normal magnitude.
+
+    a·b is exact in float64 (24 + 24 significant bits).  s = fl64(a·b + c) and
+    its remainder e (Knuth's TwoSum) give a·b + c = s + e exactly.  Rounding s
+    to float32 gives the right answer unless s is itself a float32 midpoint and
+    e ≠ 0: no other float32 midpoint can lie between s and s + e, since s is
+    the float64 nearest to s + e.  At such a midpoint the exact value lies on
+    e's side."""
+    a64 = np.asarray(a, dtype=np.float32).astype(np.float64)
+    b64 = np.asarray(b, dtype=np.float32).astype(np.float64)
+    c64 = np.asarray(c, dtype=np.float32).astype(np.float64)
+    prod = a64 * b64
+    s = prod + c64
+    bv = s - prod
+    e = (prod - (s - bv)) + (c64 - bv)
+    r = s.astype(np.float32)
+    r64 = r.astype(np.float64)
+    nb = np.nextafter(r, np.where(s > r64, np.float32(np.inf), np.float32(-np.inf)).astype(np.float32))
+    nb64 = nb.astype(np.float64)
+    tie = (s != r64) & (s == (r64 + nb64) * 0.5) & (e != 0)
+    fixed = np.where(e > 0, np.maximum(r64, nb64), np.minimum(r64, nb64)).astype(np.float32)
+    return np.where(tie, fixed, r).astype(np.float32)
+
+
 def exp32(x: np.ndarray) -> np.ndarray:
     """e^x for float32 x ≤ 0, in float32 with a fixed sequence of roundings:
-    n = rint(x·log2 e); r = (x − n·LN2_HI) − n·LN2_LO (Cody–Waite); p(r) the
-    degree-7 Taylor polynomial of e^r by Horner's rule; e = p·2^n.  Values
-    below EXP_X_MIN give 0."""
+    n = rint(x·log2 e); r = (x − n·LN2_HI) − n·LN2_LO (Cody–Waite; the first
+    difference is exact, the second one fused multiply-add); p(r) the degree-7
+    Taylor polynomial of e^r by Horner's rule, one fused multiply-add per
+    coefficient; e = p·2^n.  Values below EXP_X_MIN give 0."""
     x = np.asarray(x, dtype=np.float32)
     xs = np.maximum(x, EXP_X_MIN)
     n = np.rint(xs * LOG2E).astype(np.float32)
-    r = (xs - n * LN2_HI) - n * LN2_LO
+    r = fma32(-n, LN2_LO, xs - n * LN2_HI)
     p = np.full_like(r, EXP_COEF[0])
     for c in EXP_COEF[1:]:
-        p = p * r + c
+        p = fma32(p, r, c)
     e = np.ldexp(p, n.astype(np.int32)).astype(np.float32)
     return np.where(x < EXP_X_MIN, np.float32(0.0), e).astype(np.float32)
 

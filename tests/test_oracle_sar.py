@@ -10,6 +10,7 @@ integer scores, float64 softmax, float64 products) and plain float64 masked
 attention within the quantization error.
 """
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -20,6 +21,42 @@ from oracle import sar
 
 
 # ---------------------------------------------------------------- exp32
+
+def _f32_nearest(q: Fraction) -> np.float32:
+    """The float32 nearest to the rational q, ties to even (brute force over
+    the neighbours of a float64 approximation)."""
+    f = np.float32(float(q))
+    cands = [f, np.nextafter(f, np.float32(np.inf)), np.nextafter(f, np.float32(-np.inf))]
+    best = min(abs(Fraction(float(c)) - q) for c in cands)
+    ties = [c for c in cands if abs(Fraction(float(c)) - q) == best]
+    if len(ties) == 1:
+        return ties[0]
+    return [c for c in ties if (int(np.array(c, np.float32).view(np.uint32)) & 1) == 0][0]
+
+
+def test_fma32_is_one_rounding_of_the_exact_value():
+    rng = np.random.default_rng(7)
+    n = 3000
+    a = (rng.uniform(-2, 2, n) * 2.0 ** rng.integers(-20, 2, n)).astype(np.float32)
+    b = (rng.uniform(-1, 1, n) * 2.0 ** rng.integers(-12, 1, n)).astype(np.float32)
+    c = (rng.uniform(-1, 1, n) * 2.0 ** rng.integers(-14, 1, n)).astype(np.float32)
+    # exact sums on a float32 midpoint after float64 rounding, where rounding
+    # twice (to float64, then to float32) picks the wrong neighbour:
+    # (2^-12(1+2^-23))·(2^-12(1-2^-23)) = 2^-24 - 2^-70, and c = 1 + 2^-23 puts
+    # a·b + c just below the midpoint 1 + 3·2^-24
+    x, y = np.float32(2.0 ** -12 * (1 + 2.0 ** -23)), np.float32(2.0 ** -12 * (1 - 2.0 ** -23))
+    a = np.concatenate([a, [x, -x, x, y]]).astype(np.float32)
+    b = np.concatenate([b, [y, y, x, y]]).astype(np.float32)
+    c = np.concatenate([c, [np.float32(1 + 2.0 ** -23), np.float32(-(1 + 2.0 ** -23)), np.float32(1.0),
+                            np.float32(1 + 2.0 ** -23)]]).astype(np.float32)
+    got = sar.fma32(a, b, c)
+    for i in range(len(a)):
+        want = _f32_nearest(Fraction(float(a[i])) * Fraction(float(b[i])) + Fraction(float(c[i])))
+        assert got[i] == want, (i, a[i], b[i], c[i], got[i], want)
+    # the constructed case differs from two roundings
+    two = np.float32(np.float64(x) * np.float64(y) + np.float64(np.float32(1 + 2.0 ** -23)))
+    assert got[n] != two and got[n] == np.float32(1 + 2.0 ** -23)
+
 
 def test_exp32_against_math_exp():
     x = np.concatenate([np.linspace(-26, 0, 200001), -np.logspace(-8, 0, 2000),
