@@ -319,6 +319,105 @@ def write_kernel_summary(trace_dir: str, which: str = "linear", workload: str = 
     print("\n".join(lines))
 
 
+SQ_LINEAR = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_I8", "SQ_INSTS_VALU_MFMA_I8", "SQ_BUSY_CYCLES",
+             "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY", "GRBM_GUI_ACTIVE")
+SQ_ATTENTION = ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+                "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU")
+N_SIMD, N_XCD = 1024, 8      # MI355X: 256 CUs of 4 SIMDs, in 8 XCDs
+
+
+def write_sq_summary(counter_dir: str, which: str = "linear", workload: str = HEADLINE,
+                     out_dir: str | None = None) -> str:
+    """Summarizes one rocprofv3 --pmc run of SQ counters: for the stage-3
+    kernels (linear) the matrix-core busy fraction and executed int8 ops, for
+    the attention kernels the issue and wait fractions of the waves' resident
+    cycles; means per dispatch."""
+    import csv
+    rows = []
+    for root, _, fs in os.walk(counter_dir):
+        for fn in fs:
+            if fn.endswith("counter_collection.csv"):
+                rows += list(csv.DictReader(open(os.path.join(root, fn))))
+    per = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if which == "linear" and KERNEL_NAME["linear"] not in name:
+            continue
+        if which == "attention" and not ("scores_kernel" in name or "pv_kernel" in name):
+            continue
+        short = name.replace("dstar::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        key = (short, int(r["Grid_Size"]))
+        d = per.setdefault(key, {"dur": {}, "c": {}})
+        d["c"].setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        d["dur"][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    mean = lambda v: sum(v) / len(v)
+    if which == "linear":
+        from gen import workloads as wl
+        spec = next(v for v in wl.CONFIGS.values() if v["name"] == workload)
+        grid_layer = {layer_grids(spec["rows"], spec["token_tile"], k, n)["linear"]: (L, k, n)
+                      for L, (k, n) in spec["layers"].items()}
+        args = f"--workload {workload} --steps 5 --warmup 2 --no-cpu-baseline --no-dynamic --no-chain " \
+               f"--no-slices --no-attention --no-cold --no-per-workload"
+        fname = f"sq_counters_linear_{workload}.md"
+        title = f"# SQ / MFMA counters, stage-3 kernels, {workload} workload"
+        counters = SQ_LINEAR
+    else:
+        args = "--only-attention"
+        fname = "sq_counters_sar_attention_pixart1024.md"
+        title = "# SQ counters, SAR attention kernels, PixArt-alpha-style 1024px attention"
+        counters = SQ_ATTENTION
+    lines = [title, "",
+             "One rocprofv3 counter pass (one run), from the repository root, then the summary:", "",
+             "```",
+             f"rocprofv3 --pmc {' '.join(counters)} --output-format csv -d {counter_dir} -o run -- python3 bench.py {args}",
+             f"python bench.py --write-sq-summary {counter_dir} --summary {which} --workload {workload}",
+             "```", "",
+             "Means per dispatch over the run's launches of each kernel; durations are the counter run's own "
+             "(it serialises launches)."]
+    if which == "linear":
+        lines += ["GRBM_GUI_ACTIVE is summed over the 8 XCDs, so the busy fraction is "
+                  "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs × GRBM_GUI_ACTIVE / 8); executed int8 ops are "
+                  "SQ_INSTS_VALU_MFMA_MOPS_I8 × 512; the spec peak is 5.0 POP/s.", "",
+                  "| kernel | layer | grid | dispatches | us | MFMA instr | busy cycles per MFMA | "
+                  "**MFMA busy / GRBM active** | implied GRBM GHz | executed / algorithmic ops | "
+                  "executed TOP/s (frac) | algorithmic TOP/s (frac) | wait / wave | active / wave |",
+                  "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+        for (short, grid), d in sorted(per.items(), key=lambda x: x[0][1]):
+            c = {k: mean(v) for k, v in d["c"].items()}
+            us = mean(list(d["dur"].values()))
+            L, k, n = grid_layer.get(grid, ("?", 0, 0))
+            alg = 2.0 * spec["rows"] * k * n
+            ops = c["SQ_INSTS_VALU_MFMA_MOPS_I8"] * 512
+            busy = c["SQ_VALU_MFMA_BUSY_CYCLES"]
+            grbm = c["GRBM_GUI_ACTIVE"] / N_XCD
+            lines.append(
+                f"| `{short}` | {L} ({k}→{n}) | {grid} | {len(d['dur'])} | {us:.1f} | "
+                f"{c['SQ_INSTS_VALU_MFMA_I8']:.4g} | {busy / max(c['SQ_INSTS_VALU_MFMA_I8'], 1):.1f} | "
+                f"**{busy / N_SIMD / grbm:.3f}** | {grbm / us / 1e3:.2f} | {ops / alg if alg else 0:.3f} | "
+                f"{ops / us / 1e6:.0f} ({ops / us / 1e6 / INT8_PEAK_TOPS:.3f}) | "
+                f"{alg / us / 1e6:.0f} ({alg / us / 1e6 / INT8_PEAK_TOPS:.3f}) | "
+                f"{c['SQ_WAIT_ANY'] / c['SQ_WAVE_CYCLES']:.3f} | {c['SQ_ACTIVE_INST_ANY'] / c['SQ_WAVE_CYCLES']:.3f} |")
+    else:
+        lines += ["Ratios are to SQ_WAVE_CYCLES (cycles that waves were resident): how much of a wave's life issues "
+                  "instructions, issues vector-ALU instructions, or waits on memory counters (SQ_WAIT_ANY) or on "
+                  "instruction dependencies (SQ_WAIT_INST_ANY).", "",
+                  "| kernel | dispatches | us | SQ_WAVES | SQ_WAVE_CYCLES | SQ_INSTS_VALU | active any / wave | "
+                  "active VALU / wave | wait any / wave | wait inst / wave |",
+                  "|---|---|---|---|---|---|---|---|---|---|"]
+        for (short, grid), d in sorted(per.items()):
+            c = {k: mean(v) for k, v in d["c"].items()}
+            wc = c["SQ_WAVE_CYCLES"]
+            lines.append(f"| `{short}` | {len(d['dur'])} | {mean(list(d['dur'].values())):.1f} | {c['SQ_WAVES']:.0f} | "
+                         f"{wc:.4g} | {c['SQ_INSTS_VALU']:.4g} | {c['SQ_ACTIVE_INST_ANY'] / wc:.3f} | "
+                         f"{c['SQ_ACTIVE_INST_VALU'] / wc:.3f} | {c['SQ_WAIT_ANY'] / wc:.3f} | "
+                         f"{c['SQ_WAIT_INST_ANY'] / wc:.3f} |")
+    out = os.path.join(out_dir or os.path.join(ROOT, "profiles"), fname)
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return out
+
+
 def slice_stream(dm, torch, state, layers, rows, T, stream) -> dict:
     """The 2-bit slice stream (DSTAR §3.1 steps 2-4) of each layer's latest
     codes, timed with HIP events (it is not part of the step: the MFMA path
@@ -648,7 +747,7 @@ def uses_ping_pong(rows: int, T: int, K: int, N: int, cus: int = 256) -> bool:
     """Whether the library's stage-3 dispatch picks the ping-pong kernel
     (the rule of csrc/fmdq_linear.hip)."""
     nt = (rows + T - 1) // T
-    return T == 32 and K % 64 == 0 and K >= 4096 and 2 * ((nt + 7) // 8) * ((N + 255) // 256) >= cus
+    return T == 32 and K % 16 == 0 and K >= 4096 and 2 * ((nt + 7) // 8) * ((N + 255) // 256) >= cus
 
 
 def layer_grids(rows: int, T: int, K: int, N: int) -> dict:
@@ -837,6 +936,8 @@ def main() -> int:
     ap.add_argument("--no-per-workload", action="store_true", help="skip the other workloads' steps")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--write-kernel-summary", metavar="TRACE_DIR")
+    ap.add_argument("--write-sq-summary", metavar="COUNTER_DIR",
+                    help="summarize an SQ counter pass (--summary picks the kernels)")
     ap.add_argument("--summary", choices=["linear", "attention"], default="linear",
                     help="which kernel-time summary --write-kernel-summary writes")
     ap.add_argument("--only-attention", action="store_true", help="time only the SAR attention workload")
@@ -846,6 +947,9 @@ def main() -> int:
         return 0
     if args.write_kernel_summary:
         write_kernel_summary(args.write_kernel_summary, args.summary, args.workload)
+        return 0
+    if args.write_sq_summary:
+        write_sq_summary(args.write_sq_summary, args.summary, args.workload)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the layer shards by token tiles with no "

@@ -64,3 +64,32 @@ def test_roofline_takes_the_longest_stage():
     r = bench.roofline_of(kernels)
     assert r["kernel"] == "linear@fc1" and r["bound"] == "mfma" and r["unit"] == "TOP/s"
     assert abs(r["frac"] - 1740.0 / bench.INT8_PEAK_TOPS) < 1e-12 and r["traffic"] == 123
+
+
+def test_sq_summary_busy_fraction_from_counters(tmp_path):
+    """The stage-3 SQ summary: busy fraction = busy cycles / (1024 SIMDs ·
+    GRBM cycles / 8), executed ops = MOPS · 512, against 2·M·K·N of the layer
+    that the launch grid names."""
+    from gen import workloads as wl
+    spec = next(v for v in wl.CONFIGS.values() if v["name"] == "flux-large")
+    k, n = spec["layers"]["fc2"]
+    grid = bench.layer_grids(spec["rows"], spec["token_tile"], k, n)["linear"]
+    alg = 2 * spec["rows"] * k * n
+    vals = {"SQ_VALU_MFMA_BUSY_CYCLES": 1024 * 32 * 1000, "SQ_INSTS_VALU_MFMA_MOPS_I8": alg / 512,
+            "SQ_INSTS_VALU_MFMA_I8": 1024 * 1000, "SQ_BUSY_CYCLES": 1, "SQ_WAVE_CYCLES": 1000,
+            "SQ_WAIT_ANY": 250, "SQ_ACTIVE_INST_ANY": 500, "GRBM_GUI_ACTIVE": 8 * 64000}
+    d = tmp_path / "pmc"
+    d.mkdir()
+    with open(d / "run_counter_collection.csv", "w") as f:
+        f.write("Dispatch_Id,Grid_Size,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp\n")
+        for disp in (1, 2):
+            for c, v in vals.items():
+                f.write(f'{disp},{grid},"void dstar::(anonymous namespace)::linear_pp_kernel<32, true, false>'
+                        f'(dstar::LinearArgs, int, int)",{c},{v},0,100000\n')
+    out = bench.write_sq_summary(str(d), "linear", "flux-large", out_dir=str(tmp_path))
+    row = [l for l in open(out) if l.startswith("| `linear_pp_kernel")][0]
+    cells = [c.strip() for c in row.strip().strip("|").split("|")]
+    assert cells[1].startswith("fc2") and cells[3] == "2" and cells[4] == "100.0"
+    assert cells[6] == "32.0" and cells[7] == "**0.500**"          # 32000 busy of 64000 per SIMD
+    assert cells[9] == "1.000"                                        # executed = algorithmic
+    assert cells[12] == "0.250" and cells[13] == "0.500"
