@@ -520,6 +520,41 @@ def par_linear_s(codes, tags, perm, off, w, w_scale, y_prev, base, T):
 
 # Shapes large enough for the dispatch to take the ping-pong kernel (T = 32,
 # K >= 4096, its 256 x 256 blocks filling at least half of the CUs).
+def _random_cases(n: int, seed: int) -> list:
+    """Seeded random small shapes across the dispatch: K mostly a multiple of
+    16 (the product kernels, partial last chunks included), sometimes not (the
+    per-group kernel); T of 16, 32 or 64; ragged tiles; batches of two
+    sequences; no, some or all sub-channels heavy; narrow and wide scales."""
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        T = int(r.choice([16, 32, 64]))
+        K = int(16 * r.integers(1, 130)) if r.random() < 0.8 else int(r.integers(1, 700))
+        N = int(4 * r.integers(1, 160))
+        two = r.random() < 0.25
+        tps = int(T * r.integers(1, 8)) if two else int(r.integers(1, 700))
+        rows = 2 * tps if two else tps
+        heavy = float(r.choice([0.0, 0.05, 0.3, 1.0]))
+        c_range = [(0.5, 8.0), (0.02, 4000.0), (4.0, 8.0)][int(r.integers(0, 3))]
+        out.append(dict(rows=rows, K=K, N=N, T=T, seed=200 + i, heavy=heavy, c_range=c_range,
+                        tokens_per_seq=tps))
+    return out
+
+
+RANDOM_CASES = _random_cases(48, 2026)
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES,
+                         ids=lambda c: f"{c['rows']}x{c['K']}x{c['N']}-T{c['T']}-s{c['seed']}")
+def test_random_shapes_match_oracle(dm, case):
+    """Every stage bit for bit against the oracle: codes, tags, histogram,
+    perm and offsets, the exact S of the kernel that runs, the per-group
+    accumulators, and Y_t of both stage-3 paths."""
+    c = dict(case)
+    d = wl.make_custom(c.pop("rows"), c.pop("K"), c.pop("N"), c.pop("T"), seed=c.pop("seed"), **c)
+    full_compare(dm, d)
+
+
 PP_CASES = [
     dict(rows=2041, K=4096, N=4096, T=32, seed=91, heavy=0.2, c_range=(0.5, 64.0)),      # ragged last tile
     dict(rows=2048, K=4096, N=4100, T=32, seed=92, heavy=0.3, c_range=(0.02, 4000.0)),   # N % 16 != 0, d2
