@@ -8,8 +8,9 @@
 // Measured on MI355X over the five workloads: the ping-pong kernel is faster
 // where the reduction is long (K ≥ 4096, so the matrix work dominates the Y
 // stream) and its blocks fill at least half of the CUs; the other kernel
-// everywhere else.  Both need T of 32 (the ping-pong one) or 32/64, K a
-// multiple of 16, the aligned codes, digit planes and W^T.  The general
+// everywhere else.  They need T of 32 (the ping-pong one) or 16/32/64, K a
+// multiple of 16, the aligned codes, digit planes and W^T, and buffers small
+// enough for 32-bit offsets.  The general
 // kernel runs for other shapes and whenever the per-group accumulators are
 // dumped (only it keeps one accumulator per FPoT group).  The S dump is
 // written by whichever kernel runs.

@@ -105,16 +105,21 @@ constexpr int kAhead = kUnits - 1;                         // units in flight ah
 constexpr int kBatch = 32;                                 // units whose ids are staged
 constexpr int kDataBytes = kStages * kStageDense;          // 73728
 static_assert(kUnits * kUnitBytes == kDataBytes, "the two rings share one region");
+// Per-tile metadata is sized for the most token tiles a workgroup holds (8,
+// at T = 16).  The bound parts and digit-list lengths are only used before
+// the first channel ids are written, so they share the ids' region.
+constexpr int kMaxTiles = BM / 16;
 constexpr int kOffEnt = kDataBytes;                        // uint16 [kBatch][KU] channel ids
-constexpr int kOffBp = kOffEnt + kBatch * KU * 2;          // uint64 [4][16] bound parts
-constexpr int kOffOff = kOffBp + 4 * kTags * 8;            // int32 [4][65] bin offsets
-constexpr int kOffRs = kOffOff + 4 * (kBins + 1) * 4;      // int32 [4][16] group starts in perm
-constexpr int kOffRc = kOffRs + 4 * kTags * 4;             // int32 [2][4][16] digit-list lengths
-constexpr int kOffPre = kOffRc + 2 * 4 * kTags * 4;        // int32 [2][4][17] their prefix sums
-constexpr int kOffUs = kOffPre + 2 * 4 * 17 * 4;           // int32 [9] (+pad) unit starts
-constexpr int kOffUi = kOffUs + 12 * 4;                    // uint32 [kBatch] unit tile/rows/plane
-constexpr int kOffElig = kOffUi + kBatch * 4;              // int32 [4]
-constexpr int kLdsBytes = kOffElig + 4 * 4;
+constexpr int kOffBp = kOffEnt;                            // uint64 [8][16] bound parts (meta only)
+constexpr int kOffRc = kOffBp + kMaxTiles * kTags * 8;     // int32 [2][8][16] digit-list lengths (meta only)
+static_assert(kOffRc + 2 * kMaxTiles * kTags * 4 <= kOffEnt + kBatch * KU * 2, "meta fits the ids region");
+constexpr int kOffOff = kOffEnt + kBatch * KU * 2;         // int32 [8][65] bin offsets
+constexpr int kOffRs = kOffOff + kMaxTiles * (kBins + 1) * 4;  // int32 [8][16] group starts in perm
+constexpr int kOffPre = kOffRs + kMaxTiles * kTags * 4;    // int32 [2][8][17] list prefix sums
+constexpr int kOffUs = kOffPre + 2 * kMaxTiles * 17 * 4;   // int32 [17] (+pad) unit starts
+constexpr int kOffUi = kOffUs + 20 * 4;                    // uint32 [kBatch] unit tile/rows/plane
+constexpr int kOffElig = kOffUi + kBatch * 4;              // int32 [8]
+constexpr int kLdsBytes = kOffElig + kMaxTiles * 4;
 static_assert(2 * kLdsBytes <= 160 * 1024, "two workgroups per CU");
 
 // Operand loads go through buffer resources: a load whose offset lies outside
@@ -201,6 +206,12 @@ template <int T, bool VecW, bool Gelu>
 __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, int32_t row_blocks,
                                                                   int32_t col_blocks) {
   constexpr int kTiles = Cfg<T>::kTiles;
+  // Gathered units are scheduled per (32-row block, list): per block, first
+  // the third-digit lists, then the second-digit lists, of the kTPB token
+  // tiles that share the block (two at T = 16, else one).
+  constexpr int kTPB = T < 32 ? 32 / T : 1;
+  constexpr int kSched = 2 * RB * kTPB;             // schedule entries (8 or 16)
+  constexpr int kGo = (kTiles * (kBins + 1) + kThreads - 1) / kThreads;   // offset loads per thread
   // Direct-to-LDS loads per wave per gathered unit: two dword loads of digit
   // codes, and the W rows as four 16-byte or sixteen 4-byte loads.
   constexpr int kOpsUnit = VecW ? 6 : 18;
@@ -211,9 +222,9 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   unsigned long long* bpart = reinterpret_cast<unsigned long long*>(smem + kOffBp);
   int32_t* off_s = reinterpret_cast<int32_t*>(smem + kOffOff);          // [kTiles][65]
   int32_t* rstart = reinterpret_cast<int32_t*>(smem + kOffRs);          // [kTiles][16]
-  int32_t* rc = reinterpret_cast<int32_t*>(smem + kOffRc);              // [2][4][16]
-  int32_t* pre = reinterpret_cast<int32_t*>(smem + kOffPre);            // [2][4][17]
-  int32_t* ustart = reinterpret_cast<int32_t*>(smem + kOffUs);          // [9]
+  int32_t* rc = reinterpret_cast<int32_t*>(smem + kOffRc);              // [2][kTiles][16]
+  int32_t* pre = reinterpret_cast<int32_t*>(smem + kOffPre);            // [2][kTiles][17]
+  int32_t* ustart = reinterpret_cast<int32_t*>(smem + kOffUs);          // [kSched + 1]
   uint32_t* uinfo = reinterpret_cast<uint32_t*>(smem + kOffUi);         // [kBatch]
   int32_t* eligible = reinterpret_cast<int32_t*>(smem + kOffElig);      // [kTiles]
 
@@ -292,9 +303,9 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   // (Unconditional loads: the compiler then waits for exactly these, not for
   // the dense loads issued after them.)
   const rsrc_t r_off = make_rsrc(a.group_off + tile0 * (kBins + 1), (uint32_t)(tiles_here * (kBins + 1) * 4));
-  uint32_t go[2];
+  uint32_t go[kGo];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
+  for (int m = 0; m < kGo; ++m) {
     const int idx = tid + kThreads * m;
     go[m] = __builtin_amdgcn_raw_buffer_load_b32(r_off, idx < kTiles * (kBins + 1) ? (uint32_t)(4 * idx) : kOob, 0, 0);
   }
@@ -302,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
 #pragma unroll
   for (int c = 0; c < kStages; ++c) issue(c, c);   // a chunk past K loads zeros
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
+  for (int m = 0; m < kGo; ++m) {
     const int idx = tid + kThreads * m;
     if (idx < kTiles * (kBins + 1)) off_s[idx] = (int32_t)go[m];
   }
@@ -318,7 +329,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     const int pc14 = max(0, (kTwoDigitPotMax + 2 - e) / 2);   // PoT ≥ 14
     rstart[tid] = o[4 * g];
     rc[tid] = pc7 <= 3 ? o[4 * g + 4 - pc7] - o[4 * g] : 0;
-    rc[4 * kTags + tid] = pc14 <= 3 ? o[4 * g + 4 - pc14] - o[4 * g] : 0;
+    rc[kTiles * kTags + tid] = pc14 <= 3 ? o[4 * g + 4 - pc14] - o[4 * g] : 0;
     unsigned long long b = 0;
 #pragma unroll
     for (int pc = 0; pc < 4; ++pc)
@@ -326,17 +337,16 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     bpart[tid] = b;
   }
   bar_lds();
-  if (wave == 0) {
-    // lane = 16 · tile + group
-    const int i = lane >> 4, g = lane & 15;
-    const bool tile_ok = i < kTiles;
+  if (tid < kTiles * 16) {
+    // thread = 16 · tile + group (up to two waves; a tile's 16 threads sit in
+    // one wave)
+    const int i = tid >> 4, g = tid & 15;
     unsigned long long b = 0;
-    if (tile_ok)
-      for (int g2 = 0; g2 < kTags; ++g2) b += bpart[i * kTags + g2];
-    const bool el = tile_ok && i < tiles_here && b <= kBoundLimit;
-    if (tile_ok && g == 0) eligible[i] = el ? 1 : 0;
+    for (int g2 = 0; g2 < kTags; ++g2) b += bpart[i * kTags + g2];
+    const bool el = i < tiles_here && b <= kBoundLimit;
+    if (g == 0) eligible[i] = el ? 1 : 0;
     // Inclusive prefix sums of both list lengths over the tile's groups.
-    int s0 = tile_ok ? rc[lane] : 0, s1 = tile_ok ? rc[4 * kTags + lane] : 0;
+    int s0 = rc[tid], s1 = rc[kTiles * kTags + tid];
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) {
       const int n0 = __shfl_up(s0, o, 16), n1 = __shfl_up(s1, o, 16);
@@ -345,30 +355,35 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
         s1 += n1;
       }
     }
-    if (tile_ok) {
-      pre[i * 17 + g + 1] = s0;
-      pre[4 * 17 + i * 17 + g + 1] = s1;
-      if (g == 0) {
-        pre[i * 17] = 0;
-        pre[4 * 17 + i * 17] = 0;
-      }
+    pre[i * 17 + g + 1] = s0;
+    pre[kTiles * 17 + i * 17 + g + 1] = s1;
+    if (g == 0) {
+      pre[i * 17] = 0;
+      pre[kTiles * 17 + i * 17] = 0;
     }
-    // Units of (32-row block rb, slot x & 1): slot 0 = third digits, slot 1 =
-    // second digits; unit starts by an exclusive scan over x = 2·rb + slot.
-    const int x = lane & 7, ti = (32 * (x >> 1)) / T;
-    const int tot0 = __shfl(s0, ti * 16 + 15, 64), tot1 = __shfl(s1, ti * 16 + 15, 64);
-    const int elx = __shfl(el ? 1 : 0, ti * 16, 64);
-    int v = (lane < 8 && elx) ? (((x & 1) ? tot0 : tot1) + KU - 1) / KU : 0;
+  }
+  bar_lds();
+  if (wave == 0) {
+    // Unit starts: an exclusive scan over the schedule entries x: block
+    // rb = x / (2·kTPB), entry e = x % (2·kTPB); e < kTPB is the third-digit
+    // list (plane 1) of the block's tile e, the rest the second-digit lists
+    // (plane 0).
+    const int x = lane;
+    const int rb = x / (2 * kTPB), e = x % (2 * kTPB);
+    const int lvl = e < kTPB ? 1 : 0;
+    const int ti = T < 32 ? rb * kTPB + e % kTPB : (32 * rb) / T;
+    int v = 0;
+    if (x < kSched && eligible[ti]) v = (pre[lvl * kTiles * 17 + ti * 17 + 16] + KU - 1) / KU;
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
+    for (int o = 1; o < 16; o <<= 1) {
       const int n = __shfl_up(v, o, 64);
       if (lane >= o) v += n;
     }
-    if (lane < 8) ustart[lane + 1] = v;
+    if (lane < kSched) ustart[lane + 1] = v;
     if (lane == 0) ustart[0] = 0;
   }
   bar_lds();
-  const int U = ustart[2 * RB];   // gathered units of this workgroup
+  const int U = ustart[kSched];   // gathered units of this workgroup
 
   // Channel ids of units [ubase, ubase + kBatch): thread → (unit, 8 ids).
   // fetch() issues the loads into registers, commit() writes them to LDS.
@@ -377,11 +392,16 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     const int uu = ubase + (tid >> 3), q8 = tid & 7;
     int x = 0;
 #pragma unroll
-    for (int st = 4; st >= 1; st >>= 1)   // largest x with ustart[x] <= uu
-      if (x + st < 2 * RB && ustart[x + st] <= uu) x += st;
+    for (int st = 8; st >= 1; st >>= 1)   // largest x with ustart[x] <= uu
+      if (x + st < kSched && ustart[x + st] <= uu) x += st;
     const bool valid = uu < U;
-    const int rb = x >> 1, lvl = (x & 1) ? 0 : 1, i = (32 * rb) / T;
-    const int32_t* pr = pre + lvl * 4 * 17 + i * 17;
+    const int rb = x / (2 * kTPB), e = x % (2 * kTPB);
+    const int lvl = e < kTPB ? 1 : 0;
+    const int i = T < 32 ? rb * kTPB + e % kTPB : (32 * rb) / T;
+    // which part of the unit's 32 rows the tile fills (T = 16: its half), or
+    // which 32 rows of the tile the unit covers (T = 64)
+    const int sub = T < 32 ? e % kTPB : rb % (T / 32 > 0 ? T / 32 : 1);
+    const int32_t* pr = pre + lvl * kTiles * 17 + i * 17;
     const int total = valid ? pr[16] : 0;
     int pos = KU * (uu - ustart[x]) + 8 * q8;
     int g = 0;
@@ -399,7 +419,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
       fid[jj] = __builtin_amdgcn_raw_buffer_load_b16(r_perm, off, 0, 0);
       fok |= (ok ? 1u : 0u) << jj;
     }
-    finfo = (uint32_t)i | ((uint32_t)(rb % (T / 32)) << 2) | ((uint32_t)lvl << 3);
+    finfo = (uint32_t)i | ((uint32_t)sub << 3) | ((uint32_t)lvl << 4);
   };
   auto commit = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -528,8 +548,8 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     commit();
     bar_lds();   // ids visible; every wave is done with the dense ring
     int ubase = 0, u = 0;
-    // Unit starts: lane x holds ustart[x] (x ≤ 8), read with readlane.
-    const int us_lane = ustart[min(lane, 2 * RB)];
+    // Unit starts: lane x holds ustart[x] (x ≤ kSched), read with readlane.
+    const int us_lane = ustart[min(lane, kSched)];
     auto us_at = [&](int x) -> int { return __builtin_amdgcn_readlane(us_lane, x); };
     // Both digit planes of this workgroup's tiles through one resource: the
     // second plane starts plane_off bytes after the first (n_t·K·T < 2^31).
@@ -552,17 +572,23 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
         d.chB[m] = VecW ? en[4 * (4 * wave + m) + (lane >> 4)] : en[16 * wave + m];
     };
     auto issue_ids = [&](int v, const UnitIds& d, bool live) __attribute__((always_inline)) {
-      const int i = (int)(d.inf & 3u);
-      const int rowoff = 32 * (int)((d.inf >> 2) & 1u);
-      const uint32_t poff = (d.inf & 8u) ? plane_off : 0u;
+      const int i = (int)(d.inf & 7u);
+      const int sub = (int)((d.inf >> 3) & 1u);
+      const uint32_t poff = (d.inf & 16u) ? plane_off : 0u;
+      // dword of the tile's T-byte code run this lane loads (rows 4·dw ..
+      // 4·dw + 3 of the run), and whether it lies in the run: at T = 16 the
+      // tile fills rows 16·sub .. 16·sub + 15 of the unit and the other half
+      // reads zeros; at T = 64 the unit is rows 32·sub .. 32·sub + 31 of it
+      const int dw = T < 32 ? (lane & 7) - 4 * sub : (T == 64 ? 8 * sub : 0) + (lane & 7);
+      const bool in_run = T < 32 ? (dw >= 0 && dw < T / 4) : true;
       uint8_t* sA = smem + (v % kUnits) * kUnitBytes;
       uint8_t* sB = sA + kUnitA;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const int mm = 2 * wave + m;              // channels 8·mm .. 8·mm + 7
         const uint32_t ch = d.chA[m];
-        const uint32_t off = live && ch != 0xFFFFu
-                                 ? poff + (uint32_t)(((int64_t)i * K + ch) * T + rowoff + 4 * (lane & 7)) : kOob;
+        const uint32_t off = live && in_run && ch != 0xFFFFu
+                                 ? poff + (uint32_t)(((int64_t)i * K + ch) * T + 4 * dw) : kOob;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r_h, (lds_ptr)(sA + 256 * mm), 4, off, 0, 0, 0);
       }
 #pragma unroll
@@ -627,8 +653,9 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     };
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const int n2 = us_at(2 * rb + 1) - us_at(2 * rb);       // third-digit units
-      const int n1 = us_at(2 * rb + 2) - us_at(2 * rb + 1);   // second-digit units
+      const int x0 = 2 * kTPB * rb;
+      const int n2 = us_at(x0 + kTPB) - us_at(x0);              // third-digit units
+      const int n1 = us_at(x0 + 2 * kTPB) - us_at(x0 + kTPB);   // second-digit units
       if (n1 + n2 == 0) continue;
       v16i tmp[CB];
 #pragma unroll
@@ -659,17 +686,17 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   if (a.s_dbg != nullptr) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const int i = (32 * rb) / T;
-      const int64_t tau = tile0 + i;
-      if (i >= tiles_here || !eligible[i] || tau < a.dbg_lo || tau >= a.dbg_hi) continue;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const int64_t n = nw + 32 * cb + li;
         if (n >= N) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t t = (32 * rb) % T + 8 * (r >> 2) + 4 * h + (r & 3);
-          a.s_dbg[((tau - a.dbg_lo) * T + t) * N + n] = (int64_t)acc[rb][cb][r];
+          const int row = 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);   // of the workgroup's rows
+          const int i = row / T;
+          const int64_t tau = tile0 + i;
+          if (i >= tiles_here || !eligible[i] || tau < a.dbg_lo || tau >= a.dbg_hi) continue;
+          a.s_dbg[((tau - a.dbg_lo) * T + row % T) * N + n] = (int64_t)acc[rb][cb][r];
         }
       }
     }
@@ -712,11 +739,11 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
       if (n >= N) continue;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const int i = (32 * rb) / T;
-        if (!eligible[i]) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t grow = tile0 * T + 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int row = 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (!eligible[row / T]) continue;
+          const int64_t grow = tile0 * T + row;
           if (grow >= a.rows) continue;
           const int64_t idx = grow * N + n;
           const double d = __dmul_rn(__dmul_rn((double)acc[rb][cb][r], base), ws[cb]);
@@ -739,22 +766,23 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     const uint16_t* pm = a.perm + tau * K;
     const int8_t* cd = a.codes + tau * K * T;
     const double wsn = (double)a.w_scale[n];
-    for (int t0 = 0; t0 < T; t0 += 32) {
-      int64_t sum[32];
+    constexpr int TR = T < 32 ? T : 32;   // rows per pass
+    for (int t0 = 0; t0 < T; t0 += TR) {
+      int64_t sum[TR];
 #pragma unroll
-      for (int t = 0; t < 32; ++t) sum[t] = 0;
+      for (int t = 0; t < TR; ++t) sum[t] = 0;
       for (int g = 0; g < kTags; ++g) {
         const int lo = off[4 * g], hi = off[4 * g + 4];
         if (lo == hi) continue;
-        int32_t gs[32];
+        int32_t gs[TR];
 #pragma unroll
-        for (int t = 0; t < 32; ++t) gs[t] = 0;
+        for (int t = 0; t < TR; ++t) gs[t] = 0;
         for (int j = lo; j < hi; ++j) {
           const int64_t k = pm[j];
           const int32_t wv = (int32_t)a.w[k * N + n];
           const int4* c4 = reinterpret_cast<const int4*>(cd + k * T + t0);
 #pragma unroll
-          for (int v = 0; v < 2; ++v) {
+          for (int v = 0; v < TR / 16; ++v) {
             const int4 c = c4[v];
             const int words[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
@@ -762,14 +790,14 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
           }
         }
 #pragma unroll
-        for (int t = 0; t < 32; ++t) sum[t] += (int64_t)gs[t] << (DSTAR_FMDQ_TAG_OFFSET - g);
+        for (int t = 0; t < TR; ++t) sum[t] += (int64_t)gs[t] << (DSTAR_FMDQ_TAG_OFFSET - g);
       }
       if (a.s_dbg != nullptr && tau >= a.dbg_lo && tau < a.dbg_hi) {
 #pragma unroll
-        for (int t = 0; t < 32; ++t) a.s_dbg[((tau - a.dbg_lo) * T + t0 + t) * N + n] = sum[t];
+        for (int t = 0; t < TR; ++t) a.s_dbg[((tau - a.dbg_lo) * T + t0 + t) * N + n] = sum[t];
       }
 #pragma unroll
-      for (int t = 0; t < 32; ++t) {
+      for (int t = 0; t < TR; ++t) {
         const int64_t grow = tau * T + t0 + t;
         if (grow >= a.rows) continue;
         const int64_t idx = grow * N + n;
@@ -810,17 +838,20 @@ int launch_t(const LinearArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Handles token tiles of 32 or 64 rows, K a multiple of 16 (whole 16-byte
-// columns of a dense chunk) and W below 2^31 bytes (32-bit buffer offsets),
-// given the aligned codes and W^T.
+// Handles token tiles of 16, 32 or 64 rows, K a multiple of 16 (whole
+// 16-byte columns of a dense chunk), W below 2^31 bytes and each digit
+// plane at most 2^30 bytes (32-bit buffer offsets, with the out-of-range
+// offset 2^31 past every resource), given the aligned codes and W^T.
 bool linear_mfma_supported(const LinearArgs& a) {
-  return a.acodes != nullptr && a.hcodes != nullptr && a.w_t != nullptr && (a.T == 32 || a.T == 64) &&
-         (a.K % 16) == 0 && n_tiles(a.rows, a.T) * a.K * a.T < (int64_t(1) << 31) &&
-         (int64_t)a.K * a.N < (int64_t(1) << 31);
+  return a.acodes != nullptr && a.hcodes != nullptr && a.w_t != nullptr &&
+         (a.T == 16 || a.T == 32 || a.T == 64) &&
+         (a.K % 16) == 0 && 2 * n_tiles(a.rows, a.T) * a.K * a.T <= (int64_t(1) << 31) &&
+         (int64_t)a.K * a.N < (int64_t(1) << 31) && (int64_t)a.N * 4 * BM < (int64_t(1) << 32);
 }
 
 int launch_linear_mfma(const LinearArgs& a, hipStream_t s) {
   switch (a.T) {
+    case 16: return launch_t<16>(a, s);
     case 32: return launch_t<32>(a, s);
     case 64: return launch_t<64>(a, s);
     default: return set_error(DSTAR_EUNSUPPORTED, "fmdq_linear (mfma): token_tile %d", a.T);

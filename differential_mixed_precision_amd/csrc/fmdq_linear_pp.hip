@@ -834,12 +834,13 @@ int launch_t(const LinearArgs& a, hipStream_t s) {
 }  // namespace
 
 // Handles token tiles of 32 or 64 rows, K a multiple of 16 (whole 16-byte
-// columns of a dense chunk) and W below 2^31 bytes (32-bit buffer offsets),
-// given the aligned codes and W^T.
+// columns of a dense chunk), W below 2^31 bytes and each digit plane at
+// most 2^30 bytes (32-bit buffer offsets, with the out-of-range offset 2^31
+// past every resource), given the aligned codes and W^T.
 bool linear_pp_supported(const LinearArgs& a) {
   return a.acodes != nullptr && a.hcodes != nullptr && a.w_t != nullptr && (a.T == 32 || a.T == 64) &&
-         (a.K % 16) == 0 && n_tiles(a.rows, a.T) * a.K * a.T < (int64_t(1) << 31) &&
-         (int64_t)a.K * a.N < (int64_t(1) << 31);
+         (a.K % 16) == 0 && 2 * n_tiles(a.rows, a.T) * a.K * a.T <= (int64_t(1) << 31) &&
+         (int64_t)a.K * a.N < (int64_t(1) << 31) && (int64_t)a.N * 4 * HM < (int64_t(1) << 32);
 }
 
 int launch_linear_pp(const LinearArgs& a, hipStream_t s) {

@@ -217,8 +217,8 @@ int dstar_fmdq_pack_weights(int32_t K, int32_t N, const int8_t* w, int8_t* w_t,
  *              the shape allows it, else the per-group kernel.  For checking.
  * Per output: S = Σ_g acc_g * 2^(15-g) (an exact integer);
  * y_out = fl32(f64(y_prev) + (f64(S) * f64(base)) * f64(w_scale[n])).
- * With acodes, hcodes and w_t given (T of 32 or 64, K % 16 == 0, K*N and
- * n_t*K*T below 2^31) the MFMA kernel runs: S = acodes x w_t + 2^7 * (d1
+ * With acodes, hcodes and w_t given (T of 16, 32 or 64, K % 16 == 0, K*N
+ * below 2^31, n_t*K*T at most 2^30, N below 2^23) the MFMA kernel runs: S = acodes x w_t + 2^7 * (d1
  * digits x w) + 2^15 * (d2 digits x w), the digit terms over the channels
  * with PoT >= 7 (resp. >= 14) of each token tile, which are prefixes of the
  * FPoT groups in perm; a token tile whose int32 accumulator it cannot prove

@@ -215,6 +215,10 @@ SMALL = [
     dict(rows=64, K=16, N=64, T=32, seed=27),
     dict(rows=300, K=1040, N=264, T=32, seed=28, heavy=0.2, c_range=(0.02, 4000.0)),
     dict(rows=256, K=1072, N=132, T=64, seed=29, heavy=0.3, c_range=(0.02, 4000.0)),
+    # T = 16 through the MFMA kernel (two token tiles per 32-row block)
+    dict(rows=200, K=1152, N=260, T=16, seed=36, heavy=0.3, c_range=(0.02, 4000.0)),  # d2, ragged
+    dict(rows=96, K=4096, N=96, T=16, seed=37, heavy=1.0, c_range=(4.0, 8.0)),
+    dict(rows=64, K=8192, N=72, T=16, seed=38, heavy=1.0, c_range=(4.0, 8.0)),
 ]
 
 # Limits of the ABI: the largest K (the bucket's global-memory variant above
@@ -314,6 +318,27 @@ def test_saturated_and_extreme_subchannels(dm):
         d["k0"] = k0
         d["name"] = f"extreme-k0={k0}"
         full_compare(dm, d)
+
+
+def test_t16_block_with_one_ineligible_tile(dm):
+    """T = 16: the two token tiles of the first 32-row block differ in
+    eligibility (tile 1 has sixteen sub-channels at PoT 21, so 128·Σ 2^PoT
+    reaches 2^31 and it takes the exact per-group path) while tile 0 and the
+    next block's tiles (one with a third digit) go through the MFMA sums."""
+    rng = np.random.default_rng(39)
+    rows, K, N, T = 64, 64, 48, 16
+    base = np.float32(0.01)
+    x_prev = rng.standard_normal((rows, K)).astype(np.float32)
+    delta = rng.standard_normal((rows, K)) * 0.05
+    delta[16, :16] = base * 2.0 ** 21
+    delta[40, 20] = -base * 2.0 ** 15
+    delta[50, 21] = base * 2.0 ** 9
+    x_t = (x_prev.astype(np.float64) + delta).astype(np.float32)
+    d = dict(x_t=x_t, x_prev=x_prev, w=rng.integers(-128, 128, (K, N)).astype(np.int8),
+             w_scale=rng.uniform(1e-3, 1e-2, N).astype(np.float32),
+             y_prev=rng.standard_normal((rows, N)).astype(np.float32), base=base, k0=2,
+             token_tile=T, rows=rows, tokens_per_seq=rows, K=K, N=N, name="t16-mixed")
+    full_compare(dm, d)
 
 
 def test_config0_full(dm):
