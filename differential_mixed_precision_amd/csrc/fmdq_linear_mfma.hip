@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases stay scalar
   const int li = lane & 31, h = lane >> 5;
   const int64_t K = a.K, N = a.N;
   const int64_t nt = n_tiles(a.rows, T);
@@ -571,10 +571,25 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
       for (int m = 0; m < kNB; ++m)
         d.chB[m] = VecW ? en[4 * (4 * wave + m) + (lane >> 4)] : en[16 * wave + m];
     };
+    // The lane's fixed part of each W-row load: the 16-byte piece (VecW: of
+    // 16 bytes, else a dword of it) of its channel's 256-byte row segment.
+    uint32_t colB[kNB];
+#pragma unroll
+    for (int m = 0; m < kNB; ++m) {
+      if constexpr (VecW) {
+        const int c = 4 * (4 * wave + m) + (lane >> 4);
+        colB[m] = (uint32_t)(n0 + 16 * ((lane & 15) ^ (c & 7)));
+      } else {
+        const int c = 16 * wave + m;
+        colB[m] = (uint32_t)(n0 + 16 * ((lane >> 2) ^ (c & 7)) + 4 * (lane & 3));
+      }
+    }
+    const uint32_t tileKT = (uint32_t)(K * T);   // bytes of one tile's digit plane
     auto issue_ids = [&](int v, const UnitIds& d, bool live) __attribute__((always_inline)) {
-      const int i = (int)(d.inf & 7u);
-      const int sub = (int)((d.inf >> 3) & 1u);
-      const uint32_t poff = (d.inf & 16u) ? plane_off : 0u;
+      const uint32_t inf = __builtin_amdgcn_readfirstlane(d.inf);   // the same in every lane
+      const int i = (int)(inf & 7u);
+      const int sub = (int)((inf >> 3) & 1u);
+      const uint32_t abase = ((inf & 16u) ? plane_off : 0u) + (uint32_t)i * tileKT;
       // dword of the tile's T-byte code run this lane loads (rows 4·dw ..
       // 4·dw + 3 of the run), and whether it lies in the run: at T = 16 the
       // tile fills rows 16·sub .. 16·sub + 15 of the unit and the other half
@@ -583,29 +598,25 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
       const bool in_run = T < 32 ? (dw >= 0 && dw < T / 4) : true;
       uint8_t* sA = smem + (v % kUnits) * kUnitBytes;
       uint8_t* sB = sA + kUnitA;
+      // Offsets in 32 bits: ch·T + the tile's plane part < 2^31 and, with
+      // ch < 2^16 and N < 2^23, ch·N is a 24-bit product below K·N < 2^31.
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const int mm = 2 * wave + m;              // channels 8·mm .. 8·mm + 7
         const uint32_t ch = d.chA[m];
-        const uint32_t off = live && in_run && ch != 0xFFFFu
-                                 ? poff + (uint32_t)(((int64_t)i * K + ch) * T + 4 * dw) : kOob;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_h, (lds_ptr)(sA + 256 * mm), 4, off, 0, 0, 0);
+        const uint32_t off = abase + ch * (uint32_t)T + (uint32_t)(4 * dw);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_h, (lds_ptr)(sA + 256 * mm), 4,
+                                                 live && in_run && ch != 0xFFFFu ? off : kOob, 0, 0, 0);
       }
 #pragma unroll
       for (int m = 0; m < kNB; ++m) {
         const uint32_t ch = d.chB[m];
+        const uint32_t off = __umul24(ch, (uint32_t)N) + colB[m];
+        const uint32_t o = live && ch != 0xFFFFu ? off : kOob;
         if constexpr (VecW) {
-          const int jj = 4 * wave + m;            // channels 4·jj .. 4·jj + 3
-          const int c = 4 * jj + (lane >> 4);
-          const int piece = (lane & 15) ^ (c & 7);
-          const uint32_t off = live && ch != 0xFFFFu ? (uint32_t)((int64_t)ch * N + n0 + 16 * piece) : kOob;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr)(sB + 1024 * jj), 16, off, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr)(sB + 1024 * (4 * wave + m)), 16, o, 0, 0, 0);
         } else {
-          const int c = 16 * wave + m;            // one channel row of 256 bytes
-          const int piece = (lane >> 2) ^ (c & 7);
-          const uint32_t off = live && ch != 0xFFFFu
-                                   ? (uint32_t)((int64_t)ch * N + n0 + 16 * piece + 4 * (lane & 3)) : kOob;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr)(sB + BN * c), 4, off, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr)(sB + BN * (16 * wave + m)), 4, o, 0, 0, 0);
         }
       }
     };
