@@ -46,7 +46,7 @@ class FmdqLayer:
     """
 
     def __init__(self, w, w_scale, rows: int, token_tile: int, base: float, thr0_log2: int,
-                 tokens_per_seq: int | None = None):
+                 tokens_per_seq: int | None = None, plain_codes: bool = True):
         import torch
         assert w.dtype == torch.int8 and w.is_cuda and w.dim() == 2
         self.K, self.N = int(w.shape[0]), int(w.shape[1])
@@ -55,7 +55,11 @@ class FmdqLayer:
         self.T = token_tile
         nt = n_tiles(rows, token_tile)
         dev = w.device
-        self.codes = torch.empty((nt, self.K, token_tile), dtype=torch.int8, device=dev)
+        # The plain codes ([n_t][K][T]) are read only by the per-group kernel
+        # and the 2-bit slice stream; the MFMA kernels multiply the aligned
+        # codes and digit planes, so with plain_codes=False stage 1 skips them.
+        self.codes = (torch.empty((nt, self.K, token_tile), dtype=torch.int8, device=dev)
+                      if plain_codes else None)
         self.tags = torch.empty((nt, self.K), dtype=torch.uint8, device=dev)
         self.acodes = torch.empty((nt * token_tile, self.K), dtype=torch.int8, device=dev)
         self.hcodes = torch.empty((2, nt, self.K, token_tile), dtype=torch.int8, device=dev)

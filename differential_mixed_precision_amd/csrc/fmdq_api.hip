@@ -78,9 +78,11 @@ int quantize_impl(const dstar_fmdq_params* p, const float* base_dev, const float
   int64_t nt = 0;
   if (int rc = check_params(p, &nt)) return rc;
   if (p->rows == 0) return DSTAR_OK;
-  if (!x_t || !x_prev || !codes || !tags)
-    return set_error(DSTAR_ENULL, "quantize: x_t, x_prev, codes and tags must not be NULL");
-  if (!aligned(x_t, 16) || !aligned(x_prev, 16) || !aligned(codes, 16) || !aligned(tags, 4))
+  if (!x_t || !x_prev || !tags)
+    return set_error(DSTAR_ENULL, "quantize: x_t, x_prev and tags must not be NULL");
+  if (!codes && !acodes)
+    return set_error(DSTAR_ENULL, "quantize: codes may be NULL only when acodes and hcodes are given");
+  if (!aligned(x_t, 16) || !aligned(x_prev, 16) || (codes && !aligned(codes, 16)) || !aligned(tags, 4))
     return set_error(DSTAR_EALIGN,
                      "quantize: x_t, x_prev and codes must be 16-byte aligned, tags 4-byte aligned");
   if (bit_hist && !aligned(bit_hist, 4))
@@ -288,10 +290,12 @@ int linear_impl(const dstar_fmdq_params* p, const float* base_dev, int32_t N, co
     return set_error(DSTAR_EINVAL, "linear: debug tile range [%d, %d) not within [0, %lld)",
                      dbg_tile_lo, dbg_tile_hi, (long long)nt);
   if (nt == 0) return DSTAR_OK;
-  if (!codes || !perm || !group_off || !w || !w_scale || !y_prev || !y_out)
+  if (!perm || !group_off || !w || !w_scale || !y_prev || !y_out)
     return set_error(DSTAR_ENULL,
-                     "linear: codes, perm, group_off, w, w_scale, y_prev and y_out must not be NULL");
-  if (!aligned(codes, 16) || !aligned(w, 16) || !aligned(y_prev, 16) || !aligned(y_out, 16) ||
+                     "linear: perm, group_off, w, w_scale, y_prev and y_out must not be NULL");
+  if (!codes && (!acodes || !hcodes))
+    return set_error(DSTAR_ENULL, "linear: codes may be NULL only when acodes and hcodes are given");
+  if ((codes && !aligned(codes, 16)) || !aligned(w, 16) || !aligned(y_prev, 16) || !aligned(y_out, 16) ||
       !aligned(w_scale, 4) || !aligned(perm, 2) || !aligned(group_off, 4) ||
       (acc_dbg && !aligned(acc_dbg, 4)) || (s_dbg && !aligned(s_dbg, 8)) ||
       (acodes && !aligned(acodes, 16)) ||

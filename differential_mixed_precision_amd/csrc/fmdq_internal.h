@@ -81,6 +81,58 @@ struct LinearArgs {
   float* gelu_out;         // non-NULL: GELU(Y_t) is stored here as well
 };
 int launch_linear(const LinearArgs& a, hipStream_t s);
+// The exact S of rows t0 .. t0 + TR − 1 of token tile tau at column n, for a
+// tile the product kernels cannot prove exact in int32: every channel's
+// shift-aligned value a = q·2^e = d0 + 2^7·d1 + 2^15·d2 is rebuilt from the
+// aligned codes (d0) and the digit planes, whose entries exist only for the
+// sub-channels with PoT ≥ 7 (d1) and PoT ≥ 14 (d2), and S = Σ_k a·W[k][n]
+// is summed in int64 (|a| ≤ 2^21, |W| ≤ 128, K < 2^16).  The channels are
+// walked bin by bin in perm order: bin b holds FPoT tag g = b / 4 and
+// precision code pc = 3 − b mod 4, so PoT = (15 − g) + 2·pc.  This is
+// Σ_g 2^(15−g) · Σ_{k in group g} q·W of §3.1 step 5 regrouped by channel.
+template <int T, int TR>
+__device__ __forceinline__ void aligned_tile_sums(const LinearArgs& a, const int32_t* off, int64_t tau, int t0,
+                                                  int64_t n, int64_t (&sum)[TR]) {
+  const int64_t K = a.K, N = a.N;
+  const uint16_t* pm = a.perm + tau * K;
+  const int8_t* ac = a.acodes + (tau * T + t0) * K;           // row t0 of the tile, [rows][K]
+  const int8_t* h1 = a.hcodes + tau * K * T + t0;             // [n_t][K][T] planes
+  const int8_t* h2 = h1 + n_tiles(a.rows, T) * K * T;
+#pragma unroll
+  for (int t = 0; t < TR; ++t) sum[t] = 0;
+  for (int b = 0; b < DSTAR_FMDQ_NUM_BINS; ++b) {
+    const int lo = off[b], hi = off[b + 1];
+    if (lo == hi) continue;
+    const int pot = (DSTAR_FMDQ_TAG_OFFSET - (b >> 2)) + 2 * (3 - (b & 3));
+    for (int j = lo; j < hi; ++j) {
+      const int64_t k = pm[j];
+      const int64_t wv = (int64_t)a.w[k * N + n];
+      int32_t av[TR];
+#pragma unroll
+      for (int t = 0; t < TR; ++t) av[t] = (int32_t)ac[t * K + k];
+      if (pot >= 7) {
+#pragma unroll
+        for (int v = 0; v < TR / 16; ++v) {
+          const int4 c = reinterpret_cast<const int4*>(h1 + k * T)[v];
+          const int words[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+          for (int q = 0; q < 16; ++q) av[16 * v + q] += 128 * (int32_t)(int8_t)(words[q >> 2] >> (8 * (q & 3)));
+        }
+      }
+      if (pot >= 14) {
+#pragma unroll
+        for (int v = 0; v < TR / 16; ++v) {
+          const int4 c = reinterpret_cast<const int4*>(h2 + k * T)[v];
+          const int words[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+          for (int q = 0; q < 16; ++q) av[16 * v + q] += 32768 * (int32_t)(int8_t)(words[q >> 2] >> (8 * (q & 3)));
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < TR; ++t) sum[t] += (int64_t)av[t] * wv;
+    }
+  }
+}
 struct BaseArgs {
   const float* x_t;
   const float* x_prev;

@@ -12,8 +12,9 @@
 // multiple of 16, the aligned codes, digit planes and W^T, and buffers small
 // enough for 32-bit offsets.  The general
 // kernel runs for other shapes and whenever the per-group accumulators are
-// dumped (only it keeps one accumulator per FPoT group).  The S dump is
-// written by whichever kernel runs.
+// dumped (only it keeps one accumulator per FPoT group); it alone reads the
+// plain codes, which the MFMA kernels do not need.  The S dump is written by
+// whichever kernel runs.
 #include "fmdq_internal.h"
 
 namespace dstar {
@@ -39,6 +40,10 @@ int launch_linear(const LinearArgs& a, hipStream_t s) {
     if (2 * blocks >= cu_count()) return launch_linear_pp(a, s);
   }
   if (a.acc_dbg == nullptr && linear_mfma_supported(a)) return launch_linear_mfma(a, s);
+  if (a.codes == nullptr)
+    return set_error(DSTAR_ENULL,
+                     "fmdq_linear: codes are needed here (the per-group kernel runs: acc_dbg given, no W^T, "
+                     "or a shape the MFMA kernels do not take)");
   return launch_linear_general(a, s);
 }
 

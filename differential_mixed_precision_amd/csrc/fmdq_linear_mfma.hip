@@ -29,10 +29,10 @@
 // so the final accumulator equals S whenever |S| < 2^31; |W| ≤ 128 (any
 // int8, −128 included) gives |S| ≤ 128 · Σ_k 2^PoT_k, so a token tile is
 // handled here only if 128 · Σ_k 2^PoT_k < 2^31 (computed from stage 2's bin
-// counts).  Any other tile ("ineligible") is
-// finished by an exact scalar path in the same workgroup that walks the
-// tile's FPoT groups in perm order with int32 group sums shifted into an int64
-// sum.
+// counts).  Any other tile ("ineligible") is finished by an exact scalar path
+// in the same workgroup: int64 sums of every channel's aligned value, rebuilt
+// from the aligned codes and digit planes while walking perm bin by bin
+// (aligned_tile_sums).  Neither path reads the plain codes.
 //
 // Stage 2 orders each FPoT group widest precision first, so the channels of a
 // group with PoT ≥ 7 are a prefix of the group in perm, found from the bin
@@ -766,43 +766,19 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     }
   }
 
-  // ---- Ineligible tiles: exact scalar path over the FPoT groups in perm
-  // order, int32 group sums shifted into int64.  Thread = one column.
+  // ---- Ineligible tiles: exact int64 path over the channels in perm order,
+  // from the aligned codes and digit planes.  Thread = one column.
   for (int i = 0; i < tiles_here; ++i) {
     if (eligible[i]) continue;
     const int64_t tau = tile0 + i;
     const int64_t n = n0 + tid;
     if (n >= N) continue;
     const int32_t* off = off_s + i * (kBins + 1);
-    const uint16_t* pm = a.perm + tau * K;
-    const int8_t* cd = a.codes + tau * K * T;
     const double wsn = (double)a.w_scale[n];
     constexpr int TR = T < 32 ? T : 32;   // rows per pass
     for (int t0 = 0; t0 < T; t0 += TR) {
       int64_t sum[TR];
-#pragma unroll
-      for (int t = 0; t < TR; ++t) sum[t] = 0;
-      for (int g = 0; g < kTags; ++g) {
-        const int lo = off[4 * g], hi = off[4 * g + 4];
-        if (lo == hi) continue;
-        int32_t gs[TR];
-#pragma unroll
-        for (int t = 0; t < TR; ++t) gs[t] = 0;
-        for (int j = lo; j < hi; ++j) {
-          const int64_t k = pm[j];
-          const int32_t wv = (int32_t)a.w[k * N + n];
-          const int4* c4 = reinterpret_cast<const int4*>(cd + k * T + t0);
-#pragma unroll
-          for (int v = 0; v < TR / 16; ++v) {
-            const int4 c = c4[v];
-            const int words[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-            for (int b = 0; b < 16; ++b) gs[16 * v + b] += (int32_t)(int8_t)(words[b >> 2] >> (8 * (b & 3))) * wv;
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < TR; ++t) sum[t] += (int64_t)gs[t] << (DSTAR_FMDQ_TAG_OFFSET - g);
-      }
+      aligned_tile_sums<T, TR>(a, off, tau, t0, n, sum);
       if (a.s_dbg != nullptr && tau >= a.dbg_lo && tau < a.dbg_hi) {
 #pragma unroll
         for (int t = 0; t < TR; ++t) a.s_dbg[((tau - a.dbg_lo) * T + t0 + t) * N + n] = sum[t];

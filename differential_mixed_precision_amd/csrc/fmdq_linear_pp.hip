@@ -29,8 +29,9 @@
 // int8, −128 included) gives |S| ≤ 128 · Σ_k 2^PoT_k, so a token tile is
 // handled here only if 128 · Σ_k 2^PoT_k < 2^31 (computed from stage 2's bin
 // counts).  Any other tile ("ineligible") is finished by an exact scalar path
-// in the same workgroup that walks the tile's FPoT groups in perm order with
-// int32 group sums shifted into an int64 sum.
+// in the same workgroup: int64 sums of every channel's aligned value, rebuilt
+// from the aligned codes and digit planes while walking perm bin by bin
+// (aligned_tile_sums).  Neither path reads the plain codes.
 //
 // Layout.  Workgroup = 512 threads = 8 waves (two per SIMD: waves w and w+4
 // share one), output block 256 rows × 256 columns, one workgroup per CU.  The
@@ -760,8 +761,8 @@ __global__ __launch_bounds__(kThreads, 1) void linear_pp_kernel(LinearArgs a, in
     }
   }
 
-  // ---- Ineligible tiles: exact scalar path over the FPoT groups in perm
-  // order, int32 group sums shifted into int64.  Thread of the half = one
+  // ---- Ineligible tiles: exact int64 path over the channels in perm order,
+  // from the aligned codes and digit planes.  Thread of the half = one
   // column.
   for (int il = 0; il < kTilesH; ++il) {
     const int i = half * kTilesH + il;
@@ -770,34 +771,10 @@ __global__ __launch_bounds__(kThreads, 1) void linear_pp_kernel(LinearArgs a, in
     const int64_t n = n0 + htid;
     if (n >= N) continue;
     const int32_t* off = off_s + i * (kBins + 1);
-    const uint16_t* pm = a.perm + tau * K;
-    const int8_t* cd = a.codes + tau * K * T;
     const double wsn = (double)a.w_scale[n];
     for (int t0 = 0; t0 < T; t0 += 32) {
       int64_t sum[32];
-#pragma unroll
-      for (int t = 0; t < 32; ++t) sum[t] = 0;
-      for (int g = 0; g < kTags; ++g) {
-        const int lo = off[4 * g], hi = off[4 * g + 4];
-        if (lo == hi) continue;
-        int32_t gs[32];
-#pragma unroll
-        for (int t = 0; t < 32; ++t) gs[t] = 0;
-        for (int j = lo; j < hi; ++j) {
-          const int64_t k = pm[j];
-          const int32_t wv = (int32_t)a.w[k * N + n];
-          const int4* c4 = reinterpret_cast<const int4*>(cd + k * T + t0);
-#pragma unroll
-          for (int v = 0; v < 2; ++v) {
-            const int4 c = c4[v];
-            const int words[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-            for (int b = 0; b < 16; ++b) gs[16 * v + b] += (int32_t)(int8_t)(words[b >> 2] >> (8 * (b & 3))) * wv;
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < 32; ++t) sum[t] += (int64_t)gs[t] << (DSTAR_FMDQ_TAG_OFFSET - g);
-      }
+      aligned_tile_sums<T, 32>(a, off, tau, t0, n, sum);
       if (a.s_dbg != nullptr && tau >= a.dbg_lo && tau < a.dbg_hi) {
 #pragma unroll
         for (int t = 0; t < 32; ++t) a.s_dbg[((tau - a.dbg_lo) * T + t0 + t) * N + n] = sum[t];

@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kThreads, 2) void quantize_kernel(QuantizeArgs a, i
       // This lane's RT codes of channel k+c: bytes sub*RT .. sub*RT+RT-1 of
       // the channel's run at codes[(tile*K + k + c)*T].
       const int64_t run = (tile * K + k + c) * T + sub * RT;
-      store_codes<RT>(a.codes + run, q);
+      if (a.codes != nullptr) store_codes<RT>(a.codes + run, q);
       if (pot <= 6) {
 #pragma unroll
         for (int t = 0; t < RT; ++t) arow[t] = put_byte(arow[t], (uint32_t)q[t] << e, c);

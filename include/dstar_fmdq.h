@@ -24,7 +24,8 @@
  * offsets; stage 3 taking codes, tags, ids, offsets and W):
  *   - stage 1 also writes the shift-aligned codes and their high digits
  *     (acodes, hcodes), the operands of the MFMA kernels (DSTAR §3.1 step 5:
- *     the alignment is applied to the codes before the multiply);
+ *     the alignment is applied to the codes before the multiply), and may
+ *     then leave out the plain codes, which only the per-group kernel reads;
  *   - stage 2 orders ties inside one tag by precision, widest first, then by
  *     channel, and writes 65 offsets, one per (tag, precision) bin plus the
  *     end (DSTAR §3.1 step 3 fixes only the tag order);
@@ -109,7 +110,9 @@ typedef struct {
  *   x_t, x_prev  [rows][K] float32 row-major, 16-byte aligned.
  *   codes        [n_t][K][T] int8 (out): code of row τT+t, channel k at
  *                codes[(τK + k)T + t]; rows past the end of a ragged last tile
- *                are written 0.  16-byte aligned.
+ *                are written 0.  16-byte aligned.  May be NULL when acodes
+ *                and hcodes are given (they hold the same codes, aligned);
+ *                NULL without them is DSTAR_ENULL.
  *   tags         [n_t][K] uint8 (out), 4-byte aligned: bits 0-3 the FPoT tag
  *                g = (b-2) - PoT + 15 (ascending g = ascending FPoT; the
  *                sub-channel's step is base * 2^(15-g)), bits 4-5 the
@@ -192,7 +195,10 @@ int dstar_fmdq_pack_weights(int32_t K, int32_t N, const int8_t* w, int8_t* w_t,
  *   N          output channels, a multiple of 4 in [4, 2^20].
  *   codes      from stage 1; perm, group_off ([n_t][65]) from stage 2.
  *              Channel k of FPoT group g of tile τ is multiplied at step
- *              2^(15-g) * base.
+ *              2^(15-g) * base.  codes may be NULL when acodes and hcodes
+ *              are given and the MFMA kernel runs (below); a call that needs
+ *              the per-group kernel (acc_dbg, no w_t, or a shape the MFMA
+ *              kernels do not take) without codes returns DSTAR_ENULL.
  *   acodes     NULL, or stage 1's aligned codes.
  *   hcodes     NULL, or stage 1's digit planes (given with acodes).
  *   w          [K][N] int8 row-major, 16-byte aligned; any int8 value
@@ -222,8 +228,10 @@ int dstar_fmdq_pack_weights(int32_t K, int32_t N, const int8_t* w, int8_t* w_t,
  * digits x w) + 2^15 * (d2 digits x w), the digit terms over the channels
  * with PoT >= 7 (resp. >= 14) of each token tile, which are prefixes of the
  * FPoT groups in perm; a token tile whose int32 accumulator it cannot prove
- * exact (128 * Σ_k 2^PoT_k >= 2^31; |W| <= 128) is finished by a per-group path over perm
- * and group_off.  Otherwise the per-group kernel runs. */
+ * exact (128 * Σ_k 2^PoT_k >= 2^31; |W| <= 128) is finished by an exact int64
+ * path that rebuilds each channel's aligned value d0 + 2^7*d1 + 2^15*d2 from
+ * acodes and hcodes, walking perm bin by bin (the bin fixes the PoT and so
+ * which digits exist).  Otherwise the per-group kernel runs. */
 int dstar_fmdq_linear(const dstar_fmdq_params* p, int32_t N,
                       const int8_t* codes, const uint16_t* perm,
                       const int32_t* group_off, const int8_t* acodes,

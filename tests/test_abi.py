@@ -116,6 +116,11 @@ def test_null_and_alignment_errors(lib):
     assert _q(lib, p, acodes=FAKE, hcodes=FAKE + 8) == lib.EALIGN
     assert _q(lib, p, acodes=FAKE) == lib.ENULL          # the digit planes come with acodes
     assert _q(lib, p, hcodes=FAKE) == lib.ENULL
+    # the plain codes may be left out only when the aligned codes are written
+    assert _q(lib, p, codes=None) == lib.ENULL
+    assert _q(lib, p, codes=None, acodes=FAKE + 4, hcodes=FAKE) == lib.EALIGN   # past the NULL check
+    assert _l(lib, p, codes=None) == lib.ENULL
+    assert _l(lib, p, codes=None, acodes=FAKE, hcodes=FAKE, w_t=FAKE + 4) == lib.EALIGN
     assert _l(lib, p, acodes=FAKE + 8, hcodes=FAKE, w_t=FAKE) == lib.EALIGN
     assert _l(lib, p, acodes=FAKE, hcodes=FAKE + 4, w_t=FAKE) == lib.EALIGN
     assert _l(lib, p, acodes=FAKE, hcodes=FAKE, w_t=FAKE + 4) == lib.EALIGN

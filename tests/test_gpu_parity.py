@@ -36,7 +36,8 @@ def dm():
     return dm
 
 
-def gpu_layer(dm, d, dbg=None, inplace=False, y_prev_np=None, dynamic=False, sdump=None):
+def gpu_layer(dm, d, dbg=None, inplace=False, y_prev_np=None, dynamic=False, sdump=None,
+              plain_codes=True):
     """Runs the three stages on cuda:0; every output buffer starts as garbage.
 
     Stage 3 runs twice from the same codes: once as the product path (no
@@ -46,7 +47,9 @@ def gpu_layer(dm, d, dbg=None, inplace=False, y_prev_np=None, dynamic=False, sdu
     the group accumulators dumped (the per-group kernel) -> "y_dbg" and
     "acc".  With ``dynamic`` the base is found on the device first
     (dynamic_base -> "base") and stages 1 and 3 read it from there
-    (quantize_dyn, linear_dyn)."""
+    (quantize_dyn, linear_dyn).  With ``plain_codes=False`` stages 1 and 3
+    get no plain-codes buffer (stage 1 writes only tags, aligned codes and
+    digit planes)."""
     import torch
     dev = torch.device("cuda:0")
     rows, K, N, T = d["rows"], d["K"], d["N"], d["token_tile"]
@@ -58,7 +61,7 @@ def gpu_layer(dm, d, dbg=None, inplace=False, y_prev_np=None, dynamic=False, sdu
     y_np = d["y_prev"] if y_prev_np is None else y_prev_np
     y0 = torch.from_numpy(y_np).to(dev)
     p = dm.make_params(rows, K, T, float(d["base"]), d["k0"], d["tokens_per_seq"])
-    codes = torch.full((nt, K, T), 90, dtype=torch.int8, device=dev)
+    codes = torch.full((nt, K, T), 90, dtype=torch.int8, device=dev) if plain_codes else None
     tags = torch.full((nt, K), 0xEE, dtype=torch.uint8, device=dev)
     acodes = torch.full((nt * T, K), 77, dtype=torch.int8, device=dev)
     hcodes = torch.full((2, nt, K, T), 66, dtype=torch.int8, device=dev)
@@ -101,7 +104,7 @@ def gpu_layer(dm, d, dbg=None, inplace=False, y_prev_np=None, dynamic=False, sdu
             dm.linear(p, N, codes, perm, off, acodes, hcodes, w, w_t, ws, y0b, y2, acc, lo, hi)
         out.update(acc=acc, y_dbg=y2)
     torch.cuda.synchronize()
-    out = {k: v.cpu().numpy() for k, v in out.items()}
+    out = {k: v.cpu().numpy() for k, v in out.items() if v is not None}
     out["perm"] = out["perm"].view(np.uint16)
     return out
 
@@ -624,6 +627,62 @@ def test_ping_pong_kernel_matches_oracle(dm, case):
     log(f"  done {time.time() - t0:.1f}s")
 
 
+# Stage 1 without the plain codes and stage 3 on the MFMA kernels: tiles that
+# the kernels finish with the exact int64 path (every sub-channel heavy, or a
+# tile at the bound), T of 16, 32 and 64, third digits, both kernels.
+NO_PLAIN = [
+    dict(rows=64, K=8192, N=72, T=32, seed=20, heavy=1.0, c_range=(4.0, 8.0)),
+    dict(rows=128, K=8192, N=64, T=64, seed=22, heavy=1.0, c_range=(4.0, 8.0)),
+    dict(rows=64, K=8192, N=72, T=16, seed=38, heavy=1.0, c_range=(4.0, 8.0)),
+    dict(rows=200, K=1152, N=260, T=16, seed=36, heavy=0.3, c_range=(0.02, 4000.0)),
+    dict(rows=300, K=1040, N=264, T=32, seed=28, heavy=0.2, c_range=(0.02, 4000.0)),
+    dict(rows=2048, K=4096, N=4096, T=32, seed=94, heavy=0.05, c_range=(0.5, 64.0), wide_tiles=(5, 40)),
+]
+
+
+@pytest.mark.parametrize("case", NO_PLAIN, ids=lambda c: f"{c['rows']}x{c['K']}x{c['N']}-T{c['T']}-s{c['seed']}")
+def test_product_path_without_plain_codes(dm, case):
+    """No plain-codes buffer anywhere: tags, aligned codes, digit planes,
+    histogram and bucket bit-exact; S of every tile and Y_t of every output
+    bit for bit against the oracle."""
+    c = dict(case)
+    wide = c.pop("wide_tiles", ())
+    d = wl.make_custom(c.pop("rows"), c.pop("K"), c.pop("N"), c.pop("T"), seed=c.pop("seed"), **c)
+    rows, T = d["rows"], d["token_tile"]
+    nt = (rows + T - 1) // T
+    for tau in wide:
+        x = d["x_prev"][tau * T:(tau + 1) * T, :1024].astype(np.float64)
+        d["x_t"][tau * T:(tau + 1) * T, :1024] = (x - float(d["base"]) * 2.0 ** 14).astype(np.float32)
+    log(f"case {d['name']} without plain codes, tiles at the bound: {list(wide)}")
+    g = gpu_layer(dm, d, sdump=(0, nt), plain_codes=False)
+    assert "codes" not in g
+    codes, tags, hist = fmdq.quantize(d["x_t"], d["x_prev"], T, d["base"], d["k0"])
+    perm, off = fmdq.bucket(tags)
+    np.testing.assert_array_equal(g["tags"], tags, err_msg=f"{d['name']}: tags")
+    digits.check_operands(g["acodes"], g["hcodes"], codes, tags, d["name"])
+    np.testing.assert_array_equal(g["hist"].astype(np.int64), hist, err_msg=f"{d['name']}: bit histogram")
+    np.testing.assert_array_equal(g["perm"], perm, err_msg=f"{d['name']}: bucket order")
+    np.testing.assert_array_equal(g["group_off"], off, err_msg=f"{d['name']}: group offsets")
+    y, s_all = par_linear_s(codes, tags, perm, off, d["w"], d["w_scale"], d["y_prev"], d["base"], T)
+    np.testing.assert_array_equal(g["s"], s_all, err_msg=f"{d['name']}: S (product kernel)")
+    check_y(g["y"], y, d["y_prev"], d["name"])
+
+
+def test_per_group_kernel_needs_plain_codes(dm):
+    """Asking for the group accumulators (the per-group kernel) without the
+    plain codes is an error, not a silent fallback."""
+    import torch
+    dev = torch.device("cuda:0")
+    d = wl.make_custom(64, 64, 32, 32, seed=3)
+    p = dm.make_params(64, 64, 32, float(d["base"]), d["k0"])
+    z = lambda *shape, dt=torch.int8: torch.zeros(shape, dtype=dt, device=dev)
+    acc = z(1, 16, 32, 32, dt=torch.int32)
+    y = torch.zeros((64, 32), dtype=torch.float32, device=dev)
+    with pytest.raises(RuntimeError, match="codes"):
+        dm.linear(p, 32, None, z(2, 64, dt=torch.int16), z(2, 65, dt=torch.int32), z(64, 64), z(2, 2, 64, 32),
+                  z(64, 32), z(32, 64), torch.ones(32, device=dev), y, y, acc, 0, 1)
+
+
 CHAIN = [(1, "fc1"), (1, "fc2"), (4, "fc1"), (4, "fc2")]
 
 
@@ -641,8 +700,11 @@ def test_full_size_chain_in_place(dm, cfg, layer):
     rows, T = d["rows"], d["token_tile"]
     log(f"case chain config {cfg} {layer}: rows={rows} K={d['K']} N={d['N']} pairs 1-3 "
         f"(inputs {time.time() - t0:.1f}s)")
+    # the timed step's configuration: no plain codes (the MFMA kernels read
+    # the aligned codes and digit planes only)
     lay = dm.FmdqLayer(torch.from_numpy(d["w"]).to(dev), torch.from_numpy(d["w_scale"]).to(dev), rows, T,
-                       float(d["base"]), d["k0"], d["tokens_per_seq"])
+                       float(d["base"]), d["k0"], d["tokens_per_seq"], plain_codes=False)
+    assert lay.codes is None
     y = torch.from_numpy(d["y_prev"]).to(dev)
     y_orc = d["y_prev"]
     for pair in (1, 2, 3):
