@@ -212,6 +212,10 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   constexpr int kTPB = T < 32 ? 32 / T : 1;
   constexpr int kSched = 2 * RB * kTPB;             // schedule entries (8 or 16)
   constexpr int kGo = (kTiles * (kBins + 1) + kThreads - 1) / kThreads;   // offset loads per thread
+  // Workgroups whose second-digit lists are long (text-like tiles where most
+  // channels have PoT ≥ 7) run those digits as a masked dense pass instead of
+  // gathered units; written for 32-row tiles and N a multiple of 16.
+  constexpr bool kDense1 = T == 32 && VecW;
   // Direct-to-LDS loads per wave per gathered unit: two dword loads of digit
   // codes, and the W rows as four 16-byte or sixteen 4-byte loads.
   constexpr int kOpsUnit = VecW ? 6 : 18;
@@ -374,6 +378,18 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     const int ti = T < 32 ? rb * kTPB + e % kTPB : (32 * rb) / T;
     int v = 0;
     if (x < kSched && eligible[ti]) v = (pre[lvl * kTiles * 17 + ti * 17 + 16] + KU - 1) / KU;
+    if constexpr (kDense1) {
+      // More second-digit units than dense chunks: a dense pass over all K
+      // channels (masked to the sub-channels with PoT ≥ 7) does less work, so
+      // the second-digit lists leave the schedule (K ≤ 8192: the mask's
+      // bitmap fits the id region).
+      int u1 = lvl == 0 ? v : 0;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) u1 += __shfl_xor(u1, o, 64);
+      const bool d1 = u1 > nchunks && K <= 8192;
+      if (d1 && lvl == 0) v = 0;
+      if (lane == 0) ustart[19] = d1 ? 1 : 0;
+    }
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) {
       const int n = __shfl_up(v, o, 64);
@@ -446,6 +462,124 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   // so that the loop's first two waits can count them).
   fetch(0);
   __asm__ __volatile__("" ::: "memory");
+
+  // ---- Masked dense pass over the second digits (workgroups chosen above).
+  // Horner order of the shift alignment: acc = Σ_k d1·W over the sub-channels
+  // with PoT ≥ 7, then acc ·= 2^7, the dense loop below adds Σ_k d0·W, and
+  // the gathered third digits are added ·2^15.  First a bitmap of those
+  // sub-channels is built in the id region (one bit per (tile, channel),
+  // K ≤ 8192; the region is free until the ids are committed) from the
+  // second-digit prefixes of the FPoT groups, read from the tiles' perm rows
+  // staged in the ring.  Then chunks of 64 channels flow through the ring as
+  // in the dense loop: A = each tile's [64 channels][32 rows] block of digit
+  // plane 0 (wave w loads tile w's), a sub-channel's 32 bytes loaded only if
+  // its bit is set (that plane is unwritten elsewhere); B = the chunk of W^T.
+  const bool dense1 = kDense1 && ustart[19] != 0;
+  if constexpr (kDense1) {
+    if (dense1) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the first dense chunks and the ids
+      bar_lds();                              // every wave past the meta phase
+      const int kw = (int)((K + 31) / 32);    // bitmap words per tile
+      uint32_t* bm = reinterpret_cast<uint32_t*>(smem + kOffEnt);   // [kTiles][kw]
+      const uint16_t* pst = reinterpret_cast<const uint16_t*>(smem);   // [tiles][K] staged perm
+      for (int q = tid; q < kTiles * kw; q += kThreads) bm[q] = 0u;
+      const int pbytes = (int)(kTiles * K * 2);
+      for (int b0 = 0; b0 < pbytes; b0 += kThreads * 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_perm, (lds_ptr)(smem + b0 + 1024 * wave), 16,
+                                                 (uint32_t)(b0 + 16 * tid), 0, 0, 0);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      bar_lds();
+      for (int i = 0; i < tiles_here; ++i) {
+        if (!eligible[i]) continue;
+        for (int g = 0; g < kTags; ++g) {
+          const int lo = rstart[i * kTags + g];
+          const int n = pre[i * 17 + g + 1] - pre[i * 17 + g];   // the group's PoT ≥ 7 prefix
+          for (int q = tid; q < n; q += kThreads) {
+            const uint32_t k = pst[i * K + lo + q];
+            atomicOr(&bm[i * kw + (int)(k >> 5)], 1u << (k & 31u));
+          }
+        }
+      }
+      bar_lds();
+      const rsrc_t r_d1 = make_rsrc(a.hcodes + tile0 * K * T, (uint32_t)(tiles_here * K * T));
+      const uint32_t* bmw = bm + wave * kw;
+      auto issue1 = [&](int64_t c, int st) __attribute__((always_inline)) {
+        const int64_t k0 = c * BK;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int64_t k = k0 + 32 * j + (lane >> 1);   // lane pair → one sub-channel's 32 bytes
+          const bool in = c < nchunks && k < K;
+          const bool ok = in && ((bmw[in ? (int)(k >> 5) : 0] >> (k & 31)) & 1u);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              r_d1, (lds_ptr)(stageA(st) + 2048 * wave + 1024 * j), 16,
+              ok ? (uint32_t)((wave * K + k) * T + 16 * (lane & 1)) : kOob, 0, 0, 0);
+        }
+        const bool live = c < nchunks && k0 + 16 * c16 < K;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t n = nw + 16 * j + r16;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r_wt, (lds_ptr)(stageB(st, wave) + 1024 * j), 16,
+                                                   live && n < N ? (uint32_t)(n * K + k0 + 16 * c16) : kOob, 0, 0,
+                                                   0);
+        }
+      };
+      struct Frags1 { v4i a[RB], b[CB]; };
+      auto read1 = [&](Frags1& f, int st, int ks) __attribute__((always_inline)) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const int row = 32 * cb + li, cc = 2 * ks + h;
+          f.b[cb] = *reinterpret_cast<const v4i*>(stageB(st, wave) + row * BK + 16 * (cc ^ ((row >> 2) & 3)));
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) f.a[rb] = tr_frag<32>(stageA(st) + 2048 * rb + KS * 32 * ks, 0, lane);
+      };
+      // the transpose reads are inline assembly: wait for them by hand
+      auto wait1 = [&](Frags1& f) __attribute__((always_inline)) {
+        __asm__ __volatile__("s_waitcnt lgkmcnt(0)" : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]));
+      };
+      auto mma1 = [&](const Frags1& f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            acc[rb][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[rb], f.b[cb], acc[rb][cb], 0, 0, 0);
+      };
+#pragma unroll
+      for (int c = 0; c < kStages; ++c) issue1(c, c);
+      __builtin_amdgcn_s_waitcnt(wait_vm(12));  // chunk 0
+      __asm__ __volatile__("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      __asm__ __volatile__("" ::: "memory");
+      Frags1 g0, g1;
+      read1(g0, 0, 0);
+      for (int64_t c = 0; c < nchunks; ++c) {
+        const int st = (int)(c % kStages);
+        const int st1 = (int)((c + 1) % kStages);
+        wait1(g0);
+        mma1(g0);
+        read1(g1, st, 1);
+        __builtin_amdgcn_s_waitcnt(kWaitVmChunk);   // chunk c + 1 (chunk c + 2 after it)
+        bar_lds();                                   // also completes g1's reads
+        issue1(c + kStages, st);
+        wait1(g1);
+        mma1(g1);
+        read1(g0, st1, 0);
+      }
+      wait1(g0);                                // the last (unused) reads
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);     // the chunks issued past K
+      bar_lds();                                // every wave done with the ring and the bitmap
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) shift_acc(acc[rb][cb], 7);
+      // The dense loop's first chunks again, then the ids again: the same
+      // loads in flight, in the same order, as its waits count.
+#pragma unroll
+      for (int c = 0; c < kStages; ++c) issue(c, c);
+      fetch(0);
+      __asm__ __volatile__("" ::: "memory");
+    }
+  }
 
   // ---- Dense loop.
   {
@@ -680,12 +814,14 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
         }
         step(tmp);
       }
-      // acc += (Σ d1·W + 2^8 Σ d2·W) · 2^7
+      // acc += (Σ d1·W + 2^8 Σ d2·W) · 2^7, or after the second-digit pass
+      // (tmp = Σ d2·W alone) acc += tmp · 2^15
+      const int sh = dense1 ? 15 : 7;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          acc[rb][cb][r] = (int)((uint32_t)acc[rb][cb][r] + ((uint32_t)tmp[cb][r] << 7));
+          acc[rb][cb][r] = (int)((uint32_t)acc[rb][cb][r] + ((uint32_t)tmp[cb][r] << sh));
     }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);   // the loads issued past the last unit
   }
