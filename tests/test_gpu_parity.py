@@ -344,6 +344,26 @@ def test_t16_block_with_one_ineligible_tile(dm):
     full_compare(dm, d)
 
 
+def test_second_digit_dense_pass(dm):
+    """A workgroup whose second-digit lists outnumber its dense chunks takes
+    the masked dense pass over the second digits (32-row tiles, N % 16 == 0,
+    K <= 8192): here with a ragged last tile, a partial last chunk
+    (K % 64 = 16), an ineligible tile (sixteen sub-channels at PoT 21) and
+    third digits in another; every integer stage, S and Y_t bit for bit."""
+    rows, K, N, T = 120, 1040, 64, 32
+    d = wl.make_custom(rows, K, N, T, seed=47, heavy=1.0, c_range=(4.0, 8.0))
+    base = float(d["base"])
+    x = d["x_prev"].astype(np.float64)
+    d["x_t"][32, :16] = (x[32, :16] + base * 2.0 ** 21).astype(np.float32)      # tile 1 ineligible
+    d["x_t"][70, 100:104] = (x[70, 100:104] - base * 2.0 ** 14.5).astype(np.float32)   # tile 2: PoT 15
+    delta = fmdq.differential(d["x_t"], d["x_prev"])
+    pot = fmdq.pot_exponent(fmdq.subchannel_max(delta, T), d["base"])
+    elig = [128 * np.sum(2.0 ** pot[t].astype(np.int64)) < 2 ** 31 for t in range(4)]
+    units = sum(int(np.ceil((pot[t] >= 7).sum() / 64)) for t in range(4) if elig[t])
+    assert elig == [True, False, True, True] and units > (K + 63) // 64 and (pot[2] >= 14).sum() == 4
+    full_compare(dm, d)
+
+
 def test_config0_full(dm):
     d = wl.make_inputs(0, "fc1", 1)
     t = time.time()
