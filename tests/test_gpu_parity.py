@@ -603,6 +603,55 @@ def test_random_shapes_match_oracle(dm, case):
     full_compare(dm, d)
 
 
+def _dense_digit_cases(n: int, seed: int) -> list:
+    """Seeded random shapes that send a workgroup through the dense
+    second-digit pass: 32-row tiles, N % 16 == 0, K a multiple of 16 up to
+    4096, at least three tiles per 128-row block, most sub-channels heavy
+    (about half at PoT >= 7), sometimes wide scales (third digits, tiles
+    above the int32 bound) and two sequences."""
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        K = int(16 * r.integers(1, 257))
+        N = int(16 * r.integers(1, 41))
+        two = r.random() < 0.25
+        tps = int(32 * r.integers(2, 7)) if two else int(r.integers(65, 520))
+        rows = 2 * tps if two else tps
+        heavy = float(r.choice([0.6, 1.0]))
+        c_range = [(4.0, 8.0), (2.0, 16.0), (3.0, 40.0), (0.02, 4000.0)][int(r.integers(0, 4))]
+        out.append(dict(rows=rows, K=K, N=N, T=32, seed=600 + i, heavy=heavy, c_range=c_range,
+                        tokens_per_seq=tps))
+    return out
+
+
+DENSE_DIGIT_CASES = _dense_digit_cases(24, 2027)
+
+
+def _dense_digit_workgroups(d) -> int:
+    """Workgroups (128-row blocks) that the two-workgroup kernel sends through
+    the dense second-digit pass: more second-digit units (64 channels with
+    PoT >= 7 of an eligible tile) than 64-channel chunks."""
+    T, K = d["token_tile"], d["K"]
+    pot = fmdq.pot_exponent(fmdq.subchannel_max(fmdq.differential(d["x_t"], d["x_prev"]), T), d["base"])
+    nt = pot.shape[0]
+    elig = [128 * np.sum(2.0 ** pot[t].astype(np.int64)) < 2 ** 31 for t in range(nt)]
+    units = [int(np.ceil((pot[t] >= 7).sum() / 64)) if elig[t] else 0 for t in range(nt)]
+    return sum(1 for w in range(0, nt, 4) if sum(units[w:w + 4]) > (K + 63) // 64)
+
+
+@pytest.mark.parametrize("case", DENSE_DIGIT_CASES,
+                         ids=lambda c: f"{c['rows']}x{c['K']}x{c['N']}-s{c['seed']}")
+def test_dense_digit_shapes_match_oracle(dm, case):
+    """Random shapes where some workgroup takes the dense second-digit pass:
+    every stage bit for bit against the oracle."""
+    c = dict(case)
+    d = wl.make_custom(c.pop("rows"), c.pop("K"), c.pop("N"), c.pop("T"), seed=c.pop("seed"), **c)
+    n = _dense_digit_workgroups(d)
+    log(f"  {n} workgroup(s) through the dense second-digit pass")
+    assert n > 0
+    full_compare(dm, d)
+
+
 PP_CASES = [
     dict(rows=2041, K=4096, N=4096, T=32, seed=91, heavy=0.2, c_range=(0.5, 64.0)),      # ragged last tile
     dict(rows=2048, K=4096, N=4100, T=32, seed=92, heavy=0.3, c_range=(0.02, 4000.0)),   # N % 16 != 0, d2
