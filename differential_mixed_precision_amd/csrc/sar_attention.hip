@@ -13,7 +13,8 @@
 //           sweeps over the kept key blocks of its query block (row maximum of
 //           the logits, sum of the fixed-point exponentials, then P and its
 //           FMDQ-INT8 codes), each recomputing the exact integer scores; the
-//           next block's K fragments are loaded while one is computed.
+//           next block's K fragments are loaded while one is computed.  Waves
+//           take the query blocks with the most kept key blocks first.
 //   pv      cached and reused steps: one wave per (image·head, token tile),
 //           one int32 MFMA accumulator per (column tile, digit plane) over all
 //           kept keys, combined in int64 at the end.
@@ -59,29 +60,43 @@ constexpr int kWaves = kThreads / 64;
 
 // exp32 constants, float32 (hex literals so that both implementations start
 // from the same bits): log2(e); ln 2 = LN2_HI + LN2_LO with LN2_HI = 355/512,
-// whose product with the small integer n is exact; Taylor coefficients of e^r
-// from 1/7! down to 1.
+// whose product with a small integer n is exact; Taylor coefficients of e^r
+// from 1/7! down to 1, here times 2^36 (the fixed-point scale of E): a
+// power-of-two factor on every coefficient scales every Horner step by it
+// exactly, so p·2^36 comes out of the polynomial with the same bits.
 constexpr float kLog2e = 0x1.715476p+0f;
 constexpr float kLn2Hi = 0x1.63p-1f;
 constexpr float kLn2Lo = -0x1.bd0106p-13f;
+constexpr float kExpScale = (float)(1ull << DSTAR_SAR_EXP_FRAC);
+static_assert(DSTAR_SAR_EXP_FRAC == 36, "coefficient scale");
+constexpr float kXMin = -26.0f;       // exp32 cut-off: E = 0 below it
+constexpr float kXSafe = 16384.0f;    // |x| below which no clamp is needed
 
-// exp32 without its final power of two: e^x = p·2^n (Cody–Waite reduction,
-// then the Taylor polynomial of e^r by Horner's rule, one fused multiply-add
-// per step, each rounded once to float32).  x − n·ln2_hi is exact (n·ln2_hi
-// is exact and close to x).  Branch-free; see exp_fixed_d for the cut-off.
-__device__ __forceinline__ float exp32_poly(float x, int& n_out) {
+// E = rint(exp32(x)·2^36) as a float (an exact integer ≤ 2^36), x ≤ 0.
+// exp32: Cody–Waite reduction n = rint(x·log2 e), r = (x − n·LN2_HI) −
+// n·LN2_LO, then the degree-7 Taylor polynomial of e^r by Horner's rule, one
+// fused multiply-add per step, each rounded once to float32; e = p·2^n.
+// x − n·LN2_HI is one fused multiply-add: while |n| < 2^15 the product
+// n·LN2_HI is exact, so it rounds the same value as a product followed by
+// a difference.  The cut-off needs no clamp for −kXSafe ≤ x < −26: there
+// n ≤ −38, p·2^(n+36) ≤ 1.42/4 and rint gives 0, as below the cut-off.
+// Farther out the reduction loses the leading bits of x and the polynomial
+// can overflow, so kClamp raises x to −26 first (E(−26) = 0).
+template <bool kClamp>
+__device__ __forceinline__ float exp_fixed(float x) {
+  if constexpr (kClamp) x = fmaxf(x, kXMin);
   const float n = rintf(__fmul_rn(x, kLog2e));
-  const float r = __builtin_fmaf(-n, kLn2Lo, __fsub_rn(x, __fmul_rn(n, kLn2Hi)));
-  float p = 0x1.a01a02p-13f;                       // 1/5040
-  p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);       // 1/720
-  p = __builtin_fmaf(p, r, 0x1.111112p-7f);        // 1/120
-  p = __builtin_fmaf(p, r, 0x1.555556p-5f);        // 1/24
-  p = __builtin_fmaf(p, r, 0x1.555556p-3f);        // 1/6
-  p = __builtin_fmaf(p, r, 0.5f);
-  p = __builtin_fmaf(p, r, 1.0f);
-  p = __builtin_fmaf(p, r, 1.0f);
-  n_out = (int)n;
-  return p;
+  float r = __builtin_fmaf(-n, kLn2Hi, x);
+  r = __builtin_fmaf(-n, kLn2Lo, r);
+  float p = 0x1.a01a02p-13f * kExpScale;                 // 1/5040
+  p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f * kExpScale);  // 1/720
+  p = __builtin_fmaf(p, r, 0x1.111112p-7f * kExpScale);   // 1/120
+  p = __builtin_fmaf(p, r, 0x1.555556p-5f * kExpScale);   // 1/24
+  p = __builtin_fmaf(p, r, 0x1.555556p-3f * kExpScale);   // 1/6
+  p = __builtin_fmaf(p, r, 0.5f * kExpScale);
+  p = __builtin_fmaf(p, r, kExpScale);
+  p = __builtin_fmaf(p, r, kExpScale);
+  return rintf(ldexpf(p, (int)n));
 }
 
 // PoT: the number of bin edges base·2^j (j = 0..20) strictly below m, i.e.
@@ -114,6 +129,32 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+// Sum of v over the lanes below this one.
+__device__ __forceinline__ int wave_excl_sum_i(int v) {
+  const int lane = threadIdx.x & 63;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  return incl - v;
 }
 __device__ __forceinline__ int wave_max_i(int v) {
 #pragma unroll
@@ -289,12 +330,96 @@ struct ScoreArgs {
   uint8_t* ppot;
   double g;          // (base_q·2^-6)·sm_scale
   float base_p, inv_base_p;
+  int32_t clip_p;    // base_p·2^21 < 1: P codes can exceed 64 and are clipped
 };
 
 // Kept-block range of a query block, clamped to [0, nnz].
 __device__ __forceinline__ void block_range(const int32_t* row_ptr, int64_t r, int32_t nnz, int& j0, int& j1) {
   j0 = min(max(row_ptr[r], 0), nnz);
   j1 = min(max(row_ptr[r + 1], j0), nnz);
+}
+
+constexpr int kOrderPerLane = 16;                  // counts a lane holds
+constexpr int kOrderMax = 64 * kOrderPerLane;      // (head, query block) pairs
+
+// The (head, query block) pair at position `rank` when all U pairs are taken
+// in descending order of their kept-block counts, ties in index order; the
+// result is wave-uniform.  Lane l holds the counts of pairs 16·l .. 16·l+15
+// (−1 past U).  The count c at that position is the largest c with at least
+// rank + 1 pairs counting c or more (a binary search over c); the pair is
+// then the k-th pair counting exactly c, k = rank − #(counts above c).
+// U ≤ kOrderMax.
+__device__ int pair_by_rank(const int32_t* row_ptr, int32_t nnz, int U, int rank) {
+  const int lane = threadIdx.x & 63;
+  const int u0 = lane * kOrderPerLane;
+  int rp[kOrderPerLane + 1];
+#pragma unroll
+  for (int i = 0; i <= kOrderPerLane; ++i) rp[i] = row_ptr[min(u0 + i, U)];   // all in flight at once
+  int cnt[kOrderPerLane];
+  int cmax = 0;
+#pragma unroll
+  for (int i = 0; i < kOrderPerLane; ++i) {
+    const int j0 = min(max(rp[i], 0), nnz);
+    const int j1 = min(max(rp[i + 1], j0), nnz);
+    cnt[i] = u0 + i < U ? j1 - j0 : -1;
+    cmax = max(cmax, cnt[i]);
+  }
+  cmax = __builtin_amdgcn_readfirstlane(wave_max_i(cmax));
+  auto count_at_least = [&](int c) {
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < kOrderPerLane; ++i) n += cnt[i] >= c ? 1 : 0;
+    return __builtin_amdgcn_readfirstlane(wave_sum_i(n));
+  };
+  int lo = 0, hi = cmax;          // count_at_least(lo) = U > rank
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (count_at_least(mid) > rank) lo = mid;
+    else hi = mid - 1;
+  }
+  int k = rank - (lo < cmax ? count_at_least(lo + 1) : 0);
+  int m = 0;
+#pragma unroll
+  for (int i = 0; i < kOrderPerLane; ++i) m += cnt[i] == lo ? 1 : 0;
+  const int before = wave_excl_sum_i(m);
+  int pick = 0x7FFFFFFF;
+  if (before <= k && k < before + m) {
+    int t = k - before;
+#pragma unroll
+    for (int i = 0; i < kOrderPerLane; ++i) {
+      if (cnt[i] == lo) {
+        if (t == 0) pick = u0 + i;
+        --t;
+      }
+    }
+  }
+  return __builtin_amdgcn_readfirstlane(min(wave_min_i(pick), U - 1));
+}
+
+// The tile of wave g of the scores kernel: g / (2·batch) is the rank of its
+// (head, query block) pair in the order above, so waves with the most kept
+// blocks start first and the shortest fill in at the end (longest processing
+// time first; the grid runs two waves per SIMD over several rounds);
+// g % (2·batch) picks the image and which of the block's two token tiles.
+// Pairs beyond kOrderMax keep index order.
+struct TileWork {
+  int64_t bh;
+  int tau, b, h, qb, half;
+};
+__device__ __forceinline__ TileWork tile_work(const Dims& m, const int32_t* row_ptr, int32_t nnz, int B,
+                                              int64_t g) {
+  const int U = m.heads * m.nb;
+  const int per = 2 * B;
+  const int rank = (int)(g / per), sub = (int)(g % per);
+  const int pair = U <= kOrderMax ? pair_by_rank(row_ptr, nnz, U, rank) : rank;
+  TileWork w;
+  w.h = pair / m.nb;
+  w.qb = pair % m.nb;
+  w.b = sub >> 1;
+  w.half = sub & 1;
+  w.bh = (int64_t)w.b * m.heads + w.h;
+  w.tau = 2 * w.qb + w.half;
+  return w;
 }
 
 // Digit planes 0..NP-1 of 16 values a_i = code_i·2^pot_i (codes: signed
@@ -378,19 +503,6 @@ __device__ __forceinline__ void tile_logits(const v4i (&A)[NKS][NP], const v4i (
   }
 }
 
-// E = rint(exp32(x)·2^36) as a double, x ≤ 0.  For x ≥ −26 (the cut-off),
-// exp32(x) = p·2^n is a normal float (n ≥ −38), so e·2^36 = p·2^(n+36) is
-// formed exactly in float32 (at most 2^36, as e ≤ 1) and its float32 rint is
-// the integer E.  Below the cut-off exp32 is 0, and so is this: e^x·2^36 <
-// 0.36 there, p·2^(n+36) is that within a few ulps (or flushes to 0 for very
-// negative x), and rint gives 0; no clamp or select is needed.  E ≤ 2^36, so
-// sums of up to 2^16 of them stay exact in float64.
-__device__ __forceinline__ double exp_fixed_d(float x) {
-  int n;
-  const float p = exp32_poly(x, n);
-  return (double)rintf(ldexpf(p, n + DSTAR_SAR_EXP_FRAC));
-}
-
 __device__ __forceinline__ double half_sum_d(double v) {
 #pragma unroll
   for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -447,33 +559,35 @@ __device__ __forceinline__ void sweep_blocks(const ScoreArgs& a, int64_t bh, int
   }
 }
 
-// The three sweeps of one 32-row query tile (a wave) with NP digit planes of
-// a_Q: row maxima of the logits, exact sums of the fixed-point exponentials,
-// then P, its FMDQ-INT8 codes per (tile, key) sub-channel and the cache.
-template <int NKS, int NP>
-__device__ __forceinline__ void scores_tile(const ScoreArgs& a, int64_t bh, int tau, int b, int half, int j0, int j1,
-                                            const v4i (&cw)[NKS], const v4i (&pw)[NKS]) {
+// The low byte of rint(r) for r in [0, 2^22]: r + 2^23 rounds to the integer
+// nearest r (ties to even) in the low mantissa bits, and a byte store keeps
+// those bits.
+__device__ __forceinline__ int8_t rint_byte(float r) {
+  return (int8_t)__float_as_uint(__fadd_rn(r, 0x1p23f));
+}
+
+// Sweeps 2 and 3 of one 32-row query tile, given the row maxima of the
+// logits: exact sums of the fixed-point exponentials E (ΣE ≥ 2^36, as the
+// row maximum gives E = 2^36), then P = fl32(f64(E)·(1/f64(ΣE))) in [0, 1],
+// its FMDQ-INT8 codes per (tile, key) sub-channel and the cache.  kClamp
+// selects the exponential with the cut-off clamp (logit spreads beyond
+// kXSafe).  Codes: q = rint(fl32(fl32(P·inv_base)·2^(6−PoT))), clipped to
+// 64.  The power of two is folded into inv_base once per column; that product
+// is exact for bases in [2^-100, 2^100], and fl32(P·(inv_base·2^(6−PoT))) is
+// then the same float while both forms are normal (otherwise both are below
+// 2^-126 and give 0).  P ≥ 0 gives q ≥ 0, and P ≤ max P ≤ base·2^PoT keeps q
+// ≤ 64 unless the PoT saturates, which needs base·2^21 < 1 (P ≤ 1): only
+// then is the clip applied (a.clip_p).
+template <int NKS, int NP, bool kClamp>
+__device__ __forceinline__ void scores_sweeps23(const ScoreArgs& a, int64_t bh, int b, int half, int j0, int j1,
+                                                const v4i (&A)[NKS][NP], const float (&mrow)[16]) {
   const int lane = threadIdx.x & 63, li = lane & 31, hi = lane >> 5;
-  v4i A[NKS][NP];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) digits_np<NP>(cw[ks], pw[ks], A[ks]);
-
-  float mrow[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) mrow[r] = -INFINITY;
-  sweep_blocks<NKS, NP>(a, bh, j0, j1, A, [&](int, int, const float (&z)[16]) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mrow[r] = fmaxf(mrow[r], z[r]);
-  });
-#pragma unroll
-  for (int r = 0; r < 16; ++r) mrow[r] = half_max(mrow[r]);
-
   double inv[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) inv[r] = 0.0;
   sweep_blocks<NKS, NP>(a, bh, j0, j1, A, [&](int, int, const float (&z)[16]) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) inv[r] += exp_fixed_d(__fsub_rn(z[r], mrow[r]));
+    for (int r = 0; r < 16; ++r) inv[r] += (double)exp_fixed<kClamp>(__fsub_rn(z[r], mrow[r]));
   });
 #pragma unroll
   for (int r = 0; r < 16; ++r) inv[r] = 1.0 / half_sum_d(inv[r]);
@@ -484,17 +598,62 @@ __device__ __forceinline__ void scores_tile(const ScoreArgs& a, int64_t bh, int 
     float mx = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      P[r] = (float)(exp_fixed_d(__fsub_rn(z[r], mrow[r])) * inv[r]);
+      P[r] = (float)((double)exp_fixed<kClamp>(__fsub_rn(z[r], mrow[r])) * inv[r]);
       mx = fmaxf(mx, P[r]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));    // the other 16 rows of the column
     const int pot = pot_of(mx, a.base_p);
+    const float ib = ldexpf(a.inv_base_p, kP8 - pot);
     int8_t* dst = a.pc + (blk * kBlock + 32 * half) * kBlock + 32 * ct + li;
+    if (a.clip_p) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      dst[(8 * (r >> 2) + 4 * hi + (r & 3)) * kBlock] = (int8_t)code8(P[r], a.inv_base_p, pot);
+      for (int r = 0; r < 16; ++r)
+        dst[(8 * (r >> 2) + 4 * hi + (r & 3)) * kBlock] = rint_byte(fminf(__fmul_rn(P[r], ib), 64.0f));
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        dst[(8 * (r >> 2) + 4 * hi + (r & 3)) * kBlock] = rint_byte(__fmul_rn(P[r], ib));
+    }
     if (hi == 0) a.ppot[(blk * 2 + half) * kBlock + 32 * ct + li] = (uint8_t)pot;
   });
+}
+
+// The three sweeps of one 32-row query tile (a wave) with NP digit planes of
+// a_Q: row maxima of the logits (and the wave's smallest logit), then sweeps
+// 2 and 3.  Exponent arguments x = z − max z stay within [−kXSafe, 0] when
+// the wave's logits span at most kXSafe, and then need no clamp.
+template <int NKS, int NP>
+__device__ __forceinline__ void scores_tile(const ScoreArgs& a, int64_t bh, int b, int half, int j0, int j1,
+                                            const v4i (&cw)[NKS], const v4i (&pw)[NKS]) {
+  v4i A[NKS][NP];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) digits_np<NP>(cw[ks], pw[ks], A[ks]);
+
+  float mrow[16];
+  float zlo = INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mrow[r] = -INFINITY;
+  sweep_blocks<NKS, NP>(a, bh, j0, j1, A, [&](int, int, const float (&z)[16]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      mrow[r] = fmaxf(mrow[r], z[r]);
+      zlo = fminf(zlo, z[r]);
+    }
+  });
+  float mhi = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    mrow[r] = half_max(mrow[r]);
+    mhi = fmaxf(mhi, mrow[r]);
+  }
+  mhi = wave_max(mhi);
+  zlo = wave_min(zlo);
+  // wave-uniform: a scalar branch, not two masked bodies
+  const int wide = __builtin_amdgcn_readfirstlane(mhi - zlo <= kXSafe ? 0 : 1);
+  if (wide)
+    scores_sweeps23<NKS, NP, true>(a, bh, b, half, j0, j1, A, mrow);
+  else
+    scores_sweeps23<NKS, NP, false>(a, bh, b, half, j0, j1, A, mrow);
 }
 
 // One wave per (image·head, 32-row token tile); NKS = dp/32 k-steps.  Two
@@ -509,12 +668,11 @@ __global__ __launch_bounds__(kThreads, 2) void scores_kernel(ScoreArgs a) {
   // scalar loads, which the vector-load counts do not include
   const int64_t tile = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWaves + (threadIdx.x >> 6)));
   if (tile >= a.m.BH * tpb) return;
-  const int64_t bh = tile / tpb;
-  const int tau = (int)(tile % tpb);
-  const int b = (int)(bh / a.m.heads), h = (int)(bh % a.m.heads);
-  const int qb = tau >> 1, half = tau & 1;
+  const TileWork w = tile_work(a.m, a.row_ptr, a.nnz, a.B, tile);
+  const int64_t bh = w.bh;
+  const int tau = w.tau, b = w.b, half = w.half;
   int j0, j1;
-  block_range(a.row_ptr, (int64_t)h * a.m.nb + qb, a.nnz, j0, j1);
+  block_range(a.row_ptr, (int64_t)w.h * a.m.nb + w.qb, a.nnz, j0, j1);
   if (j0 >= j1) return;
 
   v4i cw[NKS], pw[NKS];
@@ -530,9 +688,9 @@ __global__ __launch_bounds__(kThreads, 2) void scores_kernel(ScoreArgs a) {
     }
   }
   if (planes_for(wave_max_i(pmax)) <= 2)
-    scores_tile<NKS, 2>(a, bh, tau, b, half, j0, j1, cw, pw);
+    scores_tile<NKS, 2>(a, bh, b, half, j0, j1, cw, pw);
   else
-    scores_tile<NKS, kPlanes>(a, bh, tau, b, half, j0, j1, cw, pw);
+    scores_tile<NKS, kPlanes>(a, bh, b, half, j0, j1, cw, pw);
 }
 
 // ---------------------------------------------------------------- P·V
@@ -649,6 +807,8 @@ __global__ __launch_bounds__(kThreads, 2) void pv_kernel(PvArgs a) {
   const int tpb = a.m.L / kTile;
   // wave-uniform (readfirstlane): the index and mask loads below become
   // scalar loads, which the vector-load counts do not include
+  // index order: a pv wave is short enough (about a third of a scores wave)
+  // that the longest-first lookup costs more than it evens out
   const int64_t tile = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kWaves + (threadIdx.x >> 6)));
   if (tile >= a.m.BH * tpb) return;
   const int64_t bh = tile / tpb;
@@ -795,6 +955,7 @@ int dstar_sar_scores(const dstar_sar_params* p, const int32_t* row_ptr, const in
   a.g = ((double)p->base_q * 0x1p-6) * (double)p->sm_scale;
   a.base_p = p->base_p;
   a.inv_base_p = (float)(1.0 / (double)p->base_p);
+  a.clip_p = (double)p->base_p * 0x1p21 < 1.0 ? 1 : 0;
   if (nnz == 0) return DSTAR_OK;
   const dim3 grid(waves_grid(a.m.BH * (a.m.L / kTile)));
   const hipStream_t s = (hipStream_t)stream;

@@ -145,6 +145,60 @@ def test_sar_digit_plane_counts_match_oracle(dm, case):
     np.testing.assert_array_equal(g["o_reused"], u["o"])
 
 
+WIDE_CASES = [
+    # (key outlier factor, Q outlier factor, seed): whole key rows scaled by
+    # the factor spread a tile's logits far past 2^14, the range in which the
+    # exponential needs no clamp at its cut-off; at 1e14, z − max z reaches
+    # beyond 2^45, where the reduction of an unclamped argument loses its
+    # leading bits and the polynomial overflows
+    (2e4, 1.0, 21),
+    (1e14, 1.0, 22),
+    (1e14, 2000.0, 23),
+]
+
+
+def logit_spread(d, H):
+    """Largest max − min of q·k·sm_scale (float64) over the kept keys of any
+    32-row query tile."""
+    L = d["L"]
+    nb = L // 64
+    best = 0.0
+    for h in range(H):
+        z = d["q"][h].astype(np.float64) @ d["k"][h].astype(np.float64).T * float(d["sm_scale"])
+        for qb in range(nb):
+            keys = np.concatenate([np.arange(kb * 64, kb * 64 + 64) for kb in np.nonzero(d["mask"][h, qb])[0]])
+            for t in range(2):
+                zz = z[qb * 64 + 32 * t:qb * 64 + 32 * t + 32][:, keys]
+                best = max(best, float(zz.max() - zz.min()))
+    return best
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=[f"k{c[0]:g}q{c[1]:g}" for c in WIDE_CASES])
+def test_sar_wide_logit_spread_matches_oracle(dm, case):
+    """Tiles whose logits span more than 2^14 take the exponential with the
+    clamp at its cut-off (E = 0 below it), up to spreads of 10^16 and more:
+    bit-equal to the oracle in every stage, cached and reused step."""
+    ko, qo, seed = case
+    d = ga.make_attention(1, 2, 256, 72, 0.63, seed)
+    rng = np.random.default_rng(seed)
+    hot = rng.random(d["k"].shape[:2]) < 0.02
+    d["k"] = np.where(hot[..., None], d["k"] * np.float32(ko), d["k"]).astype(np.float32)
+    if qo != 1.0:
+        hq = rng.random(d["q"].shape) < 0.002
+        d["q"] = np.where(hq, d["q"] * np.float32(qo), d["q"]).astype(np.float32)
+    spread = logit_spread(d, 2)
+    log(f"case k_outlier={ko:g} q_outlier={qo:g} seed={seed} spread={spread:.3g}")
+    assert spread > (1e5 if ko < 1e10 else 2.0 ** 46)
+    g = run_gpu(dm, d, reuse_v=d["v_next"])
+    row_ptr, cols = sar.mask_to_csr(d["mask"])
+    r = sar.cached_step(d["q"], d["k"], d["v"], row_ptr, cols, 2, d["base_q"], d["sm_scale"], d["base_p"])
+    if qo != 1.0:
+        assert r["qpot"].max() > 8
+    compare(g, r, d)
+    u = sar.reused_step(r["pcodes"], r["ppot"], d["v_next"], row_ptr, cols, 2, d["base_p"])
+    np.testing.assert_array_equal(g["o_reused"], u["o"])
+
+
 def test_sar_empty_query_blocks_and_sparse_rows(dm):
     """Query blocks without any kept key block get O = 0; single kept blocks
     far from the diagonal work."""
