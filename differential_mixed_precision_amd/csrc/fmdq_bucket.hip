@@ -11,11 +11,12 @@
 //
 // For K <= 16384 (every workload) the count is a wave-level split: a wave
 // takes 64 consecutive channels ("chunk"), and for each lane the lanes with
-// the same bin are found with six ballots (one per bit of the bin); the
-// lowest of them writes the group's size into a [64 bins][chunks] table, and
-// a lane's rank among its peers is the number of lower peers.  The ballots
-// are the kernel's main cost (vector ALU, one workgroup per tile), so each
-// lane keeps its bin and rank in a register from the count to the placement.
+// the same bin come from a per-wave LDS table of 64 lane masks (each lane ORs
+// its bit into its bin's entry and reads the entry back); the lowest of them
+// writes the group's size into a [64 bins][chunks] table, and a lane's rank
+// among its peers is the number of lower peers.  Each lane keeps its bin and
+// rank in a register from the count to the placement, and a wave loads the
+// tags of all its chunks (16 at most) at once, straight from global memory.
 // One exclusive scan over the table in (bin, chunk) order then gives every
 // (bin, chunk) its first output slot — the stable order, since chunks and
 // lanes both run in channel order — and each lane places its channel at
@@ -87,18 +88,15 @@ __host__ __device__ __forceinline__ int count_row(int C) {
   return 2 * (w % 2 == 1 ? w : w + 1);
 }
 
-// Lanes of this wave whose 6-bit bin equals this lane's (active lanes only).
-__device__ __forceinline__ uint64_t peers_of(int bin, uint64_t active) {
-  uint64_t m = active;
-#pragma unroll
-  for (int bit = 0; bit < 6; ++bit) {
-    const uint64_t b = __ballot((bin >> bit) & 1);
-    m &= ((bin >> bit) & 1) ? b : ~b;
-  }
-  return m;
-}
+constexpr int kBallotWaves = kBallotThreads / 64;
 
+// NCH bounds both the chunks of a wave (⌈C/16⌉) and the count-table entries
+// a thread scans (⌈64·C/1024⌉, the same number); the host picks the smallest
+// of 1, 2, 4, 8, 16 that covers K.
+template <int NCH>
 __global__ __launch_bounds__(kBallotThreads) void bucket_ballot_kernel(BucketArgs a) {
+  constexpr int kChunksPerWave = NCH;
+  constexpr int kScanPer = NCH;
   extern __shared__ __align__(16) uint8_t smem[];
   const int K = a.K;
   const int C = (K + 63) / 64;                  // chunks of 64 channels
@@ -107,55 +105,86 @@ __global__ __launch_bounds__(kBallotThreads) void bucket_ballot_kernel(BucketArg
   const int epad = (kBins * CP + 7) & ~7;
   uint16_t* cnt = reinterpret_cast<uint16_t*>(smem);                   // [64][CP]
   uint32_t* wave_tot = reinterpret_cast<uint32_t*>(smem + 2 * epad);   // [16]
-  uint8_t* tags_s = smem + 2 * epad + 64;                              // [K]
-  const int kpad = (K + 15) & ~15;
-  uint16_t* perm_s = reinterpret_cast<uint16_t*>(tags_s + kpad);       // [K]
-  uint16_t* br_s = perm_s + kpad;                                      // [K]
+  unsigned long long* mk = reinterpret_cast<unsigned long long*>(smem + 2 * epad + 64);   // [16 waves][64]
+  uint16_t* perm_s = reinterpret_cast<uint16_t*>(smem + 2 * epad + 64 + 8 * kBallotThreads);  // [K]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t below = (1ull << lane) - 1ull;
-  const int per = (E + kBallotThreads - 1) / kBallotThreads;   // scan entries per thread
+  const unsigned long long me = 1ull << lane;
+  mk += 64 * wave;
+  const int per = (E + kBallotThreads - 1) / kBallotThreads;   // scan entries per thread (≤ NCH)
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
-  // Tags in 4-byte words and ids in 16-byte pieces when every tile's row is
-  // so aligned (the staging buffers in LDS always are).
-  const bool tags4 = ((reinterpret_cast<uintptr_t>(a.tags) | (uintptr_t)K) & 3u) == 0;
+  // Ids in 16-byte pieces when every tile's row is so aligned (the staging
+  // buffer in LDS always is).
   const bool perm16 = ((reinterpret_cast<uintptr_t>(a.perm) | (uintptr_t)(2 * K)) & 15u) == 0;
 
-  for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+  // one tile per workgroup (the grid is the tiles): nothing is carried from a
+  // tile to the next, so nothing is held across one
+  {
+    const int64_t tile = blockIdx.x;
     const uint8_t* tg = a.tags + tile * (int64_t)K;
     uint16_t* out = a.perm + tile * (int64_t)K;
-    if (tags4) {
-      for (int i = tid; i < K / 4; i += kBallotThreads)
-        reinterpret_cast<uint32_t*>(tags_s)[i] = reinterpret_cast<const uint32_t*>(tg)[i];
-    } else {
-      for (int i = tid; i < K; i += kBallotThreads) tags_s[i] = tg[i];
-    }
+    // The wave's chunks are c = wave + 16·i.  Their tags are loaded at once
+    // (clamped indices, so the number of loads is fixed and all are in
+    // flight together) while the count table is cleared.
+    uint32_t tb[kChunksPerWave];
+#pragma unroll
+    for (int i = 0; i < kChunksPerWave; ++i) tb[i] = tg[min(64 * (wave + kBallotWaves * i) + lane, K - 1)];
     for (int i = tid; i < epad / 8; i += kBallotThreads) reinterpret_cast<uint4*>(cnt)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
-    // Count.  The lane's bin and its rank among the lanes of its chunk with
-    // the same bin are kept (bin | rank << 8, at the channel's own index) for
-    // the placement, so the ballots run once per chunk.
-    for (int c = wave; c < C; c += kBallotThreads / 64) {
-      const int k = 64 * c + lane;
-      const bool act = k < K;
-      const uint64_t active = __ballot(act);
-      const int bin = act ? bin_of(tags_s[k]) : 0;
-      const uint64_t peers = peers_of(bin, active);
-      const uint32_t rank = (uint32_t)__popcll(peers & below);
-      if (act) {
-        if (rank == 0u) cnt[bin * CP + c] = (uint16_t)__popcll(peers);
-        br_s[k] = (uint16_t)((uint32_t)bin | (rank << 8));
+    // Count.  A lane's bin and its rank among the lanes of its chunk with the
+    // same bin stay in a register (bin | rank << 8) until the placement.
+    // The lanes of a chunk with this lane's bin: every lane clears its own
+    // entry of the wave's [64] mask table, ORs its lane bit into the entry of
+    // its bin and reads that entry back.  A wave's LDS operations execute in
+    // the order issued, so the three steps of a chunk (and the next chunk's
+    // clear after this chunk's read) need no wait between them; the compiler
+    // barriers keep that order in the code.
+    uint64_t peers[kChunksPerWave];
+#pragma unroll
+    for (int i = 0; i < kChunksPerWave; ++i) {
+      const int c = wave + kBallotWaves * i;
+      peers[i] = 0;
+      if (c < C) {                                 // wave-uniform
+        const bool act = 64 * c + lane < K;
+        const int bin = bin_of(tb[i]);
+        mk[lane] = 0ull;
+        __builtin_amdgcn_wave_barrier();
+        if (act) atomicOr(&mk[bin], me);
+        __builtin_amdgcn_wave_barrier();
+        peers[i] = mk[bin];
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+    uint32_t br[(kChunksPerWave + 1) / 2];        // two (bin | rank << 8) halves per word
+#pragma unroll
+    for (int i = 0; i < (kChunksPerWave + 1) / 2; ++i) br[i] = 0;
+#pragma unroll
+    for (int i = 0; i < kChunksPerWave; ++i) {
+      const int c = wave + kBallotWaves * i;
+      if (c < C) {
+        const bool act = 64 * c + lane < K;
+        const int bin = bin_of(tb[i]);
+        const uint32_t rank = (uint32_t)__popcll(peers[i] & below);
+        if (act && rank == 0u) cnt[bin * CP + c] = (uint16_t)__popcll(peers[i]);
+        br[i / 2] |= ((uint32_t)bin | (rank << 8)) << (16 * (i & 1));
       }
     }
     __syncthreads();
-    // exclusive scan of cnt in (bin, chunk) order
-    uint32_t sum = 0;
+    // Exclusive scan of cnt in (bin, chunk) order: a thread's entries are
+    // read at once, summed, offset by the wave scan and the lower waves'
+    // totals, and written back from registers.
+    uint32_t v[kScanPer];
     {
-      int b = e0 / max(C, 1), c = e0 - b * C;
-      for (int e = e0; e < e1; ++e) {
-        sum += cnt[b * CP + c];
-        if (++c == C) { c = 0; ++b; }
+      int bb = e0 / max(C, 1), cc = e0 - bb * C;
+#pragma unroll
+      for (int i = 0; i < kScanPer; ++i) {
+        v[i] = e0 + i < e1 ? cnt[bb * CP + cc] : 0u;
+        if (++cc == C) { cc = 0; ++bb; }
       }
     }
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i) sum += v[i];
     uint32_t inc = sum;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -167,20 +196,24 @@ __global__ __launch_bounds__(kBallotThreads) void bucket_ballot_kernel(BucketArg
     uint32_t run = inc - sum;
     for (int w = 0; w < wave; ++w) run += wave_tot[w];
     {
-      int b = e0 / max(C, 1), c = e0 - b * C;
-      for (int e = e0; e < e1; ++e) {
-        const uint32_t v = cnt[b * CP + c];
-        cnt[b * CP + c] = (uint16_t)run;
-        run += v;
-        if (++c == C) { c = 0; ++b; }
+      int bb = e0 / max(C, 1), cc = e0 - bb * C;
+#pragma unroll
+      for (int i = 0; i < kScanPer; ++i) {
+        if (e0 + i < e1) cnt[bb * CP + cc] = (uint16_t)run;
+        run += v[i];
+        if (++cc == C) { cc = 0; ++bb; }
       }
     }
     __syncthreads();
     if (tid < kBins) a.group_off[tile * (kBins + 1) + tid] = (int32_t)cnt[tid * CP];
     if (tid == kBins) a.group_off[tile * (kBins + 1) + kBins] = K;
-    for (int k = tid; k < K; k += kBallotThreads) {
-      const uint32_t v = br_s[k];
-      perm_s[cnt[(int)(v & 0xFFu) * CP + (k >> 6)] + (v >> 8)] = (uint16_t)k;
+    // Place: channel k goes to its (bin, chunk) slot plus its rank.
+#pragma unroll
+    for (int i = 0; i < kChunksPerWave; ++i) {
+      const int c = wave + kBallotWaves * i;
+      const int k = 64 * c + lane;
+      const uint32_t v2 = (br[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
+      if (c < C && k < K) perm_s[cnt[(int)(v2 & 0xFFu) * CP + c] + (v2 >> 8)] = (uint16_t)k;
     }
     __syncthreads();
     if (perm16) {
@@ -189,7 +222,6 @@ __global__ __launch_bounds__(kBallotThreads) void bucket_ballot_kernel(BucketArg
     } else {
       for (int i = tid; i < K; i += kBallotThreads) out[i] = perm_s[i];
     }
-    __syncthreads();
   }
 }
 
@@ -248,15 +280,32 @@ int launch_bucket(const BucketArgs& a, hipStream_t s) {
   const int64_t grid = a.n_tiles < 2048 ? a.n_tiles : 2048;
   if (a.K <= kBallotMaxK) {
     const size_t E = (size_t)kBins * count_row((a.K + 63) / 64);
-    const size_t lds = 2 * ((E + 7) & ~(size_t)7) + 64 + 5 * (size_t)((a.K + 15) & ~15);
+    const size_t lds = 2 * ((E + 7) & ~(size_t)7) + 64 + 8 * (size_t)kBallotThreads + 2 * (size_t)((a.K + 15) & ~15);
     if (lds > 65536) {
-      hipError_t e = hipFuncSetAttribute((const void*)bucket_ballot_kernel,
+      // only the widest instantiation (K > 8192) needs more than 64 KB
+      hipError_t e = hipFuncSetAttribute((const void*)bucket_ballot_kernel<16>,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess)
         return set_error(DSTAR_EHIP, "fmdq_bucket: hipFuncSetAttribute: %s", hipGetErrorString(e));
     }
-    hipLaunchKernelGGL(bucket_ballot_kernel, dim3((unsigned)grid), dim3(kBallotThreads), lds, s, a);
-    return check_launch("fmdq_bucket");
+    // one workgroup per tile, at most 2^20 tiles (2^30 threads) per launch
+    constexpr int64_t kMaxGrid = int64_t(1) << 20;
+    for (int64_t t0 = 0; t0 < a.n_tiles; t0 += kMaxGrid) {
+      BucketArgs b = a;
+      b.n_tiles = a.n_tiles - t0 < kMaxGrid ? a.n_tiles - t0 : kMaxGrid;
+      b.tags = a.tags + t0 * a.K;
+      b.perm = a.perm + t0 * a.K;
+      b.group_off = a.group_off + t0 * (kBins + 1);
+      const int C = (a.K + 63) / 64;
+      const dim3 grid((unsigned)b.n_tiles), block(kBallotThreads);
+      if (C <= 16) hipLaunchKernelGGL(bucket_ballot_kernel<1>, grid, block, lds, s, b);
+      else if (C <= 32) hipLaunchKernelGGL(bucket_ballot_kernel<2>, grid, block, lds, s, b);
+      else if (C <= 64) hipLaunchKernelGGL(bucket_ballot_kernel<4>, grid, block, lds, s, b);
+      else if (C <= 128) hipLaunchKernelGGL(bucket_ballot_kernel<8>, grid, block, lds, s, b);
+      else hipLaunchKernelGGL(bucket_ballot_kernel<16>, grid, block, lds, s, b);
+      if (int rc = check_launch("fmdq_bucket")) return rc;
+    }
+    return DSTAR_OK;
   }
   const size_t base = (size_t)kBins * kThreads * 2 + 64;
   size_t lds = base;

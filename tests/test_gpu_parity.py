@@ -371,6 +371,38 @@ def test_config0_full(dm):
     log(f"  config 0 done in {time.time() - t:.1f}s")
 
 
+BUCKET_K = [1024, 1025, 2048, 2049, 4096, 4097, 8192, 8193, 12288, 16383, 16384, 16385]
+
+
+@pytest.mark.parametrize("K", BUCKET_K)
+def test_bucket_chunk_counts_match_oracle(dm, K):
+    """Stage 2 alone on seeded tag bytes, at both sides of every boundary of
+    its instantiations (1, 2, 4, 8 or 16 chunks of 64 channels per wave, and
+    the other variant above K = 16384): perm and offsets bit-equal to the
+    oracle.  Tiles: skewed over a few bins, uniform over all 64, and a single
+    bin."""
+    import torch
+    dev = torch.device("cuda:0")
+    T, nt = 32, 3
+    rng = np.random.default_rng(K)
+    g = np.minimum(rng.geometric(0.35, size=(nt, K)) - 1, 15)
+    pc = rng.choice(4, size=(nt, K), p=[0.1, 0.2, 0.3, 0.4])
+    g[1] = rng.integers(0, 16, size=K)
+    pc[1] = rng.integers(0, 4, size=K)
+    g[2], pc[2] = 7, 2
+    tags = (g | (pc << fmdq.PREC_SHIFT)).astype(np.uint8)
+    perm_r, off_r = fmdq.bucket(tags)
+    p = dm.make_params(nt * T, K, T, 1.0, 2, nt * T)
+    tg = torch.from_numpy(tags).to(dev)
+    perm = torch.full((nt, K), -1, dtype=torch.int16, device=dev)
+    off = torch.full((nt, 65), -7, dtype=torch.int32, device=dev)
+    log(f"  gpu bucket K={K}")
+    dm.bucket(p, tg, perm, off)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(perm.cpu().numpy().view(np.uint16), perm_r)
+    np.testing.assert_array_equal(off.cpu().numpy(), off_r)
+
+
 def test_determinism(dm):
     """Ten runs of the same layer give the same bits in every output (the
     stages have no atomics whose order could change a result)."""
