@@ -92,6 +92,9 @@ CASES = [
     (1, 2, 192, 40, 0.8, 5),
     (1, 1, 64, 1, 1.0, 6),
     (2, 1, 128, 96, 1.0, 7),
+    # more (head, query block) pairs than the scores kernel orders longest
+    # first (1040 > 1024): its waves keep index order
+    (1, 65, 1024, 16, 0.4, 18),
 ]
 
 
