@@ -240,7 +240,7 @@ def cpu_baseline(ins: list[dict], layer_names: list[str], budget_s: float = 10.0
 
 def kernel_trace_args(workload: str) -> str:
     return (f"--workload {workload} --steps 10 --warmup 3 --no-cpu-baseline --no-dynamic --no-chain "
-            f"--no-slices --no-attention --no-per-workload")
+            f"--no-slices --no-attention --no-per-workload --no-cold")
 
 
 def summary_spec(which: str, workload: str):
@@ -309,13 +309,14 @@ def write_kernel_summary(trace_dir: str, which: str = "linear", workload: str = 
     lines += ["", "Per kernel and launch grid (threads), from the trace" +
               (" (launches attributed to their layer by the stage-3 launch that follows them: stages 1 and 2"
                " launch with the same grid at fc1 and fc2):" if which == "linear" else ":"), "",
-              "| kernel | grid | layer (stage-3 grid) | calls | mean us | min us | max us |",
-              "|---|---|---|---|---|---|---|"]
+              "| kernel | grid | layer (stage-3 grid) | calls | mean us | median us | min us | max us |",
+              "|---|---|---|---|---|---|---|---|"]
     for (name, grid, lg), v in sorted(per.items(), key=lambda x: -sum(x[1])):
         short = name.replace("dstar::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
         short = short if len(short) <= 80 else short[:80] + "..."
+        med = sorted(v)[len(v) // 2] if len(v) % 2 else 0.5 * sum(sorted(v)[len(v) // 2 - 1:len(v) // 2 + 1])
         lines.append(f"| `{short}` | {grid} | {lg if lg is not None else '-'} | {len(v)} | {sum(v) / len(v):.1f} | "
-                     f"{min(v):.1f} | {max(v):.1f} |")
+                     f"{med:.1f} | {min(v):.1f} | {max(v):.1f} |")
     out = os.path.join(ROOT, "profiles", fname)
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
