@@ -4,7 +4,8 @@
 // Kernels:
 //   qquant  FMDQ-INT8 of Q: one wave per 32-row token tile, a lane per channel
 //           (two channel passes), the tile's rows streamed with coalesced loads.
-//   kquant  int8 of K with a scale per key: one wave per 8 key rows.
+//   kquant  int8 of K with a scale per key: eight lanes per key row (one wave
+//           per 8 rows when d is not a multiple of 4).
 //   vquant  int8 of V with a scale per channel: a column-maximum pass (partial
 //           maxima of 256-row chunks lowered into the scale buffer by atomic
 //           max on the float bits), a quantize pass that writes the codes
@@ -241,6 +242,56 @@ __global__ __launch_bounds__(kThreads) void kquant_kernel(const float* k, int8_t
     if (lane < m.dp) kc[row * m.dp + lane] = (int8_t)code_w(x0[i], s);
     if (lane + 64 < m.dp) kc[row * m.dp + lane + 64] = (int8_t)code_w(x1[i], s);
     if (lane == 0) ks[row] = s;
+  }
+}
+
+// Eight lanes per key row when d is a multiple of 4: lane j of a row's group
+// holds channels [j·W, j·W + W) (W = dp/8, so the group covers the padded
+// row), read as 16-byte pieces and written back as W code bytes; the row's
+// maximum takes three shuffles within the group.  A wave takes 8·kKSets rows,
+// all their loads in flight together.  Same codes and scales as kquant_kernel.
+constexpr int kKSets = 2;
+template <int W>
+__global__ __launch_bounds__(kThreads) void kquant8_kernel(const float* k, int8_t* kc, float* ks, Dims m) {
+  constexpr int NV = W / 4;
+  const int lane = threadIdx.x & 63, j = lane & 7, grp = lane >> 3;
+  const int64_t rows = m.BH * m.L;
+  const int64_t row0 = ((int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6)) * (8 * kKSets);
+  if (row0 >= rows) return;
+  float4 x[kKSets][NV];
+#pragma unroll
+  for (int st = 0; st < kKSets; ++st) {
+    const int64_t row = min(row0 + 8 * st + grp, rows - 1);   // rows past the end are never stored
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = j * W + 4 * i;
+      x[st][i] = *reinterpret_cast<const float4*>(k + row * m.d + (c < m.d ? c : 0));   // unconditional
+    }
+  }
+#pragma unroll
+  for (int st = 0; st < kKSets; ++st) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if (j * W + 4 * i >= m.d) x[st][i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      mx = fmaxf(fmaxf(mx, fmaxf(fabsf(x[st][i].x), fabsf(x[st][i].y))), fmaxf(fabsf(x[st][i].z), fabsf(x[st][i].w)));
+    mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+    const float sc = (float)((double)mx / 127.0);
+    const int64_t row = row0 + 8 * st + grp;
+    if (row < rows) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(kc + row * m.dp + j * W);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const float4 v = x[st][i];
+        dst[i] = ((uint32_t)code_w(v.x, sc) & 0xFFu) | (((uint32_t)code_w(v.y, sc) & 0xFFu) << 8) |
+                 (((uint32_t)code_w(v.z, sc) & 0xFFu) << 16) | (((uint32_t)code_w(v.w, sc) & 0xFFu) << 24);
+      }
+      if (j == 0) ks[row] = sc;
+    }
   }
 }
 
@@ -907,8 +958,19 @@ int dstar_sar_quantize_k(const dstar_sar_params* p, const float* k, int8_t* kcod
   if (int rc = check(p)) return rc;
   if (int rc = check_ptrs({{k, 4}, {kcodes, 16}, {kscale, 4}})) return rc;
   const Dims m = dims_of(p);
-  hipLaunchKernelGGL(kquant_kernel, dim3(waves_grid((m.BH * m.L + kKRows - 1) / kKRows)), dim3(kThreads), 0,
-                     (hipStream_t)stream, k, kcodes, kscale, m);
+  const hipStream_t s = (hipStream_t)stream;
+  if (m.d % 4 == 0 && aligned(k, 16)) {
+    const dim3 grid(waves_grid((m.BH * m.L + 8 * kKSets - 1) / (8 * kKSets))), block(kThreads);
+    switch (m.dp / 8) {
+      case 4: hipLaunchKernelGGL(kquant8_kernel<4>, grid, block, 0, s, k, kcodes, kscale, m); break;
+      case 8: hipLaunchKernelGGL(kquant8_kernel<8>, grid, block, 0, s, k, kcodes, kscale, m); break;
+      case 12: hipLaunchKernelGGL(kquant8_kernel<12>, grid, block, 0, s, k, kcodes, kscale, m); break;
+      default: hipLaunchKernelGGL(kquant8_kernel<16>, grid, block, 0, s, k, kcodes, kscale, m); break;
+    }
+  } else {
+    hipLaunchKernelGGL(kquant_kernel, dim3(waves_grid((m.BH * m.L + kKRows - 1) / kKRows)), dim3(kThreads), 0, s,
+                       k, kcodes, kscale, m);
+  }
   return check_launch("sar_quantize_k");
 }
 
