@@ -384,6 +384,13 @@ struct ScoreArgs {
   int32_t clip_p;    // base_p·2^21 < 1: P codes can exceed 64 and are clipped
 };
 
+// Kept-block column at a wave-uniform index.  The mask is read-only for the
+// whole launch, so it is read through the constant address space: the load
+// becomes a scalar load, which the vector-memory counter does not include
+// (a vector load here made every iteration wait for all loads in flight).
+typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
+__device__ __forceinline__ int mask_col(const int32_t* cols, int j) { return ((const_i32_ptr)cols)[j]; }
+
 // Kept-block range of a query block, clamped to [0, nnz].
 __device__ __forceinline__ void block_range(const int32_t* row_ptr, int64_t r, int32_t nnz, int& j0, int& j1) {
   j0 = min(max(row_ptr[r], 0), nnz);
@@ -573,7 +580,7 @@ __device__ __forceinline__ void sweep_blocks(const ScoreArgs& a, int64_t bh, int
   v4i Bn[2][NKS];
   float sn[2];
   auto fetch = [&](int j) {
-    int kb = a.cols[j];
+    int kb = mask_col(a.cols, j);
     kb = (kb < 0 || kb >= a.m.nb) ? 0 : kb;     // skipped below; any block in range
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
@@ -586,7 +593,7 @@ __device__ __forceinline__ void sweep_blocks(const ScoreArgs& a, int64_t bh, int
   constexpr bool kPrefetch = NP <= 2;
   if (kPrefetch) fetch(j0);
   for (int j = j0; j < j1; ++j) {
-    const int kb = a.cols[j];
+    const int kb = mask_col(a.cols, j);
     if (!kPrefetch) fetch(j);
     v4i B[2][NKS];
     float sc[2];
@@ -792,7 +799,7 @@ __device__ __forceinline__ void pv_pass(const PvArgs& a, int64_t bh, int tau, in
   const int8_t* vbh = a.vct + (bh * a.m.dp + li) * (int64_t)a.m.L + 16 * hi;
   if (j0 < j1) fetch(j0);
   for (int j = j0; j < j1; ++j) {
-    const int kb = a.cols[j];
+    const int kb = mask_col(a.cols, j);
     const bool valid = kb >= 0 && kb < a.m.nb;
     const v4i cw0 = cn[0], cw1 = cn[1], pw0 = pn[0], pw1 = pn[1];
     // V fragments of this block first, then the next block's P: vector loads
