@@ -5,7 +5,8 @@
 //   qquant  FMDQ-INT8 of Q: one wave per 32-row token tile, a lane per channel
 //           (two channel passes), the tile's rows streamed with coalesced loads.
 //   kquant  int8 of K with a scale per key: eight lanes per key row (one wave
-//           per 8 rows when d is not a multiple of 4).
+//           per 8 rows when d is not a multiple of 4 or K is not 16-byte
+//           aligned).
 //   vquant  int8 of V with a scale per channel: a column-maximum pass (partial
 //           maxima of 256-row chunks lowered into the scale buffer by atomic
 //           max on the float bits), a quantize pass that writes the codes
@@ -245,11 +246,12 @@ __global__ __launch_bounds__(kThreads) void kquant_kernel(const float* k, int8_t
   }
 }
 
-// Eight lanes per key row when d is a multiple of 4: lane j of a row's group
-// holds channels [j·W, j·W + W) (W = dp/8, so the group covers the padded
-// row), read as 16-byte pieces and written back as W code bytes; the row's
-// maximum takes three shuffles within the group.  A wave takes 8·kKSets rows,
-// all their loads in flight together.  Same codes and scales as kquant_kernel.
+// Eight lanes per key row when d is a multiple of 4 and K is 16-byte aligned:
+// lane j of a row's group holds channels [j·W, j·W + W) (W = dp/8, so the
+// group covers the padded row), read as 16-byte pieces and written back as W
+// code bytes; the row's maximum takes three shuffles within the group.  A
+// wave takes 8·kKSets rows, all their loads in flight together.  Same codes
+// and scales as kquant_kernel.
 constexpr int kKSets = 2;
 template <int W>
 __global__ __launch_bounds__(kThreads) void kquant8_kernel(const float* k, int8_t* kc, float* ks, Dims m) {
