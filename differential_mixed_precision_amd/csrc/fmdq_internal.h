@@ -169,6 +169,7 @@ int layer_impl(const dstar_fmdq_params* p, int32_t N, const float* x_t, const fl
                const int8_t* w, const int8_t* w_t, const float* w_scale, const float* y_prev,
                float* y_out, uint32_t* bit_hist, void* workspace, int64_t workspace_bytes,
                void* stream);
+int cu_count();   // compute units of the current device
 bool linear_mfma_supported(const LinearArgs& a);
 int launch_linear_mfma(const LinearArgs& a, hipStream_t s);
 bool linear_pp_supported(const LinearArgs& a);

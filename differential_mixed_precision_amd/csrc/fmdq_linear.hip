@@ -3,7 +3,8 @@
 //     waves per CU, the two waves of each SIMD alternating matrix and memory
 //     phases): the faster dense loop, but its Y_{t-1}/Y_t stream cannot
 //     overlap another workgroup's matrix work on the same CU;
-//   - the two-workgroups-per-CU kernel (128 × 256 blocks of four waves),
+//   - the two-workgroups-per-CU kernel (128 × 256 blocks of four waves, or
+//     128 × 128 where the wider blocks would number fewer than the CUs),
 //     whose workgroups hide each other's Y stream.
 // Measured on MI355X over the five workloads: the ping-pong kernel is faster
 // where the reduction is long (K ≥ 4096, so the matrix work dominates the Y
@@ -19,7 +20,6 @@
 
 namespace dstar {
 
-namespace {
 // Compute units of the current device (looked up once per device).
 int cu_count() {
   static int counts[64] = {};
@@ -32,7 +32,6 @@ int cu_count() {
   }
   return counts[dev];
 }
-}  // namespace
 
 int launch_linear(const LinearArgs& a, hipStream_t s) {
   if (a.acc_dbg == nullptr && linear_pp_supported(a) && a.T == 32 && a.K >= 4096) {

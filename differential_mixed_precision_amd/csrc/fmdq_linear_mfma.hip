@@ -40,7 +40,9 @@
 //
 // Layout.  Workgroup = 256 threads = 4 waves, output block 128 rows × 256
 // columns; wave w owns all 128 rows and columns 64w .. 64w+63 (4 × 2 MFMA
-// 32x32x32 int8 tiles).  Dense part: 64-channel chunks of stage 1's aligned
+// 32x32x32 int8 tiles).  Grids that would give the CUs fewer workgroups than
+// there are CUs use blocks of 128 × 128 instead (wave w: columns 32w ..
+// 32w+31, 4 × 1 tiles; the same rings, half the W bytes per stage).  Dense part: 64-channel chunks of stage 1's aligned
 // codes ([rows][K]) and of W^T ([N][K]), both channel innermost, flow through
 // a 3-stage LDS ring filled by direct global-to-LDS buffer loads; a chunk's
 // stage is refilled as soon as every wave holds the fragments of its second
@@ -71,11 +73,9 @@ typedef __attribute__((address_space(3))) v2i lds_v2i;
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int BM = 128;            // rows per workgroup
-constexpr int WN = 64;             // output columns per wave
-constexpr int BN = kWaves * WN;    // output columns per workgroup (256)
+constexpr int WN = 64;             // output columns per wave (the wide blocks)
+constexpr int BN = kWaves * WN;    // output columns per workgroup (256; the LDS regions are sized for it)
 constexpr int RB = BM / 32;        // 32-row MFMA blocks per wave (4)
-constexpr int CB = WN / 32;        // 32-column MFMA blocks per wave (2)
-static_assert(CB == 2, "the gathered step is written for two column blocks");
 constexpr int BK = 64;             // channels per dense chunk (2 MFMA k-steps)
 constexpr int KS = 32;             // channels per MFMA k-step (= per gathered unit)
 constexpr int kTags = DSTAR_FMDQ_NUM_TAGS;
@@ -135,9 +135,6 @@ constexpr uint32_t kOob = 0x80000000u;
 // 6:4, lgkmcnt 11:8; the counters not waited on at their maximum).
 constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 constexpr int kWaitVm0 = wait_vm(0);
-constexpr int kWaitVmChunk = wait_vm(6);   // one dense chunk's six loads
-constexpr int kWaitVmChunkIds = wait_vm(14);  // ... and eight id loads
-constexpr int kWaitVmFirst = wait_vm(20);  // two chunks and the eight id loads
 constexpr int kWaitLgkm0 = 0xC07F;         // lgkmcnt(0)
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
@@ -181,17 +178,19 @@ __device__ __forceinline__ v4i tr_frag(const uint8_t* tile, int col0, int lane) 
   return v4i{lo[0], lo[1], hi[0], hi[1]};
 }
 
-// The same from a gathered W tile [32 channels][256 columns] whose 16-byte
-// pieces are stored XOR-swizzled: column piece P of channel c sits at piece
-// P ^ (c mod 8), so the 8 channels one 16-lane group reads hit 8 different
-// pieces (no bank conflicts).  Channels c and c + 8 share the swizzle.
+// The same from a gathered W tile [32 channels][NB columns] (NB = 256 or
+// 128) whose 16-byte pieces are stored XOR-swizzled: column piece P of
+// channel c sits at piece P ^ (c mod 8), so the 8 channels one 16-lane group
+// reads hit 8 different pieces (no bank conflicts).  Channels c and c + 8
+// share the swizzle.
+template <int NB>
 __device__ __forceinline__ v4i tr_frag_wsw(const uint8_t* tile, int col0, int lane) {
   const int q = lane >> 4, r = lane & 15;
   const int c = 16 * (q >> 1) + (r >> 1);
   const int piece = ((col0 >> 4) + (q & 1)) ^ (c & 7);
-  const uint8_t* p = tile + c * BN + 16 * piece + 8 * (r & 1);
+  const uint8_t* p = tile + c * NB + 16 * piece + 8 * (r & 1);
   const v2i lo = tr8(p);
-  const v2i hi = tr8(p + 8 * BN);
+  const v2i hi = tr8(p + 8 * NB);
   return v4i{lo[0], lo[1], hi[0], hi[1]};
 }
 
@@ -202,9 +201,23 @@ __device__ __forceinline__ void shift_acc(v16i& acc, int s) {
 
 // Gelu: the epilogue also stores GELU(Y_t) (a separate instantiation, so the
 // plain kernel carries none of its code).
-template <int T, bool VecW, bool Gelu>
+// WNt: output columns per wave, 64 (blocks of 128 × 256) or 32 (128 × 128,
+// for grids that would leave CUs without a workgroup; 16-byte W loads only).
+template <int T, bool VecW, bool Gelu, int WNt>
 __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, int32_t row_blocks,
                                                                   int32_t col_blocks) {
+  constexpr int WN = WNt;                 // output columns per wave
+  constexpr int BN = kWaves * WN;         // output columns per workgroup
+  constexpr int CB = WN / 32;             // 32-column MFMA blocks per wave
+  static_assert(WN == 64 || (WN == 32 && VecW), "column widths");
+  constexpr int kNB1 = WN / 16;           // W^T loads per wave and dense chunk (16 rows each)
+  constexpr int kStageDenseT = (BM + BN) * BK;
+  constexpr int kUnitBT = KU * BN;
+  constexpr int kUnitBytesT = kUnitA + kUnitBT;
+  static_assert(kStages * kStageDenseT <= kDataBytes && kUnits * kUnitBytesT <= kDataBytes, "rings fit");
+  constexpr int kWaitVmChunkT = wait_vm(2 + kNB1);           // one dense chunk's loads
+  constexpr int kWaitVmChunkIdsT = wait_vm(2 + kNB1 + 8);    // ... and eight id loads
+  constexpr int kWaitVmFirstT = wait_vm(2 * (2 + kNB1) + 8); // two chunks and the eight id loads
   constexpr int kTiles = Cfg<T>::kTiles;
   // Gathered units are scheduled per (32-row block, list): per block, first
   // the third-digit lists, then the second-digit lists, of the kTPB token
@@ -217,8 +230,8 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   // gathered units; written for 32-row tiles and N a multiple of 16.
   constexpr bool kDense1 = T == 32 && VecW;
   // Direct-to-LDS loads per wave per gathered unit: two dword loads of digit
-  // codes, and the W rows as four 16-byte or sixteen 4-byte loads.
-  constexpr int kOpsUnit = VecW ? 6 : 18;
+  // codes, and the W rows as BN/64 16-byte or sixteen 4-byte loads.
+  constexpr int kOpsUnit = VecW ? 2 + BN / 64 : 18;
   constexpr int kWaitVmUnits = wait_vm(kOpsUnit * (kAhead - 1));   // unit u landed
   static_assert(kOpsUnit * (kAhead - 1) <= 63, "vmcnt range");
   extern __shared__ __align__(16) uint8_t smem[];
@@ -273,8 +286,8 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   // reads (one ds_read_b128) are free of bank conflicts.  A direct load
   // writes lane l's 16 bytes at base + 16·l: one wave instruction fills 16
   // rows.  Each wave issues 2 A and 4 B instructions per chunk.
-  auto stageA = [&](int st) { return smem + st * kStageDense; };
-  auto stageB = [&](int st, int w) { return smem + st * kStageDense + BM * BK + w * WN * BK; };
+  auto stageA = [&](int st) { return smem + st * kStageDenseT; };
+  auto stageB = [&](int st, int w) { return smem + st * kStageDenseT + BM * BK + w * WN * BK; };
   const int r16 = lane >> 2;                       // row of this lane within a 16-row group
   const int c16 = (lane & 3) ^ ((r16 >> 2) & 3);   // global 16-byte column it loads
   // K a multiple of 16: the last chunk may hold fewer than 64 channels; a
@@ -291,7 +304,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
                                                live ? (uint32_t)(row * K + k0 + 16 * c16) : kOob, 0, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kNB1; ++j) {
       const int64_t n = nw + 16 * j + r16;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r_wt, (lds_ptr)(stageB(st, wave) + 1024 * j), 16,
                                                live && n < N ? (uint32_t)(n * K + k0 + 16 * c16) : kOob, 0, 0, 0);
@@ -516,7 +529,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
         }
         const bool live = c < nchunks && k0 + 16 * c16 < K;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < kNB1; ++j) {
           const int64_t n = nw + 16 * j + r16;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(r_wt, (lds_ptr)(stageB(st, wave) + 1024 * j), 16,
                                                    live && n < N ? (uint32_t)(n * K + k0 + 16 * c16) : kOob, 0, 0,
@@ -546,7 +559,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
       };
 #pragma unroll
       for (int c = 0; c < kStages; ++c) issue1(c, c);
-      __builtin_amdgcn_s_waitcnt(wait_vm(12));  // chunk 0
+      __builtin_amdgcn_s_waitcnt(wait_vm(2 * (2 + kNB1)));  // chunk 0
       __asm__ __volatile__("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       __asm__ __volatile__("" ::: "memory");
@@ -558,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
         wait1(g0);
         mma1(g0);
         read1(g1, st, 1);
-        __builtin_amdgcn_s_waitcnt(kWaitVmChunk);   // chunk c + 1 (chunk c + 2 after it)
+        __builtin_amdgcn_s_waitcnt(kWaitVmChunkT);   // chunk c + 1 (chunk c + 2 after it)
         bar_lds();                                   // also completes g1's reads
         issue1(c + kStages, st);
         wait1(g1);
@@ -603,12 +616,14 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
           acc[rb][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[rb], f.b[cb], acc[rb][cb], 0, 0, 0);
+      constexpr int kPairs = RB * CB < RB + CB ? RB * CB : RB + CB;
 #pragma unroll
-      for (int i = 0; i < RB + CB; ++i) {
+      for (int i = 0; i < kPairs; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, RB * CB - RB - CB, 0);
+      if constexpr (RB * CB > kPairs) __builtin_amdgcn_sched_group_barrier(0x008, RB * CB - kPairs, 0);
+      if constexpr (RB + CB > kPairs) __builtin_amdgcn_sched_group_barrier(0x100, RB + CB - kPairs, 0);
     };
     // Chunk c's stage is free once every wave holds its second k-step's
     // fragments, so the wait for chunk c + 1 and the barrier sit between the
@@ -618,7 +633,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     // in the first two waits the eight id loads (issued after chunk 2) may
     // also be in flight.
     Frags f0, f1;
-    __builtin_amdgcn_s_waitcnt(kWaitVmFirst);
+    __builtin_amdgcn_s_waitcnt(kWaitVmFirstT);
     __asm__ __volatile__("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __asm__ __volatile__("" ::: "memory");
@@ -629,9 +644,9 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
       read(f1, st, 1);
       mma(f0);
       if (c < 2) {
-        __builtin_amdgcn_s_waitcnt(kWaitVmChunkIds);
+        __builtin_amdgcn_s_waitcnt(kWaitVmChunkIdsT);
       } else {
-        __builtin_amdgcn_s_waitcnt(kWaitVmChunk);
+        __builtin_amdgcn_s_waitcnt(kWaitVmChunkT);
       }
       bar_lds();
       issue(c + kStages, st);
@@ -691,7 +706,10 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     const rsrc_t r_h = make_rsrc(a.hcodes + tile0 * K * T, plane_off + (uint32_t)(tiles_here * K * T));
     // The ids one wave needs for one unit's loads (all LDS reads first, so
     // they share one wait).
-    constexpr int kNB = VecW ? 4 : 16;
+    // W rows: with 16-byte loads one 1 KB load holds kCh channels' row
+    // segments (BN bytes each), kLpc lanes per channel.
+    constexpr int kNB = VecW ? BN / 64 : 16;
+    constexpr int kCh = 1024 / BN, kLpc = BN / 16;
     struct UnitIds {
       uint32_t inf, chA[2], chB[kNB];
     };
@@ -703,7 +721,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
       for (int m = 0; m < 2; ++m) d.chA[m] = en[8 * (2 * wave + m) + (lane >> 3)];
 #pragma unroll
       for (int m = 0; m < kNB; ++m)
-        d.chB[m] = VecW ? en[4 * (4 * wave + m) + (lane >> 4)] : en[16 * wave + m];
+        d.chB[m] = VecW ? en[kCh * (kNB * wave + m) + lane / kLpc] : en[16 * wave + m];
     };
     // The lane's fixed part of each W-row load: the 16-byte piece (VecW: of
     // 16 bytes, else a dword of it) of its channel's 256-byte row segment.
@@ -711,8 +729,8 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
 #pragma unroll
     for (int m = 0; m < kNB; ++m) {
       if constexpr (VecW) {
-        const int c = 4 * (4 * wave + m) + (lane >> 4);
-        colB[m] = (uint32_t)(n0 + 16 * ((lane & 15) ^ (c & 7)));
+        const int c = kCh * (kNB * wave + m) + lane / kLpc;
+        colB[m] = (uint32_t)(n0 + 16 * ((lane % kLpc) ^ (c & 7)));
       } else {
         const int c = 16 * wave + m;
         colB[m] = (uint32_t)(n0 + 16 * ((lane >> 2) ^ (c & 7)) + 4 * (lane & 3));
@@ -730,7 +748,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
       // reads zeros; at T = 64 the unit is rows 32·sub .. 32·sub + 31 of it
       const int dw = T < 32 ? (lane & 7) - 4 * sub : (T == 64 ? 8 * sub : 0) + (lane & 7);
       const bool in_run = T < 32 ? (dw >= 0 && dw < T / 4) : true;
-      uint8_t* sA = smem + (v % kUnits) * kUnitBytes;
+      uint8_t* sA = smem + (v % kUnits) * kUnitBytesT;
       uint8_t* sB = sA + kUnitA;
       // Offsets in 32 bits: ch·T + the tile's plane part < 2^31 and, with
       // ch < 2^16 and N < 2^23, ch·N is a 24-bit product below K·N < 2^31.
@@ -748,7 +766,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
         const uint32_t off = __umul24(ch, (uint32_t)N) + colB[m];
         const uint32_t o = live && ch != 0xFFFFu ? off : kOob;
         if constexpr (VecW) {
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr)(sB + 1024 * (4 * wave + m)), 16, o, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr)(sB + 1024 * (kNB * wave + m)), 16, o, 0, 0, 0);
         } else {
           __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr)(sB + BN * (16 * wave + m)), 4, o, 0, 0, 0);
         }
@@ -783,16 +801,16 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
       __builtin_amdgcn_s_barrier();
       __asm__ __volatile__("" ::: "memory");
       issue_ids(u + kAhead, nx, live);
-      const uint8_t* sA = smem + (u % kUnits) * kUnitBytes;
+      const uint8_t* sA = smem + (u % kUnits) * kUnitBytesT;
       const uint8_t* sB = sA + kUnitA;
 #pragma unroll
       for (int ks = 0; ks < KU / KS; ++ks) {
         v4i af = tr_frag<32>(sA + ks * KS * 32, 0, lane);
-        v4i b0 = tr_frag_wsw(sB + ks * KS * BN, WN * wave, lane);
-        v4i b1 = tr_frag_wsw(sB + ks * KS * BN, WN * wave + 32, lane);
+        v4i b0 = tr_frag_wsw<BN>(sB + ks * KS * BN, WN * wave, lane);
+        v4i b1 = CB > 1 ? tr_frag_wsw<BN>(sB + ks * KS * BN, WN * wave + 32, lane) : b0;
         lgkm_wait(af, b0, b1);
         tmp[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, b0, tmp[0], 0, 0, 0);
-        tmp[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, b1, tmp[1], 0, 0, 0);
+        if constexpr (CB > 1) tmp[CB - 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af, b1, tmp[CB - 1], 0, 0, 0);
       }
       ++u;
     };
@@ -908,7 +926,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     if (eligible[i]) continue;
     const int64_t tau = tile0 + i;
     const int64_t n = n0 + tid;
-    if (n >= N) continue;
+    if (tid >= BN || n >= N) continue;
     const int32_t* off = off_s + i * (kBins + 1);
     const double wsn = (double)a.w_scale[n];
     constexpr int TR = T < 32 ? T : 32;   // rows per pass
@@ -933,23 +951,38 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   }
 }
 
-template <int T, bool VecW, bool Gelu>
-int launch_tv(const LinearArgs& a, hipStream_t s) {
+template <int T, bool VecW, bool Gelu, int WNt>
+int launch_tvw(const LinearArgs& a, hipStream_t s) {
+  constexpr int kBN = kWaves * WNt;
   const int64_t nt = n_tiles(a.rows, T);
   const int64_t row_blocks = (nt + Cfg<T>::kTiles - 1) / Cfg<T>::kTiles;
-  const int32_t col_blocks = (int32_t)((a.N + BN - 1) / BN);
+  const int32_t col_blocks = (int32_t)((a.N + kBN - 1) / kBN);
   const int64_t grid = row_blocks * col_blocks;
   if (grid > 0x7FFFFFFF || row_blocks > 0x7FFFFFFF)
     return set_error(DSTAR_EUNSUPPORTED, "fmdq_linear: grid too large");
   // The LDS limit is a per-device property of the kernel: set it on every
   // launch (a host-side call; cheap, thread-safe, right on any device).
-  hipError_t e = hipFuncSetAttribute((const void*)linear_mfma_kernel<T, VecW, Gelu>,
+  hipError_t e = hipFuncSetAttribute((const void*)linear_mfma_kernel<T, VecW, Gelu, WNt>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
   if (e != hipSuccess)
     return set_error(DSTAR_EHIP, "fmdq_linear: hipFuncSetAttribute: %s", hipGetErrorString(e));
-  hipLaunchKernelGGL((linear_mfma_kernel<T, VecW, Gelu>), dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s,
-                     a, (int32_t)row_blocks, col_blocks);
+  hipLaunchKernelGGL((linear_mfma_kernel<T, VecW, Gelu, WNt>), dim3((unsigned)grid), dim3(kThreads), kLdsBytes,
+                     s, a, (int32_t)row_blocks, col_blocks);
   return check_launch("fmdq_linear (mfma)");
+}
+
+// Blocks of 128 × 256, or of 128 × 128 when the wider blocks would number
+// fewer than the CUs (each workgroup then has half the work, and the slowest
+// one, often a block of text tiles that runs two dense passes, finishes
+// sooner).  The narrow blocks need 16-byte W loads.
+template <int T, bool VecW, bool Gelu>
+int launch_tv(const LinearArgs& a, hipStream_t s) {
+  if constexpr (VecW) {
+    const int64_t row_blocks = (n_tiles(a.rows, T) + Cfg<T>::kTiles - 1) / Cfg<T>::kTiles;
+    const int64_t wide = row_blocks * ((a.N + BN - 1) / BN);
+    if (wide < cu_count()) return launch_tvw<T, VecW, Gelu, 32>(a, s);
+  }
+  return launch_tvw<T, VecW, Gelu, 64>(a, s);
 }
 
 template <int T>
