@@ -212,12 +212,22 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   static_assert(WN == 64 || (WN == 32 && VecW), "column widths");
   constexpr int kNB1 = WN / 16;           // W^T loads per wave and dense chunk (16 rows each)
   constexpr int kStageDenseT = (BM + BN) * BK;
+  // Dense ring stages: the narrow blocks' stages are half the size, so their
+  // ring is one stage deeper (more chunks in flight where a CU often holds a
+  // single workgroup).
+  constexpr int kStagesT = WN == 64 ? kStages : 4;
   constexpr int kUnitBT = KU * BN;
   constexpr int kUnitBytesT = kUnitA + kUnitBT;
-  static_assert(kStages * kStageDenseT <= kDataBytes && kUnits * kUnitBytesT <= kDataBytes, "rings fit");
-  constexpr int kWaitVmChunkT = wait_vm(2 + kNB1);           // one dense chunk's loads
-  constexpr int kWaitVmChunkIdsT = wait_vm(2 + kNB1 + 8);    // ... and eight id loads
-  constexpr int kWaitVmFirstT = wait_vm(2 * (2 + kNB1) + 8); // two chunks and the eight id loads
+  static_assert(kStagesT * kStageDenseT <= kDataBytes && kUnits * kUnitBytesT <= kDataBytes, "rings fit");
+  // Waits of the dense loops, in loads per wave (L per chunk; loads complete
+  // in order): chunk c + 1 has landed once at most the later kStagesT − 2
+  // chunks' loads (and, in the first iterations, the eight id loads issued
+  // after the first kStagesT chunks) are in flight.
+  constexpr int kLChunk = 2 + kNB1;
+  constexpr int kWaitVmChunkT = wait_vm((kStagesT - 2) * kLChunk);
+  constexpr int kWaitVmChunkIdsT = wait_vm((kStagesT - 2) * kLChunk + 8);
+  constexpr int kWaitVmFirstT = wait_vm((kStagesT - 1) * kLChunk + 8);
+  static_assert((kStagesT - 1) * kLChunk + 8 <= 63, "vmcnt range");
   constexpr int kTiles = Cfg<T>::kTiles;
   // Gathered units are scheduled per (32-row block, list): per block, first
   // the third-digit lists, then the second-digit lists, of the kTPB token
@@ -328,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
   }
   __asm__ __volatile__("" ::: "memory");   // keep these loads ahead of the dense ones
 #pragma unroll
-  for (int c = 0; c < kStages; ++c) issue(c, c);   // a chunk past K loads zeros
+  for (int c = 0; c < kStagesT; ++c) issue(c, c);   // a chunk past K loads zeros
 #pragma unroll
   for (int m = 0; m < kGo; ++m) {
     const int idx = tid + kThreads * m;
@@ -558,22 +568,22 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
             acc[rb][cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[rb], f.b[cb], acc[rb][cb], 0, 0, 0);
       };
 #pragma unroll
-      for (int c = 0; c < kStages; ++c) issue1(c, c);
-      __builtin_amdgcn_s_waitcnt(wait_vm(2 * (2 + kNB1)));  // chunk 0
+      for (int c = 0; c < kStagesT; ++c) issue1(c, c);
+      __builtin_amdgcn_s_waitcnt(wait_vm((kStagesT - 1) * kLChunk));  // chunk 0
       __asm__ __volatile__("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       __asm__ __volatile__("" ::: "memory");
       Frags1 g0, g1;
       read1(g0, 0, 0);
       for (int64_t c = 0; c < nchunks; ++c) {
-        const int st = (int)(c % kStages);
-        const int st1 = (int)((c + 1) % kStages);
+        const int st = (int)(c % kStagesT);
+        const int st1 = (int)((c + 1) % kStagesT);
         wait1(g0);
         mma1(g0);
         read1(g1, st, 1);
         __builtin_amdgcn_s_waitcnt(kWaitVmChunkT);   // chunk c + 1 (chunk c + 2 after it)
         bar_lds();                                   // also completes g1's reads
-        issue1(c + kStages, st);
+        issue1(c + kStagesT, st);
         wait1(g1);
         mma1(g1);
         read1(g0, st1, 0);
@@ -588,7 +598,7 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
       // The dense loop's first chunks again, then the ids again: the same
       // loads in flight, in the same order, as its waits count.
 #pragma unroll
-      for (int c = 0; c < kStages; ++c) issue(c, c);
+      for (int c = 0; c < kStagesT; ++c) issue(c, c);
       fetch(0);
       __asm__ __volatile__("" ::: "memory");
     }
@@ -627,11 +637,11 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     };
     // Chunk c's stage is free once every wave holds its second k-step's
     // fragments, so the wait for chunk c + 1 and the barrier sit between the
-    // two k-steps of chunk c, and chunk c + 3 is issued into that stage right
-    // after: three chunks are in flight.  Chunks past K load zeros (their
-    // fragments are read but never used), so every wait has the same count;
-    // in the first two waits the eight id loads (issued after chunk 2) may
-    // also be in flight.
+    // two k-steps of chunk c, and chunk c + kStagesT is issued into that stage
+    // right after: kStagesT chunks are in flight.  Chunks past K load zeros
+    // (their fragments are read but never used), so every wait has the same
+    // count; in the first kStagesT − 1 waits the eight id loads (issued after
+    // the first kStagesT chunks) may also be in flight.
     Frags f0, f1;
     __builtin_amdgcn_s_waitcnt(kWaitVmFirstT);
     __asm__ __volatile__("" ::: "memory");
@@ -639,17 +649,17 @@ __global__ __launch_bounds__(kThreads, 2) void linear_mfma_kernel(LinearArgs a, 
     __asm__ __volatile__("" ::: "memory");
     read(f0, 0, 0);
     for (int64_t c = 0; c < nchunks; ++c) {
-      const int st = (int)(c % kStages);
-      const int st1 = (int)((c + 1) % kStages);
+      const int st = (int)(c % kStagesT);
+      const int st1 = (int)((c + 1) % kStagesT);
       read(f1, st, 1);
       mma(f0);
-      if (c < 2) {
+      if (c < kStagesT - 1) {
         __builtin_amdgcn_s_waitcnt(kWaitVmChunkIdsT);
       } else {
         __builtin_amdgcn_s_waitcnt(kWaitVmChunkT);
       }
       bar_lds();
-      issue(c + kStages, st);
+      issue(c + kStagesT, st);
       read(f0, st1, 0);
       mma(f1);
     }
