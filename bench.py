@@ -91,11 +91,38 @@ def algorithmic(stage: str, rows: int, K: int, N: int, T: int) -> dict:
                 ops=2 * rows * N * K, extra_bytes=0)
 
 
+def code_only(text: str) -> str:
+    """C++ source without its comments and blank lines (string and character
+    literals kept whole), so that an edit of a comment does not change what
+    a stored counter reading is keyed by."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (ln.rstrip() for ln in "".join(out).split("\n"))
+    return "\n".join(ln for ln in lines if ln)
+
+
 def src_sha(stage: str) -> str:
+    """Hash of a stage's kernel sources, comments left out."""
     h = hashlib.sha256()
     for f in KERNEL_SRC[stage]:
-        with open(os.path.join(ROOT, "differential_mixed_precision_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "differential_mixed_precision_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_only(fh.read()).encode("utf-8"))
     return h.hexdigest()[:16]
 
 

@@ -42,9 +42,10 @@
 // columns; wave w owns all 128 rows and columns 64w .. 64w+63 (4 × 2 MFMA
 // 32x32x32 int8 tiles).  Grids that would give the CUs fewer workgroups than
 // there are CUs use blocks of 128 × 128 instead (wave w: columns 32w ..
-// 32w+31, 4 × 1 tiles; the same rings, half the W bytes per stage).  Dense part: 64-channel chunks of stage 1's aligned
-// codes ([rows][K]) and of W^T ([N][K]), both channel innermost, flow through
-// a 3-stage LDS ring filled by direct global-to-LDS buffer loads; a chunk's
+// 32w+31, 4 × 1 tiles; half the W bytes per stage, so the dense ring holds
+// four stages instead of three).  Dense part: 64-channel chunks of stage 1's
+// aligned codes ([rows][K]) and of W^T ([N][K]), both channel innermost, flow
+// through a 3-stage LDS ring filled by direct global-to-LDS buffer loads; a chunk's
 // stage is refilled as soon as every wave holds the fragments of its second
 // k-step, so three chunks are in flight, and each k-step's six fragment reads
 // are interleaved with the previous k-step's MFMAs.  The four 16-byte columns
@@ -58,8 +59,11 @@
 // three units ahead; the channel ids of up to 32 units at a time are staged
 // in LDS.  Both tiles have the channel outermost, so each lane assembles its
 // fragment with two ds_read_b64_tr_b8 transpose reads (W rows XOR-swizzled in
-// 16-byte pieces by channel mod 8).  The bin offsets and the unit schedule
-// are read while the first dense chunks are in flight.
+// 16-byte pieces by channel mod 8).  A workgroup whose second-digit units
+// would outnumber its dense chunks (tiles where most channels have PoT ≥ 7)
+// runs those digits instead as one dense pass over K, masked to its
+// sub-channels with PoT ≥ 7, before the dense loop.  The bin offsets and the
+// unit schedule are read while the first dense chunks are in flight.
 #include "fmdq_internal.h"
 
 namespace dstar {

@@ -93,3 +93,21 @@ def test_sq_summary_busy_fraction_from_counters(tmp_path):
     assert cells[6] == "32.0" and cells[7] == "**0.500**"          # 32000 busy of 64000 per SIMD
     assert cells[9] == "1.000"                                        # executed = algorithmic
     assert cells[12] == "0.250" and cells[13] == "0.500"
+
+
+def test_counter_readings_are_keyed_by_code_not_comments():
+    src = ('int f(int x) { // doubles x\n'
+           '  /* a block\n     comment */ return 2 * x;\n'
+           '}\n\n'
+           'const char* s = "a // b /* c */";\n'
+           "char q = '\"';  // a quote\n")
+    assert bench.code_only(src) == ('int f(int x) {\n   return 2 * x;\n}\n'
+                                    'const char* s = "a // b /* c */";\n'
+                                    "char q = '\"';")
+    # a comment edit keeps the key; a code edit changes it
+    assert bench.code_only(src.replace("doubles x", "twice x")) == bench.code_only(src)
+    assert bench.code_only(src.replace("2 * x", "3 * x")) != bench.code_only(src)
+    # every stage's sources hash to a short hex key
+    for stage in bench.KERNEL_SRC:
+        h = bench.src_sha(stage)
+        assert len(h) == 16 and int(h, 16) >= 0
