@@ -962,6 +962,43 @@ def test_linear_gelu_matches_oracle(dm, case):
     check_gelu(g.cpu().numpy(), r["y"], d["name"])
 
 
+# Shapes whose stage 3 takes each GELU instantiation of the product kernels:
+# 128 x 256 blocks of the two-workgroup kernel (its grid, 4 x 80 workgroups,
+# is not below the CU count, so the 128 x 128 variant is not taken), and the
+# ping-pong kernel (T = 32, K >= 4096, 8 x 16 blocks of 256 x 256 filling
+# half of the CUs).  The small cases above take the 128 x 128 blocks.
+GELU_WIDE = [
+    dict(rows=512, K=256, N=20480, T=32, seed=131, heavy=0.2, c_range=(0.02, 4000.0)),
+    dict(rows=2048, K=4096, N=4096, T=32, seed=132, heavy=0.1, c_range=(0.5, 64.0)),
+]
+
+
+@pytest.mark.parametrize("case", GELU_WIDE, ids=lambda c: f"{c['rows']}x{c['K']}x{c['N']}-s{c['seed']}")
+def test_linear_gelu_wide_blocks_match_oracle(dm, case):
+    """The fused GELU at the wide-block and ping-pong dispatch: Y_t of every
+    output bit for bit (oracle over every tile), GELU(Y_t) within an ulp."""
+    import torch
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    c = dict(case)
+    d = wl.make_custom(c.pop("rows"), c.pop("K"), c.pop("N"), c.pop("T"), seed=c.pop("seed"), **c)
+    rows, N, T = d["rows"], d["N"], d["token_tile"]
+    log(f"case {d['name']} (fused GELU, wide blocks)")
+    lay = dm.FmdqLayer(torch.from_numpy(d["w"]).to(dev), torch.from_numpy(d["w_scale"]).to(dev), rows, T,
+                       float(d["base"]), d["k0"], d["tokens_per_seq"])
+    y = torch.from_numpy(d["y_prev"]).to(dev)
+    g = torch.full((rows, N), float("nan"), dtype=torch.float32, device=dev)
+    lay.step(torch.from_numpy(d["x_t"]).to(dev), torch.from_numpy(d["x_prev"]).to(dev), y, gelu_out=g)
+    torch.cuda.synchronize()
+    y_gpu, g_gpu = y.cpu().numpy(), g.cpu().numpy()
+    codes, tags, _ = fmdq.quantize(d["x_t"], d["x_prev"], T, d["base"], d["k0"])
+    perm, off = fmdq.bucket(tags)
+    y_orc = par_linear(codes, tags, perm, off, d["w"], d["w_scale"], d["y_prev"], d["base"], T)
+    log(f"  oracle done {time.time() - t0:.1f}s")
+    check_y(y_gpu, y_orc, d["y_prev"], d["name"])
+    check_gelu(g_gpu, y_orc, d["name"])
+
+
 def test_mlp_chain_matches_oracle(dm):
     """Three timestep pairs through fc1 (fused GELU) → fc2 of the PixArt-alpha
     MLP at 256 rows: Y1 and Y2 bit for bit, G within an ulp.  The oracle's
