@@ -728,6 +728,47 @@ def test_ping_pong_kernel_matches_oracle(dm, case):
     log(f"  done {time.time() - t0:.1f}s")
 
 
+# Shapes whose stage-3 grid of 128 x 256 blocks is not below the CU count, so
+# the two-workgroup kernel keeps its wide blocks (the small cases take the
+# 128 x 128 variant): token tiles of 16, 32 and 64 rows, ragged last tiles,
+# third digits, and at T = 32 every sub-channel heavy (the masked dense
+# second-digit pass).
+WIDE_BLOCK_CASES = [
+    dict(rows=500, K=256, N=20480, T=16, seed=141, heavy=0.3, c_range=(0.02, 4000.0)),
+    dict(rows=500, K=256, N=20480, T=32, seed=142, heavy=1.0, c_range=(4.0, 8.0)),
+    dict(rows=520, K=320, N=20480, T=64, seed=143, heavy=0.05, c_range=(0.5, 64.0)),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_BLOCK_CASES, ids=lambda c: f"{c['rows']}x{c['K']}x{c['N']}-T{c['T']}")
+def test_wide_blocks_match_oracle(dm, case):
+    """The two-workgroup kernel's 128 x 256 blocks: every integer stage, S of
+    every tile and Y_t of every output bit for bit, and the per-group
+    accumulators of the last two tiles."""
+    t0 = time.time()
+    c = dict(case)
+    d = wl.make_custom(c.pop("rows"), c.pop("K"), c.pop("N"), c.pop("T"), seed=c.pop("seed"), **c)
+    rows, T = d["rows"], d["token_tile"]
+    nt = (rows + T - 1) // T
+    if T == 32:
+        assert _dense_digit_workgroups(d) > 0, "the case no longer takes the dense second-digit pass"
+    log(f"case {d['name']} (two-workgroup kernel, 128 x 256 blocks)")
+    g = gpu_layer(dm, d, dbg=(nt - 2, nt), sdump=(0, nt))
+    codes, tags, hist = fmdq.quantize(d["x_t"], d["x_prev"], T, d["base"], d["k0"])
+    perm, off = fmdq.bucket(tags)
+    check_integer_stages(g, codes, tags, hist, perm, off, d["name"], d["w"])
+    y, s_all = par_linear_s(codes, tags, perm, off, d["w"], d["w_scale"], d["y_prev"], d["base"], T)
+    log(f"  oracle done {time.time() - t0:.1f}s")
+    np.testing.assert_array_equal(g["s"], s_all, err_msg=f"{d['name']}: S (product kernel)")
+    check_y(g["y"], y, d["y_prev"], d["name"])
+    check_y(g["y_dbg"], y, d["y_prev"], d["name"] + " (per-group kernel)")
+    _, accs = fmdq.linear(codes, tags, perm, off, d["w"], d["w_scale"], d["y_prev"], d["base"], T,
+                          tiles=[nt - 2, nt - 1], return_acc=True)
+    for tau in (nt - 2, nt - 1):
+        np.testing.assert_array_equal(g["acc"][tau - (nt - 2)].astype(np.int64), accs[tau])
+    log(f"  done {time.time() - t0:.1f}s")
+
+
 # Stage 1 without the plain codes and stage 3 on the MFMA kernels: tiles that
 # the kernels finish with the exact int64 path (every sub-channel heavy, or a
 # tile at the bound), T of 16, 32 and 64, third digits, both kernels.
