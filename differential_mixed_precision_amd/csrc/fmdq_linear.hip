@@ -16,21 +16,24 @@
 // dumped (only it keeps one accumulator per FPoT group); it alone reads the
 // plain codes, which the MFMA kernels do not need.  The S dump is written by
 // whichever kernel runs.
+#include <atomic>
+
 #include "fmdq_internal.h"
 
 namespace dstar {
 
-// Compute units of the current device (looked up once per device).
+// Compute units of the current device (looked up once per device; threads
+// that race on the first lookup store the same value).
 int cu_count() {
-  static int counts[64] = {};
+  static std::atomic<int> counts[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (counts[dev] == 0) {
-    int n = 0;
+  int n = counts[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    counts[dev] = n;
+    counts[dev].store(n, std::memory_order_relaxed);
   }
-  return counts[dev];
+  return n;
 }
 
 int launch_linear(const LinearArgs& a, hipStream_t s) {
