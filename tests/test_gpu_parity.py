@@ -738,13 +738,22 @@ WIDE_BLOCK_CASES = [
     dict(rows=500, K=256, N=20480, T=32, seed=142, heavy=1.0, c_range=(4.0, 8.0)),
     dict(rows=520, K=320, N=20480, T=64, seed=143, heavy=0.05, c_range=(0.5, 64.0)),
 ]
+# Grids whose 128 x 256 blocks number fewer than the CUs but whose 128 x 128
+# blocks number more (8 x 40 = 320), so that some CUs run two narrow
+# workgroups (the small cases give every workgroup a CU of its own).
+NARROW4_CASES = [
+    dict(rows=1000, K=320, N=5120, T=32, seed=144, heavy=1.0, c_range=(4.0, 8.0)),
+    dict(rows=1024, K=256, N=5120, T=16, seed=145, heavy=0.3, c_range=(0.02, 4000.0)),
+]
 
 
-@pytest.mark.parametrize("case", WIDE_BLOCK_CASES, ids=lambda c: f"{c['rows']}x{c['K']}x{c['N']}-T{c['T']}")
+@pytest.mark.parametrize("case", WIDE_BLOCK_CASES + NARROW4_CASES,
+                         ids=lambda c: f"{c['rows']}x{c['K']}x{c['N']}-T{c['T']}")
 def test_wide_blocks_match_oracle(dm, case):
-    """The two-workgroup kernel's 128 x 256 blocks: every integer stage, S of
-    every tile and Y_t of every output bit for bit, and the per-group
-    accumulators of the last two tiles."""
+    """The two-workgroup kernel's 128 x 256 blocks, and its 128 x 128 blocks
+    on a grid larger than the CU count: every integer stage, S of every tile
+    and Y_t of every output bit for bit, and the per-group accumulators of
+    the last two tiles."""
     t0 = time.time()
     c = dict(case)
     d = wl.make_custom(c.pop("rows"), c.pop("K"), c.pop("N"), c.pop("T"), seed=c.pop("seed"), **c)
@@ -752,7 +761,7 @@ def test_wide_blocks_match_oracle(dm, case):
     nt = (rows + T - 1) // T
     if T == 32:
         assert _dense_digit_workgroups(d) > 0, "the case no longer takes the dense second-digit pass"
-    log(f"case {d['name']} (two-workgroup kernel, 128 x 256 blocks)")
+    log(f"case {d['name']} (two-workgroup kernel, {'128 x 128 blocks' if d['N'] == 5120 else '128 x 256 blocks'})")
     g = gpu_layer(dm, d, dbg=(nt - 2, nt), sdump=(0, nt))
     codes, tags, hist = fmdq.quantize(d["x_t"], d["x_prev"], T, d["base"], d["k0"])
     perm, off = fmdq.bucket(tags)
